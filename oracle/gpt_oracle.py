@@ -1,0 +1,346 @@
+"""Float64 CPU oracle for one pretraining step (forward + backward) of nanochat's GPT.
+
+TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the CPU-baseline
+leg of the benchmark may import this module. The product path (the HIP library
+and its Python binding) never calls it and shares no code with it.
+
+Every function below is the plain definition of what it computes, in float64,
+with no blocking or fusion beyond chunking the LM head over rows to bound
+memory. It takes the exact values the GPU holds (fp32 or bf16 widened to
+float64) and rounds nothing in between.
+
+Citation keys (page, then section on that page):
+
+* [P1] aethryn.com, "Nanochat: full-stack LLM training in 8,000 lines for $72";
+  sections "One dial controls everything" and "A Llama-class transformer with
+  ten modern departures".
+* [P2] aimarketly.com model card "nanochat-train" with the nanochat README;
+  section "Precision / dtype".
+* [P4] atlas.blal.pro wiki "nanochat — full-stack ChatGPT in ~8k lines";
+  section "How it works", item "0. The model".
+* [P5] energyai.berlin, "nanochat vs GPT-OSS"; section "Architectural
+  decisions" (subsections RoPE, RMSNorm, MQA, Squared ReLU, QK normalization,
+  Logit softcap) and section "Model scale and parameters".
+
+Readings where the pages are silent (each also fixed in the HIP path):
+
+* RMSNorm has no gain and eps = 2**-23 everywhere (the pages give no formula).
+* Attention scale is 1/sqrt(D) (SDPA's default; the pages name SDPA as the
+  fallback path).
+* RoPE pairs element i with i + D/2 ("split halves"), rotates by +angle with
+  angle = t * theta**(-2i/D), positions restart at 0 in every batch row.
+* QK-norm is a per-(token, head) RMSNorm over D, applied after RoPE.
+* Plain causal mask over the whole row; no document masking.
+* Loss is the mean over all B*T positions; targets are given explicitly.
+
+Parity pins: every function here is pinned by a test in ``tests/`` against a
+closed form, an invariant, a library routine or finite differences; none is
+"parity unpinned".
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+EPS = 2.0 ** -23          # RMSNorm epsilon (reading: float32 machine epsilon)
+ROPE_THETA = 10000.0      # [P1] "A Llama-class transformer..."; RoPE base
+SOFTCAP = 15.0            # [P1] same section; logits = 15 * tanh(z / 15)
+
+
+# ---------------------------------------------------------------------------
+# Shapes: the depth dial
+# ---------------------------------------------------------------------------
+
+def config_from_depth(depth: int, vocab: int = 65536, seq_len: int = 2048, n_kv_head: int = 1) -> dict:
+    """[P1] "One dial controls everything": width = 64 * depth, heads = width / 128.
+
+    [P4] item "0. The model": head dim 128; [P5] "Squared ReLU": MLP 4x wide;
+    MQA ([P5] "Multi-Query Attention") by default, so one K/V head.
+    """
+    C = 64 * depth
+    D = 128
+    return dict(n_layer=depth, model_dim=C, n_head=C // D, n_kv_head=n_kv_head,
+                head_dim=D, mlp_dim=4 * C, vocab_size=vocab, max_seq_len=seq_len,
+                rope_theta=ROPE_THETA, logit_softcap=SOFTCAP, norm_eps=EPS)
+
+
+def param_shapes(cfg: dict):
+    """Canonical parameter order and shapes (rows, cols) of every weight.
+
+    Untied embedding and LM head ([P1] "untied"; [P5] "Embedding strategy"),
+    bias-free linears ([P4] item 0: bias=False). W_qkv stacks the query heads,
+    then the K head(s), then the V head(s).
+    """
+    C, H, Hkv, D = cfg["model_dim"], cfg["n_head"], cfg["n_kv_head"], cfg["head_dim"]
+    F, V = cfg["mlp_dim"], cfg["vocab_size"]
+    shapes = [("wte", V, C)]
+    for l in range(cfg["n_layer"]):
+        shapes += [(f"h{l}.w_qkv", (H + 2 * Hkv) * D, C), (f"h{l}.w_o", C, H * D),
+                   (f"h{l}.w_1", F, C), (f"h{l}.w_2", C, F)]
+    shapes.append(("lm_head", V, C))
+    return shapes
+
+
+def param_count(cfg: dict) -> int:
+    return sum(r * c for _, r, c in param_shapes(cfg))
+
+
+def unflatten(cfg: dict, flat: np.ndarray) -> dict:
+    out, off = {}, 0
+    for name, r, c in param_shapes(cfg):
+        out[name] = flat[off:off + r * c].reshape(r, c)
+        off += r * c
+    assert off == flat.size
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Building blocks
+# ---------------------------------------------------------------------------
+
+def rmsnorm(x: np.ndarray, eps: float = EPS):
+    """Parameter-free RMSNorm over the last axis ([P1] "A Llama-class
+    transformer..."; [P5] "RMSNorm without learnable parameters").
+
+    y = x / sqrt(mean(x**2) + eps). Returns (y, r) with r = 1/sqrt(mean + eps).
+    """
+    r = 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    return x * r, r
+
+
+def rmsnorm_bwd(dy: np.ndarray, y: np.ndarray, r: np.ndarray) -> np.ndarray:
+    """Gradient of y = x*r(x): dx = r * (dy - y * mean(dy*y))."""
+    return r * (dy - y * np.mean(dy * y, axis=-1, keepdims=True))
+
+
+def rope_tables(T: int, D: int, theta: float = ROPE_THETA):
+    """cos/sin of angle[t, i] = t * theta**(-2i/D), i < D/2 ([P1]; [P5] "RoPE")."""
+    i = np.arange(D // 2, dtype=np.float64)
+    inv_freq = theta ** (-2.0 * i / D)
+    ang = np.arange(T, dtype=np.float64)[:, None] * inv_freq[None, :]
+    return np.cos(ang), np.sin(ang)
+
+
+def rope(x: np.ndarray, cos: np.ndarray, sin: np.ndarray) -> np.ndarray:
+    """Rotate pairs (x_i, x_{i+D/2}) by +angle. x is [B, T, heads, D]."""
+    h = x.shape[-1] // 2
+    x1, x2 = x[..., :h], x[..., h:]
+    c = cos[None, :, None, :]
+    s = sin[None, :, None, :]
+    return np.concatenate([x1 * c - x2 * s, x1 * s + x2 * c], axis=-1)
+
+
+def rope_bwd(dy: np.ndarray, cos: np.ndarray, sin: np.ndarray) -> np.ndarray:
+    """Transpose of the rotation (the inverse rotation, by -angle)."""
+    h = dy.shape[-1] // 2
+    d1, d2 = dy[..., :h], dy[..., h:]
+    c = cos[None, :, None, :]
+    s = sin[None, :, None, :]
+    return np.concatenate([d1 * c + d2 * s, -d1 * s + d2 * c], axis=-1)
+
+
+def causal_mqa_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray):
+    """Causal attention where all query heads share one K/V head
+    ([P5] "Multi-Query Attention"; [P1] causal decoder).
+
+    q [B, T, H, D]; k, v [B, T, D]. Scores s = q.k / sqrt(D), key u <= query t.
+    Returns o [B, T, H, D] and the log-sum-exp of the scaled scores [B, H, T].
+    """
+    B, T, H, D = q.shape
+    scale = 1.0 / math.sqrt(D)
+    mask = np.tril(np.ones((T, T), dtype=bool))
+    o = np.empty_like(q)
+    lse = np.empty((B, H, T))
+    for b in range(B):
+        s = np.einsum("thd,ud->htu", q[b], k[b]) * scale
+        s = np.where(mask[None], s, -np.inf)
+        m = s.max(axis=-1, keepdims=True)
+        e = np.exp(s - m)
+        z = e.sum(axis=-1, keepdims=True)
+        p = e / z
+        o[b] = np.einsum("htu,ud->thd", p, v[b])
+        lse[b] = (m + np.log(z))[..., 0]
+    return o, lse
+
+
+def causal_mqa_attention_bwd(do, q, k, v):
+    """Backward of ``causal_mqa_attention`` through the softmax Jacobian.
+
+    dP = do.v ; dS = P * (dP - sum_u P dP) ; dq = dS.k/sqrt(D) ;
+    dk = sum over heads and queries of dS^T q / sqrt(D) ; dv = sum of P^T do.
+    """
+    B, T, H, D = q.shape
+    scale = 1.0 / math.sqrt(D)
+    mask = np.tril(np.ones((T, T), dtype=bool))
+    dq = np.empty_like(q)
+    dk = np.empty_like(k)
+    dv = np.empty_like(v)
+    for b in range(B):
+        s = np.einsum("thd,ud->htu", q[b], k[b]) * scale
+        s = np.where(mask[None], s, -np.inf)
+        e = np.exp(s - s.max(axis=-1, keepdims=True))
+        p = e / e.sum(axis=-1, keepdims=True)
+        dp = np.einsum("thd,ud->htu", do[b], v[b])
+        ds = p * (dp - (p * dp).sum(axis=-1, keepdims=True))
+        dq[b] = np.einsum("htu,ud->thd", ds, k[b]) * scale
+        dk[b] = np.einsum("htu,thd->ud", ds, q[b]) * scale
+        dv[b] = np.einsum("htu,thd->ud", p, do[b])
+    return dq, dk, dv
+
+
+def softcap(z: np.ndarray, c: float = SOFTCAP) -> np.ndarray:
+    """[P1]: logits are squashed to c * tanh(z / c) with c = 15, in fp32 or wider."""
+    return c * np.tanh(z / c)
+
+
+def softcap_bwd(dzc: np.ndarray, zc: np.ndarray, c: float = SOFTCAP) -> np.ndarray:
+    """d/dz [c tanh(z/c)] = 1 - tanh^2 = 1 - (zc/c)^2."""
+    return dzc * (1.0 - (zc / c) ** 2)
+
+
+def logsumexp(z: np.ndarray) -> np.ndarray:
+    m = z.max(axis=-1, keepdims=True)
+    return (m + np.log(np.exp(z - m).sum(axis=-1, keepdims=True)))[..., 0]
+
+
+# ---------------------------------------------------------------------------
+# The step
+# ---------------------------------------------------------------------------
+
+def _split_qkv(qkv, H, Hkv, D):
+    B, T, _ = qkv.shape
+    q = qkv[..., :H * D].reshape(B, T, H, D)
+    k = qkv[..., H * D:(H + Hkv) * D].reshape(B, T, Hkv, D)
+    v = qkv[..., (H + Hkv) * D:].reshape(B, T, Hkv, D)
+    return q, k, v
+
+
+def forward(cfg: dict, params: dict, idx: np.ndarray, targets: np.ndarray, row_chunk: int = 4096):
+    """Forward pass and mean cross-entropy loss. Returns (loss, row_loss[B,T], cache).
+
+    Block order ([P1] "A Llama-class transformer..."; [P4] item 0; [P5]):
+    x = rmsnorm(wte[idx]); per layer x += attn(rmsnorm(x)), x += mlp(rmsnorm(x));
+    logits = softcap(rmsnorm(x) W_lm^T); loss = mean(lse(logits) - logits[target]).
+    """
+    assert cfg["n_kv_head"] == 1, "the oracle's attention is multi-query (one K/V head)"
+    B, T = idx.shape
+    C, H, D = cfg["model_dim"], cfg["n_head"], cfg["head_dim"]
+    eps, c = cfg["norm_eps"], cfg["logit_softcap"]
+    cos, sin = rope_tables(T, D, cfg["rope_theta"])
+    W = {k: np.asarray(v, dtype=np.float64) for k, v in params.items()}
+
+    x, r0 = rmsnorm(W["wte"][idx], eps)
+    cache = dict(r0=r0, layers=[], cos=cos, sin=sin)
+    for l in range(cfg["n_layer"]):
+        h1, r1 = rmsnorm(x, eps)
+        qkv = h1 @ W[f"h{l}.w_qkv"].T
+        q, k, v = _split_qkv(qkv, H, 1, D)
+        qr, kr = rope(q, cos, sin), rope(k, cos, sin)
+        qn, rq = rmsnorm(qr, eps)
+        kn, rk = rmsnorm(kr, eps)
+        o, lse = causal_mqa_attention(qn, kn[:, :, 0], v[:, :, 0])
+        o2 = o.reshape(B, T, H * D)
+        x = x + o2 @ W[f"h{l}.w_o"].T
+        h2, r2 = rmsnorm(x, eps)
+        u = h2 @ W[f"h{l}.w_1"].T
+        a = np.maximum(u, 0.0) ** 2
+        x = x + a @ W[f"h{l}.w_2"].T
+        cache["layers"].append(dict(h1=h1, r1=r1, qn=qn, rq=rq, kn=kn, rk=rk, v=v,
+                                    o=o, lse=lse, h2=h2, r2=r2, u=u, a=a))
+    hf, rf = rmsnorm(x, eps)
+    cache.update(hf=hf, rf=rf)
+
+    N = B * T
+    hf2 = hf.reshape(N, C)
+    tg = targets.reshape(N)
+    row_loss = np.empty(N)
+    lse_rows = np.empty(N)
+    for s0 in range(0, N, row_chunk):
+        s1 = min(N, s0 + row_chunk)
+        zc = softcap(hf2[s0:s1] @ W["lm_head"].T, c)
+        lse_rows[s0:s1] = logsumexp(zc)
+        row_loss[s0:s1] = lse_rows[s0:s1] - zc[np.arange(s1 - s0), tg[s0:s1]]
+    cache["lse_rows"] = lse_rows
+    loss = float(row_loss.mean())
+    return loss, row_loss.reshape(B, T), cache
+
+
+def backward(cfg: dict, params: dict, idx: np.ndarray, targets: np.ndarray, cache: dict,
+             dloss: float = 1.0, row_chunk: int = 4096) -> dict:
+    """Analytic gradients of dloss * loss with respect to every weight."""
+    B, T = idx.shape
+    N = B * T
+    C, H, D = cfg["model_dim"], cfg["n_head"], cfg["head_dim"]
+    c = cfg["logit_softcap"]
+    cos, sin = cache["cos"], cache["sin"]
+    W = {k: np.asarray(v, dtype=np.float64) for k, v in params.items()}
+    G = {k: np.zeros_like(v) for k, v in W.items()}
+
+    # LM head + softcap + cross-entropy
+    hf2 = cache["hf"].reshape(N, C)
+    tg = targets.reshape(N)
+    dhf = np.empty((N, C))
+    for s0 in range(0, N, row_chunk):
+        s1 = min(N, s0 + row_chunk)
+        zc = softcap(hf2[s0:s1] @ W["lm_head"].T, c)
+        p = np.exp(zc - cache["lse_rows"][s0:s1, None])
+        p[np.arange(s1 - s0), tg[s0:s1]] -= 1.0
+        dz = softcap_bwd(p * (dloss / N), zc, c)
+        G["lm_head"] += dz.T @ hf2[s0:s1]
+        dhf[s0:s1] = dz @ W["lm_head"]
+    dx = rmsnorm_bwd(dhf.reshape(B, T, C), cache["hf"], cache["rf"])
+
+    for l in reversed(range(cfg["n_layer"])):
+        L = cache["layers"][l]
+        # MLP: x_out = x_mid + relu(u)^2 W2^T, u = rmsnorm(x_mid) W1^T
+        G[f"h{l}.w_2"] += dx.reshape(N, C).T @ L["a"].reshape(N, -1)
+        da = dx @ W[f"h{l}.w_2"]
+        du = da * 2.0 * np.maximum(L["u"], 0.0)
+        G[f"h{l}.w_1"] += du.reshape(N, -1).T @ L["h2"].reshape(N, C)
+        dh2 = du @ W[f"h{l}.w_1"]
+        dx = dx + rmsnorm_bwd(dh2, L["h2"], L["r2"])
+        # attention: x_mid = x_in + o W_o^T
+        o2 = L["o"].reshape(B, T, H * D)
+        G[f"h{l}.w_o"] += dx.reshape(N, C).T @ o2.reshape(N, -1)
+        do = (dx @ W[f"h{l}.w_o"]).reshape(B, T, H, D)
+        dqn, dkn, dv = causal_mqa_attention_bwd(do, L["qn"], L["kn"][:, :, 0], L["v"][:, :, 0])
+        dqr = rmsnorm_bwd(dqn, L["qn"], L["rq"])
+        dkr = rmsnorm_bwd(dkn[:, :, None, :], L["kn"], L["rk"])
+        dq = rope_bwd(dqr, cos, sin)
+        dk = rope_bwd(dkr, cos, sin)
+        dqkv = np.concatenate([dq.reshape(B, T, H * D), dk.reshape(B, T, D),
+                               dv.reshape(B, T, D)], axis=-1)
+        G[f"h{l}.w_qkv"] += dqkv.reshape(N, -1).T @ L["h1"].reshape(N, C)
+        dh1 = dqkv @ W[f"h{l}.w_qkv"]
+        dx = dx + rmsnorm_bwd(dh1, L["h1"], L["r1"])
+
+    # embedding: x0 = rmsnorm(wte[idx]); dwte[v] = sum over positions with idx == v
+    e = W["wte"][idx]
+    y0 = e * cache["r0"]
+    de = rmsnorm_bwd(dx, y0, cache["r0"])
+    np.add.at(G["wte"], idx.reshape(N), de.reshape(N, C))
+    return G
+
+
+def step(cfg: dict, params: dict, idx: np.ndarray, targets: np.ndarray, dloss: float = 1.0):
+    """One forward + backward. Returns (loss, row_loss [B, T], grads dict)."""
+    loss, row_loss, cache = forward(cfg, params, idx, targets)
+    grads = backward(cfg, params, idx, targets, cache, dloss)
+    return loss, row_loss, grads
+
+
+def forward_rows(cfg: dict, params: dict, idx: np.ndarray, targets: np.ndarray) -> np.ndarray:
+    """Per-position losses only (no cache kept beyond one layer's use)."""
+    _, row_loss, _ = forward(cfg, params, idx, targets)
+    return row_loss
+
+
+def flops_per_token(cfg: dict, T: int) -> dict:
+    """Algorithmic FLOPs per token for fwd+bwd: 6 * (matmul params) plus causal
+    attention counted over the T(T+1)/2 needed (query, key) pairs."""
+    C, H, D, F, V, Lyr = (cfg["model_dim"], cfg["n_head"], cfg["head_dim"],
+                          cfg["mlp_dim"], cfg["vocab_size"], cfg["n_layer"])
+    n_mm = Lyr * ((H + 2) * D * C + C * H * D + 2 * F * C) + V * C
+    attn = 6.0 * Lyr * H * D * (T + 1)
+    return dict(matmul=6.0 * n_mm, attention=attn, total=6.0 * n_mm + attn)

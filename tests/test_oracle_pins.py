@@ -1,0 +1,364 @@
+"""Pins of the float64 oracle against closed forms, invariants, printed values and
+library routines (CPU only). Each test names what a plausible mistake in the
+oracle would break."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import gpt_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "pages_facts.json")
+
+
+def _facts():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+def tiny_cfg(**kw):
+    cfg = dict(n_layer=2, model_dim=128, n_head=1, n_kv_head=1, head_dim=128, mlp_dim=512,
+               vocab_size=512, max_seq_len=64, rope_theta=O.ROPE_THETA,
+               logit_softcap=O.SOFTCAP, norm_eps=O.EPS)
+    cfg.update(kw)
+    return cfg
+
+
+def rand_params(cfg, seed=0, std=0.02):
+    rng = np.random.default_rng(seed)
+    return {n: rng.standard_normal((r, c)) * std for n, r, c in O.param_shapes(cfg)}
+
+
+# ---------------------------------------------------------------- shapes ---
+
+def test_depth_dial_matches_pages():
+    f = _facts()
+    cfg = O.config_from_depth(20)
+    assert cfg["model_dim"] == f["d20_shape"]["model_dim"]
+    assert cfg["n_head"] == f["d20_shape"]["n_head"]
+    assert cfg["head_dim"] == f["d20_shape"]["head_dim"]
+    assert cfg["mlp_dim"] == f["mlp_expansion"]["value"] * cfg["model_dim"]
+    assert cfg["vocab_size"] == f["vocab_size"]["value"]
+    assert O.ROPE_THETA == f["rope_theta"]["value"]
+    assert O.SOFTCAP == f["logit_softcap"]["value"]
+
+
+def test_param_count_printed_values_mha():
+    """With one K/V head per query head the printed d20 and d32 sizes reproduce."""
+    f = _facts()
+    d20 = O.config_from_depth(20)
+    d20["n_kv_head"] = d20["n_head"]
+    # the page prints 560.9 million: 560,988,160 truncated (not rounded) to 0.1 M
+    assert math.floor(O.param_count(d20) / 1e5) / 10 == f["d20_params_mha_millions_1dp"]["value"]
+    assert O.param_count(d20) == 560_988_160
+    d32 = O.config_from_depth(32)
+    d32["n_kv_head"] = d32["n_head"]
+    assert round(O.param_count(d32) / 1e9, 2) == f["d32_params_mha_billions_2dp"]["value"]
+    assert O.param_count(d32) == 1_879_048_192
+
+
+def test_param_count_mqa_closed_form():
+    for depth in (4, 12, 20, 24):
+        cfg = O.config_from_depth(depth)
+        C, H, D, V, L = cfg["model_dim"], cfg["n_head"], 128, 65536, depth
+        expect = 2 * V * C + L * ((H + 2) * D * C + C * H * D + 8 * C * C)
+        assert O.param_count(cfg) == expect
+    assert O.param_count(O.config_from_depth(20)) == 502_005_760
+    assert O.param_count(tiny_cfg()) == 524_288
+
+
+# --------------------------------------------------------------- rmsnorm ---
+
+def test_rmsnorm_output_rms_closed_form():
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((50, 256)) * np.exp(rng.uniform(-8, 2, size=(50, 1)))
+    y, r = O.rmsnorm(x)
+    m = np.mean(x * x, axis=-1)
+    np.testing.assert_allclose(np.sqrt(np.mean(y * y, axis=-1)), np.sqrt(m / (m + O.EPS)), rtol=1e-13)
+    np.testing.assert_allclose(r[:, 0], 1 / np.sqrt(m + O.EPS), rtol=1e-14)
+
+
+def test_rmsnorm_matches_bare_torch_rms_norm_fp32():
+    """Bare F.rms_norm on float32 input (no eps given) is the op the pages name;
+    at weight scale 0.02 an eps other than 2**-23 would differ by >1e-3."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(4)
+    x32 = (rng.standard_normal((64, 256)) * 0.02).astype(np.float32)
+    yt = torch.nn.functional.rms_norm(torch.from_numpy(x32), (256,)).double().numpy()
+    yo, _ = O.rmsnorm(x32.astype(np.float64))
+    np.testing.assert_allclose(yt, yo, rtol=0, atol=4e-7)
+
+
+def test_rmsnorm_bwd_euler_identity_and_fd():
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((8, 64)) * 0.01
+    dy = rng.standard_normal((8, 64))
+    y, r = O.rmsnorm(x)
+    dx = O.rmsnorm_bwd(dy, y, r)
+    m = np.mean(x * x, axis=-1)
+    np.testing.assert_allclose(np.sum(x * dx, -1), O.EPS / (m + O.EPS) * np.sum(y * dy, -1),
+                               rtol=1e-9, atol=1e-18)
+    h = 1e-7
+    for (i, j) in [(0, 0), (3, 17), (7, 63)]:
+        xp, xm = x.copy(), x.copy()
+        xp[i, j] += h
+        xm[i, j] -= h
+        fd = (np.sum(O.rmsnorm(xp)[0] * dy) - np.sum(O.rmsnorm(xm)[0] * dy)) / (2 * h)
+        assert abs(fd - dx[i, j]) <= 1e-6 * max(1.0, abs(dx[i, j]))
+
+
+# ------------------------------------------------------------------ rope ---
+
+def test_rope_matches_complex_rotation_convention():
+    """Pairs (x_i, x_{i+D/2}) as the complex number x_i + 1j x_{i+D/2}, multiplied
+    by exp(1j * t * theta**(-2i/D)). Pins pairing, sign and frequencies."""
+    rng = np.random.default_rng(6)
+    T, D = 37, 128
+    x = rng.standard_normal((2, T, 3, D))
+    cos, sin = O.rope_tables(T, D)
+    y = O.rope(x, cos, sin)
+    zc = x[..., :D // 2] + 1j * x[..., D // 2:]
+    t = np.arange(T)[None, :, None, None]
+    freq = 10000.0 ** (-np.arange(0, D, 2) / D)
+    rot = zc * np.exp(1j * t * freq)
+    np.testing.assert_allclose(y[..., :D // 2], rot.real, atol=1e-12)
+    np.testing.assert_allclose(y[..., D // 2:], rot.imag, atol=1e-12)
+
+
+def test_rope_invariants():
+    rng = np.random.default_rng(7)
+    T, D = 64, 128
+    cos, sin = O.rope_tables(T, D)
+    x = rng.standard_normal((1, T, 2, D))
+    y = O.rope(x, cos, sin)
+    np.testing.assert_allclose(np.linalg.norm(y, axis=-1), np.linalg.norm(x, axis=-1), rtol=1e-13)
+    np.testing.assert_array_equal(y[:, 0], x[:, 0])           # position 0 is the identity
+    np.testing.assert_allclose(O.rope_bwd(y, cos, sin), x, atol=1e-12)   # R^T R = I
+    # relative position: <R_m a, R_n b> depends only on m - n
+    a, b = rng.standard_normal(D), rng.standard_normal(D)
+    xa = np.broadcast_to(a, (1, T, 1, D)).copy()
+    xb = np.broadcast_to(b, (1, T, 1, D)).copy()
+    ra, rb = O.rope(xa, cos, sin)[0, :, 0], O.rope(xb, cos, sin)[0, :, 0]
+    for (m, n, s) in [(10, 3, 20), (5, 5, 40), (0, 30, 33)]:
+        assert abs(ra[m] @ rb[n] - ra[m + s] @ rb[n + s]) < 1e-10
+    # adjoint
+    g = rng.standard_normal(x.shape)
+    assert abs(np.sum(y * g) - np.sum(x * O.rope_bwd(g, cos, sin))) < 1e-10
+
+
+def test_rope_commutes_with_qk_norm():
+    rng = np.random.default_rng(8)
+    T, D = 16, 128
+    cos, sin = O.rope_tables(T, D)
+    x = rng.standard_normal((2, T, 3, D)) * 0.3
+    a = O.rmsnorm(O.rope(x, cos, sin))[0]
+    b = O.rope(O.rmsnorm(x)[0], cos, sin)
+    np.testing.assert_allclose(a, b, atol=1e-14)
+
+
+# ------------------------------------------------------------- attention ---
+
+def _qkn(rng, B, T, H, D, scale=1.0):
+    q = O.rmsnorm(rng.standard_normal((B, T, H, D)) * scale)[0]
+    k = O.rmsnorm(rng.standard_normal((B, T, D)) * scale)[0]
+    v = rng.standard_normal((B, T, D))
+    return q, k, v
+
+
+def test_attention_special_cases():
+    rng = np.random.default_rng(9)
+    B, T, H, D = 2, 24, 3, 128
+    q, k, v = _qkn(rng, B, T, H, D)
+    o, lse = O.causal_mqa_attention(q, k, v)
+    # position 0 attends only to itself
+    for h in range(H):
+        np.testing.assert_allclose(o[:, 0, h], v[:, 0], atol=1e-14)
+    # q = 0 gives uniform weights over the causal prefix
+    o0, lse0 = O.causal_mqa_attention(np.zeros_like(q), k, v)
+    prefix_mean = np.cumsum(v, axis=1) / np.arange(1, T + 1)[None, :, None]
+    for h in range(H):
+        np.testing.assert_allclose(o0[:, :, h], prefix_mean, atol=1e-13)
+    np.testing.assert_allclose(lse0[0, 0], np.log(np.arange(1, T + 1)), atol=1e-13)
+    # identical query heads give identical outputs (one shared K/V head)
+    q2 = np.repeat(q[:, :, :1], H, axis=2)
+    o2, _ = O.causal_mqa_attention(q2, k, v)
+    for h in range(1, H):
+        np.testing.assert_array_equal(o2[:, :, h], o2[:, :, 0])
+    # |scaled score| <= sqrt(D) for RMS-normalised q, k (Cauchy-Schwarz)
+    s = np.einsum("bthd,bud->bhtu", q, k) / math.sqrt(D)
+    assert np.abs(s).max() <= math.sqrt(D)
+
+
+def test_attention_matches_torch_sdpa_float64():
+    torch = pytest.importorskip("torch")
+    import torch.nn.functional as F
+    rng = np.random.default_rng(10)
+    B, T, H, D = 2, 33, 4, 128
+    q, k, v = _qkn(rng, B, T, H, D)
+    o, _ = O.causal_mqa_attention(q, k, v)
+    qt = torch.tensor(q).permute(0, 2, 1, 3).requires_grad_()
+    kt = torch.tensor(k)[:, None].requires_grad_()
+    vt = torch.tensor(v)[:, None].requires_grad_()
+    ot = F.scaled_dot_product_attention(qt, kt, vt, is_causal=True, enable_gqa=True)
+    np.testing.assert_allclose(ot.permute(0, 2, 1, 3).detach().numpy(), o, atol=1e-13)
+    do = rng.standard_normal(o.shape)
+    ot.backward(torch.tensor(do).permute(0, 2, 1, 3))
+    dq, dk, dv = O.causal_mqa_attention_bwd(do, q, k, v)
+    np.testing.assert_allclose(qt.grad.permute(0, 2, 1, 3).numpy(), dq, atol=1e-12)
+    np.testing.assert_allclose(kt.grad[:, 0].numpy(), dk, atol=1e-12)
+    np.testing.assert_allclose(vt.grad[:, 0].numpy(), dv, atol=1e-12)
+
+
+# ------------------------------------------------------- softcap and CE ---
+
+def test_softcap_bound_and_derivative():
+    z = np.linspace(-200, 200, 4001)
+    zc = O.softcap(z)
+    assert np.all(np.abs(zc) <= O.SOFTCAP)
+    assert np.all(np.abs(zc[np.abs(z) < 30]) < O.SOFTCAP)
+    small = np.abs(z) < 0.2
+    np.testing.assert_allclose(zc[small], z[small], atol=1e-4)
+    h = 1e-6
+    fd = (O.softcap(z + h) - O.softcap(z - h)) / (2 * h)
+    np.testing.assert_allclose(O.softcap_bwd(np.ones_like(z), zc), fd, atol=1e-8)
+
+
+def test_zero_head_gives_log_vocab_and_closed_form_grads():
+    """W_lm = 0: every logit is 0, loss = ln V exactly, dW_lm = ((1/V - onehot)^T h_f)/N
+    and every other gradient is exactly zero (dh_f = dz W_lm = 0)."""
+    cfg = tiny_cfg(n_layer=1)
+    P = rand_params(cfg, seed=11)
+    P["lm_head"] = np.zeros_like(P["lm_head"])
+    rng = np.random.default_rng(12)
+    B, T, V = 2, 16, cfg["vocab_size"]
+    idx = rng.integers(0, V, (B, T))
+    tg = rng.integers(0, V, (B, T))
+    loss, rows, cache = O.forward(cfg, P, idx, tg)
+    assert loss == pytest.approx(math.log(V), abs=1e-15)
+    assert math.log(512) == pytest.approx(6.238324625039508, abs=1e-15)
+    G = O.backward(cfg, P, idx, tg, cache)
+    for name, g in G.items():
+        if name != "lm_head":
+            assert np.all(g == 0.0), name
+    N = B * T
+    onehot = np.zeros((N, V))
+    onehot[np.arange(N), tg.reshape(N)] = 1.0
+    expect = (np.full((N, V), 1.0 / V) - onehot).T @ cache["hf"].reshape(N, -1) / N
+    np.testing.assert_allclose(G["lm_head"], expect, atol=1e-15)
+
+
+def test_cross_entropy_matches_torch_on_softcapped_logits():
+    torch = pytest.importorskip("torch")
+    cfg = tiny_cfg(n_layer=1)
+    P = rand_params(cfg, seed=13, std=0.2)
+    rng = np.random.default_rng(14)
+    idx = rng.integers(0, 512, (2, 20))
+    tg = rng.integers(0, 512, (2, 20))
+    loss, rows, cache = O.forward(cfg, P, idx, tg)
+    z = cache["hf"].reshape(40, -1) @ P["lm_head"].T
+    zc = torch.tensor(15.0 * np.tanh(z / 15.0))
+    ref = torch.nn.functional.cross_entropy(zc, torch.tensor(tg.reshape(-1)), reduction="none")
+    np.testing.assert_allclose(rows.reshape(-1), ref.numpy(), rtol=1e-13)
+    assert 0 < loss < math.log(512) + 2 * 15
+
+
+# ------------------------------------------------------------ whole step ---
+
+def test_whole_step_central_differences():
+    """Analytic backward vs central differences of the float64 loss, on every tensor."""
+    cfg = tiny_cfg(n_layer=2, vocab_size=64, mlp_dim=512)
+    P = rand_params(cfg, seed=15, std=0.1)
+    rng = np.random.default_rng(16)
+    B, T = 2, 8
+    idx = rng.integers(0, 64, (B, T))
+    tg = rng.integers(0, 64, (B, T))
+    dloss = 0.75
+    loss, _, G = O.step(cfg, P, idx, tg, dloss)
+    h = 1e-5
+    for name, W in P.items():
+        pick = [tuple(rng.integers(0, s) for s in W.shape) for _ in range(4)]
+        if name == "wte":   # rows that are actually used
+            pick = [(int(idx[0, 0]), 5), (int(idx[1, 3]), 100), (int(idx[0, 7]), 0)]
+        for ij in pick:
+            old = W[ij]
+            W[ij] = old + h
+            lp = O.forward(cfg, P, idx, tg)[0]
+            W[ij] = old - h
+            lm = O.forward(cfg, P, idx, tg)[0]
+            W[ij] = old
+            fd = dloss * (lp - lm) / (2 * h)
+            # float64 central differences: truncation O(h^2) plus round-off ~ 1e-16 * loss / h
+            assert abs(fd - G[name][ij]) <= 1e-6 * abs(fd) + 2e-10, (name, ij, fd, G[name][ij])
+
+
+def _torch_step(cfg, P, idx, tg):
+    """A second, independent float64 implementation with torch autograd and
+    torch's own rms_norm, SDPA and cross_entropy."""
+    import torch
+    import torch.nn.functional as F
+    eps, c, H, D = cfg["norm_eps"], cfg["logit_softcap"], cfg["n_head"], cfg["head_dim"]
+    W = {k: torch.tensor(v, requires_grad=True) for k, v in P.items()}
+    B, T = idx.shape
+    idx_t, tg_t = torch.tensor(idx), torch.tensor(tg)
+    pos = torch.arange(T, dtype=torch.float64)
+    inv = cfg["rope_theta"] ** (-torch.arange(0, D, 2, dtype=torch.float64) / D)
+    ang = pos[:, None] * inv[None]
+    cs, sn = torch.cos(ang)[None, None], torch.sin(ang)[None, None]
+
+    def rot(x):   # x [B, h, T, D]
+        a, b = x[..., :D // 2], x[..., D // 2:]
+        return torch.cat([a * cs - b * sn, a * sn + b * cs], -1)
+
+    def norm(x):
+        return F.rms_norm(x, (x.shape[-1],), eps=eps)
+
+    x = norm(W["wte"][idx_t])
+    for l in range(cfg["n_layer"]):
+        qkv = norm(x) @ W[f"h{l}.w_qkv"].T
+        q = qkv[..., :H * D].view(B, T, H, D).transpose(1, 2)
+        k = qkv[..., H * D:(H + 1) * D].view(B, T, 1, D).transpose(1, 2)
+        v = qkv[..., (H + 1) * D:].view(B, T, 1, D).transpose(1, 2)
+        q, k = norm(rot(q)), norm(rot(k))
+        y = F.scaled_dot_product_attention(q, k, v, is_causal=True, enable_gqa=True)
+        x = x + y.transpose(1, 2).reshape(B, T, H * D) @ W[f"h{l}.w_o"].T
+        x = x + F.relu(norm(x) @ W[f"h{l}.w_1"].T).square() @ W[f"h{l}.w_2"].T
+    logits = norm(x) @ W["lm_head"].T
+    logits = c * torch.tanh(logits / c)
+    loss = F.cross_entropy(logits.view(B * T, -1), tg_t.view(-1))
+    loss.backward()
+    return loss.item(), {k: v.grad.numpy() for k, v in W.items()}
+
+
+@pytest.mark.parametrize("H", [1, 3])
+def test_whole_step_matches_torch_autograd_float64(H):
+    pytest.importorskip("torch")
+    cfg = tiny_cfg(n_layer=2, n_head=H, model_dim=128 * H, mlp_dim=512 * H, vocab_size=96)
+    P = rand_params(cfg, seed=17, std=0.05)
+    rng = np.random.default_rng(18)
+    idx = rng.integers(0, 96, (2, 21))
+    tg = rng.integers(0, 96, (2, 21))
+    loss, _, G = O.step(cfg, P, idx, tg)
+    tl, TG = _torch_step(cfg, P, idx, tg)
+    assert loss == pytest.approx(tl, rel=1e-13)
+    for k in G:
+        np.testing.assert_allclose(G[k], TG[k], rtol=1e-9, atol=1e-13, err_msg=k)
+
+
+def test_causality_and_row_independence():
+    cfg = tiny_cfg(n_layer=1, vocab_size=128)
+    P = rand_params(cfg, seed=19, std=0.1)
+    rng = np.random.default_rng(20)
+    idx = rng.integers(0, 128, (3, 12))
+    tg = rng.integers(0, 128, (3, 12))
+    _, rows, _ = O.forward(cfg, P, idx, tg)
+    idx2 = idx.copy()
+    idx2[1, 7] = (idx2[1, 7] + 5) % 128
+    _, rows2, _ = O.forward(cfg, P, idx2, tg)
+    np.testing.assert_array_equal(rows2[1, :7], rows[1, :7])
+    np.testing.assert_array_equal(rows2[0], rows[0])
+    assert not np.array_equal(rows2[1, 7:], rows[1, 7:])
+    perm = [2, 0, 1]
+    _, rows3, _ = O.forward(cfg, P, idx[perm], tg[perm])
+    np.testing.assert_allclose(rows3, rows[perm], rtol=1e-14)
