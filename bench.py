@@ -1,0 +1,213 @@
+"""Training-step throughput of the HIP library on one MI355X.
+
+A step is gpt_forward_loss(need_grad=1) + gpt_backward on one stream, over one
+synthetic batch already resident in HBM: the whole forward and backward pass
+of nanochat's GPT (no optimiser, no data loading). Default workload: d20
+(depth 20, width 1280, 10 query heads / 1 K/V head, MLP 5120, vocab 65,536),
+batch 32 x 2048 Zipf(1.1) tokens, bf16 weights/activations with fp32
+accumulation and fp32 gradients.
+
+Prints one JSON line: tokens/s, bf16 MFU, the roofline of the kernel with the
+largest share of step time (timed with HIP events on the library's stream
+inside the timed region) and the float64 oracle's throughput on a bounded
+sample on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CUs x 4096 FLOP/clk x 2.4 GHz ("2.5 PFLOP/s")
+PEAK_FP32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+METRIC = "train tokens/sec + bf16 MFU, d20 fwd+bwd, seq 2048, 1 MI355X"
+
+
+def step_flops(cfg, T: int) -> dict:
+    """Algorithmic FLOPs per token (fwd+bwd): 6 x matmul weights + causal attention
+    over the T(T+1)/2 needed pairs; the embedding gather counts zero."""
+    C, H, D, F, V, L = cfg.model_dim, cfg.n_head, 128, cfg.mlp_dim, cfg.vocab_size, cfg.n_layer
+    n_mm = L * ((H + 2) * D * C + C * H * D + 2 * F * C) + V * C
+    return {"total": 6.0 * n_mm + 6.0 * L * H * D * (T + 1),
+            "palm": 6.0 * n_mm + 12.0 * L * H * D * T}
+
+
+def kernel_flops_per_launch(tag: str, cfg, B: int, T: int) -> float | None:
+    """Algorithmic FLOPs of one launch of a GEMM / attention call site."""
+    N, C, H, F, V, D = B * T, cfg.model_dim, cfg.n_head, cfg.mlp_dim, cfg.vocab_size, 128
+    QKV, HD = (H + 2) * D, H * D
+    g = {"gemm_qkv": (N, QKV, C), "gemm_o": (N, C, HD), "gemm_w1_relu2": (N, F, C), "gemm_w2": (N, C, F),
+         "gemm_lm_head_softcap": (N, V, C), "gemm_lm_head_dw": (V, C, N), "gemm_lm_head_dx": (N, C, V),
+         "gemm_w2_dw": (C, F, N), "gemm_w2_dx": (N, F, C), "gemm_w1_dw": (F, C, N), "gemm_w1_dx_relu2bwd": (N, C, F),
+         "gemm_o_dw": (C, HD, N), "gemm_o_dx": (N, HD, C), "gemm_qkv_dw": (QKV, C, N), "gemm_qkv_dx": (N, C, QKV)}
+    if tag in g:
+        m, n, k = g[tag]
+        return 2.0 * m * n * k
+    pairs = B * H * T * (T + 1) / 2.0
+    if tag == "attn_fwd":
+        return 4.0 * D * pairs
+    if tag == "attn_bwd":
+        return 8.0 * D * pairs
+    return None
+
+
+def kernel_bytes_per_launch(tag: str, cfg, B: int, T: int, es: int) -> float | None:
+    """Algorithmic HBM bytes of one launch of a memory-bound kernel."""
+    N, C, H, V = B * T, cfg.model_dim, cfg.n_head, cfg.vocab_size
+    b = {"embed_rmsnorm": N * (4 + 2 * C * es + 4), "rmsnorm": N * (2 * C * es + 4),
+         "rope_qknorm": N * (2 * (H + 1) * 128 * es + 4 * (H + 1)),
+         "ce_bwd": N * (2 * V * es + 8), "rmsnorm_bwd": N * (2 * C * es + 8 * C + C * es + 4),
+         "rope_qknorm_bwd": N * (3 * (H + 1) * 128 * es + 4 * (H + 1))}
+    return b.get(tag)
+
+
+def cpu_baseline(cfg_lib, seconds_hint: float = 20.0) -> dict:
+    """The float64 oracle, as it stands, on a bounded sample of the workload."""
+    import numpy as np
+
+    from decoder_only_transformer_gpt_amd import _lib, synthetic
+    from oracle import gpt_oracle as O
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    B, T = 1, 1024
+    shapes = [(n, r, c) for n, _, r, c in _lib.gpt_param_layout(cfg_lib)]
+    _, vals = synthetic.make_weights(shapes, seed=0, dtype="bf16")
+    idx, tgt = synthetic.make_tokens(B, T, cfg_lib.vocab_size, "zipf", seed=1)
+    P, off = {}, 0
+    for n, r, c in shapes:
+        P[n] = vals[off:off + r * c].reshape(r, c).astype(np.float64)
+        off += r * c
+    oc = cfg_lib.as_dict()
+    oc["norm_eps"] = float(np.float32(oc["norm_eps"]))
+    t0 = time.perf_counter()
+    O.step(oc, P, idx, tgt)
+    dt = time.perf_counter() - t0
+    return {"value": round(B * T / dt, 2), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"float64 NumPy oracle, one fwd+bwd of the same model on 1 x {T} Zipf tokens "
+                      f"({dt:.1f} s, {len(os.sched_getaffinity(0))} host cores visible)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="d20", choices=["tiny", "d4", "d12", "d20"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernel-table", action="store_true", help="print per-tag timings to stderr")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from decoder_only_transformer_gpt_amd import _lib, synthetic
+    from decoder_only_transformer_gpt_amd.model import GPT
+    from decoder_only_transformer_gpt_amd.workloads import WORKLOADS
+
+    wl = WORKLOADS[args.workload]
+    cfg = wl.config()
+    B, T = wl.batch, wl.seq_len
+    torch.cuda.set_device(0)
+    shapes = [(n, r, c) for n, _, r, c in _lib.gpt_param_layout(cfg)]
+    storage, _ = synthetic.make_weights(shapes, seed=0, dtype=wl.dtype)
+    idx_np, tgt_np = synthetic.make_tokens(B, T, cfg.vocab_size, wl.tokens, seed=1)
+    m = GPT(cfg, GPT.params_from_numpy(storage, cfg), B, T)
+    idx = torch.from_numpy(idx_np).cuda()
+    tgt = torch.from_numpy(tgt_np).cuda()
+    print(f"[bench] workload {wl.name}: B={B} T={T} params={_lib.gpt_param_count(cfg)} "
+          f"workspace={m.ws_bytes / 2**30:.1f} GiB", file=sys.stderr, flush=True)
+
+    def step():
+        m.forward_loss(idx, tgt, need_grad=True)
+        m.backward(1.0, accumulate=False)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if m.sync_status() != _lib.GPT_OK:
+        raise RuntimeError("device flag raised during warmup")
+
+    # one profiled step (every launch timed) to find the kernel with the largest share of time
+    tags = _lib.gpt_kernel_tag_names()
+    per_tag = {}
+    for t_i, t in enumerate(tags):
+        _lib.gpt_profile_begin(m.h, t_i)
+        step()
+        ms, n = _lib.gpt_profile_end(m.h)
+        if n:
+            per_tag[t] = (ms, n)
+    dominant = max(per_tag, key=lambda t: per_tag[t][0])
+    if args.kernel_table:
+        tot = sum(v[0] for v in per_tag.values())
+        for t, (ms, n) in sorted(per_tag.items(), key=lambda kv: -kv[1][0]):
+            f = kernel_flops_per_launch(t, cfg, B, T)
+            rate = f"{f * n / ms / 1e9:8.1f} TFLOP/s" if f else ""
+            print(f"[bench] {t:24s} {ms:9.3f} ms {n:4d} launches {100 * ms / tot:5.1f}% {rate}",
+                  file=sys.stderr, flush=True)
+
+    # timed region: K steps, the dominant kernel's launches timed with HIP events on its stream
+    dom_tag = tags.index(dominant)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    _lib.gpt_profile_begin(m.h, dom_tag)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    dom_ms, dom_n = _lib.gpt_profile_end(m.h)
+    if m.sync_status() != _lib.GPT_OK:
+        raise RuntimeError("device flag raised")
+    loss = float(m.loss.item())
+
+    elapsed = t1 - t0
+    tokens = B * T * args.steps
+    tok_s = tokens / elapsed
+    fl = step_flops(cfg, T)
+    mfu = fl["total"] * tok_s / (PEAK_BF16_TFLOPS * 1e12)
+    avg_ms = dom_ms / max(dom_n, 1)
+    es = 2 if wl.dtype == "bf16" else 4
+    kf = kernel_flops_per_launch(dominant, cfg, B, T)
+    if kf is not None:
+        peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP32_TFLOPS
+        achieved = kf / (avg_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": None}
+    else:
+        kb = kernel_bytes_per_launch(dominant, cfg, B, T, es) or 0.0
+        achieved = kb / (avg_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
+    roof.update({"kernel": dominant, "launches": dom_n, "avg_ms": round(avg_ms, 4)})
+
+    out = {
+        "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(1e3 * elapsed / args.steps, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
+        "config": {"workload": f"{wl.name}: depth {cfg.n_layer}, width {cfg.model_dim}, {cfg.n_head} query heads / "
+                               f"1 kv head, head_dim 128, MLP {cfg.mlp_dim}, vocab {cfg.vocab_size}",
+                   "global_batch": B, "seq_len": T, "tokens": wl.tokens, "parallelism": "single GPU"},
+        "mfu_bf16": round(mfu, 4), "mfu_palm_convention": round(fl["palm"] * tok_s / (PEAK_BF16_TFLOPS * 1e12), 4),
+        "loss": round(loss, 5), "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

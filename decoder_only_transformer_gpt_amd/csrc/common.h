@@ -1,0 +1,125 @@
+// Device-side helpers shared by the gfx950 kernels: storage types, 16-byte
+// vector loads/stores, MFMA wrappers. Written for CDNA4 (wave64) only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define DEV __device__ __forceinline__
+
+constexpr int WAVE = 64;
+
+// ----------------------------------------------------------------- scalars --
+
+DEV float to_f32(float x) { return x; }
+DEV float to_f32(bf16 x) { return (float)x; }
+template <typename T> DEV T from_f32(float x);
+template <> DEV float from_f32<float>(float x) { return x; }
+template <> DEV bf16 from_f32<bf16>(float x) { return (bf16)x; }  // RNE (v_cvt_pk_bf16_f32)
+
+// ------------------------------------------------------ 16-byte vector I/O --
+
+DEV u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+DEV void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+DEV u32x2 ld8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }
+DEV void st8(void* p, u32x2 v) { *reinterpret_cast<u32x2*>(p) = v; }
+
+// Elements of T per 16 bytes.
+template <typename T> struct Vec;
+template <> struct Vec<bf16> { static constexpr int N = 8; };
+template <> struct Vec<float> { static constexpr int N = 4; };
+
+// Load / store 8 consecutive elements as fp32.
+DEV void load8(const bf16* p, float (&v)[8]) {
+  u32x4 r = ld16(p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(r[i] << 16);
+    v[2 * i + 1] = __uint_as_float(r[i] & 0xffff0000u);
+  }
+}
+DEV void load8(const float* p, float (&v)[8]) {
+  u32x4 a = ld16(p), b = ld16(p + 4);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { v[i] = __uint_as_float(a[i]); v[4 + i] = __uint_as_float(b[i]); }
+}
+DEV uint32_t pack_bf16x2(float lo, float hi) {
+  bf16 a = (bf16)lo, b = (bf16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+DEV void store8(bf16* p, const float (&v)[8]) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
+  st16(p, r);
+}
+DEV void store8(float* p, const float (&v)[8]) {
+  u32x4 a, b;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { a[i] = __float_as_uint(v[i]); b[i] = __float_as_uint(v[4 + i]); }
+  st16(p, a);
+  st16(p + 4, b);
+}
+// 4 consecutive elements.
+DEV void load4(const bf16* p, float (&v)[4]) {
+  u32x2 r = ld8(p);
+  v[0] = __uint_as_float(r[0] << 16); v[1] = __uint_as_float(r[0] & 0xffff0000u);
+  v[2] = __uint_as_float(r[1] << 16); v[3] = __uint_as_float(r[1] & 0xffff0000u);
+}
+DEV void load4(const float* p, float (&v)[4]) {
+  u32x4 r = ld16(p);
+  for (int i = 0; i < 4; ++i) v[i] = __uint_as_float(r[i]);
+}
+DEV void store4(bf16* p, const float (&v)[4]) {
+  u32x2 r; r[0] = pack_bf16x2(v[0], v[1]); r[1] = pack_bf16x2(v[2], v[3]);
+  st8(p, r);
+}
+DEV void store4(float* p, const float (&v)[4]) {
+  u32x4 r; for (int i = 0; i < 4; ++i) r[i] = __float_as_uint(v[i]);
+  st16(p, r);
+}
+
+// ---------------------------------------------------------- reductions -----
+
+DEV float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+DEV float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// ------------------------------------------------------------- MFMA -------
+// Lane layout (checked on gfx950): for the 32x32 shapes, lane l feeds row
+// (l % 32) of the A operand and column (l % 32) of the B operand with the
+// k-slice owned by lane group g = l / 32; the 16 accumulator values of lane l
+// are C[blk*8 + g*4 + r][l % 32] at index blk*4 + r. Any fixed assignment of
+// k values to (g, element) works as long as A and B use the same one.
+
+// One 16-byte fragment per operand per lane: bf16 -> one 32x32x16 MFMA;
+// fp32 -> four 32x32x2 MFMAs (one element each), i.e. 8 k per fragment pair.
+DEV f32x16 mfma16(u32x4 a, u32x4 b, f32x16 c, bf16*) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+DEV f32x16 mfma16(u32x4 a, u32x4 b, f32x16 c, float*) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a[j]), __uint_as_float(b[j]), c, 0, 0, 0);
+  return c;
+}
+
+// -------------------------------------------------------- device flag ------
+// Bit 0: a token id outside [0, V). Set with a plain vector store (no atomics
+// needed: every writer stores the same bit pattern).
+enum { FLAG_BAD_TOKEN = 1 };

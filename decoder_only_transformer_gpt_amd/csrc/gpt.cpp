@@ -1,0 +1,658 @@
+// Host side of the library: configuration, parameter layout, workspace
+// planning and the forward/backward schedule of one pretraining step.
+//
+// Step structure (aethryn.com "Nanochat: full-stack LLM training in 8,000 lines
+// for $72", section "A Llama-class transformer with ten modern departures";
+// atlas.blal.pro "nanochat — full-stack ChatGPT in ~8k lines", section
+// "How it works", item 0): x = rmsnorm(wte[idx]); per layer
+// x += W_o attn(rope_qknorm(W_qkv rmsnorm(x))), x += W_2 relu(W_1 rmsnorm(x))^2;
+// logits = softcap(W_lm rmsnorm(x)); loss = mean cross-entropy.
+//
+// The library owns no device memory: the caller hands in parameters,
+// gradients and one workspace, which is carved up here.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/gpt.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+gpt_status fail(gpt_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+#define HIP_TRY(expr)                                                                    \
+  do {                                                                                   \
+    hipError_t e_ = (expr);                                                              \
+    if (e_ != hipSuccess)                                                                \
+      return fail(GPT_E_HIP, "%s failed: %s (%s:%d)", #expr, hipGetErrorString(e_), __FILE__, __LINE__); \
+  } while (0)
+
+constexpr int kHeadDim = 128;
+
+// Kernel tags (measurement). Order fixes the tag numbers.
+enum Tag : int {
+  K_EMBED = 0, K_RMSNORM, K_GEMM_QKV, K_ROPE_QKNORM, K_ATTN_FWD, K_GEMM_O, K_GEMM_W1, K_GEMM_W2, K_GEMM_LM,
+  K_CE_LOSS, K_CE_BWD, K_GEMM_LM_DW, K_GEMM_LM_DX, K_RMSNORM_BWD, K_GEMM_W2_DW, K_GEMM_W2_DX, K_GEMM_W1_DW,
+  K_GEMM_W1_DX, K_GEMM_O_DW, K_GEMM_O_DX, K_ATTN_BWD, K_ROPE_QKNORM_BWD, K_GEMM_QKV_DW, K_GEMM_QKV_DX,
+  K_EMBED_BWD, K_NUM_TAGS
+};
+const char* kTagNames[K_NUM_TAGS] = {
+  "embed_rmsnorm", "rmsnorm", "gemm_qkv", "rope_qknorm", "attn_fwd", "gemm_o", "gemm_w1_relu2", "gemm_w2",
+  "gemm_lm_head_softcap", "ce_loss", "ce_bwd", "gemm_lm_head_dw", "gemm_lm_head_dx", "rmsnorm_bwd", "gemm_w2_dw",
+  "gemm_w2_dx", "gemm_w1_dw", "gemm_w1_dx_relu2bwd", "gemm_o_dw", "gemm_o_dx", "attn_bwd", "rope_qknorm_bwd",
+  "gemm_qkv_dw", "gemm_qkv_dx", "embed_bwd"};
+
+struct Layout {  // byte offsets inside the workspace
+  size_t flag, loss_rows, rope_cos, rope_sin;
+  size_t x, rstd0, hf, rstdf, logits, part, ztgt, lse_ce;
+  std::vector<size_t> h1, rstd1, qkv, rstd_qk, o, lse, h2, rstd2, u, a;
+  size_t dres, dres_lp, dh, du, dqkv, dout, delta, split;
+  size_t keys_a, vals_a, keys_b, vals_b, hist, coef, carry;
+  size_t total;
+  size_t split_elems;
+};
+
+size_t esize(int dtype) { return dtype == GPT_BF16 ? 2 : 4; }
+
+struct Planner {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    size_t o = off;
+    off += (bytes + 255) & ~size_t(255);
+    return o;
+  }
+};
+
+// Split-K slices for a dW GEMM [M, N] reduced over K tokens: enough blocks
+// to cover the 256 CUs about twice, at least 1024 k per slice.
+int dw_splits(int M, int N, int K) {
+  const int64_t tiles = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
+  int s = (int)std::max<int64_t>(1, (512 + tiles - 1) / tiles);
+  s = std::min(s, std::max(1, K / 1024));
+  return std::min(s, 32);
+}
+
+Layout plan(const gpt_config& c, int maxB, int maxT) {
+  Layout L{};
+  Planner p;
+  const size_t N = (size_t)maxB * maxT, C = c.model_dim, H = c.n_head, F = c.mlp_dim, V = c.vocab_size;
+  const size_t es = esize(c.dtype);
+  const size_t QKV = (H + 2) * kHeadDim;
+  L.flag = p.take(256);
+  L.loss_rows = p.take(N * 4);
+  L.rope_cos = p.take((size_t)maxT * 64 * 4);
+  L.rope_sin = p.take((size_t)maxT * 64 * 4);
+  L.x = p.take(N * C * es);
+  L.rstd0 = p.take(N * 4);
+  for (int l = 0; l < c.n_layer; ++l) {
+    L.h1.push_back(p.take(N * C * es));
+    L.rstd1.push_back(p.take(N * 4));
+    L.qkv.push_back(p.take(N * QKV * es));
+    L.rstd_qk.push_back(p.take(N * (H + 1) * 4));
+    L.o.push_back(p.take(N * H * kHeadDim * es));
+    L.lse.push_back(p.take(N * H * 4));
+    L.h2.push_back(p.take(N * C * es));
+    L.rstd2.push_back(p.take(N * 4));
+    L.u.push_back(p.take(N * F * es));
+    L.a.push_back(p.take(N * F * es));
+  }
+  L.hf = p.take(N * C * es);
+  L.rstdf = p.take(N * 4);
+  L.logits = p.take(N * V * es);
+  L.part = p.take(N * (V / gk::kLMHeadPartCols) * 4);
+  L.ztgt = p.take(N * 4);
+  L.lse_ce = p.take(N * 4);
+  L.dres = p.take(N * C * 4);
+  L.dres_lp = p.take(N * C * es);
+  L.dh = p.take(N * C * es);
+  L.du = p.take(N * F * es);
+  L.dqkv = p.take(N * QKV * es);
+  L.dout = p.take(N * H * kHeadDim * es);
+  L.delta = p.take(N * H * 4);
+  // split-K partial buffer: largest splits*M*N over the per-layer dW GEMMs
+  size_t se = 0;
+  const int K = (int)N;
+  auto upd = [&](int M, int Nn) {
+    int s = dw_splits(M, Nn, K);
+    if (s > 1) se = std::max(se, (size_t)s * M * Nn);
+  };
+  upd((int)QKV, (int)C);
+  upd((int)C, (int)(H * kHeadDim));
+  upd((int)F, (int)C);
+  upd((int)C, (int)F);
+  upd((int)V, (int)C);
+  L.split_elems = se;
+  L.split = p.take(se * 4);
+  L.keys_a = p.take(N * 4);
+  L.vals_a = p.take(N * 4);
+  L.keys_b = p.take(N * 4);
+  L.vals_b = p.take(N * 4);
+  L.hist = p.take(gk::embed_bwd_hist_elems((int)N) * 4);
+  L.coef = p.take(N * 4);
+  L.carry = p.take(gk::embed_bwd_carry_elems((int)N, (int)C) * 4);
+  L.total = p.off;
+  return L;
+}
+
+// Layout checks that do not depend on kernel support.
+gpt_status check_shape(const gpt_config* c) {
+  if (!c) return fail(GPT_E_INVALID_ARG, "config is NULL");
+  if (c->n_layer < 1 || c->model_dim < 1 || c->n_head < 1 || c->n_kv_head < 1 || c->head_dim < 1 ||
+      c->mlp_dim < 1 || c->vocab_size < 1 || c->max_seq_len < 1)
+    return fail(GPT_E_INVALID_ARG, "config sizes must be positive");
+  return GPT_OK;
+}
+
+struct Profiler {
+  bool armed = false;
+  int tag = -1;
+  std::vector<hipEvent_t> ev;  // pairs
+  size_t used = 0;             // pairs used
+  static constexpr size_t kCap = 65536;
+};
+
+}  // namespace
+
+struct gpt_model {
+  gpt_config cfg;
+  const void* params;
+  float* grads;
+  char* ws;
+  size_t ws_bytes;
+  int maxB, maxT;
+  Layout L;
+  // parameter offsets (elements)
+  int64_t off_wte, off_lm;
+  std::vector<int64_t> off_qkv, off_o, off_w1, off_w2;
+  // state of the last forward
+  bool pending = false;
+  int B = 0, T = 0;
+  const int32_t* idx = nullptr;
+  const int32_t* targets = nullptr;
+  Profiler prof;
+};
+
+namespace {
+
+template <typename P>
+P* wsp(gpt_model* m, size_t off) { return reinterpret_cast<P*>(m->ws + off); }
+
+const char* pbase(gpt_model* m, int64_t elem_off) {
+  return reinterpret_cast<const char*>(m->params) + elem_off * (int64_t)esize(m->cfg.dtype);
+}
+
+// Runs `fn` (which enqueues kernels and returns hipError_t) under the given tag.
+template <typename Fn>
+gpt_status run(gpt_model* m, int tag, hipStream_t s, Fn&& fn) {
+  Profiler& P = m->prof;
+  const bool timed = P.armed && (P.tag < 0 || P.tag == tag) && P.used < Profiler::kCap;
+  if (timed) {
+    if (P.ev.size() < 2 * (P.used + 1)) {
+      hipEvent_t a, b;
+      HIP_TRY(hipEventCreate(&a));
+      HIP_TRY(hipEventCreate(&b));
+      P.ev.push_back(a);
+      P.ev.push_back(b);
+    }
+    HIP_TRY(hipEventRecord(P.ev[2 * P.used], s));
+  }
+  hipError_t e = fn();
+  if (e != hipSuccess) return fail(GPT_E_HIP, "launch of %s failed: %s", kTagNames[tag], hipGetErrorString(e));
+  if (timed) {
+    HIP_TRY(hipEventRecord(P.ev[2 * P.used + 1], s));
+    P.used++;
+  }
+  return GPT_OK;
+}
+
+#define RUN(tag, body)                                                       \
+  do {                                                                       \
+    gpt_status st_ = run(m, tag, stream, [&]() -> hipError_t { body });      \
+    if (st_ != GPT_OK) return st_;                                           \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* gpt_status_string(gpt_status s) {
+  switch (s) {
+    case GPT_OK: return "GPT_OK";
+    case GPT_E_INVALID_ARG: return "GPT_E_INVALID_ARG";
+    case GPT_E_UNSUPPORTED: return "GPT_E_UNSUPPORTED";
+    case GPT_E_WORKSPACE: return "GPT_E_WORKSPACE";
+    case GPT_E_STATE: return "GPT_E_STATE";
+    case GPT_E_HIP: return "GPT_E_HIP";
+    case GPT_E_DEVICE: return "GPT_E_DEVICE";
+    default: return "GPT_E_UNKNOWN";
+  }
+}
+
+const char* gpt_last_error_message(void) { return g_last_error.c_str(); }
+
+gpt_status gpt_config_from_depth(int32_t depth, int32_t dtype, gpt_config* out) {
+  if (!out) return fail(GPT_E_INVALID_ARG, "out is NULL");
+  if (depth < 2) return fail(GPT_E_INVALID_ARG, "depth must be >= 2 (width 64*depth holds 128-wide heads)");
+  if (dtype != GPT_F32 && dtype != GPT_BF16) return fail(GPT_E_INVALID_ARG, "dtype must be GPT_F32 or GPT_BF16");
+  gpt_config c;
+  c.n_layer = depth;
+  c.model_dim = 64 * depth;
+  c.n_head = c.model_dim / kHeadDim;
+  c.n_kv_head = 1;
+  c.head_dim = kHeadDim;
+  c.mlp_dim = 4 * c.model_dim;
+  c.vocab_size = 65536;
+  c.max_seq_len = 2048;
+  c.rope_theta = 10000.f;
+  c.logit_softcap = 15.f;
+  c.norm_eps = 1.1920928955078125e-07f;  // 2^-23
+  c.dtype = dtype;
+  *out = c;
+  return GPT_OK;
+}
+
+gpt_status gpt_config_validate(const gpt_config* c) {
+  gpt_status s = check_shape(c);
+  if (s != GPT_OK) return s;
+  if (c->dtype != GPT_F32 && c->dtype != GPT_BF16) return fail(GPT_E_UNSUPPORTED, "dtype %d not supported", c->dtype);
+  if (c->n_kv_head != 1) return fail(GPT_E_UNSUPPORTED, "n_kv_head must be 1 (multi-query attention)");
+  if (c->head_dim != kHeadDim) return fail(GPT_E_UNSUPPORTED, "head_dim must be 128");
+  if (c->n_head * c->head_dim != c->model_dim)
+    return fail(GPT_E_UNSUPPORTED, "n_head * head_dim must equal model_dim");
+  if (c->model_dim % 128 != 0 || c->model_dim > 4096)
+    return fail(GPT_E_UNSUPPORTED, "model_dim must be a multiple of 128 and <= 4096");
+  if (c->mlp_dim % 128 != 0) return fail(GPT_E_UNSUPPORTED, "mlp_dim must be a multiple of 128");
+  if (c->vocab_size % 256 != 0 || c->vocab_size > 65536)
+    return fail(GPT_E_UNSUPPORTED, "vocab_size must be a multiple of 256 and <= 65536");
+  if (!(c->logit_softcap > 0.f) || !(c->norm_eps > 0.f) || !(c->rope_theta > 0.f))
+    return fail(GPT_E_INVALID_ARG, "rope_theta, logit_softcap and norm_eps must be positive");
+  return GPT_OK;
+}
+
+int64_t gpt_param_count(const gpt_config* c) {
+  if (check_shape(c) != GPT_OK) return -1;
+  const int64_t C = c->model_dim, H = c->n_head, Hkv = c->n_kv_head, D = c->head_dim, F = c->mlp_dim,
+                V = c->vocab_size;
+  const int64_t per_layer = (H + 2 * Hkv) * D * C + C * H * D + F * C + C * F;
+  return 2 * V * C + c->n_layer * per_layer;
+}
+
+gpt_status gpt_param_layout(const gpt_config* c, gpt_tensor_desc* out, int32_t* n) {
+  gpt_status s = check_shape(c);
+  if (s != GPT_OK) return s;
+  if (!n) return fail(GPT_E_INVALID_ARG, "n is NULL");
+  const int32_t count = 2 + 4 * c->n_layer;
+  if (!out) {
+    *n = count;
+    return GPT_OK;
+  }
+  if (*n < count) return fail(GPT_E_INVALID_ARG, "capacity %d < %d tensors", *n, count);
+  const int64_t C = c->model_dim, H = c->n_head, Hkv = c->n_kv_head, D = c->head_dim, F = c->mlp_dim,
+                V = c->vocab_size;
+  int64_t off = 0;
+  int k = 0;
+  auto add = [&](const char* name, int64_t r, int64_t cc) {
+    gpt_tensor_desc& d = out[k++];
+    memset(d.name, 0, sizeof(d.name));
+    snprintf(d.name, sizeof(d.name), "%s", name);
+    d.offset = off;
+    d.rows = r;
+    d.cols = cc;
+    off += r * cc;
+  };
+  add("wte", V, C);
+  char nm[32];
+  for (int l = 0; l < c->n_layer; ++l) {
+    snprintf(nm, sizeof(nm), "h%d.w_qkv", l); add(nm, (H + 2 * Hkv) * D, C);
+    snprintf(nm, sizeof(nm), "h%d.w_o", l); add(nm, C, H * D);
+    snprintf(nm, sizeof(nm), "h%d.w_1", l); add(nm, F, C);
+    snprintf(nm, sizeof(nm), "h%d.w_2", l); add(nm, C, F);
+  }
+  add("lm_head", V, C);
+  *n = count;
+  return GPT_OK;
+}
+
+gpt_status gpt_workspace_bytes(const gpt_config* c, int32_t max_B, int32_t max_T, size_t* bytes) {
+  gpt_status s = gpt_config_validate(c);
+  if (s != GPT_OK) return s;
+  if (!bytes) return fail(GPT_E_INVALID_ARG, "bytes is NULL");
+  if (max_B < 1 || max_T < 1 || max_T > c->max_seq_len)
+    return fail(GPT_E_INVALID_ARG, "need 1 <= max_B and 1 <= max_T <= max_seq_len");
+  if ((int64_t)max_B * max_T > (int64_t)1 << 24) return fail(GPT_E_INVALID_ARG, "max_B * max_T too large");
+  *bytes = plan(*c, max_B, max_T).total;
+  return GPT_OK;
+}
+
+gpt_status gpt_init(const gpt_config* cfg, const void* params, float* grads, void* workspace, size_t ws_bytes,
+                    int32_t max_B, int32_t max_T, void* stream_, gpt_model** out) {
+  if (!out) return fail(GPT_E_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  gpt_status s = gpt_config_validate(cfg);
+  if (s != GPT_OK) return s;
+  if (!params || !grads || !workspace) return fail(GPT_E_INVALID_ARG, "params, grads and workspace must be non-NULL");
+  if (((uintptr_t)workspace & 255) != 0) return fail(GPT_E_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (((uintptr_t)params & 15) != 0 || ((uintptr_t)grads & 15) != 0)
+    return fail(GPT_E_INVALID_ARG, "params and grads must be 16-byte aligned");
+  size_t need = 0;
+  s = gpt_workspace_bytes(cfg, max_B, max_T, &need);
+  if (s != GPT_OK) return s;
+  if (ws_bytes < need) return fail(GPT_E_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
+  hipStream_t stream = (hipStream_t)stream_;
+
+  gpt_model* m = new (std::nothrow) gpt_model();
+  if (!m) return fail(GPT_E_INVALID_ARG, "out of host memory");
+  m->cfg = *cfg;
+  m->params = params;
+  m->grads = grads;
+  m->ws = reinterpret_cast<char*>(workspace);
+  m->ws_bytes = ws_bytes;
+  m->maxB = max_B;
+  m->maxT = max_T;
+  m->L = plan(*cfg, max_B, max_T);
+  std::vector<gpt_tensor_desc> d(2 + 4 * cfg->n_layer);
+  int32_t n = (int32_t)d.size();
+  gpt_param_layout(cfg, d.data(), &n);
+  m->off_wte = d[0].offset;
+  for (int l = 0; l < cfg->n_layer; ++l) {
+    m->off_qkv.push_back(d[1 + 4 * l].offset);
+    m->off_o.push_back(d[2 + 4 * l].offset);
+    m->off_w1.push_back(d[3 + 4 * l].offset);
+    m->off_w2.push_back(d[4 + 4 * l].offset);
+  }
+  m->off_lm = d[n - 1].offset;
+
+  // RoPE tables: angle = t * theta^(-2i/D) in double precision, stored as fp32.
+  std::vector<float> ct((size_t)max_T * 64), st((size_t)max_T * 64);
+  for (int t = 0; t < max_T; ++t)
+    for (int i = 0; i < 64; ++i) {
+      const double ang = (double)t * std::pow((double)cfg->rope_theta, -2.0 * i / (double)kHeadDim);
+      ct[(size_t)t * 64 + i] = (float)std::cos(ang);
+      st[(size_t)t * 64 + i] = (float)std::sin(ang);
+    }
+  hipError_t e = hipMemcpyAsync(m->ws + m->L.rope_cos, ct.data(), ct.size() * 4, hipMemcpyHostToDevice, stream);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(m->ws + m->L.rope_sin, st.data(), st.size() * 4, hipMemcpyHostToDevice, stream);
+  if (e == hipSuccess) e = hipMemsetAsync(m->ws + m->L.flag, 0, 256, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);  // host tables go out of scope
+  if (e != hipSuccess) {
+    delete m;
+    return fail(GPT_E_HIP, "gpt_init upload failed: %s", hipGetErrorString(e));
+  }
+  *out = m;
+  return GPT_OK;
+}
+
+gpt_status gpt_forward_loss(gpt_model* m, const int32_t* idx, const int32_t* targets, int32_t B, int32_t T,
+                            int32_t need_grad, float* loss, float* row_loss, void* stream_) {
+  if (!m || !idx || !targets || !loss) return fail(GPT_E_INVALID_ARG, "NULL argument");
+  if (B < 1 || T < 1 || B > m->maxB || T > m->maxT)
+    return fail(GPT_E_INVALID_ARG, "B=%d T=%d outside [1, %d] x [1, %d]", B, T, m->maxB, m->maxT);
+  hipStream_t stream = (hipStream_t)stream_;
+  const gpt_config& c = m->cfg;
+  const int dt = c.dtype;
+  const int N = B * T, C = c.model_dim, H = c.n_head, F = c.mlp_dim, V = c.vocab_size;
+  const int QKV = (H + 2) * kHeadDim, HD = H * kHeadDim;
+  const Layout& L = m->L;
+  int* flag = wsp<int>(m, L.flag);
+  m->pending = false;
+
+  RUN(K_EMBED, return gk::launch_embed_rmsnorm(dt, pbase(m, m->off_wte), idx, N, C, V, c.norm_eps, m->ws + L.x,
+                                               wsp<float>(m, L.rstd0), flag, stream););
+  for (int l = 0; l < c.n_layer; ++l) {
+    RUN(K_RMSNORM, return gk::launch_rmsnorm(dt, m->ws + L.x, N, C, c.norm_eps, m->ws + L.h1[l],
+                                             wsp<float>(m, L.rstd1[l]), stream););
+    RUN(K_GEMM_QKV, {
+      gk::GemmArgs a;
+      a.A = m->ws + L.h1[l]; a.lda = C;
+      a.B = pbase(m, m->off_qkv[l]); a.ldb = C;
+      a.M = N; a.N = QKV; a.K = C;
+      a.C = m->ws + L.qkv[l]; a.ldc = QKV;
+      return gk::launch_gemm(dt, gk::Epi::Store, a, stream);
+    });
+    RUN(K_ROPE_QKNORM, return gk::launch_rope_qknorm(dt, m->ws + L.qkv[l], B, T, H, c.norm_eps,
+                                                     wsp<float>(m, L.rope_cos), wsp<float>(m, L.rope_sin),
+                                                     wsp<float>(m, L.rstd_qk[l]), stream););
+    RUN(K_ATTN_FWD, return gk::launch_attn_fwd(dt, m->ws + L.qkv[l], B, T, H, m->ws + L.o[l],
+                                               wsp<float>(m, L.lse[l]), stream););
+    RUN(K_GEMM_O, {
+      gk::GemmArgs a;
+      a.A = m->ws + L.o[l]; a.lda = HD;
+      a.B = pbase(m, m->off_o[l]); a.ldb = HD;
+      a.M = N; a.N = C; a.K = HD;
+      a.C = m->ws + L.x; a.ldc = C;
+      return gk::launch_gemm(dt, gk::Epi::Residual, a, stream);
+    });
+    RUN(K_RMSNORM, return gk::launch_rmsnorm(dt, m->ws + L.x, N, C, c.norm_eps, m->ws + L.h2[l],
+                                             wsp<float>(m, L.rstd2[l]), stream););
+    RUN(K_GEMM_W1, {
+      gk::GemmArgs a;
+      a.A = m->ws + L.h2[l]; a.lda = C;
+      a.B = pbase(m, m->off_w1[l]); a.ldb = C;
+      a.M = N; a.N = F; a.K = C;
+      a.C = m->ws + L.u[l]; a.ldc = F;
+      a.C2 = m->ws + L.a[l]; a.ldc2 = F;
+      return gk::launch_gemm(dt, gk::Epi::Relu2, a, stream);
+    });
+    RUN(K_GEMM_W2, {
+      gk::GemmArgs a;
+      a.A = m->ws + L.a[l]; a.lda = F;
+      a.B = pbase(m, m->off_w2[l]); a.ldb = F;
+      a.M = N; a.N = C; a.K = F;
+      a.C = m->ws + L.x; a.ldc = C;
+      return gk::launch_gemm(dt, gk::Epi::Residual, a, stream);
+    });
+  }
+  RUN(K_RMSNORM, return gk::launch_rmsnorm(dt, m->ws + L.x, N, C, c.norm_eps, m->ws + L.hf,
+                                           wsp<float>(m, L.rstdf), stream););
+  RUN(K_GEMM_LM, {
+    gk::GemmArgs a;
+    a.A = m->ws + L.hf; a.lda = C;
+    a.B = pbase(m, m->off_lm); a.ldb = C;
+    a.M = N; a.N = V; a.K = C;
+    a.C = m->ws + L.logits; a.ldc = V;
+    a.part = wsp<float>(m, L.part);
+    a.targets = targets;
+    a.ztgt = wsp<float>(m, L.ztgt);
+    a.softcap = c.logit_softcap;
+    return gk::launch_gemm(dt, gk::Epi::LMHead, a, stream);
+  });
+  RUN(K_CE_LOSS, return gk::launch_ce_loss(wsp<float>(m, L.part), V / gk::kLMHeadPartCols, wsp<float>(m, L.ztgt),
+                                           targets, N, V, c.logit_softcap, wsp<float>(m, L.lse_ce),
+                                           wsp<float>(m, L.loss_rows), row_loss, loss, flag, stream););
+  m->B = B;
+  m->T = T;
+  m->idx = idx;
+  m->targets = targets;
+  m->pending = need_grad != 0;
+  return GPT_OK;
+}
+
+gpt_status gpt_backward(gpt_model* m, float dloss, int32_t accumulate, void* stream_) {
+  if (!m) return fail(GPT_E_INVALID_ARG, "NULL model");
+  if (!m->pending) return fail(GPT_E_STATE, "gpt_backward needs a preceding gpt_forward_loss with need_grad = 1");
+  hipStream_t stream = (hipStream_t)stream_;
+  const gpt_config& c = m->cfg;
+  const int dt = c.dtype;
+  const int B = m->B, T = m->T, N = B * T, C = c.model_dim, H = c.n_head, F = c.mlp_dim, V = c.vocab_size;
+  const int QKV = (H + 2) * kHeadDim, HD = H * kHeadDim;
+  const Layout& L = m->L;
+  float* G = m->grads;
+  const int acc = accumulate ? 1 : 0;
+  m->pending = false;
+
+  auto dw = [&](int tag, const void* dy, int ldy, const void* x, int ldx, int M, int Nn, int64_t goff) -> gpt_status {
+    RUN(tag, {
+      gk::GemmArgs a;
+      a.A = dy; a.lda = ldy; a.a_kcontig = false;
+      a.B = x; a.ldb = ldx; a.b_kcontig = false;
+      a.M = M; a.N = Nn; a.K = N;
+      a.splits = dw_splits(M, Nn, N);
+      a.C = G + goff; a.ldc = Nn;
+      a.accumulate = acc;
+      a.split_buf = wsp<float>(m, L.split);
+      return gk::launch_gemm(dt, gk::Epi::GradF32, a, stream);
+    });
+    return GPT_OK;
+  };
+  auto dx = [&](int tag, gk::Epi epi, const void* dy, int ldy, const void* w, int ldw, int Nn, int K, void* out,
+                const void* aux) -> gpt_status {
+    RUN(tag, {
+      gk::GemmArgs a;
+      a.A = dy; a.lda = ldy;
+      a.B = w; a.ldb = ldw; a.b_kcontig = false;
+      a.M = N; a.N = Nn; a.K = K;
+      a.C = out; a.ldc = Nn;
+      a.C2 = const_cast<void*>(aux); a.ldc2 = Nn;
+      return gk::launch_gemm(dt, epi, a, stream);
+    });
+    return GPT_OK;
+  };
+#define TRY(x) do { gpt_status s_ = (x); if (s_ != GPT_OK) return s_; } while (0)
+
+  RUN(K_CE_BWD, return gk::launch_ce_bwd(dt, m->ws + L.logits, wsp<float>(m, L.lse_ce), m->targets, N, V,
+                                         c.logit_softcap, dloss / (float)N, stream););
+  TRY(dw(K_GEMM_LM_DW, m->ws + L.logits, V, m->ws + L.hf, C, V, C, m->off_lm));
+  TRY(dx(K_GEMM_LM_DX, gk::Epi::Store, m->ws + L.logits, V, pbase(m, m->off_lm), C, C, V, m->ws + L.dh, nullptr));
+  RUN(K_RMSNORM_BWD, return gk::launch_rmsnorm_bwd(dt, m->ws + L.dh, m->ws + L.hf, wsp<float>(m, L.rstdf), N, C, 0,
+                                                   wsp<float>(m, L.dres), m->ws + L.dres_lp, stream););
+  for (int l = c.n_layer - 1; l >= 0; --l) {
+    // MLP
+    TRY(dw(K_GEMM_W2_DW, m->ws + L.dres_lp, C, m->ws + L.a[l], F, C, F, m->off_w2[l]));
+    TRY(dx(K_GEMM_W2_DX, gk::Epi::Relu2Bwd, m->ws + L.dres_lp, C, pbase(m, m->off_w2[l]), F, F, C, m->ws + L.du,
+           m->ws + L.u[l]));
+    TRY(dw(K_GEMM_W1_DW, m->ws + L.du, F, m->ws + L.h2[l], C, F, C, m->off_w1[l]));
+    TRY(dx(K_GEMM_W1_DX, gk::Epi::Store, m->ws + L.du, F, pbase(m, m->off_w1[l]), C, C, F, m->ws + L.dh, nullptr));
+    RUN(K_RMSNORM_BWD, return gk::launch_rmsnorm_bwd(dt, m->ws + L.dh, m->ws + L.h2[l], wsp<float>(m, L.rstd2[l]),
+                                                     N, C, 1, wsp<float>(m, L.dres), m->ws + L.dres_lp, stream););
+    // attention
+    TRY(dw(K_GEMM_O_DW, m->ws + L.dres_lp, C, m->ws + L.o[l], HD, C, HD, m->off_o[l]));
+    TRY(dx(K_GEMM_O_DX, gk::Epi::Store, m->ws + L.dres_lp, C, pbase(m, m->off_o[l]), HD, HD, C, m->ws + L.dout,
+           nullptr));
+    RUN(K_ATTN_BWD, return gk::launch_attn_bwd(dt, m->ws + L.qkv[l], m->ws + L.o[l], m->ws + L.dout,
+                                               wsp<float>(m, L.lse[l]), B, T, H, wsp<float>(m, L.delta),
+                                               m->ws + L.dqkv, stream););
+    RUN(K_ROPE_QKNORM_BWD, return gk::launch_rope_qknorm_bwd(dt, m->ws + L.dqkv, m->ws + L.qkv[l],
+                                                             wsp<float>(m, L.rstd_qk[l]), B, T, H,
+                                                             wsp<float>(m, L.rope_cos), wsp<float>(m, L.rope_sin),
+                                                             stream););
+    TRY(dw(K_GEMM_QKV_DW, m->ws + L.dqkv, QKV, m->ws + L.h1[l], C, QKV, C, m->off_qkv[l]));
+    TRY(dx(K_GEMM_QKV_DX, gk::Epi::Store, m->ws + L.dqkv, QKV, pbase(m, m->off_qkv[l]), C, C, QKV, m->ws + L.dh,
+           nullptr));
+    RUN(K_RMSNORM_BWD, return gk::launch_rmsnorm_bwd(dt, m->ws + L.dh, m->ws + L.h1[l], wsp<float>(m, L.rstd1[l]),
+                                                     N, C, 1, wsp<float>(m, L.dres), m->ws + L.dres_lp, stream););
+  }
+  RUN(K_EMBED_BWD, {
+    gk::EmbedBwdArgs a;
+    a.dtype = dt;
+    a.wte = pbase(m, m->off_wte);
+    a.idx = m->idx;
+    a.dres = wsp<float>(m, L.dres);
+    a.rstd0 = wsp<float>(m, L.rstd0);
+    a.N = N; a.C = C; a.V = V;
+    a.accumulate = acc;
+    a.dwte = G + m->off_wte;
+    a.keys_a = wsp<int32_t>(m, L.keys_a);
+    a.vals_a = wsp<int32_t>(m, L.vals_a);
+    a.keys_b = wsp<int32_t>(m, L.keys_b);
+    a.vals_b = wsp<int32_t>(m, L.vals_b);
+    a.hist = wsp<int32_t>(m, L.hist);
+    a.coef = wsp<float>(m, L.coef);
+    a.carry = wsp<float>(m, L.carry);
+    return gk::launch_embed_bwd(a, stream);
+  });
+#undef TRY
+  return GPT_OK;
+}
+
+gpt_status gpt_sync_status(gpt_model* m, void* stream_) {
+  if (!m) return fail(GPT_E_INVALID_ARG, "NULL model");
+  hipStream_t stream = (hipStream_t)stream_;
+  int flag = 0;
+  HIP_TRY(hipStreamSynchronize(stream));
+  HIP_TRY(hipMemcpy(&flag, m->ws + m->L.flag, sizeof(int), hipMemcpyDeviceToHost));
+  if (flag) return fail(GPT_E_DEVICE, "device flag 0x%x: token id outside [0, vocab_size)", flag);
+  return GPT_OK;
+}
+
+gpt_status gpt_destroy(gpt_model* m) {
+  if (!m) return GPT_OK;
+  for (hipEvent_t e : m->prof.ev) (void)hipEventDestroy(e);
+  delete m;
+  return GPT_OK;
+}
+
+gpt_status gpt_profile_begin(gpt_model* m, int32_t tag) {
+  if (!m) return fail(GPT_E_INVALID_ARG, "NULL model");
+  if (tag >= K_NUM_TAGS) return fail(GPT_E_INVALID_ARG, "unknown tag %d", tag);
+  m->prof.armed = true;
+  m->prof.tag = tag;
+  m->prof.used = 0;
+  return GPT_OK;
+}
+
+gpt_status gpt_profile_end(gpt_model* m, double* total_ms, int64_t* launches) {
+  if (!m || !total_ms || !launches) return fail(GPT_E_INVALID_ARG, "NULL argument");
+  Profiler& P = m->prof;
+  double tot = 0.0;
+  for (size_t i = 0; i < P.used; ++i) {
+    HIP_TRY(hipEventSynchronize(P.ev[2 * i + 1]));
+    float ms = 0.f;
+    HIP_TRY(hipEventElapsedTime(&ms, P.ev[2 * i], P.ev[2 * i + 1]));
+    tot += ms;
+  }
+  *total_ms = tot;
+  *launches = (int64_t)P.used;
+  P.armed = false;
+  P.used = 0;
+  return GPT_OK;
+}
+
+const char* gpt_kernel_tag_name(int32_t tag) {
+  if (tag < 0 || tag >= K_NUM_TAGS) return nullptr;
+  return kTagNames[tag];
+}
+
+gpt_status gpt_debug_buffer(gpt_model* m, const char* name, int32_t layer, void** ptr, size_t* bytes) {
+  if (!m || !name || !ptr || !bytes) return fail(GPT_E_INVALID_ARG, "NULL argument");
+  const gpt_config& c = m->cfg;
+  const Layout& L = m->L;
+  const size_t N = (size_t)m->B * m->T, es = esize(c.dtype), C = c.model_dim, H = c.n_head;
+  const bool lv = layer >= 0 && layer < c.n_layer;
+  auto set = [&](size_t off, size_t b) { *ptr = m->ws + off; *bytes = b; return GPT_OK; };
+  const std::string s(name);
+  if (s == "x") return set(L.x, N * C * es);
+  if (s == "hf") return set(L.hf, N * C * es);
+  if (s == "rstd0") return set(L.rstd0, N * 4);
+  if (s == "logits") return set(L.logits, N * (size_t)c.vocab_size * es);
+  if (!lv) return fail(GPT_E_INVALID_ARG, "unknown buffer '%s' or layer %d out of range", name, layer);
+  if (s == "h1") return set(L.h1[layer], N * C * es);
+  if (s == "qkv") return set(L.qkv[layer], N * (H + 2) * kHeadDim * es);
+  if (s == "o") return set(L.o[layer], N * H * kHeadDim * es);
+  if (s == "lse") return set(L.lse[layer], N * H * 4);
+  if (s == "h2") return set(L.h2[layer], N * C * es);
+  if (s == "u") return set(L.u[layer], N * (size_t)c.mlp_dim * es);
+  if (s == "a") return set(L.a[layer], N * (size_t)c.mlp_dim * es);
+  return fail(GPT_E_INVALID_ARG, "unknown buffer '%s'", name);
+}
+
+}  // extern "C"

@@ -1,0 +1,95 @@
+// Host-side launch interface of the gfx950 kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gk {
+
+enum class Epi : int {
+  Store = 0,     // C = acc (activation dtype)
+  Residual = 1,  // C += acc in place (the residual stream)
+  Relu2 = 2,     // C = acc (u), C2 = max(acc, 0)^2 (a)
+  LMHead = 3,    // C = c*tanh(acc/c) (logits), exp-sum partials, logit at target
+  Relu2Bwd = 4,  // C = acc * 2*max(u, 0) with u read from C2
+  GradF32 = 5,   // fp32 gradient: C = acc or C += acc; split-K writes partials
+};
+
+struct GemmArgs {
+  // C[m, n] = sum_k A(m, k) * B(n, k)
+  const void* A = nullptr;
+  int64_t lda = 0;
+  bool a_kcontig = true;  // A(m,k) at A[m*lda + k] if true, else A[k*lda + m]
+  const void* B = nullptr;
+  int64_t ldb = 0;
+  bool b_kcontig = true;  // B(n,k) at B[n*ldb + k] if true, else B[k*ldb + n]
+  int M = 0, N = 0, K = 0;
+  int splits = 1;          // split-K slices (GradF32 only)
+  void* C = nullptr;
+  int64_t ldc = 0;
+  void* C2 = nullptr;
+  int64_t ldc2 = 0;
+  // LMHead
+  float* part = nullptr;   // [M, N / 128] exp-sum partials
+  const int32_t* targets = nullptr;
+  float* ztgt = nullptr;   // [M] logit at the target, fp32
+  float softcap = 15.f;
+  // GradF32
+  int accumulate = 0;
+  float* split_buf = nullptr;  // [splits, M, N] partials when splits > 1
+};
+
+// dtype: 0 = fp32, 1 = bf16 (gpt.h GPT_F32 / GPT_BF16)
+hipError_t launch_gemm(int dtype, Epi epi, const GemmArgs& a, hipStream_t s);
+// Partial-column width of the LMHead epilogue (exp-sum partials per row).
+constexpr int kLMHeadPartCols = 128;
+
+// Row-wise kernels ---------------------------------------------------------
+hipError_t launch_embed_rmsnorm(int dtype, const void* wte, const int32_t* idx, int N, int C, int V,
+                                float eps, void* x, float* rstd, int* flag, hipStream_t s);
+hipError_t launch_rmsnorm(int dtype, const void* x, int N, int C, float eps, void* y, float* rstd,
+                          hipStream_t s);
+// dres = (accumulate ? dres : 0) + r * (dy - y * mean(dy*y)); dres_lp = dres in the activation dtype
+hipError_t launch_rmsnorm_bwd(int dtype, const void* dy, const void* y, const float* rstd, int N, int C,
+                              int accumulate, float* dres, void* dres_lp, hipStream_t s);
+hipError_t launch_rope_qknorm(int dtype, void* qkv, int B, int T, int H, float eps, const float* cos_t,
+                              const float* sin_t, float* rstd_qk, hipStream_t s);
+hipError_t launch_rope_qknorm_bwd(int dtype, void* dqkv, const void* qkv, const float* rstd_qk, int B,
+                                  int T, int H, const float* cos_t, const float* sin_t, hipStream_t s);
+
+// Attention (causal, multi-query, head_dim 128) ----------------------------
+hipError_t launch_attn_fwd(int dtype, const void* qkv, int B, int T, int H, void* o, float* lse,
+                           hipStream_t s);
+hipError_t launch_attn_bwd(int dtype, const void* qkv, const void* o, const void* dout, const float* lse,
+                           int B, int T, int H, float* delta, void* dqkv, hipStream_t s);
+
+// Cross-entropy -------------------------------------------------------------
+hipError_t launch_ce_loss(const float* part, int nparts, const float* ztgt, const int32_t* targets, int N,
+                          int V, float softcap, float* lse, float* row_loss, float* row_loss_out,
+                          float* loss, int* flag, hipStream_t s);
+hipError_t launch_ce_bwd(int dtype, void* logits, const float* lse, const int32_t* targets, int N, int V,
+                         float softcap, float scale, hipStream_t s);
+
+// Embedding backward ---------------------------------------------------------
+struct EmbedBwdArgs {
+  int dtype;
+  const void* wte;       // [V, C]
+  const int32_t* idx;    // [N]
+  const float* dres;     // [N, C] gradient w.r.t. x0 (the normalised embedding)
+  const float* rstd0;    // [N]
+  int N, C, V;
+  int accumulate;
+  float* dwte;           // [V, C] fp32
+  // scratch (inside the workspace)
+  int32_t* keys_a; int32_t* vals_a; int32_t* keys_b; int32_t* vals_b;  // [N] each
+  int32_t* hist;         // [256 * nchunks]
+  float* coef;           // [N]
+  float* carry;          // [2 * nseg_chunks * (C + 1)]
+};
+hipError_t launch_embed_bwd(const EmbedBwdArgs& a, hipStream_t s);
+size_t embed_bwd_hist_elems(int N);
+size_t embed_bwd_carry_elems(int N, int C);
+
+hipError_t launch_fill_f32(float* p, float v, int64_t n, hipStream_t s);
+
+}  // namespace gk

@@ -1,0 +1,175 @@
+/*
+ * gpt.h — C ABI of the MI355X (gfx950) library that runs one pretraining step
+ * (forward + backward) of nanochat's GPT.
+ *
+ * The model (page citations, by page title and section):
+ *   - Depth dial: width = 64 * depth, heads = width / 128, head dim 128
+ *     (aethryn.com "Nanochat: full-stack LLM training in 8,000 lines for $72",
+ *     section "One dial controls everything"; atlas.blal.pro "nanochat —
+ *     full-stack ChatGPT in ~8k lines", section "How it works", item 0).
+ *   - Token embedding, parameter-free RMSNorm after the embedding, before every
+ *     attention and MLP and before the head; RoPE with base 10,000 on q and k,
+ *     then QK-RMSNorm; relu^2 MLP 4x wide; untied LM head with logits squashed
+ *     to 15*tanh(z/15) in fp32 (aethryn.com, section "A Llama-class transformer
+ *     with ten modern departures"; energyai.berlin "nanochat vs GPT-OSS",
+ *     section "Architectural decisions").
+ *   - Multi-query attention: every query head shares one K/V head
+ *     (energyai.berlin, section "Architectural decisions", subsection MQA).
+ *   - Bias-free linears (atlas.blal.pro, section "How it works", item 0).
+ *   - bf16 compute with fp32 gradients; gradient accumulation on one GPU
+ *     (aimarketly.com "nanochat-train" README, sections "Precision / dtype" and
+ *     "Getting started").
+ *
+ * Conventions fixed where the pages are silent: RMSNorm eps = 2^-23 with no
+ * gain; attention scale 1/sqrt(head_dim); RoPE pairs element i with i + D/2
+ * and rotates by +t * theta^(-2i/D), positions restart at 0 in every batch
+ * row; QK-norm is per (token, head) over D; plain causal mask; the loss is the
+ * mean over all B*T positions.
+ *
+ * Memory ownership: the caller owns every device buffer (parameters,
+ * gradients, workspace, token ids, outputs). The library never allocates or
+ * frees device memory. The model handle is host memory owned by the library.
+ *
+ * Errors: every function returns a gpt_status; GPT_OK is 0, errors are
+ * negative. Nothing is thrown across the ABI. gpt_last_error_message() gives a
+ * thread-local detail string for the last failing call on that thread.
+ *
+ * Threading: a handle serves one stream at a time and is not re-entrant;
+ * distinct handles are independent.
+ *
+ * Streams are passed as `void*` holding a hipStream_t (NULL = default stream).
+ * All device work is enqueued asynchronously on that stream.
+ */
+#ifndef GPT_AMD_GPT_H
+#define GPT_AMD_GPT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t gpt_status;
+enum {
+  GPT_OK = 0,
+  GPT_E_INVALID_ARG = -1,  /* null pointer, non-positive size, B > max_B, T > max_T, ... */
+  GPT_E_UNSUPPORTED = -2,  /* config outside what the kernels implement (n_kv_head != 1, head_dim != 128, ...) */
+  GPT_E_WORKSPACE = -3,    /* workspace smaller than gpt_workspace_bytes() */
+  GPT_E_STATE = -4,        /* gpt_backward without a preceding gpt_forward_loss(need_grad = 1) */
+  GPT_E_HIP = -5,          /* a HIP runtime call failed (detail in gpt_last_error_message) */
+  GPT_E_DEVICE = -6        /* sticky device-side flag, e.g. a token id outside [0, vocab_size) */
+};
+
+/* Compute/storage dtype of parameters and activations. Gradients are always fp32. */
+enum { GPT_F32 = 0, GPT_BF16 = 1 };
+
+typedef struct gpt_config {
+  int32_t n_layer;      /* depth */
+  int32_t model_dim;    /* C = 64 * depth; multiple of 128 */
+  int32_t n_head;       /* H query heads, n_head * head_dim == model_dim */
+  int32_t n_kv_head;    /* must be 1 (multi-query attention) */
+  int32_t head_dim;     /* must be 128 */
+  int32_t mlp_dim;      /* F = 4 * C; multiple of 128 */
+  int32_t vocab_size;   /* V; multiple of 256 */
+  int32_t max_seq_len;  /* longest T the model accepts */
+  float rope_theta;     /* 10000 */
+  float logit_softcap;  /* 15 */
+  float norm_eps;       /* 2^-23 */
+  int32_t dtype;        /* GPT_F32 or GPT_BF16 */
+} gpt_config;
+
+/* One parameter tensor inside the flat parameter (and gradient) buffer. */
+typedef struct gpt_tensor_desc {
+  char name[32];   /* "wte", "h<l>.w_qkv", "h<l>.w_o", "h<l>.w_1", "h<l>.w_2", "lm_head" */
+  int64_t offset;  /* in elements from the start of the flat buffer */
+  int64_t rows;    /* row-major [rows, cols] */
+  int64_t cols;
+} gpt_tensor_desc;
+
+typedef struct gpt_model gpt_model;
+
+/* Static name of a status code. Never NULL. */
+const char* gpt_status_string(gpt_status s);
+
+/* Thread-local detail of the last error raised on this thread ("" if none). */
+const char* gpt_last_error_message(void);
+
+/* Shapes from the depth dial: C = 64*depth, H = C/128, n_kv_head = 1, D = 128,
+ * F = 4C, V = 65536, max_seq_len = 2048, theta = 1e4, softcap 15, eps = 2^-23.
+ * Host only. GPT_E_INVALID_ARG for depth < 2 (C must hold one 128-wide head
+ * per 128 columns) or a null `out`. */
+gpt_status gpt_config_from_depth(int32_t depth, int32_t dtype, gpt_config* out);
+
+/* Checks a config against what the kernels implement. Host only. */
+gpt_status gpt_config_validate(const gpt_config* cfg);
+
+/* Number of parameters (elements). Host only; -1 if cfg is invalid.
+ * Layout queries accept any n_kv_head >= 1 so that multi-head counts can be
+ * checked; gpt_init accepts only n_kv_head == 1. */
+int64_t gpt_param_count(const gpt_config* cfg);
+
+/* Fills out[0..*n) with the canonical parameter order: wte [V, C]; per layer
+ * w_qkv [(H + 2*n_kv_head)*D, C] (query heads, then K heads, then V heads),
+ * w_o [C, H*D], w_1 [F, C], w_2 [C, F]; lm_head [V, C]. On entry *n is the
+ * capacity of `out`; on return it is the number of tensors (2 + 4*n_layer).
+ * `out` may be NULL to query the count. Host only. */
+gpt_status gpt_param_layout(const gpt_config* cfg, gpt_tensor_desc* out, int32_t* n);
+
+/* Bytes of device workspace gpt_init needs for batches up to max_B x max_T.
+ * Host only. */
+gpt_status gpt_workspace_bytes(const gpt_config* cfg, int32_t max_B, int32_t max_T, size_t* bytes);
+
+/* Creates a handle. `params` is the flat parameter buffer in the config dtype
+ * (read only, never written); `grads` the flat fp32 gradient buffer with the
+ * same offsets; `workspace` a device buffer of at least
+ * gpt_workspace_bytes(cfg, max_B, max_T) bytes, 256-byte aligned. All three are
+ * device pointers owned by the caller and must outlive the handle. Uploads
+ * the RoPE cos/sin tables into the workspace on `stream`. */
+gpt_status gpt_init(const gpt_config* cfg, const void* params, float* grads, void* workspace,
+                    size_t ws_bytes, int32_t max_B, int32_t max_T, void* stream, gpt_model** out);
+
+/* Forward pass and mean cross-entropy loss over all B*T positions.
+ * idx, targets: device int32 [B, T] row-major; targets are the next tokens,
+ * each in [0, V). loss: device fp32 scalar. row_loss: optional device fp32
+ * [B*T] per-position losses (may be NULL). need_grad = 1 keeps the stash that
+ * gpt_backward consumes. An id outside [0, V) sets the sticky device flag
+ * (read by gpt_sync_status) and makes the loss NaN. Asynchronous. */
+gpt_status gpt_forward_loss(gpt_model* m, const int32_t* idx, const int32_t* targets, int32_t B,
+                            int32_t T, int32_t need_grad, float* loss, float* row_loss, void* stream);
+
+/* Backward of the last need_grad forward: grads = dloss * d(loss)/d(theta).
+ * accumulate = 1 adds into the gradient buffer; 0 overwrites all of it
+ * (including embedding rows no token touched). GPT_E_STATE if no forward is
+ * pending. Asynchronous. */
+gpt_status gpt_backward(gpt_model* m, float dloss, int32_t accumulate, void* stream);
+
+/* Synchronises `stream` and reads the sticky device flag: GPT_E_DEVICE if a
+ * kernel flagged bad input since gpt_init, else GPT_OK. */
+gpt_status gpt_sync_status(gpt_model* m, void* stream);
+
+/* Frees the handle (host memory only). */
+gpt_status gpt_destroy(gpt_model* m);
+
+/* Measurement support. gpt_profile_begin arms timing of every launch whose
+ * kernel tag equals `tag` (see gpt_kernel_tag_name) with HIP events on the
+ * stream the kernel runs on, or of every launch if tag < 0; gpt_profile_end
+ * synchronises and returns the summed duration in milliseconds and the number
+ * of timed launches, and disarms. At most 65536 launches are timed. */
+gpt_status gpt_profile_begin(gpt_model* m, int32_t tag);
+gpt_status gpt_profile_end(gpt_model* m, double* total_ms, int64_t* launches);
+
+/* Name of a kernel tag (NULL past the last tag); tags run 0..n-1. */
+const char* gpt_kernel_tag_name(int32_t tag);
+
+/* Debug access to a stashed activation of the last forward: device pointer and
+ * byte size of the named buffer ("x", "h1", "qkv", "o", "lse", "h2", "u", "a",
+ * "hf", "logits", "rstd0") for `layer` (ignored by non-layer buffers). The
+ * pointer aliases the workspace and is valid until the next call. */
+gpt_status gpt_debug_buffer(gpt_model* m, const char* name, int32_t layer, void** ptr, size_t* bytes);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GPT_AMD_GPT_H */

@@ -1,0 +1,129 @@
+"""Host half of the C ABI, no GPU needed: the library loads, exports every
+function include/gpt.h declares, and its host-only queries (shapes, layout,
+validation, workspace planning, error paths) behave as documented."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from decoder_only_transformer_gpt_amd import _lib
+from oracle import gpt_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "gpt.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gpt_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    L = _lib.lib()
+    names = header_functions()
+    assert len(names) >= 16
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(_lib._SIGS), "binding and header disagree"
+
+
+def test_status_strings():
+    assert _lib.status_string(0) == "GPT_OK"
+    assert _lib.status_string(-6) == "GPT_E_DEVICE"
+    assert _lib.status_string(-99) == "GPT_E_UNKNOWN"
+
+
+@pytest.mark.parametrize("depth", [2, 4, 12, 20, 24, 32])
+def test_depth_dial_matches_oracle(depth):
+    c = _lib.gpt_config_from_depth(depth, _lib.GPT_BF16)
+    o = O.config_from_depth(depth)
+    for k in ("n_layer", "model_dim", "n_head", "n_kv_head", "head_dim", "mlp_dim", "vocab_size", "max_seq_len"):
+        assert getattr(c, k) == o[k], k
+    assert c.rope_theta == 10000.0 and c.logit_softcap == 15.0
+    assert c.norm_eps == pytest.approx(2.0 ** -23, rel=0, abs=0)
+    assert _lib.gpt_param_count(c) == O.param_count(o)
+    assert _lib.gpt_config_validate(c) == _lib.GPT_OK
+
+
+def test_param_counts_printed_on_pages():
+    c = _lib.gpt_config_from_depth(20)
+    c.n_kv_head = c.n_head
+    assert _lib.gpt_param_count(c) == 560_988_160   # "560.9 million" (truncated)
+    c = _lib.gpt_config_from_depth(32)
+    c.n_kv_head = c.n_head
+    assert _lib.gpt_param_count(c) == 1_879_048_192  # "~1.88B"
+    assert _lib.gpt_param_count(_lib.gpt_config_from_depth(20)) == 502_005_760
+
+
+def test_layout_matches_oracle_order():
+    c = _lib.gpt_config_from_depth(4)
+    lay = _lib.gpt_param_layout(c)
+    shapes = O.param_shapes(O.config_from_depth(4))
+    assert [(n, r, cc) for n, _, r, cc in lay] == [(n, r, cc) for n, r, cc in shapes]
+    off = 0
+    for _, o, r, cc in lay:
+        assert o == off
+        off += r * cc
+    assert off == _lib.gpt_param_count(c)
+
+
+def test_validation_errors():
+    c = _lib.gpt_config_from_depth(4)
+    c.n_kv_head = 2
+    assert _lib.gpt_config_validate(c) == _lib.GPT_E_UNSUPPORTED
+    c = _lib.gpt_config_from_depth(4)
+    c.head_dim = 64
+    assert _lib.gpt_config_validate(c) == _lib.GPT_E_UNSUPPORTED
+    c = _lib.gpt_config_from_depth(4)
+    c.vocab_size = 70000
+    assert _lib.gpt_config_validate(c) == _lib.GPT_E_UNSUPPORTED
+    c = _lib.gpt_config_from_depth(4)
+    c.dtype = 7
+    assert _lib.gpt_config_validate(c) == _lib.GPT_E_UNSUPPORTED
+    c = _lib.gpt_config_from_depth(4)
+    c.n_layer = 0
+    assert _lib.gpt_config_validate(c) == _lib.GPT_E_INVALID_ARG
+    assert _lib.gpt_param_count(c) == -1
+    with pytest.raises(_lib.GptError) as e:
+        _lib.gpt_config_from_depth(1)
+    assert e.value.status == _lib.GPT_E_INVALID_ARG
+    assert "depth" in str(e.value)
+
+
+def test_workspace_planning():
+    c = _lib.gpt_config_from_depth(4)
+    a = _lib.gpt_workspace_bytes(c, 1, 64)
+    b = _lib.gpt_workspace_bytes(c, 2, 64)
+    d = _lib.gpt_workspace_bytes(c, 4, 512)
+    assert 0 < a < b < d
+    assert a % 256 == 0
+    with pytest.raises(_lib.GptError):
+        _lib.gpt_workspace_bytes(c, 1, 4096)   # longer than max_seq_len
+    with pytest.raises(_lib.GptError):
+        _lib.gpt_workspace_bytes(c, 0, 64)
+    d20 = _lib.gpt_config_from_depth(20)
+    gb = _lib.gpt_workspace_bytes(d20, 32, 2048) / 2 ** 30
+    assert 30 < gb < 80, gb   # fits one 288 GB MI355X with room to spare
+
+
+def test_init_argument_errors_touch_no_device():
+    """These errors are raised before any HIP call, so they work without a GPU."""
+    L = _lib.lib()
+    c = _lib.gpt_config_from_depth(4)
+    h = ctypes.c_void_p()
+    assert L.gpt_init(ctypes.byref(c), None, None, None, 0, 1, 64, None, ctypes.byref(h)) == _lib.GPT_E_INVALID_ARG
+    assert h.value is None
+    assert L.gpt_init(ctypes.byref(c), 256, 256, 257, 1 << 40, 1, 64, None, ctypes.byref(h)) == _lib.GPT_E_INVALID_ARG
+    assert "aligned" in _lib.lib().gpt_last_error_message().decode()
+    assert L.gpt_init(ctypes.byref(c), 256, 256, 512, 1024, 1, 64, None, ctypes.byref(h)) == _lib.GPT_E_WORKSPACE
+    c.n_kv_head = 3
+    assert L.gpt_init(ctypes.byref(c), 256, 256, 512, 1 << 40, 1, 64, None, ctypes.byref(h)) == _lib.GPT_E_UNSUPPORTED
+    assert L.gpt_backward(None, ctypes.c_float(1.0), 0, None) == _lib.GPT_E_INVALID_ARG
+    assert L.gpt_forward_loss(None, None, None, 1, 1, 1, None, None, None) == _lib.GPT_E_INVALID_ARG
+
+
+def test_kernel_tags():
+    names = _lib.gpt_kernel_tag_names()
+    assert "gemm_lm_head_softcap" in names and "attn_fwd" in names and "embed_bwd" in names
+    assert len(names) == len(set(names))
