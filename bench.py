@@ -106,6 +106,8 @@ def main():
     ap.add_argument("--workload", default="d20", choices=["tiny", "d4", "d12", "d20"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-table", action="store_true", help="print per-tag timings to stderr")
+    ap.add_argument("--dominant", default=None,
+                    help="kernel tag to report in the roofline (skips the one-step-per-tag scan)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -145,13 +147,14 @@ def main():
     # one profiled step (every launch timed) to find the kernel with the largest share of time
     tags = _lib.gpt_kernel_tag_names()
     per_tag = {}
-    for t_i, t in enumerate(tags):
-        _lib.gpt_profile_begin(m.h, t_i)
-        step()
-        ms, n = _lib.gpt_profile_end(m.h)
-        if n:
-            per_tag[t] = (ms, n)
-    dominant = max(per_tag, key=lambda t: per_tag[t][0])
+    if args.dominant is None or args.kernel_table:
+        for t_i, t in enumerate(tags):
+            _lib.gpt_profile_begin(m.h, t_i)
+            step()
+            ms, n = _lib.gpt_profile_end(m.h)
+            if n:
+                per_tag[t] = (ms, n)
+    dominant = args.dominant or max(per_tag, key=lambda t: per_tag[t][0])
     if args.kernel_table:
         tot = sum(v[0] for v in per_tag.values())
         for t, (ms, n) in sorted(per_tag.items(), key=lambda kv: -kv[1][0]):

@@ -12,13 +12,20 @@
 // sum therefore accumulates without a running maximum or rescaling, and
 // lse = sqrt(D) + log(sum) is exact up to rounding. (This relies on QK-norm.)
 //
-// All contractions run on MFMA 32x32 tiles. The kernels put the output
-// dimension that must be reduced over on the accumulator's lane axis, e.g.
-// the forward computes S^T = K Q^T so each lane owns one query and its
-// softmax row sum stays inside the lane. When an operand held in registers
-// (P, dS) feeds the next MFMA, the k index of that MFMA is permuted to match
-// the accumulator layout; the LDS operand is read with the same permutation
-// (any fixed k order gives the same sum).
+// All contractions run on MFMA 32x32 tiles. The kernels put the dimension
+// that is reduced over on the accumulator's lane axis where it helps: the
+// forward computes S^T = K Q^T so each lane owns one query and its softmax row
+// sum stays inside the lane. When a register-held operand (P, dS) feeds the
+// next MFMA, that MFMA's k index is permuted to match the accumulator layout
+// and the LDS operand is read with the same permutation (any fixed k order
+// gives the same sum).
+//
+// Contractions over the sequence need operands that are contiguous along the
+// sequence: V^T, K^T, Q^T and dO^T. A tiled transpose kernel writes them once
+// per layer into [B, heads, 128, Tp] (Tp = T rounded up to 64, zero padded),
+// so every attention kernel stages plain 16-byte row loads. Each kernel
+// double-buffers its LDS tiles (one barrier per tile) and prefetches the next
+// tile into registers while computing on the current one.
 //
 // qkv row (one token): [H query heads | K | V] x 128. LSE and delta are fp32
 // [B, H, T]. Grid blocks are ordered heavy-first for causal load balance.
@@ -39,58 +46,31 @@ struct AT {
   static constexpr int NDS = D / KS;      // fragment steps over D
   static constexpr int P = D + V;         // pitch of [rows][D] tiles
   static constexpr int PT = 64 + V;       // pitch of [D][64] tiles
+  static constexpr int NBUF = sizeof(T) == 2 ? 2 : 1;  // fp32 tiles only fit LDS once
 };
 
-// rows x 128 tile, rows contiguous in global (pitch ld), to LDS [rows][P].
-template <typename T, int ROWS>
-DEV void tile_rows(T* lds, const T* src, int64_t ld, int rows_valid, int tid) {
-  constexpr int V = AT<T>::V, CPR = D / V;  // 16-byte chunks per row
-  constexpr int ITEMS = ROWS * CPR / 256;
+// A ROWS x COLS tile staged through registers (rows contiguous in global).
+template <typename T, int ROWS, int COLS>
+struct Stage {
+  static constexpr int V = Vec<T>::N, CPR = COLS / V;
+  static constexpr int ITEMS = ROWS * CPR / 256;
+  static_assert(ROWS * CPR % 256 == 0, "tile must split evenly over 256 threads");
+  u32x4 r[ITEMS];
+  DEV void load(const T* src, int64_t ld, int rows_valid, int tid) {
 #pragma unroll
-  for (int i = 0; i < ITEMS; ++i) {
-    const int q = tid + i * 256;
-    const int r = q / CPR, c = q % CPR;
-    u32x4 v = {0, 0, 0, 0};
-    if (r < rows_valid) v = ld16(src + (int64_t)r * ld + c * V);
-    st16(lds + r * AT<T>::P + c * V, v);
-  }
-}
-
-// rows x 128 tile to LDS transposed: [128][PT] with the row index contiguous.
-// Loaded as V x V blocks and transposed in registers.
-template <typename T, int ROWS>
-DEV void tile_T(T* lds, const T* src, int64_t ld, int rows_valid, int tid) {
-  constexpr int V = AT<T>::V;
-  constexpr int RB = ROWS / V, CB = D / V, NB = RB * CB;
-  constexpr int ITEMS = (NB + 255) / 256;
-#pragma unroll
-  for (int i = 0; i < ITEMS; ++i) {
-    const int b = tid + i * 256;
-    if (b >= NB) break;
-    const int rb = b % RB, cb = b / RB;
-    u32x4 in[V], out[V];
-#pragma unroll
-    for (int e = 0; e < V; ++e) {
-      const int r = rb * V + e;
-      in[e] = (r < rows_valid) ? ld16(src + (int64_t)r * ld + cb * V) : u32x4{0, 0, 0, 0};
+    for (int i = 0; i < ITEMS; ++i) {
+      const int q = tid + i * 256, row = q / CPR, c = q % CPR;
+      r[i] = (row < rows_valid) ? ld16(src + (int64_t)row * ld + c * V) : u32x4{0, 0, 0, 0};
     }
-    if constexpr (V == 8) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-#pragma unroll
-        for (int d = 0; d < 4; ++d)
-          out[j][d] = __builtin_amdgcn_perm(in[2 * d + 1][j >> 1], in[2 * d][j >> 1],
-                                            (j & 1) ? 0x07060302u : 0x05040100u);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) out[j][e] = in[e][j];
-    }
-#pragma unroll
-    for (int j = 0; j < V; ++j) st16(lds + (cb * V + j) * AT<T>::PT + rb * V, out[j]);
   }
-}
+  DEV void store(T* lds, int pitch, int tid) const {
+#pragma unroll
+    for (int i = 0; i < ITEMS; ++i) {
+      const int q = tid + i * 256, row = q / CPR, c = q % CPR;
+      st16(lds + row * pitch + c * V, r[i]);
+    }
+  }
+};
 
 // Packs accumulator values of 32x32 block `acc` into the register operand of
 // the next MFMA for k-step kk: element e is the value at accumulator row
@@ -134,21 +114,59 @@ DEV f32x16 zero16() {
   return z;
 }
 
+// --------------------------------------------------------- transposition --
+// dst[((b*nh + h)*D + d)*Tp + t] = src[(b*T + t)*ld + col0 + h*D + d], zero for T <= t < Tp.
+// Block: 64 tokens x 128 columns of one (b, h); V x V blocks transposed in registers.
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_heads_kernel(const T* __restrict__ src, int64_t ld, int col0,
+                                                              int nh, int T_, int Tp, T* __restrict__ dst) {
+  constexpr int V = Vec<T>::N, RB = 64 / V, CB = D / V, NB = RB * CB;
+  const int t0 = blockIdx.x * 64, h = blockIdx.y, b = blockIdx.z;
+  const T* s = src + ((int64_t)b * T_ + t0) * ld + col0 + h * D;
+  T* d0 = dst + ((int64_t)b * nh + h) * D * Tp + t0;
+  for (int bi = threadIdx.x; bi < NB; bi += 256) {
+    const int rb = bi % RB, cb = bi / RB;
+    u32x4 in[V], out[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      const int t = rb * V + e;
+      in[e] = (t0 + t < T_) ? ld16(s + (int64_t)t * ld + cb * V) : u32x4{0, 0, 0, 0};
+    }
+    if constexpr (V == 8) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          out[j][q] = __builtin_amdgcn_perm(in[2 * q + 1][j >> 1], in[2 * q][j >> 1],
+                                            (j & 1) ? 0x07060302u : 0x05040100u);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out[j][e] = in[e][j];
+    }
+#pragma unroll
+    for (int j = 0; j < V; ++j) st16(d0 + (int64_t)(cb * V + j) * Tp + rb * V, out[j]);
+  }
+}
+
 // ------------------------------------------------------------- forward --
 // Block: 128 queries of one (batch, head) = 4 waves x 32. KV tiles of 64 keys.
 template <typename T>
-__global__ __launch_bounds__(256) void attn_fwd_kernel(const T* __restrict__ qkv, int T_, int H, T* __restrict__ o,
-                                                       float* __restrict__ lse) {
+__global__ __launch_bounds__(256) void attn_fwd_kernel(const T* __restrict__ qkv, const T* __restrict__ vT, int T_,
+                                                       int Tp, int H, T* __restrict__ o, float* __restrict__ lse) {
   using A = AT<T>;
-  constexpr int V = A::V;
-  __shared__ __attribute__((aligned(16))) T Ks[64 * A::P];
-  __shared__ __attribute__((aligned(16))) T VTs[D * A::PT];
+  constexpr int V = A::V, NBUF = A::NBUF;
+  __shared__ __attribute__((aligned(16))) T Ks[NBUF][64 * A::P];
+  __shared__ __attribute__((aligned(16))) T VTs[NBUF][D * A::PT];
   const int nqb = (T_ + 127) / 128;
   const int qb = nqb - 1 - blockIdx.x;
   const int h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
   const int64_t ld = (int64_t)(H + 2) * D;
   const T* base = qkv + (int64_t)b * T_ * ld;
+  const T* kbase = base + H * D;
+  const T* vtb = vT + (int64_t)b * D * Tp;
   const int q = qb * 128 + w * 32 + l32;
 
   u32x4 qf[A::NDS];
@@ -163,18 +181,32 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const T* __restrict__ qkv
   const float shift = sqrtf((float)D);
   const float sl2 = kLog2e / shift, sh2 = shift * kLog2e;
   const int kend = min(T_, qb * 128 + 128);
+  const int nt = (kend + 63) / 64;
 
-  for (int k0 = 0; k0 < kend; k0 += 64) {
-    tile_rows<T, 64>(Ks, base + (int64_t)k0 * ld + H * D, ld, T_ - k0, tid);
-    tile_T<T, 64>(VTs, base + (int64_t)k0 * ld + (H + 1) * D, ld, T_ - k0, tid);
-    __syncthreads();
+  Stage<T, 64, D> sk;
+  Stage<T, D, 64> sv;
+  sk.load(kbase, ld, T_, tid);
+  sv.load(vtb, Tp, D, tid);
+  sk.store(Ks[0], A::P, tid);
+  sv.store(VTs[0], A::PT, tid);
+  __syncthreads();
+
+  for (int it = 0; it < nt; ++it) {
+    const int cur = it % NBUF, k0 = it * 64;
+    const bool more = it + 1 < nt;
+    if (more) {
+      sk.load(kbase + (int64_t)(k0 + 64) * ld, ld, T_ - k0 - 64, tid);
+      sv.load(vtb + k0 + 64, Tp, D, tid);
+    }
+    const T* K_ = Ks[cur];
+    const T* VT_ = VTs[cur];
     f32x16 s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       s[kb] = zero16();
 #pragma unroll
       for (int ks = 0; ks < A::NDS; ++ks)
-        s[kb] = mfma16(ld16(Ks + (kb * 32 + l32) * A::P + ks * A::KS + g * V), qf[ks], s[kb], (T*)nullptr);
+        s[kb] = mfma16(ld16(K_ + (kb * 32 + l32) * A::P + ks * A::KS + g * V), qf[ks], s[kb], (T*)nullptr);
 #pragma unroll
       for (int blk = 0; blk < 4; ++blk)
 #pragma unroll
@@ -192,8 +224,13 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const T* __restrict__ qkv
         const u32x4 pf = pack_frag<T>(s[kb], kk);
 #pragma unroll
         for (int db = 0; db < 4; ++db)
-          acc[db] = mfma16(read_perm<T>(VTs, db * 32 + l32, kb * 32, kk, g), pf, acc[db], (T*)nullptr);
+          acc[db] = mfma16(read_perm<T>(VT_, db * 32 + l32, kb * 32, kk, g), pf, acc[db], (T*)nullptr);
       }
+    if (NBUF == 1) __syncthreads();
+    if (more) {
+      sk.store(Ks[(it + 1) % NBUF], A::P, tid);
+      sv.store(VTs[(it + 1) % NBUF], A::PT, tid);
+    }
     __syncthreads();
   }
   rsum += __shfl_xor(rsum, 32, 64);
@@ -239,20 +276,23 @@ __global__ __launch_bounds__(256) void attn_delta_kernel(const T* __restrict__ o
 
 // dQ: block = 128 queries of one (batch, head); loops over KV tiles.
 template <typename T>
-__global__ __launch_bounds__(256) void attn_dq_kernel(const T* __restrict__ qkv, const T* __restrict__ dout,
-                                                      const float* __restrict__ lse, const float* __restrict__ delta,
-                                                      int T_, int H, T* __restrict__ dqkv) {
+__global__ __launch_bounds__(256) void attn_dq_kernel(const T* __restrict__ qkv, const T* __restrict__ kT,
+                                                      const T* __restrict__ dout, const float* __restrict__ lse,
+                                                      const float* __restrict__ delta, int T_, int Tp, int H,
+                                                      T* __restrict__ dqkv) {
   using A = AT<T>;
-  constexpr int V = A::V;
-  __shared__ __attribute__((aligned(16))) T Ks[64 * A::P];
-  __shared__ __attribute__((aligned(16))) T Vs[64 * A::P];
-  __shared__ __attribute__((aligned(16))) T KTs[D * A::PT];
+  constexpr int V = A::V, NBUF = A::NBUF;
+  __shared__ __attribute__((aligned(16))) T Ks[NBUF][64 * A::P];
+  __shared__ __attribute__((aligned(16))) T Vs[NBUF][64 * A::P];
+  __shared__ __attribute__((aligned(16))) T KTs[NBUF][D * A::PT];
   const int nqb = (T_ + 127) / 128;
   const int qb = nqb - 1 - blockIdx.x;
   const int h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
   const int64_t ld = (int64_t)(H + 2) * D;
   const T* base = qkv + (int64_t)b * T_ * ld;
+  const T* kbase = base + H * D;
+  const T* ktb = kT + (int64_t)b * D * Tp;
   const int q = qb * 128 + w * 32 + l32;
   const bool qv = q < T_;
 
@@ -272,20 +312,38 @@ __global__ __launch_bounds__(256) void attn_dq_kernel(const T* __restrict__ qkv,
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc[i] = zero16();
   const int kend = min(T_, qb * 128 + 128);
-  for (int k0 = 0; k0 < kend; k0 += 64) {
-    const T* kp = base + (int64_t)k0 * ld + H * D;
-    tile_rows<T, 64>(Ks, kp, ld, T_ - k0, tid);
-    tile_rows<T, 64>(Vs, kp + D, ld, T_ - k0, tid);
-    tile_T<T, 64>(KTs, kp, ld, T_ - k0, tid);
-    __syncthreads();
+  const int nt = (kend + 63) / 64;
+
+  Stage<T, 64, D> sk, sv;
+  Stage<T, D, 64> skt;
+  sk.load(kbase, ld, T_, tid);
+  sv.load(kbase + D, ld, T_, tid);
+  skt.load(ktb, Tp, D, tid);
+  sk.store(Ks[0], A::P, tid);
+  sv.store(Vs[0], A::P, tid);
+  skt.store(KTs[0], A::PT, tid);
+  __syncthreads();
+
+  for (int it = 0; it < nt; ++it) {
+    const int cur = it % NBUF, k0 = it * 64;
+    const bool more = it + 1 < nt;
+    if (more) {
+      const T* kp = kbase + (int64_t)(k0 + 64) * ld;
+      sk.load(kp, ld, T_ - k0 - 64, tid);
+      sv.load(kp + D, ld, T_ - k0 - 64, tid);
+      skt.load(ktb + k0 + 64, Tp, D, tid);
+    }
+    const T* K_ = Ks[cur];
+    const T* V_ = Vs[cur];
+    const T* KT_ = KTs[cur];
     f32x16 ds[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       f32x16 s = zero16(), dp = zero16();
 #pragma unroll
       for (int ks = 0; ks < A::NDS; ++ks) {
-        s = mfma16(ld16(Ks + (kb * 32 + l32) * A::P + ks * A::KS + g * V), qf[ks], s, (T*)nullptr);
-        dp = mfma16(ld16(Vs + (kb * 32 + l32) * A::P + ks * A::KS + g * V), df[ks], dp, (T*)nullptr);
+        s = mfma16(ld16(K_ + (kb * 32 + l32) * A::P + ks * A::KS + g * V), qf[ks], s, (T*)nullptr);
+        dp = mfma16(ld16(V_ + (kb * 32 + l32) * A::P + ks * A::KS + g * V), df[ks], dp, (T*)nullptr);
       }
 #pragma unroll
       for (int blk = 0; blk < 4; ++blk)
@@ -304,8 +362,15 @@ __global__ __launch_bounds__(256) void attn_dq_kernel(const T* __restrict__ qkv,
         const u32x4 pf = pack_frag<T>(ds[kb], kk);
 #pragma unroll
         for (int db = 0; db < 4; ++db)
-          acc[db] = mfma16(read_perm<T>(KTs, db * 32 + l32, kb * 32, kk, g), pf, acc[db], (T*)nullptr);
+          acc[db] = mfma16(read_perm<T>(KT_, db * 32 + l32, kb * 32, kk, g), pf, acc[db], (T*)nullptr);
       }
+    if (NBUF == 1) __syncthreads();
+    if (more) {
+      const int nb = (it + 1) % NBUF;
+      sk.store(Ks[nb], A::P, tid);
+      sv.store(Vs[nb], A::P, tid);
+      skt.store(KTs[nb], A::PT, tid);
+    }
     __syncthreads();
   }
   if (qv) {
@@ -324,17 +389,18 @@ __global__ __launch_bounds__(256) void attn_dq_kernel(const T* __restrict__ qkv,
 // dK, dV: block = 128 keys of one batch row (4 waves x 32 keys), summed over
 // every query head and every query tile at or after the keys (no atomics).
 template <typename T>
-__global__ __launch_bounds__(256) void attn_dkv_kernel(const T* __restrict__ qkv, const T* __restrict__ dout,
+__global__ __launch_bounds__(256) void attn_dkv_kernel(const T* __restrict__ qkv, const T* __restrict__ qT,
+                                                       const T* __restrict__ dout, const T* __restrict__ doT,
                                                        const float* __restrict__ lse,
-                                                       const float* __restrict__ delta, int T_, int H,
+                                                       const float* __restrict__ delta, int T_, int Tp, int H,
                                                        T* __restrict__ dqkv) {
   using A = AT<T>;
-  constexpr int V = A::V;
-  __shared__ __attribute__((aligned(16))) T Qs[64 * A::P];
-  __shared__ __attribute__((aligned(16))) T QTs[D * A::PT];
-  __shared__ __attribute__((aligned(16))) T Ds[64 * A::P];
-  __shared__ __attribute__((aligned(16))) T DTs[D * A::PT];
-  __shared__ float Ls[64], Es[64];
+  constexpr int V = A::V, NBUF = A::NBUF;
+  __shared__ __attribute__((aligned(16))) T Qs[NBUF][64 * A::P];
+  __shared__ __attribute__((aligned(16))) T QTs[NBUF][D * A::PT];
+  __shared__ __attribute__((aligned(16))) T Ds[NBUF][64 * A::P];
+  __shared__ __attribute__((aligned(16))) T DTs[NBUF][D * A::PT];
+  __shared__ float Ls[NBUF][64], Es[NBUF][64];
   const int kb = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
   const int64_t ld = (int64_t)(H + 2) * D;
@@ -354,57 +420,84 @@ __global__ __launch_bounds__(256) void attn_dkv_kernel(const T* __restrict__ qkv
 #pragma unroll
   for (int i = 0; i < 4; ++i) { adk[i] = zero16(); adv[i] = zero16(); }
 
-  for (int h = 0; h < H; ++h) {
-    const float* lh = lse + ((int64_t)b * H + h) * T_;
-    const float* eh = delta + ((int64_t)b * H + h) * T_;
-    for (int q0 = kb * 128; q0 < T_; q0 += 64) {
-      const T* qp = base + (int64_t)q0 * ld + h * D;
-      const T* dp_ = dout + ((int64_t)b * T_ + q0) * H * D + h * D;
-      tile_rows<T, 64>(Qs, qp, ld, T_ - q0, tid);
-      tile_T<T, 64>(QTs, qp, ld, T_ - q0, tid);
-      tile_rows<T, 64>(Ds, dp_, (int64_t)H * D, T_ - q0, tid);
-      tile_T<T, 64>(DTs, dp_, (int64_t)H * D, T_ - q0, tid);
-      if (tid < 64) {
-        const bool v = q0 + tid < T_;
-        Ls[tid] = v ? lh[q0 + tid] : 0.f;
-        Es[tid] = v ? eh[q0 + tid] : 0.f;
-      }
-      __syncthreads();
-      f32x16 p[2], ds[2];
-#pragma unroll
-      for (int qb2 = 0; qb2 < 2; ++qb2) {
-        f32x16 s = zero16(), dpv = zero16();
-#pragma unroll
-        for (int ks = 0; ks < A::NDS; ++ks) {
-          s = mfma16(ld16(Qs + (qb2 * 32 + l32) * A::P + ks * A::KS + g * V), kf[ks], s, (T*)nullptr);
-          dpv = mfma16(ld16(Ds + (qb2 * 32 + l32) * A::P + ks * A::KS + g * V), vf[ks], dpv, (T*)nullptr);
-        }
-#pragma unroll
-        for (int blk = 0; blk < 4; ++blk)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int qi = qb2 * 32 + blk * 8 + g * 4 + r;
-            const int qq = q0 + qi;
-            const int i = blk * 4 + r;
-            const float pv = (qq >= key && qq < T_ && kv) ? exp2f(s[i] * sl2 - Ls[qi] * kLog2e) : 0.f;
-            p[qb2][i] = pv;
-            ds[qb2][i] = pv * (dpv[i] - Es[qi]);
-          }
-      }
-#pragma unroll
-      for (int qb2 = 0; qb2 < 2; ++qb2)
-#pragma unroll
-        for (int kk = 0; kk < 32 / A::KS; ++kk) {
-          const u32x4 pf = pack_frag<T>(p[qb2], kk);
-          const u32x4 sf = pack_frag<T>(ds[qb2], kk);
-#pragma unroll
-          for (int db = 0; db < 4; ++db) {
-            adv[db] = mfma16(read_perm<T>(DTs, db * 32 + l32, qb2 * 32, kk, g), pf, adv[db], (T*)nullptr);
-            adk[db] = mfma16(read_perm<T>(QTs, db * 32 + l32, qb2 * 32, kk, g), sf, adk[db], (T*)nullptr);
-          }
-        }
-      __syncthreads();
+  const int qt0 = 2 * kb, nqt = Tp / 64, nq = nqt - qt0;
+  const int total = H * nq;
+  Stage<T, 64, D> sq, sd;
+  Stage<T, D, 64> sqt, sdt;
+  float pl = 0.f, pe = 0.f;
+  auto issue = [&](int it) {
+    const int h = it / nq, q0 = (qt0 + it % nq) * 64;
+    sq.load(base + (int64_t)q0 * ld + h * D, ld, T_ - q0, tid);
+    sqt.load(qT + ((int64_t)b * H + h) * D * Tp + q0, Tp, D, tid);
+    sd.load(dout + ((int64_t)b * T_ + q0) * H * D + h * D, (int64_t)H * D, T_ - q0, tid);
+    sdt.load(doT + ((int64_t)b * H + h) * D * Tp + q0, Tp, D, tid);
+    if (tid < 64) {
+      const bool v = q0 + tid < T_;
+      pl = v ? lse[((int64_t)b * H + h) * T_ + q0 + tid] : 0.f;
+      pe = v ? delta[((int64_t)b * H + h) * T_ + q0 + tid] : 0.f;
     }
+  };
+  auto commit = [&](int nb) {
+    sq.store(Qs[nb], A::P, tid);
+    sqt.store(QTs[nb], A::PT, tid);
+    sd.store(Ds[nb], A::P, tid);
+    sdt.store(DTs[nb], A::PT, tid);
+    if (tid < 64) {
+      Ls[nb][tid] = pl;
+      Es[nb][tid] = pe;
+    }
+  };
+  if (total > 0) {
+    issue(0);
+    commit(0);
+  }
+  __syncthreads();
+
+  for (int it = 0; it < total; ++it) {
+    const int cur = it % NBUF;
+    const int q0 = (qt0 + it % nq) * 64;
+    const bool more = it + 1 < total;
+    if (more) issue(it + 1);
+    const T* Q_ = Qs[cur];
+    const T* QT_ = QTs[cur];
+    const T* D_ = Ds[cur];
+    const T* DT_ = DTs[cur];
+    f32x16 p[2], ds[2];
+#pragma unroll
+    for (int qb2 = 0; qb2 < 2; ++qb2) {
+      f32x16 s = zero16(), dpv = zero16();
+#pragma unroll
+      for (int ks = 0; ks < A::NDS; ++ks) {
+        s = mfma16(ld16(Q_ + (qb2 * 32 + l32) * A::P + ks * A::KS + g * V), kf[ks], s, (T*)nullptr);
+        dpv = mfma16(ld16(D_ + (qb2 * 32 + l32) * A::P + ks * A::KS + g * V), vf[ks], dpv, (T*)nullptr);
+      }
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int qi = qb2 * 32 + blk * 8 + g * 4 + r;
+          const int qq = q0 + qi;
+          const int i = blk * 4 + r;
+          const float pv = (qq >= key && qq < T_ && kv) ? exp2f(s[i] * sl2 - Ls[cur][qi] * kLog2e) : 0.f;
+          p[qb2][i] = pv;
+          ds[qb2][i] = pv * (dpv[i] - Es[cur][qi]);
+        }
+    }
+#pragma unroll
+    for (int qb2 = 0; qb2 < 2; ++qb2)
+#pragma unroll
+      for (int kk = 0; kk < 32 / A::KS; ++kk) {
+        const u32x4 pf = pack_frag<T>(p[qb2], kk);
+        const u32x4 sf = pack_frag<T>(ds[qb2], kk);
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          adv[db] = mfma16(read_perm<T>(DT_, db * 32 + l32, qb2 * 32, kk, g), pf, adv[db], (T*)nullptr);
+          adk[db] = mfma16(read_perm<T>(QT_, db * 32 + l32, qb2 * 32, kk, g), sf, adk[db], (T*)nullptr);
+        }
+      }
+    if (NBUF == 1) __syncthreads();
+    if (more) commit((it + 1) % NBUF);
+    __syncthreads();
   }
   if (kv) {
     T* outk = dqkv + ((int64_t)b * T_ + key) * ld + H * D;
@@ -423,35 +516,52 @@ __global__ __launch_bounds__(256) void attn_dkv_kernel(const T* __restrict__ qkv
 }
 
 template <typename T>
-hipError_t fwd_typed(const void* qkv, int B, int T_, int H, void* o, float* lse, hipStream_t s) {
-  dim3 grid((T_ + 127) / 128, H, B);
-  hipLaunchKernelGGL(attn_fwd_kernel<T>, grid, dim3(256), 0, s, (const T*)qkv, T_, H, (T*)o, lse);
+hipError_t transpose(const void* src, int64_t ld, int col0, int nh, int B, int T_, int Tp, void* dst, hipStream_t s) {
+  hipLaunchKernelGGL(transpose_heads_kernel<T>, dim3(Tp / 64, nh, B), dim3(256), 0, s, (const T*)src, ld, col0, nh,
+                     T_, Tp, (T*)dst);
   return hipGetLastError();
 }
 
 template <typename T>
-hipError_t bwd_typed(const void* qkv, const void* o, const void* dout, const float* lse, int B, int T_, int H,
-                     float* delta, void* dqkv, hipStream_t s) {
+hipError_t fwd_typed(const void* qkv, int B, int T_, int H, void* o, float* lse, void* vT, hipStream_t s) {
+  const int Tp = attn_padded_len(T_);
+  hipError_t e = transpose<T>(qkv, (int64_t)(H + 2) * D, (H + 1) * D, 1, B, T_, Tp, vT, s);
+  if (e != hipSuccess) return e;
+  dim3 grid((T_ + 127) / 128, H, B);
+  hipLaunchKernelGGL(attn_fwd_kernel<T>, grid, dim3(256), 0, s, (const T*)qkv, (const T*)vT, T_, Tp, H, (T*)o, lse);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t bwd_typed(const AttnBwdArgs& a, hipStream_t s) {
+  const int T_ = a.T, H = a.H, B = a.B;
+  const int Tp = attn_padded_len(T_);
+  const int64_t ld = (int64_t)(H + 2) * D;
+  hipError_t e;
+  if ((e = transpose<T>(a.qkv, ld, 0, H, B, T_, Tp, a.qT, s)) != hipSuccess) return e;
+  if ((e = transpose<T>(a.qkv, ld, H * D, 1, B, T_, Tp, a.kT, s)) != hipSuccess) return e;
+  if ((e = transpose<T>(a.dout, (int64_t)H * D, 0, H, B, T_, Tp, a.doT, s)) != hipSuccess) return e;
   const int64_t groups = (int64_t)B * T_ * H;
   hipLaunchKernelGGL(attn_delta_kernel<T>, dim3((unsigned)((groups * 16 + 255) / 256)), dim3(256), 0, s,
-                     (const T*)o, (const T*)dout, B * T_, T_, H, delta);
-  hipLaunchKernelGGL(attn_dq_kernel<T>, dim3((T_ + 127) / 128, H, B), dim3(256), 0, s, (const T*)qkv,
-                     (const T*)dout, lse, delta, T_, H, (T*)dqkv);
-  hipLaunchKernelGGL(attn_dkv_kernel<T>, dim3((T_ + 127) / 128, B), dim3(256), 0, s, (const T*)qkv, (const T*)dout,
-                     lse, delta, T_, H, (T*)dqkv);
+                     (const T*)a.o, (const T*)a.dout, B * T_, T_, H, a.delta);
+  hipLaunchKernelGGL(attn_dq_kernel<T>, dim3((T_ + 127) / 128, H, B), dim3(256), 0, s, (const T*)a.qkv,
+                     (const T*)a.kT, (const T*)a.dout, a.lse, a.delta, T_, Tp, H, (T*)a.dqkv);
+  hipLaunchKernelGGL(attn_dkv_kernel<T>, dim3((T_ + 127) / 128, B), dim3(256), 0, s, (const T*)a.qkv,
+                     (const T*)a.qT, (const T*)a.dout, (const T*)a.doT, a.lse, a.delta, T_, Tp, H, (T*)a.dqkv);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_attn_fwd(int dtype, const void* qkv, int B, int T, int H, void* o, float* lse, hipStream_t s) {
-  return dtype == 1 ? fwd_typed<bf16>(qkv, B, T, H, o, lse, s) : fwd_typed<float>(qkv, B, T, H, o, lse, s);
+int attn_padded_len(int T) { return (T + 63) / 64 * 64; }
+
+hipError_t launch_attn_fwd(int dtype, const void* qkv, int B, int T, int H, void* o, float* lse, void* vT,
+                           hipStream_t s) {
+  return dtype == 1 ? fwd_typed<bf16>(qkv, B, T, H, o, lse, vT, s) : fwd_typed<float>(qkv, B, T, H, o, lse, vT, s);
 }
 
-hipError_t launch_attn_bwd(int dtype, const void* qkv, const void* o, const void* dout, const float* lse, int B,
-                           int T, int H, float* delta, void* dqkv, hipStream_t s) {
-  return dtype == 1 ? bwd_typed<bf16>(qkv, o, dout, lse, B, T, H, delta, dqkv, s)
-                    : bwd_typed<float>(qkv, o, dout, lse, B, T, H, delta, dqkv, s);
+hipError_t launch_attn_bwd(int dtype, const AttnBwdArgs& a, hipStream_t s) {
+  return dtype == 1 ? bwd_typed<bf16>(a, s) : bwd_typed<float>(a, s);
 }
 
 }  // namespace gk

@@ -21,6 +21,8 @@
 // holding 4 consecutive output columns of one output row: the epilogue writes
 // 8- or 16-byte vectors and row-wise epilogue reductions stay inside a lane.
 
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -37,7 +39,12 @@ struct TileK {
   static constexpr int KSTEP = 2 * V;        // k per fragment pair (2 lane groups)
 };
 
-// Loads a ROWS x BK tile (rows along m or n) into registers.
+// Loads a ROWS x BK tile (rows along m or n) into registers with buffer
+// loads. Per-lane byte offsets inside the tile are computed once; each K tile
+// gets a fresh buffer resource (SGPRs) whose base points at the tile and
+// whose record count ends at the last valid row, so rows past M and k past
+// the end of a ragged split read as zero in hardware: no per-load address
+// arithmetic and no selects in the loop.
 template <typename T, int ROWS, bool KCONTIG>
 struct TileLoader {
   using TK = TileK<T>;
@@ -46,58 +53,65 @@ struct TileLoader {
   static constexpr int ITEMS = KCONTIG ? (ROWS * 8 / kThreads)
                                        : ((ROWS / V) * (TK::BK / V) + kThreads - 1) / kThreads;
   static constexpr int REGS = KCONTIG ? ITEMS : ITEMS * V;  // u32x4 registers
-  u32x4 r[REGS > 0 ? REGS : 1];
+  static constexpr uint32_t kOOB = 0x7ffffff0u;             // beyond any record count used
+  // 16-byte LDS stores per thread per tile
+  static constexpr int NSTORE = KCONTIG ? ITEMS
+                                        : ((ROWS / V) * (TK::BK / V) >= kThreads ? ITEMS * V : V);
+  using Regs = u32x4[REGS];
+  uint32_t voff[REGS];
 
-  // base: element (row0, k0) of the operand; rows < rows_valid and
-  // k < k_valid are real, the rest reads as zero (k-contiguous operands have
-  // K a multiple of BK, so only their rows are checked).
-  DEV void load(const T* __restrict__ base, int64_t ld, int rows_valid, int k_valid, int tid) {
+  DEV void init(int64_t ld, int tid) {
+    const uint32_t ldb = (uint32_t)(ld * (int64_t)sizeof(T));
     if constexpr (KCONTIG) {
 #pragma unroll
       for (int i = 0; i < ITEMS; ++i) {
-        int v = tid + i * kThreads;
-        int row = v >> 3, kv = v & 7;
-        if (row < rows_valid)
-          r[i] = ld16(base + (int64_t)row * ld + kv * V);
-        else
-          r[i] = u32x4{0, 0, 0, 0};
+        const int v = tid + i * kThreads;
+        voff[i] = (uint32_t)(v >> 3) * ldb + (uint32_t)(v & 7) * 16u;
       }
     } else {
-      constexpr int KB = TK::BK / V;  // blocks along k (8)
-      constexpr int NB = (ROWS / V) * KB;
+      constexpr int KB = TK::BK / V, NB = (ROWS / V) * KB;
 #pragma unroll
       for (int i = 0; i < ITEMS; ++i) {
-        int b = tid + i * kThreads;
-        int kb = b % KB, rb = b / KB;
+        const int b = tid + i * kThreads;
+        const int kb = b % KB, rb = b / KB;
 #pragma unroll
-        for (int e = 0; e < V; ++e) {
-          int k = kb * V + e;
-          if (b < NB && k < k_valid && rb * V < rows_valid)
-            r[i * V + e] = ld16(base + (int64_t)k * ld + rb * V);
-          else
-            r[i * V + e] = u32x4{0, 0, 0, 0};
-        }
+        for (int e = 0; e < V; ++e)
+          voff[i * V + e] = (b < NB) ? (uint32_t)(kb * V + e) * ldb + (uint32_t)rb * 16u : kOOB;
       }
     }
   }
 
+  // Resource for the tile whose element (row 0, k 0) is at `base`: for a
+  // k-contiguous operand rows < rows_valid are real; for an mn-contiguous one
+  // k < k_valid are real.
+  static DEV __amdgpu_buffer_rsrc_t rsrc(const T* base, int64_t ld, int rows_valid, int k_valid) {
+    int64_t n = KCONTIG ? (int64_t)rows_valid * ld * (int64_t)sizeof(T) - 0
+                        : (int64_t)min(k_valid, TK::BK) * ld * (int64_t)sizeof(T);
+    n = n < 0 ? 0 : (n > (1 << 30) ? (1 << 30) : n);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(base), (short)0, (int)n, 0x00020000);
+  }
+
+  DEV void load(Regs& r, __amdgpu_buffer_rsrc_t rs) const {
+#pragma unroll
+    for (int q = 0; q < REGS; ++q) r[q] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff[q], 0, 0);
+  }
+
   // Store to LDS tile [ROWS][LDK] (k contiguous).
-  DEV void store(T* lds, int tid) {
+  static DEV void store(const Regs& r, T* lds, int tid) {
     if constexpr (KCONTIG) {
 #pragma unroll
       for (int i = 0; i < ITEMS; ++i) {
-        int v = tid + i * kThreads;
-        int row = v >> 3, kv = v & 7;
-        st16(lds + row * TK::LDK + kv * V, r[i]);
+        const int v = tid + i * kThreads;
+        st16(lds + (v >> 3) * TK::LDK + (v & 7) * V, r[i]);
       }
     } else {
       constexpr int KB = TK::BK / V;
       constexpr int NB = (ROWS / V) * KB;
 #pragma unroll
       for (int i = 0; i < ITEMS; ++i) {
-        int b = tid + i * kThreads;
-        if (b >= NB) continue;
-        int kb = b % KB, rb = b / KB;
+        const int b = tid + i * kThreads;
+        if (NB % kThreads != 0 && b >= NB) continue;
+        const int kb = b % KB, rb = b / KB;
         u32x4 out[V];
         transpose(&r[i * V], out);
 #pragma unroll
@@ -137,9 +151,9 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs args) {
   constexpr int TM = WM / 32, TN = WN / 32;
   static_assert(TM >= 1 && TN >= 1, "tile too small");
 
-  __shared__ __attribute__((aligned(16))) T smem[(BM + BN) * LDK];
-  T* As = smem;
-  T* Bs = smem + BM * LDK;
+  // Two LDS stages: tile kt is consumed from stage kt&1 while tile kt+1 is
+  // written to the other stage; one barrier per K tile.
+  __shared__ __attribute__((aligned(16))) T smem[2][(BM + BN) * LDK];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -166,14 +180,22 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs args) {
   const T* Ap = reinterpret_cast<const T*>(args.A);
   const T* Bp = reinterpret_cast<const T*>(args.B);
 
-  TileLoader<T, BM, AK> la;
-  TileLoader<T, BN, BKc> lb;
-
-  auto a_base = [&](int k0) -> const T* {
-    return AK ? Ap + (int64_t)m0 * args.lda + k0 : Ap + (int64_t)k0 * args.lda + m0;
+  using LA = TileLoader<T, BM, AK>;
+  using LB = TileLoader<T, BN, BKc>;
+  LA la;
+  LB lb;
+  la.init(args.lda, tid);
+  lb.init(args.ldb, tid);
+  // element (row 0, k 0) of K tile kt for each operand, and its resource
+  auto rs_a = [&](int kt) {
+    const int k0 = kbeg + kt * BK;
+    const T* p = AK ? Ap + (int64_t)m0 * args.lda + k0 : Ap + (int64_t)k0 * args.lda + m0;
+    return LA::rsrc(p, args.lda, M - m0, kend - k0);
   };
-  auto b_base = [&](int k0) -> const T* {
-    return BKc ? Bp + (int64_t)n0 * args.ldb + k0 : Bp + (int64_t)k0 * args.ldb + n0;
+  auto rs_b = [&](int kt) {
+    const int k0 = kbeg + kt * BK;
+    const T* p = BKc ? Bp + (int64_t)n0 * args.ldb + k0 : Bp + (int64_t)k0 * args.ldb + n0;
+    return LB::rsrc(p, args.ldb, N - n0, kend - k0);
   };
 
   f32x16 acc[TM][TN];
@@ -184,104 +206,178 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs args) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
+  // Global prefetch runs two K tiles ahead in two register sets: tile t is
+  // loaded into set t&1 two iterations before it is consumed and stored to
+  // LDS stage t&1 one iteration before. Past the end the prefetch re-reads
+  // the last tile and the store hits the idle stage (uniform, branch-free
+  // body). The loop is unrolled by two so the register set is static.
+  typename LA::Regs ra0, ra1;
+  typename LB::Regs rb0, rb1;
   if (nk > 0) {
-    la.load(a_base(kbeg), args.lda, M - m0, kend - kbeg, tid);
-    lb.load(b_base(kbeg), args.ldb, N - n0, kend - kbeg, tid);
+    la.load(ra0, rs_a(0));
+    lb.load(rb0, rs_b(0));
+    la.load(ra1, rs_a(min(1, nk - 1)));
+    lb.load(rb1, rs_b(min(1, nk - 1)));
+    LA::store(ra0, smem[0], tid);
+    LB::store(rb0, smem[0] + BM * LDK, tid);
+    la.load(ra0, rs_a(min(2, nk - 1)));
+    lb.load(rb0, rs_b(min(2, nk - 1)));
   }
-  for (int kt = 0; kt < nk; ++kt) {
-    la.store(As, tid);
-    lb.store(Bs, tid);
-    __syncthreads();
-    if (kt + 1 < nk) {
-      const int k0 = kbeg + (kt + 1) * BK;
-      la.load(a_base(k0), args.lda, M - m0, kend - k0, tid);
-      lb.load(b_base(k0), args.ldb, N - n0, kend - k0, tid);
-    }
+  __syncthreads();
+
+  constexpr int KSTEPS = BK / TK::KSTEP;
+  auto step = [&](int kt, typename LA::Regs& ran, typename LB::Regs& rbn) {
+    const T* As = smem[kt & 1];
+    const T* Bs = As + BM * LDK;
+    LA::store(ran, smem[(kt + 1) & 1], tid);
+    LB::store(rbn, smem[(kt + 1) & 1] + BM * LDK, tid);
+    la.load(ran, rs_a(min(kt + 3, nk - 1)));
+    lb.load(rbn, rs_b(min(kt + 3, nk - 1)));
+    __builtin_amdgcn_sched_barrier(0);
+    u32x4 af[2][TM], bfr[2][TN];
 #pragma unroll
-    for (int kk = 0; kk < BK; kk += TK::KSTEP) {
-      u32x4 af[TM], bfr[TN];
+    for (int i = 0; i < TM; ++i) af[0][i] = ld16(As + (wm * WM + i * 32 + l32) * LDK + g * V);
 #pragma unroll
-      for (int i = 0; i < TM; ++i) af[i] = ld16(As + (wm * WM + i * 32 + l32) * LDK + kk + g * V);
+    for (int j = 0; j < TN; ++j) bfr[0][j] = ld16(Bs + (wn * WN + j * 32 + l32) * LDK + g * V);
 #pragma unroll
-      for (int j = 0; j < TN; ++j) bfr[j] = ld16(Bs + (wn * WN + j * 32 + l32) * LDK + kk + g * V);
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      const int c = ks & 1;
+      if (ks + 1 < KSTEPS) {
+        const int kk = (ks + 1) * TK::KSTEP;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) af[c ^ 1][i] = ld16(As + (wm * WM + i * 32 + l32) * LDK + kk + g * V);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) bfr[c ^ 1][j] = ld16(Bs + (wn * WN + j * 32 + l32) * LDK + kk + g * V);
+      }
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = mfma16(bfr[j], af[i], acc[i][j], (T*)nullptr);
+        for (int j = 0; j < TN; ++j) acc[i][j] = mfma16(bfr[c][j], af[c][i], acc[i][j], (T*)nullptr);
+    }
+    // MFMA / fragment-read interleave: (TM+TN) reads per step spread over its TM*TN MFMAs
+    constexpr int NR = TM + TN, NM = TM * TN, PER = NM / NR > 0 ? NM / NR : 1;
+    __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      if (ks + 1 < KSTEPS) {
+#pragma unroll
+        for (int q = 0; q < NR; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        if (NM > NR * PER) __builtin_amdgcn_sched_group_barrier(0x008, NM - NR * PER, 0);
+      } else {
+        __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
+      }
+    }
+    __syncthreads();
+  };
+  for (int kt = 0; kt < nk; kt += 2) {
+    step(kt, ra1, rb1);   // tile kt+1 sits in set 1
+    if (kt + 1 < nk) step(kt + 1, ra0, rb0);
+  }
+
+  static_assert(4 * 32 * (WN + 4) * sizeof(float) <= sizeof(smem), "epilogue staging must fit the LDS tiles");
+  Epilogue<T, E>::template run<TM, TN, WN>(args, acc, reinterpret_cast<float*>(&smem[0][0]), wave,
+                                             m0 + wm * WM, n0 + wn * WN, lane);
+}
+
+// Writes a wave's (TM*32) x WN accumulator tile through LDS so that global
+// stores are row-contiguous: one 32-row slab at a time, the wave stores its
+// accumulators (lane = row, 4 consecutive columns per register group) into a
+// private [32][WN+4] fp32 region, then reads it back with WN/4 lanes per row
+// and hands each lane 4 consecutive columns: op(m, n, v[4]). The +4 pitch
+// keeps both the slab writes and the row reads free of bank conflicts.
+template <int TM, int TN, int WN, class Op>
+DEV void staged_store(f32x16 (&acc)[TM][TN], float* lds, int wave, int mbase, int nbase, int lane, Op op) {
+  constexpr int P = WN + 4, LPR = WN / 4, RPP = 64 / LPR;
+  const int g = lane >> 5, l32 = lane & 31;
+  float* st = lds + wave * 32 * P;
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk) {
+        float v[4] = {acc[i][j][blk * 4], acc[i][j][blk * 4 + 1], acc[i][j][blk * 4 + 2], acc[i][j][blk * 4 + 3]};
+        store4(st + l32 * P + j * 32 + blk * 8 + g * 4, v);
+      }
+    __syncthreads();
+#pragma unroll
+    for (int r0 = 0; r0 < 32; r0 += RPP) {
+      const int row = r0 + lane / LPR, col = (lane % LPR) * 4;
+      float v[4];
+      load4(st + row * P + col, v);
+      op(mbase + i * 32 + row, nbase + col, v);
     }
     __syncthreads();
   }
-
-  Epilogue<T, E>::run(args, acc, m0 + wm * WM, n0 + wn * WN, l32, g);
 }
-
-// Walks the accumulators of one wave: row m = mbase + i*32 + l32 and
-// columns n = nbase + j*32 + blk*8 + g*4 + {0..3}.
-#define EPI_LOOP(BODY)                                                        \
-  _Pragma("unroll") for (int i = 0; i < TM; ++i) {                            \
-    const int m = mbase + i * 32 + l32;                                        \
-    _Pragma("unroll") for (int j = 0; j < TN; ++j)                            \
-    _Pragma("unroll") for (int blk = 0; blk < 4; ++blk) {                     \
-      const int n = nbase + j * 32 + blk * 8 + g * 4;                          \
-      float v[4] = {acc[i][j][blk * 4 + 0], acc[i][j][blk * 4 + 1],           \
-                    acc[i][j][blk * 4 + 2], acc[i][j][blk * 4 + 3]};          \
-      if (m < a.M && n < a.N) { BODY }                                         \
-    }                                                                          \
-  }
 
 template <typename T>
 struct Epilogue<T, Epi::Store> {
-  template <int TM, int TN>
-  static DEV void run(const GemmArgs& a, f32x16 (&acc)[TM][TN], int mbase, int nbase, int l32, int g) {
+  template <int TM, int TN, int WN>
+  static DEV void run(const GemmArgs& a, f32x16 (&acc)[TM][TN], float* lds, int wave, int mbase, int nbase,
+                      int lane) {
     T* C = reinterpret_cast<T*>(a.C);
-    EPI_LOOP(store4(C + (int64_t)m * a.ldc + n, v);)
+    staged_store<TM, TN, WN>(acc, lds, wave, mbase, nbase, lane, [&](int m, int n, float (&v)[4]) {
+      if (m < a.M && n < a.N) store4(C + (int64_t)m * a.ldc + n, v);
+    });
   }
 };
 
 template <typename T>
 struct Epilogue<T, Epi::Residual> {
-  template <int TM, int TN>
-  static DEV void run(const GemmArgs& a, f32x16 (&acc)[TM][TN], int mbase, int nbase, int l32, int g) {
+  template <int TM, int TN, int WN>
+  static DEV void run(const GemmArgs& a, f32x16 (&acc)[TM][TN], float* lds, int wave, int mbase, int nbase,
+                      int lane) {
     T* C = reinterpret_cast<T*>(a.C);
-    EPI_LOOP({
-      float x[4];
-      load4(C + (int64_t)m * a.ldc + n, x);
-      for (int r = 0; r < 4; ++r) x[r] += v[r];
-      store4(C + (int64_t)m * a.ldc + n, x);
-    })
+    staged_store<TM, TN, WN>(acc, lds, wave, mbase, nbase, lane, [&](int m, int n, float (&v)[4]) {
+      if (m < a.M && n < a.N) {
+        float x[4];
+        load4(C + (int64_t)m * a.ldc + n, x);
+        for (int r = 0; r < 4; ++r) x[r] += v[r];
+        store4(C + (int64_t)m * a.ldc + n, x);
+      }
+    });
   }
 };
 
 // relu^2 MLP activation (aethryn.com, section "A Llama-class transformer with
-// ten modern departures"): stores u and a = max(u, 0)^2.
+// ten modern departures"): stores a = max(u, 0)^2 only; the backward recovers
+// max(u, 0) as sqrt(a).
 template <typename T>
 struct Epilogue<T, Epi::Relu2> {
-  template <int TM, int TN>
-  static DEV void run(const GemmArgs& a, f32x16 (&acc)[TM][TN], int mbase, int nbase, int l32, int g) {
-    T* U = reinterpret_cast<T*>(a.C);
-    T* A2 = reinterpret_cast<T*>(a.C2);
-    EPI_LOOP({
-      float s[4];
-      for (int r = 0; r < 4; ++r) { float p = fmaxf(v[r], 0.f); s[r] = p * p; }
-      store4(U + (int64_t)m * a.ldc + n, v);
-      store4(A2 + (int64_t)m * a.ldc2 + n, s);
-    })
+  template <int TM, int TN, int WN>
+  static DEV void run(const GemmArgs& a, f32x16 (&acc)[TM][TN], float* lds, int wave, int mbase, int nbase,
+                      int lane) {
+    T* A2 = reinterpret_cast<T*>(a.C);
+    staged_store<TM, TN, WN>(acc, lds, wave, mbase, nbase, lane, [&](int m, int n, float (&v)[4]) {
+      if (m < a.M && n < a.N) {
+        float s[4];
+        for (int r = 0; r < 4; ++r) { const float p = fmaxf(v[r], 0.f); s[r] = p * p; }
+        store4(A2 + (int64_t)m * a.ldc + n, s);
+      }
+    });
   }
 };
 
-// du = da * 2 max(u, 0)
+// du = da * 2 max(u, 0) = da * 2 sqrt(a), with a = max(u, 0)^2 read from C2
 template <typename T>
 struct Epilogue<T, Epi::Relu2Bwd> {
-  template <int TM, int TN>
-  static DEV void run(const GemmArgs& a, f32x16 (&acc)[TM][TN], int mbase, int nbase, int l32, int g) {
-    T* D = reinterpret_cast<T*>(a.C);
-    const T* U = reinterpret_cast<const T*>(a.C2);
-    EPI_LOOP({
-      float u[4];
-      load4(U + (int64_t)m * a.ldc2 + n, u);
-      for (int r = 0; r < 4; ++r) v[r] *= 2.f * fmaxf(u[r], 0.f);
-      store4(D + (int64_t)m * a.ldc + n, v);
-    })
+  template <int TM, int TN, int WN>
+  static DEV void run(const GemmArgs& a, f32x16 (&acc)[TM][TN], float* lds, int wave, int mbase, int nbase,
+                      int lane) {
+    T* Dp = reinterpret_cast<T*>(a.C);
+    const T* A2 = reinterpret_cast<const T*>(a.C2);
+    staged_store<TM, TN, WN>(acc, lds, wave, mbase, nbase, lane, [&](int m, int n, float (&v)[4]) {
+      if (m < a.M && n < a.N) {
+        float x[4];
+        load4(A2 + (int64_t)m * a.ldc2 + n, x);
+        for (int r = 0; r < 4; ++r) v[r] *= 2.f * sqrtf(x[r]);
+        store4(Dp + (int64_t)m * a.ldc + n, v);
+      }
+    });
   }
 };
 
@@ -290,63 +386,60 @@ struct Epilogue<T, Epi::Relu2Bwd> {
 // departures": softcap 15, in float32). Emits the capped logits in the
 // activation dtype, one fp32 partial sum of exp(z' - c) per row and 128
 // columns (terms lie in (e^-2c, 1], so partial sums add without rescaling),
-// and the fp32 capped logit at the row's target.
+// and the fp32 capped logit at the row's target. Done on the staged rows: a
+// row's 128 wave columns sit in 32 lanes (4 each), reduced with shuffles.
 template <typename T>
 struct Epilogue<T, Epi::LMHead> {
-  template <int TM, int TN>
-  static DEV void run(const GemmArgs& a, f32x16 (&acc)[TM][TN], int mbase, int nbase, int l32, int g) {
-    static_assert(TN * 32 == kLMHeadPartCols, "one partial per wave column");
-    T* Z = reinterpret_cast<T*>(a.C);
+  template <int TM, int TN, int WN>
+  static DEV void run(const GemmArgs& a, f32x16 (&acc)[TM][TN], float* lds, int wave, int mbase, int nbase,
+                      int lane) {
+    static_assert(WN == kLMHeadPartCols, "one partial per wave column block");
     const float c = a.softcap, inv_c = 1.f / a.softcap;
     const int nparts = a.N / kLMHeadPartCols;
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int m = mbase + i * 32 + l32;
+    T* Z = reinterpret_cast<T*>(a.C);
+    staged_store<TM, TN, WN>(acc, lds, wave, mbase, nbase, lane, [&](int m, int n, float (&v)[4]) {
       const bool mv = m < a.M;
       const int tgt = mv ? a.targets[m] : -1;
-      float s = 0.f;
+      float sum = 0.f;
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
+      for (int r = 0; r < 4; ++r) {
+        v[r] = c * tanhf(v[r] * inv_c);
+        sum += __expf(v[r] - c);
+      }
+      const unsigned d = (unsigned)(tgt - n);
+      if (d < 4u) a.ztgt[m] = v[d];
+      if (mv) store4(Z + (int64_t)m * a.ldc + n, v);
 #pragma unroll
-        for (int blk = 0; blk < 4; ++blk) {
-          const int n = nbase + j * 32 + blk * 8 + g * 4;
-          float z[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            z[r] = c * tanhf(acc[i][j][blk * 4 + r] * inv_c);
-            s += __expf(z[r] - c);
-          }
-          if (mv) {
-            store4(Z + (int64_t)m * a.ldc + n, z);
-            const unsigned d = (unsigned)(tgt - n);
-            if (d < 4u) a.ztgt[m] = z[d];
-          }
-        }
-      s += __shfl_xor(s, 32, 64);
-      if (mv && g == 0) a.part[(int64_t)m * nparts + nbase / kLMHeadPartCols] = s;
-    }
+      for (int o = 16; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 32);
+      if (mv && (lane & 31) == 0) a.part[(int64_t)m * nparts + nbase / kLMHeadPartCols] = sum;
+    });
   }
 };
 
 template <typename T>
 struct Epilogue<T, Epi::GradF32> {
-  template <int TM, int TN>
-  static DEV void run(const GemmArgs& a, f32x16 (&acc)[TM][TN], int mbase, int nbase, int l32, int g) {
+  template <int TM, int TN, int WN>
+  static DEV void run(const GemmArgs& a, f32x16 (&acc)[TM][TN], float* lds, int wave, int mbase, int nbase,
+                      int lane) {
     if (a.splits > 1) {
       float* P = a.split_buf + (int64_t)blockIdx.z * a.M * a.N;
-      EPI_LOOP(store4(P + (int64_t)m * a.N + n, v);)
+      staged_store<TM, TN, WN>(acc, lds, wave, mbase, nbase, lane, [&](int m, int n, float (&v)[4]) {
+        if (m < a.M && n < a.N) store4(P + (int64_t)m * a.N + n, v);
+      });
     } else {
       float* G = reinterpret_cast<float*>(a.C);
       const bool accum = a.accumulate != 0;
-      EPI_LOOP({
-        float* p = G + (int64_t)m * a.ldc + n;
-        if (accum) {
-          float x[4];
-          load4(p, x);
-          for (int r = 0; r < 4; ++r) v[r] += x[r];
+      staged_store<TM, TN, WN>(acc, lds, wave, mbase, nbase, lane, [&](int m, int n, float (&v)[4]) {
+        if (m < a.M && n < a.N) {
+          float* p = G + (int64_t)m * a.ldc + n;
+          if (accum) {
+            float x[4];
+            load4(p, x);
+            for (int r = 0; r < 4; ++r) v[r] += x[r];
+          }
+          store4(p, v);
         }
-        store4(p, v);
-      })
+      });
     }
   }
 };

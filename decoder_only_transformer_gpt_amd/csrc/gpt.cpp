@@ -64,8 +64,9 @@ const char* kTagNames[K_NUM_TAGS] = {
 struct Layout {  // byte offsets inside the workspace
   size_t flag, loss_rows, rope_cos, rope_sin;
   size_t x, rstd0, hf, rstdf, logits, part, ztgt, lse_ce;
-  std::vector<size_t> h1, rstd1, qkv, rstd_qk, o, lse, h2, rstd2, u, a;
+  std::vector<size_t> h1, rstd1, qkv, rstd_qk, o, lse, h2, rstd2, a;
   size_t dres, dres_lp, dh, du, dqkv, dout, delta, split;
+  size_t qT, kT, vT, doT;  // attention's transposed copies [B, heads, 128, Tp]
   size_t keys_a, vals_a, keys_b, vals_b, hist, coef, carry;
   size_t total;
   size_t split_elems;
@@ -112,7 +113,6 @@ Layout plan(const gpt_config& c, int maxB, int maxT) {
     L.lse.push_back(p.take(N * H * 4));
     L.h2.push_back(p.take(N * C * es));
     L.rstd2.push_back(p.take(N * 4));
-    L.u.push_back(p.take(N * F * es));
     L.a.push_back(p.take(N * F * es));
   }
   L.hf = p.take(N * C * es);
@@ -128,6 +128,13 @@ Layout plan(const gpt_config& c, int maxB, int maxT) {
   L.dqkv = p.take(N * QKV * es);
   L.dout = p.take(N * H * kHeadDim * es);
   L.delta = p.take(N * H * 4);
+  {
+    const size_t Tp = (size_t)gk::attn_padded_len(maxT), BT = (size_t)maxB * Tp * kHeadDim;
+    L.qT = p.take(BT * H * es);
+    L.doT = p.take(BT * H * es);
+    L.kT = p.take(BT * es);
+    L.vT = p.take(BT * es);
+  }
   // split-K partial buffer: largest splits*M*N over the per-layer dW GEMMs
   size_t se = 0;
   const int K = (int)N;
@@ -433,7 +440,7 @@ gpt_status gpt_forward_loss(gpt_model* m, const int32_t* idx, const int32_t* tar
                                                      wsp<float>(m, L.rope_cos), wsp<float>(m, L.rope_sin),
                                                      wsp<float>(m, L.rstd_qk[l]), stream););
     RUN(K_ATTN_FWD, return gk::launch_attn_fwd(dt, m->ws + L.qkv[l], B, T, H, m->ws + L.o[l],
-                                               wsp<float>(m, L.lse[l]), stream););
+                                               wsp<float>(m, L.lse[l]), m->ws + L.vT, stream););
     RUN(K_GEMM_O, {
       gk::GemmArgs a;
       a.A = m->ws + L.o[l]; a.lda = HD;
@@ -449,8 +456,7 @@ gpt_status gpt_forward_loss(gpt_model* m, const int32_t* idx, const int32_t* tar
       a.A = m->ws + L.h2[l]; a.lda = C;
       a.B = pbase(m, m->off_w1[l]); a.ldb = C;
       a.M = N; a.N = F; a.K = C;
-      a.C = m->ws + L.u[l]; a.ldc = F;
-      a.C2 = m->ws + L.a[l]; a.ldc2 = F;
+      a.C = m->ws + L.a[l]; a.ldc = F;
       return gk::launch_gemm(dt, gk::Epi::Relu2, a, stream);
     });
     RUN(K_GEMM_W2, {
@@ -539,7 +545,7 @@ gpt_status gpt_backward(gpt_model* m, float dloss, int32_t accumulate, void* str
     // MLP
     TRY(dw(K_GEMM_W2_DW, m->ws + L.dres_lp, C, m->ws + L.a[l], F, C, F, m->off_w2[l]));
     TRY(dx(K_GEMM_W2_DX, gk::Epi::Relu2Bwd, m->ws + L.dres_lp, C, pbase(m, m->off_w2[l]), F, F, C, m->ws + L.du,
-           m->ws + L.u[l]));
+           m->ws + L.a[l]));
     TRY(dw(K_GEMM_W1_DW, m->ws + L.du, F, m->ws + L.h2[l], C, F, C, m->off_w1[l]));
     TRY(dx(K_GEMM_W1_DX, gk::Epi::Store, m->ws + L.du, F, pbase(m, m->off_w1[l]), C, C, F, m->ws + L.dh, nullptr));
     RUN(K_RMSNORM_BWD, return gk::launch_rmsnorm_bwd(dt, m->ws + L.dh, m->ws + L.h2[l], wsp<float>(m, L.rstd2[l]),
@@ -548,9 +554,20 @@ gpt_status gpt_backward(gpt_model* m, float dloss, int32_t accumulate, void* str
     TRY(dw(K_GEMM_O_DW, m->ws + L.dres_lp, C, m->ws + L.o[l], HD, C, HD, m->off_o[l]));
     TRY(dx(K_GEMM_O_DX, gk::Epi::Store, m->ws + L.dres_lp, C, pbase(m, m->off_o[l]), HD, HD, C, m->ws + L.dout,
            nullptr));
-    RUN(K_ATTN_BWD, return gk::launch_attn_bwd(dt, m->ws + L.qkv[l], m->ws + L.o[l], m->ws + L.dout,
-                                               wsp<float>(m, L.lse[l]), B, T, H, wsp<float>(m, L.delta),
-                                               m->ws + L.dqkv, stream););
+    RUN(K_ATTN_BWD, {
+      gk::AttnBwdArgs a;
+      a.qkv = m->ws + L.qkv[l];
+      a.o = m->ws + L.o[l];
+      a.dout = m->ws + L.dout;
+      a.lse = wsp<float>(m, L.lse[l]);
+      a.B = B; a.T = T; a.H = H;
+      a.delta = wsp<float>(m, L.delta);
+      a.qT = m->ws + L.qT;
+      a.kT = m->ws + L.kT;
+      a.doT = m->ws + L.doT;
+      a.dqkv = m->ws + L.dqkv;
+      return gk::launch_attn_bwd(dt, a, stream);
+    });
     RUN(K_ROPE_QKNORM_BWD, return gk::launch_rope_qknorm_bwd(dt, m->ws + L.dqkv, m->ws + L.qkv[l],
                                                              wsp<float>(m, L.rstd_qk[l]), B, T, H,
                                                              wsp<float>(m, L.rope_cos), wsp<float>(m, L.rope_sin),
@@ -650,7 +667,6 @@ gpt_status gpt_debug_buffer(gpt_model* m, const char* name, int32_t layer, void*
   if (s == "o") return set(L.o[layer], N * H * kHeadDim * es);
   if (s == "lse") return set(L.lse[layer], N * H * 4);
   if (s == "h2") return set(L.h2[layer], N * C * es);
-  if (s == "u") return set(L.u[layer], N * (size_t)c.mlp_dim * es);
   if (s == "a") return set(L.a[layer], N * (size_t)c.mlp_dim * es);
   return fail(GPT_E_INVALID_ARG, "unknown buffer '%s'", name);
 }

@@ -9,9 +9,9 @@ namespace gk {
 enum class Epi : int {
   Store = 0,     // C = acc (activation dtype)
   Residual = 1,  // C += acc in place (the residual stream)
-  Relu2 = 2,     // C = acc (u), C2 = max(acc, 0)^2 (a)
+  Relu2 = 2,     // C = max(acc, 0)^2 (a); the backward recovers max(u, 0) = sqrt(a)
   LMHead = 3,    // C = c*tanh(acc/c) (logits), exp-sum partials, logit at target
-  Relu2Bwd = 4,  // C = acc * 2*max(u, 0) with u read from C2
+  Relu2Bwd = 4,  // C = acc * 2*sqrt(a) with a = max(u, 0)^2 read from C2
   GradF32 = 5,   // fp32 gradient: C = acc or C += acc; split-K writes partials
 };
 
@@ -58,10 +58,24 @@ hipError_t launch_rope_qknorm_bwd(int dtype, void* dqkv, const void* qkv, const 
                                   int T, int H, const float* cos_t, const float* sin_t, hipStream_t s);
 
 // Attention (causal, multi-query, head_dim 128) ----------------------------
-hipError_t launch_attn_fwd(int dtype, const void* qkv, int B, int T, int H, void* o, float* lse,
+// Transposed copies use [B, heads, 128, Tp] with Tp = attn_padded_len(T).
+int attn_padded_len(int T);
+// vT: scratch of B * 128 * Tp elements.
+hipError_t launch_attn_fwd(int dtype, const void* qkv, int B, int T, int H, void* o, float* lse, void* vT,
                            hipStream_t s);
-hipError_t launch_attn_bwd(int dtype, const void* qkv, const void* o, const void* dout, const float* lse,
-                           int B, int T, int H, float* delta, void* dqkv, hipStream_t s);
+struct AttnBwdArgs {
+  const void* qkv;   // [N, (H+2)*128] normalised q, k and v
+  const void* o;     // [N, H*128]
+  const void* dout;  // [N, H*128]
+  const float* lse;  // [B, H, T]
+  int B, T, H;
+  float* delta;      // [B, H, T] scratch
+  void* qT;          // [B, H, 128, Tp] scratch
+  void* kT;          // [B, 1, 128, Tp] scratch
+  void* doT;         // [B, H, 128, Tp] scratch
+  void* dqkv;        // [N, (H+2)*128] output
+};
+hipError_t launch_attn_bwd(int dtype, const AttnBwdArgs& a, hipStream_t s);
 
 // Cross-entropy -------------------------------------------------------------
 hipError_t launch_ce_loss(const float* part, int nparts, const float* ztgt, const int32_t* targets, int N,

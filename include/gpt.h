@@ -133,8 +133,10 @@ gpt_status gpt_init(const gpt_config* cfg, const void* params, float* grads, voi
  * idx, targets: device int32 [B, T] row-major; targets are the next tokens,
  * each in [0, V). loss: device fp32 scalar. row_loss: optional device fp32
  * [B*T] per-position losses (may be NULL). need_grad = 1 keeps the stash that
- * gpt_backward consumes. An id outside [0, V) sets the sticky device flag
- * (read by gpt_sync_status) and makes the loss NaN. Asynchronous. */
+ * gpt_backward consumes; idx and targets must then stay valid until that
+ * gpt_backward has run (it reads them again). An id outside [0, V) sets the
+ * sticky device flag (read by gpt_sync_status) and makes the loss NaN.
+ * Asynchronous. */
 gpt_status gpt_forward_loss(gpt_model* m, const int32_t* idx, const int32_t* targets, int32_t B,
                             int32_t T, int32_t need_grad, float* loss, float* row_loss, void* stream);
 
@@ -163,7 +165,7 @@ gpt_status gpt_profile_end(gpt_model* m, double* total_ms, int64_t* launches);
 const char* gpt_kernel_tag_name(int32_t tag);
 
 /* Debug access to a stashed activation of the last forward: device pointer and
- * byte size of the named buffer ("x", "h1", "qkv", "o", "lse", "h2", "u", "a",
+ * byte size of the named buffer ("x", "h1", "qkv", "o", "lse", "h2", "a",
  * "hf", "logits", "rstd0") for `layer` (ignored by non-layer buffers). The
  * pointer aliases the workspace and is valid until the next call. */
 gpt_status gpt_debug_buffer(gpt_model* m, const char* name, int32_t layer, void** ptr, size_t* bytes);
