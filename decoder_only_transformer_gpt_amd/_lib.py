@@ -22,6 +22,7 @@ GPT_E_HIP = -5
 GPT_E_DEVICE = -6
 GPT_F32 = 0
 GPT_BF16 = 1
+GPT_OPT_GEMM_TILE = 1
 
 
 class gpt_config(ctypes.Structure):
@@ -71,6 +72,7 @@ _SIGS = {
     "gpt_profile_begin": (ctypes.c_int32, [_P, ctypes.c_int32]),
     "gpt_profile_end": (ctypes.c_int32, [_P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]),
     "gpt_kernel_tag_name": (ctypes.c_char_p, [ctypes.c_int32]),
+    "gpt_set_option": (ctypes.c_int32, [_P, ctypes.c_int32, ctypes.c_int32]),
     "gpt_debug_buffer": (ctypes.c_int32, [_P, ctypes.c_char_p, ctypes.c_int32, ctypes.POINTER(_P),
                                           ctypes.POINTER(ctypes.c_size_t)]),
 }
@@ -183,6 +185,10 @@ def gpt_profile_end(h):
     ms, n = ctypes.c_double(0), ctypes.c_int64(0)
     _check(lib().gpt_profile_end(h, ctypes.byref(ms), ctypes.byref(n)), "gpt_profile_end")
     return ms.value, n.value
+
+
+def gpt_set_option(h, option: int, value: int):
+    _check(lib().gpt_set_option(h, option, value), "gpt_set_option")
 
 
 def gpt_debug_buffer(h, name: str, layer: int = 0):

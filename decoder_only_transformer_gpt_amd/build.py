@@ -48,6 +48,11 @@ def build(verbose: bool = True) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
+    # a kernel whose host stub was silently not emitted would only fail at load time
+    nm = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True)
+    missing = [ln.split()[-1] for ln in nm.stdout.splitlines() if "device_stub" in ln]
+    if missing:
+        raise RuntimeError(f"kernel stubs missing from {tmp}: {missing[:4]}")
     os.replace(tmp, OUT)
     if verbose:
         print(f"built {OUT}")

@@ -278,7 +278,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs args) {
   }
 
   static_assert(4 * 32 * (WN + 4) * sizeof(float) <= sizeof(smem), "epilogue staging must fit the LDS tiles");
-  Epilogue<T, E>::template run<TM, TN, WN>(args, acc, reinterpret_cast<float*>(&smem[0][0]), wave,
+  Epilogue<T, E>::template run<TM, TN, WN>(args, acc, reinterpret_cast<float*>(&smem[0][0]) + wave * 32 * (WN + 4),
                                              m0 + wm * WM, n0 + wn * WN, lane);
 }
 
@@ -289,10 +289,9 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs args) {
 // and hands each lane 4 consecutive columns: op(m, n, v[4]). The +4 pitch
 // keeps both the slab writes and the row reads free of bank conflicts.
 template <int TM, int TN, int WN, class Op>
-DEV void staged_store(f32x16 (&acc)[TM][TN], float* lds, int wave, int mbase, int nbase, int lane, Op op) {
+DEV void staged_store(f32x16 (&acc)[TM][TN], float* st, int mbase, int nbase, int lane, Op op) {
   constexpr int P = WN + 4, LPR = WN / 4, RPP = 64 / LPR;
   const int g = lane >> 5, l32 = lane & 31;
-  float* st = lds + wave * 32 * P;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -317,10 +316,9 @@ DEV void staged_store(f32x16 (&acc)[TM][TN], float* lds, int wave, int mbase, in
 template <typename T>
 struct Epilogue<T, Epi::Store> {
   template <int TM, int TN, int WN>
-  static DEV void run(const GemmArgs& a, f32x16 (&acc)[TM][TN], float* lds, int wave, int mbase, int nbase,
-                      int lane) {
+  static DEV void run(const GemmArgs& a, f32x16 (&acc)[TM][TN], float* lds, int mbase, int nbase, int lane) {
     T* C = reinterpret_cast<T*>(a.C);
-    staged_store<TM, TN, WN>(acc, lds, wave, mbase, nbase, lane, [&](int m, int n, float (&v)[4]) {
+    staged_store<TM, TN, WN>(acc, lds, mbase, nbase, lane, [&](int m, int n, float (&v)[4]) {
       if (m < a.M && n < a.N) store4(C + (int64_t)m * a.ldc + n, v);
     });
   }
@@ -329,10 +327,9 @@ struct Epilogue<T, Epi::Store> {
 template <typename T>
 struct Epilogue<T, Epi::Residual> {
   template <int TM, int TN, int WN>
-  static DEV void run(const GemmArgs& a, f32x16 (&acc)[TM][TN], float* lds, int wave, int mbase, int nbase,
-                      int lane) {
+  static DEV void run(const GemmArgs& a, f32x16 (&acc)[TM][TN], float* lds, int mbase, int nbase, int lane) {
     T* C = reinterpret_cast<T*>(a.C);
-    staged_store<TM, TN, WN>(acc, lds, wave, mbase, nbase, lane, [&](int m, int n, float (&v)[4]) {
+    staged_store<TM, TN, WN>(acc, lds, mbase, nbase, lane, [&](int m, int n, float (&v)[4]) {
       if (m < a.M && n < a.N) {
         float x[4];
         load4(C + (int64_t)m * a.ldc + n, x);
@@ -349,10 +346,9 @@ struct Epilogue<T, Epi::Residual> {
 template <typename T>
 struct Epilogue<T, Epi::Relu2> {
   template <int TM, int TN, int WN>
-  static DEV void run(const GemmArgs& a, f32x16 (&acc)[TM][TN], float* lds, int wave, int mbase, int nbase,
-                      int lane) {
+  static DEV void run(const GemmArgs& a, f32x16 (&acc)[TM][TN], float* lds, int mbase, int nbase, int lane) {
     T* A2 = reinterpret_cast<T*>(a.C);
-    staged_store<TM, TN, WN>(acc, lds, wave, mbase, nbase, lane, [&](int m, int n, float (&v)[4]) {
+    staged_store<TM, TN, WN>(acc, lds, mbase, nbase, lane, [&](int m, int n, float (&v)[4]) {
       if (m < a.M && n < a.N) {
         float s[4];
         for (int r = 0; r < 4; ++r) { const float p = fmaxf(v[r], 0.f); s[r] = p * p; }
@@ -366,11 +362,10 @@ struct Epilogue<T, Epi::Relu2> {
 template <typename T>
 struct Epilogue<T, Epi::Relu2Bwd> {
   template <int TM, int TN, int WN>
-  static DEV void run(const GemmArgs& a, f32x16 (&acc)[TM][TN], float* lds, int wave, int mbase, int nbase,
-                      int lane) {
+  static DEV void run(const GemmArgs& a, f32x16 (&acc)[TM][TN], float* lds, int mbase, int nbase, int lane) {
     T* Dp = reinterpret_cast<T*>(a.C);
     const T* A2 = reinterpret_cast<const T*>(a.C2);
-    staged_store<TM, TN, WN>(acc, lds, wave, mbase, nbase, lane, [&](int m, int n, float (&v)[4]) {
+    staged_store<TM, TN, WN>(acc, lds, mbase, nbase, lane, [&](int m, int n, float (&v)[4]) {
       if (m < a.M && n < a.N) {
         float x[4];
         load4(A2 + (int64_t)m * a.ldc2 + n, x);
@@ -391,13 +386,12 @@ struct Epilogue<T, Epi::Relu2Bwd> {
 template <typename T>
 struct Epilogue<T, Epi::LMHead> {
   template <int TM, int TN, int WN>
-  static DEV void run(const GemmArgs& a, f32x16 (&acc)[TM][TN], float* lds, int wave, int mbase, int nbase,
-                      int lane) {
+  static DEV void run(const GemmArgs& a, f32x16 (&acc)[TM][TN], float* lds, int mbase, int nbase, int lane) {
     static_assert(WN == kLMHeadPartCols, "one partial per wave column block");
     const float c = a.softcap, inv_c = 1.f / a.softcap;
     const int nparts = a.N / kLMHeadPartCols;
     T* Z = reinterpret_cast<T*>(a.C);
-    staged_store<TM, TN, WN>(acc, lds, wave, mbase, nbase, lane, [&](int m, int n, float (&v)[4]) {
+    staged_store<TM, TN, WN>(acc, lds, mbase, nbase, lane, [&](int m, int n, float (&v)[4]) {
       const bool mv = m < a.M;
       const int tgt = mv ? a.targets[m] : -1;
       float sum = 0.f;
@@ -419,17 +413,16 @@ struct Epilogue<T, Epi::LMHead> {
 template <typename T>
 struct Epilogue<T, Epi::GradF32> {
   template <int TM, int TN, int WN>
-  static DEV void run(const GemmArgs& a, f32x16 (&acc)[TM][TN], float* lds, int wave, int mbase, int nbase,
-                      int lane) {
+  static DEV void run(const GemmArgs& a, f32x16 (&acc)[TM][TN], float* lds, int mbase, int nbase, int lane) {
     if (a.splits > 1) {
       float* P = a.split_buf + (int64_t)blockIdx.z * a.M * a.N;
-      staged_store<TM, TN, WN>(acc, lds, wave, mbase, nbase, lane, [&](int m, int n, float (&v)[4]) {
+      staged_store<TM, TN, WN>(acc, lds, mbase, nbase, lane, [&](int m, int n, float (&v)[4]) {
         if (m < a.M && n < a.N) store4(P + (int64_t)m * a.N + n, v);
       });
     } else {
       float* G = reinterpret_cast<float*>(a.C);
       const bool accum = a.accumulate != 0;
-      staged_store<TM, TN, WN>(acc, lds, wave, mbase, nbase, lane, [&](int m, int n, float (&v)[4]) {
+      staged_store<TM, TN, WN>(acc, lds, mbase, nbase, lane, [&](int m, int n, float (&v)[4]) {
         if (m < a.M && n < a.N) {
           float* p = G + (int64_t)m * a.ldc + n;
           if (accum) {
@@ -443,6 +436,173 @@ struct Epilogue<T, Epi::GradF32> {
     }
   }
 };
+
+// 16-byte direct-to-LDS buffer load: lane L of the wave writes LDS bytes
+// [lds + 16L, lds + 16L + 16) (lds must be wave-uniform). The address-space
+// cast only exists in the device pass.
+DEV void lds_direct16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
+#endif
+}
+
+// bf16 GEMM with both operands k-contiguous (y = x W^T and, with a
+// transposed weight copy, dx = dy W), fed by direct-to-LDS buffer loads.
+//
+// K tiles are 32 wide (64-byte rows) and live in NSTAGE LDS stages; tile kt+3
+// is in flight while tile kt is consumed, so each global load has three tiles
+// of MFMA work to land. A wave's buffer_load ... lds writes 1 KiB contiguous
+// (lane L at +16L), i.e. 16 rows of 64 bytes; each lane picks the global 16-byte
+// chunk it fetches so that chunk c of row r lands at position c ^ ((r>>1)&3).
+// The MFMA fragment reads (32 rows, one chunk) then hit 8 distinct 4-bank
+// groups per 8 lanes: conflict-free without padding. Rows past M read as zero
+// (buffer record count). One explicit vmcnt wait and one barrier per K tile.
+template <int BM, int BN, int NSTAGE, int OCC, Epi E>
+__global__ __launch_bounds__(kThreads, OCC) void gemm_nt_lds_kernel(GemmArgs args) {
+  using T = bf16;
+  constexpr int BK = 32, ROWB = BK * 2;
+  constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
+  constexpr int STAGE = (BM + BN) * ROWB;                  // bytes per stage
+  constexpr int LA = BM * ROWB / 1024 / 4, LB = BN * ROWB / 1024 / 4;  // 1 KiB loads per wave per tile
+  constexpr int NLOAD = LA + LB;
+  static_assert(LA >= 1 && LB >= 1, "tile too small for 4 waves");
+  // one array per stage, so the compiler can tell the stages' LDS-direct
+  // loads apart and wait only for the oldest tile
+  __shared__ __attribute__((aligned(1024))) char st0[STAGE];
+  __shared__ __attribute__((aligned(1024))) char st1[STAGE];
+  __shared__ __attribute__((aligned(1024))) char st2[STAGE];
+  __shared__ __attribute__((aligned(1024))) char st3[NSTAGE == 4 ? STAGE : 1024];
+  static_assert(NSTAGE == 3 || NSTAGE == 4, "three or four stage arrays");
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
+  const int wm = wave >> 1, wn = wave & 1, g = lane >> 5, l32 = lane & 31;
+  const int M = args.M, N = args.N, K = args.K;
+  const int tiles_n = (N + BN - 1) / BN;
+  int bid = blockIdx.x;
+  const int nb = gridDim.x;
+  if ((nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
+  const int m0 = (bid / tiles_n) * BM, n0 = (bid % tiles_n) * BN;
+  const int nk = K / BK;
+  const T* Ap = reinterpret_cast<const T*>(args.A) + (int64_t)m0 * args.lda;
+  const T* Bp = reinterpret_cast<const T*>(args.B) + (int64_t)n0 * args.ldb;
+  const uint32_t lda_b = (uint32_t)(args.lda * 2), ldb_b = (uint32_t)(args.ldb * 2);
+  // record counts (bytes from the tile's first row), clamped to 1 GiB; plain
+  // integer ternaries (a templated 64-bit min() would go through f64 VALU
+  // math and make the resource look divergent)
+  const int64_t ra64 = (int64_t)(M - m0 < BM ? M - m0 : BM) * lda_b;
+  const int64_t rb64 = (int64_t)(N - n0 < BN ? N - n0 : BN) * ldb_b;
+  const int rec_a = ra64 > (1 << 30) ? (1 << 30) : (int)ra64;
+  const int rec_b = rb64 > (1 << 30) ? (1 << 30) : (int)rb64;
+
+  // per-lane global byte offsets of this wave's 1 KiB slots (16 rows each)
+  const int lrow = lane >> 2, lpos = lane & 3;
+  const uint32_t lchunk = (uint32_t)(lpos ^ ((lrow >> 1) & 3));
+  uint32_t voa[LA], vob[LB];
+#pragma unroll
+  for (int i = 0; i < LA; ++i) voa[i] = (uint32_t)((wave * LA + i) * 16 + lrow) * lda_b + lchunk * 16u;
+#pragma unroll
+  for (int i = 0; i < LB; ++i) vob[i] = (uint32_t)((wave * LB + i) * 16 + lrow) * ldb_b + lchunk * 16u;
+
+  // buffer resources must be wave-uniform (SGPRs): build them from
+  // readfirstlane'd pointer halves and record counts
+  auto uni_rsrc = [](const void* p, int rec) {
+    const uint64_t v = (uint64_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    const int n = __builtin_amdgcn_readfirstlane(rec);
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), (short)0, n, 0x00020000);
+  };
+  auto stage = [&](int q) -> char* { return q == 0 ? st0 : q == 1 ? st1 : q == 2 ? st2 : st3; };
+  auto issue = [&](int kt, char* st) {
+    const int k0 = kt * BK;
+    const __amdgpu_buffer_rsrc_t ra = uni_rsrc(Ap + k0, rec_a);
+    const __amdgpu_buffer_rsrc_t rb = uni_rsrc(Bp + k0, rec_b);
+#pragma unroll
+    for (int i = 0; i < LA; ++i)
+      lds_direct16(ra, st + (wave * LA + i) * 1024, voa[i]);
+#pragma unroll
+    for (int i = 0; i < LB; ++i)
+      lds_direct16(rb, st + BM * ROWB + (wave * LB + i) * 1024, vob[i]);
+  };
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  // fragment byte offsets inside a stage for k-step 0 / 1 (row l32 of a 32-row block)
+  const int swz = (l32 >> 1) & 3;
+  const int fo0 = l32 * ROWB + ((0 * 2 + g) ^ swz) * 16, fo1 = l32 * ROWB + ((1 * 2 + g) ^ swz) * 16;
+
+  issue(0, st0);
+  issue(min(1, nk - 1), st1);
+  if (NSTAGE == 4) issue(min(2, nk - 1), st2);
+  // tile kt sits in stage kt % 4; the loop is unrolled by four so every
+  // stage is a distinct, statically known LDS object
+  auto tile = [&](int kt, const char* cur, char* nxt) {
+    // tile kt's loads are the oldest outstanding: wait until only the
+    // NSTAGE-2 younger tiles' loads remain, then make everyone's visible
+    // (a bare s_barrier: __syncthreads' release fence would wait for every
+    // outstanding LDS-direct load, including the younger tiles')
+    constexpr int YOUNG = NLOAD * (NSTAGE - 2);
+    __builtin_amdgcn_s_waitcnt(((YOUNG >> 4) << 14) | (0x7 << 4) | (0xF << 8) | (YOUNG & 15));
+    __builtin_amdgcn_s_barrier();
+    issue(min(kt + NSTAGE - 1, nk - 1), nxt);  // into the stage freed by tile kt-1 (past the end: harmless re-read)
+    const char* As = cur + wm * WM * ROWB;
+    const char* Bs = cur + BM * ROWB + wn * WN * ROWB;
+    u32x4 af[2][TM], bfr[2][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) af[0][i] = ld16(As + i * 32 * ROWB + fo0);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) bfr[0][j] = ld16(Bs + j * 32 * ROWB + fo0);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) af[1][i] = ld16(As + i * 32 * ROWB + fo1);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) bfr[1][j] = ld16(Bs + j * 32 * ROWB + fo1);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = mfma16(bfr[ks][j], af[ks][i], acc[i][j], (T*)nullptr);
+    constexpr int NR = TM + TN, NM = TM * TN, PER = NM / NR > 0 ? NM / NR : 1;
+    __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+#pragma unroll
+    for (int q = 0; q < NR; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * NM - NR * PER, 0);
+  };
+  if constexpr (NSTAGE == 4) {
+    for (int kt = 0; kt < nk; kt += 4) {
+      tile(kt, st0, st3);
+      if (kt + 1 < nk) tile(kt + 1, st1, st0);
+      if (kt + 2 < nk) tile(kt + 2, st2, st1);
+      if (kt + 3 < nk) tile(kt + 3, st3, st2);
+    }
+  } else {
+    for (int kt = 0; kt < nk; kt += 3) {
+      tile(kt, st0, st2);
+      if (kt + 1 < nk) tile(kt + 1, st1, st0);
+      if (kt + 2 < nk) tile(kt + 2, st2, st1);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // no LDS-direct load may land during the epilogue
+  __syncthreads();
+  // each wave stages its 32-row slabs in a private region: two waves per
+  // stage when two slabs fit, else one stage per wave (needs 4 stages)
+  constexpr int SLAB = 32 * (WN + 4) * (int)sizeof(float);
+  constexpr bool TWO = 2 * SLAB <= STAGE;
+  static_assert(TWO || (NSTAGE == 4 && SLAB <= STAGE), "epilogue slabs must fit the stages");
+  float* slab = TWO ? reinterpret_cast<float*>(stage(wave >> 1) + (wave & 1) * SLAB)
+                    : reinterpret_cast<float*>(stage(wave));
+  Epilogue<T, E>::template run<TM, TN, WN>(args, acc, slab, m0 + wm * WM, n0 + wn * WN, lane);
+}
 
 // Sums split-K partials in slice order into the fp32 gradient.
 __global__ __launch_bounds__(256) void splitk_reduce(const float* __restrict__ P, int splits, int M, int N,
@@ -485,21 +645,62 @@ hipError_t launch_tile(const GemmArgs& a, hipStream_t s) {
 // Tile size: the largest that still gives at least ~1 tile per CU.
 template <typename T, bool AK, bool BKc, Epi E>
 hipError_t launch_layout(const GemmArgs& a, hipStream_t s) {
+  // tile: 1 = 256x256, 2 = 128x128, 3 = 64x64 (0 = by shape)
   if constexpr (E == Epi::LMHead) {
     // one 128-column partial per wave column => BN = 256
-    if ((int64_t)((a.M + 255) / 256) * (a.N / 256) >= 256) return launch_tile<T, 256, 256, AK, BKc, E>(a, s);
+    int tile = a.tile;
+    if (tile == 0) tile = (int64_t)((a.M + 255) / 256) * (a.N / 256) >= 256 ? 1 : 3;
+    if (tile == 1) return launch_tile<T, 256, 256, AK, BKc, E>(a, s);
     return launch_tile<T, 64, 256, AK, BKc, E>(a, s);
   } else {
     const int64_t t256 = (int64_t)((a.M + 255) / 256) * ((a.N + 255) / 256) * a.splits;
     const int64_t t128 = (int64_t)((a.M + 127) / 128) * ((a.N + 127) / 128) * a.splits;
-    if (t256 >= 512 && a.N % 256 == 0) return launch_tile<T, 256, 256, AK, BKc, E>(a, s);
-    if (t128 >= 256 || a.N % 64 != 0) return launch_tile<T, 128, 128, AK, BKc, E>(a, s);
+    int tile = a.tile;
+    if (tile == 0) tile = (t256 >= 512 && a.N % 256 == 0) ? 1 : (t128 >= 256 ? 2 : 3);
+    if (tile == 1) return launch_tile<T, 256, 256, AK, BKc, E>(a, s);
+    if (tile == 2) return launch_tile<T, 128, 128, AK, BKc, E>(a, s);
     return launch_tile<T, 64, 64, AK, BKc, E>(a, s);
+  }
+}
+
+template <int BM, int BN, int NSTAGE, int OCC, Epi E>
+hipError_t launch_nt_lds(const GemmArgs& a, hipStream_t s) {
+  const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  hipLaunchKernelGGL((gemm_nt_lds_kernel<BM, BN, NSTAGE, OCC, E>), dim3(tiles), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+
+template <Epi E>
+hipError_t launch_nt_lds_tile(const GemmArgs& a, hipStream_t s) {
+  const int64_t t256 = (int64_t)((a.M + 255) / 256) * ((a.N + 255) / 256);
+  // tile: 1 = 256x256 (one CTA per CU), 2 = 256x128 (two per CU), 3 = 128x128
+  int tile = a.tile;
+  if (tile == 0) tile = (t256 >= 512 && a.N % 256 == 0) ? 1 : 3;
+  if constexpr (E == Epi::LMHead) {  // one exp-sum partial per 128 columns: BN = 256
+    if (tile == 1 || tile == 2) return launch_nt_lds<256, 256, 4, 1, E>(a, s);
+    return launch_nt_lds<128, 256, 4, 1, E>(a, s);
+  } else {
+    if (tile == 1) return launch_nt_lds<256, 256, 4, 1, E>(a, s);
+    if (tile == 2) return launch_nt_lds<256, 128, 3, 2, E>(a, s);
+    return launch_nt_lds<128, 128, 4, 1, E>(a, s);
   }
 }
 
 template <typename T>
 hipError_t launch_typed(Epi epi, const GemmArgs& a, hipStream_t s) {
+  if constexpr (sizeof(T) == 2) {
+    if (a.a_kcontig && a.b_kcontig && a.K % 32 == 0) {
+      switch (epi) {
+        case Epi::Store: return launch_nt_lds_tile<Epi::Store>(a, s);
+        case Epi::Residual: return launch_nt_lds_tile<Epi::Residual>(a, s);
+        case Epi::Relu2: return launch_nt_lds_tile<Epi::Relu2>(a, s);
+        case Epi::LMHead: return launch_nt_lds_tile<Epi::LMHead>(a, s);
+        case Epi::Relu2Bwd: return launch_nt_lds_tile<Epi::Relu2Bwd>(a, s);
+        default: break;
+      }
+    }
+  }
   const bool nt = a.a_kcontig && a.b_kcontig, nn = a.a_kcontig && !a.b_kcontig,
              tn = !a.a_kcontig && !a.b_kcontig;
   switch (epi) {
@@ -518,6 +719,7 @@ hipError_t launch_typed(Epi epi, const GemmArgs& a, hipStream_t s) {
       break;
     case Epi::Relu2Bwd:
       if (nn) return launch_layout<T, true, false, Epi::Relu2Bwd>(a, s);
+      if (nt) return launch_layout<T, true, true, Epi::Relu2Bwd>(a, s);
       break;
     case Epi::GradF32:
       if (tn) return launch_layout<T, false, false, Epi::GradF32>(a, s);

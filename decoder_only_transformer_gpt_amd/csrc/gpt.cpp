@@ -17,6 +17,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 #include <string>
@@ -53,13 +54,13 @@ enum Tag : int {
   K_EMBED = 0, K_RMSNORM, K_GEMM_QKV, K_ROPE_QKNORM, K_ATTN_FWD, K_GEMM_O, K_GEMM_W1, K_GEMM_W2, K_GEMM_LM,
   K_CE_LOSS, K_CE_BWD, K_GEMM_LM_DW, K_GEMM_LM_DX, K_RMSNORM_BWD, K_GEMM_W2_DW, K_GEMM_W2_DX, K_GEMM_W1_DW,
   K_GEMM_W1_DX, K_GEMM_O_DW, K_GEMM_O_DX, K_ATTN_BWD, K_ROPE_QKNORM_BWD, K_GEMM_QKV_DW, K_GEMM_QKV_DX,
-  K_EMBED_BWD, K_NUM_TAGS
+  K_EMBED_BWD, K_WEIGHT_T, K_NUM_TAGS
 };
 const char* kTagNames[K_NUM_TAGS] = {
   "embed_rmsnorm", "rmsnorm", "gemm_qkv", "rope_qknorm", "attn_fwd", "gemm_o", "gemm_w1_relu2", "gemm_w2",
   "gemm_lm_head_softcap", "ce_loss", "ce_bwd", "gemm_lm_head_dw", "gemm_lm_head_dx", "rmsnorm_bwd", "gemm_w2_dw",
   "gemm_w2_dx", "gemm_w1_dw", "gemm_w1_dx_relu2bwd", "gemm_o_dw", "gemm_o_dx", "attn_bwd", "rope_qknorm_bwd",
-  "gemm_qkv_dw", "gemm_qkv_dx", "embed_bwd"};
+  "gemm_qkv_dw", "gemm_qkv_dx", "embed_bwd", "weight_transpose"};
 
 struct Layout {  // byte offsets inside the workspace
   size_t flag, loss_rows, rope_cos, rope_sin;
@@ -67,6 +68,7 @@ struct Layout {  // byte offsets inside the workspace
   std::vector<size_t> h1, rstd1, qkv, rstd_qk, o, lse, h2, rstd2, a;
   size_t dres, dres_lp, dh, du, dqkv, dout, delta, split;
   size_t qT, kT, vT, doT;  // attention's transposed copies [B, heads, 128, Tp]
+  size_t wT, tdesc;        // transposed weights (bf16 models) and their descriptor table
   size_t keys_a, vals_a, keys_b, vals_b, hist, coef, carry;
   size_t total;
   size_t split_elems;
@@ -149,6 +151,11 @@ Layout plan(const gpt_config& c, int maxB, int maxT) {
   upd((int)V, (int)C);
   L.split_elems = se;
   L.split = p.take(se * 4);
+  {
+    const int64_t np = gpt_param_count(&c);
+    L.wT = c.dtype == GPT_BF16 ? p.take((size_t)np * es) : p.take(0);
+    L.tdesc = p.take((size_t)(2 + 4 * c.n_layer) * sizeof(gk::TransposeDesc));
+  }
   L.keys_a = p.take(N * 4);
   L.vals_a = p.take(N * 4);
   L.keys_b = p.take(N * 4);
@@ -190,6 +197,9 @@ struct gpt_model {
   // parameter offsets (elements)
   int64_t off_wte, off_lm;
   std::vector<int64_t> off_qkv, off_o, off_w1, off_w2;
+  int gemm_tile = 0;      // GPT_OPT_GEMM_TILE
+  int ntdesc = 0;
+  int64_t wt_tiles = 0;   // total 64x64 tiles of the batched weight transpose
   // state of the last forward
   bool pending = false;
   int B = 0, T = 0;
@@ -396,7 +406,25 @@ gpt_status gpt_init(const gpt_config* cfg, const void* params, float* grads, voi
       ct[(size_t)t * 64 + i] = (float)std::cos(ang);
       st[(size_t)t * 64 + i] = (float)std::sin(ang);
     }
+  // transposed-weight descriptors (all matrices except the embedding, which
+  // is never multiplied)
+  std::vector<gk::TransposeDesc> td;
+  int64_t tiles = 0;
+  for (int i = 1; i < n; ++i) {
+    gk::TransposeDesc t;
+    t.offset = d[i].offset;
+    t.rows = (int32_t)d[i].rows;
+    t.cols = (int32_t)d[i].cols;
+    t.tile0 = tiles;
+    tiles += ((d[i].rows + 63) / 64) * ((d[i].cols + 63) / 64);
+    td.push_back(t);
+  }
+  m->ntdesc = (int)td.size();
+  m->wt_tiles = tiles;
   hipError_t e = hipMemcpyAsync(m->ws + m->L.rope_cos, ct.data(), ct.size() * 4, hipMemcpyHostToDevice, stream);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(m->ws + m->L.tdesc, td.data(), td.size() * sizeof(gk::TransposeDesc), hipMemcpyHostToDevice,
+                       stream);
   if (e == hipSuccess)
     e = hipMemcpyAsync(m->ws + m->L.rope_sin, st.data(), st.size() * 4, hipMemcpyHostToDevice, stream);
   if (e == hipSuccess) e = hipMemsetAsync(m->ws + m->L.flag, 0, 256, stream);
@@ -430,6 +458,7 @@ gpt_status gpt_forward_loss(gpt_model* m, const int32_t* idx, const int32_t* tar
                                              wsp<float>(m, L.rstd1[l]), stream););
     RUN(K_GEMM_QKV, {
       gk::GemmArgs a;
+      a.tile = m->gemm_tile;
       a.A = m->ws + L.h1[l]; a.lda = C;
       a.B = pbase(m, m->off_qkv[l]); a.ldb = C;
       a.M = N; a.N = QKV; a.K = C;
@@ -443,6 +472,7 @@ gpt_status gpt_forward_loss(gpt_model* m, const int32_t* idx, const int32_t* tar
                                                wsp<float>(m, L.lse[l]), m->ws + L.vT, stream););
     RUN(K_GEMM_O, {
       gk::GemmArgs a;
+      a.tile = m->gemm_tile;
       a.A = m->ws + L.o[l]; a.lda = HD;
       a.B = pbase(m, m->off_o[l]); a.ldb = HD;
       a.M = N; a.N = C; a.K = HD;
@@ -453,6 +483,7 @@ gpt_status gpt_forward_loss(gpt_model* m, const int32_t* idx, const int32_t* tar
                                              wsp<float>(m, L.rstd2[l]), stream););
     RUN(K_GEMM_W1, {
       gk::GemmArgs a;
+      a.tile = m->gemm_tile;
       a.A = m->ws + L.h2[l]; a.lda = C;
       a.B = pbase(m, m->off_w1[l]); a.ldb = C;
       a.M = N; a.N = F; a.K = C;
@@ -461,6 +492,7 @@ gpt_status gpt_forward_loss(gpt_model* m, const int32_t* idx, const int32_t* tar
     });
     RUN(K_GEMM_W2, {
       gk::GemmArgs a;
+      a.tile = m->gemm_tile;
       a.A = m->ws + L.a[l]; a.lda = F;
       a.B = pbase(m, m->off_w2[l]); a.ldb = F;
       a.M = N; a.N = C; a.K = F;
@@ -472,6 +504,7 @@ gpt_status gpt_forward_loss(gpt_model* m, const int32_t* idx, const int32_t* tar
                                            wsp<float>(m, L.rstdf), stream););
   RUN(K_GEMM_LM, {
     gk::GemmArgs a;
+      a.tile = m->gemm_tile;
     a.A = m->ws + L.hf; a.lda = C;
     a.B = pbase(m, m->off_lm); a.ldb = C;
     a.M = N; a.N = V; a.K = C;
@@ -509,6 +542,7 @@ gpt_status gpt_backward(gpt_model* m, float dloss, int32_t accumulate, void* str
   auto dw = [&](int tag, const void* dy, int ldy, const void* x, int ldx, int M, int Nn, int64_t goff) -> gpt_status {
     RUN(tag, {
       gk::GemmArgs a;
+      a.tile = m->gemm_tile;
       a.A = dy; a.lda = ldy; a.a_kcontig = false;
       a.B = x; a.ldb = ldx; a.b_kcontig = false;
       a.M = M; a.N = Nn; a.K = N;
@@ -520,12 +554,21 @@ gpt_status gpt_backward(gpt_model* m, float dloss, int32_t accumulate, void* str
     });
     return GPT_OK;
   };
-  auto dx = [&](int tag, gk::Epi epi, const void* dy, int ldy, const void* w, int ldw, int Nn, int K, void* out,
+  // dX = dY W for W [K, Nn] (row-major, w at element offset woff). bf16
+  // models multiply by the transposed copy W^T [Nn, K] (both operands
+  // k-contiguous, the direct-to-LDS kernel); fp32 reads W as is.
+  const bool use_wt = dt == GPT_BF16;
+  auto dx = [&](int tag, gk::Epi epi, const void* dy, int ldy, int64_t woff, int Nn, int K, void* out,
                 const void* aux) -> gpt_status {
     RUN(tag, {
       gk::GemmArgs a;
+      a.tile = m->gemm_tile;
       a.A = dy; a.lda = ldy;
-      a.B = w; a.ldb = ldw; a.b_kcontig = false;
+      if (use_wt) {
+        a.B = m->ws + L.wT + woff * (int64_t)esize(dt); a.ldb = K; a.b_kcontig = true;
+      } else {
+        a.B = pbase(m, woff); a.ldb = Nn; a.b_kcontig = false;
+      }
       a.M = N; a.N = Nn; a.K = K;
       a.C = out; a.ldc = Nn;
       a.C2 = const_cast<void*>(aux); a.ldc2 = Nn;
@@ -533,27 +576,30 @@ gpt_status gpt_backward(gpt_model* m, float dloss, int32_t accumulate, void* str
     });
     return GPT_OK;
   };
+  if (use_wt)
+    RUN(K_WEIGHT_T, return gk::launch_transpose_batched(dt, m->params, m->ws + L.wT,
+                                                        reinterpret_cast<const gk::TransposeDesc*>(m->ws + L.tdesc),
+                                                        m->ntdesc, m->wt_tiles, stream););
 #define TRY(x) do { gpt_status s_ = (x); if (s_ != GPT_OK) return s_; } while (0)
 
   RUN(K_CE_BWD, return gk::launch_ce_bwd(dt, m->ws + L.logits, wsp<float>(m, L.lse_ce), m->targets, N, V,
                                          c.logit_softcap, dloss / (float)N, stream););
   TRY(dw(K_GEMM_LM_DW, m->ws + L.logits, V, m->ws + L.hf, C, V, C, m->off_lm));
-  TRY(dx(K_GEMM_LM_DX, gk::Epi::Store, m->ws + L.logits, V, pbase(m, m->off_lm), C, C, V, m->ws + L.dh, nullptr));
+  TRY(dx(K_GEMM_LM_DX, gk::Epi::Store, m->ws + L.logits, V, m->off_lm, C, V, m->ws + L.dh, nullptr));
   RUN(K_RMSNORM_BWD, return gk::launch_rmsnorm_bwd(dt, m->ws + L.dh, m->ws + L.hf, wsp<float>(m, L.rstdf), N, C, 0,
                                                    wsp<float>(m, L.dres), m->ws + L.dres_lp, stream););
   for (int l = c.n_layer - 1; l >= 0; --l) {
     // MLP
     TRY(dw(K_GEMM_W2_DW, m->ws + L.dres_lp, C, m->ws + L.a[l], F, C, F, m->off_w2[l]));
-    TRY(dx(K_GEMM_W2_DX, gk::Epi::Relu2Bwd, m->ws + L.dres_lp, C, pbase(m, m->off_w2[l]), F, F, C, m->ws + L.du,
+    TRY(dx(K_GEMM_W2_DX, gk::Epi::Relu2Bwd, m->ws + L.dres_lp, C, m->off_w2[l], F, C, m->ws + L.du,
            m->ws + L.a[l]));
     TRY(dw(K_GEMM_W1_DW, m->ws + L.du, F, m->ws + L.h2[l], C, F, C, m->off_w1[l]));
-    TRY(dx(K_GEMM_W1_DX, gk::Epi::Store, m->ws + L.du, F, pbase(m, m->off_w1[l]), C, C, F, m->ws + L.dh, nullptr));
+    TRY(dx(K_GEMM_W1_DX, gk::Epi::Store, m->ws + L.du, F, m->off_w1[l], C, F, m->ws + L.dh, nullptr));
     RUN(K_RMSNORM_BWD, return gk::launch_rmsnorm_bwd(dt, m->ws + L.dh, m->ws + L.h2[l], wsp<float>(m, L.rstd2[l]),
                                                      N, C, 1, wsp<float>(m, L.dres), m->ws + L.dres_lp, stream););
     // attention
     TRY(dw(K_GEMM_O_DW, m->ws + L.dres_lp, C, m->ws + L.o[l], HD, C, HD, m->off_o[l]));
-    TRY(dx(K_GEMM_O_DX, gk::Epi::Store, m->ws + L.dres_lp, C, pbase(m, m->off_o[l]), HD, HD, C, m->ws + L.dout,
-           nullptr));
+    TRY(dx(K_GEMM_O_DX, gk::Epi::Store, m->ws + L.dres_lp, C, m->off_o[l], HD, C, m->ws + L.dout, nullptr));
     RUN(K_ATTN_BWD, {
       gk::AttnBwdArgs a;
       a.qkv = m->ws + L.qkv[l];
@@ -573,8 +619,7 @@ gpt_status gpt_backward(gpt_model* m, float dloss, int32_t accumulate, void* str
                                                              wsp<float>(m, L.rope_cos), wsp<float>(m, L.rope_sin),
                                                              stream););
     TRY(dw(K_GEMM_QKV_DW, m->ws + L.dqkv, QKV, m->ws + L.h1[l], C, QKV, C, m->off_qkv[l]));
-    TRY(dx(K_GEMM_QKV_DX, gk::Epi::Store, m->ws + L.dqkv, QKV, pbase(m, m->off_qkv[l]), C, C, QKV, m->ws + L.dh,
-           nullptr));
+    TRY(dx(K_GEMM_QKV_DX, gk::Epi::Store, m->ws + L.dqkv, QKV, m->off_qkv[l], C, QKV, m->ws + L.dh, nullptr));
     RUN(K_RMSNORM_BWD, return gk::launch_rmsnorm_bwd(dt, m->ws + L.dh, m->ws + L.h1[l], wsp<float>(m, L.rstd1[l]),
                                                      N, C, 1, wsp<float>(m, L.dres), m->ws + L.dres_lp, stream););
   }
@@ -642,6 +687,18 @@ gpt_status gpt_profile_end(gpt_model* m, double* total_ms, int64_t* launches) {
   P.armed = false;
   P.used = 0;
   return GPT_OK;
+}
+
+gpt_status gpt_set_option(gpt_model* m, int32_t option, int32_t value) {
+  if (!m) return fail(GPT_E_INVALID_ARG, "NULL model");
+  switch (option) {
+    case GPT_OPT_GEMM_TILE:
+      if (value < 0 || value > 3) return fail(GPT_E_INVALID_ARG, "GEMM tile option %d not in 0..3", value);
+      m->gemm_tile = value;
+      return GPT_OK;
+    default:
+      return fail(GPT_E_INVALID_ARG, "unknown option %d", option);
+  }
 }
 
 const char* gpt_kernel_tag_name(int32_t tag) {

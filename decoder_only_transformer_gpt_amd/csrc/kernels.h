@@ -25,6 +25,7 @@ struct GemmArgs {
   bool b_kcontig = true;  // B(n,k) at B[n*ldb + k] if true, else B[k*ldb + n]
   int M = 0, N = 0, K = 0;
   int splits = 1;          // split-K slices (GradF32 only)
+  int tile = 0;            // 0: by shape; 1..3: force a tile variant (largest first)
   void* C = nullptr;
   int64_t ldc = 0;
   void* C2 = nullptr;
@@ -105,5 +106,15 @@ size_t embed_bwd_hist_elems(int N);
 size_t embed_bwd_carry_elems(int N, int C);
 
 hipError_t launch_fill_f32(float* p, float v, int64_t n, hipStream_t s);
+
+// Batched transpose of row-major [rows, cols] tensors stored at `offset`
+// (elements) in src into [cols, rows] at the same offset in dst.
+struct TransposeDesc {
+  int64_t offset;
+  int32_t rows, cols;
+  int64_t tile0;  // index of the tensor's first 64x64 tile
+};
+hipError_t launch_transpose_batched(int dtype, const void* src, void* dst, const TransposeDesc* desc, int ndesc,
+                                    int64_t total_tiles, hipStream_t s);
 
 }  // namespace gk

@@ -270,3 +270,50 @@ hipError_t launch_fill_f32(float* p, float v, int64_t n, hipStream_t s) {
 }
 
 }  // namespace gk
+
+namespace gk {
+namespace {
+
+// Batched 2-D transpose of activation-dtype matrices: for every tensor t,
+// dst[t][c][r] = src[t][r][c]. One 64x64 tile per block, staged through LDS
+// (+1 column of padding against bank conflicts); tiles of all tensors are
+// numbered consecutively and a block finds its tensor by a linear scan of
+// the (few dozen) tile-start offsets.
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_batched_kernel(const T* __restrict__ src, T* __restrict__ dst,
+                                                                const TransposeDesc* __restrict__ desc, int ndesc) {
+  __shared__ float tile[64][65];
+  int t = 0;
+  while (t + 1 < ndesc && (int64_t)blockIdx.x >= desc[t + 1].tile0) ++t;
+  const TransposeDesc d = desc[t];
+  const int64_t local = blockIdx.x - d.tile0;
+  const int tiles_c = (d.cols + 63) / 64;
+  const int r0 = (int)(local / tiles_c) * 64, c0 = (int)(local % tiles_c) * 64;
+  const T* s = src + d.offset;
+  T* o = dst + d.offset;
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int r = i / 64, c = i % 64;
+    if (r0 + r < d.rows && c0 + c < d.cols) tile[r][c] = to_f32(s[(int64_t)(r0 + r) * d.cols + c0 + c]);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int c = i / 64, r = i % 64;
+    if (r0 + r < d.rows && c0 + c < d.cols) o[(int64_t)(c0 + c) * d.rows + r0 + r] = from_f32<T>(tile[r][c]);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_transpose_batched(int dtype, const void* src, void* dst, const TransposeDesc* desc, int ndesc,
+                                    int64_t total_tiles, hipStream_t s) {
+  if (total_tiles <= 0) return hipSuccess;
+  if (dtype == 1)
+    hipLaunchKernelGGL(transpose_batched_kernel<bf16>, dim3((unsigned)total_tiles), dim3(256), 0, s,
+                       (const bf16*)src, (bf16*)dst, desc, ndesc);
+  else
+    hipLaunchKernelGGL(transpose_batched_kernel<float>, dim3((unsigned)total_tiles), dim3(256), 0, s,
+                       (const float*)src, (float*)dst, desc, ndesc);
+  return hipGetLastError();
+}
+
+}  // namespace gk

@@ -62,6 +62,9 @@ class GPT:
         off = ptr - base
         return self.ws[off:off + nbytes].view(dtype).view(*shape)
 
+    def set_gemm_tile(self, tile: int):
+        _lib.gpt_set_option(self.h, _lib.GPT_OPT_GEMM_TILE, tile)
+
     def close(self):
         if self.h is not None:
             _lib.gpt_destroy(self.h)

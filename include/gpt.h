@@ -161,6 +161,15 @@ gpt_status gpt_destroy(gpt_model* m);
 gpt_status gpt_profile_begin(gpt_model* m, int32_t tag);
 gpt_status gpt_profile_end(gpt_model* m, double* total_ms, int64_t* launches);
 
+/* Options of a handle (take effect for the following calls).
+ * GPT_OPT_GEMM_TILE: 0 (default) picks each GEMM's tile by its shape;
+ * 1..3 force one tile variant for every GEMM, largest first (bf16
+ * k-contiguous GEMMs: 256x256, 256x128 with two workgroups per CU, 128x128;
+ * others: 256x256, 128x128, 64x64). Results are the same up to rounding
+ * order; the option exists to measure and test every variant. */
+enum { GPT_OPT_GEMM_TILE = 1 };
+gpt_status gpt_set_option(gpt_model* m, int32_t option, int32_t value);
+
 /* Name of a kernel tag (NULL past the last tag); tags run 0..n-1. */
 const char* gpt_kernel_tag_name(int32_t tag);
 

@@ -54,11 +54,13 @@ class Case:
 
 
 def run_gpu(case: Case, dloss: float = 1.0, accumulate: bool = False, row_loss: bool = True, backward: bool = True,
-            max_B: int | None = None, max_T: int | None = None, params_override=None):
+            max_B: int | None = None, max_T: int | None = None, params_override=None, tile: int = 0):
     torch = require_gpu()
     from decoder_only_transformer_gpt_amd.model import GPT
     params = GPT.params_from_numpy(case.storage if params_override is None else params_override, case.cfg)
     m = GPT(case.cfg, params, max_B or case.B, max_T or case.T)
+    if tile:
+        m.set_gemm_tile(tile)
     idx = torch.from_numpy(case.idx).cuda()
     tgt = torch.from_numpy(case.tgt).cuda()
     rl = torch.zeros(case.B * case.T, dtype=torch.float32, device="cuda") if row_loss else None

@@ -52,11 +52,12 @@ def check_bf16(case, gpu, loss, G, label):
         assert U.cosine(gg[k], go[k]) >= 0.999, k
 
 
-def test_tiny_fp32_full_step():
+@pytest.mark.parametrize("tile", [0, 1, 2, 3])
+def test_tiny_fp32_full_step(tile):
     U.require_gpu()
     case = U.Case(tiny_cfg(), B=2, T=64, law="uniform")
-    U.log("case tiny fp32 B=2 T=64 V=512 seed 0/1")
-    gpu = U.run_gpu(case)
+    U.log(f"case tiny fp32 B=2 T=64 V=512 seed 0/1 gemm tile {tile}")
+    gpu = U.run_gpu(case, tile=tile)
     assert gpu["status"] == _lib.GPT_OK
     loss, rows, G = O.step(U.oracle_cfg(case.cfg), case.oracle_params(), case.idx, case.tgt)
     np.testing.assert_allclose(gpu["row_loss"], rows.reshape(-1), rtol=2e-5)
@@ -83,23 +84,26 @@ def test_tiny_fp32_ragged_and_scaled():
     check_fp32(case, gpu, loss, G, "tiny-ragged")
 
 
-def test_d4_bf16_full_step():
+@pytest.mark.parametrize("tile", [0, 1, 2, 3])
+def test_d4_bf16_full_step(tile):
     U.require_gpu()
     case = U.Case(d4_cfg(), B=4, T=512, law="uniform")
-    U.log("case d4 bf16 B=4 T=512 uniform")
-    gpu = U.run_gpu(case)
+    U.log(f"case d4 bf16 B=4 T=512 uniform gemm tile {tile}")
+    gpu = U.run_gpu(case, tile=tile)
     assert gpu["status"] == _lib.GPT_OK
     loss, rows, G = O.step(U.oracle_cfg(case.cfg), case.oracle_params(), case.idx, case.tgt)
     check_bf16(case, gpu, loss, G, "d4")
 
 
-def test_bf16_ragged_zipf():
-    """bf16, Zipf ids (heavy repeats in the embedding backward), ragged T and M."""
+@pytest.mark.parametrize("tile", [0, 1, 2, 3])
+def test_bf16_ragged_zipf(tile):
+    """bf16, Zipf ids (heavy repeats in the embedding backward), ragged T and M
+    (partial GEMM tiles in every variant)."""
     U.require_gpu()
     c = d4_cfg()
     case = U.Case(c, B=3, T=333, law="zipf", wseed=2, tseed=3)
-    U.log("case d4 bf16 ragged B=3 T=333 zipf")
-    gpu = U.run_gpu(case)
+    U.log(f"case d4 bf16 ragged B=3 T=333 zipf gemm tile {tile}")
+    gpu = U.run_gpu(case, tile=tile)
     loss, rows, G = O.step(U.oracle_cfg(case.cfg), case.oracle_params(), case.idx, case.tgt)
     check_bf16(case, gpu, loss, G, "d4-ragged-zipf")
 
