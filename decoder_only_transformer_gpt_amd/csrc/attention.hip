@@ -107,6 +107,22 @@ DEV u32x4 read_perm(const T* lds, int row, int base, int kk, int g) {
   }
 }
 
+// Blocks are dealt round-robin to the 8 XCDs (block id % 8). Map linear ids
+// so that every block of a batch row lands on one XCD (its L2 then holds that
+// row's shared K/V or Q/dO tiles): XCD x takes rows x, x+8, ... in order, and
+// within a row the `per_row` blocks in index order (heavy work first).
+// Returns (b, r) with r in [0, per_row). Needs B % 8 == 0, else identity.
+DEV void xcd_row_map(int id, int B, int per_row, int& b, int& r) {
+  if ((B & 7) == 0) {
+    const int x = id & 7, j = id >> 3;
+    b = x + 8 * (j / per_row);
+    r = j % per_row;
+  } else {
+    b = id / per_row;
+    r = id % per_row;
+  }
+}
+
 DEV f32x16 zero16() {
   f32x16 z;
 #pragma unroll
@@ -160,8 +176,9 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const T* __restrict__ qkv
   __shared__ __attribute__((aligned(16))) T Ks[NBUF][64 * A::P];
   __shared__ __attribute__((aligned(16))) T VTs[NBUF][D * A::PT];
   const int nqb = (T_ + 127) / 128;
-  const int qb = nqb - 1 - blockIdx.x;
-  const int h = blockIdx.y, b = blockIdx.z;
+  int b, r;
+  xcd_row_map(blockIdx.x, gridDim.x / (nqb * H), nqb * H, b, r);
+  const int qb = nqb - 1 - r / H, h = r % H;   // heavy (late) query blocks first
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
   const int64_t ld = (int64_t)(H + 2) * D;
   const T* base = qkv + (int64_t)b * T_ * ld;
@@ -286,8 +303,9 @@ __global__ __launch_bounds__(256) void attn_dq_kernel(const T* __restrict__ qkv,
   __shared__ __attribute__((aligned(16))) T Vs[NBUF][64 * A::P];
   __shared__ __attribute__((aligned(16))) T KTs[NBUF][D * A::PT];
   const int nqb = (T_ + 127) / 128;
-  const int qb = nqb - 1 - blockIdx.x;
-  const int h = blockIdx.y, b = blockIdx.z;
+  int b, r;
+  xcd_row_map(blockIdx.x, gridDim.x / (nqb * H), nqb * H, b, r);
+  const int qb = nqb - 1 - r / H, h = r % H;   // heavy (late) query blocks first
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
   const int64_t ld = (int64_t)(H + 2) * D;
   const T* base = qkv + (int64_t)b * T_ * ld;
@@ -401,7 +419,9 @@ __global__ __launch_bounds__(256) void attn_dkv_kernel(const T* __restrict__ qkv
   __shared__ __attribute__((aligned(16))) T Ds[NBUF][64 * A::P];
   __shared__ __attribute__((aligned(16))) T DTs[NBUF][D * A::PT];
   __shared__ float Ls[NBUF][64], Es[NBUF][64];
-  const int kb = blockIdx.x, b = blockIdx.y;
+  const int nkb = (T_ + 127) / 128;
+  int b, kb;
+  xcd_row_map(blockIdx.x, gridDim.x / nkb, nkb, b, kb);   // key block 0 (most query tiles) first
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
   const int64_t ld = (int64_t)(H + 2) * D;
   const T* base = qkv + (int64_t)b * T_ * ld;
@@ -425,8 +445,11 @@ __global__ __launch_bounds__(256) void attn_dkv_kernel(const T* __restrict__ qkv
   Stage<T, 64, D> sq, sd;
   Stage<T, D, 64> sqt, sdt;
   float pl = 0.f, pe = 0.f;
+  // (query tile, head) pairs in one descending order for every key block:
+  // blocks of a batch row running side by side read the same Q/dO tiles at
+  // the same time; a block stops after its first query tile.
   auto issue = [&](int it) {
-    const int h = it / nq, q0 = (qt0 + it % nq) * 64;
+    const int h = it % H, q0 = (nqt - 1 - it / H) * 64;
     sq.load(base + (int64_t)q0 * ld + h * D, ld, T_ - q0, tid);
     sqt.load(qT + ((int64_t)b * H + h) * D * Tp + q0, Tp, D, tid);
     sd.load(dout + ((int64_t)b * T_ + q0) * H * D + h * D, (int64_t)H * D, T_ - q0, tid);
@@ -455,7 +478,7 @@ __global__ __launch_bounds__(256) void attn_dkv_kernel(const T* __restrict__ qkv
 
   for (int it = 0; it < total; ++it) {
     const int cur = it % NBUF;
-    const int q0 = (qt0 + it % nq) * 64;
+    const int q0 = (nqt - 1 - it / H) * 64;
     const bool more = it + 1 < total;
     if (more) issue(it + 1);
     const T* Q_ = Qs[cur];
@@ -527,7 +550,7 @@ hipError_t fwd_typed(const void* qkv, int B, int T_, int H, void* o, float* lse,
   const int Tp = attn_padded_len(T_);
   hipError_t e = transpose<T>(qkv, (int64_t)(H + 2) * D, (H + 1) * D, 1, B, T_, Tp, vT, s);
   if (e != hipSuccess) return e;
-  dim3 grid((T_ + 127) / 128, H, B);
+  dim3 grid(((T_ + 127) / 128) * H * B);
   hipLaunchKernelGGL(attn_fwd_kernel<T>, grid, dim3(256), 0, s, (const T*)qkv, (const T*)vT, T_, Tp, H, (T*)o, lse);
   return hipGetLastError();
 }
@@ -544,9 +567,9 @@ hipError_t bwd_typed(const AttnBwdArgs& a, hipStream_t s) {
   const int64_t groups = (int64_t)B * T_ * H;
   hipLaunchKernelGGL(attn_delta_kernel<T>, dim3((unsigned)((groups * 16 + 255) / 256)), dim3(256), 0, s,
                      (const T*)a.o, (const T*)a.dout, B * T_, T_, H, a.delta);
-  hipLaunchKernelGGL(attn_dq_kernel<T>, dim3((T_ + 127) / 128, H, B), dim3(256), 0, s, (const T*)a.qkv,
+  hipLaunchKernelGGL(attn_dq_kernel<T>, dim3(((T_ + 127) / 128) * H * B), dim3(256), 0, s, (const T*)a.qkv,
                      (const T*)a.kT, (const T*)a.dout, a.lse, a.delta, T_, Tp, H, (T*)a.dqkv);
-  hipLaunchKernelGGL(attn_dkv_kernel<T>, dim3((T_ + 127) / 128, B), dim3(256), 0, s, (const T*)a.qkv,
+  hipLaunchKernelGGL(attn_dkv_kernel<T>, dim3(((T_ + 127) / 128) * B), dim3(256), 0, s, (const T*)a.qkv,
                      (const T*)a.qT, (const T*)a.dout, (const T*)a.doT, a.lse, a.delta, T_, Tp, H, (T*)a.dqkv);
   return hipGetLastError();
 }
