@@ -50,11 +50,17 @@ def kernel_flops_per_launch(tag: str, cfg, B: int, T: int) -> float | None:
     if tag in g:
         m, n, k = g[tag]
         return 2.0 * m * n * k
+    # causal attention counts only the T(T+1)/2 needed (query, key) pairs; per
+    # pair the forward's S and PV contractions are 2D FLOPs each. The backward's
+    # four contractions (dP, dQ, dK, dV; 2D each) are split between its two
+    # kernels: dP and dQ to the dQ kernel, dK and dV to the dK/dV kernel. The
+    # recomputation of S (both kernels) and of dP (the dK/dV kernel) is not
+    # algorithmic work and is not counted.
     pairs = B * H * T * (T + 1) / 2.0
     if tag == "attn_fwd":
         return 4.0 * D * pairs
-    if tag == "attn_bwd":
-        return 8.0 * D * pairs
+    if tag in ("attn_bwd_dq", "attn_bwd_dkv"):
+        return 4.0 * D * pairs
     return None
 
 
@@ -64,7 +70,11 @@ def kernel_bytes_per_launch(tag: str, cfg, B: int, T: int, es: int) -> float | N
     b = {"embed_rmsnorm": N * (4 + 2 * C * es + 4), "rmsnorm": N * (2 * C * es + 4),
          "rope_qknorm": N * (2 * (H + 1) * 128 * es + 4 * (H + 1)),
          "ce_bwd": N * (2 * V * es + 8), "rmsnorm_bwd": N * (2 * C * es + 8 * C + C * es + 4),
-         "rope_qknorm_bwd": N * (3 * (H + 1) * 128 * es + 4 * (H + 1))}
+         "rope_qknorm_bwd": N * (3 * (H + 1) * 128 * es + 4 * (H + 1)),
+         # transposed copies: read and write each (V; then Q, K, dO) once, plus delta's
+         # read of O and dO and its fp32 write
+         "attn_fwd_transpose": N * 128 * es * 2,
+         "attn_bwd_prep": N * (2 * (2 * H + 1) * 128 * es + 2 * H * 128 * es + 4 * H)}
     return b.get(tag)
 
 
@@ -108,6 +118,9 @@ def main():
     ap.add_argument("--kernel-table", action="store_true", help="print per-tag timings to stderr")
     ap.add_argument("--dominant", default=None,
                     help="kernel tag to report in the roofline (skips the one-step-per-tag scan)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run one torch.neg over a buffer of this many MiB (reference kernel for "
+                         "the FETCH_SIZE/WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -143,6 +156,14 @@ def main():
     torch.cuda.synchronize()
     if m.sync_status() != _lib.GPT_OK:
         raise RuntimeError("device flag raised during warmup")
+
+    if args.copy_calibration_mib:
+        nbytes = args.copy_calibration_mib << 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     # one profiled step (every launch timed) to find the kernel with the largest share of time
     tags = _lib.gpt_kernel_tag_names()
@@ -195,6 +216,9 @@ def main():
         achieved = kb / (avg_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
+    from decoder_only_transformer_gpt_amd import profsum
+    tr = profsum.read_traffic(os.path.join(ROOT, "profiles", f"{dominant}_{wl.name}_traffic.txt"), dominant)
+    roof["traffic"] = None if tr is None else round(tr)
     roof.update({"kernel": dominant, "launches": dom_n, "avg_ms": round(avg_ms, 4)})
 
     out = {

@@ -546,31 +546,34 @@ hipError_t transpose(const void* src, int64_t ld, int col0, int nh, int B, int T
 }
 
 template <typename T>
-hipError_t fwd_typed(const void* qkv, int B, int T_, int H, void* o, float* lse, void* vT, hipStream_t s) {
+hipError_t fwd_typed(const void* qkv, int B, int T_, int H, void* o, float* lse, void* vT, int stage, hipStream_t s) {
   const int Tp = attn_padded_len(T_);
-  hipError_t e = transpose<T>(qkv, (int64_t)(H + 2) * D, (H + 1) * D, 1, B, T_, Tp, vT, s);
-  if (e != hipSuccess) return e;
+  if (stage == 0) return transpose<T>(qkv, (int64_t)(H + 2) * D, (H + 1) * D, 1, B, T_, Tp, vT, s);
   dim3 grid(((T_ + 127) / 128) * H * B);
   hipLaunchKernelGGL(attn_fwd_kernel<T>, grid, dim3(256), 0, s, (const T*)qkv, (const T*)vT, T_, Tp, H, (T*)o, lse);
   return hipGetLastError();
 }
 
 template <typename T>
-hipError_t bwd_typed(const AttnBwdArgs& a, hipStream_t s) {
+hipError_t bwd_typed(const AttnBwdArgs& a, int stage, hipStream_t s) {
   const int T_ = a.T, H = a.H, B = a.B;
   const int Tp = attn_padded_len(T_);
   const int64_t ld = (int64_t)(H + 2) * D;
   hipError_t e;
-  if ((e = transpose<T>(a.qkv, ld, 0, H, B, T_, Tp, a.qT, s)) != hipSuccess) return e;
-  if ((e = transpose<T>(a.qkv, ld, H * D, 1, B, T_, Tp, a.kT, s)) != hipSuccess) return e;
-  if ((e = transpose<T>(a.dout, (int64_t)H * D, 0, H, B, T_, Tp, a.doT, s)) != hipSuccess) return e;
-  const int64_t groups = (int64_t)B * T_ * H;
-  hipLaunchKernelGGL(attn_delta_kernel<T>, dim3((unsigned)((groups * 16 + 255) / 256)), dim3(256), 0, s,
-                     (const T*)a.o, (const T*)a.dout, B * T_, T_, H, a.delta);
-  hipLaunchKernelGGL(attn_dq_kernel<T>, dim3(((T_ + 127) / 128) * H * B), dim3(256), 0, s, (const T*)a.qkv,
-                     (const T*)a.kT, (const T*)a.dout, a.lse, a.delta, T_, Tp, H, (T*)a.dqkv);
-  hipLaunchKernelGGL(attn_dkv_kernel<T>, dim3(((T_ + 127) / 128) * B), dim3(256), 0, s, (const T*)a.qkv,
-                     (const T*)a.qT, (const T*)a.dout, (const T*)a.doT, a.lse, a.delta, T_, Tp, H, (T*)a.dqkv);
+  if (stage == 0) {
+    if ((e = transpose<T>(a.qkv, ld, 0, H, B, T_, Tp, a.qT, s)) != hipSuccess) return e;
+    if ((e = transpose<T>(a.qkv, ld, H * D, 1, B, T_, Tp, a.kT, s)) != hipSuccess) return e;
+    if ((e = transpose<T>(a.dout, (int64_t)H * D, 0, H, B, T_, Tp, a.doT, s)) != hipSuccess) return e;
+    const int64_t groups = (int64_t)B * T_ * H;
+    hipLaunchKernelGGL(attn_delta_kernel<T>, dim3((unsigned)((groups * 16 + 255) / 256)), dim3(256), 0, s,
+                       (const T*)a.o, (const T*)a.dout, B * T_, T_, H, a.delta);
+  } else if (stage == 1) {
+    hipLaunchKernelGGL(attn_dq_kernel<T>, dim3(((T_ + 127) / 128) * H * B), dim3(256), 0, s, (const T*)a.qkv,
+                       (const T*)a.kT, (const T*)a.dout, a.lse, a.delta, T_, Tp, H, (T*)a.dqkv);
+  } else {
+    hipLaunchKernelGGL(attn_dkv_kernel<T>, dim3(((T_ + 127) / 128) * B), dim3(256), 0, s, (const T*)a.qkv,
+                       (const T*)a.qT, (const T*)a.dout, (const T*)a.doT, a.lse, a.delta, T_, Tp, H, (T*)a.dqkv);
+  }
   return hipGetLastError();
 }
 
@@ -578,13 +581,14 @@ hipError_t bwd_typed(const AttnBwdArgs& a, hipStream_t s) {
 
 int attn_padded_len(int T) { return (T + 63) / 64 * 64; }
 
-hipError_t launch_attn_fwd(int dtype, const void* qkv, int B, int T, int H, void* o, float* lse, void* vT,
+hipError_t launch_attn_fwd(int dtype, const void* qkv, int B, int T, int H, void* o, float* lse, void* vT, int stage,
                            hipStream_t s) {
-  return dtype == 1 ? fwd_typed<bf16>(qkv, B, T, H, o, lse, vT, s) : fwd_typed<float>(qkv, B, T, H, o, lse, vT, s);
+  return dtype == 1 ? fwd_typed<bf16>(qkv, B, T, H, o, lse, vT, stage, s)
+                    : fwd_typed<float>(qkv, B, T, H, o, lse, vT, stage, s);
 }
 
-hipError_t launch_attn_bwd(int dtype, const AttnBwdArgs& a, hipStream_t s) {
-  return dtype == 1 ? bwd_typed<bf16>(a, s) : bwd_typed<float>(a, s);
+hipError_t launch_attn_bwd(int dtype, const AttnBwdArgs& a, int stage, hipStream_t s) {
+  return dtype == 1 ? bwd_typed<bf16>(a, stage, s) : bwd_typed<float>(a, stage, s);
 }
 
 }  // namespace gk

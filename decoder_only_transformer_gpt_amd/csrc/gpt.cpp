@@ -51,16 +51,17 @@ constexpr int kHeadDim = 128;
 
 // Kernel tags (measurement). Order fixes the tag numbers.
 enum Tag : int {
-  K_EMBED = 0, K_RMSNORM, K_GEMM_QKV, K_ROPE_QKNORM, K_ATTN_FWD, K_GEMM_O, K_GEMM_W1, K_GEMM_W2, K_GEMM_LM,
-  K_CE_LOSS, K_CE_BWD, K_GEMM_LM_DW, K_GEMM_LM_DX, K_RMSNORM_BWD, K_GEMM_W2_DW, K_GEMM_W2_DX, K_GEMM_W1_DW,
-  K_GEMM_W1_DX, K_GEMM_O_DW, K_GEMM_O_DX, K_ATTN_BWD, K_ROPE_QKNORM_BWD, K_GEMM_QKV_DW, K_GEMM_QKV_DX,
-  K_EMBED_BWD, K_WEIGHT_T, K_NUM_TAGS
+  K_EMBED = 0, K_RMSNORM, K_GEMM_QKV, K_ROPE_QKNORM, K_ATTN_FWD_PREP, K_ATTN_FWD, K_GEMM_O, K_GEMM_W1, K_GEMM_W2,
+  K_GEMM_LM, K_CE_LOSS, K_CE_BWD, K_GEMM_LM_DW, K_GEMM_LM_DX, K_RMSNORM_BWD, K_GEMM_W2_DW, K_GEMM_W2_DX,
+  K_GEMM_W1_DW, K_GEMM_W1_DX, K_GEMM_O_DW, K_GEMM_O_DX, K_ATTN_BWD_PREP, K_ATTN_BWD_DQ, K_ATTN_BWD_DKV,
+  K_ROPE_QKNORM_BWD, K_GEMM_QKV_DW, K_GEMM_QKV_DX, K_EMBED_BWD, K_WEIGHT_T, K_NUM_TAGS
 };
 const char* kTagNames[K_NUM_TAGS] = {
-  "embed_rmsnorm", "rmsnorm", "gemm_qkv", "rope_qknorm", "attn_fwd", "gemm_o", "gemm_w1_relu2", "gemm_w2",
-  "gemm_lm_head_softcap", "ce_loss", "ce_bwd", "gemm_lm_head_dw", "gemm_lm_head_dx", "rmsnorm_bwd", "gemm_w2_dw",
-  "gemm_w2_dx", "gemm_w1_dw", "gemm_w1_dx_relu2bwd", "gemm_o_dw", "gemm_o_dx", "attn_bwd", "rope_qknorm_bwd",
-  "gemm_qkv_dw", "gemm_qkv_dx", "embed_bwd", "weight_transpose"};
+  "embed_rmsnorm", "rmsnorm", "gemm_qkv", "rope_qknorm", "attn_fwd_transpose", "attn_fwd", "gemm_o",
+  "gemm_w1_relu2", "gemm_w2", "gemm_lm_head_softcap", "ce_loss", "ce_bwd", "gemm_lm_head_dw", "gemm_lm_head_dx",
+  "rmsnorm_bwd", "gemm_w2_dw", "gemm_w2_dx", "gemm_w1_dw", "gemm_w1_dx_relu2bwd", "gemm_o_dw", "gemm_o_dx",
+  "attn_bwd_prep", "attn_bwd_dq", "attn_bwd_dkv", "rope_qknorm_bwd", "gemm_qkv_dw", "gemm_qkv_dx", "embed_bwd",
+  "weight_transpose"};
 
 struct Layout {  // byte offsets inside the workspace
   size_t flag, loss_rows, rope_cos, rope_sin;
@@ -468,8 +469,10 @@ gpt_status gpt_forward_loss(gpt_model* m, const int32_t* idx, const int32_t* tar
     RUN(K_ROPE_QKNORM, return gk::launch_rope_qknorm(dt, m->ws + L.qkv[l], B, T, H, c.norm_eps,
                                                      wsp<float>(m, L.rope_cos), wsp<float>(m, L.rope_sin),
                                                      wsp<float>(m, L.rstd_qk[l]), stream););
+    RUN(K_ATTN_FWD_PREP, return gk::launch_attn_fwd(dt, m->ws + L.qkv[l], B, T, H, m->ws + L.o[l],
+                                                    wsp<float>(m, L.lse[l]), m->ws + L.vT, 0, stream););
     RUN(K_ATTN_FWD, return gk::launch_attn_fwd(dt, m->ws + L.qkv[l], B, T, H, m->ws + L.o[l],
-                                               wsp<float>(m, L.lse[l]), m->ws + L.vT, stream););
+                                               wsp<float>(m, L.lse[l]), m->ws + L.vT, 1, stream););
     RUN(K_GEMM_O, {
       gk::GemmArgs a;
       a.tile = m->gemm_tile;
@@ -600,20 +603,20 @@ gpt_status gpt_backward(gpt_model* m, float dloss, int32_t accumulate, void* str
     // attention
     TRY(dw(K_GEMM_O_DW, m->ws + L.dres_lp, C, m->ws + L.o[l], HD, C, HD, m->off_o[l]));
     TRY(dx(K_GEMM_O_DX, gk::Epi::Store, m->ws + L.dres_lp, C, m->off_o[l], HD, C, m->ws + L.dout, nullptr));
-    RUN(K_ATTN_BWD, {
-      gk::AttnBwdArgs a;
-      a.qkv = m->ws + L.qkv[l];
-      a.o = m->ws + L.o[l];
-      a.dout = m->ws + L.dout;
-      a.lse = wsp<float>(m, L.lse[l]);
-      a.B = B; a.T = T; a.H = H;
-      a.delta = wsp<float>(m, L.delta);
-      a.qT = m->ws + L.qT;
-      a.kT = m->ws + L.kT;
-      a.doT = m->ws + L.doT;
-      a.dqkv = m->ws + L.dqkv;
-      return gk::launch_attn_bwd(dt, a, stream);
-    });
+    gk::AttnBwdArgs ab;
+    ab.qkv = m->ws + L.qkv[l];
+    ab.o = m->ws + L.o[l];
+    ab.dout = m->ws + L.dout;
+    ab.lse = wsp<float>(m, L.lse[l]);
+    ab.B = B; ab.T = T; ab.H = H;
+    ab.delta = wsp<float>(m, L.delta);
+    ab.qT = m->ws + L.qT;
+    ab.kT = m->ws + L.kT;
+    ab.doT = m->ws + L.doT;
+    ab.dqkv = m->ws + L.dqkv;
+    RUN(K_ATTN_BWD_PREP, return gk::launch_attn_bwd(dt, ab, 0, stream););
+    RUN(K_ATTN_BWD_DQ, return gk::launch_attn_bwd(dt, ab, 1, stream););
+    RUN(K_ATTN_BWD_DKV, return gk::launch_attn_bwd(dt, ab, 2, stream););
     RUN(K_ROPE_QKNORM_BWD, return gk::launch_rope_qknorm_bwd(dt, m->ws + L.dqkv, m->ws + L.qkv[l],
                                                              wsp<float>(m, L.rstd_qk[l]), B, T, H,
                                                              wsp<float>(m, L.rope_cos), wsp<float>(m, L.rope_sin),

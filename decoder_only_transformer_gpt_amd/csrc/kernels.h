@@ -61,8 +61,9 @@ hipError_t launch_rope_qknorm_bwd(int dtype, void* dqkv, const void* qkv, const 
 // Attention (causal, multi-query, head_dim 128) ----------------------------
 // Transposed copies use [B, heads, 128, Tp] with Tp = attn_padded_len(T).
 int attn_padded_len(int T);
-// vT: scratch of B * 128 * Tp elements.
-hipError_t launch_attn_fwd(int dtype, const void* qkv, int B, int T, int H, void* o, float* lse, void* vT,
+// vT: scratch of B * 128 * Tp elements. Stage 0 writes vT (the V transpose),
+// stage 1 runs the attention kernel; they are separate so each can be timed.
+hipError_t launch_attn_fwd(int dtype, const void* qkv, int B, int T, int H, void* o, float* lse, void* vT, int stage,
                            hipStream_t s);
 struct AttnBwdArgs {
   const void* qkv;   // [N, (H+2)*128] normalised q, k and v
@@ -76,7 +77,8 @@ struct AttnBwdArgs {
   void* doT;         // [B, H, 128, Tp] scratch
   void* dqkv;        // [N, (H+2)*128] output
 };
-hipError_t launch_attn_bwd(int dtype, const AttnBwdArgs& a, hipStream_t s);
+// Stage 0: transposed copies + delta; stage 1: dQ; stage 2: dK and dV.
+hipError_t launch_attn_bwd(int dtype, const AttnBwdArgs& a, int stage, hipStream_t s);
 
 // Cross-entropy -------------------------------------------------------------
 hipError_t launch_ce_loss(const float* part, int nparts, const float* ztgt, const int32_t* targets, int N,
