@@ -538,6 +538,441 @@ __global__ __launch_bounds__(256) void attn_dkv_kernel(const T* __restrict__ qkv
   }
 }
 
+// ============================================= bf16 kernels: LDS-direct ==
+// Tiles of 64 rows x 128 bf16 (256-byte rows) come in with direct-to-LDS
+// buffer loads: no staging registers, and rows past the sequence end read as
+// zero (buffer range check). A wave's load writes 1 KiB = 4 rows; each lane
+// picks the global 16-byte chunk it fetches so that chunk c of tile row r sits
+// at position c ^ (r & 15). Operands whose k index runs along a row (q.k over
+// D) are read as row fragments; operands whose k index runs down the rows
+// (V^T for P.V, K^T for dS.K, Q^T and dO^T for dK and dV) are read with the
+// transposing LDS read, so no transposed copies exist in global memory. Both
+// read patterns touch 16 distinct chunk positions per 16 lanes.
+//
+// Tiles cycle through four LDS stages: tile i+3 is requested while tile i is
+// consumed. Each wave waits only for its own oldest tile (vmcnt), then one
+// barrier makes every wave's part visible; stage (i+3) % 4 was last read in
+// step i-1, which every wave finished before that barrier. Past the last
+// tile the request repeats the last tile into a stage nothing reads again, so
+// every step issues the same loads and waits on the same count (which also
+// lets the compiler prove the reads of the current stage independent of the
+// loads in flight, instead of waiting for all of them).
+//
+// Softmax: P = exp2(S * log2(e)/sqrt(D) - lse * log2(e)) on v_exp_f32. Query
+// or key tiles that lie entirely on the allowed side of the diagonal skip the
+// mask; tiles entirely past it are skipped per wave.
+
+constexpr int kRowB = 256;          // bytes per tile row (128 bf16)
+constexpr int kTileB = 64 * kRowB;  // bytes per 64-row tile
+
+// Global byte offsets (from the tile's first row) of the lane's chunks in the
+// four 1 KiB loads of wave `wave` (tile rows 16*wave .. 16*wave + 15).
+DEV void tile_offsets(uint32_t (&vo)[4], int wave, int lane, uint32_t ld_b) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = (wave * 4 + i) * 4 + (lane >> 4);
+    const int c = (lane & 15) ^ (r & 15);
+    vo[i] = (uint32_t)r * ld_b + (uint32_t)c * 16u;
+  }
+}
+DEV void tile_issue(__amdgpu_buffer_rsrc_t rs, char* tile, const uint32_t (&vo)[4], int wave) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) lds_direct16(rs, tile + (wave * 4 + i) * 1024, vo[i]);
+}
+
+// Row fragment: lane (l32, g) reads row 32*blk + l32, k chunk 2*ks + g.
+struct RowFrag {
+  int base, w;
+  DEV explicit RowFrag(int lane) {
+    const int l32 = lane & 31, g = lane >> 5;
+    base = l32 * kRowB;
+    w = g ^ (l32 & 15);
+  }
+  DEV int off(int blk, int ks) const { return blk * 32 * kRowB + base + (((2 * ks) ^ w) << 4); }
+};
+
+// Transposed fragment: A operand of C[d][j] = sum_k X[k][d] B[k][j] for a row
+// tile X (k = tile row). MFMA k-step kk covers rows 16kk .. 16kk + 15; the
+// lane's 8 k values are rows 16kk + 4g + e, then 16kk + 8 + 4g + e (e = 0..3),
+// the accumulator rows pack_frag hands the same lane. Column block db: lane
+// l32 gets column 32*db + l32.
+struct TrFrag {
+  int b0, b1, y0, y1;
+  DEV explicit TrFrag(int lane) {
+    const int g = lane >> 5, e = (lane >> 2) & 3, c = lane & 3, grp = lane >> 4;
+    const int c0 = 2 * (grp & 1) + (c >> 1);  // chunk inside a 32-column block
+    const int x0 = 4 * g + e, x1 = 8 + 4 * g + e;
+    b0 = x0 * kRowB + (c & 1) * 8;
+    b1 = x1 * kRowB + (c & 1) * 8;
+    y0 = c0 ^ x0;
+    y1 = c0 ^ x1;
+  }
+  DEV u32x4 read(const char* tile, int kk, int db) const {
+    const u32x2 a = ld_tr16(tile + kk * 16 * kRowB + b0 + (((db * 4) ^ y0) << 4));
+    const u32x2 b = ld_tr16(tile + kk * 16 * kRowB + b1 + (((db * 4) ^ y1) << 4));
+    return u32x4{a[0], a[1], b[0], b[1]};
+  }
+};
+
+// Row fragments of the lane's own row (32 rows per wave) straight from global
+// memory: 16-byte chunk 2*ks + g of row `row`; rows at or past `rows` read zero.
+DEV void load_row_frags(u32x4 (&f)[8], const void* base, int rows, uint32_t ld_b, int row, int g) {
+  const __amdgpu_buffer_rsrc_t rs = uniform_rsrc(base, rows > 0 ? rows * (int)ld_b : 0);
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks)
+    f[ks] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)row * ld_b +
+                                                                            (uint32_t)(ks * 2 + g) * 16u, 0, 0));
+}
+
+DEV float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+struct KvStage {
+  char k[kTileB];
+  char v[kTileB];
+};
+
+// ---------------------------------------------------------- forward (bf16) --
+// Block: 128 queries of one (batch, head) = 4 waves x 32; key tiles of 64.
+// S^T = K Q^T puts each query on one lane (its row sum stays in the lane).
+template <bool MASK>
+DEV void fwd_tile(const KvStage& s, const RowFrag& rf, const TrFrag& tf, const u32x4 (&qf)[8], f32x16 (&acc)[4],
+                  float& rsum, float sl2, float sh2, int krel, int g) {
+  f32x16 sc[2];
+#pragma unroll
+  for (int kb2 = 0; kb2 < 2; ++kb2) {
+    sc[kb2] = zero16();
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) sc[kb2] = mfma16(ld16(s.k + rf.off(kb2, ks)), qf[ks], sc[kb2], (bf16*)nullptr);
+  }
+#pragma unroll
+  for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float p = fast_exp2(sc[kb2][i] * sl2 - sh2);
+      // key (tile row kb2*32 + (i/4)*8 + 4g + i%4) <= query
+      if (MASK) p = (kb2 * 32 + (i >> 2) * 8 + (i & 3) + krel <= 0) ? p : 0.f;
+      sc[kb2][i] = p;
+      rsum += p;
+    }
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const u32x4 pf = pack_frag<bf16>(sc[kk >> 1], kk & 1);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) acc[db] = mfma16(tf.read(s.v, kk, db), pf, acc[db], (bf16*)nullptr);
+  }
+  (void)g;
+}
+
+__global__ __launch_bounds__(256, 1) void attn_fwd_bf16_kernel(const bf16* __restrict__ qkv, int T_, int H,
+                                                               bf16* __restrict__ o, float* __restrict__ lse) {
+  __shared__ __attribute__((aligned(1024))) KvStage st0, st1, st2, st3;
+  const int nqb = (T_ + 127) / 128;
+  int b, r;
+  xcd_row_map(blockIdx.x, gridDim.x / (nqb * H), nqb * H, b, r);
+  const int qb = nqb - 1 - r / H, h = r % H;  // heavy (late) query blocks first
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t ld = (int64_t)(H + 2) * D;
+  const uint32_t ld_b = (uint32_t)ld * 2u;
+  const bf16* base = qkv + (int64_t)b * T_ * ld;
+  const int qw = qb * 128 + wave * 32;  // the wave's first query
+  const int q = qw + l32;
+
+  u32x4 qf[8];
+  load_row_frags(qf, base + (int64_t)qw * ld + h * D, T_ - qw, ld_b, l32, g);
+  f32x16 acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = zero16();
+  float rsum = 0.f;
+  const float shift = sqrtf((float)D);
+  const float sl2 = kLog2e / shift, sh2 = shift * kLog2e;
+  const int nt = (min(T_, qb * 128 + 128) + 63) / 64;
+
+  uint32_t vo[4];
+  tile_offsets(vo, wave, lane, ld_b);
+  const RowFrag rf(lane);
+  const TrFrag tf(lane);
+  auto issue = [&](int t, KvStage& s) {
+    const int k0 = t * 64, rows = min(64, T_ - k0);
+    const bf16* kp = base + (int64_t)k0 * ld + H * D;
+    tile_issue(uniform_rsrc(kp, rows * (int)ld_b), s.k, vo, wave);
+    tile_issue(uniform_rsrc(kp + D, rows * (int)ld_b), s.v, vo, wave);
+  };
+  auto step = [&](int t, const KvStage& cur, KvStage& nxt) {
+    wait_vmcnt<2 * 8>();  // this wave's part of tile t has landed
+    __builtin_amdgcn_s_barrier();
+    issue(min(t + 3, nt - 1), nxt);
+    const int k0 = t * 64;
+    if (k0 > qw + 31) return;                       // every key after every query of this wave
+    if (k0 + 63 <= qw) fwd_tile<false>(cur, rf, tf, qf, acc, rsum, sl2, sh2, 0, g);
+    else fwd_tile<true>(cur, rf, tf, qf, acc, rsum, sl2, sh2, k0 + 4 * g - q, g);
+  };
+  issue(0, st0);
+  issue(min(1, nt - 1), st1);
+  issue(min(2, nt - 1), st2);
+  for (int t = 0; t < nt; t += 4) {
+    step(t, st0, st3);
+    if (t + 1 < nt) step(t + 1, st1, st0);
+    if (t + 2 < nt) step(t + 2, st2, st1);
+    if (t + 3 < nt) step(t + 3, st3, st2);
+  }
+  wait_vmcnt<0>();
+  rsum += __shfl_xor(rsum, 32, 64);
+  if (q < T_) {
+    const float inv = 1.f / rsum;
+    bf16* op = o + ((int64_t)b * T_ + q) * H * D + h * D;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk) {
+        float v[4] = {acc[db][blk * 4] * inv, acc[db][blk * 4 + 1] * inv, acc[db][blk * 4 + 2] * inv,
+                      acc[db][blk * 4 + 3] * inv};
+        store4(op + db * 32 + blk * 8 + g * 4, v);
+      }
+    if (g == 0) lse[((int64_t)b * H + h) * T_ + q] = shift + logf(rsum);
+  }
+}
+
+// --------------------------------------------------------------- dQ (bf16) --
+// Block: 128 queries of one (batch, head) = 4 waves x 32; key tiles of 64.
+template <bool MASK>
+DEV void dq_tile(const KvStage& s, const RowFrag& rf, const TrFrag& tf, const u32x4 (&qf)[8], const u32x4 (&df)[8],
+                 f32x16 (&acc)[4], float sl2, float l2, float dlt, int krel) {
+  f32x16 sc[2], dp[2];
+#pragma unroll
+  for (int kb2 = 0; kb2 < 2; ++kb2) {
+    sc[kb2] = zero16();
+    dp[kb2] = zero16();
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      sc[kb2] = mfma16(ld16(s.k + rf.off(kb2, ks)), qf[ks], sc[kb2], (bf16*)nullptr);
+      dp[kb2] = mfma16(ld16(s.v + rf.off(kb2, ks)), df[ks], dp[kb2], (bf16*)nullptr);
+    }
+  }
+#pragma unroll
+  for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float p = fast_exp2(sc[kb2][i] * sl2 - l2);
+      if (MASK) p = (kb2 * 32 + (i >> 2) * 8 + (i & 3) + krel <= 0) ? p : 0.f;
+      dp[kb2][i] = p * (dp[kb2][i] - dlt);
+    }
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const u32x4 sf = pack_frag<bf16>(dp[kk >> 1], kk & 1);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) acc[db] = mfma16(tf.read(s.k, kk, db), sf, acc[db], (bf16*)nullptr);
+  }
+}
+
+__global__ __launch_bounds__(256, 1) void attn_dq_bf16_kernel(const bf16* __restrict__ qkv,
+                                                              const bf16* __restrict__ dout,
+                                                              const float* __restrict__ lse,
+                                                              const float* __restrict__ delta, int T_, int H,
+                                                              bf16* __restrict__ dqkv) {
+  __shared__ __attribute__((aligned(1024))) KvStage st0, st1, st2, st3;
+  const int nqb = (T_ + 127) / 128;
+  int b, r;
+  xcd_row_map(blockIdx.x, gridDim.x / (nqb * H), nqb * H, b, r);
+  const int qb = nqb - 1 - r / H, h = r % H;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t ld = (int64_t)(H + 2) * D;
+  const uint32_t ld_b = (uint32_t)ld * 2u;
+  const bf16* base = qkv + (int64_t)b * T_ * ld;
+  const int qw = qb * 128 + wave * 32;
+  const int q = qw + l32;
+  const bool qv = q < T_;
+
+  u32x4 qf[8], df[8];
+  load_row_frags(qf, base + (int64_t)qw * ld + h * D, T_ - qw, ld_b, l32, g);
+  load_row_frags(df, dout + ((int64_t)b * T_ + qw) * H * D + h * D, T_ - qw, (uint32_t)H * D * 2u, l32, g);
+  const int64_t si = ((int64_t)b * H + h) * T_ + q;
+  const float l2 = qv ? lse[si] * kLog2e : 0.f;
+  const float dlt = qv ? delta[si] : 0.f;
+  const float scale = rsqrtf((float)D);
+  const float sl2 = kLog2e * scale;
+  f32x16 acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = zero16();
+  const int nt = (min(T_, qb * 128 + 128) + 63) / 64;
+
+  uint32_t vo[4];
+  tile_offsets(vo, wave, lane, ld_b);
+  const RowFrag rf(lane);
+  const TrFrag tf(lane);
+  auto issue = [&](int t, KvStage& s) {
+    const int k0 = t * 64, rows = min(64, T_ - k0);
+    const bf16* kp = base + (int64_t)k0 * ld + H * D;
+    tile_issue(uniform_rsrc(kp, rows * (int)ld_b), s.k, vo, wave);
+    tile_issue(uniform_rsrc(kp + D, rows * (int)ld_b), s.v, vo, wave);
+  };
+  auto step = [&](int t, const KvStage& cur, KvStage& nxt) {
+    wait_vmcnt<2 * 8>();  // this wave's part of tile t has landed
+    __builtin_amdgcn_s_barrier();
+    issue(min(t + 3, nt - 1), nxt);
+    const int k0 = t * 64;
+    if (k0 > qw + 31) return;
+    if (k0 + 63 <= qw) dq_tile<false>(cur, rf, tf, qf, df, acc, sl2, l2, dlt, 0);
+    else dq_tile<true>(cur, rf, tf, qf, df, acc, sl2, l2, dlt, k0 + 4 * g - q);
+  };
+  issue(0, st0);
+  issue(min(1, nt - 1), st1);
+  issue(min(2, nt - 1), st2);
+  for (int t = 0; t < nt; t += 4) {
+    step(t, st0, st3);
+    if (t + 1 < nt) step(t + 1, st1, st0);
+    if (t + 2 < nt) step(t + 2, st2, st1);
+    if (t + 3 < nt) step(t + 3, st3, st2);
+  }
+  wait_vmcnt<0>();
+  if (qv) {
+    bf16* outp = dqkv + ((int64_t)b * T_ + q) * ld + h * D;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk) {
+        float v[4] = {acc[db][blk * 4] * scale, acc[db][blk * 4 + 1] * scale, acc[db][blk * 4 + 2] * scale,
+                      acc[db][blk * 4 + 3] * scale};
+        store4(outp + db * 32 + blk * 8 + g * 4, v);
+      }
+  }
+}
+
+// ---------------------------------------------------------- dK, dV (bf16) --
+// Block: 128 keys of one batch row (4 waves x 32 keys), summed over every
+// query head and every query tile at or after the keys. Steps walk (query
+// tile, head) pairs in one descending order for every key block, so blocks
+// of a batch row running side by side read the same Q/dO tiles together.
+struct DkvStage {
+  char q[kTileB];
+  char d[kTileB];
+  float l[4][64];  // lse of the tile's queries (one copy per wave)
+  float e[4][64];  // delta
+};
+
+template <bool MASK>
+DEV void dkv_tile(const DkvStage& s, int wave, const RowFrag& rf, const TrFrag& tf, const u32x4 (&kf)[8],
+                  const u32x4 (&vf)[8], f32x16 (&adk)[4], f32x16 (&adv)[4], float sl2, int qrel, int g) {
+  f32x16 sc[2], dp[2];
+#pragma unroll
+  for (int qb2 = 0; qb2 < 2; ++qb2) {
+    sc[qb2] = zero16();
+    dp[qb2] = zero16();
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      sc[qb2] = mfma16(ld16(s.q + rf.off(qb2, ks)), kf[ks], sc[qb2], (bf16*)nullptr);
+      dp[qb2] = mfma16(ld16(s.d + rf.off(qb2, ks)), vf[ks], dp[qb2], (bf16*)nullptr);
+    }
+  }
+#pragma unroll
+  for (int qb2 = 0; qb2 < 2; ++qb2)
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) {
+      const int q4 = qb2 * 32 + blk * 8 + g * 4;
+      const f32x4 L = *reinterpret_cast<const f32x4*>(&s.l[wave][q4]);
+      const f32x4 E = *reinterpret_cast<const f32x4*>(&s.e[wave][q4]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = blk * 4 + r;
+        float p = fast_exp2(sc[qb2][i] * sl2 - L[r] * kLog2e);
+        // query (tile row qb2*32 + blk*8 + 4g + r) >= key
+        if (MASK) p = (qb2 * 32 + blk * 8 + r + qrel >= 0) ? p : 0.f;
+        sc[qb2][i] = p;
+        dp[qb2][i] = p * (dp[qb2][i] - E[r]);
+      }
+    }
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const u32x4 pf = pack_frag<bf16>(sc[kk >> 1], kk & 1);
+    const u32x4 sf = pack_frag<bf16>(dp[kk >> 1], kk & 1);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      adv[db] = mfma16(tf.read(s.d, kk, db), pf, adv[db], (bf16*)nullptr);
+      adk[db] = mfma16(tf.read(s.q, kk, db), sf, adk[db], (bf16*)nullptr);
+    }
+  }
+}
+
+__global__ __launch_bounds__(256, 1) void attn_dkv_bf16_kernel(const bf16* __restrict__ qkv,
+                                                               const bf16* __restrict__ dout,
+                                                               const float* __restrict__ lse,
+                                                               const float* __restrict__ delta, int T_, int H,
+                                                               bf16* __restrict__ dqkv) {
+  __shared__ __attribute__((aligned(1024))) DkvStage st0, st1, st2, st3;
+  const int nkb = (T_ + 127) / 128;
+  int b, kb;
+  xcd_row_map(blockIdx.x, gridDim.x / nkb, nkb, b, kb);  // key block 0 (most query tiles) first
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t ld = (int64_t)(H + 2) * D;
+  const uint32_t ld_b = (uint32_t)ld * 2u, ldo_b = (uint32_t)H * D * 2u;
+  const bf16* base = qkv + (int64_t)b * T_ * ld;
+  const int kw = kb * 128 + wave * 32;  // the wave's first key
+  const int key = kw + l32;
+
+  u32x4 kf[8], vf[8];
+  load_row_frags(kf, base + (int64_t)kw * ld + H * D, T_ - kw, ld_b, l32, g);
+  load_row_frags(vf, base + (int64_t)kw * ld + (H + 1) * D, T_ - kw, ld_b, l32, g);
+  const float scale = rsqrtf((float)D);
+  const float sl2 = kLog2e * scale;
+  f32x16 adk[4], adv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    adk[i] = zero16();
+    adv[i] = zero16();
+  }
+  const int nqt = (T_ + 63) / 64, nq = nqt - 2 * kb;
+  const int total = H * nq;
+
+  uint32_t voq[4], vod[4];
+  tile_offsets(voq, wave, lane, ld_b);
+  tile_offsets(vod, wave, lane, ldo_b);
+  const RowFrag rf(lane);
+  const TrFrag tf(lane);
+  auto issue = [&](int it, DkvStage& s) {
+    const int h = it % H, q0 = (nqt - 1 - it / H) * 64, rows = min(64, T_ - q0);
+    tile_issue(uniform_rsrc(base + (int64_t)q0 * ld + h * D, rows * (int)ld_b), s.q, voq, wave);
+    tile_issue(uniform_rsrc(dout + ((int64_t)b * T_ + q0) * H * D + h * D, rows * (int)ldo_b), s.d, vod, wave);
+    const int64_t lo = ((int64_t)b * H + h) * T_ + q0;
+    lds_direct4(uniform_rsrc(lse + lo, rows * 4), &s.l[wave][0], (uint32_t)lane * 4u);
+    lds_direct4(uniform_rsrc(delta + lo, rows * 4), &s.e[wave][0], (uint32_t)lane * 4u);
+  };
+  auto step = [&](int it, const DkvStage& cur, DkvStage& nxt) {
+    wait_vmcnt<2 * 10>();  // this wave's part of step it's tiles has landed
+    __builtin_amdgcn_s_barrier();
+    issue(min(it + 3, total - 1), nxt);
+    const int q0 = (nqt - 1 - it / H) * 64;
+    if (q0 + 63 < kw) return;  // every query before every key of this wave
+    if (q0 >= kw + 31) dkv_tile<false>(cur, wave, rf, tf, kf, vf, adk, adv, sl2, 0, g);
+    else dkv_tile<true>(cur, wave, rf, tf, kf, vf, adk, adv, sl2, q0 + 4 * g - key, g);
+  };
+  issue(0, st0);
+  issue(min(1, total - 1), st1);
+  issue(min(2, total - 1), st2);
+  for (int it = 0; it < total; it += 4) {
+    step(it, st0, st3);
+    if (it + 1 < total) step(it + 1, st1, st0);
+    if (it + 2 < total) step(it + 2, st2, st1);
+    if (it + 3 < total) step(it + 3, st3, st2);
+  }
+  wait_vmcnt<0>();
+  if (key < T_) {
+    bf16* outk = dqkv + ((int64_t)b * T_ + key) * ld + H * D;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk) {
+        const int d = db * 32 + blk * 8 + g * 4;
+        float vk[4] = {adk[db][blk * 4] * scale, adk[db][blk * 4 + 1] * scale, adk[db][blk * 4 + 2] * scale,
+                       adk[db][blk * 4 + 3] * scale};
+        float vv[4] = {adv[db][blk * 4], adv[db][blk * 4 + 1], adv[db][blk * 4 + 2], adv[db][blk * 4 + 3]};
+        store4(outk + d, vk);
+        store4(outk + D + d, vv);
+      }
+  }
+}
+
 template <typename T>
 hipError_t transpose(const void* src, int64_t ld, int col0, int nh, int B, int T_, int Tp, void* dst, hipStream_t s) {
   hipLaunchKernelGGL(transpose_heads_kernel<T>, dim3(Tp / 64, nh, B), dim3(256), 0, s, (const T*)src, ld, col0, nh,
@@ -548,8 +983,13 @@ hipError_t transpose(const void* src, int64_t ld, int col0, int nh, int B, int T
 template <typename T>
 hipError_t fwd_typed(const void* qkv, int B, int T_, int H, void* o, float* lse, void* vT, int stage, hipStream_t s) {
   const int Tp = attn_padded_len(T_);
-  if (stage == 0) return transpose<T>(qkv, (int64_t)(H + 2) * D, (H + 1) * D, 1, B, T_, Tp, vT, s);
   dim3 grid(((T_ + 127) / 128) * H * B);
+  if constexpr (sizeof(T) == 2) {
+    if (stage == 0) return hipSuccess;  // no transposed copy on this path
+    hipLaunchKernelGGL(attn_fwd_bf16_kernel, grid, dim3(256), 0, s, (const bf16*)qkv, T_, H, (bf16*)o, lse);
+    return hipGetLastError();
+  }
+  if (stage == 0) return transpose<T>(qkv, (int64_t)(H + 2) * D, (H + 1) * D, 1, B, T_, Tp, vT, s);
   hipLaunchKernelGGL(attn_fwd_kernel<T>, grid, dim3(256), 0, s, (const T*)qkv, (const T*)vT, T_, Tp, H, (T*)o, lse);
   return hipGetLastError();
 }
@@ -559,20 +999,33 @@ hipError_t bwd_typed(const AttnBwdArgs& a, int stage, hipStream_t s) {
   const int T_ = a.T, H = a.H, B = a.B;
   const int Tp = attn_padded_len(T_);
   const int64_t ld = (int64_t)(H + 2) * D;
+  constexpr bool kBf16 = sizeof(T) == 2;
   hipError_t e;
   if (stage == 0) {
-    if ((e = transpose<T>(a.qkv, ld, 0, H, B, T_, Tp, a.qT, s)) != hipSuccess) return e;
-    if ((e = transpose<T>(a.qkv, ld, H * D, 1, B, T_, Tp, a.kT, s)) != hipSuccess) return e;
-    if ((e = transpose<T>(a.dout, (int64_t)H * D, 0, H, B, T_, Tp, a.doT, s)) != hipSuccess) return e;
+    if (!kBf16) {
+      if ((e = transpose<T>(a.qkv, ld, 0, H, B, T_, Tp, a.qT, s)) != hipSuccess) return e;
+      if ((e = transpose<T>(a.qkv, ld, H * D, 1, B, T_, Tp, a.kT, s)) != hipSuccess) return e;
+      if ((e = transpose<T>(a.dout, (int64_t)H * D, 0, H, B, T_, Tp, a.doT, s)) != hipSuccess) return e;
+    }
     const int64_t groups = (int64_t)B * T_ * H;
     hipLaunchKernelGGL(attn_delta_kernel<T>, dim3((unsigned)((groups * 16 + 255) / 256)), dim3(256), 0, s,
                        (const T*)a.o, (const T*)a.dout, B * T_, T_, H, a.delta);
   } else if (stage == 1) {
-    hipLaunchKernelGGL(attn_dq_kernel<T>, dim3(((T_ + 127) / 128) * H * B), dim3(256), 0, s, (const T*)a.qkv,
-                       (const T*)a.kT, (const T*)a.dout, a.lse, a.delta, T_, Tp, H, (T*)a.dqkv);
+    const dim3 grid(((T_ + 127) / 128) * H * B);
+    if constexpr (kBf16)
+      hipLaunchKernelGGL(attn_dq_bf16_kernel, grid, dim3(256), 0, s, (const bf16*)a.qkv, (const bf16*)a.dout, a.lse,
+                         a.delta, T_, H, (bf16*)a.dqkv);
+    else
+      hipLaunchKernelGGL(attn_dq_kernel<T>, grid, dim3(256), 0, s, (const T*)a.qkv, (const T*)a.kT,
+                         (const T*)a.dout, a.lse, a.delta, T_, Tp, H, (T*)a.dqkv);
   } else {
-    hipLaunchKernelGGL(attn_dkv_kernel<T>, dim3(((T_ + 127) / 128) * B), dim3(256), 0, s, (const T*)a.qkv,
-                       (const T*)a.qT, (const T*)a.dout, (const T*)a.doT, a.lse, a.delta, T_, Tp, H, (T*)a.dqkv);
+    const dim3 grid(((T_ + 127) / 128) * B);
+    if constexpr (kBf16)
+      hipLaunchKernelGGL(attn_dkv_bf16_kernel, grid, dim3(256), 0, s, (const bf16*)a.qkv, (const bf16*)a.dout,
+                         a.lse, a.delta, T_, H, (bf16*)a.dqkv);
+    else
+      hipLaunchKernelGGL(attn_dkv_kernel<T>, grid, dim3(256), 0, s, (const T*)a.qkv, (const T*)a.qT,
+                         (const T*)a.dout, (const T*)a.doT, a.lse, a.delta, T_, Tp, H, (T*)a.dqkv);
   }
   return hipGetLastError();
 }

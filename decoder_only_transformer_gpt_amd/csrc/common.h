@@ -119,6 +119,57 @@ DEV f32x16 mfma16(u32x4 a, u32x4 b, f32x16 c, float*) {
   return c;
 }
 
+// ------------------------------------------------- buffer loads to LDS -----
+// Buffer resource over [p, p + bytes) (raw, stride 0): loads at offsets past
+// `bytes` return zero. Made wave-uniform (SGPRs) with readfirstlane; callers
+// pass block-uniform values. `bytes` must be below 2^31.
+DEV __amdgpu_buffer_rsrc_t uniform_rsrc(const void* p, int bytes) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  const int n = __builtin_amdgcn_readfirstlane(bytes);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), (short)0, n, 0x00020000);
+}
+
+// Direct-to-LDS buffer loads: lane L of the wave writes LDS bytes
+// [lds + 16L, lds + 16L + 16) (resp. 4 bytes at lds + 4L); `lds` must be
+// wave-uniform. The address-space cast only exists in the device pass.
+DEV void lds_direct16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
+#endif
+}
+DEV void lds_direct4(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4, voff, 0, 0, 0);
+#endif
+}
+
+// s_waitcnt on the vector-memory counter only: wait until at most n (< 64)
+// vector loads of this wave are outstanding (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14, expcnt and lgkmcnt left at their maxima).
+template <int N>
+DEV void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(((N >> 4) << 14) | (0x7 << 4) | (0xF << 8) | (N & 15));
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16). Within each group of 16 lanes,
+// lane j names 8 bytes (4 consecutive 16-bit values) at its address; lane i
+// receives value (i % 4) of lane 4e + i/4 as its element e, e = 0..3. Pointing
+// lane 4e + c at row r_e, columns [col0 + 4c, col0 + 4c + 4) of a row-major
+// tile therefore hands lane i column col0 + i of rows r_0..r_3.
+DEV u32x2 ld_tr16(const void* p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
+  return __builtin_bit_cast(u32x2, v);
+#else
+  (void)p;
+  return u32x2{0, 0};
+#endif
+}
+
 // -------------------------------------------------------- device flag ------
 // Bit 0: a token id outside [0, V). Set with a plain vector store (no atomics
 // needed: every writer stores the same bit pattern).

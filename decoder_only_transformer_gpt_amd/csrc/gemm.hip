@@ -437,15 +437,6 @@ struct Epilogue<T, Epi::GradF32> {
   }
 };
 
-// 16-byte direct-to-LDS buffer load: lane L of the wave writes LDS bytes
-// [lds + 16L, lds + 16L + 16) (lds must be wave-uniform). The address-space
-// cast only exists in the device pass.
-DEV void lds_direct16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
-#endif
-}
-
 // bf16 GEMM with both operands k-contiguous (y = x W^T and, with a
 // transposed weight copy, dx = dy W), fed by direct-to-LDS buffer loads.
 //
@@ -504,20 +495,11 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_nt_lds_kernel(GemmArgs arg
 #pragma unroll
   for (int i = 0; i < LB; ++i) vob[i] = (uint32_t)((wave * LB + i) * 16 + lrow) * ldb_b + lchunk * 16u;
 
-  // buffer resources must be wave-uniform (SGPRs): build them from
-  // readfirstlane'd pointer halves and record counts
-  auto uni_rsrc = [](const void* p, int rec) {
-    const uint64_t v = (uint64_t)p;
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-    const int n = __builtin_amdgcn_readfirstlane(rec);
-    return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), (short)0, n, 0x00020000);
-  };
   auto stage = [&](int q) -> char* { return q == 0 ? st0 : q == 1 ? st1 : q == 2 ? st2 : st3; };
   auto issue = [&](int kt, char* st) {
     const int k0 = kt * BK;
-    const __amdgpu_buffer_rsrc_t ra = uni_rsrc(Ap + k0, rec_a);
-    const __amdgpu_buffer_rsrc_t rb = uni_rsrc(Bp + k0, rec_b);
+    const __amdgpu_buffer_rsrc_t ra = uniform_rsrc(Ap + k0, rec_a);
+    const __amdgpu_buffer_rsrc_t rb = uniform_rsrc(Bp + k0, rec_b);
 #pragma unroll
     for (int i = 0; i < LA; ++i)
       lds_direct16(ra, st + (wave * LA + i) * 1024, voa[i]);
