@@ -11,6 +11,8 @@
 // |s| <= sqrt(D) ~ 11.31 and exp(s - sqrt(D)) lies in [e^-22.7, ~1]. The row
 // sum therefore accumulates without a running maximum or rescaling, and
 // lse = sqrt(D) + log(sum) is exact up to rounding. (This relies on QK-norm.)
+// The forward stores it in base-2 units, lse * log2(e), the form every
+// backward kernel consumes: P = exp2(S * log2(e)/sqrt(D) - lse * log2(e)).
 //
 // All contractions run on MFMA 32x32 tiles. The kernels put the dimension
 // that is reduced over on the accumulator's lane axis where it helps: the
@@ -29,6 +31,8 @@
 //
 // qkv row (one token): [H query heads | K | V] x 128. LSE and delta are fp32
 // [B, H, T]. Grid blocks are ordered heavy-first for causal load balance.
+
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -262,7 +266,7 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const T* __restrict__ qkv
                       acc[db][blk * 4 + 3] * inv};
         store4(op + db * 32 + blk * 8 + g * 4, v);
       }
-    if (g == 0) lse[((int64_t)b * H + h) * T_ + q] = shift + logf(rsum);
+    if (g == 0) lse[((int64_t)b * H + h) * T_ + q] = sh2 + log2f(rsum);
   }
 }
 
@@ -324,7 +328,7 @@ __global__ __launch_bounds__(256) void attn_dq_kernel(const T* __restrict__ qkv,
   const float lq = qv ? lse[((int64_t)b * H + h) * T_ + q] : 0.f;
   const float dq_ = qv ? delta[((int64_t)b * H + h) * T_ + q] : 0.f;
   const float scale = rsqrtf((float)D);
-  const float sl2 = kLog2e * scale, l2 = lq * kLog2e;
+  const float sl2 = kLog2e * scale, l2 = lq;
 
   f32x16 acc[4];
 #pragma unroll
@@ -501,7 +505,7 @@ __global__ __launch_bounds__(256) void attn_dkv_kernel(const T* __restrict__ qkv
           const int qi = qb2 * 32 + blk * 8 + g * 4 + r;
           const int qq = q0 + qi;
           const int i = blk * 4 + r;
-          const float pv = (qq >= key && qq < T_ && kv) ? exp2f(s[i] * sl2 - Ls[cur][qi] * kLog2e) : 0.f;
+          const float pv = (qq >= key && qq < T_ && kv) ? exp2f(s[i] * sl2 - Ls[cur][qi]) : 0.f;
           p[qb2][i] = pv;
           ds[qb2][i] = pv * (dpv[i] - Es[cur][qi]);
         }
@@ -558,11 +562,13 @@ __global__ __launch_bounds__(256) void attn_dkv_kernel(const T* __restrict__ qkv
 // lets the compiler prove the reads of the current stage independent of the
 // loads in flight, instead of waiting for all of them).
 //
-// Softmax: P = exp2(S * log2(e)/sqrt(D) - lse * log2(e)) on v_exp_f32. Query
+// Softmax: P = exp2(S * log2(e)/sqrt(D) - lse2) on v_exp_f32. Query
 // or key tiles that lie entirely on the allowed side of the diagonal skip the
 // mask; tiles entirely past it are skipped per wave.
 
 constexpr int kRowB = 256;          // bytes per tile row (128 bf16)
+constexpr int kFwdStages = 2;       // 64 KiB of LDS: two blocks per CU
+constexpr int kDqStages = 4;
 constexpr int kTileB = 64 * kRowB;  // bytes per 64-row tile
 
 // Global byte offsets (from the tile's first row) of the lane's chunks in the
@@ -636,14 +642,28 @@ struct KvStage {
 // S^T = K Q^T puts each query on one lane (its row sum stays in the lane).
 template <bool MASK>
 DEV void fwd_tile(const KvStage& s, const RowFrag& rf, const TrFrag& tf, const u32x4 (&qf)[8], f32x16 (&acc)[4],
-                  float& rsum, float sl2, float sh2, int krel, int g) {
+                  float& rsum, float sl2, float sh2, int krel) {
   f32x16 sc[2];
+  // key rows 0-31, then 32-63; fragments read ahead, re-filled as consumed
+  u32x4 fa[8];
 #pragma unroll
-  for (int kb2 = 0; kb2 < 2; ++kb2) {
-    sc[kb2] = zero16();
+  for (int ks = 0; ks < 8; ++ks) fa[ks] = ld16(s.k + rf.off(0, ks));
+  sc[0] = zero16();
+  sc[1] = zero16();
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) sc[kb2] = mfma16(ld16(s.k + rf.off(kb2, ks)), qf[ks], sc[kb2], (bf16*)nullptr);
+  for (int ks = 0; ks < 8; ++ks) {
+    sc[0] = mfma16(fa[ks], qf[ks], sc[0], (bf16*)nullptr);
+    fa[ks] = ld16(s.k + rf.off(1, ks));
   }
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) sc[1] = mfma16(fa[ks], qf[ks], sc[1], (bf16*)nullptr);
+  __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
 #pragma unroll
   for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
@@ -657,15 +677,21 @@ DEV void fwd_tile(const KvStage& s, const RowFrag& rf, const TrFrag& tf, const u
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
     const u32x4 pf = pack_frag<bf16>(sc[kk >> 1], kk & 1);
+    u32x4 tv[4];
 #pragma unroll
-    for (int db = 0; db < 4; ++db) acc[db] = mfma16(tf.read(s.v, kk, db), pf, acc[db], (bf16*)nullptr);
+    for (int db = 0; db < 4; ++db) tv[db] = tf.read(s.v, kk, db);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) acc[db] = mfma16(tv[db], pf, acc[db], (bf16*)nullptr);
   }
-  (void)g;
 }
 
-__global__ __launch_bounds__(256, 1) void attn_fwd_bf16_kernel(const bf16* __restrict__ qkv, int T_, int H,
-                                                               bf16* __restrict__ o, float* __restrict__ lse) {
-  __shared__ __attribute__((aligned(1024))) KvStage st0, st1, st2, st3;
+template <int NST>
+__global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void attn_fwd_bf16_kernel(const bf16* __restrict__ qkv, int T_,
+                                                                              int H, bf16* __restrict__ o,
+                                                                              float* __restrict__ lse) {
+  static_assert(NST == 2 || NST == 4, "two or four stages");
+  __shared__ __attribute__((aligned(1024))) KvStage st0, st1;
+  __shared__ __attribute__((aligned(1024))) std::conditional_t<NST == 4, KvStage, char[16]> st2, st3;
   const int nqb = (T_ + 127) / 128;
   int b, r;
   xcd_row_map(blockIdx.x, gridDim.x / (nqb * H), nqb * H, b, r);
@@ -699,22 +725,30 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_bf16_kernel(const bf16* __res
     tile_issue(uniform_rsrc(kp + D, rows * (int)ld_b), s.v, vo, wave);
   };
   auto step = [&](int t, const KvStage& cur, KvStage& nxt) {
-    wait_vmcnt<2 * 8>();  // this wave's part of tile t has landed
+    wait_vmcnt<(NST - 2) * 8>();  // this wave's part of tile t has landed
     __builtin_amdgcn_s_barrier();
-    issue(min(t + 3, nt - 1), nxt);
+    issue(min(t + NST - 1, nt - 1), nxt);
     const int k0 = t * 64;
     if (k0 > qw + 31) return;                       // every key after every query of this wave
-    if (k0 + 63 <= qw) fwd_tile<false>(cur, rf, tf, qf, acc, rsum, sl2, sh2, 0, g);
-    else fwd_tile<true>(cur, rf, tf, qf, acc, rsum, sl2, sh2, k0 + 4 * g - q, g);
+    if (k0 + 63 <= qw) fwd_tile<false>(cur, rf, tf, qf, acc, rsum, sl2, sh2, 0);
+    else fwd_tile<true>(cur, rf, tf, qf, acc, rsum, sl2, sh2, k0 + 4 * g - q);
   };
-  issue(0, st0);
-  issue(min(1, nt - 1), st1);
-  issue(min(2, nt - 1), st2);
-  for (int t = 0; t < nt; t += 4) {
-    step(t, st0, st3);
-    if (t + 1 < nt) step(t + 1, st1, st0);
-    if (t + 2 < nt) step(t + 2, st2, st1);
-    if (t + 3 < nt) step(t + 3, st3, st2);
+  if constexpr (NST == 4) {
+    issue(0, st0);
+    issue(min(1, nt - 1), st1);
+    issue(min(2, nt - 1), st2);
+    for (int t = 0; t < nt; t += 4) {
+      step(t, st0, st3);
+      if (t + 1 < nt) step(t + 1, st1, st0);
+      if (t + 2 < nt) step(t + 2, st2, st1);
+      if (t + 3 < nt) step(t + 3, st3, st2);
+    }
+  } else {
+    issue(0, st0);
+    for (int t = 0; t < nt; t += 2) {
+      step(t, st0, st1);
+      if (t + 1 < nt) step(t + 1, st1, st0);
+    }
   }
   wait_vmcnt<0>();
   rsum += __shfl_xor(rsum, 32, 64);
@@ -729,7 +763,7 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_bf16_kernel(const bf16* __res
                       acc[db][blk * 4 + 3] * inv};
         store4(op + db * 32 + blk * 8 + g * 4, v);
       }
-    if (g == 0) lse[((int64_t)b * H + h) * T_ + q] = shift + logf(rsum);
+    if (g == 0) lse[((int64_t)b * H + h) * T_ + q] = sh2 + log2f(rsum);
   }
 }
 
@@ -739,16 +773,37 @@ template <bool MASK>
 DEV void dq_tile(const KvStage& s, const RowFrag& rf, const TrFrag& tf, const u32x4 (&qf)[8], const u32x4 (&df)[8],
                  f32x16 (&acc)[4], float sl2, float l2, float dlt, int krel) {
   f32x16 sc[2], dp[2];
+  // S and dP for key rows 0-31, then 32-63; fragments read ahead and
+  // re-filled as their MFMAs issue
+  u32x4 fa[8], fb[8];
 #pragma unroll
-  for (int kb2 = 0; kb2 < 2; ++kb2) {
-    sc[kb2] = zero16();
-    dp[kb2] = zero16();
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      sc[kb2] = mfma16(ld16(s.k + rf.off(kb2, ks)), qf[ks], sc[kb2], (bf16*)nullptr);
-      dp[kb2] = mfma16(ld16(s.v + rf.off(kb2, ks)), df[ks], dp[kb2], (bf16*)nullptr);
-    }
+  for (int ks = 0; ks < 8; ++ks) {
+    fa[ks] = ld16(s.k + rf.off(0, ks));
+    fb[ks] = ld16(s.v + rf.off(0, ks));
   }
+  sc[0] = zero16();
+  dp[0] = zero16();
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    sc[0] = mfma16(fa[ks], qf[ks], sc[0], (bf16*)nullptr);
+    dp[0] = mfma16(fb[ks], df[ks], dp[0], (bf16*)nullptr);
+    fa[ks] = ld16(s.k + rf.off(1, ks));
+    fb[ks] = ld16(s.v + rf.off(1, ks));
+  }
+  sc[1] = zero16();
+  dp[1] = zero16();
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    sc[1] = mfma16(fa[ks], qf[ks], sc[1], (bf16*)nullptr);
+    dp[1] = mfma16(fb[ks], df[ks], dp[1], (bf16*)nullptr);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
 #pragma unroll
   for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
@@ -760,17 +815,23 @@ DEV void dq_tile(const KvStage& s, const RowFrag& rf, const TrFrag& tf, const u3
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
     const u32x4 sf = pack_frag<bf16>(dp[kk >> 1], kk & 1);
+    u32x4 tk[4];
 #pragma unroll
-    for (int db = 0; db < 4; ++db) acc[db] = mfma16(tf.read(s.k, kk, db), sf, acc[db], (bf16*)nullptr);
+    for (int db = 0; db < 4; ++db) tk[db] = tf.read(s.k, kk, db);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) acc[db] = mfma16(tk[db], sf, acc[db], (bf16*)nullptr);
   }
 }
 
-__global__ __launch_bounds__(256, 1) void attn_dq_bf16_kernel(const bf16* __restrict__ qkv,
-                                                              const bf16* __restrict__ dout,
-                                                              const float* __restrict__ lse,
-                                                              const float* __restrict__ delta, int T_, int H,
-                                                              bf16* __restrict__ dqkv) {
-  __shared__ __attribute__((aligned(1024))) KvStage st0, st1, st2, st3;
+template <int NST>
+__global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void attn_dq_bf16_kernel(const bf16* __restrict__ qkv,
+                                                                             const bf16* __restrict__ dout,
+                                                                             const float* __restrict__ lse,
+                                                                             const float* __restrict__ delta, int T_,
+                                                                             int H, bf16* __restrict__ dqkv) {
+  static_assert(NST == 2 || NST == 4, "two or four stages");
+  __shared__ __attribute__((aligned(1024))) KvStage st0, st1;
+  __shared__ __attribute__((aligned(1024))) std::conditional_t<NST == 4, KvStage, char[16]> st2, st3;
   const int nqb = (T_ + 127) / 128;
   int b, r;
   xcd_row_map(blockIdx.x, gridDim.x / (nqb * H), nqb * H, b, r);
@@ -788,7 +849,7 @@ __global__ __launch_bounds__(256, 1) void attn_dq_bf16_kernel(const bf16* __rest
   load_row_frags(qf, base + (int64_t)qw * ld + h * D, T_ - qw, ld_b, l32, g);
   load_row_frags(df, dout + ((int64_t)b * T_ + qw) * H * D + h * D, T_ - qw, (uint32_t)H * D * 2u, l32, g);
   const int64_t si = ((int64_t)b * H + h) * T_ + q;
-  const float l2 = qv ? lse[si] * kLog2e : 0.f;
+  const float l2 = qv ? lse[si] : 0.f;
   const float dlt = qv ? delta[si] : 0.f;
   const float scale = rsqrtf((float)D);
   const float sl2 = kLog2e * scale;
@@ -808,22 +869,30 @@ __global__ __launch_bounds__(256, 1) void attn_dq_bf16_kernel(const bf16* __rest
     tile_issue(uniform_rsrc(kp + D, rows * (int)ld_b), s.v, vo, wave);
   };
   auto step = [&](int t, const KvStage& cur, KvStage& nxt) {
-    wait_vmcnt<2 * 8>();  // this wave's part of tile t has landed
+    wait_vmcnt<(NST - 2) * 8>();  // this wave's part of tile t has landed
     __builtin_amdgcn_s_barrier();
-    issue(min(t + 3, nt - 1), nxt);
+    issue(min(t + NST - 1, nt - 1), nxt);
     const int k0 = t * 64;
     if (k0 > qw + 31) return;
     if (k0 + 63 <= qw) dq_tile<false>(cur, rf, tf, qf, df, acc, sl2, l2, dlt, 0);
     else dq_tile<true>(cur, rf, tf, qf, df, acc, sl2, l2, dlt, k0 + 4 * g - q);
   };
-  issue(0, st0);
-  issue(min(1, nt - 1), st1);
-  issue(min(2, nt - 1), st2);
-  for (int t = 0; t < nt; t += 4) {
-    step(t, st0, st3);
-    if (t + 1 < nt) step(t + 1, st1, st0);
-    if (t + 2 < nt) step(t + 2, st2, st1);
-    if (t + 3 < nt) step(t + 3, st3, st2);
+  if constexpr (NST == 4) {
+    issue(0, st0);
+    issue(min(1, nt - 1), st1);
+    issue(min(2, nt - 1), st2);
+    for (int t = 0; t < nt; t += 4) {
+      step(t, st0, st3);
+      if (t + 1 < nt) step(t + 1, st1, st0);
+      if (t + 2 < nt) step(t + 2, st2, st1);
+      if (t + 3 < nt) step(t + 3, st3, st2);
+    }
+  } else {
+    issue(0, st0);
+    for (int t = 0; t < nt; t += 2) {
+      step(t, st0, st1);
+      if (t + 1 < nt) step(t + 1, st1, st0);
+    }
   }
   wait_vmcnt<0>();
   if (qv) {
@@ -847,7 +916,7 @@ __global__ __launch_bounds__(256, 1) void attn_dq_bf16_kernel(const bf16* __rest
 struct DkvStage {
   char q[kTileB];
   char d[kTileB];
-  float l[4][64];  // lse of the tile's queries (one copy per wave)
+  float l[4][64];  // lse2 of the tile's queries (one copy per wave)
   float e[4][64];  // delta
 };
 
@@ -855,16 +924,39 @@ template <bool MASK>
 DEV void dkv_tile(const DkvStage& s, int wave, const RowFrag& rf, const TrFrag& tf, const u32x4 (&kf)[8],
                   const u32x4 (&vf)[8], f32x16 (&adk)[4], f32x16 (&adv)[4], float sl2, int qrel, int g) {
   f32x16 sc[2], dp[2];
+  // S^T and dP^T for query rows 0-31, then 32-63: four accumulation chains.
+  // Fragments for rows 0-31 are read up front; each is re-filled with its
+  // rows-32-63 counterpart as soon as its MFMA has been issued.
+  u32x4 fa[8], fb[8];
 #pragma unroll
-  for (int qb2 = 0; qb2 < 2; ++qb2) {
-    sc[qb2] = zero16();
-    dp[qb2] = zero16();
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      sc[qb2] = mfma16(ld16(s.q + rf.off(qb2, ks)), kf[ks], sc[qb2], (bf16*)nullptr);
-      dp[qb2] = mfma16(ld16(s.d + rf.off(qb2, ks)), vf[ks], dp[qb2], (bf16*)nullptr);
-    }
+  for (int ks = 0; ks < 8; ++ks) {
+    fa[ks] = ld16(s.q + rf.off(0, ks));
+    fb[ks] = ld16(s.d + rf.off(0, ks));
   }
+  sc[0] = zero16();
+  dp[0] = zero16();
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    sc[0] = mfma16(fa[ks], kf[ks], sc[0], (bf16*)nullptr);
+    dp[0] = mfma16(fb[ks], vf[ks], dp[0], (bf16*)nullptr);
+    fa[ks] = ld16(s.q + rf.off(1, ks));
+    fb[ks] = ld16(s.d + rf.off(1, ks));
+  }
+  sc[1] = zero16();
+  dp[1] = zero16();
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    sc[1] = mfma16(fa[ks], kf[ks], sc[1], (bf16*)nullptr);
+    dp[1] = mfma16(fb[ks], vf[ks], dp[1], (bf16*)nullptr);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);  // 16 fragment reads
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // next fragment read
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+  // P = exp2(S log2(e)/sqrt(D) - lse2), dS = P (dP - delta), in place
 #pragma unroll
   for (int qb2 = 0; qb2 < 2; ++qb2)
 #pragma unroll
@@ -875,21 +967,28 @@ DEV void dkv_tile(const DkvStage& s, int wave, const RowFrag& rf, const TrFrag& 
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = blk * 4 + r;
-        float p = fast_exp2(sc[qb2][i] * sl2 - L[r] * kLog2e);
+        float p = fast_exp2(sc[qb2][i] * sl2 - L[r]);
         // query (tile row qb2*32 + blk*8 + 4g + r) >= key
         if (MASK) p = (qb2 * 32 + blk * 8 + r + qrel >= 0) ? p : 0.f;
         sc[qb2][i] = p;
         dp[qb2][i] = p * (dp[qb2][i] - E[r]);
       }
     }
+  // dV += P^T dO, dK += dS^T Q over the tile's 64 queries (4 k-steps of 16)
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
     const u32x4 pf = pack_frag<bf16>(sc[kk >> 1], kk & 1);
     const u32x4 sf = pack_frag<bf16>(dp[kk >> 1], kk & 1);
+    u32x4 ta[4], tb[4];
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
-      adv[db] = mfma16(tf.read(s.d, kk, db), pf, adv[db], (bf16*)nullptr);
-      adk[db] = mfma16(tf.read(s.q, kk, db), sf, adk[db], (bf16*)nullptr);
+      ta[db] = tf.read(s.d, kk, db);
+      tb[db] = tf.read(s.q, kk, db);
+    }
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      adv[db] = mfma16(ta[db], pf, adv[db], (bf16*)nullptr);
+      adk[db] = mfma16(tb[db], sf, adk[db], (bf16*)nullptr);
     }
   }
 }
@@ -986,7 +1085,7 @@ hipError_t fwd_typed(const void* qkv, int B, int T_, int H, void* o, float* lse,
   dim3 grid(((T_ + 127) / 128) * H * B);
   if constexpr (sizeof(T) == 2) {
     if (stage == 0) return hipSuccess;  // no transposed copy on this path
-    hipLaunchKernelGGL(attn_fwd_bf16_kernel, grid, dim3(256), 0, s, (const bf16*)qkv, T_, H, (bf16*)o, lse);
+    hipLaunchKernelGGL(attn_fwd_bf16_kernel<kFwdStages>, grid, dim3(256), 0, s, (const bf16*)qkv, T_, H, (bf16*)o, lse);
     return hipGetLastError();
   }
   if (stage == 0) return transpose<T>(qkv, (int64_t)(H + 2) * D, (H + 1) * D, 1, B, T_, Tp, vT, s);
@@ -1013,7 +1112,7 @@ hipError_t bwd_typed(const AttnBwdArgs& a, int stage, hipStream_t s) {
   } else if (stage == 1) {
     const dim3 grid(((T_ + 127) / 128) * H * B);
     if constexpr (kBf16)
-      hipLaunchKernelGGL(attn_dq_bf16_kernel, grid, dim3(256), 0, s, (const bf16*)a.qkv, (const bf16*)a.dout, a.lse,
+      hipLaunchKernelGGL(attn_dq_bf16_kernel<kDqStages>, grid, dim3(256), 0, s, (const bf16*)a.qkv, (const bf16*)a.dout, a.lse,
                          a.delta, T_, H, (bf16*)a.dqkv);
     else
       hipLaunchKernelGGL(attn_dq_kernel<T>, grid, dim3(256), 0, s, (const T*)a.qkv, (const T*)a.kT,

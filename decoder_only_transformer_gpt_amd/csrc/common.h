@@ -51,9 +51,12 @@ DEV void load8(const float* p, float (&v)[8]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) { v[i] = __uint_as_float(a[i]); v[4 + i] = __uint_as_float(b[i]); }
 }
+// Two floats to a bf16 pair (RNE), lo in the low half: one v_cvt_pk_bf16_f32.
 DEV uint32_t pack_bf16x2(float lo, float hi) {
-  bf16 a = (bf16)lo, b = (bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 DEV void store8(bf16* p, const float (&v)[8]) {
   u32x4 r;

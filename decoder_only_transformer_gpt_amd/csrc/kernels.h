@@ -69,7 +69,7 @@ struct AttnBwdArgs {
   const void* qkv;   // [N, (H+2)*128] normalised q, k and v
   const void* o;     // [N, H*128]
   const void* dout;  // [N, H*128]
-  const float* lse;  // [B, H, T]
+  const float* lse;  // [B, H, T], base 2: lse * log2(e)
   int B, T, H;
   float* delta;      // [B, H, T] scratch
   void* qT;          // [B, H, 128, Tp] scratch

@@ -176,7 +176,9 @@ const char* gpt_kernel_tag_name(int32_t tag);
 /* Debug access to a stashed activation of the last forward: device pointer and
  * byte size of the named buffer ("x", "h1", "qkv", "o", "lse", "h2", "a",
  * "hf", "logits", "rstd0") for `layer` (ignored by non-layer buffers). The
- * pointer aliases the workspace and is valid until the next call. */
+ * pointer aliases the workspace and is valid until the next call. "lse" holds
+ * the attention log-sum-exp per (batch row, head, position) in base 2, i.e.
+ * ln(sum) * log2(e), fp32 [B, H, T]. */
 gpt_status gpt_debug_buffer(gpt_model* m, const char* name, int32_t layer, void** ptr, size_t* bytes);
 
 #ifdef __cplusplus
