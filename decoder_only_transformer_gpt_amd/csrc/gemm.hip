@@ -586,6 +586,165 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_nt_lds_kernel(GemmArgs arg
   Epilogue<T, E>::template run<TM, TN, WN>(args, acc, slab, m0 + wm * WM, n0 + wn * WN, lane);
 }
 
+// bf16 GEMM with both operands mn-contiguous (dW = dy^T x: A = dy [K, M] and
+// B = x [K, N], k = token), fed by direct-to-LDS buffer loads and read with
+// the transposing LDS read (ds_read_b64_tr_b16), so no register transposes.
+//
+// A K tile of 32 rows lands as [32][BM] and [32][BN] bf16. A wave's 1 KiB
+// load covers 1024/(2*BM) k rows; chunk c of k row r sits at position
+// c ^ s(r) with s(r) = ((r & 7) << 2) mod (chunks per row), which shifts each
+// row's 64-byte windows so that the four k rows one half-wave's transposing
+// read touches fall on distinct banks. The MFMA k order is the one the
+// transposing read delivers (rows 4g+e, then 8+4g+e, of each 16-row step),
+// the same for both operands. Pipeline and epilogue as in the NT kernel;
+// blockIdx.z selects a split-K slice (whole K tiles).
+template <int BM, int BN, int NSTAGE, int OCC, Epi E>
+__global__ __launch_bounds__(kThreads, OCC) void gemm_tn_lds_kernel(GemmArgs args) {
+  using T = bf16;
+  constexpr int BK = 32;
+  constexpr int ROWA = BM * 2, ROWB = BN * 2;   // bytes per k row
+  constexpr int CHA = ROWA / 16, CHB = ROWB / 16;
+  constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
+  constexpr int STAGE = BK * (ROWA + ROWB);
+  constexpr int LA = BK * ROWA / 1024 / 4, LB = BK * ROWB / 1024 / 4;  // 1 KiB loads per wave per tile
+  constexpr int NLOAD = LA + LB;
+  static_assert(LA >= 1 && LB >= 1 && CHA >= 16 && CHB >= 16, "tile shape");
+  __shared__ __attribute__((aligned(1024))) char st0[STAGE];
+  __shared__ __attribute__((aligned(1024))) char st1[STAGE];
+  __shared__ __attribute__((aligned(1024))) char st2[STAGE];
+  __shared__ __attribute__((aligned(1024))) char st3[NSTAGE == 4 ? STAGE : 1024];
+  static_assert(NSTAGE == 3 || NSTAGE == 4, "three or four stage arrays");
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1, g = lane >> 5;
+  const int M = args.M, N = args.N, K = args.K;
+  const int tiles_n = (N + BN - 1) / BN;
+  int bid = blockIdx.x;
+  const int nb = gridDim.x;
+  if ((nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
+  const int m0 = (bid / tiles_n) * BM, n0 = (bid % tiles_n) * BN;
+  const int kper = ((K + args.splits - 1) / args.splits + BK - 1) / BK * BK;
+  const int kbeg = blockIdx.z * kper;
+  const int kend = min(K, kbeg + kper);
+  const int nk = kend > kbeg ? (kend - kbeg) / BK : 0;
+  const T* Ap = reinterpret_cast<const T*>(args.A) + m0;
+  const T* Bp = reinterpret_cast<const T*>(args.B) + n0;
+  const uint32_t lda_b = (uint32_t)(args.lda * 2), ldb_b = (uint32_t)(args.ldb * 2);
+  // record counts from a tile's first element: 31 full rows, then the last
+  // row up to column M (resp. N); integer ternaries keep them scalar
+  const int64_t ra64 = (int64_t)(BK - 1) * lda_b + (int64_t)(M - m0 < BM ? M - m0 : BM) * 2;
+  const int64_t rb64 = (int64_t)(BK - 1) * ldb_b + (int64_t)(N - n0 < BN ? N - n0 : BN) * 2;
+  const int rec_a = ra64 > (1 << 30) ? (1 << 30) : (int)ra64;
+  const int rec_b = rb64 > (1 << 30) ? (1 << 30) : (int)rb64;
+
+  // per-lane global offsets of this wave's 1 KiB slots
+  uint32_t voa[LA], vob[LB];
+#pragma unroll
+  for (int i = 0; i < LA; ++i) {
+    const int r = (wave * LA + i) * (1024 / ROWA) + lane / CHA, p = lane % CHA;
+    const int c = p ^ (((r & 7) << 2) & (CHA - 1));
+    voa[i] = (uint32_t)r * lda_b + (uint32_t)c * 16u;
+  }
+#pragma unroll
+  for (int i = 0; i < LB; ++i) {
+    const int r = (wave * LB + i) * (1024 / ROWB) + lane / CHB, p = lane % CHB;
+    const int c = p ^ (((r & 7) << 2) & (CHB - 1));
+    vob[i] = (uint32_t)r * ldb_b + (uint32_t)c * 16u;
+  }
+  auto stage = [&](int q) -> char* { return q == 0 ? st0 : q == 1 ? st1 : q == 2 ? st2 : st3; };
+  auto issue = [&](int kt, char* st) {
+    const int64_t k0 = kbeg + (int64_t)kt * BK;
+    const __amdgpu_buffer_rsrc_t ra = uniform_rsrc(Ap + k0 * args.lda, rec_a);
+    const __amdgpu_buffer_rsrc_t rb = uniform_rsrc(Bp + k0 * args.ldb, rec_b);
+#pragma unroll
+    for (int i = 0; i < LA; ++i) lds_direct16(ra, st + (wave * LA + i) * 1024, voa[i]);
+#pragma unroll
+    for (int i = 0; i < LB; ++i) lds_direct16(rb, st + BK * ROWA + (wave * LB + i) * 1024, vob[i]);
+  };
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  // transposing-read offsets: source lane 4e + c of each 16-lane group names k
+  // row 4g + e (+8 for the second half) and columns [4c, 4c + 4) of its
+  // group's 16 (group parity picks columns 0-15 or 16-31 of a 32-column block)
+  const int e4 = (lane >> 2) & 3, c4 = lane & 3, grp = lane >> 4;
+  const int x = 4 * g + e4;                    // k row within a 16-row step (first half)
+  const int c0 = 2 * (grp & 1) + (c4 >> 1);    // chunk within a 32-column block
+  const int sa = (x << 2) & (CHA - 1), sb = (x << 2) & (CHB - 1);
+  int ofa[TM], ofb[TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) ofa[i] = x * ROWA + ((((wm * WM + i * 32) >> 3) ^ sa) + c0) * 16 + (c4 & 1) * 8;
+#pragma unroll
+  for (int j = 0; j < TN; ++j) ofb[j] = x * ROWB + ((((wn * WN + j * 32) >> 3) ^ sb) + c0) * 16 + (c4 & 1) * 8;
+  auto frag = [](const char* base, int off, int row_b) -> u32x4 {
+    const u32x2 lo = ld_tr16(base + off), hi = ld_tr16(base + off + 8 * row_b);
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+  };
+
+  issue(0, st0);
+  issue(min(1, nk - 1), st1);
+  if (NSTAGE == 4) issue(min(2, nk - 1), st2);
+  auto tile = [&](int kt, const char* cur, char* nxt) {
+    constexpr int YOUNG = NLOAD * (NSTAGE - 2);
+    __builtin_amdgcn_s_waitcnt(((YOUNG >> 4) << 14) | (0x7 << 4) | (0xF << 8) | (YOUNG & 15));
+    __builtin_amdgcn_s_barrier();
+    issue(min(kt + NSTAGE - 1, nk - 1), nxt);
+    const char* As = cur;
+    const char* Bs = cur + BK * ROWA;
+    u32x4 af[2][TM], bfr[2][TN];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) af[kk][i] = frag(As + kk * 16 * ROWA, ofa[i], ROWA);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) bfr[kk][j] = frag(Bs + kk * 16 * ROWB, ofb[j], ROWB);
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = mfma16(bfr[kk][j], af[kk][i], acc[i][j], (T*)nullptr);
+    constexpr int NR = 2 * (TM + TN), NM = TM * TN, PER = NM / NR > 0 ? NM / NR : 1;
+    __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+#pragma unroll
+    for (int q = 0; q < NR; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * NM - NR * PER, 0);
+  };
+  if constexpr (NSTAGE == 4) {
+    for (int kt = 0; kt < nk; kt += 4) {
+      tile(kt, st0, st3);
+      if (kt + 1 < nk) tile(kt + 1, st1, st0);
+      if (kt + 2 < nk) tile(kt + 2, st2, st1);
+      if (kt + 3 < nk) tile(kt + 3, st3, st2);
+    }
+  } else {
+    for (int kt = 0; kt < nk; kt += 3) {
+      tile(kt, st0, st2);
+      if (kt + 1 < nk) tile(kt + 1, st1, st0);
+      if (kt + 2 < nk) tile(kt + 2, st2, st1);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  constexpr int SLAB = 32 * (WN + 4) * (int)sizeof(float);
+  constexpr bool TWO = 2 * SLAB <= STAGE;
+  static_assert(TWO || (NSTAGE == 4 && SLAB <= STAGE), "epilogue slabs must fit the stages");
+  float* slab = TWO ? reinterpret_cast<float*>(stage(wave >> 1) + (wave & 1) * SLAB)
+                    : reinterpret_cast<float*>(stage(wave));
+  Epilogue<T, E>::template run<TM, TN, WN>(args, acc, slab, m0 + wm * WM, n0 + wn * WN, lane);
+}
+
 // Sums split-K partials in slice order into the fp32 gradient.
 __global__ __launch_bounds__(256) void splitk_reduce(const float* __restrict__ P, int splits, int M, int N,
                                                      float* __restrict__ G, int64_t ldg, int accumulate) {
@@ -653,6 +812,19 @@ hipError_t launch_nt_lds(const GemmArgs& a, hipStream_t s) {
 }
 
 
+template <int BM, int BN, int NSTAGE, int OCC, Epi E>
+hipError_t launch_tn_lds(const GemmArgs& a, hipStream_t s) {
+  const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  hipLaunchKernelGGL((gemm_tn_lds_kernel<BM, BN, NSTAGE, OCC, E>), dim3(tiles, 1, a.splits), dim3(kThreads), 0, s, a);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || a.splits <= 1) return err;
+  const int64_t total4 = (int64_t)a.M * a.N / 4;
+  const int blocks = (int)std::min<int64_t>((total4 + 255) / 256, 4096);
+  hipLaunchKernelGGL(splitk_reduce, dim3(blocks), dim3(256), 0, s, a.split_buf, a.splits, a.M, a.N,
+                     reinterpret_cast<float*>(a.C), a.ldc, a.accumulate);
+  return hipGetLastError();
+}
+
 template <Epi E>
 hipError_t launch_nt_lds_tile(const GemmArgs& a, hipStream_t s) {
   const int64_t t256 = (int64_t)((a.M + 255) / 256) * ((a.N + 255) / 256);
@@ -681,6 +853,17 @@ hipError_t launch_typed(Epi epi, const GemmArgs& a, hipStream_t s) {
         case Epi::Relu2Bwd: return launch_nt_lds_tile<Epi::Relu2Bwd>(a, s);
         default: break;
       }
+    }
+  }
+  if constexpr (sizeof(T) == 2) {
+    if (!a.a_kcontig && !a.b_kcontig && epi == Epi::GradF32 && a.K % 32 == 0 && a.M % 128 == 0 &&
+        a.N % 128 == 0) {
+      // tile: 1 = 256x256, 2 = 128x128 (0 = 256x256 when that fills the chip)
+      const int64_t t256 = (int64_t)((a.M + 255) / 256) * ((a.N + 255) / 256) * a.splits;
+      int tile = a.tile;
+      if (tile == 0) tile = (t256 >= 256 && a.M % 256 == 0 && a.N % 256 == 0) ? 1 : 2;
+      if (tile == 1 && a.M % 256 == 0 && a.N % 256 == 0) return launch_tn_lds<256, 256, 4, 1, Epi::GradF32>(a, s);
+      return launch_tn_lds<128, 128, 4, 1, Epi::GradF32>(a, s);
     }
   }
   const bool nt = a.a_kcontig && a.b_kcontig, nn = a.a_kcontig && !a.b_kcontig,
