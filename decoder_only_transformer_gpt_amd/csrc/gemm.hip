@@ -313,6 +313,47 @@ DEV void staged_store(f32x16 (&acc)[TM][TN], float* st, int mbase, int nbase, in
   }
 }
 
+// staged_store with a prefetch: pre(m, n) is issued for every (row, 4
+// columns) item of a slab before the slab's accumulators go to LDS, so those
+// global loads are in flight during the staging; op(m, n, v, pre_value).
+template <int TM, int TN, int WN, class Pre, class Op>
+DEV void staged_store_pre(f32x16 (&acc)[TM][TN], float* st, int mbase, int nbase, int lane, Pre pre, Op op) {
+  constexpr int P = WN + 4, LPR = WN / 4, RPP = 64 / LPR, NP = 32 / RPP;
+  using PV = decltype(pre(0, 0));
+  const int g = lane >> 5, l32 = lane & 31;
+  const int prow = lane / LPR, pcol = (lane % LPR) * 4;
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    PV pv[NP];
+#pragma unroll
+    for (int q = 0; q < NP; ++q) pv[q] = pre(mbase + i * 32 + q * RPP + prow, nbase + pcol);
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk) {
+        float v[4] = {acc[i][j][blk * 4], acc[i][j][blk * 4 + 1], acc[i][j][blk * 4 + 2], acc[i][j][blk * 4 + 3]};
+        store4(st + l32 * P + j * 32 + blk * 8 + g * 4, v);
+      }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < NP; ++q) {
+      const int row = q * RPP + prow;
+      float v[4];
+      load4(st + row * P + pcol, v);
+      op(mbase + i * 32 + row, nbase + pcol, v, pv[q]);
+    }
+    __syncthreads();
+  }
+}
+
+// tanh(y) = 1 - 2 / (exp(2y) + 1) on v_exp_f32 and v_rcp_f32; saturates to
+// +-1 through exp's overflow to inf and underflow to 0. Absolute error a few
+// 1e-7 (cancellation near 0 bounds it in absolute, not relative, terms).
+DEV float tanh_fast(float y) {
+  const float e = __builtin_amdgcn_exp2f(y * 2.8853900817779268f);  // 2 log2(e)
+  return 1.f - 2.f * __builtin_amdgcn_rcpf(e + 1.f);
+}
+
 template <typename T>
 struct Epilogue<T, Epi::Store> {
   template <int TM, int TN, int WN>
@@ -359,16 +400,20 @@ struct Epilogue<T, Epi::Relu2> {
 };
 
 // du = da * 2 max(u, 0) = da * 2 sqrt(a), with a = max(u, 0)^2 read from C2
+// (prefetched per slab)
 template <typename T>
 struct Epilogue<T, Epi::Relu2Bwd> {
   template <int TM, int TN, int WN>
   static DEV void run(const GemmArgs& a, f32x16 (&acc)[TM][TN], float* lds, int mbase, int nbase, int lane) {
     T* Dp = reinterpret_cast<T*>(a.C);
     const T* A2 = reinterpret_cast<const T*>(a.C2);
-    staged_store<TM, TN, WN>(acc, lds, mbase, nbase, lane, [&](int m, int n, float (&v)[4]) {
+    auto pre = [&](int m, int n) {
+      float x[4] = {0.f, 0.f, 0.f, 0.f};
+      if (m < a.M && n < a.N) load4(A2 + (int64_t)m * a.ldc2 + n, x);
+      return f32x4{x[0], x[1], x[2], x[3]};
+    };
+    staged_store_pre<TM, TN, WN>(acc, lds, mbase, nbase, lane, pre, [&](int m, int n, float (&v)[4], f32x4 x) {
       if (m < a.M && n < a.N) {
-        float x[4];
-        load4(A2 + (int64_t)m * a.ldc2 + n, x);
         for (int r = 0; r < 4; ++r) v[r] *= 2.f * sqrtf(x[r]);
         store4(Dp + (int64_t)m * a.ldc + n, v);
       }
@@ -379,33 +424,34 @@ struct Epilogue<T, Epi::Relu2Bwd> {
 // LM head with the logit softcap c*tanh(z/c), evaluated on the fp32
 // accumulator (aethryn.com, section "A Llama-class transformer with ten modern
 // departures": softcap 15, in float32). Emits the capped logits in the
-// activation dtype, one fp32 partial sum of exp(z' - c) per row and 128
+// activation dtype, one fp32 partial sum of exp(z' - c) per row and 64
 // columns (terms lie in (e^-2c, 1], so partial sums add without rescaling),
-// and the fp32 capped logit at the row's target. Done on the staged rows: a
-// row's 128 wave columns sit in 32 lanes (4 each), reduced with shuffles.
+// and the fp32 capped logit at the row's target. Done on the staged rows: 64
+// columns of a row sit in 16 lanes (4 each), reduced with shuffles. The
+// row's target id is prefetched with the slab.
 template <typename T>
 struct Epilogue<T, Epi::LMHead> {
   template <int TM, int TN, int WN>
   static DEV void run(const GemmArgs& a, f32x16 (&acc)[TM][TN], float* lds, int mbase, int nbase, int lane) {
-    static_assert(WN == kLMHeadPartCols, "one partial per wave column block");
+    static_assert(WN % kLMHeadPartCols == 0 && kLMHeadPartCols == 64, "16 lanes per partial");
     const float c = a.softcap, inv_c = 1.f / a.softcap;
     const int nparts = a.N / kLMHeadPartCols;
     T* Z = reinterpret_cast<T*>(a.C);
-    staged_store<TM, TN, WN>(acc, lds, mbase, nbase, lane, [&](int m, int n, float (&v)[4]) {
+    auto pre = [&](int m, int) { return m < a.M ? a.targets[m] : -1; };
+    staged_store_pre<TM, TN, WN>(acc, lds, mbase, nbase, lane, pre, [&](int m, int n, float (&v)[4], int tgt) {
       const bool mv = m < a.M;
-      const int tgt = mv ? a.targets[m] : -1;
       float sum = 0.f;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        v[r] = c * tanhf(v[r] * inv_c);
-        sum += __expf(v[r] - c);
+        v[r] = c * tanh_fast(v[r] * inv_c);
+        sum += __builtin_amdgcn_exp2f((v[r] - c) * 1.4426950408889634f);
       }
       const unsigned d = (unsigned)(tgt - n);
-      if (d < 4u) a.ztgt[m] = v[d];
+      if (d < 4u) a.ztgt[m] = d == 0 ? v[0] : d == 1 ? v[1] : d == 2 ? v[2] : v[3];
       if (mv) store4(Z + (int64_t)m * a.ldc + n, v);
 #pragma unroll
-      for (int o = 16; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 32);
-      if (mv && (lane & 31) == 0) a.part[(int64_t)m * nparts + nbase / kLMHeadPartCols] = sum;
+      for (int o = 8; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 16);
+      if (mv && (lane & 15) == 0) a.part[(int64_t)m * nparts + n / kLMHeadPartCols] = sum;
     });
   }
 };
@@ -828,11 +874,17 @@ hipError_t launch_tn_lds(const GemmArgs& a, hipStream_t s) {
 template <Epi E>
 hipError_t launch_nt_lds_tile(const GemmArgs& a, hipStream_t s) {
   const int64_t t256 = (int64_t)((a.M + 255) / 256) * ((a.N + 255) / 256);
-  // tile: 1 = 256x256 (one CTA per CU), 2 = 256x128 (two per CU), 3 = 128x128
+  // tile: 1 = 256x256 (one CTA per CU), 2 = 256x128 (two per CU), 3 = 128x128.
+  // By shape: 256x256 when there are at least two tiles per CU, except that
+  // heavy epilogues over a short K loop (the relu^2 backward and residual
+  // reads, the LM head's softcap and exp sums) prefer two CTAs per CU, so one
+  // CTA's epilogue runs under the other's MFMA work.
+  const bool heavy_epi = E == Epi::Relu2Bwd || E == Epi::LMHead || (E == Epi::Residual && a.K <= 2048);
   int tile = a.tile;
-  if (tile == 0) tile = (t256 >= 512 && a.N % 256 == 0) ? 1 : 3;
-  if constexpr (E == Epi::LMHead) {  // one exp-sum partial per 128 columns: BN = 256
-    if (tile == 1 || tile == 2) return launch_nt_lds<256, 256, 4, 1, E>(a, s);
+  if (tile == 0) tile = (t256 >= 512 && a.N % 256 == 0) ? (heavy_epi ? 2 : 1) : 3;
+  if constexpr (E == Epi::LMHead) {  // exp-sum partials per 64 columns: BN a multiple of 128
+    if (tile == 1) return launch_nt_lds<256, 256, 4, 1, E>(a, s);
+    if (tile == 2) return launch_nt_lds<256, 128, 3, 2, E>(a, s);
     return launch_nt_lds<128, 256, 4, 1, E>(a, s);
   } else {
     if (tile == 1) return launch_nt_lds<256, 256, 4, 1, E>(a, s);

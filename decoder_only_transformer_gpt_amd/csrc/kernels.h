@@ -43,7 +43,7 @@ struct GemmArgs {
 // dtype: 0 = fp32, 1 = bf16 (gpt.h GPT_F32 / GPT_BF16)
 hipError_t launch_gemm(int dtype, Epi epi, const GemmArgs& a, hipStream_t s);
 // Partial-column width of the LMHead epilogue (exp-sum partials per row).
-constexpr int kLMHeadPartCols = 128;
+constexpr int kLMHeadPartCols = 64;
 
 // Row-wise kernels ---------------------------------------------------------
 hipError_t launch_embed_rmsnorm(int dtype, const void* wte, const int32_t* idx, int N, int C, int V,
