@@ -547,11 +547,15 @@ __global__ __launch_bounds__(256) void attn_dkv_kernel(const T* __restrict__ qkv
 // buffer loads: no staging registers, and rows past the sequence end read as
 // zero (buffer range check). A wave's load writes 1 KiB = 4 rows; each lane
 // picks the global 16-byte chunk it fetches so that chunk c of tile row r sits
-// at position c ^ (r & 15). Operands whose k index runs along a row (q.k over
-// D) are read as row fragments; operands whose k index runs down the rows
-// (V^T for P.V, K^T for dS.K, Q^T and dO^T for dK and dV) are read with the
-// transposing LDS read, so no transposed copies exist in global memory. Both
-// read patterns touch 16 distinct chunk positions per 16 lanes.
+// at position c ^ f(r & 15), f(x) = ((x & 3) << 2) | (x >> 2). Operands whose
+// k index runs along a row (q.k over D) are read as row fragments; operands
+// whose k index runs down the rows (V^T for P.V, K^T for dS.K, Q^T and dO^T for
+// dK and dV) are read with the transposing LDS read, so no transposed copies
+// exist in global memory. f is a bijection on 0..15, so a row-fragment read
+// (16 consecutive rows, one chunk) covers 16 distinct chunk positions; and
+// rows 4a+e, e = 0..3, get distinct bits 2-3 of f, so the four rows of a
+// transposing half-wave read (each a 64-byte window of 4 chunks) sit in four
+// distinct 64-byte bank ranges.
 //
 // Tiles cycle through four LDS stages: tile i+3 is requested while tile i is
 // consumed. Each wave waits only for its own oldest tile (vmcnt), then one
@@ -571,13 +575,16 @@ constexpr int kFwdStages = 2;       // 64 KiB of LDS: two blocks per CU
 constexpr int kDqStages = 4;
 constexpr int kTileB = 64 * kRowB;  // bytes per 64-row tile
 
+// chunk swizzle of a tile row (see above)
+DEV int row_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
 // Global byte offsets (from the tile's first row) of the lane's chunks in the
 // four 1 KiB loads of wave `wave` (tile rows 16*wave .. 16*wave + 15).
 DEV void tile_offsets(uint32_t (&vo)[4], int wave, int lane, uint32_t ld_b) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = (wave * 4 + i) * 4 + (lane >> 4);
-    const int c = (lane & 15) ^ (r & 15);
+    const int c = (lane & 15) ^ row_swz(r & 15);
     vo[i] = (uint32_t)r * ld_b + (uint32_t)c * 16u;
   }
 }
@@ -592,7 +599,7 @@ struct RowFrag {
   DEV explicit RowFrag(int lane) {
     const int l32 = lane & 31, g = lane >> 5;
     base = l32 * kRowB;
-    w = g ^ (l32 & 15);
+    w = g ^ row_swz(l32 & 15);
   }
   DEV int off(int blk, int ks) const { return blk * 32 * kRowB + base + (((2 * ks) ^ w) << 4); }
 };
@@ -610,8 +617,8 @@ struct TrFrag {
     const int x0 = 4 * g + e, x1 = 8 + 4 * g + e;
     b0 = x0 * kRowB + (c & 1) * 8;
     b1 = x1 * kRowB + (c & 1) * 8;
-    y0 = c0 ^ x0;
-    y1 = c0 ^ x1;
+    y0 = c0 ^ row_swz(x0);
+    y1 = c0 ^ row_swz(x1);
   }
   DEV u32x4 read(const char* tile, int kk, int db) const {
     const u32x2 a = ld_tr16(tile + kk * 16 * kRowB + b0 + (((db * 4) ^ y0) << 4));

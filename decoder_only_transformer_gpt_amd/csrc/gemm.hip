@@ -486,34 +486,39 @@ struct Epilogue<T, Epi::GradF32> {
 // bf16 GEMM with both operands k-contiguous (y = x W^T and, with a
 // transposed weight copy, dx = dy W), fed by direct-to-LDS buffer loads.
 //
-// K tiles are 32 wide (64-byte rows) and live in NSTAGE LDS stages; tile kt+3
-// is in flight while tile kt is consumed, so each global load has three tiles
-// of MFMA work to land. A wave's buffer_load ... lds writes 1 KiB contiguous
-// (lane L at +16L), i.e. 16 rows of 64 bytes; each lane picks the global 16-byte
-// chunk it fetches so that chunk c of row r lands at position c ^ ((r>>1)&3).
-// The MFMA fragment reads (32 rows, one chunk) then hit 8 distinct 4-bank
-// groups per 8 lanes: conflict-free without padding. Rows past M read as zero
-// (buffer record count). One explicit vmcnt wait and one barrier per K tile.
-template <int BM, int BN, int NSTAGE, int OCC, Epi E>
-__global__ __launch_bounds__(kThreads, OCC) void gemm_nt_lds_kernel(GemmArgs args) {
+// K tiles are BK = 32 or 64 wide (64- or 128-byte rows) and live in NSTAGE
+// LDS stages; tile kt + NSTAGE - 1 is requested while tile kt is consumed. A
+// wave's buffer_load ... lds writes 1 KiB contiguous (lane L at +16L), i.e.
+// 1024/ROWB rows; each lane picks the global 16-byte chunk it fetches so that
+// chunk c of row r lands at position c ^ ((r / RP) mod CH), RP = 256/ROWB
+// rows per 256 bytes, CH = ROWB/16 chunks per row. A 16-lane slice of an
+// MFMA fragment read (16 consecutive rows, one chunk) then covers all 64 banks
+// once: rows in one 256-byte bank line differ in their row offset, rows RP
+// apart in the chunk position. Rows past M read as zero (buffer record count).
+// One explicit vmcnt wait and one barrier per K tile.
+template <int BM, int BN, int NSTAGE, int OCC, Epi E, int NW = 4, int BK = 32>
+__global__ __launch_bounds__(NW * 64, OCC) void gemm_nt_lds_kernel(GemmArgs args) {
   using T = bf16;
-  constexpr int BK = 32, ROWB = BK * 2;
-  constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
+  constexpr int ROWB = BK * 2, CH = ROWB / 16, RP = 256 / ROWB, RPK = 1024 / ROWB;
+  constexpr int KSTEPS = BK / 16;
+  constexpr int WGN = NW / 2;                              // waves along n (2 along m)
+  constexpr int WM = BM / 2, WN = BN / WGN, TM = WM / 32, TN = WN / 32;
   constexpr int STAGE = (BM + BN) * ROWB;                  // bytes per stage
-  constexpr int LA = BM * ROWB / 1024 / 4, LB = BN * ROWB / 1024 / 4;  // 1 KiB loads per wave per tile
+  constexpr int LA = BM * ROWB / 1024 / NW, LB = BN * ROWB / 1024 / NW;  // 1 KiB loads per wave per tile
   constexpr int NLOAD = LA + LB;
-  static_assert(LA >= 1 && LB >= 1, "tile too small for 4 waves");
+  static_assert(BK == 32 || BK == 64, "K tile");
+  static_assert(LA >= 1 && LB >= 1, "tile too small for the wave count");
+  static_assert(NSTAGE >= 2 && NSTAGE <= 4, "two to four stage arrays");
   // one array per stage, so the compiler can tell the stages' LDS-direct
   // loads apart and wait only for the oldest tile
   __shared__ __attribute__((aligned(1024))) char st0[STAGE];
   __shared__ __attribute__((aligned(1024))) char st1[STAGE];
-  __shared__ __attribute__((aligned(1024))) char st2[STAGE];
+  __shared__ __attribute__((aligned(1024))) char st2[NSTAGE >= 3 ? STAGE : 1024];
   __shared__ __attribute__((aligned(1024))) char st3[NSTAGE == 4 ? STAGE : 1024];
-  static_assert(NSTAGE == 3 || NSTAGE == 4, "three or four stage arrays");
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
-  const int wm = wave >> 1, wn = wave & 1, g = lane >> 5, l32 = lane & 31;
+  const int wm = wave / WGN, wn = wave % WGN, g = lane >> 5, l32 = lane & 31;
   const int M = args.M, N = args.N, K = args.K;
   const int tiles_n = (N + BN - 1) / BN;
   int bid = blockIdx.x;
@@ -532,14 +537,20 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_nt_lds_kernel(GemmArgs arg
   const int rec_a = ra64 > (1 << 30) ? (1 << 30) : (int)ra64;
   const int rec_b = rb64 > (1 << 30) ? (1 << 30) : (int)rb64;
 
-  // per-lane global byte offsets of this wave's 1 KiB slots (16 rows each)
-  const int lrow = lane >> 2, lpos = lane & 3;
-  const uint32_t lchunk = (uint32_t)(lpos ^ ((lrow >> 1) & 3));
+  // per-lane global byte offsets of this wave's 1 KiB slots (RPK rows each);
+  // the swizzle depends on the tile row, not on the row within the slot
+  const int lrow = lane / CH, lpos = lane % CH;
   uint32_t voa[LA], vob[LB];
 #pragma unroll
-  for (int i = 0; i < LA; ++i) voa[i] = (uint32_t)((wave * LA + i) * 16 + lrow) * lda_b + lchunk * 16u;
+  for (int i = 0; i < LA; ++i) {
+    const int r = (wave * LA + i) * RPK + lrow;
+    voa[i] = (uint32_t)r * lda_b + (uint32_t)(lpos ^ ((r / RP) & (CH - 1))) * 16u;
+  }
 #pragma unroll
-  for (int i = 0; i < LB; ++i) vob[i] = (uint32_t)((wave * LB + i) * 16 + lrow) * ldb_b + lchunk * 16u;
+  for (int i = 0; i < LB; ++i) {
+    const int r = (wave * LB + i) * RPK + lrow;
+    vob[i] = (uint32_t)r * ldb_b + (uint32_t)(lpos ^ ((r / RP) & (CH - 1))) * 16u;
+  }
 
   auto stage = [&](int q) -> char* { return q == 0 ? st0 : q == 1 ? st1 : q == 2 ? st2 : st3; };
   auto issue = [&](int kt, char* st) {
@@ -562,15 +573,17 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_nt_lds_kernel(GemmArgs arg
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  // fragment byte offsets inside a stage for k-step 0 / 1 (row l32 of a 32-row block)
-  const int swz = (l32 >> 1) & 3;
-  const int fo0 = l32 * ROWB + ((0 * 2 + g) ^ swz) * 16, fo1 = l32 * ROWB + ((1 * 2 + g) ^ swz) * 16;
+  // fragment byte offsets inside a stage for each k-step (row l32 of a 32-row block)
+  const int swz = (l32 / RP) & (CH - 1);
+  int fo[KSTEPS];
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks) fo[ks] = l32 * ROWB + ((ks * 2 + g) ^ swz) * 16;
 
   issue(0, st0);
-  issue(min(1, nk - 1), st1);
+  if (NSTAGE >= 3) issue(min(1, nk - 1), st1);
   if (NSTAGE == 4) issue(min(2, nk - 1), st2);
-  // tile kt sits in stage kt % 4; the loop is unrolled by four so every
-  // stage is a distinct, statically known LDS object
+  // tile kt sits in stage kt % NSTAGE; the loop is unrolled by NSTAGE so
+  // every stage is a distinct, statically known LDS object
   auto tile = [&](int kt, const char* cur, char* nxt) {
     // tile kt's loads are the oldest outstanding: wait until only the
     // NSTAGE-2 younger tiles' loads remain, then make everyone's visible
@@ -582,17 +595,16 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_nt_lds_kernel(GemmArgs arg
     issue(min(kt + NSTAGE - 1, nk - 1), nxt);  // into the stage freed by tile kt-1 (past the end: harmless re-read)
     const char* As = cur + wm * WM * ROWB;
     const char* Bs = cur + BM * ROWB + wn * WN * ROWB;
-    u32x4 af[2][TM], bfr[2][TN];
+    u32x4 af[KSTEPS][TM], bfr[KSTEPS][TN];
 #pragma unroll
-    for (int i = 0; i < TM; ++i) af[0][i] = ld16(As + i * 32 * ROWB + fo0);
+    for (int ks = 0; ks < KSTEPS; ++ks) {
 #pragma unroll
-    for (int j = 0; j < TN; ++j) bfr[0][j] = ld16(Bs + j * 32 * ROWB + fo0);
+      for (int i = 0; i < TM; ++i) af[ks][i] = ld16(As + i * 32 * ROWB + fo[ks]);
 #pragma unroll
-    for (int i = 0; i < TM; ++i) af[1][i] = ld16(As + i * 32 * ROWB + fo1);
+      for (int j = 0; j < TN; ++j) bfr[ks][j] = ld16(Bs + j * 32 * ROWB + fo[ks]);
+    }
 #pragma unroll
-    for (int j = 0; j < TN; ++j) bfr[1][j] = ld16(Bs + j * 32 * ROWB + fo1);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+    for (int ks = 0; ks < KSTEPS; ++ks)
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -600,11 +612,18 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_nt_lds_kernel(GemmArgs arg
     constexpr int NR = TM + TN, NM = TM * TN, PER = NM / NR > 0 ? NM / NR : 1;
     __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
 #pragma unroll
-    for (int q = 0; q < NR; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      if (ks + 1 < KSTEPS) {
+#pragma unroll
+        for (int q = 0; q < NR; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        if (NM > NR * PER) __builtin_amdgcn_sched_group_barrier(0x008, NM - NR * PER, 0);
+      } else {
+        __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
+      }
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 2 * NM - NR * PER, 0);
   };
   if constexpr (NSTAGE == 4) {
     for (int kt = 0; kt < nk; kt += 4) {
@@ -613,22 +632,26 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_nt_lds_kernel(GemmArgs arg
       if (kt + 2 < nk) tile(kt + 2, st2, st1);
       if (kt + 3 < nk) tile(kt + 3, st3, st2);
     }
-  } else {
+  } else if constexpr (NSTAGE == 3) {
     for (int kt = 0; kt < nk; kt += 3) {
       tile(kt, st0, st2);
       if (kt + 1 < nk) tile(kt + 1, st1, st0);
       if (kt + 2 < nk) tile(kt + 2, st2, st1);
     }
+  } else {
+    for (int kt = 0; kt < nk; kt += 2) {
+      tile(kt, st0, st1);
+      if (kt + 1 < nk) tile(kt + 1, st1, st0);
+    }
   }
   __builtin_amdgcn_s_waitcnt(0);  // no LDS-direct load may land during the epilogue
   __syncthreads();
   // each wave stages its 32-row slabs in a private region: two waves per
-  // stage when two slabs fit, else one stage per wave (needs 4 stages)
+  // stage when two slabs fit, else one stage per wave
   constexpr int SLAB = 32 * (WN + 4) * (int)sizeof(float);
-  constexpr bool TWO = 2 * SLAB <= STAGE;
-  static_assert(TWO || (NSTAGE == 4 && SLAB <= STAGE), "epilogue slabs must fit the stages");
-  float* slab = TWO ? reinterpret_cast<float*>(stage(wave >> 1) + (wave & 1) * SLAB)
-                    : reinterpret_cast<float*>(stage(wave));
+  constexpr int PERST = STAGE / SLAB;  // slabs per stage
+  static_assert(PERST >= 1 && (NW + PERST - 1) / PERST <= NSTAGE, "epilogue slabs must fit the stages");
+  float* slab = reinterpret_cast<float*>(stage(wave / PERST) + (wave % PERST) * SLAB);
   Epilogue<T, E>::template run<TM, TN, WN>(args, acc, slab, m0 + wm * WM, n0 + wn * WN, lane);
 }
 
@@ -644,26 +667,28 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_nt_lds_kernel(GemmArgs arg
 // transposing read delivers (rows 4g+e, then 8+4g+e, of each 16-row step),
 // the same for both operands. Pipeline and epilogue as in the NT kernel;
 // blockIdx.z selects a split-K slice (whole K tiles).
-template <int BM, int BN, int NSTAGE, int OCC, Epi E>
-__global__ __launch_bounds__(kThreads, OCC) void gemm_tn_lds_kernel(GemmArgs args) {
+template <int BM, int BN, int NSTAGE, int OCC, Epi E, int NW = 4, int BK = 32>
+__global__ __launch_bounds__(NW * 64, OCC) void gemm_tn_lds_kernel(GemmArgs args) {
   using T = bf16;
-  constexpr int BK = 32;
+  constexpr int KK = BK / 16;                   // MFMA k-steps per K tile
   constexpr int ROWA = BM * 2, ROWB = BN * 2;   // bytes per k row
   constexpr int CHA = ROWA / 16, CHB = ROWB / 16;
-  constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
+  constexpr int WGN = NW / 2;                   // waves along n (2 along m)
+  constexpr int WM = BM / 2, WN = BN / WGN, TM = WM / 32, TN = WN / 32;
   constexpr int STAGE = BK * (ROWA + ROWB);
-  constexpr int LA = BK * ROWA / 1024 / 4, LB = BK * ROWB / 1024 / 4;  // 1 KiB loads per wave per tile
+  constexpr int LA = BK * ROWA / 1024 / NW, LB = BK * ROWB / 1024 / NW;  // 1 KiB loads per wave per tile
   constexpr int NLOAD = LA + LB;
   static_assert(LA >= 1 && LB >= 1 && CHA >= 16 && CHB >= 16, "tile shape");
+  static_assert(BK == 32 || BK == 64, "K tile");
   __shared__ __attribute__((aligned(1024))) char st0[STAGE];
   __shared__ __attribute__((aligned(1024))) char st1[STAGE];
-  __shared__ __attribute__((aligned(1024))) char st2[STAGE];
+  __shared__ __attribute__((aligned(1024))) char st2[NSTAGE >= 3 ? STAGE : 1024];
   __shared__ __attribute__((aligned(1024))) char st3[NSTAGE == 4 ? STAGE : 1024];
-  static_assert(NSTAGE == 3 || NSTAGE == 4, "three or four stage arrays");
+  static_assert(NSTAGE >= 2 && NSTAGE <= 4, "two to four stage arrays");
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1, g = lane >> 5;
+  const int wm = wave / WGN, wn = wave % WGN, g = lane >> 5;
   const int M = args.M, N = args.N, K = args.K;
   const int tiles_n = (N + BN - 1) / BN;
   int bid = blockIdx.x;
@@ -735,7 +760,7 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_tn_lds_kernel(GemmArgs arg
   };
 
   issue(0, st0);
-  issue(min(1, nk - 1), st1);
+  if (NSTAGE >= 3) issue(min(1, nk - 1), st1);
   if (NSTAGE == 4) issue(min(2, nk - 1), st2);
   auto tile = [&](int kt, const char* cur, char* nxt) {
     constexpr int YOUNG = NLOAD * (NSTAGE - 2);
@@ -744,28 +769,36 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_tn_lds_kernel(GemmArgs arg
     issue(min(kt + NSTAGE - 1, nk - 1), nxt);
     const char* As = cur;
     const char* Bs = cur + BK * ROWA;
-    u32x4 af[2][TM], bfr[2][TN];
+    u32x4 af[KK][TM], bfr[KK][TN];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+    for (int kk = 0; kk < KK; ++kk) {
 #pragma unroll
       for (int i = 0; i < TM; ++i) af[kk][i] = frag(As + kk * 16 * ROWA, ofa[i], ROWA);
 #pragma unroll
       for (int j = 0; j < TN; ++j) bfr[kk][j] = frag(Bs + kk * 16 * ROWB, ofb[j], ROWB);
     }
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
+    for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = mfma16(bfr[kk][j], af[kk][i], acc[i][j], (T*)nullptr);
+    // per k-step: 2 (TM+TN) transposing reads spread over its TM*TN MFMAs
     constexpr int NR = 2 * (TM + TN), NM = TM * TN, PER = NM / NR > 0 ? NM / NR : 1;
     __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
 #pragma unroll
-    for (int q = 0; q < NR; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    for (int kk = 0; kk < KK; ++kk) {
+      if (kk + 1 < KK) {
+#pragma unroll
+        for (int q = 0; q < NR; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        if (NM > NR * PER) __builtin_amdgcn_sched_group_barrier(0x008, NM - NR * PER, 0);
+      } else {
+        __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
+      }
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 2 * NM - NR * PER, 0);
   };
   if constexpr (NSTAGE == 4) {
     for (int kt = 0; kt < nk; kt += 4) {
@@ -774,20 +807,24 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_tn_lds_kernel(GemmArgs arg
       if (kt + 2 < nk) tile(kt + 2, st2, st1);
       if (kt + 3 < nk) tile(kt + 3, st3, st2);
     }
-  } else {
+  } else if constexpr (NSTAGE == 3) {
     for (int kt = 0; kt < nk; kt += 3) {
       tile(kt, st0, st2);
       if (kt + 1 < nk) tile(kt + 1, st1, st0);
       if (kt + 2 < nk) tile(kt + 2, st2, st1);
     }
+  } else {
+    for (int kt = 0; kt < nk; kt += 2) {
+      tile(kt, st0, st1);
+      if (kt + 1 < nk) tile(kt + 1, st1, st0);
+    }
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   constexpr int SLAB = 32 * (WN + 4) * (int)sizeof(float);
-  constexpr bool TWO = 2 * SLAB <= STAGE;
-  static_assert(TWO || (NSTAGE == 4 && SLAB <= STAGE), "epilogue slabs must fit the stages");
-  float* slab = TWO ? reinterpret_cast<float*>(stage(wave >> 1) + (wave & 1) * SLAB)
-                    : reinterpret_cast<float*>(stage(wave));
+  constexpr int PERST = STAGE / SLAB;  // slabs per stage
+  static_assert(PERST >= 1 && (NW + PERST - 1) / PERST <= NSTAGE, "epilogue slabs must fit the stages");
+  float* slab = reinterpret_cast<float*>(stage(wave / PERST) + (wave % PERST) * SLAB);
   Epilogue<T, E>::template run<TM, TN, WN>(args, acc, slab, m0 + wm * WM, n0 + wn * WN, lane);
 }
 
@@ -850,18 +887,22 @@ hipError_t launch_layout(const GemmArgs& a, hipStream_t s) {
   }
 }
 
-template <int BM, int BN, int NSTAGE, int OCC, Epi E>
+template <int BM, int BN, int NSTAGE, int OCC, Epi E, int NW = 4, int BK = 32>
 hipError_t launch_nt_lds(const GemmArgs& a, hipStream_t s) {
+  if (a.K % BK != 0) return hipErrorInvalidValue;
   const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_nt_lds_kernel<BM, BN, NSTAGE, OCC, E>), dim3(tiles), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((gemm_nt_lds_kernel<BM, BN, NSTAGE, OCC, E, NW, BK>), dim3(tiles), dim3(NW * 64), 0, s, a);
   return hipGetLastError();
 }
 
 
-template <int BM, int BN, int NSTAGE, int OCC, Epi E>
+template <int BM, int BN, int NSTAGE, int OCC, Epi E, int NW = 4, int BK = 32>
 hipError_t launch_tn_lds(const GemmArgs& a, hipStream_t s) {
+  // split-K slices are whole K tiles and K itself a whole number of them
+  if (a.K % BK != 0) return hipErrorInvalidValue;
   const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_tn_lds_kernel<BM, BN, NSTAGE, OCC, E>), dim3(tiles, 1, a.splits), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((gemm_tn_lds_kernel<BM, BN, NSTAGE, OCC, E, NW, BK>), dim3(tiles, 1, a.splits), dim3(NW * 64), 0,
+                     s, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.splits <= 1) return err;
   const int64_t total4 = (int64_t)a.M * a.N / 4;
@@ -874,20 +915,19 @@ hipError_t launch_tn_lds(const GemmArgs& a, hipStream_t s) {
 template <Epi E>
 hipError_t launch_nt_lds_tile(const GemmArgs& a, hipStream_t s) {
   const int64_t t256 = (int64_t)((a.M + 255) / 256) * ((a.N + 255) / 256);
-  // tile: 1 = 256x256 (one CTA per CU), 2 = 256x128 (two per CU), 3 = 128x128.
-  // By shape: 256x256 when there are at least two tiles per CU, except that
-  // heavy epilogues over a short K loop (the relu^2 backward and residual
-  // reads, the LM head's softcap and exp sums) prefer two CTAs per CU, so one
-  // CTA's epilogue runs under the other's MFMA work.
-  const bool heavy_epi = E == Epi::Relu2Bwd || E == Epi::LMHead || (E == Epi::Residual && a.K <= 2048);
+  // tile: 1 = 256x256 (8 waves, two per SIMD; 64-wide K tiles when K allows),
+  // 2 = 256x128 (4 waves, two CTAs per CU), 3 = 128x128. By shape: 256x256
+  // when there are at least two tiles per CU, else 128x128.
   int tile = a.tile;
-  if (tile == 0) tile = (t256 >= 512 && a.N % 256 == 0) ? (heavy_epi ? 2 : 1) : 3;
+  if (tile == 0) tile = (t256 >= 512 && a.N % 256 == 0) ? 1 : 3;
   if constexpr (E == Epi::LMHead) {  // exp-sum partials per 64 columns: BN a multiple of 128
+    if (tile == 1 && a.K % 64 == 0) return launch_nt_lds<256, 256, 2, 1, E, 8, 64>(a, s);
     if (tile == 1) return launch_nt_lds<256, 256, 4, 1, E>(a, s);
     if (tile == 2) return launch_nt_lds<256, 128, 3, 2, E>(a, s);
     return launch_nt_lds<128, 256, 4, 1, E>(a, s);
   } else {
-    if (tile == 1) return launch_nt_lds<256, 256, 4, 1, E>(a, s);
+    if (tile == 1 && a.K % 64 == 0) return launch_nt_lds<256, 256, 2, 1, E, 8, 64>(a, s);
+    if (tile == 1) return launch_nt_lds<256, 256, 4, 1, E, 8>(a, s);
     if (tile == 2) return launch_nt_lds<256, 128, 3, 2, E>(a, s);
     return launch_nt_lds<128, 128, 4, 1, E>(a, s);
   }
@@ -914,7 +954,7 @@ hipError_t launch_typed(Epi epi, const GemmArgs& a, hipStream_t s) {
       const int64_t t256 = (int64_t)((a.M + 255) / 256) * ((a.N + 255) / 256) * a.splits;
       int tile = a.tile;
       if (tile == 0) tile = (t256 >= 256 && a.M % 256 == 0 && a.N % 256 == 0) ? 1 : 2;
-      if (tile == 1 && a.M % 256 == 0 && a.N % 256 == 0) return launch_tn_lds<256, 256, 4, 1, Epi::GradF32>(a, s);
+      if (tile == 1 && a.M % 256 == 0 && a.N % 256 == 0) return launch_tn_lds<256, 256, 4, 1, Epi::GradF32, 8>(a, s);
       return launch_tn_lds<128, 128, 4, 1, Epi::GradF32>(a, s);
     }
   }
