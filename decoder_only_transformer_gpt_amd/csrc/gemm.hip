@@ -461,7 +461,8 @@ struct Epilogue<T, Epi::GradF32> {
   template <int TM, int TN, int WN>
   static DEV void run(const GemmArgs& a, f32x16 (&acc)[TM][TN], float* lds, int mbase, int nbase, int lane) {
     if (a.splits > 1) {
-      float* P = a.split_buf + (int64_t)blockIdx.z * a.M * a.N;
+      const int z = a.zslice >= 0 ? a.zslice : (int)blockIdx.z;
+      float* P = a.split_buf + (int64_t)z * a.M * a.N;
       staged_store<TM, TN, WN>(acc, lds, mbase, nbase, lane, [&](int m, int n, float (&v)[4]) {
         if (m < a.M && n < a.N) store4(P + (int64_t)m * a.N + n, v);
       });
@@ -666,7 +667,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm_nt_lds_kernel(GemmArgs args
 // read touches fall on distinct banks. The MFMA k order is the one the
 // transposing read delivers (rows 4g+e, then 8+4g+e, of each 16-row step),
 // the same for both operands. Pipeline and epilogue as in the NT kernel;
-// blockIdx.z selects a split-K slice (whole K tiles).
+// split-K slices are whole K tiles.
 template <int BM, int BN, int NSTAGE, int OCC, Epi E, int NW = 4, int BK = 32>
 __global__ __launch_bounds__(NW * 64, OCC) void gemm_tn_lds_kernel(GemmArgs args) {
   using T = bf16;
@@ -690,13 +691,18 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm_tn_lds_kernel(GemmArgs args
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WGN, wn = wave % WGN, g = lane >> 5;
   const int M = args.M, N = args.N, K = args.K;
-  const int tiles_n = (N + BN - 1) / BN;
-  int bid = blockIdx.x;
+  const int tiles_n = (N + BN - 1) / BN, tiles = ((M + BM - 1) / BM) * tiles_n;
+  // 1-D grid over (split-K slice, tile), slice-major. Blocks are dealt
+  // round-robin to the 8 XCDs; remap so that each XCD takes a contiguous run
+  // of items, i.e. whole slices: the tiles of one slice stream through the
+  // same K window together and share it in that XCD's L2.
+  int item = blockIdx.x;
   const int nb = gridDim.x;
-  if ((nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
+  if ((nb & 7) == 0) item = (item & 7) * (nb >> 3) + (item >> 3);
+  const int split = item / tiles, bid = item % tiles;
   const int m0 = (bid / tiles_n) * BM, n0 = (bid % tiles_n) * BN;
   const int kper = ((K + args.splits - 1) / args.splits + BK - 1) / BK * BK;
-  const int kbeg = blockIdx.z * kper;
+  const int kbeg = split * kper;
   const int kend = min(K, kbeg + kper);
   const int nk = kend > kbeg ? (kend - kbeg) / BK : 0;
   const T* Ap = reinterpret_cast<const T*>(args.A) + m0;
@@ -825,7 +831,9 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm_tn_lds_kernel(GemmArgs args
   constexpr int PERST = STAGE / SLAB;  // slabs per stage
   static_assert(PERST >= 1 && (NW + PERST - 1) / PERST <= NSTAGE, "epilogue slabs must fit the stages");
   float* slab = reinterpret_cast<float*>(stage(wave / PERST) + (wave % PERST) * SLAB);
-  Epilogue<T, E>::template run<TM, TN, WN>(args, acc, slab, m0 + wm * WM, n0 + wn * WN, lane);
+  GemmArgs ea = args;
+  ea.zslice = split;
+  Epilogue<T, E>::template run<TM, TN, WN>(ea, acc, slab, m0 + wm * WM, n0 + wn * WN, lane);
 }
 
 // Sums split-K partials in slice order into the fp32 gradient.
@@ -901,7 +909,7 @@ hipError_t launch_tn_lds(const GemmArgs& a, hipStream_t s) {
   // split-K slices are whole K tiles and K itself a whole number of them
   if (a.K % BK != 0) return hipErrorInvalidValue;
   const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_tn_lds_kernel<BM, BN, NSTAGE, OCC, E, NW, BK>), dim3(tiles, 1, a.splits), dim3(NW * 64), 0,
+  hipLaunchKernelGGL((gemm_tn_lds_kernel<BM, BN, NSTAGE, OCC, E, NW, BK>), dim3(tiles * a.splits), dim3(NW * 64), 0,
                      s, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.splits <= 1) return err;

@@ -87,12 +87,16 @@ struct Planner {
 };
 
 // Split-K slices for a dW GEMM [M, N] reduced over K tokens: enough blocks
-// to cover the 256 CUs about twice, at least 1024 k per slice.
+// to cover the 256 CUs about twice, at least 1024 k per slice, and (where
+// that stays within the limits) tiles * slices a multiple of 8, so the
+// kernel can hand each XCD whole slices.
 int dw_splits(int M, int N, int K) {
   const int64_t tiles = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
-  int s = (int)std::max<int64_t>(1, (512 + tiles - 1) / tiles);
-  s = std::min(s, std::max(1, K / 1024));
-  return std::min(s, 32);
+  const int cap = std::min(32, std::max(1, K / 1024));
+  int s = std::min(cap, (int)std::max<int64_t>(1, (512 + tiles - 1) / tiles));
+  for (int t = s; t <= cap; ++t)
+    if ((tiles * t) % 8 == 0) return t;
+  return s;
 }
 
 Layout plan(const gpt_config& c, int maxB, int maxT) {

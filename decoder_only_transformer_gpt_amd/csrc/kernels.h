@@ -38,6 +38,7 @@ struct GemmArgs {
   // GradF32
   int accumulate = 0;
   float* split_buf = nullptr;  // [splits, M, N] partials when splits > 1
+  int zslice = -1;             // split-K slice of the block; -1: blockIdx.z
 };
 
 // dtype: 0 = fp32, 1 = bf16 (gpt.h GPT_F32 / GPT_BF16)
