@@ -86,17 +86,31 @@ struct Planner {
   }
 };
 
-// Split-K slices for a dW GEMM [M, N] reduced over K tokens: enough blocks
-// to cover the 256 CUs about twice, at least 1024 k per slice, and (where
-// that stays within the limits) tiles * slices a multiple of 8, so the
-// kernel can hand each XCD whole slices.
+// Split-K slices for a dW GEMM [M, N] reduced over K tokens (256x256 tiles,
+// one CTA per CU, 256 CUs). Candidates give at least two rounds of CTAs (at
+// least 1024 k per slice, at most 32 slices). Score of a slice count t: the
+// busy fraction of the rounds, with a 10 % handicap when tiles * t is not a
+// multiple of 8 (the kernel then cannot hand each XCD whole slices, whose K
+// windows share its L2). The fewest slices scoring at least 0.93 (each slice
+// adds an M x N fp32 partial), else the best score.
 int dw_splits(int M, int N, int K) {
   const int64_t tiles = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
   const int cap = std::min(32, std::max(1, K / 1024));
-  int s = std::min(cap, (int)std::max<int64_t>(1, (512 + tiles - 1) / tiles));
-  for (int t = s; t <= cap; ++t)
-    if ((tiles * t) % 8 == 0) return t;
-  return s;
+  int best = cap;
+  double best_score = -1.0;
+  for (int t = 1; t <= cap; ++t) {
+    const int64_t blocks = tiles * t;
+    if (blocks < 512 && t < cap) continue;
+    const int64_t rounds = (blocks + 255) / 256;
+    double score = (double)blocks / (double)(rounds * 256);
+    if (blocks % 8 != 0) score *= 0.9;
+    if (score >= 0.93) return t;
+    if (score > best_score + 1e-9) {
+      best_score = score;
+      best = t;
+    }
+  }
+  return best;
 }
 
 Layout plan(const gpt_config& c, int maxB, int maxT) {
