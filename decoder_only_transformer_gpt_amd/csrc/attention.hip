@@ -572,7 +572,7 @@ __global__ __launch_bounds__(256) void attn_dkv_kernel(const T* __restrict__ qkv
 
 constexpr int kRowB = 256;          // bytes per tile row (128 bf16)
 constexpr int kFwdStages = 2;       // 64 KiB of LDS: two blocks per CU
-constexpr int kDqStages = 4;
+constexpr int kDqStages = 2;        // likewise
 constexpr int kTileB = 64 * kRowB;  // bytes per 64-row tile
 
 // chunk swizzle of a tile row (see above)
@@ -780,37 +780,16 @@ template <bool MASK>
 DEV void dq_tile(const KvStage& s, const RowFrag& rf, const TrFrag& tf, const u32x4 (&qf)[8], const u32x4 (&df)[8],
                  f32x16 (&acc)[4], float sl2, float l2, float dlt, int krel) {
   f32x16 sc[2], dp[2];
-  // S and dP for key rows 0-31, then 32-63; fragments read ahead and
-  // re-filled as their MFMAs issue
-  u32x4 fa[8], fb[8];
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
-    fa[ks] = ld16(s.k + rf.off(0, ks));
-    fb[ks] = ld16(s.v + rf.off(0, ks));
-  }
-  sc[0] = zero16();
-  dp[0] = zero16();
+  for (int kb2 = 0; kb2 < 2; ++kb2) {
+    sc[kb2] = zero16();
+    dp[kb2] = zero16();
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
-    sc[0] = mfma16(fa[ks], qf[ks], sc[0], (bf16*)nullptr);
-    dp[0] = mfma16(fb[ks], df[ks], dp[0], (bf16*)nullptr);
-    fa[ks] = ld16(s.k + rf.off(1, ks));
-    fb[ks] = ld16(s.v + rf.off(1, ks));
+    for (int ks = 0; ks < 8; ++ks) {
+      sc[kb2] = mfma16(ld16(s.k + rf.off(kb2, ks)), qf[ks], sc[kb2], (bf16*)nullptr);
+      dp[kb2] = mfma16(ld16(s.v + rf.off(kb2, ks)), df[ks], dp[kb2], (bf16*)nullptr);
+    }
   }
-  sc[1] = zero16();
-  dp[1] = zero16();
-#pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
-    sc[1] = mfma16(fa[ks], qf[ks], sc[1], (bf16*)nullptr);
-    dp[1] = mfma16(fb[ks], df[ks], dp[1], (bf16*)nullptr);
-  }
-  __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-  }
-  __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
 #pragma unroll
   for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
@@ -822,11 +801,8 @@ DEV void dq_tile(const KvStage& s, const RowFrag& rf, const TrFrag& tf, const u3
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
     const u32x4 sf = pack_frag<bf16>(dp[kk >> 1], kk & 1);
-    u32x4 tk[4];
 #pragma unroll
-    for (int db = 0; db < 4; ++db) tk[db] = tf.read(s.k, kk, db);
-#pragma unroll
-    for (int db = 0; db < 4; ++db) acc[db] = mfma16(tk[db], sf, acc[db], (bf16*)nullptr);
+    for (int db = 0; db < 4; ++db) acc[db] = mfma16(tf.read(s.k, kk, db), sf, acc[db], (bf16*)nullptr);
   }
 }
 
