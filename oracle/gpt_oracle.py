@@ -31,6 +31,12 @@ Readings where the pages are silent (each also fixed in the HIP path):
   angle = t * theta**(-2i/D), positions restart at 0 in every batch row.
 * QK-norm is a per-(token, head) RMSNorm over D, applied after RoPE.
 * Plain causal mask over the whole row; no document masking.
+* Sliding windows ([P1] "A Llama-class transformer...": the "SSSL" pattern of
+  three short-window layers then one full-context layer, the final layer
+  always full; [P4] item 0: a per-layer window pattern) are optional and off
+  by default. A short window W admits key u for query t iff 0 <= t - u < W
+  (the query itself and the W-1 tokens before it); the pages do not say
+  whether the window counts the query token.
 * Loss is the mean over all B*T positions; targets are given explicitly.
 
 Parity pins: every function here is pinned by a test in ``tests/`` against a
@@ -140,16 +146,39 @@ def rope_bwd(dy: np.ndarray, cos: np.ndarray, sin: np.ndarray) -> np.ndarray:
     return np.concatenate([d1 * c + d2 * s, -d1 * s + d2 * c], axis=-1)
 
 
-def causal_mqa_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray):
+def attention_mask(T: int, window: int | None = None) -> np.ndarray:
+    """[T, T] boolean mask over (query t, key u): u <= t, and t - u < window
+    when a sliding window is given ([P1] "A Llama-class transformer...")."""
+    t = np.arange(T)[:, None]
+    u = np.arange(T)[None, :]
+    m = u <= t
+    if window is not None:
+        m &= (t - u) < window
+    return m
+
+
+def layer_window(cfg: dict, layer: int) -> int | None:
+    """Window of a layer under the config's pattern ([P1]: "SSSL" = three
+    short-window layers then one full-context layer, repeating; the final layer
+    always full). None means full causal context."""
+    pattern = cfg.get("window_pattern", "") or ""
+    short = int(cfg.get("window_short", 0) or 0)
+    if not pattern or short <= 0 or layer == cfg["n_layer"] - 1:
+        return None
+    return short if pattern[layer % len(pattern)] == "S" else None
+
+
+def causal_mqa_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, window: int | None = None):
     """Causal attention where all query heads share one K/V head
     ([P5] "Multi-Query Attention"; [P1] causal decoder).
 
-    q [B, T, H, D]; k, v [B, T, D]. Scores s = q.k / sqrt(D), key u <= query t.
+    q [B, T, H, D]; k, v [B, T, D]. Scores s = q.k / sqrt(D), key u <= query t
+    (and t - u < window for a sliding-window layer).
     Returns o [B, T, H, D] and the log-sum-exp of the scaled scores [B, H, T].
     """
     B, T, H, D = q.shape
     scale = 1.0 / math.sqrt(D)
-    mask = np.tril(np.ones((T, T), dtype=bool))
+    mask = attention_mask(T, window)
     o = np.empty_like(q)
     lse = np.empty((B, H, T))
     for b in range(B):
@@ -164,7 +193,7 @@ def causal_mqa_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray):
     return o, lse
 
 
-def causal_mqa_attention_bwd(do, q, k, v):
+def causal_mqa_attention_bwd(do, q, k, v, window: int | None = None):
     """Backward of ``causal_mqa_attention`` through the softmax Jacobian.
 
     dP = do.v ; dS = P * (dP - sum_u P dP) ; dq = dS.k/sqrt(D) ;
@@ -172,7 +201,7 @@ def causal_mqa_attention_bwd(do, q, k, v):
     """
     B, T, H, D = q.shape
     scale = 1.0 / math.sqrt(D)
-    mask = np.tril(np.ones((T, T), dtype=bool))
+    mask = attention_mask(T, window)
     dq = np.empty_like(q)
     dk = np.empty_like(k)
     dv = np.empty_like(v)
@@ -239,7 +268,7 @@ def forward(cfg: dict, params: dict, idx: np.ndarray, targets: np.ndarray, row_c
         qr, kr = rope(q, cos, sin), rope(k, cos, sin)
         qn, rq = rmsnorm(qr, eps)
         kn, rk = rmsnorm(kr, eps)
-        o, lse = causal_mqa_attention(qn, kn[:, :, 0], v[:, :, 0])
+        o, lse = causal_mqa_attention(qn, kn[:, :, 0], v[:, :, 0], layer_window(cfg, l))
         o2 = o.reshape(B, T, H * D)
         x = x + o2 @ W[f"h{l}.w_o"].T
         h2, r2 = rmsnorm(x, eps)
@@ -304,7 +333,8 @@ def backward(cfg: dict, params: dict, idx: np.ndarray, targets: np.ndarray, cach
         o2 = L["o"].reshape(B, T, H * D)
         G[f"h{l}.w_o"] += dx.reshape(N, C).T @ o2.reshape(N, -1)
         do = (dx @ W[f"h{l}.w_o"]).reshape(B, T, H, D)
-        dqn, dkn, dv = causal_mqa_attention_bwd(do, L["qn"], L["kn"][:, :, 0], L["v"][:, :, 0])
+        dqn, dkn, dv = causal_mqa_attention_bwd(do, L["qn"], L["kn"][:, :, 0], L["v"][:, :, 0],
+                                                layer_window(cfg, l))
         dqr = rmsnorm_bwd(dqn, L["qn"], L["rq"])
         dkr = rmsnorm_bwd(dkn[:, :, None, :], L["kn"], L["rk"])
         dq = rope_bwd(dqr, cos, sin)

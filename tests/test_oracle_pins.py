@@ -295,7 +295,8 @@ def test_whole_step_central_differences():
 
 def _torch_step(cfg, P, idx, tg):
     """A second, independent float64 implementation with torch autograd and
-    torch's own rms_norm, SDPA and cross_entropy."""
+    torch's own rms_norm, SDPA and cross_entropy (sliding-window layers through
+    SDPA's boolean mask, built here from the window rule itself)."""
     import torch
     import torch.nn.functional as F
     eps, c, H, D = cfg["norm_eps"], cfg["logit_softcap"], cfg["n_head"], cfg["head_dim"]
@@ -321,7 +322,13 @@ def _torch_step(cfg, P, idx, tg):
         k = qkv[..., H * D:(H + 1) * D].view(B, T, 1, D).transpose(1, 2)
         v = qkv[..., (H + 1) * D:].view(B, T, 1, D).transpose(1, 2)
         q, k = norm(rot(q)), norm(rot(k))
-        y = F.scaled_dot_product_attention(q, k, v, is_causal=True, enable_gqa=True)
+        pattern, short = cfg.get("window_pattern", ""), cfg.get("window_short", 0)
+        if pattern and short and l != cfg["n_layer"] - 1 and pattern[l % len(pattern)] == "S":
+            t_i, u_i = torch.arange(T)[:, None], torch.arange(T)[None, :]
+            allowed = (u_i <= t_i) & (t_i - u_i < short)
+            y = F.scaled_dot_product_attention(q, k, v, attn_mask=allowed, enable_gqa=True)
+        else:
+            y = F.scaled_dot_product_attention(q, k, v, is_causal=True, enable_gqa=True)
         x = x + y.transpose(1, 2).reshape(B, T, H * D) @ W[f"h{l}.w_o"].T
         x = x + F.relu(norm(x) @ W[f"h{l}.w_1"].T).square() @ W[f"h{l}.w_2"].T
     logits = norm(x) @ W["lm_head"].T
@@ -362,3 +369,105 @@ def test_causality_and_row_independence():
     perm = [2, 0, 1]
     _, rows3, _ = O.forward(cfg, P, idx[perm], tg[perm])
     np.testing.assert_allclose(rows3, rows[perm], rtol=1e-14)
+
+
+# ------------------------------------------------------ sliding windows ---
+
+def test_layer_window_pattern():
+    """[P1]: "SSSL" = three short-window layers then one full-context layer,
+    repeating, with the final layer always full."""
+    cfg = tiny_cfg(n_layer=6, window_pattern="SSSL", window_short=4)
+    assert [O.layer_window(cfg, l) for l in range(6)] == [4, 4, 4, None, 4, None]
+    cfg = tiny_cfg(n_layer=4, window_pattern="SSSL", window_short=4)
+    assert [O.layer_window(cfg, l) for l in range(4)] == [4, 4, 4, None]
+    assert all(O.layer_window(tiny_cfg(n_layer=3), l) is None for l in range(3))
+    assert all(O.layer_window(tiny_cfg(n_layer=3, window_pattern="SSSL"), l) is None for l in range(3))
+    # the mask is the set {(t, u): u <= t and t - u < W}, element by element
+    T, W = 9, 3
+    m = O.attention_mask(T, W)
+    for t in range(T):
+        for u in range(T):
+            assert m[t, u] == (u <= t and t - u < W)
+    np.testing.assert_array_equal(O.attention_mask(T, None), np.tril(np.ones((T, T), dtype=bool)))
+
+
+def test_windowed_attention_special_cases_and_brute_force():
+    rng = np.random.default_rng(31)
+    B, T, H, D = 2, 20, 2, 128
+    q, k, v = _qkn(rng, B, T, H, D)
+    full, lse_full = O.causal_mqa_attention(q, k, v)
+    # a window as long as the sequence is plain causal attention
+    o, lse = O.causal_mqa_attention(q, k, v, window=T)
+    np.testing.assert_array_equal(o, full)
+    np.testing.assert_array_equal(lse, lse_full)
+    # window 1: every query sees only itself
+    o1, lse1 = O.causal_mqa_attention(q, k, v, window=1)
+    for h in range(H):
+        np.testing.assert_allclose(o1[:, :, h], v, atol=1e-14)
+        np.testing.assert_allclose(lse1[:, h], np.einsum("btd,btd->bt", q[:, :, h], k) / math.sqrt(D), atol=1e-13)
+    # rows before the window fills agree with full causal attention
+    W = 7
+    ow, lsew = O.causal_mqa_attention(q, k, v, window=W)
+    np.testing.assert_allclose(ow[:, :W], full[:, :W], atol=1e-14)
+    # brute force: an explicit softmax over keys t-W+1 .. t for every row
+    for b in range(B):
+        for t in range(T):
+            for h in range(H):
+                us = range(max(0, t - W + 1), t + 1)
+                sc = np.array([q[b, t, h] @ k[b, u] / math.sqrt(D) for u in us])
+                w = np.exp(sc - sc.max())
+                ref = sum(wi * v[b, u] for wi, u in zip(w / w.sum(), us))
+                np.testing.assert_allclose(ow[b, t, h], ref, atol=1e-13)
+                assert lsew[b, h, t] == pytest.approx(sc.max() + math.log(w.sum()), abs=1e-13)
+
+
+def test_windowed_attention_matches_torch_sdpa_float64():
+    torch = pytest.importorskip("torch")
+    import torch.nn.functional as F
+    rng = np.random.default_rng(32)
+    B, T, H, D, W = 2, 29, 3, 128, 6
+    q, k, v = _qkn(rng, B, T, H, D)
+    o, _ = O.causal_mqa_attention(q, k, v, window=W)
+    qt = torch.tensor(q).permute(0, 2, 1, 3).requires_grad_()
+    kt = torch.tensor(k)[:, None].requires_grad_()
+    vt = torch.tensor(v)[:, None].requires_grad_()
+    t_i, u_i = torch.arange(T)[:, None], torch.arange(T)[None, :]
+    ot = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=(u_i <= t_i) & (t_i - u_i < W), enable_gqa=True)
+    np.testing.assert_allclose(ot.permute(0, 2, 1, 3).detach().numpy(), o, atol=1e-13)
+    do = rng.standard_normal(o.shape)
+    ot.backward(torch.tensor(do).permute(0, 2, 1, 3))
+    dq, dk, dv = O.causal_mqa_attention_bwd(do, q, k, v, window=W)
+    np.testing.assert_allclose(qt.grad.permute(0, 2, 1, 3).numpy(), dq, atol=1e-12)
+    np.testing.assert_allclose(kt.grad[:, 0].numpy(), dk, atol=1e-12)
+    np.testing.assert_allclose(vt.grad[:, 0].numpy(), dv, atol=1e-12)
+
+
+def test_windowed_step_matches_torch_autograd_and_fd():
+    pytest.importorskip("torch")
+    cfg = tiny_cfg(n_layer=3, n_head=2, model_dim=256, mlp_dim=1024, vocab_size=80, window_pattern="SL",
+                   window_short=5)
+    assert [O.layer_window(cfg, l) for l in range(3)] == [5, None, None]
+    P = rand_params(cfg, seed=33, std=0.05)
+    rng = np.random.default_rng(34)
+    idx = rng.integers(0, 80, (2, 17))
+    tg = rng.integers(0, 80, (2, 17))
+    loss, _, G = O.step(cfg, P, idx, tg)
+    tl, TG = _torch_step(cfg, P, idx, tg)
+    assert loss == pytest.approx(tl, rel=1e-13)
+    for name in G:
+        np.testing.assert_allclose(G[name], TG[name], rtol=1e-9, atol=1e-13, err_msg=name)
+    # and the window changes the result (the pattern is not ignored)
+    loss_full = O.forward(tiny_cfg(n_layer=3, n_head=2, model_dim=256, mlp_dim=1024, vocab_size=80), P, idx, tg)[0]
+    assert abs(loss_full - loss) > 1e-6
+    # central differences on the windowed layer's attention weights
+    h = 1e-5
+    W = P["h0.w_qkv"]
+    for ij in [(3, 7), (260, 11), (300, 200)]:
+        old = W[ij]
+        W[ij] = old + h
+        lp = O.forward(cfg, P, idx, tg)[0]
+        W[ij] = old - h
+        lm = O.forward(cfg, P, idx, tg)[0]
+        W[ij] = old
+        fd = (lp - lm) / (2 * h)
+        assert abs(fd - G["h0.w_qkv"][ij]) <= 1e-6 * abs(fd) + 2e-10
