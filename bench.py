@@ -30,13 +30,34 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "train tokens/sec + bf16 MFU, d20 fwd+bwd, seq 2048, 1 MI355X"
 
 
+def layer_windows(cfg) -> list:
+    """Sliding window of every layer (0 = full causal prefix): the pattern
+    repeats over the layers, 'S' selects window_short, the last layer is full."""
+    pat = cfg.window_pattern.decode() if isinstance(cfg.window_pattern, bytes) else cfg.window_pattern
+    out = []
+    for l in range(cfg.n_layer):
+        w = 0
+        if pat and cfg.window_short > 0 and l != cfg.n_layer - 1 and pat[l % len(pat)] == "S":
+            w = cfg.window_short
+        out.append(w)
+    return out
+
+
+def attn_pairs(T: int, W: int) -> int:
+    """(query, key) pairs a layer needs per sequence: causal, within W if W > 0."""
+    if W <= 0 or W >= T:
+        return T * (T + 1) // 2
+    return W * (W + 1) // 2 + (T - W) * W
+
+
 def step_flops(cfg, T: int) -> dict:
-    """Algorithmic FLOPs per token (fwd+bwd): 6 x matmul weights + causal attention
-    over the T(T+1)/2 needed pairs; the embedding gather counts zero."""
+    """Algorithmic FLOPs per token (fwd+bwd): 6 x matmul weights + attention over
+    the needed (query, key) pairs only (T(T+1)/2 per sequence for a causal
+    layer, fewer for a sliding-window one); the embedding gather counts zero."""
     C, H, D, F, V, L = cfg.model_dim, cfg.n_head, 128, cfg.mlp_dim, cfg.vocab_size, cfg.n_layer
     n_mm = L * ((H + 2) * D * C + C * H * D + 2 * F * C) + V * C
-    return {"total": 6.0 * n_mm + 6.0 * L * H * D * (T + 1),
-            "palm": 6.0 * n_mm + 12.0 * L * H * D * T}
+    attn = sum(12.0 * H * D * attn_pairs(T, w) / T for w in layer_windows(cfg))
+    return {"total": 6.0 * n_mm + attn, "palm": 6.0 * n_mm + 12.0 * L * H * D * T}
 
 
 def kernel_flops_per_launch(tag: str, cfg, B: int, T: int) -> float | None:
@@ -56,7 +77,9 @@ def kernel_flops_per_launch(tag: str, cfg, B: int, T: int) -> float | None:
     # kernels: dP and dQ to the dQ kernel, dK and dV to the dK/dV kernel. The
     # recomputation of S (both kernels) and of dP (the dK/dV kernel) is not
     # algorithmic work and is not counted.
-    pairs = B * H * T * (T + 1) / 2.0
+    # per-launch pairs: the mean over the layers (one launch per layer)
+    ws = layer_windows(cfg)
+    pairs = B * H * sum(attn_pairs(T, w) for w in ws) / len(ws)
     if tag == "attn_fwd":
         return 4.0 * D * pairs
     if tag in ("attn_bwd_dq", "attn_bwd_dkv"):
@@ -113,7 +136,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="d20", choices=["tiny", "d4", "d12", "d20"])
+    ap.add_argument("--workload", default="d20", choices=["tiny", "d4", "d12", "d20", "d20-sssl"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-table", action="store_true", help="print per-tag timings to stderr")
     ap.add_argument("--dominant", default=None,
@@ -226,7 +249,9 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(1e3 * elapsed / args.steps, 3), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
         "config": {"workload": f"{wl.name}: depth {cfg.n_layer}, width {cfg.model_dim}, {cfg.n_head} query heads / "
-                               f"1 kv head, head_dim 128, MLP {cfg.mlp_dim}, vocab {cfg.vocab_size}",
+                               f"1 kv head, head_dim 128, MLP {cfg.mlp_dim}, vocab {cfg.vocab_size}"
+                               + (f", windows {wl.window_pattern} (short {wl.window_short})" if wl.window_pattern
+                                  else ""),
                    "global_batch": B, "seq_len": T, "tokens": wl.tokens, "parallelism": "single GPU"},
         "mfu_bf16": round(mfu, 4), "mfu_palm_convention": round(fl["palm"] * tok_s / (PEAK_BF16_TFLOPS * 1e12), 4),
         "loss": round(loss, 5), "roofline": roof,

@@ -31,11 +31,13 @@ class gpt_config(ctypes.Structure):
         ("n_kv_head", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("mlp_dim", ctypes.c_int32),
         ("vocab_size", ctypes.c_int32), ("max_seq_len", ctypes.c_int32),
         ("rope_theta", ctypes.c_float), ("logit_softcap", ctypes.c_float), ("norm_eps", ctypes.c_float),
-        ("dtype", ctypes.c_int32),
+        ("dtype", ctypes.c_int32), ("window_short", ctypes.c_int32), ("window_pattern", ctypes.c_char * 8),
     ]
 
     def as_dict(self) -> dict:
-        return {k: getattr(self, k) for k, _ in self._fields_}
+        d = {k: getattr(self, k) for k, _ in self._fields_}
+        d["window_pattern"] = d["window_pattern"].decode()
+        return d
 
 
 class gpt_tensor_desc(ctypes.Structure):

@@ -31,6 +31,11 @@
 //
 // qkv row (one token): [H query heads | K | V] x 128. LSE and delta are fp32
 // [B, H, T]. Grid blocks are ordered heavy-first for causal load balance.
+//
+// Sliding window (aethryn.com, section "A Llama-class transformer with ten
+// modern departures": short-window layers of the SSSL pattern): with W > 0 a
+// query t sees keys u with 0 <= t - u < W; kernels skip tiles outside the
+// band and mask the tiles it crosses. W = 0 means the full causal prefix.
 
 #include <type_traits>
 
@@ -42,6 +47,10 @@ namespace {
 
 constexpr int D = 128;
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kNoWindow = 1 << 30;  // window length standing for "full causal prefix"
+
+// W = 0 (full) as a length no distance reaches
+DEV int window_len(int W) { return W > 0 ? W : kNoWindow; }
 
 template <typename T>
 struct AT {
@@ -174,7 +183,8 @@ __global__ __launch_bounds__(256) void transpose_heads_kernel(const T* __restric
 // Block: 128 queries of one (batch, head) = 4 waves x 32. KV tiles of 64 keys.
 template <typename T>
 __global__ __launch_bounds__(256) void attn_fwd_kernel(const T* __restrict__ qkv, const T* __restrict__ vT, int T_,
-                                                       int Tp, int H, T* __restrict__ o, float* __restrict__ lse) {
+                                                       int Tp, int H, int W, T* __restrict__ o,
+                                                       float* __restrict__ lse) {
   using A = AT<T>;
   constexpr int V = A::V, NBUF = A::NBUF;
   __shared__ __attribute__((aligned(16))) T Ks[NBUF][64 * A::P];
@@ -202,18 +212,20 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const T* __restrict__ qkv
   const float shift = sqrtf((float)D);
   const float sl2 = kLog2e / shift, sh2 = shift * kLog2e;
   const int kend = min(T_, qb * 128 + 128);
-  const int nt = (kend + 63) / 64;
+  const int t0 = W > 0 ? max(0, qb * 128 - W + 1) / 64 : 0;  // first key tile inside the band
+  const int nt = (kend + 63) / 64 - t0;
+  const int Wl = window_len(W);
 
   Stage<T, 64, D> sk;
   Stage<T, D, 64> sv;
-  sk.load(kbase, ld, T_, tid);
-  sv.load(vtb, Tp, D, tid);
+  sk.load(kbase + (int64_t)t0 * 64 * ld, ld, T_ - t0 * 64, tid);
+  sv.load(vtb + t0 * 64, Tp, D, tid);
   sk.store(Ks[0], A::P, tid);
   sv.store(VTs[0], A::PT, tid);
   __syncthreads();
 
   for (int it = 0; it < nt; ++it) {
-    const int cur = it % NBUF, k0 = it * 64;
+    const int cur = it % NBUF, k0 = (t0 + it) * 64;
     const bool more = it + 1 < nt;
     if (more) {
       sk.load(kbase + (int64_t)(k0 + 64) * ld, ld, T_ - k0 - 64, tid);
@@ -233,7 +245,7 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const T* __restrict__ qkv
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int key = k0 + kb * 32 + blk * 8 + g * 4 + r;
-          const float p = (key <= q && key < T_) ? exp2f(s[kb][blk * 4 + r] * sl2 - sh2) : 0.f;
+          const float p = (key <= q && key < T_ && q - key < Wl) ? exp2f(s[kb][blk * 4 + r] * sl2 - sh2) : 0.f;
           s[kb][blk * 4 + r] = p;
           rsum += p;
         }
@@ -299,7 +311,7 @@ __global__ __launch_bounds__(256) void attn_delta_kernel(const T* __restrict__ o
 template <typename T>
 __global__ __launch_bounds__(256) void attn_dq_kernel(const T* __restrict__ qkv, const T* __restrict__ kT,
                                                       const T* __restrict__ dout, const float* __restrict__ lse,
-                                                      const float* __restrict__ delta, int T_, int Tp, int H,
+                                                      const float* __restrict__ delta, int T_, int Tp, int H, int W,
                                                       T* __restrict__ dqkv) {
   using A = AT<T>;
   constexpr int V = A::V, NBUF = A::NBUF;
@@ -334,20 +346,22 @@ __global__ __launch_bounds__(256) void attn_dq_kernel(const T* __restrict__ qkv,
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc[i] = zero16();
   const int kend = min(T_, qb * 128 + 128);
-  const int nt = (kend + 63) / 64;
+  const int t0 = W > 0 ? max(0, qb * 128 - W + 1) / 64 : 0;  // first key tile inside the band
+  const int nt = (kend + 63) / 64 - t0;
+  const int Wl = window_len(W);
 
   Stage<T, 64, D> sk, sv;
   Stage<T, D, 64> skt;
-  sk.load(kbase, ld, T_, tid);
-  sv.load(kbase + D, ld, T_, tid);
-  skt.load(ktb, Tp, D, tid);
+  sk.load(kbase + (int64_t)t0 * 64 * ld, ld, T_ - t0 * 64, tid);
+  sv.load(kbase + (int64_t)t0 * 64 * ld + D, ld, T_ - t0 * 64, tid);
+  skt.load(ktb + t0 * 64, Tp, D, tid);
   sk.store(Ks[0], A::P, tid);
   sv.store(Vs[0], A::P, tid);
   skt.store(KTs[0], A::PT, tid);
   __syncthreads();
 
   for (int it = 0; it < nt; ++it) {
-    const int cur = it % NBUF, k0 = it * 64;
+    const int cur = it % NBUF, k0 = (t0 + it) * 64;
     const bool more = it + 1 < nt;
     if (more) {
       const T* kp = kbase + (int64_t)(k0 + 64) * ld;
@@ -373,7 +387,7 @@ __global__ __launch_bounds__(256) void attn_dq_kernel(const T* __restrict__ qkv,
         for (int r = 0; r < 4; ++r) {
           const int key = k0 + kb * 32 + blk * 8 + g * 4 + r;
           const int i = blk * 4 + r;
-          const float p = (key <= q && key < T_) ? exp2f(s[i] * sl2 - l2) : 0.f;
+          const float p = (key <= q && key < T_ && q - key < Wl) ? exp2f(s[i] * sl2 - l2) : 0.f;
           ds[kb][i] = p * (dp[i] - dq_);
         }
     }
@@ -414,7 +428,7 @@ template <typename T>
 __global__ __launch_bounds__(256) void attn_dkv_kernel(const T* __restrict__ qkv, const T* __restrict__ qT,
                                                        const T* __restrict__ dout, const T* __restrict__ doT,
                                                        const float* __restrict__ lse,
-                                                       const float* __restrict__ delta, int T_, int Tp, int H,
+                                                       const float* __restrict__ delta, int T_, int Tp, int H, int W,
                                                        T* __restrict__ dqkv) {
   using A = AT<T>;
   constexpr int V = A::V, NBUF = A::NBUF;
@@ -444,8 +458,12 @@ __global__ __launch_bounds__(256) void attn_dkv_kernel(const T* __restrict__ qkv
 #pragma unroll
   for (int i = 0; i < 4; ++i) { adk[i] = zero16(); adv[i] = zero16(); }
 
-  const int qt0 = 2 * kb, nqt = Tp / 64, nq = nqt - qt0;
+  const int qt0 = 2 * kb;
+  // last query tile any of the block's keys is visible from
+  const int nqt = W > 0 ? min(Tp / 64, (kb * 128 + 127 + W - 1) / 64 + 1) : Tp / 64;
+  const int nq = nqt - qt0;
   const int total = H * nq;
+  const int Wl = window_len(W);
   Stage<T, 64, D> sq, sd;
   Stage<T, D, 64> sqt, sdt;
   float pl = 0.f, pe = 0.f;
@@ -505,7 +523,7 @@ __global__ __launch_bounds__(256) void attn_dkv_kernel(const T* __restrict__ qkv
           const int qi = qb2 * 32 + blk * 8 + g * 4 + r;
           const int qq = q0 + qi;
           const int i = blk * 4 + r;
-          const float pv = (qq >= key && qq < T_ && kv) ? exp2f(s[i] * sl2 - Ls[cur][qi]) : 0.f;
+          const float pv = (qq >= key && qq < T_ && kv && qq - key < Wl) ? exp2f(s[i] * sl2 - Ls[cur][qi]) : 0.f;
           p[qb2][i] = pv;
           ds[qb2][i] = pv * (dpv[i] - Es[cur][qi]);
         }
@@ -649,7 +667,7 @@ struct KvStage {
 // S^T = K Q^T puts each query on one lane (its row sum stays in the lane).
 template <bool MASK>
 DEV void fwd_tile(const KvStage& s, const RowFrag& rf, const TrFrag& tf, const u32x4 (&qf)[8], f32x16 (&acc)[4],
-                  float& rsum, float sl2, float sh2, int krel) {
+                  float& rsum, float sl2, float sh2, int krel, int Wl) {
   f32x16 sc[2];
   // key rows 0-31, then 32-63; fragments read ahead, re-filled as consumed
   u32x4 fa[8];
@@ -676,8 +694,11 @@ DEV void fwd_tile(const KvStage& s, const RowFrag& rf, const TrFrag& tf, const u
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       float p = fast_exp2(sc[kb2][i] * sl2 - sh2);
-      // key (tile row kb2*32 + (i/4)*8 + 4g + i%4) <= query
-      if (MASK) p = (kb2 * 32 + (i >> 2) * 8 + (i & 3) + krel <= 0) ? p : 0.f;
+      // key (tile row kb2*32 + (i/4)*8 + 4g + i%4) <= query, within the window
+      if (MASK) {
+        const int dd = kb2 * 32 + (i >> 2) * 8 + (i & 3) + krel;  // key - query
+        p = (dd <= 0 && dd > -Wl) ? p : 0.f;
+      }
       sc[kb2][i] = p;
       rsum += p;
     }
@@ -694,7 +715,7 @@ DEV void fwd_tile(const KvStage& s, const RowFrag& rf, const TrFrag& tf, const u
 
 template <int NST>
 __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void attn_fwd_bf16_kernel(const bf16* __restrict__ qkv, int T_,
-                                                                              int H, bf16* __restrict__ o,
+                                                                              int H, int W, bf16* __restrict__ o,
                                                                               float* __restrict__ lse) {
   static_assert(NST == 2 || NST == 4, "two or four stages");
   __shared__ __attribute__((aligned(1024))) KvStage st0, st1;
@@ -719,14 +740,16 @@ __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void attn_fwd_bf16_kernel(co
   float rsum = 0.f;
   const float shift = sqrtf((float)D);
   const float sl2 = kLog2e / shift, sh2 = shift * kLog2e;
-  const int nt = (min(T_, qb * 128 + 128) + 63) / 64;
+  const int t0 = W > 0 ? max(0, qb * 128 - W + 1) / 64 : 0;  // first key tile inside the band
+  const int nt = (min(T_, qb * 128 + 128) + 63) / 64 - t0;
+  const int Wl = window_len(W);
 
   uint32_t vo[4];
   tile_offsets(vo, wave, lane, ld_b);
   const RowFrag rf(lane);
   const TrFrag tf(lane);
   auto issue = [&](int t, KvStage& s) {
-    const int k0 = t * 64, rows = min(64, T_ - k0);
+    const int k0 = (t0 + t) * 64, rows = min(64, T_ - k0);
     const bf16* kp = base + (int64_t)k0 * ld + H * D;
     tile_issue(uniform_rsrc(kp, rows * (int)ld_b), s.k, vo, wave);
     tile_issue(uniform_rsrc(kp + D, rows * (int)ld_b), s.v, vo, wave);
@@ -735,10 +758,10 @@ __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void attn_fwd_bf16_kernel(co
     wait_vmcnt<(NST - 2) * 8>();  // this wave's part of tile t has landed
     __builtin_amdgcn_s_barrier();
     issue(min(t + NST - 1, nt - 1), nxt);
-    const int k0 = t * 64;
-    if (k0 > qw + 31) return;                       // every key after every query of this wave
-    if (k0 + 63 <= qw) fwd_tile<false>(cur, rf, tf, qf, acc, rsum, sl2, sh2, 0);
-    else fwd_tile<true>(cur, rf, tf, qf, acc, rsum, sl2, sh2, k0 + 4 * g - q);
+    const int k0 = (t0 + t) * 64;
+    if (k0 > qw + 31 || k0 + 63 <= qw - Wl) return;  // the tile misses every query's band
+    if (k0 + 63 <= qw && k0 >= qw + 32 - Wl) fwd_tile<false>(cur, rf, tf, qf, acc, rsum, sl2, sh2, 0, Wl);
+    else fwd_tile<true>(cur, rf, tf, qf, acc, rsum, sl2, sh2, k0 + 4 * g - q, Wl);
   };
   if constexpr (NST == 4) {
     issue(0, st0);
@@ -778,7 +801,7 @@ __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void attn_fwd_bf16_kernel(co
 // Block: 128 queries of one (batch, head) = 4 waves x 32; key tiles of 64.
 template <bool MASK>
 DEV void dq_tile(const KvStage& s, const RowFrag& rf, const TrFrag& tf, const u32x4 (&qf)[8], const u32x4 (&df)[8],
-                 f32x16 (&acc)[4], float sl2, float l2, float dlt, int krel) {
+                 f32x16 (&acc)[4], float sl2, float l2, float dlt, int krel, int Wl) {
   f32x16 sc[2], dp[2];
 #pragma unroll
   for (int kb2 = 0; kb2 < 2; ++kb2) {
@@ -795,7 +818,10 @@ DEV void dq_tile(const KvStage& s, const RowFrag& rf, const TrFrag& tf, const u3
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       float p = fast_exp2(sc[kb2][i] * sl2 - l2);
-      if (MASK) p = (kb2 * 32 + (i >> 2) * 8 + (i & 3) + krel <= 0) ? p : 0.f;
+      if (MASK) {
+        const int dd = kb2 * 32 + (i >> 2) * 8 + (i & 3) + krel;  // key - query
+        p = (dd <= 0 && dd > -Wl) ? p : 0.f;
+      }
       dp[kb2][i] = p * (dp[kb2][i] - dlt);
     }
 #pragma unroll
@@ -811,7 +837,7 @@ __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void attn_dq_bf16_kernel(con
                                                                              const bf16* __restrict__ dout,
                                                                              const float* __restrict__ lse,
                                                                              const float* __restrict__ delta, int T_,
-                                                                             int H, bf16* __restrict__ dqkv) {
+                                                                             int H, int W, bf16* __restrict__ dqkv) {
   static_assert(NST == 2 || NST == 4, "two or four stages");
   __shared__ __attribute__((aligned(1024))) KvStage st0, st1;
   __shared__ __attribute__((aligned(1024))) std::conditional_t<NST == 4, KvStage, char[16]> st2, st3;
@@ -839,14 +865,16 @@ __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void attn_dq_bf16_kernel(con
   f32x16 acc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc[i] = zero16();
-  const int nt = (min(T_, qb * 128 + 128) + 63) / 64;
+  const int t0 = W > 0 ? max(0, qb * 128 - W + 1) / 64 : 0;  // first key tile inside the band
+  const int nt = (min(T_, qb * 128 + 128) + 63) / 64 - t0;
+  const int Wl = window_len(W);
 
   uint32_t vo[4];
   tile_offsets(vo, wave, lane, ld_b);
   const RowFrag rf(lane);
   const TrFrag tf(lane);
   auto issue = [&](int t, KvStage& s) {
-    const int k0 = t * 64, rows = min(64, T_ - k0);
+    const int k0 = (t0 + t) * 64, rows = min(64, T_ - k0);
     const bf16* kp = base + (int64_t)k0 * ld + H * D;
     tile_issue(uniform_rsrc(kp, rows * (int)ld_b), s.k, vo, wave);
     tile_issue(uniform_rsrc(kp + D, rows * (int)ld_b), s.v, vo, wave);
@@ -855,10 +883,10 @@ __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void attn_dq_bf16_kernel(con
     wait_vmcnt<(NST - 2) * 8>();  // this wave's part of tile t has landed
     __builtin_amdgcn_s_barrier();
     issue(min(t + NST - 1, nt - 1), nxt);
-    const int k0 = t * 64;
-    if (k0 > qw + 31) return;
-    if (k0 + 63 <= qw) dq_tile<false>(cur, rf, tf, qf, df, acc, sl2, l2, dlt, 0);
-    else dq_tile<true>(cur, rf, tf, qf, df, acc, sl2, l2, dlt, k0 + 4 * g - q);
+    const int k0 = (t0 + t) * 64;
+    if (k0 > qw + 31 || k0 + 63 <= qw - Wl) return;  // the tile misses every query's band
+    if (k0 + 63 <= qw && k0 >= qw + 32 - Wl) dq_tile<false>(cur, rf, tf, qf, df, acc, sl2, l2, dlt, 0, Wl);
+    else dq_tile<true>(cur, rf, tf, qf, df, acc, sl2, l2, dlt, k0 + 4 * g - q, Wl);
   };
   if constexpr (NST == 4) {
     issue(0, st0);
@@ -905,7 +933,7 @@ struct DkvStage {
 
 template <bool MASK>
 DEV void dkv_tile(const DkvStage& s, int wave, const RowFrag& rf, const TrFrag& tf, const u32x4 (&kf)[8],
-                  const u32x4 (&vf)[8], f32x16 (&adk)[4], f32x16 (&adv)[4], float sl2, int qrel, int g) {
+                  const u32x4 (&vf)[8], f32x16 (&adk)[4], f32x16 (&adv)[4], float sl2, int qrel, int Wl, int g) {
   f32x16 sc[2], dp[2];
   // S^T and dP^T for query rows 0-31, then 32-63: four accumulation chains.
   // Fragments for rows 0-31 are read up front; each is re-filled with its
@@ -951,8 +979,11 @@ DEV void dkv_tile(const DkvStage& s, int wave, const RowFrag& rf, const TrFrag& 
       for (int r = 0; r < 4; ++r) {
         const int i = blk * 4 + r;
         float p = fast_exp2(sc[qb2][i] * sl2 - L[r]);
-        // query (tile row qb2*32 + blk*8 + 4g + r) >= key
-        if (MASK) p = (qb2 * 32 + blk * 8 + r + qrel >= 0) ? p : 0.f;
+        // query (tile row qb2*32 + blk*8 + 4g + r) >= key, within the window
+        if (MASK) {
+          const int dd = qb2 * 32 + blk * 8 + r + qrel;  // query - key
+          p = (dd >= 0 && dd < Wl) ? p : 0.f;
+        }
         sc[qb2][i] = p;
         dp[qb2][i] = p * (dp[qb2][i] - E[r]);
       }
@@ -980,7 +1011,7 @@ __global__ __launch_bounds__(256, 1) void attn_dkv_bf16_kernel(const bf16* __res
                                                                const bf16* __restrict__ dout,
                                                                const float* __restrict__ lse,
                                                                const float* __restrict__ delta, int T_, int H,
-                                                               bf16* __restrict__ dqkv) {
+                                                               int W, bf16* __restrict__ dqkv) {
   __shared__ __attribute__((aligned(1024))) DkvStage st0, st1, st2, st3;
   const int nkb = (T_ + 127) / 128;
   int b, kb;
@@ -1004,8 +1035,12 @@ __global__ __launch_bounds__(256, 1) void attn_dkv_bf16_kernel(const bf16* __res
     adk[i] = zero16();
     adv[i] = zero16();
   }
-  const int nqt = (T_ + 63) / 64, nq = nqt - 2 * kb;
+  // query tiles 2kb .. nqt-1: from the block's first keys to the last query
+  // any of its keys is visible from
+  const int nqt = W > 0 ? min((T_ + 63) / 64, (kb * 128 + 127 + W - 1) / 64 + 1) : (T_ + 63) / 64;
+  const int nq = nqt - 2 * kb;
   const int total = H * nq;
+  const int Wl = window_len(W);
 
   uint32_t voq[4], vod[4];
   tile_offsets(voq, wave, lane, ld_b);
@@ -1025,9 +1060,9 @@ __global__ __launch_bounds__(256, 1) void attn_dkv_bf16_kernel(const bf16* __res
     __builtin_amdgcn_s_barrier();
     issue(min(it + 3, total - 1), nxt);
     const int q0 = (nqt - 1 - it / H) * 64;
-    if (q0 + 63 < kw) return;  // every query before every key of this wave
-    if (q0 >= kw + 31) dkv_tile<false>(cur, wave, rf, tf, kf, vf, adk, adv, sl2, 0, g);
-    else dkv_tile<true>(cur, wave, rf, tf, kf, vf, adk, adv, sl2, q0 + 4 * g - key, g);
+    if (q0 + 63 < kw || q0 - (kw + 31) >= Wl) return;  // the tile misses every key's band
+    if (q0 >= kw + 31 && q0 + 63 - kw < Wl) dkv_tile<false>(cur, wave, rf, tf, kf, vf, adk, adv, sl2, 0, Wl, g);
+    else dkv_tile<true>(cur, wave, rf, tf, kf, vf, adk, adv, sl2, q0 + 4 * g - key, Wl, g);
   };
   issue(0, st0);
   issue(min(1, total - 1), st1);
@@ -1063,22 +1098,25 @@ hipError_t transpose(const void* src, int64_t ld, int col0, int nh, int B, int T
 }
 
 template <typename T>
-hipError_t fwd_typed(const void* qkv, int B, int T_, int H, void* o, float* lse, void* vT, int stage, hipStream_t s) {
+hipError_t fwd_typed(const void* qkv, int B, int T_, int H, int W, void* o, float* lse, void* vT, int stage,
+                     hipStream_t s) {
   const int Tp = attn_padded_len(T_);
   dim3 grid(((T_ + 127) / 128) * H * B);
   if constexpr (sizeof(T) == 2) {
     if (stage == 0) return hipSuccess;  // no transposed copy on this path
-    hipLaunchKernelGGL(attn_fwd_bf16_kernel<kFwdStages>, grid, dim3(256), 0, s, (const bf16*)qkv, T_, H, (bf16*)o, lse);
+    hipLaunchKernelGGL(attn_fwd_bf16_kernel<kFwdStages>, grid, dim3(256), 0, s, (const bf16*)qkv, T_, H, W, (bf16*)o,
+                       lse);
     return hipGetLastError();
   }
   if (stage == 0) return transpose<T>(qkv, (int64_t)(H + 2) * D, (H + 1) * D, 1, B, T_, Tp, vT, s);
-  hipLaunchKernelGGL(attn_fwd_kernel<T>, grid, dim3(256), 0, s, (const T*)qkv, (const T*)vT, T_, Tp, H, (T*)o, lse);
+  hipLaunchKernelGGL(attn_fwd_kernel<T>, grid, dim3(256), 0, s, (const T*)qkv, (const T*)vT, T_, Tp, H, W, (T*)o,
+                     lse);
   return hipGetLastError();
 }
 
 template <typename T>
 hipError_t bwd_typed(const AttnBwdArgs& a, int stage, hipStream_t s) {
-  const int T_ = a.T, H = a.H, B = a.B;
+  const int T_ = a.T, H = a.H, B = a.B, W = a.window > 0 && a.window < a.T ? a.window : 0;
   const int Tp = attn_padded_len(T_);
   const int64_t ld = (int64_t)(H + 2) * D;
   constexpr bool kBf16 = sizeof(T) == 2;
@@ -1095,19 +1133,19 @@ hipError_t bwd_typed(const AttnBwdArgs& a, int stage, hipStream_t s) {
   } else if (stage == 1) {
     const dim3 grid(((T_ + 127) / 128) * H * B);
     if constexpr (kBf16)
-      hipLaunchKernelGGL(attn_dq_bf16_kernel<kDqStages>, grid, dim3(256), 0, s, (const bf16*)a.qkv, (const bf16*)a.dout, a.lse,
-                         a.delta, T_, H, (bf16*)a.dqkv);
+      hipLaunchKernelGGL(attn_dq_bf16_kernel<kDqStages>, grid, dim3(256), 0, s, (const bf16*)a.qkv,
+                         (const bf16*)a.dout, a.lse, a.delta, T_, H, W, (bf16*)a.dqkv);
     else
       hipLaunchKernelGGL(attn_dq_kernel<T>, grid, dim3(256), 0, s, (const T*)a.qkv, (const T*)a.kT,
-                         (const T*)a.dout, a.lse, a.delta, T_, Tp, H, (T*)a.dqkv);
+                         (const T*)a.dout, a.lse, a.delta, T_, Tp, H, W, (T*)a.dqkv);
   } else {
     const dim3 grid(((T_ + 127) / 128) * B);
     if constexpr (kBf16)
       hipLaunchKernelGGL(attn_dkv_bf16_kernel, grid, dim3(256), 0, s, (const bf16*)a.qkv, (const bf16*)a.dout,
-                         a.lse, a.delta, T_, H, (bf16*)a.dqkv);
+                         a.lse, a.delta, T_, H, W, (bf16*)a.dqkv);
     else
       hipLaunchKernelGGL(attn_dkv_kernel<T>, grid, dim3(256), 0, s, (const T*)a.qkv, (const T*)a.qT,
-                         (const T*)a.dout, (const T*)a.doT, a.lse, a.delta, T_, Tp, H, (T*)a.dqkv);
+                         (const T*)a.dout, (const T*)a.doT, a.lse, a.delta, T_, Tp, H, W, (T*)a.dqkv);
   }
   return hipGetLastError();
 }
@@ -1116,10 +1154,11 @@ hipError_t bwd_typed(const AttnBwdArgs& a, int stage, hipStream_t s) {
 
 int attn_padded_len(int T) { return (T + 63) / 64 * 64; }
 
-hipError_t launch_attn_fwd(int dtype, const void* qkv, int B, int T, int H, void* o, float* lse, void* vT, int stage,
-                           hipStream_t s) {
-  return dtype == 1 ? fwd_typed<bf16>(qkv, B, T, H, o, lse, vT, stage, s)
-                    : fwd_typed<float>(qkv, B, T, H, o, lse, vT, stage, s);
+hipError_t launch_attn_fwd(int dtype, const void* qkv, int B, int T, int H, int window, void* o, float* lse, void* vT,
+                           int stage, hipStream_t s) {
+  const int W = window > 0 && window < T ? window : 0;
+  return dtype == 1 ? fwd_typed<bf16>(qkv, B, T, H, W, o, lse, vT, stage, s)
+                    : fwd_typed<float>(qkv, B, T, H, W, o, lse, vT, stage, s);
 }
 
 hipError_t launch_attn_bwd(int dtype, const AttnBwdArgs& a, int stage, hipStream_t s) {

@@ -113,6 +113,14 @@ int dw_splits(int M, int N, int K) {
   return best;
 }
 
+// Sliding window of layer l (0 = full causal prefix): the pattern repeats over
+// the layers, 'S' selects window_short, and the last layer is always full.
+int layer_window(const gpt_config& c, int l) {
+  const int n = (int)strnlen(c.window_pattern, sizeof(c.window_pattern));
+  if (n == 0 || c.window_short <= 0 || l == c.n_layer - 1) return 0;
+  return c.window_pattern[l % n] == 'S' ? c.window_short : 0;
+}
+
 Layout plan(const gpt_config& c, int maxB, int maxT) {
   Layout L{};
   Planner p;
@@ -302,6 +310,8 @@ gpt_status gpt_config_from_depth(int32_t depth, int32_t dtype, gpt_config* out) 
   c.logit_softcap = 15.f;
   c.norm_eps = 1.1920928955078125e-07f;  // 2^-23
   c.dtype = dtype;
+  c.window_short = 0;
+  std::memset(c.window_pattern, 0, sizeof(c.window_pattern));
   *out = c;
   return GPT_OK;
 }
@@ -321,6 +331,19 @@ gpt_status gpt_config_validate(const gpt_config* c) {
     return fail(GPT_E_UNSUPPORTED, "vocab_size must be a multiple of 256 and <= 65536");
   if (!(c->logit_softcap > 0.f) || !(c->norm_eps > 0.f) || !(c->rope_theta > 0.f))
     return fail(GPT_E_INVALID_ARG, "rope_theta, logit_softcap and norm_eps must be positive");
+  bool nul = false, any_short = false;
+  for (int i = 0; i < (int)sizeof(c->window_pattern); ++i) {
+    const char ch = c->window_pattern[i];
+    if (ch == 0) {
+      nul = true;
+      break;
+    }
+    if (ch != 'S' && ch != 'L') return fail(GPT_E_INVALID_ARG, "window_pattern may hold only 'S' and 'L'");
+    any_short |= ch == 'S';
+  }
+  if (!nul) return fail(GPT_E_INVALID_ARG, "window_pattern must be NUL-terminated within 8 bytes");
+  if (any_short && c->window_short < 1) return fail(GPT_E_INVALID_ARG, "window_short must be >= 1 for 'S' layers");
+  if (c->window_short < 0) return fail(GPT_E_INVALID_ARG, "window_short must be >= 0");
   return GPT_OK;
 }
 
@@ -487,9 +510,10 @@ gpt_status gpt_forward_loss(gpt_model* m, const int32_t* idx, const int32_t* tar
     RUN(K_ROPE_QKNORM, return gk::launch_rope_qknorm(dt, m->ws + L.qkv[l], B, T, H, c.norm_eps,
                                                      wsp<float>(m, L.rope_cos), wsp<float>(m, L.rope_sin),
                                                      wsp<float>(m, L.rstd_qk[l]), stream););
-    RUN(K_ATTN_FWD_PREP, return gk::launch_attn_fwd(dt, m->ws + L.qkv[l], B, T, H, m->ws + L.o[l],
+    const int win = layer_window(c, l);
+    RUN(K_ATTN_FWD_PREP, return gk::launch_attn_fwd(dt, m->ws + L.qkv[l], B, T, H, win, m->ws + L.o[l],
                                                     wsp<float>(m, L.lse[l]), m->ws + L.vT, 0, stream););
-    RUN(K_ATTN_FWD, return gk::launch_attn_fwd(dt, m->ws + L.qkv[l], B, T, H, m->ws + L.o[l],
+    RUN(K_ATTN_FWD, return gk::launch_attn_fwd(dt, m->ws + L.qkv[l], B, T, H, win, m->ws + L.o[l],
                                                wsp<float>(m, L.lse[l]), m->ws + L.vT, 1, stream););
     RUN(K_GEMM_O, {
       gk::GemmArgs a;
@@ -627,6 +651,7 @@ gpt_status gpt_backward(gpt_model* m, float dloss, int32_t accumulate, void* str
     ab.dout = m->ws + L.dout;
     ab.lse = wsp<float>(m, L.lse[l]);
     ab.B = B; ab.T = T; ab.H = H;
+    ab.window = layer_window(m->cfg, l);
     ab.delta = wsp<float>(m, L.delta);
     ab.qT = m->ws + L.qT;
     ab.kT = m->ws + L.kT;

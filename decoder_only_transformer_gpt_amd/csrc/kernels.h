@@ -64,14 +64,17 @@ hipError_t launch_rope_qknorm_bwd(int dtype, void* dqkv, const void* qkv, const 
 int attn_padded_len(int T);
 // vT: scratch of B * 128 * Tp elements. Stage 0 writes vT (the V transpose),
 // stage 1 runs the attention kernel; they are separate so each can be timed.
-hipError_t launch_attn_fwd(int dtype, const void* qkv, int B, int T, int H, void* o, float* lse, void* vT, int stage,
-                           hipStream_t s);
+// window: sliding-window length (keys u with 0 <= t - u < window); 0 or >= T
+// means the full causal prefix.
+hipError_t launch_attn_fwd(int dtype, const void* qkv, int B, int T, int H, int window, void* o, float* lse, void* vT,
+                           int stage, hipStream_t s);
 struct AttnBwdArgs {
   const void* qkv;   // [N, (H+2)*128] normalised q, k and v
   const void* o;     // [N, H*128]
   const void* dout;  // [N, H*128]
   const float* lse;  // [B, H, T], base 2: lse * log2(e)
   int B, T, H;
+  int window = 0;    // sliding-window length; 0 (or >= T) = full causal prefix
   float* delta;      // [B, H, T] scratch
   void* qT;          // [B, H, 128, Tp] scratch
   void* kT;          // [B, 1, 128, Tp] scratch

@@ -26,6 +26,8 @@ class Workload:
     batch: int
     dtype: str          # "f32" | "bf16"
     tokens: str         # "uniform" | "zipf"
+    window_pattern: str = ""   # sliding-window layer pattern, e.g. "SSSL"; "" = all full
+    window_short: int = 0
 
     def config(self) -> _lib.gpt_config:
         dt = _lib.GPT_BF16 if self.dtype == "bf16" else _lib.GPT_F32
@@ -35,6 +37,8 @@ class Workload:
         c.mlp_dim = self.mlp_dim
         c.vocab_size = self.vocab_size
         c.max_seq_len = max(self.seq_len, 2048)
+        c.window_pattern = self.window_pattern.encode()
+        c.window_short = self.window_short
         return c
 
 
@@ -43,4 +47,8 @@ WORKLOADS = {
     "d4": Workload("d4", 4, 256, 1024, 65536, 512, 4, "bf16", "uniform"),
     "d12": Workload("d12", 12, 768, 3072, 65536, 2048, 16, "bf16", "zipf"),
     "d20": Workload("d20", 20, 1280, 5120, 65536, 2048, 32, "bf16", "zipf"),
+    # d20 with the pages' sliding-window pattern: SSSL, short windows of 1,024
+    # tokens, the last layer full (aethryn.com, section "A Llama-class
+    # transformer with ten modern departures")
+    "d20-sssl": Workload("d20-sssl", 20, 1280, 5120, 65536, 2048, 32, "bf16", "zipf", "SSSL", 1024),
 }

@@ -77,6 +77,15 @@ typedef struct gpt_config {
   float logit_softcap;  /* 15 */
   float norm_eps;       /* 2^-23 */
   int32_t dtype;        /* GPT_F32 or GPT_BF16 */
+  /* Sliding-window attention (aethryn.com "Nanochat: full-stack LLM training
+   * in 8,000 lines for $72", section "A Llama-class transformer with ten
+   * modern departures": the "SSSL" pattern, three short-window layers then one
+   * full-context layer, the final layer always full). Layer l uses
+   * window_pattern[l % strlen(window_pattern)]: 'S' admits key u for query t
+   * iff 0 <= t - u < window_short, 'L' the full causal prefix. The last layer
+   * is always full; "" makes every layer full (the default). */
+  int32_t window_short;     /* W for 'S' layers; >= 1 when the pattern holds an 'S' */
+  char window_pattern[8];   /* NUL-terminated, characters 'S' and 'L' only */
 } gpt_config;
 
 /* One parameter tensor inside the flat parameter (and gradient) buffer. */
@@ -96,7 +105,8 @@ const char* gpt_status_string(gpt_status s);
 const char* gpt_last_error_message(void);
 
 /* Shapes from the depth dial: C = 64*depth, H = C/128, n_kv_head = 1, D = 128,
- * F = 4C, V = 65536, max_seq_len = 2048, theta = 1e4, softcap 15, eps = 2^-23.
+ * F = 4C, V = 65536, max_seq_len = 2048, theta = 1e4, softcap 15, eps = 2^-23,
+ * every layer full causal attention (window_short 0, window_pattern "").
  * Host only. GPT_E_INVALID_ARG for depth < 2 (C must hold one 128-wide head
  * per 128 columns) or a null `out`. */
 gpt_status gpt_config_from_depth(int32_t depth, int32_t dtype, gpt_config* out);

@@ -127,3 +127,20 @@ def test_kernel_tags():
     names = _lib.gpt_kernel_tag_names()
     assert "gemm_lm_head_softcap" in names and "attn_fwd" in names and "embed_bwd" in names
     assert len(names) == len(set(names))
+
+
+def test_window_pattern_validation():
+    """Sliding-window fields: 'S'/'L' only, NUL-terminated, W >= 1 when an 'S' is present."""
+    c = _lib.gpt_config_from_depth(4)
+    assert c.window_short == 0 and c.window_pattern == b""
+    c.window_pattern = b"SSSL"
+    assert _lib.gpt_config_validate(c) == _lib.GPT_E_INVALID_ARG   # no window length
+    c.window_short = 1024
+    assert _lib.gpt_config_validate(c) == _lib.GPT_OK
+    c.window_pattern = b"SXSL"
+    assert _lib.gpt_config_validate(c) == _lib.GPT_E_INVALID_ARG
+    c.window_pattern = b"LLLLLLLL"   # fills all 8 bytes: no terminator
+    assert _lib.gpt_config_validate(c) == _lib.GPT_E_INVALID_ARG
+    c.window_pattern = b"L"
+    c.window_short = 0
+    assert _lib.gpt_config_validate(c) == _lib.GPT_OK

@@ -153,3 +153,65 @@ def test_d20_full_batch_sampled_rows():
               f"max abs per-position {err.max():.3e}")
         assert rel <= 5e-3
         assert np.median(err / r) <= 5e-3
+
+
+# ------------------------------------------------- sliding-window layers ---
+
+def with_windows(c, pattern: str, short: int):
+    c.window_pattern = pattern.encode()
+    c.window_short = short
+    return c
+
+
+def test_tiny_fp32_sliding_window_ragged():
+    """fp32: layer 0 with a 16-token window, layer 1 (the last) full; ragged T."""
+    U.require_gpu()
+    c = with_windows(tiny_cfg(T=100), "S", 16)
+    case = U.Case(c, B=2, T=77, law="uniform", wseed=7, tseed=8)
+    U.log("case tiny fp32 B=2 T=77 window S/16")
+    gpu = U.run_gpu(case)
+    assert gpu["status"] == _lib.GPT_OK
+    loss, rows, G = O.step(U.oracle_cfg(case.cfg), case.oracle_params(), case.idx, case.tgt)
+    np.testing.assert_allclose(gpu["row_loss"], rows.reshape(-1), rtol=2e-5)
+    check_fp32(case, gpu, loss, G, "tiny-window")
+
+
+@pytest.mark.parametrize("tile", [0, 3])
+def test_bf16_sssl_window_ragged(tile):
+    """bf16 d4 with the SSSL pattern, a window that is not a multiple of the
+    64-row tiles, ragged T and Zipf ids."""
+    U.require_gpu()
+    c = with_windows(d4_cfg(), "SSSL", 100)
+    case = U.Case(c, B=3, T=333, law="zipf", wseed=9, tseed=10)
+    U.log(f"case d4 bf16 B=3 T=333 SSSL/100 gemm tile {tile}")
+    gpu = U.run_gpu(case, tile=tile)
+    assert gpu["status"] == _lib.GPT_OK
+    loss, rows, G = O.step(U.oracle_cfg(case.cfg), case.oracle_params(), case.idx, case.tgt)
+    check_bf16(case, gpu, loss, G, "d4-sssl")
+
+
+def test_bf16_window_changes_result_and_full_window_does_not():
+    """A window as long as the sequence is the full causal prefix (bitwise); a
+    shorter one changes every windowed layer's output."""
+    torch = U.require_gpu()
+    base = U.Case(d4_cfg(), B=2, T=256, law="uniform", wseed=11, tseed=12)
+    full = U.run_gpu(base)
+    longw = U.Case(with_windows(d4_cfg(), "SSSL", 256), B=2, T=256, law="uniform", wseed=11, tseed=12)
+    g_long = U.run_gpu(longw)
+    assert g_long["loss"] == full["loss"]
+    np.testing.assert_array_equal(g_long["grads"], full["grads"])
+    short = U.Case(with_windows(d4_cfg(), "SSSL", 64), B=2, T=256, law="uniform", wseed=11, tseed=12)
+    g_short = U.run_gpu(short)
+    assert g_short["loss"] != full["loss"]
+
+
+@pytest.mark.timeout(900)
+def test_d20_sssl_one_row():
+    """The pages' pattern at d20: SSSL with 1,024-token short windows, T = 2048."""
+    U.require_gpu()
+    c = with_windows(_lib.gpt_config_from_depth(20, _lib.GPT_BF16), "SSSL", 1024)
+    case = U.Case(c, B=1, T=2048, law="zipf")
+    U.log("case d20 bf16 B=1 T=2048 zipf SSSL/1024")
+    gpu = U.run_gpu(case)
+    loss, rows, G = O.step(U.oracle_cfg(case.cfg), case.oracle_params(), case.idx, case.tgt)
+    check_bf16(case, gpu, loss, G, "d20-sssl-B1")
