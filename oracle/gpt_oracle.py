@@ -38,6 +38,9 @@ Readings where the pages are silent (each also fixed in the HIP path):
   (the query itself and the W-1 tokens before it); the pages do not say
   whether the window counts the query token.
 * Loss is the mean over all B*T positions; targets are given explicitly.
+* FP8 matmuls (optional, cfg["fp8"]): readings listed with the e4m3
+  functions below. Quantisation decisions are taken in fp32, as the kernels
+  take them; everything else stays float64.
 
 Parity pins: every function here is pinned by a test in ``tests/`` against a
 closed form, an invariant, a library routine or finite differences; none is
@@ -234,6 +237,85 @@ def logsumexp(z: np.ndarray) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
+# FP8 (OCP e4m3) matmuls
+# ---------------------------------------------------------------------------
+# [P3] repo-explainer.com, section "The Engine Room: Muon and FP8": training
+# with a small FP8 implementation; [P4] item "2. Pretrain": FP8 matmuls are
+# optional. The pages give no recipe, so these readings are fixed here:
+# * format e4m3 in the OCP form (no infinities, NaN = 0x7f/0xff, largest
+#   finite 448, subnormals down to 2**-9) for both operands of every
+#   QKV / O / MLP matmul, in the forward pass and in both backward products
+#   (the output gradient is quantised too);
+# * one scale per tensor from its current absolute maximum,
+#   s = 448 / amax (s = 1 for an all-zero tensor);
+# * code = round-to-nearest-even of x * s to the e4m3 grid, saturating at
+#   +-448; the scale and the product are taken in fp32, the precision in which
+#   the quantised code is decided;
+# * the matmul of two quantised tensors is the exact product of the
+#   dequantised values q / s (float64 here); the LM head and attention stay
+#   unquantised;
+# * the backward treats quantisation as the identity (straight through):
+#   dX = Q(dY) Q(W), dW = Q(dY)^T Q(X), with Q(X), Q(W) the forward's codes.
+
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """Value of each e4m3 byte: sign bit 7, exponent bits 6..3 with bias 7,
+    mantissa bits 2..0; exponent 0 is subnormal (m/8 * 2**-6); 0x7f and 0xff
+    are NaN."""
+    c = np.asarray(codes, dtype=np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((c & 0x7F) == 0x7F, np.nan, mag)
+    return sign * mag
+
+
+def e4m3_encode(y: np.ndarray) -> np.ndarray:
+    """Nearest e4m3 code of each value (ties to the even code, i.e. the even
+    mantissa), after clamping the magnitude to 448. NaN maps to 0x7f."""
+    y = np.asarray(y, dtype=np.float64)
+    grid = e4m3_decode(np.arange(0x7F))          # codes 0..126: 0 .. 448, increasing
+    a = np.minimum(np.abs(y), E4M3_MAX)
+    a = np.where(np.isnan(a), 0.0, a)
+    hi = np.clip(np.searchsorted(grid, a, side="left"), 0, 0x7E)
+    lo = np.maximum(hi - 1, 0)
+    dlo, dhi = a - grid[lo], grid[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo)
+    code = np.where(a == grid[hi], hi, code)
+    code = code | np.where(np.signbit(y), 0x80, 0)
+    code = np.where(np.isnan(y), 0x7F, code)
+    return code.astype(np.uint8)
+
+
+def fp8_quantize(x: np.ndarray):
+    """Per-tensor current scaling: returns (codes, s) with s = 448 / max|x| in
+    fp32 and codes = e4m3(fp32(x) * s)."""
+    x32 = np.asarray(x, dtype=np.float32)
+    amax = np.float32(np.max(np.abs(x32))) if x32.size else np.float32(0.0)
+    s = np.float32(E4M3_MAX) / amax if amax > 0 else np.float32(1.0)
+    return e4m3_encode(x32 * s), s
+
+
+def fp8_dequantize(codes: np.ndarray, s) -> np.ndarray:
+    return e4m3_decode(codes) / np.float64(s)
+
+
+def fp8_round_trip(x: np.ndarray) -> np.ndarray:
+    """The value a quantised matmul operand stands for: Q(x) / s."""
+    return fp8_dequantize(*fp8_quantize(x))
+
+
+def mm_operand(cfg: dict, t: np.ndarray) -> np.ndarray:
+    """A QKV / O / MLP matmul operand as the config's precision sees it: the
+    tensor itself, or its e4m3 round trip when cfg["fp8"] is set."""
+    return fp8_round_trip(t) if cfg.get("fp8", False) else t
+
+
+# ---------------------------------------------------------------------------
 # The step
 # ---------------------------------------------------------------------------
 
@@ -263,18 +345,18 @@ def forward(cfg: dict, params: dict, idx: np.ndarray, targets: np.ndarray, row_c
     cache = dict(r0=r0, layers=[], cos=cos, sin=sin)
     for l in range(cfg["n_layer"]):
         h1, r1 = rmsnorm(x, eps)
-        qkv = h1 @ W[f"h{l}.w_qkv"].T
+        qkv = mm_operand(cfg, h1) @ mm_operand(cfg, W[f"h{l}.w_qkv"]).T
         q, k, v = _split_qkv(qkv, H, 1, D)
         qr, kr = rope(q, cos, sin), rope(k, cos, sin)
         qn, rq = rmsnorm(qr, eps)
         kn, rk = rmsnorm(kr, eps)
         o, lse = causal_mqa_attention(qn, kn[:, :, 0], v[:, :, 0], layer_window(cfg, l))
         o2 = o.reshape(B, T, H * D)
-        x = x + o2 @ W[f"h{l}.w_o"].T
+        x = x + mm_operand(cfg, o2) @ mm_operand(cfg, W[f"h{l}.w_o"]).T
         h2, r2 = rmsnorm(x, eps)
-        u = h2 @ W[f"h{l}.w_1"].T
+        u = mm_operand(cfg, h2) @ mm_operand(cfg, W[f"h{l}.w_1"]).T
         a = np.maximum(u, 0.0) ** 2
-        x = x + a @ W[f"h{l}.w_2"].T
+        x = x + mm_operand(cfg, a) @ mm_operand(cfg, W[f"h{l}.w_2"]).T
         cache["layers"].append(dict(h1=h1, r1=r1, qn=qn, rq=rq, kn=kn, rk=rk, v=v,
                                     o=o, lse=lse, h2=h2, r2=r2, u=u, a=a))
     hf, rf = rmsnorm(x, eps)
@@ -323,16 +405,21 @@ def backward(cfg: dict, params: dict, idx: np.ndarray, targets: np.ndarray, cach
     for l in reversed(range(cfg["n_layer"])):
         L = cache["layers"][l]
         # MLP: x_out = x_mid + relu(u)^2 W2^T, u = rmsnorm(x_mid) W1^T
-        G[f"h{l}.w_2"] += dx.reshape(N, C).T @ L["a"].reshape(N, -1)
-        da = dx @ W[f"h{l}.w_2"]
+        # (for FP8 models every product takes the e4m3 round trips of its
+        # operands; the quantisation itself is passed straight through)
+        dy = mm_operand(cfg, dx)
+        G[f"h{l}.w_2"] += dy.reshape(N, C).T @ mm_operand(cfg, L["a"]).reshape(N, -1)
+        da = dy @ mm_operand(cfg, W[f"h{l}.w_2"])
         du = da * 2.0 * np.maximum(L["u"], 0.0)
-        G[f"h{l}.w_1"] += du.reshape(N, -1).T @ L["h2"].reshape(N, C)
-        dh2 = du @ W[f"h{l}.w_1"]
+        duq = mm_operand(cfg, du)
+        G[f"h{l}.w_1"] += duq.reshape(N, -1).T @ mm_operand(cfg, L["h2"]).reshape(N, C)
+        dh2 = duq @ mm_operand(cfg, W[f"h{l}.w_1"])
         dx = dx + rmsnorm_bwd(dh2, L["h2"], L["r2"])
         # attention: x_mid = x_in + o W_o^T
         o2 = L["o"].reshape(B, T, H * D)
-        G[f"h{l}.w_o"] += dx.reshape(N, C).T @ o2.reshape(N, -1)
-        do = (dx @ W[f"h{l}.w_o"]).reshape(B, T, H, D)
+        dy = mm_operand(cfg, dx)
+        G[f"h{l}.w_o"] += dy.reshape(N, C).T @ mm_operand(cfg, o2).reshape(N, -1)
+        do = (dy @ mm_operand(cfg, W[f"h{l}.w_o"])).reshape(B, T, H, D)
         dqn, dkn, dv = causal_mqa_attention_bwd(do, L["qn"], L["kn"][:, :, 0], L["v"][:, :, 0],
                                                 layer_window(cfg, l))
         dqr = rmsnorm_bwd(dqn, L["qn"], L["rq"])
@@ -341,8 +428,9 @@ def backward(cfg: dict, params: dict, idx: np.ndarray, targets: np.ndarray, cach
         dk = rope_bwd(dkr, cos, sin)
         dqkv = np.concatenate([dq.reshape(B, T, H * D), dk.reshape(B, T, D),
                                dv.reshape(B, T, D)], axis=-1)
-        G[f"h{l}.w_qkv"] += dqkv.reshape(N, -1).T @ L["h1"].reshape(N, C)
-        dh1 = dqkv @ W[f"h{l}.w_qkv"]
+        dqkv = mm_operand(cfg, dqkv)
+        G[f"h{l}.w_qkv"] += dqkv.reshape(N, -1).T @ mm_operand(cfg, L["h1"]).reshape(N, C)
+        dh1 = dqkv @ mm_operand(cfg, W[f"h{l}.w_qkv"])
         dx = dx + rmsnorm_bwd(dh1, L["h1"], L["r1"])
 
     # embedding: x0 = rmsnorm(wte[idx]); dwte[v] = sum over positions with idx == v

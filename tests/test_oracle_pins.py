@@ -315,9 +315,33 @@ def _torch_step(cfg, P, idx, tg):
     def norm(x):
         return F.rms_norm(x, (x.shape[-1],), eps=eps)
 
+    def fake_quant(t):
+        # per-tensor e4m3 round trip through torch's own float8 conversion
+        t32 = t.detach().to(torch.float32)
+        amax = t32.abs().max()
+        s = torch.tensor(448.0, dtype=torch.float32) / amax if amax > 0 else torch.tensor(1.0)
+        q = (t32 * s).clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
+        return q.to(torch.float64) / s.to(torch.float64)
+
+    class QLinear(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, x, w):
+            xq, wq = fake_quant(x), fake_quant(w)
+            ctx.save_for_backward(xq, wq)
+            return xq @ wq.T
+
+        @staticmethod
+        def backward(ctx, dy):
+            xq, wq = ctx.saved_tensors
+            dyq = fake_quant(dy)
+            return dyq @ wq, dyq.reshape(-1, dyq.shape[-1]).T @ xq.reshape(-1, xq.shape[-1])
+
+    def lin(x, w):
+        return QLinear.apply(x, w) if cfg.get("fp8", False) else x @ w.T
+
     x = norm(W["wte"][idx_t])
     for l in range(cfg["n_layer"]):
-        qkv = norm(x) @ W[f"h{l}.w_qkv"].T
+        qkv = lin(norm(x), W[f"h{l}.w_qkv"])
         q = qkv[..., :H * D].view(B, T, H, D).transpose(1, 2)
         k = qkv[..., H * D:(H + 1) * D].view(B, T, 1, D).transpose(1, 2)
         v = qkv[..., (H + 1) * D:].view(B, T, 1, D).transpose(1, 2)
@@ -329,8 +353,8 @@ def _torch_step(cfg, P, idx, tg):
             y = F.scaled_dot_product_attention(q, k, v, attn_mask=allowed, enable_gqa=True)
         else:
             y = F.scaled_dot_product_attention(q, k, v, is_causal=True, enable_gqa=True)
-        x = x + y.transpose(1, 2).reshape(B, T, H * D) @ W[f"h{l}.w_o"].T
-        x = x + F.relu(norm(x) @ W[f"h{l}.w_1"].T).square() @ W[f"h{l}.w_2"].T
+        x = x + lin(y.transpose(1, 2).reshape(B, T, H * D), W[f"h{l}.w_o"])
+        x = x + lin(F.relu(lin(norm(x), W[f"h{l}.w_1"])).square(), W[f"h{l}.w_2"])
     logits = norm(x) @ W["lm_head"].T
     logits = c * torch.tanh(logits / c)
     loss = F.cross_entropy(logits.view(B * T, -1), tg_t.view(-1))
@@ -471,3 +495,129 @@ def test_windowed_step_matches_torch_autograd_and_fd():
         W[ij] = old
         fd = (lp - lm) / (2 * h)
         assert abs(fd - G["h0.w_qkv"][ij]) <= 1e-6 * abs(fd) + 2e-10
+
+
+# ------------------------------------------------------------- FP8 e4m3 ---
+
+def _torch_e4m3_values():
+    import torch
+    return torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def test_e4m3_decode_matches_spec_points_and_torch():
+    """The OCP e4m3 grid: 1.0 = 0x38, largest finite 448 = 0x7e, smallest
+    subnormal 2^-9 = 0x01, smallest normal 2^-6 = 0x08, NaN at 0x7f/0xff and no
+    infinities. A wrong bias, subnormal rule or sign bit breaks one of these."""
+    pytest.importorskip("torch")
+    v = O.e4m3_decode(np.arange(256))
+    assert v[0x38] == 1.0 and v[0x7E] == 448.0 and v[0x01] == 2.0 ** -9 and v[0x08] == 2.0 ** -6
+    assert v[0x07] == 7 * 2.0 ** -9 and v[0xB8] == -1.0 and np.signbit(v[0x80])
+    assert np.isnan(v[0x7F]) and np.isnan(v[0xFF]) and np.isfinite(v).sum() == 254
+    assert np.all(np.diff(v[:0x7F]) > 0)
+    np.testing.assert_array_equal(v, _torch_e4m3_values())
+
+
+def test_e4m3_encode_is_round_to_nearest_even_like_torch():
+    """Encoding agrees with torch's float8_e4m3fn conversion (round to nearest,
+    ties to even) on random fp32 values over the whole range, on every exact
+    midpoint between neighbouring grid values (the tie cases) and in the
+    subnormal range."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(40)
+    grid = O.e4m3_decode(np.arange(0x7F))
+    mids = (grid[:-1] + grid[1:]) / 2
+    vals = np.concatenate([
+        rng.uniform(-448, 448, 20000),
+        np.exp2(rng.uniform(-12, 8.8, 20000)) * rng.choice([-1, 1], 20000),
+        mids, -mids, grid, -grid, np.nextafter(mids, 0), np.nextafter(mids, 1000)]).astype(np.float32)
+    ours = O.e4m3_encode(vals)
+    ref = torch.from_numpy(vals).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(ours, ref)
+    # ties really go to the even mantissa: midpoint of 1.0 (0x38) and 1.125 (0x39)
+    assert O.e4m3_encode(np.float32(1.0625)) == 0x38 and O.e4m3_encode(np.float32(1.1875)) == 0x3A
+
+
+def test_e4m3_encode_saturates():
+    """Magnitudes past the largest finite value clamp to +-448 (0x7e / 0xfe)
+    rather than overflowing to NaN; zero keeps its sign; NaN stays NaN."""
+    y = np.array([448.0, 449.0, 464.0, 465.0, 1e6, np.inf, -500.0, -np.inf, 0.0, -0.0, np.nan], np.float32)
+    assert O.e4m3_encode(y).tolist() == [0x7E, 0x7E, 0x7E, 0x7E, 0x7E, 0x7E, 0xFE, 0xFE, 0x00, 0x80, 0x7F]
+
+
+def test_fp8_quantize_scale_zero_tensor_and_amax_element():
+    """s = 448 / amax in fp32; the largest element lands on +-448; an all-zero
+    tensor keeps scale 1 and all-zero codes."""
+    rng = np.random.default_rng(41)
+    x = rng.standard_normal((7, 13)) * 3.0
+    x[4, 5] = -9.5
+    q, s = O.fp8_quantize(x)
+    assert s.dtype == np.float32 and s == np.float32(448.0) / np.float32(9.5)
+    assert q[4, 5] == 0xFE
+    q0, s0 = O.fp8_quantize(np.zeros((3, 4)))
+    assert s0 == 1.0 and not q0.any()
+
+
+def test_fp8_round_trip_error_bound():
+    """|Q(x)/s - x| <= 2^-4 |x| (three mantissa bits) or, in the subnormal
+    range, half a subnormal step 2^-10 / s, plus the fp32 cast of x."""
+    rng = np.random.default_rng(42)
+    for scale in (1e-3, 1.0, 250.0):
+        x = rng.standard_normal(50000) * scale * np.exp2(rng.uniform(-8, 0, 50000))
+        r = O.fp8_round_trip(x)
+        _, s = O.fp8_quantize(x)
+        bound = np.maximum(2.0 ** -4 * np.abs(x), 2.0 ** -10 / np.float64(s)) + 2.0 ** -23 * np.abs(x)
+        assert np.all(np.abs(r - x) <= bound)
+        assert np.max(np.abs(r - x) / np.maximum(np.abs(x), 1e-300)) > 2.0 ** -6   # it does quantise
+
+
+def test_fp8_round_trip_exact_on_scaled_grid():
+    """Operands that already are e4m3 values times 2^-k, with one element at
+    448 * 2^-k, get scale 2^k and pass through exactly, so an FP8 matmul of
+    them equals the float64 matmul (catches a dropped dequantisation or a
+    scale applied the wrong way)."""
+    rng = np.random.default_rng(43)
+    grid = O.e4m3_decode(np.arange(0x7F))
+    for k in (-3, 0, 5):
+        x = rng.choice(grid, (9, 16)) * rng.choice([-1.0, 1.0], (9, 16)) * 2.0 ** -k
+        x[2, 3] = 448.0 * 2.0 ** -k
+        q, s = O.fp8_quantize(x)
+        assert s == np.float32(2.0 ** k)
+        np.testing.assert_array_equal(O.fp8_round_trip(x), x)
+    cfg = dict(fp8=True)
+    w = rng.choice(grid, (5, 16)) * 2.0 ** -7
+    w[0, 0] = 448.0 * 2.0 ** -7
+    np.testing.assert_array_equal(O.mm_operand(cfg, x) @ O.mm_operand(cfg, w).T, x @ w.T)
+
+
+def test_fp8_step_matches_torch_autograd_with_float8_fake_quant():
+    """The FP8 step (every QKV / O / MLP product on per-tensor e4m3 operands,
+    output gradients quantised too, straight-through backward) against torch
+    autograd with torch's float8 conversion as the quantiser."""
+    pytest.importorskip("torch")
+    cfg = tiny_cfg(n_layer=2, n_head=2, model_dim=256, mlp_dim=1024, vocab_size=96, fp8=True)
+    P = rand_params(cfg, seed=44, std=0.05)
+    rng = np.random.default_rng(45)
+    idx = rng.integers(0, 96, (2, 19))
+    tg = rng.integers(0, 96, (2, 19))
+    loss, _, G = O.step(cfg, P, idx, tg)
+    tl, TG = _torch_step(cfg, P, idx, tg)
+    assert loss == pytest.approx(tl, rel=1e-12)
+    for name in G:
+        np.testing.assert_allclose(G[name], TG[name], rtol=1e-8, atol=1e-12, err_msg=name)
+
+
+def test_fp8_step_close_to_unquantised_step():
+    """Quantisation noise only: the FP8 step's loss and gradients stay close to
+    the unquantised step's (e4m3 keeps 3 mantissa bits), and differ from it."""
+    cfg = tiny_cfg(n_layer=2, n_head=2, model_dim=256, mlp_dim=1024, vocab_size=96)
+    P = rand_params(cfg, seed=46, std=0.05)
+    rng = np.random.default_rng(47)
+    idx = rng.integers(0, 96, (2, 33))
+    tg = rng.integers(0, 96, (2, 33))
+    l0, _, G0 = O.step(cfg, P, idx, tg)
+    l8, _, G8 = O.step(dict(cfg, fp8=True), P, idx, tg)
+    assert l8 != l0 and abs(l8 - l0) / l0 < 1e-2
+    for name in G0:
+        a, b = G0[name].ravel(), G8[name].ravel()
+        cos = a @ b / np.linalg.norm(a) / np.linalg.norm(b)
+        assert cos > 0.99, name
