@@ -249,8 +249,10 @@ def logsumexp(z: np.ndarray) -> np.ndarray:
 # * one scale per tensor from its current absolute maximum,
 #   s = 448 / amax (s = 1 for an all-zero tensor);
 # * code = round-to-nearest-even of x * s to the e4m3 grid, saturating at
-#   +-448; the scale and the product are taken in fp32, the precision in which
-#   the quantised code is decided;
+#   +-448. The operand is quantised as the bf16 compute dtype holds it ([P2]
+#   "Precision / dtype": bf16 compute), so x is first rounded to bf16 (as
+#   every bf16 activation and gradient is stored); amax, the scale and the
+#   product are then taken in fp32, the precision in which the code is decided;
 # * the matmul of two quantised tensors is the exact product of the
 #   dequantised values q / s (float64 here); the LM head and attention stay
 #   unquantised;
@@ -291,10 +293,18 @@ def e4m3_encode(y: np.ndarray) -> np.ndarray:
     return code.astype(np.uint8)
 
 
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """x rounded to bf16 (8 significant bits), round to nearest, ties to even,
+    straight from float64: x = m * 2**e with 0.5 <= |m| < 1, keep rint(m * 2**8)."""
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)
+    return np.ldexp(np.rint(m * 256.0), e - 8)
+
+
 def fp8_quantize(x: np.ndarray):
-    """Per-tensor current scaling: returns (codes, s) with s = 448 / max|x| in
-    fp32 and codes = e4m3(fp32(x) * s)."""
-    x32 = np.asarray(x, dtype=np.float32)
+    """Per-tensor current scaling of the bf16 operand: returns (codes, s) with
+    s = 448 / max|bf16(x)| in fp32 and codes = e4m3(bf16(x) * s)."""
+    x32 = round_bf16(x).astype(np.float32)
     amax = np.float32(np.max(np.abs(x32))) if x32.size else np.float32(0.0)
     s = np.float32(E4M3_MAX) / amax if amax > 0 else np.float32(1.0)
     return e4m3_encode(x32 * s), s

@@ -316,8 +316,9 @@ def _torch_step(cfg, P, idx, tg):
         return F.rms_norm(x, (x.shape[-1],), eps=eps)
 
     def fake_quant(t):
-        # per-tensor e4m3 round trip through torch's own float8 conversion
-        t32 = t.detach().to(torch.float32)
+        # per-tensor e4m3 round trip of the bf16 operand through torch's own
+        # bfloat16 and float8 conversions
+        t32 = t.detach().to(torch.bfloat16).to(torch.float32)
         amax = t32.abs().max()
         s = torch.tensor(448.0, dtype=torch.float32) / amax if amax > 0 else torch.tensor(1.0)
         q = (t32 * s).clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
@@ -557,15 +558,29 @@ def test_fp8_quantize_scale_zero_tensor_and_amax_element():
     assert s0 == 1.0 and not q0.any()
 
 
+def test_round_bf16_matches_torch_and_ties():
+    """bf16 rounding agrees with torch's float32 -> bfloat16 conversion on
+    fp32 inputs (including exact ties, which go to the even mantissa)."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(48)
+    x = np.concatenate([rng.standard_normal(20000) * np.exp2(rng.uniform(-20, 20, 20000)),
+                        [1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, -(1 + 2.0 ** -8), 0.0]]).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(O.round_bf16(x.astype(np.float64)), ref)
+    assert O.round_bf16(1 + 2.0 ** -8) == 1.0 and O.round_bf16(1 + 3 * 2.0 ** -8) == 1 + 2.0 ** -6
+
+
 def test_fp8_round_trip_error_bound():
     """|Q(x)/s - x| <= 2^-4 |x| (three mantissa bits) or, in the subnormal
-    range, half a subnormal step 2^-10 / s, plus the fp32 cast of x."""
+    range, half a subnormal step 2^-10 / s, plus the bf16 rounding of x
+    (2^-9 |x|) and its fp32 product."""
     rng = np.random.default_rng(42)
     for scale in (1e-3, 1.0, 250.0):
         x = rng.standard_normal(50000) * scale * np.exp2(rng.uniform(-8, 0, 50000))
         r = O.fp8_round_trip(x)
         _, s = O.fp8_quantize(x)
-        bound = np.maximum(2.0 ** -4 * np.abs(x), 2.0 ** -10 / np.float64(s)) + 2.0 ** -23 * np.abs(x)
+        bound = (np.maximum(2.0 ** -4 * np.abs(x), 2.0 ** -10 / np.float64(s)) * (1 + 2.0 ** -8)
+                 + 2.0 ** -9 * np.abs(x))
         assert np.all(np.abs(r - x) <= bound)
         assert np.max(np.abs(r - x) / np.maximum(np.abs(x), 1e-300)) > 2.0 ** -6   # it does quantise
 
