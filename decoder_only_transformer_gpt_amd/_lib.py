@@ -22,6 +22,7 @@ GPT_E_HIP = -5
 GPT_E_DEVICE = -6
 GPT_F32 = 0
 GPT_BF16 = 1
+GPT_FP8_E4M3 = 2
 GPT_OPT_GEMM_TILE = 1
 
 
@@ -77,6 +78,10 @@ _SIGS = {
     "gpt_set_option": (ctypes.c_int32, [_P, ctypes.c_int32, ctypes.c_int32]),
     "gpt_debug_buffer": (ctypes.c_int32, [_P, ctypes.c_char_p, ctypes.c_int32, ctypes.POINTER(_P),
                                           ctypes.POINTER(ctypes.c_size_t)]),
+    "gpt_fp8_quantize": (ctypes.c_int32, [_P, ctypes.c_int64, ctypes.c_int64, _P, _P, ctypes.c_int64, _P, _P]),
+    "gpt_fp8_matmul": (ctypes.c_int32, [_P, ctypes.c_int64, _P, _P, ctypes.c_int64, _P, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int64, ctypes.c_int32,
+                                        ctypes.c_int32, _P, _P]),
 }
 
 
@@ -197,3 +202,13 @@ def gpt_debug_buffer(h, name: str, layer: int = 0):
     p, b = ctypes.c_void_p(), ctypes.c_size_t(0)
     _check(lib().gpt_debug_buffer(h, name.encode(), layer, ctypes.byref(p), ctypes.byref(b)), "gpt_debug_buffer")
     return p.value, b.value
+
+
+def gpt_fp8_quantize(x_ptr: int, rows: int, cols: int, q_ptr, qT_ptr, ldT: int, amax_ptr: int, stream: int):
+    _check(lib().gpt_fp8_quantize(x_ptr, rows, cols, q_ptr, qT_ptr, ldT, amax_ptr, stream), "gpt_fp8_quantize")
+
+
+def gpt_fp8_matmul(a_ptr, lda, amax_a_ptr, b_ptr, ldb, amax_b_ptr, M, N, K, out_dtype, out_ptr, ldo, tile=0,
+                   splits=1, partials_ptr=None, stream=0):
+    _check(lib().gpt_fp8_matmul(a_ptr, lda, amax_a_ptr, b_ptr, ldb, amax_b_ptr, M, N, K, out_dtype, out_ptr, ldo,
+                                tile, splits, partials_ptr, stream), "gpt_fp8_matmul")

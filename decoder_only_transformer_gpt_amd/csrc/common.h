@@ -122,6 +122,30 @@ DEV f32x16 mfma16(u32x4 a, u32x4 b, f32x16 c, float*) {
   return c;
 }
 
+// fp8 (OCP e4m3) x fp8 -> fp32, 32x32x64: each operand is 32 bytes per lane,
+// given as two 16-byte fragments (the k assignment is whatever the caller's
+// fragment reads make it, the same for both operands). Format code 0 selects
+// e4m3 for A and B; the E8M0 block scales are fixed at 2^0 (127).
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+DEV f32x16 mfma_fp8(u32x4 a0, u32x4 a1, u32x4 b0, u32x4 b1, f32x16 c) {
+  const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+  const i32x8 b = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3], (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// Four floats to four e4m3 bytes (a in the lowest byte), round to nearest
+// even. Finite magnitudes above 448 are not saturated by the conversion (it
+// gives NaN past 464): callers clamp first.
+DEV uint32_t pack_fp8x4(float a, float b, float c, float d) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, (int)lo, true);
+#else
+  (void)a; (void)b; (void)c; (void)d;
+  return 0u;
+#endif
+}
+
 // ------------------------------------------------- buffer loads to LDS -----
 // Buffer resource over [p, p + bytes) (raw, stride 0): loads at offsets past
 // `bytes` return zero. Made wave-uniform (SGPRs) with readfirstlane; callers

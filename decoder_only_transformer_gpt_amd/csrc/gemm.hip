@@ -484,10 +484,15 @@ struct Epilogue<T, Epi::GradF32> {
   }
 };
 
-// bf16 GEMM with both operands k-contiguous (y = x W^T and, with a
-// transposed weight copy, dx = dy W), fed by direct-to-LDS buffer loads.
+// GEMM with both operands k-contiguous (y = x W^T and, with a transposed
+// weight copy, dx = dy W; with token-major transposed copies also dW), fed by
+// direct-to-LDS buffer loads. ES is the operand element size: 2 = bf16
+// (32x32x16 MFMA), 1 = fp8 e4m3 (32x32x64 MFMA on the same byte tiles, two
+// 16-byte fragments per operand, and the accumulator scaled by
+// 1 / (s_a s_b) from the operands' amax slots before the epilogue). Split-K
+// (GradF32 only) runs slices of whole K tiles over a slice-major 1-D grid.
 //
-// K tiles are BK = 32 or 64 wide (64- or 128-byte rows) and live in NSTAGE
+// K tiles are 64- or 128-byte rows (BK elements) and live in NSTAGE
 // LDS stages; tile kt + NSTAGE - 1 is requested while tile kt is consumed. A
 // wave's buffer_load ... lds writes 1 KiB contiguous (lane L at +16L), i.e.
 // 1024/ROWB rows; each lane picks the global 16-byte chunk it fetches so that
@@ -497,17 +502,18 @@ struct Epilogue<T, Epi::GradF32> {
 // once: rows in one 256-byte bank line differ in their row offset, rows RP
 // apart in the chunk position. Rows past M read as zero (buffer record count).
 // One explicit vmcnt wait and one barrier per K tile.
-template <int BM, int BN, int NSTAGE, int OCC, Epi E, int NW = 4, int BK = 32>
+template <int BM, int BN, int NSTAGE, int OCC, Epi E, int NW = 4, int BK = 32, int ES = 2>
 __global__ __launch_bounds__(NW * 64, OCC) void gemm_nt_lds_kernel(GemmArgs args) {
-  using T = bf16;
-  constexpr int ROWB = BK * 2, CH = ROWB / 16, RP = 256 / ROWB, RPK = 1024 / ROWB;
-  constexpr int KSTEPS = BK / 16;
+  using T = bf16;  // output (epilogue) type
+  constexpr int ROWB = BK * ES, CH = ROWB / 16, RP = 256 / ROWB, RPK = 1024 / ROWB;
+  constexpr int KSTEPS = ROWB / 32;  // 16-byte fragment pairs (lane groups 0/1) per row
   constexpr int WGN = NW / 2;                              // waves along n (2 along m)
   constexpr int WM = BM / 2, WN = BN / WGN, TM = WM / 32, TN = WN / 32;
   constexpr int STAGE = (BM + BN) * ROWB;                  // bytes per stage
   constexpr int LA = BM * ROWB / 1024 / NW, LB = BN * ROWB / 1024 / NW;  // 1 KiB loads per wave per tile
   constexpr int NLOAD = LA + LB;
-  static_assert(BK == 32 || BK == 64, "K tile");
+  static_assert(ROWB == 64 || ROWB == 128, "K tile");
+  static_assert(ES == 2 || ES == 1, "bf16 or fp8 operands");
   static_assert(LA >= 1 && LB >= 1, "tile too small for the wave count");
   static_assert(NSTAGE >= 2 && NSTAGE <= 4, "two to four stage arrays");
   // one array per stage, so the compiler can tell the stages' LDS-direct
@@ -521,15 +527,21 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm_nt_lds_kernel(GemmArgs args
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
   const int wm = wave / WGN, wn = wave % WGN, g = lane >> 5, l32 = lane & 31;
   const int M = args.M, N = args.N, K = args.K;
-  const int tiles_n = (N + BN - 1) / BN;
-  int bid = blockIdx.x;
+  const int tiles_n = (N + BN - 1) / BN, tiles = ((M + BM - 1) / BM) * tiles_n;
+  // blocks are dealt round-robin to the 8 XCDs: remap so that each XCD takes
+  // a contiguous run of items (neighbouring tiles, whole split-K slices)
+  int item = blockIdx.x;
   const int nb = gridDim.x;
-  if ((nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
+  if ((nb & 7) == 0) item = (item & 7) * (nb >> 3) + (item >> 3);
+  const int split = item / tiles, bid = item % tiles;
   const int m0 = (bid / tiles_n) * BM, n0 = (bid % tiles_n) * BN;
-  const int nk = K / BK;
-  const T* Ap = reinterpret_cast<const T*>(args.A) + (int64_t)m0 * args.lda;
-  const T* Bp = reinterpret_cast<const T*>(args.B) + (int64_t)n0 * args.ldb;
-  const uint32_t lda_b = (uint32_t)(args.lda * 2), ldb_b = (uint32_t)(args.ldb * 2);
+  const int kper = ((K + args.splits - 1) / args.splits + BK - 1) / BK * BK;
+  const int kbeg = split * kper;
+  const int kend = min(K, kbeg + kper);
+  const int nk = kend > kbeg ? (kend - kbeg) / BK : 0;
+  const char* Ap = reinterpret_cast<const char*>(args.A) + ((int64_t)m0 * args.lda + kbeg) * ES;
+  const char* Bp = reinterpret_cast<const char*>(args.B) + ((int64_t)n0 * args.ldb + kbeg) * ES;
+  const uint32_t lda_b = (uint32_t)(args.lda * ES), ldb_b = (uint32_t)(args.ldb * ES);
   // record counts (bytes from the tile's first row), clamped to 1 GiB; plain
   // integer ternaries (a templated 64-bit min() would go through f64 VALU
   // math and make the resource look divergent)
@@ -555,7 +567,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm_nt_lds_kernel(GemmArgs args
 
   auto stage = [&](int q) -> char* { return q == 0 ? st0 : q == 1 ? st1 : q == 2 ? st2 : st3; };
   auto issue = [&](int kt, char* st) {
-    const int k0 = kt * BK;
+    const int k0 = kt * ROWB;  // bytes
     const __amdgpu_buffer_rsrc_t ra = uniform_rsrc(Ap + k0, rec_a);
     const __amdgpu_buffer_rsrc_t rb = uniform_rsrc(Bp + k0, rec_b);
 #pragma unroll
@@ -581,8 +593,8 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm_nt_lds_kernel(GemmArgs args
   for (int ks = 0; ks < KSTEPS; ++ks) fo[ks] = l32 * ROWB + ((ks * 2 + g) ^ swz) * 16;
 
   issue(0, st0);
-  if (NSTAGE >= 3) issue(min(1, nk - 1), st1);
-  if (NSTAGE == 4) issue(min(2, nk - 1), st2);
+  if (NSTAGE >= 3) issue(max(0, min(1, nk - 1)), st1);
+  if (NSTAGE == 4) issue(max(0, min(2, nk - 1)), st2);
   // tile kt sits in stage kt % NSTAGE; the loop is unrolled by NSTAGE so
   // every stage is a distinct, statically known LDS object
   auto tile = [&](int kt, const char* cur, char* nxt) {
@@ -604,17 +616,30 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm_nt_lds_kernel(GemmArgs args
 #pragma unroll
       for (int j = 0; j < TN; ++j) bfr[ks][j] = ld16(Bs + j * 32 * ROWB + fo[ks]);
     }
+    if constexpr (ES == 2) {
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks)
+      for (int ks = 0; ks < KSTEPS; ++ks)
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = mfma16(bfr[ks][j], af[ks][i], acc[i][j], (T*)nullptr);
-    constexpr int NR = TM + TN, NM = TM * TN, PER = NM / NR > 0 ? NM / NR : 1;
+          for (int j = 0; j < TN; ++j) acc[i][j] = mfma16(bfr[ks][j], af[ks][i], acc[i][j], (T*)nullptr);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ks += 2)
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            acc[i][j] = mfma_fp8(bfr[ks][j], bfr[ks + 1][j], af[ks][i], af[ks + 1][i], acc[i][j]);
+    }
+    // interleave: the reads of step s+1 between the MFMAs of step s (an fp8
+    // step consumes two fragment pairs)
+    constexpr int RPS = ES == 2 ? 1 : 2, MSTEPS = KSTEPS / RPS;
+    constexpr int NR = (TM + TN) * RPS, NM = TM * TN, PER = NM / NR > 0 ? NM / NR : 1;
     __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      if (ks + 1 < KSTEPS) {
+    for (int ms = 0; ms < MSTEPS; ++ms) {
+      if (ms + 1 < MSTEPS) {
 #pragma unroll
         for (int q = 0; q < NR; ++q) {
           __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);
@@ -653,7 +678,20 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm_nt_lds_kernel(GemmArgs args
   constexpr int PERST = STAGE / SLAB;  // slabs per stage
   static_assert(PERST >= 1 && (NW + PERST - 1) / PERST <= NSTAGE, "epilogue slabs must fit the stages");
   float* slab = reinterpret_cast<float*>(stage(wave / PERST) + (wave % PERST) * SLAB);
-  Epilogue<T, E>::template run<TM, TN, WN>(args, acc, slab, m0 + wm * WM, n0 + wn * WN, lane);
+  if constexpr (ES == 1) {
+    const float aa = *args.amax_a, ab = *args.amax_b;
+    const float sa = aa > 0.f ? 448.f / aa : 1.f, sb = ab > 0.f ? 448.f / ab : 1.f;
+    const float f = 1.f / (sa * sb);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] *= f;
+  }
+  GemmArgs ea = args;
+  ea.zslice = split;
+  Epilogue<T, E>::template run<TM, TN, WN>(ea, acc, slab, m0 + wm * WM, n0 + wn * WN, lane);
 }
 
 // bf16 GEMM with both operands mn-contiguous (dW = dy^T x: A = dy [K, M] and
@@ -766,8 +804,8 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm_tn_lds_kernel(GemmArgs args
   };
 
   issue(0, st0);
-  if (NSTAGE >= 3) issue(min(1, nk - 1), st1);
-  if (NSTAGE == 4) issue(min(2, nk - 1), st2);
+  if (NSTAGE >= 3) issue(max(0, min(1, nk - 1)), st1);
+  if (NSTAGE == 4) issue(max(0, min(2, nk - 1)), st2);
   auto tile = [&](int kt, const char* cur, char* nxt) {
     constexpr int YOUNG = NLOAD * (NSTAGE - 2);
     __builtin_amdgcn_s_waitcnt(((YOUNG >> 4) << 14) | (0x7 << 4) | (0xF << 8) | (YOUNG & 15));
@@ -895,11 +933,21 @@ hipError_t launch_layout(const GemmArgs& a, hipStream_t s) {
   }
 }
 
-template <int BM, int BN, int NSTAGE, int OCC, Epi E, int NW = 4, int BK = 32>
+template <int BM, int BN, int NSTAGE, int OCC, Epi E, int NW = 4, int BK = 32, int ES = 2>
 hipError_t launch_nt_lds(const GemmArgs& a, hipStream_t s) {
   if (a.K % BK != 0) return hipErrorInvalidValue;
+  const int splits = E == Epi::GradF32 ? a.splits : 1;
   const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_nt_lds_kernel<BM, BN, NSTAGE, OCC, E, NW, BK>), dim3(tiles), dim3(NW * 64), 0, s, a);
+  GemmArgs g = a;
+  g.splits = splits;
+  hipLaunchKernelGGL((gemm_nt_lds_kernel<BM, BN, NSTAGE, OCC, E, NW, BK, ES>), dim3(tiles * splits), dim3(NW * 64), 0,
+                     s, g);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || splits <= 1) return err;
+  const int64_t total4 = (int64_t)a.M * a.N / 4;
+  const int blocks = (int)std::min<int64_t>((total4 + 255) / 256, 4096);
+  hipLaunchKernelGGL(splitk_reduce, dim3(blocks), dim3(256), 0, s, a.split_buf, splits, a.M, a.N,
+                     reinterpret_cast<float*>(a.C), a.ldc, a.accumulate);
   return hipGetLastError();
 }
 
@@ -938,6 +986,33 @@ hipError_t launch_nt_lds_tile(const GemmArgs& a, hipStream_t s) {
     if (tile == 1) return launch_nt_lds<256, 256, 4, 1, E, 8>(a, s);
     if (tile == 2) return launch_nt_lds<256, 128, 3, 2, E>(a, s);
     return launch_nt_lds<128, 128, 4, 1, E>(a, s);
+  }
+}
+
+// fp8 operands: the bf16 kernels' byte tiles (BK doubles in elements).
+// tile: 1 = 256x256 (8 waves, 128-byte rows), 2 = 256x128 (two CTAs per CU),
+// 3 = 128x128; by shape 256x256 when that gives two tiles per CU (split-K
+// slices counted), else 128x128.
+template <Epi E>
+hipError_t launch_nt_fp8_tile(const GemmArgs& a, hipStream_t s) {
+  const int splits = E == Epi::GradF32 ? a.splits : 1;
+  const int64_t t256 = (int64_t)((a.M + 255) / 256) * ((a.N + 255) / 256) * splits;
+  int tile = a.tile;
+  if (tile == 0) tile = (t256 >= 512 && a.N % 256 == 0) ? 1 : 3;
+  if (tile == 1) return launch_nt_lds<256, 256, 2, 1, E, 8, 128, 1>(a, s);
+  if (tile == 2) return launch_nt_lds<256, 128, 3, 2, E, 4, 64, 1>(a, s);
+  return launch_nt_lds<128, 128, 4, 1, E, 4, 64, 1>(a, s);
+}
+
+hipError_t launch_fp8(Epi epi, const GemmArgs& a, hipStream_t s) {
+  if (!a.a_kcontig || !a.b_kcontig || a.K % 128 != 0 || !a.amax_a || !a.amax_b) return hipErrorInvalidValue;
+  switch (epi) {
+    case Epi::Store: return launch_nt_fp8_tile<Epi::Store>(a, s);
+    case Epi::Residual: return launch_nt_fp8_tile<Epi::Residual>(a, s);
+    case Epi::Relu2: return launch_nt_fp8_tile<Epi::Relu2>(a, s);
+    case Epi::Relu2Bwd: return launch_nt_fp8_tile<Epi::Relu2Bwd>(a, s);
+    case Epi::GradF32: return launch_nt_fp8_tile<Epi::GradF32>(a, s);
+    default: return hipErrorInvalidValue;
   }
 }
 
@@ -1000,11 +1075,12 @@ hipError_t launch_gemm(int dtype, Epi epi, const GemmArgs& a, hipStream_t s) {
   // Shapes the tile loaders assume: a k-contiguous operand has K a multiple of
   // the 128-byte K tile; an mn-contiguous operand has its rows in whole
   // 16-byte vectors; the epilogue writes groups of 4 columns.
+  if (a.splits < 1 || (a.splits > 1 && a.split_buf == nullptr)) return hipErrorInvalidValue;
+  if (dtype == 2) return a.N % 4 != 0 ? hipErrorInvalidValue : launch_fp8(epi, a, s);
   const int bk = dtype == 1 ? 64 : 32;
   if ((a.a_kcontig || a.b_kcontig) && a.K % bk != 0) return hipErrorInvalidValue;
   if ((!a.a_kcontig && a.M % 8 != 0) || (!a.b_kcontig && a.N % 8 != 0) || a.N % 4 != 0) return hipErrorInvalidValue;
   if (epi == Epi::LMHead && a.N % 256 != 0) return hipErrorInvalidValue;
-  if (a.splits < 1 || (a.splits > 1 && a.split_buf == nullptr)) return hipErrorInvalidValue;
   return dtype == 1 ? launch_typed<bf16>(epi, a, s) : launch_typed<float>(epi, a, s);
 }
 

@@ -10,6 +10,16 @@
 //
 // The library owns no device memory: the caller hands in parameters,
 // gradients and one workspace, which is carved up here.
+//
+// FP8 models (repo-explainer.com "karpathy/nanochat: The $100 Full-Stack
+// LLM", section "The Engine Room: Muon and FP8"; atlas.blal.pro, section "How
+// it works", item "2. Pretrain": optional FP8 matmuls) keep bf16 parameters
+// and activations and run the QKV, O and MLP products -- forward, dX and dW --
+// on per-tensor-scaled e4m3 operands: each operand tensor gets its |max|
+// (amax pass), then its codes (quantise pass), row-major for the forward and
+// dX products and token-major (transposed, tokens padded to 128 with zeros)
+// for dW, so that every fp8 product is one k-contiguous GEMM. The layer
+// weights are quantised once per forward and reused by the backward.
 
 #include <hip/hip_runtime.h>
 
@@ -54,14 +64,20 @@ enum Tag : int {
   K_EMBED = 0, K_RMSNORM, K_GEMM_QKV, K_ROPE_QKNORM, K_ATTN_FWD_PREP, K_ATTN_FWD, K_GEMM_O, K_GEMM_W1, K_GEMM_W2,
   K_GEMM_LM, K_CE_LOSS, K_CE_BWD, K_GEMM_LM_DW, K_GEMM_LM_DX, K_RMSNORM_BWD, K_GEMM_W2_DW, K_GEMM_W2_DX,
   K_GEMM_W1_DW, K_GEMM_W1_DX, K_GEMM_O_DW, K_GEMM_O_DX, K_ATTN_BWD_PREP, K_ATTN_BWD_DQ, K_ATTN_BWD_DKV,
-  K_ROPE_QKNORM_BWD, K_GEMM_QKV_DW, K_GEMM_QKV_DX, K_EMBED_BWD, K_WEIGHT_T, K_NUM_TAGS
+  K_ROPE_QKNORM_BWD, K_GEMM_QKV_DW, K_GEMM_QKV_DX, K_EMBED_BWD, K_WEIGHT_T, K_FP8_AMAX, K_FP8_QUANT,
+  K_FP8_WEIGHTS, K_NUM_TAGS
+};
+
+// |max| slots per layer of an FP8 model (fp32, zeroed at every forward)
+enum AmaxSlot : int {
+  A_H1 = 0, A_O, A_H2, A_A, A_DY_MLP, A_DU, A_DY_ATTN, A_DQKV, A_W_QKV, A_W_O, A_W_1, A_W_2, kAmaxSlots = 16
 };
 const char* kTagNames[K_NUM_TAGS] = {
   "embed_rmsnorm", "rmsnorm", "gemm_qkv", "rope_qknorm", "attn_fwd_transpose", "attn_fwd", "gemm_o",
   "gemm_w1_relu2", "gemm_w2", "gemm_lm_head_softcap", "ce_loss", "ce_bwd", "gemm_lm_head_dw", "gemm_lm_head_dx",
   "rmsnorm_bwd", "gemm_w2_dw", "gemm_w2_dx", "gemm_w1_dw", "gemm_w1_dx_relu2bwd", "gemm_o_dw", "gemm_o_dx",
   "attn_bwd_prep", "attn_bwd_dq", "attn_bwd_dkv", "rope_qknorm_bwd", "gemm_qkv_dw", "gemm_qkv_dx", "embed_bwd",
-  "weight_transpose"};
+  "weight_transpose", "fp8_amax", "fp8_quantize", "fp8_weights"};
 
 struct Layout {  // byte offsets inside the workspace
   size_t flag, loss_rows, rope_cos, rope_sin;
@@ -70,12 +86,22 @@ struct Layout {  // byte offsets inside the workspace
   size_t dres, dres_lp, dh, du, dqkv, dout, delta, split;
   size_t qT, kT, vT, doT;  // attention's transposed copies [B, heads, 128, Tp]
   size_t wT, tdesc;        // transposed weights (bf16 models) and their descriptor table
+  // FP8 models: amax slots; e4m3 codes of the layer weights (row-major and
+  // transposed, at each parameter's element offset) and their descriptor
+  // table; row-major codes of the current forward operand; per-layer
+  // token-major codes of the forward operands (kept for dW); codes of the
+  // current output gradient, row-major and token-major
+  size_t amax, wq, wqT, qdesc, xq, dyq, dyqT;
+  std::vector<size_t> h1qT, oqT, h2qT, aqT;
   size_t keys_a, vals_a, keys_b, vals_b, hist, coef, carry;
   size_t total;
   size_t split_elems;
 };
 
-size_t esize(int dtype) { return dtype == GPT_BF16 ? 2 : 4; }
+size_t esize(int dtype) { return dtype == GPT_F32 ? 4 : 2; }  // bf16 storage for GPT_BF16 and GPT_FP8_E4M3
+
+// Padded token count of the token-major fp8 codes (the dW products' K).
+int64_t pad_tokens(int64_t n) { return (n + 127) / 128 * 128; }
 
 struct Planner {
   size_t off = 0;
@@ -165,8 +191,9 @@ Layout plan(const gpt_config& c, int maxB, int maxT) {
     L.vT = p.take(BT * es);
   }
   // split-K partial buffer: largest splits*M*N over the per-layer dW GEMMs
+  // (calls with fewer tokens clamp their slice count to this buffer)
   size_t se = 0;
-  const int K = (int)N;
+  const int K = c.dtype == GPT_FP8_E4M3 ? (int)pad_tokens((int64_t)N) : (int)N;
   auto upd = [&](int M, int Nn) {
     int s = dw_splits(M, Nn, K);
     if (s > 1) se = std::max(se, (size_t)s * M * Nn);
@@ -180,8 +207,25 @@ Layout plan(const gpt_config& c, int maxB, int maxT) {
   L.split = p.take(se * 4);
   {
     const int64_t np = gpt_param_count(&c);
-    L.wT = c.dtype == GPT_BF16 ? p.take((size_t)np * es) : p.take(0);
+    L.wT = c.dtype != GPT_F32 ? p.take((size_t)np * es) : p.take(0);
     L.tdesc = p.take((size_t)(2 + 4 * c.n_layer) * sizeof(gk::TransposeDesc));
+  }
+  if (c.dtype == GPT_FP8_E4M3) {
+    const size_t np = (size_t)gpt_param_count(&c), Np = (size_t)pad_tokens((int64_t)N);
+    const size_t widest = std::max(QKV, std::max(C, F));
+    L.amax = p.take((size_t)c.n_layer * kAmaxSlots * 4);
+    L.wq = p.take(np);
+    L.wqT = p.take(np);
+    L.qdesc = p.take((size_t)4 * c.n_layer * sizeof(gk::QuantDesc));
+    L.xq = p.take(N * std::max(C, F));
+    L.dyq = p.take(N * widest);
+    L.dyqT = p.take(widest * Np);
+    for (int l = 0; l < c.n_layer; ++l) {
+      L.h1qT.push_back(p.take(C * Np));
+      L.oqT.push_back(p.take(H * kHeadDim * Np));
+      L.h2qT.push_back(p.take(C * Np));
+      L.aqT.push_back(p.take(F * Np));
+    }
   }
   L.keys_a = p.take(N * 4);
   L.vals_a = p.take(N * 4);
@@ -227,6 +271,8 @@ struct gpt_model {
   int gemm_tile = 0;      // GPT_OPT_GEMM_TILE
   int ntdesc = 0;
   int64_t wt_tiles = 0;   // total 64x64 tiles of the batched weight transpose
+  int nqdesc = 0;                         // FP8: layer-weight quantisation table
+  int64_t wq_amax_blocks = 0, wq_blocks = 0;
   // state of the last forward
   bool pending = false;
   int B = 0, T = 0;
@@ -273,6 +319,32 @@ gpt_status run(gpt_model* m, int tag, hipStream_t s, Fn&& fn) {
     gpt_status st_ = run(m, tag, stream, [&]() -> hipError_t { body });      \
     if (st_ != GPT_OK) return st_;                                           \
   } while (0)
+#define TRY(x) do { gpt_status s_ = (x); if (s_ != GPT_OK) return s_; } while (0)
+
+// FP8: amax pass then quantise pass of one bf16 operand [rows, cols]
+// (contiguous) into row-major codes q and/or token-major codes qT [cols, ldT].
+gpt_status quantize_operand(gpt_model* m, hipStream_t stream, const void* src, int rows, int cols, uint8_t* q,
+                            uint8_t* qT, int64_t ldT, float* amax) {
+  gk::QuantDesc d;
+  d.src = src;
+  d.ld = cols;
+  d.rows = rows;
+  d.cols = cols;
+  d.q = q;
+  d.qT = qT;
+  d.ldT = (int32_t)ldT;
+  d.amax = amax;
+  RUN(K_FP8_AMAX, return gk::launch_fp8_amax(d, stream););
+  RUN(K_FP8_QUANT, return gk::launch_fp8_quantize(d, stream););
+  return GPT_OK;
+}
+
+// dW split count, clamped to the partial buffer the workspace holds.
+int dw_splits_ws(const gpt_model* m, int M, int N, int K) {
+  int s = dw_splits(M, N, K);
+  while (s > 1 && (size_t)s * M * N > m->L.split_elems) --s;
+  return s;
+}
 
 }  // namespace
 
@@ -296,7 +368,8 @@ const char* gpt_last_error_message(void) { return g_last_error.c_str(); }
 gpt_status gpt_config_from_depth(int32_t depth, int32_t dtype, gpt_config* out) {
   if (!out) return fail(GPT_E_INVALID_ARG, "out is NULL");
   if (depth < 2) return fail(GPT_E_INVALID_ARG, "depth must be >= 2 (width 64*depth holds 128-wide heads)");
-  if (dtype != GPT_F32 && dtype != GPT_BF16) return fail(GPT_E_INVALID_ARG, "dtype must be GPT_F32 or GPT_BF16");
+  if (dtype != GPT_F32 && dtype != GPT_BF16 && dtype != GPT_FP8_E4M3)
+    return fail(GPT_E_INVALID_ARG, "dtype must be GPT_F32, GPT_BF16 or GPT_FP8_E4M3");
   gpt_config c;
   c.n_layer = depth;
   c.model_dim = 64 * depth;
@@ -319,7 +392,8 @@ gpt_status gpt_config_from_depth(int32_t depth, int32_t dtype, gpt_config* out) 
 gpt_status gpt_config_validate(const gpt_config* c) {
   gpt_status s = check_shape(c);
   if (s != GPT_OK) return s;
-  if (c->dtype != GPT_F32 && c->dtype != GPT_BF16) return fail(GPT_E_UNSUPPORTED, "dtype %d not supported", c->dtype);
+  if (c->dtype != GPT_F32 && c->dtype != GPT_BF16 && c->dtype != GPT_FP8_E4M3)
+    return fail(GPT_E_UNSUPPORTED, "dtype %d not supported", c->dtype);
   if (c->n_kv_head != 1) return fail(GPT_E_UNSUPPORTED, "n_kv_head must be 1 (multi-query attention)");
   if (c->head_dim != kHeadDim) return fail(GPT_E_UNSUPPORTED, "head_dim must be 128");
   if (c->n_head * c->head_dim != c->model_dim)
@@ -450,9 +524,10 @@ gpt_status gpt_init(const gpt_config* cfg, const void* params, float* grads, voi
     }
   // transposed-weight descriptors (all matrices except the embedding, which
   // is never multiplied)
+  // (FP8 models: only the LM head; their layer weights get e4m3 copies)
   std::vector<gk::TransposeDesc> td;
   int64_t tiles = 0;
-  for (int i = 1; i < n; ++i) {
+  for (int i = cfg->dtype == GPT_FP8_E4M3 ? n - 1 : 1; i < n; ++i) {
     gk::TransposeDesc t;
     t.offset = d[i].offset;
     t.rows = (int32_t)d[i].rows;
@@ -463,7 +538,40 @@ gpt_status gpt_init(const gpt_config* cfg, const void* params, float* grads, voi
   }
   m->ntdesc = (int)td.size();
   m->wt_tiles = tiles;
+  // FP8 layer-weight quantisation table: codes at the parameter's offset in
+  // wq (row-major) and wqT (transposed)
+  std::vector<gk::QuantDesc> qd;
+  if (cfg->dtype == GPT_FP8_E4M3) {
+    int64_t ab = 0, qb = 0;
+    for (int i = 1; i + 1 < n; ++i) {
+      const int l = (i - 1) / 4, w = (i - 1) % 4;
+      gk::QuantDesc q;
+      q.src = reinterpret_cast<const char*>(params) + d[i].offset * 2;
+      q.ld = d[i].cols;
+      q.rows = (int32_t)d[i].rows;
+      q.cols = (int32_t)d[i].cols;
+      q.q = reinterpret_cast<uint8_t*>(m->ws + m->L.wq) + d[i].offset;
+      q.qT = reinterpret_cast<uint8_t*>(m->ws + m->L.wqT) + d[i].offset;
+      q.ldT = q.rows;
+      q.amax = reinterpret_cast<float*>(m->ws + m->L.amax) + l * kAmaxSlots + A_W_QKV + w;
+      q.amax_block0 = ab;
+      q.quant_block0 = qb;
+      if (gk::check_quant_desc(q) != hipSuccess) {
+        delete m;
+        return fail(GPT_E_UNSUPPORTED, "weight %s cannot be quantised", d[i].name);
+      }
+      ab += gk::amax_blocks(q);
+      qb += gk::quant_blocks(q);
+      qd.push_back(q);
+    }
+    m->nqdesc = (int)qd.size();
+    m->wq_amax_blocks = ab;
+    m->wq_blocks = qb;
+  }
   hipError_t e = hipMemcpyAsync(m->ws + m->L.rope_cos, ct.data(), ct.size() * 4, hipMemcpyHostToDevice, stream);
+  if (e == hipSuccess && !qd.empty())
+    e = hipMemcpyAsync(m->ws + m->L.qdesc, qd.data(), qd.size() * sizeof(gk::QuantDesc), hipMemcpyHostToDevice,
+                       stream);
   if (e == hipSuccess)
     e = hipMemcpyAsync(m->ws + m->L.tdesc, td.data(), td.size() * sizeof(gk::TransposeDesc), hipMemcpyHostToDevice,
                        stream);
@@ -486,26 +594,53 @@ gpt_status gpt_forward_loss(gpt_model* m, const int32_t* idx, const int32_t* tar
     return fail(GPT_E_INVALID_ARG, "B=%d T=%d outside [1, %d] x [1, %d]", B, T, m->maxB, m->maxT);
   hipStream_t stream = (hipStream_t)stream_;
   const gpt_config& c = m->cfg;
-  const int dt = c.dtype;
+  const bool fp8 = c.dtype == GPT_FP8_E4M3;
+  const int dt = fp8 ? GPT_BF16 : c.dtype;  // activation storage
+  const int gdt = fp8 ? 2 : dt;              // operands of the QKV / O / MLP products
   const int N = B * T, C = c.model_dim, H = c.n_head, F = c.mlp_dim, V = c.vocab_size;
   const int QKV = (H + 2) * kHeadDim, HD = H * kHeadDim;
   const Layout& L = m->L;
   int* flag = wsp<int>(m, L.flag);
   m->pending = false;
+  const int64_t Np = pad_tokens(N);
+  float* amax = fp8 ? wsp<float>(m, L.amax) : nullptr;
+  auto slot = [&](int l, int k) { return amax + l * kAmaxSlots + k; };
+  uint8_t* xq = fp8 ? wsp<uint8_t>(m, L.xq) : nullptr;
+  const uint8_t* wq = fp8 ? wsp<uint8_t>(m, L.wq) : nullptr;
+  // A = activation (or its codes), B = weight at element offset woff (or its codes)
+  auto operands = [&](gk::GemmArgs& a, const void* act, int64_t woff, int l, int act_slot, int w_slot) {
+    if (fp8) {
+      a.A = xq;
+      a.B = wq + woff;
+      a.amax_a = slot(l, act_slot);
+      a.amax_b = slot(l, w_slot);
+    } else {
+      a.A = act;
+      a.B = pbase(m, woff);
+    }
+  };
+  if (fp8) {
+    RUN(K_FP8_WEIGHTS, return gk::launch_fill_f32(amax, 0.f, (int64_t)c.n_layer * kAmaxSlots, stream););
+    RUN(K_FP8_WEIGHTS, return gk::launch_fp8_amax_batched(reinterpret_cast<const gk::QuantDesc*>(m->ws + L.qdesc),
+                                                          m->nqdesc, m->wq_amax_blocks, stream););
+    RUN(K_FP8_WEIGHTS, return gk::launch_fp8_quantize_batched(
+                           reinterpret_cast<const gk::QuantDesc*>(m->ws + L.qdesc), m->nqdesc, m->wq_blocks, stream););
+  }
 
   RUN(K_EMBED, return gk::launch_embed_rmsnorm(dt, pbase(m, m->off_wte), idx, N, C, V, c.norm_eps, m->ws + L.x,
                                                wsp<float>(m, L.rstd0), flag, stream););
   for (int l = 0; l < c.n_layer; ++l) {
     RUN(K_RMSNORM, return gk::launch_rmsnorm(dt, m->ws + L.x, N, C, c.norm_eps, m->ws + L.h1[l],
                                              wsp<float>(m, L.rstd1[l]), stream););
+    if (fp8) TRY(quantize_operand(m, stream, m->ws + L.h1[l], N, C, xq, wsp<uint8_t>(m, L.h1qT[l]), Np, slot(l, A_H1)));
     RUN(K_GEMM_QKV, {
       gk::GemmArgs a;
       a.tile = m->gemm_tile;
-      a.A = m->ws + L.h1[l]; a.lda = C;
-      a.B = pbase(m, m->off_qkv[l]); a.ldb = C;
+      operands(a, m->ws + L.h1[l], m->off_qkv[l], l, A_H1, A_W_QKV);
+      a.lda = C; a.ldb = C;
       a.M = N; a.N = QKV; a.K = C;
       a.C = m->ws + L.qkv[l]; a.ldc = QKV;
-      return gk::launch_gemm(dt, gk::Epi::Store, a, stream);
+      return gk::launch_gemm(gdt, gk::Epi::Store, a, stream);
     });
     RUN(K_ROPE_QKNORM, return gk::launch_rope_qknorm(dt, m->ws + L.qkv[l], B, T, H, c.norm_eps,
                                                      wsp<float>(m, L.rope_cos), wsp<float>(m, L.rope_sin),
@@ -515,34 +650,37 @@ gpt_status gpt_forward_loss(gpt_model* m, const int32_t* idx, const int32_t* tar
                                                     wsp<float>(m, L.lse[l]), m->ws + L.vT, 0, stream););
     RUN(K_ATTN_FWD, return gk::launch_attn_fwd(dt, m->ws + L.qkv[l], B, T, H, win, m->ws + L.o[l],
                                                wsp<float>(m, L.lse[l]), m->ws + L.vT, 1, stream););
+    if (fp8) TRY(quantize_operand(m, stream, m->ws + L.o[l], N, HD, xq, wsp<uint8_t>(m, L.oqT[l]), Np, slot(l, A_O)));
     RUN(K_GEMM_O, {
       gk::GemmArgs a;
       a.tile = m->gemm_tile;
-      a.A = m->ws + L.o[l]; a.lda = HD;
-      a.B = pbase(m, m->off_o[l]); a.ldb = HD;
+      operands(a, m->ws + L.o[l], m->off_o[l], l, A_O, A_W_O);
+      a.lda = HD; a.ldb = HD;
       a.M = N; a.N = C; a.K = HD;
       a.C = m->ws + L.x; a.ldc = C;
-      return gk::launch_gemm(dt, gk::Epi::Residual, a, stream);
+      return gk::launch_gemm(gdt, gk::Epi::Residual, a, stream);
     });
     RUN(K_RMSNORM, return gk::launch_rmsnorm(dt, m->ws + L.x, N, C, c.norm_eps, m->ws + L.h2[l],
                                              wsp<float>(m, L.rstd2[l]), stream););
+    if (fp8) TRY(quantize_operand(m, stream, m->ws + L.h2[l], N, C, xq, wsp<uint8_t>(m, L.h2qT[l]), Np, slot(l, A_H2)));
     RUN(K_GEMM_W1, {
       gk::GemmArgs a;
       a.tile = m->gemm_tile;
-      a.A = m->ws + L.h2[l]; a.lda = C;
-      a.B = pbase(m, m->off_w1[l]); a.ldb = C;
+      operands(a, m->ws + L.h2[l], m->off_w1[l], l, A_H2, A_W_1);
+      a.lda = C; a.ldb = C;
       a.M = N; a.N = F; a.K = C;
       a.C = m->ws + L.a[l]; a.ldc = F;
-      return gk::launch_gemm(dt, gk::Epi::Relu2, a, stream);
+      return gk::launch_gemm(gdt, gk::Epi::Relu2, a, stream);
     });
+    if (fp8) TRY(quantize_operand(m, stream, m->ws + L.a[l], N, F, xq, wsp<uint8_t>(m, L.aqT[l]), Np, slot(l, A_A)));
     RUN(K_GEMM_W2, {
       gk::GemmArgs a;
       a.tile = m->gemm_tile;
-      a.A = m->ws + L.a[l]; a.lda = F;
-      a.B = pbase(m, m->off_w2[l]); a.ldb = F;
+      operands(a, m->ws + L.a[l], m->off_w2[l], l, A_A, A_W_2);
+      a.lda = F; a.ldb = F;
       a.M = N; a.N = C; a.K = F;
       a.C = m->ws + L.x; a.ldc = C;
-      return gk::launch_gemm(dt, gk::Epi::Residual, a, stream);
+      return gk::launch_gemm(gdt, gk::Epi::Residual, a, stream);
     });
   }
   RUN(K_RMSNORM, return gk::launch_rmsnorm(dt, m->ws + L.x, N, C, c.norm_eps, m->ws + L.hf,
@@ -576,7 +714,8 @@ gpt_status gpt_backward(gpt_model* m, float dloss, int32_t accumulate, void* str
   if (!m->pending) return fail(GPT_E_STATE, "gpt_backward needs a preceding gpt_forward_loss with need_grad = 1");
   hipStream_t stream = (hipStream_t)stream_;
   const gpt_config& c = m->cfg;
-  const int dt = c.dtype;
+  const bool fp8 = c.dtype == GPT_FP8_E4M3;
+  const int dt = fp8 ? GPT_BF16 : c.dtype;  // activation storage
   const int B = m->B, T = m->T, N = B * T, C = c.model_dim, H = c.n_head, F = c.mlp_dim, V = c.vocab_size;
   const int QKV = (H + 2) * kHeadDim, HD = H * kHeadDim;
   const Layout& L = m->L;
@@ -591,7 +730,7 @@ gpt_status gpt_backward(gpt_model* m, float dloss, int32_t accumulate, void* str
       a.A = dy; a.lda = ldy; a.a_kcontig = false;
       a.B = x; a.ldb = ldx; a.b_kcontig = false;
       a.M = M; a.N = Nn; a.K = N;
-      a.splits = dw_splits(M, Nn, N);
+      a.splits = dw_splits_ws(m, M, Nn, N);
       a.C = G + goff; a.ldc = Nn;
       a.accumulate = acc;
       a.split_buf = wsp<float>(m, L.split);
@@ -625,7 +764,48 @@ gpt_status gpt_backward(gpt_model* m, float dloss, int32_t accumulate, void* str
     RUN(K_WEIGHT_T, return gk::launch_transpose_batched(dt, m->params, m->ws + L.wT,
                                                         reinterpret_cast<const gk::TransposeDesc*>(m->ws + L.tdesc),
                                                         m->ntdesc, m->wt_tiles, stream););
-#define TRY(x) do { gpt_status s_ = (x); if (s_ != GPT_OK) return s_; } while (0)
+  // FP8 products. Output-gradient codes: row-major dyq [N, K] and token-major
+  // dyqT [K, Np]; forward operands' token-major codes from the stash; weight
+  // codes (transposed) from the forward's quantisation.
+  const int64_t Np = pad_tokens(N);
+  float* amax = fp8 ? wsp<float>(m, L.amax) : nullptr;
+  auto slot = [&](int l, int k) { return amax + l * kAmaxSlots + k; };
+  uint8_t* dyq = fp8 ? wsp<uint8_t>(m, L.dyq) : nullptr;
+  uint8_t* dyqT = fp8 ? wsp<uint8_t>(m, L.dyqT) : nullptr;
+  const uint8_t* wqT = fp8 ? wsp<uint8_t>(m, L.wqT) : nullptr;
+  auto dw8 = [&](int tag, size_t xT, int l, int dy_slot, int x_slot, int M, int Nn, int64_t goff) -> gpt_status {
+    RUN(tag, {
+      gk::GemmArgs a;
+      a.tile = m->gemm_tile;
+      a.A = dyqT; a.lda = Np;
+      a.B = m->ws + xT; a.ldb = Np;
+      a.M = M; a.N = Nn; a.K = (int)Np;
+      a.splits = dw_splits_ws(m, M, Nn, (int)Np);
+      a.C = G + goff; a.ldc = Nn;
+      a.accumulate = acc;
+      a.split_buf = wsp<float>(m, L.split);
+      a.amax_a = slot(l, dy_slot);
+      a.amax_b = slot(l, x_slot);
+      return gk::launch_gemm(2, gk::Epi::GradF32, a, stream);
+    });
+    return GPT_OK;
+  };
+  auto dx8 = [&](int tag, gk::Epi epi, int l, int dy_slot, int w_slot, int64_t woff, int Nn, int K, void* out,
+                 const void* aux) -> gpt_status {
+    RUN(tag, {
+      gk::GemmArgs a;
+      a.tile = m->gemm_tile;
+      a.A = dyq; a.lda = K;
+      a.B = wqT + woff; a.ldb = K;
+      a.M = N; a.N = Nn; a.K = K;
+      a.C = out; a.ldc = Nn;
+      a.C2 = const_cast<void*>(aux); a.ldc2 = Nn;
+      a.amax_a = slot(l, dy_slot);
+      a.amax_b = slot(l, w_slot);
+      return gk::launch_gemm(2, epi, a, stream);
+    });
+    return GPT_OK;
+  };
 
   RUN(K_CE_BWD, return gk::launch_ce_bwd(dt, m->ws + L.logits, wsp<float>(m, L.lse_ce), m->targets, N, V,
                                          c.logit_softcap, dloss / (float)N, stream););
@@ -635,16 +815,31 @@ gpt_status gpt_backward(gpt_model* m, float dloss, int32_t accumulate, void* str
                                                    wsp<float>(m, L.dres), m->ws + L.dres_lp, stream););
   for (int l = c.n_layer - 1; l >= 0; --l) {
     // MLP
-    TRY(dw(K_GEMM_W2_DW, m->ws + L.dres_lp, C, m->ws + L.a[l], F, C, F, m->off_w2[l]));
-    TRY(dx(K_GEMM_W2_DX, gk::Epi::Relu2Bwd, m->ws + L.dres_lp, C, m->off_w2[l], F, C, m->ws + L.du,
-           m->ws + L.a[l]));
-    TRY(dw(K_GEMM_W1_DW, m->ws + L.du, F, m->ws + L.h2[l], C, F, C, m->off_w1[l]));
-    TRY(dx(K_GEMM_W1_DX, gk::Epi::Store, m->ws + L.du, F, m->off_w1[l], C, F, m->ws + L.dh, nullptr));
+    if (fp8) {
+      TRY(quantize_operand(m, stream, m->ws + L.dres_lp, N, C, dyq, dyqT, Np, slot(l, A_DY_MLP)));
+      TRY(dw8(K_GEMM_W2_DW, L.aqT[l], l, A_DY_MLP, A_A, C, F, m->off_w2[l]));
+      TRY(dx8(K_GEMM_W2_DX, gk::Epi::Relu2Bwd, l, A_DY_MLP, A_W_2, m->off_w2[l], F, C, m->ws + L.du, m->ws + L.a[l]));
+      TRY(quantize_operand(m, stream, m->ws + L.du, N, F, dyq, dyqT, Np, slot(l, A_DU)));
+      TRY(dw8(K_GEMM_W1_DW, L.h2qT[l], l, A_DU, A_H2, F, C, m->off_w1[l]));
+      TRY(dx8(K_GEMM_W1_DX, gk::Epi::Store, l, A_DU, A_W_1, m->off_w1[l], C, F, m->ws + L.dh, nullptr));
+    } else {
+      TRY(dw(K_GEMM_W2_DW, m->ws + L.dres_lp, C, m->ws + L.a[l], F, C, F, m->off_w2[l]));
+      TRY(dx(K_GEMM_W2_DX, gk::Epi::Relu2Bwd, m->ws + L.dres_lp, C, m->off_w2[l], F, C, m->ws + L.du,
+             m->ws + L.a[l]));
+      TRY(dw(K_GEMM_W1_DW, m->ws + L.du, F, m->ws + L.h2[l], C, F, C, m->off_w1[l]));
+      TRY(dx(K_GEMM_W1_DX, gk::Epi::Store, m->ws + L.du, F, m->off_w1[l], C, F, m->ws + L.dh, nullptr));
+    }
     RUN(K_RMSNORM_BWD, return gk::launch_rmsnorm_bwd(dt, m->ws + L.dh, m->ws + L.h2[l], wsp<float>(m, L.rstd2[l]),
                                                      N, C, 1, wsp<float>(m, L.dres), m->ws + L.dres_lp, stream););
     // attention
-    TRY(dw(K_GEMM_O_DW, m->ws + L.dres_lp, C, m->ws + L.o[l], HD, C, HD, m->off_o[l]));
-    TRY(dx(K_GEMM_O_DX, gk::Epi::Store, m->ws + L.dres_lp, C, m->off_o[l], HD, C, m->ws + L.dout, nullptr));
+    if (fp8) {
+      TRY(quantize_operand(m, stream, m->ws + L.dres_lp, N, C, dyq, dyqT, Np, slot(l, A_DY_ATTN)));
+      TRY(dw8(K_GEMM_O_DW, L.oqT[l], l, A_DY_ATTN, A_O, C, HD, m->off_o[l]));
+      TRY(dx8(K_GEMM_O_DX, gk::Epi::Store, l, A_DY_ATTN, A_W_O, m->off_o[l], HD, C, m->ws + L.dout, nullptr));
+    } else {
+      TRY(dw(K_GEMM_O_DW, m->ws + L.dres_lp, C, m->ws + L.o[l], HD, C, HD, m->off_o[l]));
+      TRY(dx(K_GEMM_O_DX, gk::Epi::Store, m->ws + L.dres_lp, C, m->off_o[l], HD, C, m->ws + L.dout, nullptr));
+    }
     gk::AttnBwdArgs ab;
     ab.qkv = m->ws + L.qkv[l];
     ab.o = m->ws + L.o[l];
@@ -664,8 +859,14 @@ gpt_status gpt_backward(gpt_model* m, float dloss, int32_t accumulate, void* str
                                                              wsp<float>(m, L.rstd_qk[l]), B, T, H,
                                                              wsp<float>(m, L.rope_cos), wsp<float>(m, L.rope_sin),
                                                              stream););
-    TRY(dw(K_GEMM_QKV_DW, m->ws + L.dqkv, QKV, m->ws + L.h1[l], C, QKV, C, m->off_qkv[l]));
-    TRY(dx(K_GEMM_QKV_DX, gk::Epi::Store, m->ws + L.dqkv, QKV, m->off_qkv[l], C, QKV, m->ws + L.dh, nullptr));
+    if (fp8) {
+      TRY(quantize_operand(m, stream, m->ws + L.dqkv, N, QKV, dyq, dyqT, Np, slot(l, A_DQKV)));
+      TRY(dw8(K_GEMM_QKV_DW, L.h1qT[l], l, A_DQKV, A_H1, QKV, C, m->off_qkv[l]));
+      TRY(dx8(K_GEMM_QKV_DX, gk::Epi::Store, l, A_DQKV, A_W_QKV, m->off_qkv[l], C, QKV, m->ws + L.dh, nullptr));
+    } else {
+      TRY(dw(K_GEMM_QKV_DW, m->ws + L.dqkv, QKV, m->ws + L.h1[l], C, QKV, C, m->off_qkv[l]));
+      TRY(dx(K_GEMM_QKV_DX, gk::Epi::Store, m->ws + L.dqkv, QKV, m->off_qkv[l], C, QKV, m->ws + L.dh, nullptr));
+    }
     RUN(K_RMSNORM_BWD, return gk::launch_rmsnorm_bwd(dt, m->ws + L.dh, m->ws + L.h1[l], wsp<float>(m, L.rstd1[l]),
                                                      N, C, 1, wsp<float>(m, L.dres), m->ws + L.dres_lp, stream););
   }
@@ -688,7 +889,6 @@ gpt_status gpt_backward(gpt_model* m, float dloss, int32_t accumulate, void* str
     a.carry = wsp<float>(m, L.carry);
     return gk::launch_embed_bwd(a, stream);
   });
-#undef TRY
   return GPT_OK;
 }
 
@@ -771,7 +971,65 @@ gpt_status gpt_debug_buffer(gpt_model* m, const char* name, int32_t layer, void*
   if (s == "lse") return set(L.lse[layer], N * H * 4);
   if (s == "h2") return set(L.h2[layer], N * C * es);
   if (s == "a") return set(L.a[layer], N * (size_t)c.mlp_dim * es);
+  if (s == "amax" && c.dtype == GPT_FP8_E4M3) return set(L.amax + (size_t)layer * kAmaxSlots * 4, kAmaxSlots * 4);
   return fail(GPT_E_INVALID_ARG, "unknown buffer '%s'", name);
+}
+
+gpt_status gpt_fp8_matmul(const uint8_t* a, int64_t lda, const float* amax_a, const uint8_t* b, int64_t ldb,
+                          const float* amax_b, int32_t M, int32_t N, int32_t K, int32_t out_dtype, void* out,
+                          int64_t ldo, int32_t tile, int32_t splits, float* partials, void* stream_) {
+  if (!a || !b || !amax_a || !amax_b || !out) return fail(GPT_E_INVALID_ARG, "NULL argument");
+  if (M < 0 || N < 0 || K < 0 || K % 128 != 0 || N % 4 != 0)
+    return fail(GPT_E_INVALID_ARG, "need M, N, K >= 0, K a multiple of 128 and N a multiple of 4");
+  if (lda < K || ldb < K || ldo < N || lda % 16 != 0 || ldb % 16 != 0 || ldo % 4 != 0)
+    return fail(GPT_E_INVALID_ARG, "need lda, ldb >= K (multiples of 16) and ldo >= N (a multiple of 4)");
+  if (((uintptr_t)a & 15) || ((uintptr_t)b & 15) || ((uintptr_t)out & 15))
+    return fail(GPT_E_INVALID_ARG, "a, b and out must be 16-byte aligned");
+  if (tile < 0 || tile > 3) return fail(GPT_E_INVALID_ARG, "tile must be 0..3");
+  if (out_dtype != GPT_F32 && out_dtype != GPT_BF16) return fail(GPT_E_INVALID_ARG, "out_dtype must be GPT_F32 or GPT_BF16");
+  if (splits < 1 || splits > 64 || (splits > 1 && (out_dtype != GPT_F32 || !partials)))
+    return fail(GPT_E_INVALID_ARG, "splits must be 1..64; more than one needs fp32 output and a partial buffer");
+  hipStream_t stream = (hipStream_t)stream_;
+  gk::GemmArgs g;
+  g.tile = tile;
+  g.A = a; g.lda = lda;
+  g.B = b; g.ldb = ldb;
+  g.M = M; g.N = N; g.K = K;
+  g.C = out; g.ldc = ldo;
+  g.amax_a = amax_a;
+  g.amax_b = amax_b;
+  g.splits = splits;
+  g.split_buf = partials;
+  g.accumulate = 0;
+  if (M == 0 || N == 0) return GPT_OK;
+  if (K == 0) return fail(GPT_E_INVALID_ARG, "K must be positive");
+  HIP_TRY(gk::launch_gemm(2, out_dtype == GPT_F32 ? gk::Epi::GradF32 : gk::Epi::Store, g, stream));
+  return GPT_OK;
+}
+
+gpt_status gpt_fp8_quantize(const void* x, int64_t rows, int64_t cols, uint8_t* q, uint8_t* qT, int64_t ldT,
+                            float* amax, void* stream_) {
+  if (!x || !amax || (!q && !qT)) return fail(GPT_E_INVALID_ARG, "x, amax and one of q, qT must be non-NULL");
+  if (rows < 0 || cols < 0 || rows > INT32_MAX || cols > INT32_MAX || cols % 16 != 0)
+    return fail(GPT_E_INVALID_ARG, "need 0 <= rows, cols < 2^31 and cols a multiple of 16");
+  if (qT && (ldT < rows || ldT % 16 != 0 || ldT > INT32_MAX))
+    return fail(GPT_E_INVALID_ARG, "ldT must be >= rows and a multiple of 16");
+  if (((uintptr_t)x & 15) || ((uintptr_t)q & 15) || ((uintptr_t)qT & 15) || ((uintptr_t)amax & 3))
+    return fail(GPT_E_INVALID_ARG, "x, q and qT must be 16-byte aligned, amax 4-byte aligned");
+  hipStream_t stream = (hipStream_t)stream_;
+  gk::QuantDesc d;
+  d.src = x;
+  d.ld = cols;
+  d.rows = (int32_t)rows;
+  d.cols = (int32_t)cols;
+  d.q = q;
+  d.qT = qT;
+  d.ldT = (int32_t)(qT ? ldT : 0);
+  d.amax = amax;
+  HIP_TRY(gk::launch_fill_f32(amax, 0.f, 1, stream));
+  HIP_TRY(gk::launch_fp8_amax(d, stream));
+  HIP_TRY(gk::launch_fp8_quantize(d, stream));
+  return GPT_OK;
 }
 
 }  // extern "C"

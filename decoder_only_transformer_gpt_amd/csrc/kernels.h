@@ -39,9 +39,13 @@ struct GemmArgs {
   int accumulate = 0;
   float* split_buf = nullptr;  // [splits, M, N] partials when splits > 1
   int zslice = -1;             // split-K slice of the block; -1: blockIdx.z
+  // fp8 operands (dtype 2): |max| slots of A and B; acc is scaled by 1/(s_a s_b)
+  const float* amax_a = nullptr;
+  const float* amax_b = nullptr;
 };
 
-// dtype: 0 = fp32, 1 = bf16 (gpt.h GPT_F32 / GPT_BF16)
+// dtype: 0 = fp32, 1 = bf16 (gpt.h GPT_F32 / GPT_BF16), 2 = fp8 e4m3
+// operands (k-contiguous, K a multiple of 128) with bf16 / fp32 outputs
 hipError_t launch_gemm(int dtype, Epi epi, const GemmArgs& a, hipStream_t s);
 // Partial-column width of the LMHead epilogue (exp-sum partials per row).
 constexpr int kLMHeadPartCols = 64;
@@ -122,5 +126,31 @@ struct TransposeDesc {
 };
 hipError_t launch_transpose_batched(int dtype, const void* src, void* dst, const TransposeDesc* desc, int ndesc,
                                     int64_t total_tiles, hipStream_t s);
+
+// FP8 (e4m3) operands ---------------------------------------------------------
+// One bf16 tensor [rows, cols] (row pitch ld elements) and where its codes go:
+// q [rows, cols] row-major (pitch cols) and/or qT [cols, ldT] (its transpose,
+// columns rows..ldT-1 written as code 0). amax: the tensor's fp32 |max| slot,
+// to be zeroed before the amax pass (launch_fill_f32) and read by the
+// quantise pass and the GEMM epilogue; s = 448 / amax (1 if amax == 0).
+struct QuantDesc {
+  const void* src = nullptr;    // bf16
+  int64_t ld = 0;
+  int32_t rows = 0, cols = 0;   // cols a multiple of 16
+  uint8_t* q = nullptr;
+  uint8_t* qT = nullptr;
+  int32_t ldT = 0;              // >= rows, a multiple of 16
+  float* amax = nullptr;
+  int64_t amax_block0 = 0;      // first block of this tensor in a batched amax launch
+  int64_t quant_block0 = 0;     // first block of this tensor in a batched quantise launch
+};
+hipError_t check_quant_desc(const QuantDesc& d);
+int64_t amax_blocks(const QuantDesc& d);
+int64_t quant_blocks(const QuantDesc& d);
+hipError_t launch_fp8_amax(const QuantDesc& d, hipStream_t s);      // amax = max(amax, max |x|)
+hipError_t launch_fp8_quantize(const QuantDesc& d, hipStream_t s);
+// Batched over a device table of n descriptors (block offsets filled in).
+hipError_t launch_fp8_amax_batched(const QuantDesc* table, int n, int64_t total_blocks, hipStream_t s);
+hipError_t launch_fp8_quantize_batched(const QuantDesc* table, int n, int64_t total_blocks, hipStream_t s);
 
 }  // namespace gk

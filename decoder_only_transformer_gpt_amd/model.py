@@ -14,7 +14,7 @@ class GPT:
         self.cfg = cfg
         self.layout = _lib.gpt_param_layout(cfg)
         n = _lib.gpt_param_count(cfg)
-        dt = torch.bfloat16 if cfg.dtype == _lib.GPT_BF16 else torch.float32
+        dt = torch.float32 if cfg.dtype == _lib.GPT_F32 else torch.bfloat16  # FP8 models keep bf16 parameters
         if params.dtype != dt or params.numel() != n or not params.is_cuda:
             raise ValueError(f"params must be a cuda {dt} tensor of {n} elements")
         self.params = params.contiguous()
@@ -29,7 +29,7 @@ class GPT:
 
     @staticmethod
     def params_from_numpy(storage: np.ndarray, cfg: _lib.gpt_config, device="cuda") -> torch.Tensor:
-        if cfg.dtype == _lib.GPT_BF16:
+        if cfg.dtype != _lib.GPT_F32:
             return torch.from_numpy(storage.view(np.int16)).to(device).view(torch.bfloat16)
         return torch.from_numpy(storage).to(device)
 

@@ -24,13 +24,13 @@ class Workload:
     vocab_size: int
     seq_len: int
     batch: int
-    dtype: str          # "f32" | "bf16"
+    dtype: str          # "f32" | "bf16" | "fp8" (bf16 with e4m3 QKV / O / MLP products)
     tokens: str         # "uniform" | "zipf"
     window_pattern: str = ""   # sliding-window layer pattern, e.g. "SSSL"; "" = all full
     window_short: int = 0
 
     def config(self) -> _lib.gpt_config:
-        dt = _lib.GPT_BF16 if self.dtype == "bf16" else _lib.GPT_F32
+        dt = {"f32": _lib.GPT_F32, "bf16": _lib.GPT_BF16, "fp8": _lib.GPT_FP8_E4M3}[self.dtype]
         c = _lib.gpt_config_from_depth(self.depth, dt)
         c.model_dim = self.model_dim
         c.n_head = self.model_dim // 128
@@ -51,4 +51,7 @@ WORKLOADS = {
     # tokens, the last layer full (aethryn.com, section "A Llama-class
     # transformer with ten modern departures")
     "d20-sssl": Workload("d20-sssl", 20, 1280, 5120, 65536, 2048, 32, "bf16", "zipf", "SSSL", 1024),
+    # d24 with e4m3 QKV / O / MLP products (repo-explainer.com "karpathy/nanochat:
+    # The $100 Full-Stack LLM", section "The Engine Room: Muon and FP8")
+    "d24fp8": Workload("d24fp8", 24, 1536, 6144, 65536, 2048, 16, "fp8", "zipf"),
 }

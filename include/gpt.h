@@ -61,8 +61,20 @@ enum {
   GPT_E_DEVICE = -6        /* sticky device-side flag, e.g. a token id outside [0, vocab_size) */
 };
 
-/* Compute/storage dtype of parameters and activations. Gradients are always fp32. */
-enum { GPT_F32 = 0, GPT_BF16 = 1 };
+/* Compute/storage dtype of parameters and activations. Gradients are always fp32.
+ * GPT_FP8_E4M3: bf16 parameters and activations as for GPT_BF16, but the QKV,
+ * O and MLP products -- forward, input gradient and weight gradient -- take
+ * e4m3 operands with one scale per tensor, s = 448 / max|tensor| (current
+ * scaling), round to nearest even, saturating at +-448; the output gradient
+ * is quantised too and the backward passes the quantisation straight through.
+ * The LM head and attention stay bf16. (FP8 training: repo-explainer.com
+ * "karpathy/nanochat: The $100 Full-Stack LLM", section "The Engine Room: Muon
+ * and FP8"; optional FP8 matmuls: atlas.blal.pro "nanochat — full-stack
+ * ChatGPT in ~8k lines", section "How it works", item "2. Pretrain". The
+ * scaling recipe is this library's reading; the pages give none.) The layer
+ * weights are quantised by gpt_forward_loss and reused by gpt_backward, so
+ * parameters must not change in between. */
+enum { GPT_F32 = 0, GPT_BF16 = 1, GPT_FP8_E4M3 = 2 };
 
 typedef struct gpt_config {
   int32_t n_layer;      /* depth */
@@ -76,7 +88,7 @@ typedef struct gpt_config {
   float rope_theta;     /* 10000 */
   float logit_softcap;  /* 15 */
   float norm_eps;       /* 2^-23 */
-  int32_t dtype;        /* GPT_F32 or GPT_BF16 */
+  int32_t dtype;        /* GPT_F32, GPT_BF16 or GPT_FP8_E4M3 */
   /* Sliding-window attention (aethryn.com "Nanochat: full-stack LLM training
    * in 8,000 lines for $72", section "A Llama-class transformer with ten
    * modern departures": the "SSSL" pattern, three short-window layers then one
@@ -185,11 +197,45 @@ const char* gpt_kernel_tag_name(int32_t tag);
 
 /* Debug access to a stashed activation of the last forward: device pointer and
  * byte size of the named buffer ("x", "h1", "qkv", "o", "lse", "h2", "a",
- * "hf", "logits", "rstd0") for `layer` (ignored by non-layer buffers). The
- * pointer aliases the workspace and is valid until the next call. "lse" holds
- * the attention log-sum-exp per (batch row, head, position) in base 2, i.e.
- * ln(sum) * log2(e), fp32 [B, H, T]. */
+ * "hf", "logits", "rstd0"; FP8 models also "amax") for `layer` (ignored by
+ * non-layer buffers). The pointer aliases the workspace and is valid until
+ * the next call. "lse" holds the attention log-sum-exp per (batch row, head,
+ * position) in base 2, i.e. ln(sum) * log2(e), fp32 [B, H, T]. "amax" holds
+ * the layer's 16 fp32 |max| slots of the FP8 operands: h1, o, h2, a (forward
+ * inputs of the QKV, O, W1, W2 products), the output gradients of W2 and W1
+ * (d(out) of the MLP, du), of O and of QKV, then W_qkv, W_o, W_1, W_2, then 4
+ * unused. */
 gpt_status gpt_debug_buffer(gpt_model* m, const char* name, int32_t layer, void** ptr, size_t* bytes);
+
+/* The per-tensor e4m3 quantisation FP8 models apply to every QKV / O / MLP
+ * operand (see GPT_FP8_E4M3), exposed on its own. x: device bf16 [rows, cols]
+ * row-major, cols a multiple of 16. Sets *amax (device fp32) to max|x|, then
+ * writes codes e4m3(clamp(x * s, -448, 448)), s = 448 / amax computed in fp32
+ * (1 if amax is 0), round to nearest even: q (device, may be NULL) [rows, cols]
+ * row-major; qT (device, may be NULL) [cols, ldT] transposed, with columns
+ * rows..ldT-1 set to code 0 (ldT >= rows, a multiple of 16). Codes: bit 7
+ * sign, bits 6..3 exponent (bias 7), bits 2..0 mantissa; 0x7f NaN. All
+ * buffers are caller-owned, 16-byte aligned (amax 4-byte). GPT_E_INVALID_ARG
+ * on bad sizes or pointers. Asynchronous on `stream`. */
+gpt_status gpt_fp8_quantize(const void* x, int64_t rows, int64_t cols, uint8_t* q, uint8_t* qT, int64_t ldT,
+                            float* amax, void* stream);
+
+/* The e4m3 matmul FP8 models run for their QKV / O / MLP products (see
+ * GPT_FP8_E4M3), exposed on its own: out[m, n] = sum_k (a[m, k] / s_a) *
+ * (b[n, k] / s_b), with a, b e4m3 codes as gpt_fp8_quantize writes them (a
+ * [M, K] and b [N, K], both k-contiguous, row pitches lda, ldb >= K,
+ * multiples of 16) and s = 448 / *amax (1 if *amax is 0) read from the device
+ * fp32 slots amax_a, amax_b. The products accumulate in fp32. out: device
+ * [M, N], row pitch ldo >= N (a multiple of 4), fp32 (out_dtype GPT_F32) or
+ * bf16 rounded to nearest even (GPT_BF16). K must be a multiple of 128, N of
+ * 4; all pointers 16-byte aligned. tile: 0 picks the tile by shape, 1..3
+ * force 256x256, 256x128, 128x128. splits > 1 (fp32 output only) splits K
+ * into that many slices whose partial sums go to `partials` (device fp32
+ * [splits, M, N], caller-owned) and are added in slice order.
+ * GPT_E_INVALID_ARG on bad sizes or pointers. Asynchronous on `stream`. */
+gpt_status gpt_fp8_matmul(const uint8_t* a, int64_t lda, const float* amax_a, const uint8_t* b, int64_t ldb,
+                          const float* amax_b, int32_t M, int32_t N, int32_t K, int32_t out_dtype, void* out,
+                          int64_t ldo, int32_t tile, int32_t splits, float* partials, void* stream);
 
 #ifdef __cplusplus
 }

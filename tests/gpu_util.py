@@ -29,6 +29,7 @@ def oracle_cfg(c: _lib.gpt_config) -> dict:
     d["rope_theta"] = float(np.float32(d["rope_theta"]))
     d["logit_softcap"] = float(np.float32(d["logit_softcap"]))
     d["norm_eps"] = float(np.float32(d["norm_eps"]))
+    d["fp8"] = c.dtype == _lib.GPT_FP8_E4M3
     return d
 
 
@@ -38,7 +39,7 @@ class Case:
     def __init__(self, cfg: _lib.gpt_config, B: int, T: int, law: str, wseed: int = 0, tseed: int = 1):
         self.cfg, self.B, self.T, self.law = cfg, B, T, law
         self.shapes = [(n, r, c) for n, _, r, c in _lib.gpt_param_layout(cfg)]
-        dt = "bf16" if cfg.dtype == _lib.GPT_BF16 else "f32"
+        dt = "f32" if cfg.dtype == _lib.GPT_F32 else "bf16"  # FP8 models keep bf16 parameters
         self.storage, self.values = synthetic.make_weights(self.shapes, seed=wseed, dtype=dt)
         self.idx, self.tgt = synthetic.make_tokens(B, T, cfg.vocab_size, law, seed=tseed)
 

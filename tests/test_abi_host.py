@@ -16,7 +16,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def header_functions():
     src = open(os.path.join(ROOT, "include", "gpt.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(gpt_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(gpt_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_library_exports_every_declared_function():
@@ -144,3 +144,28 @@ def test_window_pattern_validation():
     c.window_pattern = b"L"
     c.window_short = 0
     assert _lib.gpt_config_validate(c) == _lib.GPT_OK
+
+
+def test_fp8_config_and_workspace():
+    c8 = _lib.gpt_config_from_depth(24, _lib.GPT_FP8_E4M3)
+    cb = _lib.gpt_config_from_depth(24, _lib.GPT_BF16)
+    assert _lib.gpt_config_validate(c8) == _lib.GPT_OK
+    assert _lib.gpt_param_count(c8) == _lib.gpt_param_count(cb)
+    # FP8 adds e4m3 weight copies and token-major operand codes
+    w8, wb = _lib.gpt_workspace_bytes(c8, 2, 2048), _lib.gpt_workspace_bytes(cb, 2, 2048)
+    assert w8 > wb + 2 * _lib.gpt_param_count(c8) - 2 * 2 * 65536 * 1536
+    bad = _lib.gpt_config_from_depth(4, _lib.GPT_BF16)
+    bad.dtype = 3
+    assert _lib.gpt_config_validate(bad) == _lib.GPT_E_UNSUPPORTED
+
+
+def test_fp8_quantize_argument_errors():
+    f = _lib.lib().gpt_fp8_quantize
+    buf = ctypes.create_string_buffer(4096 + 16)
+    p = (ctypes.addressof(buf) + 15) // 16 * 16
+    # NULL input, no output, cols not a multiple of 16, ldT < rows, misaligned: all rejected on the host
+    assert f(None, 4, 16, p, None, 0, p, None) == _lib.GPT_E_INVALID_ARG
+    assert f(p, 4, 16, None, None, 0, p, None) == _lib.GPT_E_INVALID_ARG
+    assert f(p, 4, 24, p, None, 0, p, None) == _lib.GPT_E_INVALID_ARG
+    assert f(p, 40, 16, None, p, 32, p, None) == _lib.GPT_E_INVALID_ARG
+    assert f(p + 2, 4, 16, p, None, 0, p, None) == _lib.GPT_E_INVALID_ARG

@@ -1,0 +1,241 @@
+"""FP8 (e4m3) models and the per-tensor quantiser, through the C ABI, against
+the float64 oracle's FP8 reading (per-tensor current scaling, round to nearest
+even with saturation, output gradients quantised, straight-through backward).
+
+Quantiser: codes bit-exact, amax exact (both sides decide the code from the
+bf16 operand in fp32). Matmul on the same codes: fp32 accumulation, checked
+elementwise against the float64 product of the dequantised codes.
+
+Whole step: |dloss|/loss <= 5e-3 and per-tensor gradient cosine >= 0.996.
+The cosine bar is derived, not tuned: the GPU and the oracle feed the
+quantiser slightly different values (the bf16 pipeline's own differences, up
+to the relative error eps ~ 4.5 % that the bf16 bar of cosine 0.999 admits).
+e4m3's step is 1/8..1/16 of the value, so a difference eps flips a code with
+probability ~12 eps, by one step (~value/12): the dequantised operands then
+differ by sqrt(eps/12) ~ 6.1 % RMS each, a weight gradient (two such
+operands) by ~8.7 %, i.e. cosine 1 - 0.087^2/2 = 0.996."""
+import numpy as np
+import pytest
+
+from decoder_only_transformer_gpt_amd import _lib, synthetic
+from oracle import gpt_oracle as O
+
+import gpu_util as U
+pytestmark = pytest.mark.gpu
+
+FP8_COS = 0.996
+
+
+def check_fp8(case, gpu, loss, G, label):
+    rel = abs(gpu["loss"] - loss) / abs(loss)
+    U.log(f"[{label}] loss gpu={gpu['loss']:.6f} oracle={loss:.6f} rel={rel:.2e}")
+    assert rel <= 5e-3
+    gg = U.split_tensors(case, gpu["grads"])
+    go = U.split_tensors(case, case.flat_grads(G))
+    cos = {k: U.cosine(gg[k], go[k]) for k in go}
+    U.log(f"[{label}] gradient cosines: " + " ".join(f"{k}={v:.5f}" for k, v in cos.items()))
+    for k, v in cos.items():
+        assert v >= FP8_COS, k
+
+
+def fp8_cfg(depth=4):
+    return _lib.gpt_config_from_depth(depth, _lib.GPT_FP8_E4M3)
+
+
+def _bf16_tensor(rng, rows, cols, scale):
+    bits = synthetic.f32_to_bf16_bits((rng.standard_normal((rows, cols)) * scale).astype(np.float32))
+    return bits, synthetic.bf16_bits_to_f32(bits)
+
+
+def _quantize_gpu(torch, bits, ldT):
+    rows, cols = bits.shape
+    x = torch.from_numpy(bits.view(np.int16)).cuda()
+    q = torch.full((max(rows, 1), cols), 0x55, dtype=torch.uint8, device="cuda")
+    qT = torch.full((cols, max(ldT, 1)), 0x55, dtype=torch.uint8, device="cuda")
+    amax = torch.full((1,), -1.0, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    _lib.gpt_fp8_quantize(x.data_ptr(), rows, cols, q.data_ptr(), qT.data_ptr(), ldT, amax.data_ptr(), stream)
+    torch.cuda.synchronize()
+    return q.cpu().numpy()[:rows], qT.cpu().numpy(), float(amax.item())
+
+
+@pytest.mark.parametrize("rows,cols,scale,ldT", [(999, 1536, 1.0, 1024), (64, 16, 3e-3, 64), (1, 32, 50.0, 16),
+                                                 (130, 6144, 0.02, 256), (2048, 1664, 7.0, 2048)])
+def test_quantize_bit_exact(rows, cols, scale, ldT):
+    torch = U.require_gpu()
+    rng = np.random.default_rng(rows * 7 + cols)
+    bits, vals = _bf16_tensor(rng, rows, cols, scale)
+    U.log(f"case fp8 quantize rows={rows} cols={cols} scale={scale} ldT={ldT}")
+    q, qT, amax = _quantize_gpu(torch, bits, ldT)
+    codes, s = O.fp8_quantize(vals)
+    assert amax == float(np.max(np.abs(vals)))
+    np.testing.assert_array_equal(q, codes)
+    np.testing.assert_array_equal(qT[:, :rows], codes.T)
+    assert not qT[:, rows:ldT].any()
+
+
+def test_quantize_ties_saturation_and_zero():
+    """Values that land exactly on e4m3 midpoints (ties to even), the largest
+    magnitude (448 after scaling), tiny values in the subnormal range, and an
+    all-zero tensor (scale 1, zero codes)."""
+    torch = U.require_gpu()
+    grid = O.e4m3_decode(np.arange(0x7F))
+    mids = ((grid[:-1] + grid[1:]) / 2).astype(np.float32)        # exact in bf16 (<= 4 mantissa bits)
+    vals = np.concatenate([mids, -mids, grid.astype(np.float32), [448.0], np.zeros(1, np.float32)])
+    vals = np.resize(vals, 32 * 16).reshape(32, 16).astype(np.float32)
+    vals[0, 0] = -448.0                                            # amax 448: s = 1 exactly
+    bits = synthetic.f32_to_bf16_bits(vals)
+    assert np.array_equal(synthetic.bf16_bits_to_f32(bits), vals)
+    q, qT, amax = _quantize_gpu(torch, bits, 32)
+    codes, s = O.fp8_quantize(vals)
+    assert s == 1.0 and amax == 448.0
+    np.testing.assert_array_equal(q, codes)
+    np.testing.assert_array_equal(qT, codes.T)
+    zq, zqT, zam = _quantize_gpu(torch, np.zeros((16, 32), np.uint16), 16)
+    assert zam == 0.0 and not zq.any() and not zqT.any()
+
+
+def _codes(torch, vals_bits, ldT=16):
+    """Quantise a bf16 tensor on the GPU; returns (device codes, device amax)."""
+    rows, cols = vals_bits.shape
+    x = torch.from_numpy(vals_bits.view(np.int16)).cuda()
+    q = torch.empty((rows, cols), dtype=torch.uint8, device="cuda")
+    amax = torch.empty((1,), dtype=torch.float32, device="cuda")
+    _lib.gpt_fp8_quantize(x.data_ptr(), rows, cols, q.data_ptr(), None, 0, amax.data_ptr(),
+                          torch.cuda.current_stream().cuda_stream)
+    return q, amax
+
+
+@pytest.mark.parametrize("M,N,K,out,tile,splits", [
+    (999, 1536, 1024, "bf16", 0, 1), (999, 1536, 1024, "bf16", 1, 1), (999, 1536, 1024, "bf16", 2, 1),
+    (999, 1536, 1024, "bf16", 3, 1), (300, 260, 384, "f32", 3, 1), (1536, 768, 4096, "f32", 1, 4),
+    (640, 512, 2048, "f32", 0, 3), (33, 64, 128, "bf16", 0, 1)])
+def test_fp8_matmul_on_identical_codes(M, N, K, out, tile, splits):
+    """The e4m3 GEMM against the float64 product of the same dequantised codes
+    (the oracle's codes equal the GPU's: checked bit for bit above), ragged M
+    and N, every tile variant, split-K. Bound per element: the fp32
+    accumulation, held to 2^-16 of sum |a b| (K-term fp32 summation could reach
+    K * 2^-24 of it in the worst case; normal data stays far below), plus the
+    bf16 output rounding (half an ulp: 2^-8 |ref|)."""
+    torch = U.require_gpu()
+    rng = np.random.default_rng(M + N + K)
+    ab, av = _bf16_tensor(rng, M, K, 1.0)
+    bb, bv = _bf16_tensor(rng, N, K, 0.05)
+    qa, am_a = _codes(torch, ab)
+    qb, am_b = _codes(torch, bb)
+    odt = torch.float32 if out == "f32" else torch.bfloat16
+    o = torch.full((M, N), float("nan"), dtype=odt, device="cuda")
+    part = torch.empty((splits, M, N), dtype=torch.float32, device="cuda") if splits > 1 else None
+    U.log(f"case fp8 matmul M={M} N={N} K={K} out={out} tile={tile} splits={splits}")
+    _lib.gpt_fp8_matmul(qa.data_ptr(), K, am_a.data_ptr(), qb.data_ptr(), K, am_b.data_ptr(), M, N, K,
+                        _lib.GPT_F32 if out == "f32" else _lib.GPT_BF16, o.data_ptr(), N, tile, splits,
+                        None if part is None else part.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    got = o.float().cpu().numpy().astype(np.float64)
+    ca, sa = O.fp8_quantize(av)
+    cb, sb = O.fp8_quantize(bv)
+    np.testing.assert_array_equal(qa.cpu().numpy(), ca)
+    da, db = O.fp8_dequantize(ca, sa), O.fp8_dequantize(cb, sb)
+    ref = da @ db.T
+    mag = np.abs(da) @ np.abs(db).T
+    bound = 2.0 ** -16 * mag + (2.0 ** -8 * np.abs(ref) if out == "bf16" else 0.0)
+    err = np.abs(got - ref)
+    U.log(f"[fp8-matmul] max err / sum|ab| = {np.max(err / np.maximum(mag, 1e-30)):.2e}, "
+          f"max err / bound = {np.max(err / np.maximum(bound, 1e-300)):.3f}")
+    assert np.all(err <= bound)
+
+
+@pytest.mark.parametrize("tile", [0, 1, 2, 3])
+def test_d4_fp8_full_step(tile):
+    U.require_gpu()
+    case = U.Case(fp8_cfg(), B=4, T=512, law="uniform")
+    U.log(f"case d4 fp8 B=4 T=512 uniform gemm tile {tile}")
+    gpu = U.run_gpu(case, tile=tile)
+    assert gpu["status"] == _lib.GPT_OK
+    loss, rows, G = O.step(U.oracle_cfg(case.cfg), case.oracle_params(), case.idx, case.tgt)
+    check_fp8(case, gpu, loss, G, "d4-fp8")
+
+
+@pytest.mark.parametrize("tile", [0, 3])
+def test_fp8_ragged_zipf_accumulate(tile):
+    """Ragged token count (N = 999: the token-major codes are padded to 1,024),
+    Zipf ids, and gradient accumulation over two identical steps."""
+    torch = U.require_gpu()
+    case = U.Case(fp8_cfg(), B=3, T=333, law="zipf", wseed=2, tseed=3)
+    U.log(f"case d4 fp8 ragged B=3 T=333 zipf gemm tile {tile}, accumulate")
+    from decoder_only_transformer_gpt_amd.model import GPT
+    m = GPT(case.cfg, GPT.params_from_numpy(case.storage, case.cfg), 3, 333)
+    if tile:
+        m.set_gemm_tile(tile)
+    idx, tgt = torch.from_numpy(case.idx).cuda(), torch.from_numpy(case.tgt).cuda()
+    m.forward_loss(idx, tgt)
+    m.backward(0.5, accumulate=False)
+    m.forward_loss(idx, tgt)
+    m.backward(1.5, accumulate=True)
+    torch.cuda.synchronize()
+    assert m.sync_status() == _lib.GPT_OK
+    loss, _, G = O.step(U.oracle_cfg(case.cfg), case.oracle_params(), case.idx, case.tgt, dloss=2.0)
+    gpu = dict(loss=float(m.loss.item()), grads=m.grads.cpu().numpy().astype(np.float64))
+    check_fp8(case, gpu, loss, G, "d4-fp8-ragged")
+
+
+def test_fp8_amax_slots_and_differs_from_bf16():
+    """The stashed |max| slots hold exactly the maxima of the bf16 operands
+    (activations from the debug buffers, weights from the seeded values), and
+    FP8 changes the result relative to the bf16 model on the same inputs."""
+    torch = U.require_gpu()
+    case = U.Case(fp8_cfg(), B=2, T=256, law="uniform", wseed=4, tseed=5)
+    gpu = U.run_gpu(case)
+    m = gpu["model"]
+    C, F, N = case.cfg.model_dim, case.cfg.mlp_dim, 2 * 256
+    P = case.oracle_params()
+    for l in range(case.cfg.n_layer):
+        am = m.debug_tensor("amax", l, (16,), torch.float32).cpu().numpy()
+        h1 = m.debug_tensor("h1", l, (N, C), torch.bfloat16).float().cpu().numpy()
+        a = m.debug_tensor("a", l, (N, F), torch.bfloat16).float().cpu().numpy()
+        assert am[0] == np.abs(h1).max() and am[3] == np.abs(a).max()
+        for k, w in enumerate(["w_qkv", "w_o", "w_1", "w_2"]):
+            assert am[8 + k] == np.abs(P[f"h{l}.{w}"]).max()
+        assert np.all(am[:12] > 0) and np.all(np.isfinite(am))
+    bf = U.Case(_lib.gpt_config_from_depth(4, _lib.GPT_BF16), B=2, T=256, law="uniform", wseed=4, tseed=5)
+    g_bf = U.run_gpu(bf)
+    assert gpu["loss"] != g_bf["loss"] and abs(gpu["loss"] - g_bf["loss"]) / g_bf["loss"] < 1e-2
+
+
+@pytest.mark.timeout(900)
+def test_d24fp8_one_row():
+    """The FP8 configuration's shape (d24: width 1536, 12 heads, MLP 6144), one
+    2,048-token row, the whole step against the oracle."""
+    U.require_gpu()
+    case = U.Case(fp8_cfg(24), B=1, T=2048, law="zipf")
+    U.log("case d24 fp8 B=1 T=2048 zipf")
+    gpu = U.run_gpu(case)
+    assert gpu["status"] == _lib.GPT_OK
+    loss, rows, G = O.step(U.oracle_cfg(case.cfg), case.oracle_params(), case.idx, case.tgt)
+    check_fp8(case, gpu, loss, G, "d24-fp8-B1")
+
+
+@pytest.mark.timeout(900)
+def test_d24fp8_full_batch():
+    """The FP8 configuration at its full batch (B=16, T=2048): finite loss and
+    gradients, loss = mean of the per-position losses, and two sampled rows'
+    mean losses within the quantisation noise (rel 1e-2) of the oracle's
+    unquantised forward of just those rows (per-tensor scales couple the rows,
+    so the unquantised forward is the row-local reference)."""
+    U.require_gpu()
+    c = fp8_cfg(24)
+    case = U.Case(c, B=16, T=2048, law="zipf")
+    U.log("case d24 fp8 B=16 T=2048 zipf (full batch)")
+    gpu = U.run_gpu(case)
+    assert gpu["status"] == _lib.GPT_OK
+    assert np.isfinite(gpu["loss"]) and np.all(np.isfinite(gpu["grads"]))
+    rows_gpu = gpu["row_loss"].reshape(16, 2048)
+    assert gpu["loss"] == pytest.approx(rows_gpu.mean(), rel=1e-5)
+    ocfg = dict(U.oracle_cfg(c), fp8=False)
+    P = case.oracle_params()
+    for b in (int(np.random.default_rng(8).integers(0, 16)), 15):
+        r = O.forward_rows(ocfg, P, case.idx[b:b + 1], case.tgt[b:b + 1])[0]
+        rel = abs(rows_gpu[b].mean() - r.mean()) / r.mean()
+        U.log(f"[d24-fp8-B16] row {b}: mean loss gpu={rows_gpu[b].mean():.5f} unquantised oracle={r.mean():.5f} "
+              f"rel={rel:.2e}")
+        assert rel <= 1e-2
