@@ -26,6 +26,10 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CUs x 4096 FLOP/clk x 2.4 GHz ("2.5 PFLOP/s")
 PEAK_FP32_TFLOPS = 157.3
+PEAK_FP8_TFLOPS = 5033.2    # dense fp8 (e4m3) MFMA, twice the bf16 rate
+# call sites whose operands are e4m3 codes in FP8 models
+FP8_TAGS = ("gemm_qkv", "gemm_o", "gemm_w1_relu2", "gemm_w2", "gemm_w2_dw", "gemm_w2_dx", "gemm_w1_dw",
+            "gemm_w1_dx_relu2bwd", "gemm_o_dw", "gemm_o_dx", "gemm_qkv_dw", "gemm_qkv_dx")
 PEAK_HBM_GBS = 8000.0
 METRIC = "train tokens/sec + bf16 MFU, d20 fwd+bwd, seq 2048, 1 MI355X"
 
@@ -89,8 +93,14 @@ def kernel_flops_per_launch(tag: str, cfg, B: int, T: int) -> float | None:
 
 def kernel_bytes_per_launch(tag: str, cfg, B: int, T: int, es: int) -> float | None:
     """Algorithmic HBM bytes of one launch of a memory-bound kernel."""
-    N, C, H, V = B * T, cfg.model_dim, cfg.n_head, cfg.vocab_size
-    b = {"embed_rmsnorm": N * (4 + 2 * C * es + 4), "rmsnorm": N * (2 * C * es + 4),
+    N, C, H, V, F = B * T, cfg.model_dim, cfg.n_head, cfg.vocab_size, cfg.mlp_dim
+    # FP8 operand passes: per layer the forward quantises h1, o, h2, a and the
+    # backward dy (twice), du, dqkv -- 8 tensors, N (4C + 2F + (H+2)128)
+    # elements in all; per launch the mean. amax reads each element (bf16),
+    # the quantiser reads it and writes two codes.
+    q_elems = N * (4 * C + 2 * F + (H + 2) * 128) / 8
+    b = {"fp8_amax": 2 * q_elems, "fp8_quantize": 4 * q_elems,
+         "embed_rmsnorm": N * (4 + 2 * C * es + 4), "rmsnorm": N * (2 * C * es + 4),
          "rope_qknorm": N * (2 * (H + 1) * 128 * es + 4 * (H + 1)),
          "ce_bwd": N * (2 * V * es + 8), "rmsnorm_bwd": N * (2 * C * es + 8 * C + C * es + 4),
          "rope_qknorm_bwd": N * (3 * (H + 1) * 128 * es + 4 * (H + 1)),
@@ -123,6 +133,7 @@ def cpu_baseline(cfg_lib, seconds_hint: float = 20.0) -> dict:
         off += r * c
     oc = cfg_lib.as_dict()
     oc["norm_eps"] = float(np.float32(oc["norm_eps"]))
+    oc["fp8"] = cfg_lib.dtype == _lib.GPT_FP8_E4M3
     t0 = time.perf_counter()
     O.step(oc, P, idx, tgt)
     dt = time.perf_counter() - t0
@@ -136,8 +147,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="d20", choices=["tiny", "d4", "d12", "d20", "d20-sssl"])
+    ap.add_argument("--workload", default="d20", choices=["tiny", "d4", "d12", "d20", "d20-sssl", "d24fp8"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--gemm-tile", type=int, default=0, choices=[0, 1, 2, 3],
+                    help="force one GEMM tile variant (0 = by shape)")
     ap.add_argument("--kernel-table", action="store_true", help="print per-tag timings to stderr")
     ap.add_argument("--dominant", default=None,
                     help="kernel tag to report in the roofline (skips the one-step-per-tag scan)")
@@ -162,9 +175,11 @@ def main():
     B, T = wl.batch, wl.seq_len
     torch.cuda.set_device(0)
     shapes = [(n, r, c) for n, _, r, c in _lib.gpt_param_layout(cfg)]
-    storage, _ = synthetic.make_weights(shapes, seed=0, dtype=wl.dtype)
+    storage, _ = synthetic.make_weights(shapes, seed=0, dtype="f32" if wl.dtype == "f32" else "bf16")
     idx_np, tgt_np = synthetic.make_tokens(B, T, cfg.vocab_size, wl.tokens, seed=1)
     m = GPT(cfg, GPT.params_from_numpy(storage, cfg), B, T)
+    if args.gemm_tile:
+        m.set_gemm_tile(args.gemm_tile)
     idx = torch.from_numpy(idx_np).cuda()
     tgt = torch.from_numpy(tgt_np).cuda()
     print(f"[bench] workload {wl.name}: B={B} T={T} params={_lib.gpt_param_count(cfg)} "
@@ -203,7 +218,8 @@ def main():
         tot = sum(v[0] for v in per_tag.values())
         for t, (ms, n) in sorted(per_tag.items(), key=lambda kv: -kv[1][0]):
             f = kernel_flops_per_launch(t, cfg, B, T)
-            rate = f"{f * n / ms / 1e9:8.1f} TFLOP/s" if f else ""
+            kb = kernel_bytes_per_launch(t, cfg, B, T, 4 if wl.dtype == "f32" else 2)
+            rate = f"{f * n / ms / 1e9:8.1f} TFLOP/s" if f else (f"{kb * n / ms / 1e6:8.1f} GB/s" if kb else "")
             print(f"[bench] {t:24s} {ms:9.3f} ms {n:4d} launches {100 * ms / tot:5.1f}% {rate}",
                   file=sys.stderr, flush=True)
 
@@ -227,10 +243,12 @@ def main():
     fl = step_flops(cfg, T)
     mfu = fl["total"] * tok_s / (PEAK_BF16_TFLOPS * 1e12)
     avg_ms = dom_ms / max(dom_n, 1)
-    es = 2 if wl.dtype == "bf16" else 4
+    es = 4 if wl.dtype == "f32" else 2
     kf = kernel_flops_per_launch(dominant, cfg, B, T)
     if kf is not None:
-        peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP32_TFLOPS
+        peak = PEAK_FP32_TFLOPS if wl.dtype == "f32" else PEAK_BF16_TFLOPS
+        if wl.dtype == "fp8" and dominant in FP8_TAGS:
+            peak = PEAK_FP8_TFLOPS
         achieved = kf / (avg_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": None}
@@ -247,7 +265,8 @@ def main():
     out = {
         "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(1e3 * elapsed / args.steps, 3), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8-e4m3 (QKV/O/MLP) + bf16" if wl.dtype == "fp8" else wl.dtype, "data": "synthetic",
         "config": {"workload": f"{wl.name}: depth {cfg.n_layer}, width {cfg.model_dim}, {cfg.n_head} query heads / "
                                f"1 kv head, head_dim 128, MLP {cfg.mlp_dim}, vocab {cfg.vocab_size}"
                                + (f", windows {wl.window_pattern} (short {wl.window_short})" if wl.window_pattern

@@ -16,6 +16,8 @@
 // lane out row-major, and the transpose through a byte tile in LDS so that
 // the transposed copy is also written 16 bytes per lane.
 
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -33,19 +35,24 @@ DEV int find_desc(const QuantDesc* table, int n) {
   return t;
 }
 
+// A single tensor runs on a capped grid, each block striding over chunks of
+// kAmaxElemsPerBlock elements, so that few blocks contend for the one atomic
+// slot; a batched table gives every tensor one block per chunk.
 __global__ __launch_bounds__(256) void amax_kernel(const QuantDesc* __restrict__ table, int n, QuantDesc one) {
   const QuantDesc d = table ? table[find_desc<true>(table, n)] : one;
   const int64_t ne = (int64_t)d.rows * d.cols;
-  const int64_t base = ((int64_t)blockIdx.x - d.amax_block0) * kAmaxElemsPerBlock;
+  const int64_t stride = table ? (int64_t)1 << 62 : (int64_t)gridDim.x * kAmaxElemsPerBlock;
   float m = 0.f;
+  for (int64_t base = ((int64_t)blockIdx.x - d.amax_block0) * kAmaxElemsPerBlock; base < ne; base += stride) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int64_t e = base + ((int64_t)i * 256 + threadIdx.x) * 8;
-    if (e < ne) {
-      float v[8];
-      load8(reinterpret_cast<const bf16*>(d.src) + e, v);
+    for (int i = 0; i < 8; ++i) {
+      const int64_t e = base + ((int64_t)i * 256 + threadIdx.x) * 8;
+      if (e < ne) {
+        float v[8];
+        load8(reinterpret_cast<const bf16*>(d.src) + e, v);
 #pragma unroll
-      for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(v[k]));
+        for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(v[k]));
+      }
     }
   }
   m = wave_max(m);
@@ -118,7 +125,7 @@ hipError_t launch_fp8_amax(const QuantDesc& d, hipStream_t s) {
   if (d.ld != d.cols) return hipErrorInvalidValue;  // the amax pass streams a contiguous tensor
   QuantDesc one = d;
   one.amax_block0 = 0;
-  const int64_t nb = amax_blocks(d);
+  const int64_t nb = std::min<int64_t>(amax_blocks(d), 1024);
   if (nb == 0) return hipSuccess;
   hipLaunchKernelGGL(amax_kernel, dim3((unsigned)nb), dim3(256), 0, s, (const QuantDesc*)nullptr, 0, one);
   return hipGetLastError();

@@ -288,6 +288,16 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs args) {
 // private [32][WN+4] fp32 region, then reads it back with WN/4 lanes per row
 // and hands each lane 4 consecutive columns: op(m, n, v[4]). The +4 pitch
 // keeps both the slab writes and the row reads free of bank conflicts.
+// The staging slab is private to the wave, so its LDS writes and reads only
+// need ordering within the wave (LDS instructions of one wave complete in
+// order): a wave-scope fence keeps the compiler from moving them across each
+// other, and no block barrier holds the other waves back.
+DEV void slab_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 template <int TM, int TN, int WN, class Op>
 DEV void staged_store(f32x16 (&acc)[TM][TN], float* st, int mbase, int nbase, int lane, Op op) {
   constexpr int P = WN + 4, LPR = WN / 4, RPP = 64 / LPR;
@@ -301,7 +311,7 @@ DEV void staged_store(f32x16 (&acc)[TM][TN], float* st, int mbase, int nbase, in
         float v[4] = {acc[i][j][blk * 4], acc[i][j][blk * 4 + 1], acc[i][j][blk * 4 + 2], acc[i][j][blk * 4 + 3]};
         store4(st + l32 * P + j * 32 + blk * 8 + g * 4, v);
       }
-    __syncthreads();
+    slab_sync();
 #pragma unroll
     for (int r0 = 0; r0 < 32; r0 += RPP) {
       const int row = r0 + lane / LPR, col = (lane % LPR) * 4;
@@ -309,24 +319,33 @@ DEV void staged_store(f32x16 (&acc)[TM][TN], float* st, int mbase, int nbase, in
       load4(st + row * P + col, v);
       op(mbase + i * 32 + row, nbase + col, v);
     }
-    __syncthreads();
+    slab_sync();
   }
 }
 
 // staged_store with a prefetch: pre(m, n) is issued for every (row, 4
-// columns) item of a slab before the slab's accumulators go to LDS, so those
-// global loads are in flight during the staging; op(m, n, v, pre_value).
-template <int TM, int TN, int WN, class Pre, class Op>
+// columns) item before the accumulators go to LDS, so those global loads are
+// in flight during the staging; op(m, n, v, pre_value). ALL: every slab's
+// items are requested up front (the whole tile's loads overlap), else one
+// slab's at a time.
+template <int TM, int TN, int WN, bool ALL = false, class Pre, class Op>
 DEV void staged_store_pre(f32x16 (&acc)[TM][TN], float* st, int mbase, int nbase, int lane, Pre pre, Op op) {
   constexpr int P = WN + 4, LPR = WN / 4, RPP = 64 / LPR, NP = 32 / RPP;
   using PV = decltype(pre(0, 0));
   const int g = lane >> 5, l32 = lane & 31;
   const int prow = lane / LPR, pcol = (lane % LPR) * 4;
+  PV pall[ALL ? TM : 1][NP];
+  if constexpr (ALL) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int q = 0; q < NP; ++q) pall[i][q] = pre(mbase + i * 32 + q * RPP + prow, nbase + pcol);
+  }
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
     PV pv[NP];
 #pragma unroll
-    for (int q = 0; q < NP; ++q) pv[q] = pre(mbase + i * 32 + q * RPP + prow, nbase + pcol);
+    for (int q = 0; q < NP; ++q) pv[q] = ALL ? pall[ALL ? i : 0][q] : pre(mbase + i * 32 + q * RPP + prow, nbase + pcol);
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
@@ -334,7 +353,7 @@ DEV void staged_store_pre(f32x16 (&acc)[TM][TN], float* st, int mbase, int nbase
         float v[4] = {acc[i][j][blk * 4], acc[i][j][blk * 4 + 1], acc[i][j][blk * 4 + 2], acc[i][j][blk * 4 + 3]};
         store4(st + l32 * P + j * 32 + blk * 8 + g * 4, v);
       }
-    __syncthreads();
+    slab_sync();
 #pragma unroll
     for (int q = 0; q < NP; ++q) {
       const int row = q * RPP + prow;
@@ -342,7 +361,7 @@ DEV void staged_store_pre(f32x16 (&acc)[TM][TN], float* st, int mbase, int nbase
       load4(st + row * P + pcol, v);
       op(mbase + i * 32 + row, nbase + pcol, v, pv[q]);
     }
-    __syncthreads();
+    slab_sync();
   }
 }
 
@@ -407,14 +426,25 @@ struct Epilogue<T, Epi::Relu2Bwd> {
   static DEV void run(const GemmArgs& a, f32x16 (&acc)[TM][TN], float* lds, int mbase, int nbase, int lane) {
     T* Dp = reinterpret_cast<T*>(a.C);
     const T* A2 = reinterpret_cast<const T*>(a.C2);
+    // a is prefetched raw (4 bf16 in two dwords) for the whole tile
     auto pre = [&](int m, int n) {
-      float x[4] = {0.f, 0.f, 0.f, 0.f};
-      if (m < a.M && n < a.N) load4(A2 + (int64_t)m * a.ldc2 + n, x);
-      return f32x4{x[0], x[1], x[2], x[3]};
+      u32x2 r = {0u, 0u};
+      if constexpr (sizeof(T) == 2) {
+        if (m < a.M && n < a.N) r = ld8(A2 + (int64_t)m * a.ldc2 + n);
+      }
+      return r;
     };
-    staged_store_pre<TM, TN, WN>(acc, lds, mbase, nbase, lane, pre, [&](int m, int n, float (&v)[4], f32x4 x) {
+    staged_store_pre<TM, TN, WN, sizeof(T) == 2>(acc, lds, mbase, nbase, lane, pre,
+                                                 [&](int m, int n, float (&v)[4], u32x2 r) {
       if (m < a.M && n < a.N) {
-        for (int r = 0; r < 4; ++r) v[r] *= 2.f * sqrtf(x[r]);
+        float x[4];
+        if constexpr (sizeof(T) == 2) {
+          x[0] = __uint_as_float(r[0] << 16); x[1] = __uint_as_float(r[0] & 0xffff0000u);
+          x[2] = __uint_as_float(r[1] << 16); x[3] = __uint_as_float(r[1] & 0xffff0000u);
+        } else {
+          load4(A2 + (int64_t)m * a.ldc2 + n, x);
+        }
+        for (int q = 0; q < 4; ++q) v[q] *= 2.f * sqrtf(x[q]);
         store4(Dp + (int64_t)m * a.ldc + n, v);
       }
     });
