@@ -185,13 +185,14 @@ def causal_mqa_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, window: in
     o = np.empty_like(q)
     lse = np.empty((B, H, T))
     for b in range(B):
-        s = np.einsum("thd,ud->htu", q[b], k[b]) * scale
+        qh = q[b].transpose(1, 0, 2)                      # [H, T, D]
+        s = (qh @ k[b].T) * scale                          # [H, T(query), T(key)]
         s = np.where(mask[None], s, -np.inf)
         m = s.max(axis=-1, keepdims=True)
         e = np.exp(s - m)
         z = e.sum(axis=-1, keepdims=True)
         p = e / z
-        o[b] = np.einsum("htu,ud->thd", p, v[b])
+        o[b] = (p @ v[b]).transpose(1, 0, 2)
         lse[b] = (m + np.log(z))[..., 0]
     return o, lse
 
@@ -209,15 +210,16 @@ def causal_mqa_attention_bwd(do, q, k, v, window: int | None = None):
     dk = np.empty_like(k)
     dv = np.empty_like(v)
     for b in range(B):
-        s = np.einsum("thd,ud->htu", q[b], k[b]) * scale
+        qh, doh = q[b].transpose(1, 0, 2), do[b].transpose(1, 0, 2)   # [H, T, D]
+        s = (qh @ k[b].T) * scale
         s = np.where(mask[None], s, -np.inf)
         e = np.exp(s - s.max(axis=-1, keepdims=True))
         p = e / e.sum(axis=-1, keepdims=True)
-        dp = np.einsum("thd,ud->htu", do[b], v[b])
+        dp = doh @ v[b].T
         ds = p * (dp - (p * dp).sum(axis=-1, keepdims=True))
-        dq[b] = np.einsum("htu,ud->thd", ds, k[b]) * scale
-        dk[b] = np.einsum("htu,thd->ud", ds, q[b]) * scale
-        dv[b] = np.einsum("htu,thd->ud", p, do[b])
+        dq[b] = (ds @ k[b]).transpose(1, 0, 2) * scale
+        dk[b] = (ds.transpose(0, 2, 1) @ qh).sum(axis=0) * scale
+        dv[b] = (p.transpose(0, 2, 1) @ doh).sum(axis=0)
     return dq, dk, dv
 
 
@@ -262,11 +264,11 @@ def logsumexp(z: np.ndarray) -> np.ndarray:
 E4M3_MAX = 448.0
 
 
-def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+def _e4m3_value(c: np.ndarray) -> np.ndarray:
     """Value of each e4m3 byte: sign bit 7, exponent bits 6..3 with bias 7,
     mantissa bits 2..0; exponent 0 is subnormal (m/8 * 2**-6); 0x7f and 0xff
     are NaN."""
-    c = np.asarray(codes, dtype=np.int64)
+    c = np.asarray(c, dtype=np.int64)
     sign = np.where(c & 0x80, -1.0, 1.0)
     e = (c >> 3) & 0xF
     m = (c & 7).astype(np.float64)
@@ -275,19 +277,33 @@ def e4m3_decode(codes: np.ndarray) -> np.ndarray:
     return sign * mag
 
 
+_E4M3_TABLE = _e4m3_value(np.arange(256))
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """Value of each e4m3 byte (the definition above, looked up per code)."""
+    return _E4M3_TABLE[np.asarray(codes, dtype=np.uint8)]
+
+
 def e4m3_encode(y: np.ndarray) -> np.ndarray:
-    """Nearest e4m3 code of each value (ties to the even code, i.e. the even
-    mantissa), after clamping the magnitude to 448. NaN maps to 0x7f."""
-    y = np.asarray(y, dtype=np.float64)
-    grid = e4m3_decode(np.arange(0x7F))          # codes 0..126: 0 .. 448, increasing
-    a = np.minimum(np.abs(y), E4M3_MAX)
-    a = np.where(np.isnan(a), 0.0, a)
-    hi = np.clip(np.searchsorted(grid, a, side="left"), 0, 0x7E)
-    lo = np.maximum(hi - 1, 0)
-    dlo, dhi = a - grid[lo], grid[hi] - a
-    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
-    code = np.where(pick_hi, hi, lo)
-    code = np.where(a == grid[hi], hi, code)
+    """Nearest e4m3 code of each fp32 value (ties to the even code, i.e. the
+    even mantissa), after clamping the magnitude to 448. NaN maps to 0x7f.
+
+    In the binade [2**E, 2**(E+1)) (E >= -6; the subnormals share the spacing
+    of E = -6) the grid has spacing 2**(E-3), so the nearest grid value is
+    rint(a / spacing) * spacing, rint rounding halves to even; an even
+    multiple of the spacing is an even mantissa (and an even code)."""
+    y = np.asarray(y, dtype=np.float32)
+    a = np.minimum(np.abs(y), np.float32(E4M3_MAX))
+    a = np.where(np.isnan(a), np.float32(0.0), a)
+    _, e = np.frexp(a)                              # a = f * 2**e, 0.5 <= f < 1
+    E = np.maximum(e - 1, -6)
+    step = np.ldexp(np.float32(1.0), E - 3)
+    v = np.rint(a / step) * step                    # exact in fp32 (power-of-two scaling)
+    _, e2 = np.frexp(v)
+    E2 = e2 - 1
+    code = np.where(E2 < -6, v * np.float32(2.0 ** 9), (E2 + 7) * 8 + (np.ldexp(v, -E2) - 1) * 8)
+    code = np.where(v == 0, 0, code).astype(np.int64)
     code = code | np.where(np.signbit(y), 0x80, 0)
     code = np.where(np.isnan(y), 0x7F, code)
     return code.astype(np.uint8)
@@ -351,24 +367,32 @@ def forward(cfg: dict, params: dict, idx: np.ndarray, targets: np.ndarray, row_c
     cos, sin = rope_tables(T, D, cfg["rope_theta"])
     W = {k: np.asarray(v, dtype=np.float64) for k, v in params.items()}
 
+    # matmul operands as the config's precision sees them (the e4m3 round trip
+    # for FP8 models, else the tensors themselves); the backward reuses them
+    Wm = {k: mm_operand(cfg, v) for k, v in W.items() if k.startswith("h")}
     x, r0 = rmsnorm(W["wte"][idx], eps)
-    cache = dict(r0=r0, layers=[], cos=cos, sin=sin)
+    cache = dict(r0=r0, layers=[], cos=cos, sin=sin, Wm=Wm)
     for l in range(cfg["n_layer"]):
         h1, r1 = rmsnorm(x, eps)
-        qkv = mm_operand(cfg, h1) @ mm_operand(cfg, W[f"h{l}.w_qkv"]).T
+        h1m = mm_operand(cfg, h1)
+        qkv = h1m @ Wm[f"h{l}.w_qkv"].T
         q, k, v = _split_qkv(qkv, H, 1, D)
         qr, kr = rope(q, cos, sin), rope(k, cos, sin)
         qn, rq = rmsnorm(qr, eps)
         kn, rk = rmsnorm(kr, eps)
         o, lse = causal_mqa_attention(qn, kn[:, :, 0], v[:, :, 0], layer_window(cfg, l))
         o2 = o.reshape(B, T, H * D)
-        x = x + mm_operand(cfg, o2) @ mm_operand(cfg, W[f"h{l}.w_o"]).T
+        o2m = mm_operand(cfg, o2)
+        x = x + o2m @ Wm[f"h{l}.w_o"].T
         h2, r2 = rmsnorm(x, eps)
-        u = mm_operand(cfg, h2) @ mm_operand(cfg, W[f"h{l}.w_1"]).T
+        h2m = mm_operand(cfg, h2)
+        u = h2m @ Wm[f"h{l}.w_1"].T
         a = np.maximum(u, 0.0) ** 2
-        x = x + mm_operand(cfg, a) @ mm_operand(cfg, W[f"h{l}.w_2"]).T
+        am = mm_operand(cfg, a)
+        x = x + am @ Wm[f"h{l}.w_2"].T
         cache["layers"].append(dict(h1=h1, r1=r1, qn=qn, rq=rq, kn=kn, rk=rk, v=v,
-                                    o=o, lse=lse, h2=h2, r2=r2, u=u, a=a))
+                                    o=o, lse=lse, h2=h2, r2=r2, u=u, a=a,
+                                    h1m=h1m, o2m=o2m, h2m=h2m, am=am))
     hf, rf = rmsnorm(x, eps)
     cache.update(hf=hf, rf=rf)
 
@@ -412,24 +436,25 @@ def backward(cfg: dict, params: dict, idx: np.ndarray, targets: np.ndarray, cach
         dhf[s0:s1] = dz @ W["lm_head"]
     dx = rmsnorm_bwd(dhf.reshape(B, T, C), cache["hf"], cache["rf"])
 
+    Wm = cache["Wm"]
     for l in reversed(range(cfg["n_layer"])):
         L = cache["layers"][l]
         # MLP: x_out = x_mid + relu(u)^2 W2^T, u = rmsnorm(x_mid) W1^T
         # (for FP8 models every product takes the e4m3 round trips of its
         # operands; the quantisation itself is passed straight through)
         dy = mm_operand(cfg, dx)
-        G[f"h{l}.w_2"] += dy.reshape(N, C).T @ mm_operand(cfg, L["a"]).reshape(N, -1)
-        da = dy @ mm_operand(cfg, W[f"h{l}.w_2"])
+        G[f"h{l}.w_2"] += dy.reshape(N, C).T @ L["am"].reshape(N, -1)
+        da = dy @ Wm[f"h{l}.w_2"]
         du = da * 2.0 * np.maximum(L["u"], 0.0)
         duq = mm_operand(cfg, du)
-        G[f"h{l}.w_1"] += duq.reshape(N, -1).T @ mm_operand(cfg, L["h2"]).reshape(N, C)
-        dh2 = duq @ mm_operand(cfg, W[f"h{l}.w_1"])
+        G[f"h{l}.w_1"] += duq.reshape(N, -1).T @ L["h2m"].reshape(N, C)
+        dh2 = duq @ Wm[f"h{l}.w_1"]
         dx = dx + rmsnorm_bwd(dh2, L["h2"], L["r2"])
         # attention: x_mid = x_in + o W_o^T
         o2 = L["o"].reshape(B, T, H * D)
         dy = mm_operand(cfg, dx)
-        G[f"h{l}.w_o"] += dy.reshape(N, C).T @ mm_operand(cfg, o2).reshape(N, -1)
-        do = (dy @ mm_operand(cfg, W[f"h{l}.w_o"])).reshape(B, T, H, D)
+        G[f"h{l}.w_o"] += dy.reshape(N, C).T @ L["o2m"].reshape(N, -1)
+        do = (dy @ Wm[f"h{l}.w_o"]).reshape(B, T, H, D)
         dqn, dkn, dv = causal_mqa_attention_bwd(do, L["qn"], L["kn"][:, :, 0], L["v"][:, :, 0],
                                                 layer_window(cfg, l))
         dqr = rmsnorm_bwd(dqn, L["qn"], L["rq"])
@@ -439,8 +464,8 @@ def backward(cfg: dict, params: dict, idx: np.ndarray, targets: np.ndarray, cach
         dqkv = np.concatenate([dq.reshape(B, T, H * D), dk.reshape(B, T, D),
                                dv.reshape(B, T, D)], axis=-1)
         dqkv = mm_operand(cfg, dqkv)
-        G[f"h{l}.w_qkv"] += dqkv.reshape(N, -1).T @ mm_operand(cfg, L["h1"]).reshape(N, C)
-        dh1 = dqkv @ mm_operand(cfg, W[f"h{l}.w_qkv"])
+        G[f"h{l}.w_qkv"] += dqkv.reshape(N, -1).T @ L["h1m"].reshape(N, C)
+        dh1 = dqkv @ Wm[f"h{l}.w_qkv"]
         dx = dx + rmsnorm_bwd(dh1, L["h1"], L["r1"])
 
     # embedding: x0 = rmsnorm(wte[idx]); dwte[v] = sum over positions with idx == v
