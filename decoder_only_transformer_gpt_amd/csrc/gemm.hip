@@ -389,11 +389,26 @@ struct Epilogue<T, Epi::Residual> {
   template <int TM, int TN, int WN>
   static DEV void run(const GemmArgs& a, f32x16 (&acc)[TM][TN], float* lds, int mbase, int nbase, int lane) {
     T* C = reinterpret_cast<T*>(a.C);
-    staged_store<TM, TN, WN>(acc, lds, mbase, nbase, lane, [&](int m, int n, float (&v)[4]) {
+    // bf16: the residual is requested for the whole tile up front (raw, 4
+    // values in two dwords); fp32 loads it per item
+    auto pre = [&](int m, int n) {
+      u32x2 r = {0u, 0u};
+      if constexpr (sizeof(T) == 2) {
+        if (m < a.M && n < a.N) r = ld8(C + (int64_t)m * a.ldc + n);
+      }
+      return r;
+    };
+    staged_store_pre<TM, TN, WN, sizeof(T) == 2>(acc, lds, mbase, nbase, lane, pre,
+                                                 [&](int m, int n, float (&v)[4], u32x2 r) {
       if (m < a.M && n < a.N) {
         float x[4];
-        load4(C + (int64_t)m * a.ldc + n, x);
-        for (int r = 0; r < 4; ++r) x[r] += v[r];
+        if constexpr (sizeof(T) == 2) {
+          x[0] = __uint_as_float(r[0] << 16); x[1] = __uint_as_float(r[0] & 0xffff0000u);
+          x[2] = __uint_as_float(r[1] << 16); x[3] = __uint_as_float(r[1] & 0xffff0000u);
+        } else {
+          load4(C + (int64_t)m * a.ldc + n, x);
+        }
+        for (int q = 0; q < 4; ++q) x[q] += v[q];
         store4(C + (int64_t)m * a.ldc + n, x);
       }
     });
