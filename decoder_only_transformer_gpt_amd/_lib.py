@@ -91,6 +91,14 @@ def lib():
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is not built; run decoder_only_transformer_gpt_amd.build.build()")
+        # torch ships its own HIP runtime: load it first, so that the
+        # library's libamdhip64 dependency resolves to that same runtime (one
+        # runtime and one device context per process, whichever module the
+        # caller imports first)
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         L = ctypes.CDLL(LIB_PATH)
         for name, (res, args) in _SIGS.items():
             fn = getattr(L, name)
