@@ -123,9 +123,9 @@ def cpu_baseline(cfg_lib, seconds_hint: float = 20.0) -> dict:
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = os.cpu_count() or 1
-    B, T = 1, 1024
+    B, T = 1, 2048
     shapes = [(n, r, c) for n, _, r, c in _lib.gpt_param_layout(cfg_lib)]
-    _, vals = synthetic.make_weights(shapes, seed=0, dtype="bf16")
+    _, vals = synthetic.make_weights(shapes, seed=0, dtype="f32" if cfg_lib.dtype == _lib.GPT_F32 else "bf16")
     idx, tgt = synthetic.make_tokens(B, T, cfg_lib.vocab_size, "zipf", seed=1)
     P, off = {}, 0
     for n, r, c in shapes:
