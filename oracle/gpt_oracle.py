@@ -41,6 +41,17 @@ Readings where the pages are silent (each also fixed in the HIP path):
 * FP8 matmuls (optional, cfg["fp8"]): readings listed with the e4m3
   functions below. Quantisation decisions are taken in fp32, as the kernels
   take them; everything else stays float64.
+* Residual scalars (optional, cfg["x0_lambdas"]; [P1] "A Llama-class
+  transformer...": per-layer resid_lambdas and x0_lambdas, initialised to 1.0
+  and 0.1, mixing each layer's residual stream with the normalised
+  embedding; [P4] item 0): before layer l's block the stream becomes
+  x <- resid_lambdas[l] * x + x0_lambdas[l] * x0, x0 = rmsnorm(wte[idx]).
+* Value embeddings (optional, cfg["value_embeds"]; [P1] same section: at
+  alternating layers a gated embedding lookup adds to V; [P4] item 0:
+  ve_gate): layers 0, 2, 4, ... hold a table ve_l [V, n_kv_head * D]; after
+  the QKV projection v <- v + ve_gates[j] * ve_l[idx] (j-th such layer),
+  before attention. Which layers "alternate" and the gate's form (here one
+  learned scalar per layer, i.e. per K/V head under MQA) are readings.
 
 Parity pins: every function here is pinned by a test in ``tests/`` against a
 closed form, an invariant, a library routine or finite differences; none is
@@ -88,7 +99,18 @@ def param_shapes(cfg: dict):
         shapes += [(f"h{l}.w_qkv", (H + 2 * Hkv) * D, C), (f"h{l}.w_o", C, H * D),
                    (f"h{l}.w_1", F, C), (f"h{l}.w_2", C, F)]
     shapes.append(("lm_head", V, C))
+    for l in ve_layers(cfg):
+        shapes.append((f"h{l}.ve", V, Hkv * D))
+    if cfg.get("x0_lambdas", False):
+        shapes += [("resid_lambdas", 1, cfg["n_layer"]), ("x0_lambdas", 1, cfg["n_layer"])]
+    if ve_layers(cfg):
+        shapes.append(("ve_gates", 1, len(ve_layers(cfg))))
     return shapes
+
+
+def ve_layers(cfg: dict) -> list:
+    """Layers with a value embedding: every other layer from layer 0."""
+    return list(range(0, cfg["n_layer"], 2)) if cfg.get("value_embeds", False) else []
 
 
 def param_count(cfg: dict) -> int:
@@ -369,14 +391,22 @@ def forward(cfg: dict, params: dict, idx: np.ndarray, targets: np.ndarray, row_c
 
     # matmul operands as the config's precision sees them (the e4m3 round trip
     # for FP8 models, else the tensors themselves); the backward reuses them
-    Wm = {k: mm_operand(cfg, v) for k, v in W.items() if k.startswith("h")}
+    Wm = {k: mm_operand(cfg, v) for k, v in W.items() if k.startswith("h") and not k.endswith(".ve")}
     x, r0 = rmsnorm(W["wte"][idx], eps)
-    cache = dict(r0=r0, layers=[], cos=cos, sin=sin, Wm=Wm)
+    x0 = x
+    lam = cfg.get("x0_lambdas", False)
+    vel = ve_layers(cfg)
+    cache = dict(r0=r0, layers=[], cos=cos, sin=sin, Wm=Wm, x0=x0)
     for l in range(cfg["n_layer"]):
+        xprev = x
+        if lam:
+            x = W["resid_lambdas"][0, l] * x + W["x0_lambdas"][0, l] * x0
         h1, r1 = rmsnorm(x, eps)
         h1m = mm_operand(cfg, h1)
         qkv = h1m @ Wm[f"h{l}.w_qkv"].T
         q, k, v = _split_qkv(qkv, H, 1, D)
+        if l in vel:
+            v = v + W["ve_gates"][0, vel.index(l)] * W[f"h{l}.ve"][idx][:, :, None, :]
         qr, kr = rope(q, cos, sin), rope(k, cos, sin)
         qn, rq = rmsnorm(qr, eps)
         kn, rk = rmsnorm(kr, eps)
@@ -392,7 +422,7 @@ def forward(cfg: dict, params: dict, idx: np.ndarray, targets: np.ndarray, row_c
         x = x + am @ Wm[f"h{l}.w_2"].T
         cache["layers"].append(dict(h1=h1, r1=r1, qn=qn, rq=rq, kn=kn, rk=rk, v=v,
                                     o=o, lse=lse, h2=h2, r2=r2, u=u, a=a,
-                                    h1m=h1m, o2m=o2m, h2m=h2m, am=am))
+                                    h1m=h1m, o2m=o2m, h2m=h2m, am=am, xprev=xprev))
     hf, rf = rmsnorm(x, eps)
     cache.update(hf=hf, rf=rf)
 
@@ -435,6 +465,9 @@ def backward(cfg: dict, params: dict, idx: np.ndarray, targets: np.ndarray, cach
         G["lm_head"] += dz.T @ hf2[s0:s1]
         dhf[s0:s1] = dz @ W["lm_head"]
     dx = rmsnorm_bwd(dhf.reshape(B, T, C), cache["hf"], cache["rf"])
+    lam = cfg.get("x0_lambdas", False)
+    vel = ve_layers(cfg)
+    dx0 = np.zeros_like(dx)  # gradient reaching x0 through the x0_lambdas mixes
 
     Wm = cache["Wm"]
     for l in reversed(range(cfg["n_layer"])):
@@ -461,17 +494,26 @@ def backward(cfg: dict, params: dict, idx: np.ndarray, targets: np.ndarray, cach
         dkr = rmsnorm_bwd(dkn[:, :, None, :], L["kn"], L["rk"])
         dq = rope_bwd(dqr, cos, sin)
         dk = rope_bwd(dkr, cos, sin)
+        if l in vel:
+            j = vel.index(l)
+            G["ve_gates"][0, j] += np.sum(dv * W[f"h{l}.ve"][idx])
+            np.add.at(G[f"h{l}.ve"], idx.reshape(N), W["ve_gates"][0, j] * dv.reshape(N, D))
         dqkv = np.concatenate([dq.reshape(B, T, H * D), dk.reshape(B, T, D),
                                dv.reshape(B, T, D)], axis=-1)
         dqkv = mm_operand(cfg, dqkv)
         G[f"h{l}.w_qkv"] += dqkv.reshape(N, -1).T @ L["h1m"].reshape(N, C)
         dh1 = dqkv @ Wm[f"h{l}.w_qkv"]
         dx = dx + rmsnorm_bwd(dh1, L["h1"], L["r1"])
+        if lam:  # x_in = resid_lambdas[l] * xprev + x0_lambdas[l] * x0
+            G["resid_lambdas"][0, l] += np.sum(dx * L["xprev"])
+            G["x0_lambdas"][0, l] += np.sum(dx * cache["x0"])
+            dx0 = dx0 + W["x0_lambdas"][0, l] * dx
+            dx = W["resid_lambdas"][0, l] * dx
 
     # embedding: x0 = rmsnorm(wte[idx]); dwte[v] = sum over positions with idx == v
     e = W["wte"][idx]
     y0 = e * cache["r0"]
-    de = rmsnorm_bwd(dx, y0, cache["r0"])
+    de = rmsnorm_bwd(dx + dx0, y0, cache["r0"])
     np.add.at(G["wte"], idx.reshape(N), de.reshape(N, C))
     return G
 

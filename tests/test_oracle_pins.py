@@ -341,11 +341,18 @@ def _torch_step(cfg, P, idx, tg):
         return QLinear.apply(x, w) if cfg.get("fp8", False) else x @ w.T
 
     x = norm(W["wte"][idx_t])
+    x0 = x
+    ve_l = list(range(0, cfg["n_layer"], 2)) if cfg.get("value_embeds", False) else []
     for l in range(cfg["n_layer"]):
+        if cfg.get("x0_lambdas", False):
+            x = W["resid_lambdas"][0, l] * x + W["x0_lambdas"][0, l] * x0
         qkv = lin(norm(x), W[f"h{l}.w_qkv"])
         q = qkv[..., :H * D].view(B, T, H, D).transpose(1, 2)
         k = qkv[..., H * D:(H + 1) * D].view(B, T, 1, D).transpose(1, 2)
-        v = qkv[..., (H + 1) * D:].view(B, T, 1, D).transpose(1, 2)
+        v = qkv[..., (H + 1) * D:]
+        if l in ve_l:
+            v = v + W["ve_gates"][0, ve_l.index(l)] * F.embedding(idx_t, W[f"h{l}.ve"])
+        v = v.view(B, T, 1, D).transpose(1, 2)
         q, k = norm(rot(q)), norm(rot(k))
         pattern, short = cfg.get("window_pattern", ""), cfg.get("window_short", 0)
         if pattern and short and l != cfg["n_layer"] - 1 and pattern[l % len(pattern)] == "S":
@@ -636,3 +643,92 @@ def test_fp8_step_close_to_unquantised_step():
         a, b = G0[name].ravel(), G8[name].ravel()
         cos = a @ b / np.linalg.norm(a) / np.linalg.norm(b)
         assert cos > 0.99, name
+
+
+# ------------------------------------- residual scalars, value embeddings ---
+
+def _lam_ve_params(cfg, seed, std=0.05):
+    P = rand_params(cfg, seed=seed, std=std)
+    rng = np.random.default_rng(seed + 100)
+    L = cfg["n_layer"]
+    if cfg.get("x0_lambdas"):
+        P["resid_lambdas"] = 1.0 + 0.2 * rng.standard_normal((1, L))
+        P["x0_lambdas"] = 0.1 + 0.2 * rng.standard_normal((1, L))
+    if cfg.get("value_embeds"):
+        P["ve_gates"] = 1.0 + 0.5 * rng.standard_normal((1, len(O.ve_layers(cfg))))
+        for l in O.ve_layers(cfg):
+            P[f"h{l}.ve"] = P[f"h{l}.ve"] * 20   # ve rows comparable to v
+    return P
+
+
+def test_ve_layers_and_param_shapes():
+    """Value embeddings sit on layers 0, 2, 4, ... ([V, n_kv_head*D] each),
+    then the per-layer scalars; the plain config is unchanged."""
+    cfg = tiny_cfg(n_layer=5, x0_lambdas=True, value_embeds=True)
+    assert O.ve_layers(cfg) == [0, 2, 4]
+    names = [n for n, _, _ in O.param_shapes(cfg)]
+    assert names[-6:] == ["h0.ve", "h2.ve", "h4.ve", "resid_lambdas", "x0_lambdas", "ve_gates"]
+    shapes = dict((n, (r, c)) for n, r, c in O.param_shapes(cfg))
+    assert shapes["h2.ve"] == (512, 128) and shapes["x0_lambdas"] == (1, 5) and shapes["ve_gates"] == (1, 3)
+    assert O.param_count(cfg) == O.param_count(tiny_cfg(n_layer=5)) + 3 * 512 * 128 + 2 * 5 + 3
+
+
+def test_lambdas_ve_step_matches_torch_autograd():
+    pytest.importorskip("torch")
+    cfg = tiny_cfg(n_layer=3, n_head=2, model_dim=256, mlp_dim=1024, vocab_size=80, x0_lambdas=True,
+                   value_embeds=True)
+    P = _lam_ve_params(cfg, 50)
+    rng = np.random.default_rng(51)
+    idx = rng.integers(0, 80, (2, 17))
+    tg = rng.integers(0, 80, (2, 17))
+    loss, _, G = O.step(cfg, P, idx, tg)
+    tl, TG = _torch_step(cfg, P, idx, tg)
+    assert loss == pytest.approx(tl, rel=1e-13)
+    for name in G:
+        np.testing.assert_allclose(G[name], TG[name], rtol=1e-9, atol=1e-13, err_msg=name)
+
+
+def test_lambdas_ve_central_differences():
+    cfg = tiny_cfg(n_layer=3, n_head=1, vocab_size=64, x0_lambdas=True, value_embeds=True)
+    P = _lam_ve_params(cfg, 52)
+    rng = np.random.default_rng(53)
+    idx = rng.integers(0, 64, (2, 9))
+    tg = rng.integers(0, 64, (2, 9))
+    _, _, G = O.step(cfg, P, idx, tg)
+    h = 1e-6
+    tok = int(idx[1, 3])
+    for name, ij in [("resid_lambdas", (0, 1)), ("x0_lambdas", (0, 0)), ("x0_lambdas", (0, 2)),
+                     ("ve_gates", (0, 1)), ("h2.ve", (tok, 5)), ("h0.ve", (tok, 77)), ("wte", (tok, 3))]:
+        Wt = P[name]
+        old = Wt[ij]
+        Wt[ij] = old + h
+        lp = O.forward(cfg, P, idx, tg)[0]
+        Wt[ij] = old - h
+        lm = O.forward(cfg, P, idx, tg)[0]
+        Wt[ij] = old
+        fd = (lp - lm) / (2 * h)
+        assert abs(fd - G[name][ij]) <= 1e-6 * abs(fd) + 1e-9, (name, fd, G[name][ij])
+    # rows of a value-embedding table that no token reads get no gradient
+    unused = np.setdiff1d(np.arange(64), idx)
+    assert not G["h0.ve"][unused].any()
+
+
+def test_neutral_scalars_and_zero_gate_reduce_to_the_plain_model():
+    """resid_lambdas = 1, x0_lambdas = 0 and zero gates leave the plain model:
+    the same loss and the same gradients for every shared tensor, bit for bit."""
+    base = tiny_cfg(n_layer=2, vocab_size=64)
+    cfg = dict(base, x0_lambdas=True, value_embeds=True)
+    P = _lam_ve_params(cfg, 54)
+    P["resid_lambdas"][:] = 1.0
+    P["x0_lambdas"][:] = 0.0
+    P["ve_gates"][:] = 0.0
+    rng = np.random.default_rng(55)
+    idx = rng.integers(0, 64, (2, 11))
+    tg = rng.integers(0, 64, (2, 11))
+    l1, _, G1 = O.step(cfg, P, idx, tg)
+    l0, _, G0 = O.step(base, {k: v for k, v in P.items() if k in dict((n, 0) for n, _, _ in O.param_shapes(base))},
+                       idx, tg)
+    assert l1 == l0
+    for k in G0:
+        np.testing.assert_array_equal(G1[k], G0[k], err_msg=k)
+    assert not G1["h0.ve"].any() and G1["ve_gates"][0, 0] != 0.0
