@@ -147,7 +147,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="d20", choices=["tiny", "d4", "d12", "d20", "d20-sssl", "d24fp8"])
+    ap.add_argument("--workload", default="d20", choices=["tiny", "d4", "d12", "d20", "d20-sssl", "d24fp8", "d20-ve"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--gemm-tile", type=int, default=0, choices=[0, 1, 2, 3],
                     help="force one GEMM tile variant (0 = by shape)")
@@ -270,7 +270,9 @@ def main():
         "config": {"workload": f"{wl.name}: depth {cfg.n_layer}, width {cfg.model_dim}, {cfg.n_head} query heads / "
                                f"1 kv head, head_dim 128, MLP {cfg.mlp_dim}, vocab {cfg.vocab_size}"
                                + (f", windows {wl.window_pattern} (short {wl.window_short})" if wl.window_pattern
-                                  else ""),
+                                  else "")
+                               + (", resid/x0 lambdas" if wl.x0_lambdas else "")
+                               + (", value embeddings on even layers" if wl.value_embeds else ""),
                    "global_batch": B, "seq_len": T, "tokens": wl.tokens, "parallelism": "single GPU"},
         "mfu_bf16": round(mfu, 4), "mfu_palm_convention": round(fl["palm"] * tok_s / (PEAK_BF16_TFLOPS * 1e12), 4),
         "loss": round(loss, 5), "roofline": roof,

@@ -33,6 +33,7 @@ class gpt_config(ctypes.Structure):
         ("vocab_size", ctypes.c_int32), ("max_seq_len", ctypes.c_int32),
         ("rope_theta", ctypes.c_float), ("logit_softcap", ctypes.c_float), ("norm_eps", ctypes.c_float),
         ("dtype", ctypes.c_int32), ("window_short", ctypes.c_int32), ("window_pattern", ctypes.c_char * 8),
+        ("x0_lambdas", ctypes.c_int32), ("value_embeds", ctypes.c_int32),
     ]
 
     def as_dict(self) -> dict:

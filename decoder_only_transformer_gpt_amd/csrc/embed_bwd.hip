@@ -24,12 +24,23 @@ namespace {
 constexpr int kSortChunk = 256;  // items per block in the radix passes
 constexpr int kSegChunk = 32;    // sorted entries per block in the segment sums
 
+// Sort input: key = token id, value = position (negative for an invalid id,
+// which the segment sums skip).
+__global__ __launch_bounds__(256) void sort_init_kernel(const int32_t* __restrict__ idx, int N, int V,
+                                                        int32_t* __restrict__ keys, int32_t* __restrict__ vals) {
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  if (n >= N) return;
+  const int id = idx[n];
+  const bool ok = (unsigned)id < (unsigned)V;
+  keys[n] = ok ? id : 0;
+  vals[n] = ok ? n : -1 - n;
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void embed_coef_kernel(const T* __restrict__ wte, const int32_t* __restrict__ idx,
                                                          const float* __restrict__ dres,
                                                          const float* __restrict__ rstd0, int N, int C, int V,
-                                                         float* __restrict__ coef, int32_t* __restrict__ keys,
-                                                         int32_t* __restrict__ vals) {
+                                                         float* __restrict__ coef) {
   const int lane = threadIdx.x & 63;
   const int n = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (n >= N) return;
@@ -50,8 +61,6 @@ __global__ __launch_bounds__(256) void embed_coef_kernel(const T* __restrict__ w
     const float r = rstd0[n];
     // An invalid id (the forward already raised the device flag) contributes nothing.
     coef[n] = ok ? r * r * r * dot / (float)C : 0.f;
-    keys[n] = ok ? id : 0;
-    vals[n] = ok ? n : -1 - n;  // negative: skip in the segment sums
   }
 }
 
@@ -195,7 +204,99 @@ __global__ __launch_bounds__(256) void seg_fixup_kernel(const int32_t* __restric
   }
 }
 
+// Value-embedding gradient: dve[v] += gate * sum over positions n with
+// idx[n] == v of dv[n] (128 values, at column col0 of a row of pitch ld), by
+// the same chunked segment sums over the sorted ids; one thread per column.
+template <typename T>
+__global__ __launch_bounds__(128) void ve_seg_partial_kernel(const int32_t* __restrict__ keys,
+                                                             const int32_t* __restrict__ vals,
+                                                             const T* __restrict__ src, int64_t ld, int col0,
+                                                             const T* __restrict__ gate, int N,
+                                                             float* __restrict__ dve, float* __restrict__ carry) {
+  const int c = blockIdx.x, col = threadIdx.x;
+  const int e0 = c * kSegChunk, e1 = min(N, e0 + kSegChunk);
+  const float g = to_f32(*gate);
+  float acc = 0.f;
+  int rs = e0;
+  for (int e = e0; e < e1; ++e) {
+    const int v = keys[e];
+    const int n = vals[e];
+    if (n >= 0) acc += to_f32(src[(int64_t)n * ld + col0 + col]);
+    const bool run_end = (e + 1 == e1) || keys[e + 1] != v;
+    if (!run_end) continue;
+    const bool seg_start = (rs == 0) || keys[rs - 1] != v;
+    const bool seg_end = (e + 1 == N) || keys[e + 1] != v;
+    if (seg_start && seg_end) dve[(int64_t)v * 128 + col] += g * acc;
+    else carry[((int64_t)c * 2 + (seg_start ? 1 : 0)) * 129 + col] = acc;
+    acc = 0.f;
+    rs = e + 1;
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(128) void ve_seg_fixup_kernel(const int32_t* __restrict__ keys, int N, int nchunks,
+                                                           const T* __restrict__ gate,
+                                                           const float* __restrict__ carry, float* __restrict__ dve) {
+  const int c = blockIdx.x, col = threadIdx.x;
+  const int e0 = c * kSegChunk, e1 = min(N, e0 + kSegChunk);
+  const int last = e1 - 1;
+  if (e1 >= N) return;
+  const int v = keys[last];
+  if (keys[e1] != v) return;
+  int s = last;
+  while (s > e0 && keys[s - 1] == v) --s;
+  if (s == e0 && e0 > 0 && keys[e0 - 1] == v) return;
+  float acc = carry[((int64_t)c * 2 + 1) * 129 + col];
+  for (int cc = c + 1; cc < nchunks; ++cc) {
+    acc += carry[((int64_t)cc * 2 + 0) * 129 + col];
+    const int l2 = min(N, (cc + 1) * kSegChunk) - 1;
+    if (keys[l2] != v || l2 + 1 >= N || keys[l2 + 1] != v) break;
+  }
+  dve[(int64_t)v * 128 + col] += to_f32(*gate) * acc;
+}
+
 }  // namespace
+
+hipError_t launch_embed_sort(const int32_t* idx, int N, int V, int32_t* keys_a, int32_t* vals_a, int32_t* keys_b,
+                             int32_t* vals_b, int32_t* hist, hipStream_t s) {
+  if (N <= 0) return hipSuccess;
+  hipLaunchKernelGGL(sort_init_kernel, dim3((N + 255) / 256), dim3(256), 0, s, idx, N, V, keys_a, vals_a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nchunks = (N + kSortChunk - 1) / kSortChunk;
+  int32_t *kin = keys_a, *vin = vals_a, *kout = keys_b, *vout = vals_b;
+  for (int shift = 0; shift < 16; shift += 8) {
+    hipLaunchKernelGGL(radix_hist_kernel, dim3(nchunks), dim3(kSortChunk), 0, s, kin, N, shift, nchunks, hist);
+    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, hist, 256 * nchunks);
+    hipLaunchKernelGGL(radix_scatter_kernel, dim3(nchunks), dim3(kSortChunk), 0, s, kin, vin, N, shift, nchunks, hist,
+                       kout, vout);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    std::swap(kin, kout);
+    std::swap(vin, vout);
+  }
+  return hipSuccess;  // two passes: the sorted ids are back in keys_a / vals_a
+}
+
+hipError_t launch_ve_scatter(int dtype, const int32_t* keys, const int32_t* vals, const void* dqkv, int64_t ld,
+                             int col0, const void* gate, int N, int V, int accumulate, float* dve, float* carry,
+                             hipStream_t s) {
+  hipError_t e;
+  if (!accumulate && (e = launch_fill_f32(dve, 0.f, (int64_t)V * 128, s)) != hipSuccess) return e;
+  if (N <= 0) return hipSuccess;
+  const int nseg = (N + kSegChunk - 1) / kSegChunk;
+  if (dtype == 1) {
+    hipLaunchKernelGGL(ve_seg_partial_kernel<bf16>, dim3(nseg), dim3(128), 0, s, keys, vals, (const bf16*)dqkv, ld,
+                       col0, (const bf16*)gate, N, dve, carry);
+    hipLaunchKernelGGL(ve_seg_fixup_kernel<bf16>, dim3(nseg), dim3(128), 0, s, keys, N, nseg, (const bf16*)gate,
+                       (const float*)carry, dve);
+  } else {
+    hipLaunchKernelGGL(ve_seg_partial_kernel<float>, dim3(nseg), dim3(128), 0, s, keys, vals, (const float*)dqkv, ld,
+                       col0, (const float*)gate, N, dve, carry);
+    hipLaunchKernelGGL(ve_seg_fixup_kernel<float>, dim3(nseg), dim3(128), 0, s, keys, N, nseg, (const float*)gate,
+                       (const float*)carry, dve);
+  }
+  return hipGetLastError();
+}
 
 size_t embed_bwd_hist_elems(int N) { return (size_t)256 * ((N + kSortChunk - 1) / kSortChunk); }
 size_t embed_bwd_carry_elems(int N, int C) { return (size_t)2 * ((N + kSegChunk - 1) / kSegChunk) * (C + 1); }
@@ -209,23 +310,14 @@ hipError_t launch_embed_bwd(const EmbedBwdArgs& a, hipStream_t s) {
   if (N <= 0) return hipSuccess;
   if (a.dtype == 1)
     hipLaunchKernelGGL(embed_coef_kernel<bf16>, dim3((N + 3) / 4), dim3(256), 0, s, (const bf16*)a.wte, a.idx,
-                       a.dres, a.rstd0, N, C, a.V, a.coef, a.keys_a, a.vals_a);
+                       a.dres, a.rstd0, N, C, a.V, a.coef);
   else
     hipLaunchKernelGGL(embed_coef_kernel<float>, dim3((N + 3) / 4), dim3(256), 0, s, (const float*)a.wte, a.idx,
-                       a.dres, a.rstd0, N, C, a.V, a.coef, a.keys_a, a.vals_a);
+                       a.dres, a.rstd0, N, C, a.V, a.coef);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const int nchunks = (N + kSortChunk - 1) / kSortChunk;
-  int32_t *kin = a.keys_a, *vin = a.vals_a, *kout = a.keys_b, *vout = a.vals_b;
-  for (int shift = 0; shift < 16; shift += 8) {
-    hipLaunchKernelGGL(radix_hist_kernel, dim3(nchunks), dim3(kSortChunk), 0, s, kin, N, shift, nchunks, a.hist);
-    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, a.hist, 256 * nchunks);
-    hipLaunchKernelGGL(radix_scatter_kernel, dim3(nchunks), dim3(kSortChunk), 0, s, kin, vin, N, shift, nchunks,
-                       a.hist, kout, vout);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    std::swap(kin, kout);
-    std::swap(vin, vout);
-  }
-  // after two passes the sorted data is back in keys_a / vals_a
+  // the ids were sorted by launch_embed_sort into keys_a / vals_a
+  const int32_t* kin = a.keys_a;
+  const int32_t* vin = a.vals_a;
   const int nseg = (N + kSegChunk - 1) / kSegChunk;
   hipLaunchKernelGGL(seg_partial_kernel, dim3(nseg), dim3(256), 0, s, kin, vin, a.dres, a.rstd0, a.coef, a.wte,
                      a.dtype == 1, N, C, a.dwte, a.carry);

@@ -65,7 +65,7 @@ enum Tag : int {
   K_GEMM_LM, K_CE_LOSS, K_CE_BWD, K_GEMM_LM_DW, K_GEMM_LM_DX, K_RMSNORM_BWD, K_GEMM_W2_DW, K_GEMM_W2_DX,
   K_GEMM_W1_DW, K_GEMM_W1_DX, K_GEMM_O_DW, K_GEMM_O_DX, K_ATTN_BWD_PREP, K_ATTN_BWD_DQ, K_ATTN_BWD_DKV,
   K_ROPE_QKNORM_BWD, K_GEMM_QKV_DW, K_GEMM_QKV_DX, K_EMBED_BWD, K_WEIGHT_T, K_FP8_AMAX, K_FP8_QUANT,
-  K_FP8_WEIGHTS, K_NUM_TAGS
+  K_FP8_WEIGHTS, K_EMBED_SORT, K_X0_MIX, K_X0_MIX_BWD, K_VE_ADD, K_VE_BWD, K_NUM_TAGS
 };
 
 // |max| slots per layer of an FP8 model (fp32, zeroed at every forward)
@@ -77,7 +77,8 @@ const char* kTagNames[K_NUM_TAGS] = {
   "gemm_w1_relu2", "gemm_w2", "gemm_lm_head_softcap", "ce_loss", "ce_bwd", "gemm_lm_head_dw", "gemm_lm_head_dx",
   "rmsnorm_bwd", "gemm_w2_dw", "gemm_w2_dx", "gemm_w1_dw", "gemm_w1_dx_relu2bwd", "gemm_o_dw", "gemm_o_dx",
   "attn_bwd_prep", "attn_bwd_dq", "attn_bwd_dkv", "rope_qknorm_bwd", "gemm_qkv_dw", "gemm_qkv_dx", "embed_bwd",
-  "weight_transpose", "fp8_amax", "fp8_quantize", "fp8_weights"};
+  "weight_transpose", "fp8_amax", "fp8_quantize", "fp8_weights", "embed_sort", "x0_mix", "x0_mix_bwd", "ve_add",
+  "ve_bwd"};
 
 struct Layout {  // byte offsets inside the workspace
   size_t flag, loss_rows, rope_cos, rope_sin;
@@ -93,6 +94,11 @@ struct Layout {  // byte offsets inside the workspace
   // current output gradient, row-major and token-major
   size_t amax, wq, wqT, qdesc, xq, dyq, dyqT;
   std::vector<size_t> h1qT, oqT, h2qT, aqT;
+  // residual scalars: x0 (the normalised embedding), the stream before each
+  // layer's mix, the gradient reaching x0 through the mixes; partial sums of
+  // the scalar gradients
+  size_t x0, dx0acc, rpart;
+  std::vector<size_t> xprev;
   size_t keys_a, vals_a, keys_b, vals_b, hist, coef, carry;
   size_t total;
   size_t split_elems;
@@ -146,6 +152,10 @@ int layer_window(const gpt_config& c, int l) {
   if (n == 0 || c.window_short <= 0 || l == c.n_layer - 1) return 0;
   return c.window_pattern[l % n] == 'S' ? c.window_short : 0;
 }
+
+// Value-embedding layers (0, 2, 4, ...) and their count.
+bool ve_layer(const gpt_config& c, int l) { return c.value_embeds != 0 && l % 2 == 0; }
+int n_ve_layers(const gpt_config& c) { return c.value_embeds != 0 ? (c.n_layer + 1) / 2 : 0; }
 
 Layout plan(const gpt_config& c, int maxB, int maxT) {
   Layout L{};
@@ -227,6 +237,12 @@ Layout plan(const gpt_config& c, int maxB, int maxT) {
       L.aqT.push_back(p.take(F * Np));
     }
   }
+  if (c.x0_lambdas) {
+    L.x0 = p.take(N * C * es);
+    L.dx0acc = p.take(N * C * 4);
+    for (int l = 0; l < c.n_layer; ++l) L.xprev.push_back(p.take(N * C * es));
+  }
+  L.rpart = (c.x0_lambdas || c.value_embeds) ? p.take(gk::resid_partials_elems() * 4) : p.take(0);
   L.keys_a = p.take(N * 4);
   L.vals_a = p.take(N * 4);
   L.keys_b = p.take(N * 4);
@@ -268,6 +284,8 @@ struct gpt_model {
   // parameter offsets (elements)
   int64_t off_wte, off_lm;
   std::vector<int64_t> off_qkv, off_o, off_w1, off_w2;
+  std::vector<int64_t> off_ve;                      // per layer, -1 without a value embedding
+  int64_t off_resid = -1, off_x0lam = -1, off_gates = -1;
   int gemm_tile = 0;      // GPT_OPT_GEMM_TILE
   int ntdesc = 0;
   int64_t wt_tiles = 0;   // total 64x64 tiles of the batched weight transpose
@@ -385,6 +403,8 @@ gpt_status gpt_config_from_depth(int32_t depth, int32_t dtype, gpt_config* out) 
   c.dtype = dtype;
   c.window_short = 0;
   std::memset(c.window_pattern, 0, sizeof(c.window_pattern));
+  c.x0_lambdas = 0;
+  c.value_embeds = 0;
   *out = c;
   return GPT_OK;
 }
@@ -418,6 +438,8 @@ gpt_status gpt_config_validate(const gpt_config* c) {
   if (!nul) return fail(GPT_E_INVALID_ARG, "window_pattern must be NUL-terminated within 8 bytes");
   if (any_short && c->window_short < 1) return fail(GPT_E_INVALID_ARG, "window_short must be >= 1 for 'S' layers");
   if (c->window_short < 0) return fail(GPT_E_INVALID_ARG, "window_short must be >= 0");
+  if ((c->x0_lambdas != 0 && c->x0_lambdas != 1) || (c->value_embeds != 0 && c->value_embeds != 1))
+    return fail(GPT_E_INVALID_ARG, "x0_lambdas and value_embeds must be 0 or 1");
   return GPT_OK;
 }
 
@@ -426,14 +448,16 @@ int64_t gpt_param_count(const gpt_config* c) {
   const int64_t C = c->model_dim, H = c->n_head, Hkv = c->n_kv_head, D = c->head_dim, F = c->mlp_dim,
                 V = c->vocab_size;
   const int64_t per_layer = (H + 2 * Hkv) * D * C + C * H * D + F * C + C * F;
-  return 2 * V * C + c->n_layer * per_layer;
+  const int64_t nve = c->value_embeds ? (c->n_layer + 1) / 2 : 0;
+  return 2 * V * C + c->n_layer * per_layer + nve * (V * Hkv * D + 1) + (c->x0_lambdas ? 2 * c->n_layer : 0);
 }
 
 gpt_status gpt_param_layout(const gpt_config* c, gpt_tensor_desc* out, int32_t* n) {
   gpt_status s = check_shape(c);
   if (s != GPT_OK) return s;
   if (!n) return fail(GPT_E_INVALID_ARG, "n is NULL");
-  const int32_t count = 2 + 4 * c->n_layer;
+  const int32_t nve = c->value_embeds ? (c->n_layer + 1) / 2 : 0;
+  const int32_t count = 2 + 4 * c->n_layer + nve + (c->x0_lambdas ? 2 : 0) + (nve ? 1 : 0);
   if (!out) {
     *n = count;
     return GPT_OK;
@@ -461,6 +485,16 @@ gpt_status gpt_param_layout(const gpt_config* c, gpt_tensor_desc* out, int32_t* 
     snprintf(nm, sizeof(nm), "h%d.w_2", l); add(nm, C, F);
   }
   add("lm_head", V, C);
+  for (int l = 0; l < c->n_layer; l += 2)
+    if (c->value_embeds) {
+      snprintf(nm, sizeof(nm), "h%d.ve", l);
+      add(nm, V, Hkv * D);
+    }
+  if (c->x0_lambdas) {
+    add("resid_lambdas", 1, c->n_layer);
+    add("x0_lambdas", 1, c->n_layer);
+  }
+  if (nve) add("ve_gates", 1, nve);
   *n = count;
   return GPT_OK;
 }
@@ -502,9 +536,11 @@ gpt_status gpt_init(const gpt_config* cfg, const void* params, float* grads, voi
   m->maxB = max_B;
   m->maxT = max_T;
   m->L = plan(*cfg, max_B, max_T);
-  std::vector<gpt_tensor_desc> d(2 + 4 * cfg->n_layer);
-  int32_t n = (int32_t)d.size();
+  int32_t n = 0;
+  gpt_param_layout(cfg, nullptr, &n);
+  std::vector<gpt_tensor_desc> d(n);
   gpt_param_layout(cfg, d.data(), &n);
+  const int i_lm = 1 + 4 * cfg->n_layer;  // lm_head's index; optional tensors follow it
   m->off_wte = d[0].offset;
   for (int l = 0; l < cfg->n_layer; ++l) {
     m->off_qkv.push_back(d[1 + 4 * l].offset);
@@ -512,7 +548,15 @@ gpt_status gpt_init(const gpt_config* cfg, const void* params, float* grads, voi
     m->off_w1.push_back(d[3 + 4 * l].offset);
     m->off_w2.push_back(d[4 + 4 * l].offset);
   }
-  m->off_lm = d[n - 1].offset;
+  m->off_lm = d[i_lm].offset;
+  m->off_ve.assign(cfg->n_layer, -1);
+  for (int i = i_lm + 1; i < n; ++i) {
+    const std::string nm(d[i].name);
+    if (nm == "resid_lambdas") m->off_resid = d[i].offset;
+    else if (nm == "x0_lambdas") m->off_x0lam = d[i].offset;
+    else if (nm == "ve_gates") m->off_gates = d[i].offset;
+    else m->off_ve[std::atoi(nm.c_str() + 1)] = d[i].offset;  // "h<l>.ve"
+  }
 
   // RoPE tables: angle = t * theta^(-2i/D) in double precision, stored as fp32.
   std::vector<float> ct((size_t)max_T * 64), st((size_t)max_T * 64);
@@ -527,7 +571,7 @@ gpt_status gpt_init(const gpt_config* cfg, const void* params, float* grads, voi
   // (FP8 models: only the LM head; their layer weights get e4m3 copies)
   std::vector<gk::TransposeDesc> td;
   int64_t tiles = 0;
-  for (int i = cfg->dtype == GPT_FP8_E4M3 ? n - 1 : 1; i < n; ++i) {
+  for (int i = cfg->dtype == GPT_FP8_E4M3 ? i_lm : 1; i <= i_lm; ++i) {
     gk::TransposeDesc t;
     t.offset = d[i].offset;
     t.rows = (int32_t)d[i].rows;
@@ -543,7 +587,7 @@ gpt_status gpt_init(const gpt_config* cfg, const void* params, float* grads, voi
   std::vector<gk::QuantDesc> qd;
   if (cfg->dtype == GPT_FP8_E4M3) {
     int64_t ab = 0, qb = 0;
-    for (int i = 1; i + 1 < n; ++i) {
+    for (int i = 1; i < i_lm; ++i) {
       const int l = (i - 1) / 4, w = (i - 1) % 4;
       gk::QuantDesc q;
       q.src = reinterpret_cast<const char*>(params) + d[i].offset * 2;
@@ -629,7 +673,14 @@ gpt_status gpt_forward_loss(gpt_model* m, const int32_t* idx, const int32_t* tar
 
   RUN(K_EMBED, return gk::launch_embed_rmsnorm(dt, pbase(m, m->off_wte), idx, N, C, V, c.norm_eps, m->ws + L.x,
                                                wsp<float>(m, L.rstd0), flag, stream););
+  if (c.x0_lambdas)  // keep x0 = rmsnorm(wte[idx]) for the per-layer mixes
+    RUN(K_X0_MIX, return hipMemcpyAsync(m->ws + L.x0, m->ws + L.x, (size_t)N * C * esize(dt), hipMemcpyDeviceToDevice,
+                                        stream););
   for (int l = 0; l < c.n_layer; ++l) {
+    if (c.x0_lambdas)
+      RUN(K_X0_MIX, return gk::launch_x0_mix(dt, m->ws + L.x, m->ws + L.x0, m->ws + L.xprev[l],
+                                             pbase(m, m->off_resid + l), pbase(m, m->off_x0lam + l), (int64_t)N * C,
+                                             stream););
     RUN(K_RMSNORM, return gk::launch_rmsnorm(dt, m->ws + L.x, N, C, c.norm_eps, m->ws + L.h1[l],
                                              wsp<float>(m, L.rstd1[l]), stream););
     if (fp8) TRY(quantize_operand(m, stream, m->ws + L.h1[l], N, C, xq, wsp<uint8_t>(m, L.h1qT[l]), Np, slot(l, A_H1)));
@@ -642,6 +693,9 @@ gpt_status gpt_forward_loss(gpt_model* m, const int32_t* idx, const int32_t* tar
       a.C = m->ws + L.qkv[l]; a.ldc = QKV;
       return gk::launch_gemm(gdt, gk::Epi::Store, a, stream);
     });
+    if (ve_layer(c, l))
+      RUN(K_VE_ADD, return gk::launch_ve_add(dt, m->ws + L.qkv[l], QKV, (H + 1) * kHeadDim, idx, pbase(m, m->off_ve[l]),
+                                             pbase(m, m->off_gates + l / 2), N, V, stream););
     RUN(K_ROPE_QKNORM, return gk::launch_rope_qknorm(dt, m->ws + L.qkv[l], B, T, H, c.norm_eps,
                                                      wsp<float>(m, L.rope_cos), wsp<float>(m, L.rope_sin),
                                                      wsp<float>(m, L.rstd_qk[l]), stream););
@@ -807,6 +861,11 @@ gpt_status gpt_backward(gpt_model* m, float dloss, int32_t accumulate, void* str
     return GPT_OK;
   };
 
+  // the ids sorted once: the embedding and value-embedding gradients sum over them
+  RUN(K_EMBED_SORT, return gk::launch_embed_sort(m->idx, N, V, wsp<int32_t>(m, L.keys_a), wsp<int32_t>(m, L.vals_a),
+                                                 wsp<int32_t>(m, L.keys_b), wsp<int32_t>(m, L.vals_b),
+                                                 wsp<int32_t>(m, L.hist), stream););
+  if (c.x0_lambdas) RUN(K_X0_MIX_BWD, return gk::launch_fill_f32(wsp<float>(m, L.dx0acc), 0.f, (int64_t)N * C, stream););
   RUN(K_CE_BWD, return gk::launch_ce_bwd(dt, m->ws + L.logits, wsp<float>(m, L.lse_ce), m->targets, N, V,
                                          c.logit_softcap, dloss / (float)N, stream););
   TRY(dw(K_GEMM_LM_DW, m->ws + L.logits, V, m->ws + L.hf, C, V, C, m->off_lm));
@@ -859,6 +918,14 @@ gpt_status gpt_backward(gpt_model* m, float dloss, int32_t accumulate, void* str
                                                              wsp<float>(m, L.rstd_qk[l]), B, T, H,
                                                              wsp<float>(m, L.rope_cos), wsp<float>(m, L.rope_sin),
                                                              stream););
+    if (ve_layer(c, l)) {  // v = h1 W_v^T + gate * ve[idx]: dv reaches the gate and the table
+      const int vcol = (H + 1) * kHeadDim;
+      RUN(K_VE_BWD, return gk::launch_ve_gate_grad(dt, m->ws + L.dqkv, QKV, vcol, m->idx, pbase(m, m->off_ve[l]), N, V,
+                                                   wsp<float>(m, L.rpart), G + m->off_gates + l / 2, acc, stream););
+      RUN(K_VE_BWD, return gk::launch_ve_scatter(dt, wsp<int32_t>(m, L.keys_a), wsp<int32_t>(m, L.vals_a),
+                                                 m->ws + L.dqkv, QKV, vcol, pbase(m, m->off_gates + l / 2), N, V, acc,
+                                                 G + m->off_ve[l], wsp<float>(m, L.carry), stream););
+    }
     if (fp8) {
       TRY(quantize_operand(m, stream, m->ws + L.dqkv, N, QKV, dyq, dyqT, Np, slot(l, A_DQKV)));
       TRY(dw8(K_GEMM_QKV_DW, L.h1qT[l], l, A_DQKV, A_H1, QKV, C, m->off_qkv[l]));
@@ -869,6 +936,12 @@ gpt_status gpt_backward(gpt_model* m, float dloss, int32_t accumulate, void* str
     }
     RUN(K_RMSNORM_BWD, return gk::launch_rmsnorm_bwd(dt, m->ws + L.dh, m->ws + L.h1[l], wsp<float>(m, L.rstd1[l]),
                                                      N, C, 1, wsp<float>(m, L.dres), m->ws + L.dres_lp, stream););
+    if (c.x0_lambdas)  // x_in = resid_lambdas[l] x_prev + x0_lambdas[l] x0
+      RUN(K_X0_MIX_BWD, return gk::launch_x0_mix_bwd(dt, wsp<float>(m, L.dres), m->ws + L.dres_lp, m->ws + L.xprev[l],
+                                                     m->ws + L.x0, wsp<float>(m, L.dx0acc),
+                                                     pbase(m, m->off_resid + l), pbase(m, m->off_x0lam + l), l == 0,
+                                                     (int64_t)N * C, wsp<float>(m, L.rpart), G + m->off_resid + l,
+                                                     G + m->off_x0lam + l, acc, stream););
   }
   RUN(K_EMBED_BWD, {
     gk::EmbedBwdArgs a;

@@ -105,13 +105,40 @@ struct EmbedBwdArgs {
   int N, C, V;
   int accumulate;
   float* dwte;           // [V, C] fp32
-  // scratch (inside the workspace)
+  // scratch (inside the workspace); keys_a / vals_a hold the ids sorted by launch_embed_sort
   int32_t* keys_a; int32_t* vals_a; int32_t* keys_b; int32_t* vals_b;  // [N] each
   int32_t* hist;         // [256 * nchunks]
   float* coef;           // [N]
   float* carry;          // [2 * nseg_chunks * (C + 1)]
 };
+// Stable sort of the token ids (key = id, value = position) into keys_a /
+// vals_a (keys_b / vals_b scratch); launch_embed_bwd and launch_ve_scatter
+// read the sorted arrays.
+hipError_t launch_embed_sort(const int32_t* idx, int N, int V, int32_t* keys_a, int32_t* vals_a, int32_t* keys_b,
+                             int32_t* vals_b, int32_t* hist, hipStream_t s);
 hipError_t launch_embed_bwd(const EmbedBwdArgs& a, hipStream_t s);
+// dve [V, 128] fp32 (+)= gate * sum over positions with that id of dv, dv at
+// column col0 of dqkv (row pitch ld), in sorted-id order (deterministic).
+hipError_t launch_ve_scatter(int dtype, const int32_t* keys, const int32_t* vals, const void* dqkv, int64_t ld,
+                             int col0, const void* gate, int N, int V, int accumulate, float* dve, float* carry,
+                             hipStream_t s);
+
+// Residual scalars and value embeddings ----------------------------------------
+size_t resid_partials_elems();
+// xprev = x; x = lam_r * x + lam_0 * x0 over n elements (lam_* device scalars in the param dtype)
+hipError_t launch_x0_mix(int dtype, void* x, const void* x0, void* xprev, const void* lam_r, const void* lam_0,
+                         int64_t n, hipStream_t s);
+// backward of the mix: scalar gradients (+)= <dres, xprev>, <dres, x0>; dres
+// becomes the gradient of xprev (first: of x0, dx0acc included); dres_lp = dres
+hipError_t launch_x0_mix_bwd(int dtype, float* dres, void* dres_lp, const void* xprev, const void* x0, float* dx0acc,
+                             const void* lam_r, const void* lam_0, int first, int64_t n, float* partials,
+                             float* g_lam_r, float* g_lam_0, int accumulate, hipStream_t s);
+// v[n] += gate * ve[idx[n]] (v = 128 values at column col0 of qkv, row pitch ld)
+hipError_t launch_ve_add(int dtype, void* qkv, int64_t ld, int col0, const int32_t* idx, const void* ve,
+                         const void* gate, int N, int V, hipStream_t s);
+// g_gate (+)= sum_n <dv[n], ve[idx[n]]>
+hipError_t launch_ve_gate_grad(int dtype, const void* dqkv, int64_t ld, int col0, const int32_t* idx, const void* ve,
+                               int N, int V, float* partials, float* g_gate, int accumulate, hipStream_t s);
 size_t embed_bwd_hist_elems(int N);
 size_t embed_bwd_carry_elems(int N, int C);
 

@@ -9,7 +9,12 @@ Recipe (stated once, used everywhere):
 * Weights: one ``numpy.random.default_rng(seed)`` (PCG64), tensors drawn in the
   canonical parameter order (wte, then per layer W_qkv, W_o, W_1, W_2, then
   W_lm), ``standard_normal * 0.02`` in float64, rounded to float32 by RNE and
-  then, for bf16 models, to bf16 by RNE on the float32 bits.
+  then, for bf16 models, to bf16 by RNE on the float32 bits. Optional
+  tensors come after W_lm in the same stream: value-embedding tables take
+  ``standard_normal * 0.5`` (so that the lookup is comparable to v), and the
+  per-layer scalars take their initial values (resid_lambdas 1.0,
+  x0_lambdas 0.1, ve_gates 1.0) plus ``0.1 * standard_normal``, a seeded
+  perturbation that keeps every factor away from 0 and 1.
 * Tokens: ``default_rng(seed)`` draws an int32 array [B, T+1]; ``idx`` is
   [:, :T] and ``targets`` is [:, 1:] (next-token targets). ``law="uniform"``
   draws ids uniformly from [0, V). ``law="zipf"`` draws ranks k = 1..V with
@@ -56,9 +61,16 @@ def make_weights(shapes, seed: int = 0, dtype: str = "bf16", std: float = WEIGHT
     total = sum(int(r) * int(c) for _, r, c in shapes)
     vals = np.empty(total, dtype=np.float32)
     off = 0
-    for _, r, c in shapes:
+    inits = {"resid_lambdas": 1.0, "x0_lambdas": 0.1, "ve_gates": 1.0}
+    for name, r, c in shapes:
         n = int(r) * int(c)
-        vals[off:off + n] = (rng.standard_normal(n) * std).astype(np.float32)
+        z = rng.standard_normal(n)
+        if name in inits:
+            vals[off:off + n] = (inits[name] + 0.1 * z).astype(np.float32)
+        elif name.endswith(".ve"):
+            vals[off:off + n] = (z * 0.5).astype(np.float32)
+        else:
+            vals[off:off + n] = (z * std).astype(np.float32)
         off += n
     if dtype == "f32":
         return vals, vals

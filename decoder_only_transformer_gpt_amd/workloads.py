@@ -28,6 +28,8 @@ class Workload:
     tokens: str         # "uniform" | "zipf"
     window_pattern: str = ""   # sliding-window layer pattern, e.g. "SSSL"; "" = all full
     window_short: int = 0
+    x0_lambdas: int = 0        # per-layer resid / x0 scalars
+    value_embeds: int = 0      # value embeddings on layers 0, 2, 4, ...
 
     def config(self) -> _lib.gpt_config:
         dt = {"f32": _lib.GPT_F32, "bf16": _lib.GPT_BF16, "fp8": _lib.GPT_FP8_E4M3}[self.dtype]
@@ -39,6 +41,8 @@ class Workload:
         c.max_seq_len = max(self.seq_len, 2048)
         c.window_pattern = self.window_pattern.encode()
         c.window_short = self.window_short
+        c.x0_lambdas = self.x0_lambdas
+        c.value_embeds = self.value_embeds
         return c
 
 
@@ -54,4 +58,7 @@ WORKLOADS = {
     # d24 with e4m3 QKV / O / MLP products (repo-explainer.com "karpathy/nanochat:
     # The $100 Full-Stack LLM", section "The Engine Room: Muon and FP8")
     "d24fp8": Workload("d24fp8", 24, 1536, 6144, 65536, 2048, 16, "fp8", "zipf"),
+    # d20 with the per-layer residual scalars and value embeddings (aethryn.com,
+    # section "A Llama-class transformer with ten modern departures")
+    "d20-ve": Workload("d20-ve", 20, 1280, 5120, 65536, 2048, 32, "bf16", "zipf", x0_lambdas=1, value_embeds=1),
 }

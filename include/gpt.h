@@ -98,6 +98,17 @@ typedef struct gpt_config {
    * is always full; "" makes every layer full (the default). */
   int32_t window_short;     /* W for 'S' layers; >= 1 when the pattern holds an 'S' */
   char window_pattern[8];   /* NUL-terminated, characters 'S' and 'L' only */
+  /* Residual scalars and value embeddings (aethryn.com, section "A Llama-class
+   * transformer with ten modern departures": per-layer resid_lambdas and
+   * x0_lambdas mix each layer's residual stream with the normalised
+   * embedding; gated value embeddings add to V at alternating layers;
+   * atlas.blal.pro "nanochat — full-stack ChatGPT in ~8k lines", section "How
+   * it works", item 0). Both off by default. */
+  int32_t x0_lambdas;    /* 1: before layer l, x <- resid_lambdas[l] * x + x0_lambdas[l] * x0, with
+                            x0 = rmsnorm(wte[idx]); parameters "resid_lambdas" and "x0_lambdas" [1, n_layer] */
+  int32_t value_embeds;  /* 1: layers 0, 2, 4, ... add ve_gates[j] * ve_j[idx] to v right after the QKV
+                            projection; parameters "h<l>.ve" [vocab_size, n_kv_head * head_dim] per such
+                            layer and "ve_gates" [1, number of such layers] */
 } gpt_config;
 
 /* One parameter tensor inside the flat parameter (and gradient) buffer. */
@@ -133,9 +144,12 @@ int64_t gpt_param_count(const gpt_config* cfg);
 
 /* Fills out[0..*n) with the canonical parameter order: wte [V, C]; per layer
  * w_qkv [(H + 2*n_kv_head)*D, C] (query heads, then K heads, then V heads),
- * w_o [C, H*D], w_1 [F, C], w_2 [C, F]; lm_head [V, C]. On entry *n is the
- * capacity of `out`; on return it is the number of tensors (2 + 4*n_layer).
- * `out` may be NULL to query the count. Host only. */
+ * w_o [C, H*D], w_1 [F, C], w_2 [C, F]; lm_head [V, C]; then, when enabled,
+ * the value-embedding tables h<l>.ve [V, n_kv_head*D] (l = 0, 2, 4, ...),
+ * resid_lambdas [1, n_layer], x0_lambdas [1, n_layer], ve_gates [1, n_ve].
+ * On entry *n is the capacity of `out`; on return it is the number of
+ * tensors (2 + 4*n_layer without the options). `out` may be NULL to query
+ * the count. Host only. */
 gpt_status gpt_param_layout(const gpt_config* cfg, gpt_tensor_desc* out, int32_t* n);
 
 /* Bytes of device workspace gpt_init needs for batches up to max_B x max_T.

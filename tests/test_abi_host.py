@@ -169,3 +169,18 @@ def test_fp8_quantize_argument_errors():
     assert f(p, 4, 24, p, None, 0, p, None) == _lib.GPT_E_INVALID_ARG
     assert f(p, 40, 16, None, p, 32, p, None) == _lib.GPT_E_INVALID_ARG
     assert f(p + 2, 4, 16, p, None, 0, p, None) == _lib.GPT_E_INVALID_ARG
+
+
+def test_optional_tensors_layout_matches_oracle():
+    for lam, ve, L in [(1, 0, 3), (0, 1, 3), (1, 1, 4)]:
+        c = _lib.gpt_config_from_depth(4, _lib.GPT_BF16)
+        c.n_layer = L
+        c.x0_lambdas, c.value_embeds = lam, ve
+        assert _lib.gpt_config_validate(c) == _lib.GPT_OK
+        ours = [(n, r, cc) for n, _, r, cc in _lib.gpt_param_layout(c)]
+        oc = c.as_dict()
+        assert ours == list(O.param_shapes(oc))
+        assert _lib.gpt_param_count(c) == O.param_count(oc)
+    c = _lib.gpt_config_from_depth(4, _lib.GPT_BF16)
+    c.value_embeds = 2
+    assert _lib.gpt_config_validate(c) == _lib.GPT_E_INVALID_ARG

@@ -260,3 +260,17 @@ def test_d24fp8_full_batch():
         U.log(f"[d24-fp8-B16] row {b}: mean loss gpu={rows_gpu[b].mean():.5f} unquantised oracle={r.mean():.5f} "
               f"rel={rel:.2e}")
         assert rel <= 1e-2
+
+
+def test_d4_fp8_with_lambdas_and_value_embeds():
+    """FP8 products together with the residual scalars and value embeddings
+    (the lookup adds to the bf16 v after the e4m3 QKV product)."""
+    U.require_gpu()
+    c = fp8_cfg()
+    c.x0_lambdas, c.value_embeds = 1, 1
+    case = U.Case(c, B=2, T=512, law="zipf", wseed=27, tseed=28)
+    U.log("case d4 fp8 B=2 T=512 lambdas + value embeddings")
+    gpu = U.run_gpu(case)
+    assert gpu["status"] == _lib.GPT_OK
+    l8, G8, G0 = oracle_fp8_and_unquantised(case)
+    check_fp8(case, gpu, l8, G8, G0, "d4-fp8-lam-ve", cos_bar=FP8_COS_D4)
