@@ -539,3 +539,96 @@ def flops_per_token(cfg: dict, T: int) -> dict:
     n_mm = Lyr * ((H + 2) * D * C + C * H * D + 2 * F * C) + V * C
     attn = 6.0 * Lyr * H * D * (T + 1)
     return dict(matmul=6.0 * n_mm, attention=attn, total=6.0 * n_mm + attn)
+
+
+# ---------------------------------------------------------------------------
+# The optimiser step that follows the backward
+# ---------------------------------------------------------------------------
+# [P4] item "2. Pretrain": the transformer's matrix weights go to Muon, the
+# embeddings, the unembedding and the scalars to AdamW; Muon's momentum
+# follows a schedule (0.85 -> 0.97 -> 0.90); fp32 master weights, bf16
+# compute. [P1] "A Llama-class transformer...": input and output embeddings
+# have different learning rates; Muon handles all weight matrices, AdamW the
+# embeddings and scalars. [P3] "The Engine Room: Muon and FP8" and [P5]
+# "Muon optimizer": Muon post-processes the update into an orthogonalisation.
+# Readings (the pages give no formulas):
+# * AdamW is the standard algorithm with decoupled weight decay and bias
+#   correction (w <- w (1 - lr wd); m, v moments; w <- w - (lr / (1 - b1^t))
+#   m / (sqrt(v) / sqrt(1 - b2^t) + eps)), one learning rate per group
+#   (embeddings incl. value-embedding tables, unembedding, scalars);
+# * Muon: momentum buffer u <- mu u + g (mu given per step by the caller's
+#   schedule); the update direction is the orthogonal polar factor of u,
+#   approximated by k steps of the Newton-Schulz iteration
+#   X <- a X + (b A + c A^2) X, A = X X^T, from X_0 = u / (||u||_F + 1e-7),
+#   on the orientation with fewer rows; w <- w (1 - lr wd) - lr *
+#   sqrt(max(1, rows / cols)) * X. The default coefficients (1.5, -0.5, 0)
+#   are the cubic Newton-Schulz iteration for the polar factor; the pages'
+#   "Polar Express" coefficients and variance reduction are not given.
+
+MUON_SUFFIXES = (".w_qkv", ".w_o", ".w_1", ".w_2")
+
+
+def optimizer_group(name: str) -> str:
+    """'muon' for the blocks' matrix weights, else the AdamW group."""
+    if name.startswith("h") and name.endswith(MUON_SUFFIXES):
+        return "muon"
+    if name == "lm_head":
+        return "unembed"
+    if name == "wte" or name.endswith(".ve"):
+        return "embed"
+    return "scalar"
+
+
+def adamw_update(w, g, m, v, t, lr, beta1, beta2, eps, wd):
+    """One AdamW step (decoupled weight decay, bias-corrected moments).
+    Returns (w, m, v)."""
+    w = w * (1.0 - lr * wd)
+    m = beta1 * m + (1.0 - beta1) * g
+    v = beta2 * v + (1.0 - beta2) * g * g
+    bc1, bc2 = 1.0 - beta1 ** t, 1.0 - beta2 ** t
+    w = w - (lr / bc1) * m / (np.sqrt(v) / math.sqrt(bc2) + eps)
+    return w, m, v
+
+
+def newton_schulz(u, steps: int, a: float = 1.5, b: float = -0.5, c: float = 0.0):
+    """k Newton-Schulz steps towards the orthogonal polar factor of u."""
+    X = u / (np.linalg.norm(u) + 1e-7)
+    tr = X.shape[0] > X.shape[1]
+    if tr:
+        X = X.T
+    for _ in range(steps):
+        A = X @ X.T
+        X = a * X + (b * A + c * (A @ A)) @ X
+    return X.T if tr else X
+
+
+def muon_update(w, g, u, lr, mu, wd, steps, coeffs):
+    """One Muon step. Returns (w, u)."""
+    u = mu * u + g
+    X = newton_schulz(u, steps, *coeffs)
+    scale = math.sqrt(max(1.0, w.shape[0] / w.shape[1]))
+    return w * (1.0 - lr * wd) - lr * scale * X, u
+
+
+def optimizer_step(cfg: dict, oc: dict, master: dict, grads: dict, state: dict, t: int):
+    """Updates every parameter from its gradient: Muon for the matrix
+    weights, AdamW for the rest. `state` maps a name to its buffers ("u", or
+    "m" and "v"), zeros on the first step (t = 1). Returns (master, state)."""
+    lrs = dict(embed=oc["lr_embed"], unembed=oc["lr_unembed"], scalar=oc["lr_scalar"])
+    coeffs = (oc.get("ns_a", 1.5), oc.get("ns_b", -0.5), oc.get("ns_c", 0.0))
+    new_w, new_s = {}, {}
+    for name, w in master.items():
+        g = grads[name]
+        grp = optimizer_group(name)
+        if grp == "muon":
+            u = state.get(name, {}).get("u", np.zeros_like(w))
+            new_w[name], u = muon_update(w, g, u, oc["lr_muon"], oc["momentum"], oc["wd_muon"],
+                                         oc["ns_steps"], coeffs)
+            new_s[name] = dict(u=u)
+        else:
+            s = state.get(name, {})
+            m, v = s.get("m", np.zeros_like(w)), s.get("v", np.zeros_like(w))
+            new_w[name], m, v = adamw_update(w, g, m, v, t, lrs[grp], oc["beta1"], oc["beta2"], oc["eps"],
+                                             oc["wd_adamw"])
+            new_s[name] = dict(m=m, v=v)
+    return new_w, new_s

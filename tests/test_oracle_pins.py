@@ -732,3 +732,64 @@ def test_neutral_scalars_and_zero_gate_reduce_to_the_plain_model():
     for k in G0:
         np.testing.assert_array_equal(G1[k], G0[k], err_msg=k)
     assert not G1["h0.ve"].any() and G1["ve_gates"][0, 0] != 0.0
+
+
+# ------------------------------------------------------------- optimiser ---
+
+def test_optimizer_groups():
+    cfg = tiny_cfg(n_layer=2, x0_lambdas=True, value_embeds=True)
+    groups = {n: O.optimizer_group(n) for n, _, _ in O.param_shapes(cfg)}
+    assert groups["h1.w_qkv"] == groups["h0.w_2"] == "muon"
+    assert groups["wte"] == groups["h0.ve"] == "embed" and groups["lm_head"] == "unembed"
+    assert groups["resid_lambdas"] == groups["x0_lambdas"] == groups["ve_gates"] == "scalar"
+
+
+def test_adamw_matches_torch():
+    """Three AdamW steps against torch.optim.AdamW (decoupled weight decay,
+    bias correction)."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(60)
+    w0 = rng.standard_normal((7, 5))
+    gs = [rng.standard_normal((7, 5)) for _ in range(3)]
+    p = torch.tensor(w0, requires_grad=True)
+    opt = torch.optim.AdamW([p], lr=0.01, betas=(0.8, 0.95), eps=1e-10, weight_decay=0.1)
+    w, m, v = w0, np.zeros_like(w0), np.zeros_like(w0)
+    for t, g in enumerate(gs, start=1):
+        p.grad = torch.tensor(g)
+        opt.step()
+        w, m, v = O.adamw_update(w, g, m, v, t, 0.01, 0.8, 0.95, 1e-10, 0.1)
+    np.testing.assert_allclose(w, p.detach().numpy(), rtol=1e-13, atol=1e-15)
+
+
+def test_newton_schulz_reaches_the_polar_factor():
+    """Enough cubic Newton-Schulz steps give U V^T of the SVD (the orthogonal
+    polar factor) for both orientations; the result is invariant to scaling
+    and commutes with transposition; rows of the wide result are orthonormal."""
+    rng = np.random.default_rng(61)
+    U_, _ = np.linalg.qr(rng.standard_normal((12, 12)))
+    V_, _ = np.linalg.qr(rng.standard_normal((40, 12)))
+    M = U_ @ np.diag(np.linspace(1.0, 3.0, 12)) @ V_.T          # 12 x 40, condition number 3
+    P = U_ @ V_.T
+    X = O.newton_schulz(M, 60)
+    np.testing.assert_allclose(X, P, atol=1e-10)
+    np.testing.assert_allclose(O.newton_schulz(M.T, 60), P.T, atol=1e-10)
+    np.testing.assert_allclose(O.newton_schulz(7.5 * M, 60), X, atol=1e-10)
+    np.testing.assert_allclose(X @ X.T, np.eye(12), atol=1e-10)
+    # a few steps only approach it, monotonically in the singular values
+    s5 = np.linalg.svd(O.newton_schulz(M, 5), compute_uv=False)
+    assert np.all(s5 < 1.0 + 1e-12) and np.all(s5 > 0.2)
+
+
+def test_muon_step_momentum_and_scale():
+    """u accumulates mu u + g; a converged update moves w by exactly lr *
+    sqrt(max(1, rows/cols)) in spectral norm; weight decay scales w first."""
+    rng = np.random.default_rng(62)
+    w = rng.standard_normal((30, 10))
+    g1, g2 = rng.standard_normal((30, 10)), rng.standard_normal((30, 10))
+    w1, u1 = O.muon_update(w, g1, np.zeros_like(w), 0.02, 0.9, 0.0, 60, (1.5, -0.5, 0.0))
+    w2, u2 = O.muon_update(w1, g2, u1, 0.02, 0.9, 0.0, 60, (1.5, -0.5, 0.0))
+    np.testing.assert_allclose(u2, 0.9 * g1 + g2, rtol=1e-14)
+    step = np.linalg.svd(w2 - w1, compute_uv=False)
+    np.testing.assert_allclose(step, 0.02 * math.sqrt(3.0), rtol=1e-8)
+    w3, _ = O.muon_update(w, g1, np.zeros_like(w), 0.02, 0.9, 0.5, 60, (1.5, -0.5, 0.0))
+    np.testing.assert_allclose(w3 - w1, -0.02 * 0.5 * w, rtol=1e-12, atol=1e-15)
