@@ -149,6 +149,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="d20", choices=["tiny", "d4", "d12", "d20", "d20-sssl", "d24fp8", "d20-ve"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--optimizer", action="store_true",
+                    help="also time the optimiser step (Muon + AdamW) after the timed region; reported apart")
     ap.add_argument("--gemm-tile", type=int, default=0, choices=[0, 1, 2, 3],
                     help="force one GEMM tile variant (0 = by shape)")
     ap.add_argument("--kernel-table", action="store_true", help="print per-tag timings to stderr")
@@ -277,6 +279,22 @@ def main():
         "mfu_bf16": round(mfu, 4), "mfu_palm_convention": round(fl["palm"] * tok_s / (PEAK_BF16_TFLOPS * 1e12), 4),
         "loss": round(loss, 5), "roofline": roof,
     }
+    if args.optimizer:
+        oc = _lib.gpt_optim_config()
+        oc.lr_muon, oc.lr_embed, oc.lr_unembed, oc.lr_scalar = 0.02, 0.3, 0.004, 0.5
+        oc.momentum, oc.beta1, oc.beta2, oc.eps = 0.95, 0.8, 0.95, 1e-10
+        oc.wd_muon, oc.wd_adamw, oc.ns_steps = 0.0, 0.0, 5
+        oc.ns_a, oc.ns_b, oc.ns_c = 1.5, -0.5, 0.0
+        master = m.params.float()
+        state = torch.zeros(_lib.gpt_optimizer_state_elems(cfg), dtype=torch.float32, device="cuda")
+        stream = torch.cuda.current_stream().cuda_stream
+        _lib.gpt_optimizer_step(m.h, oc, master.data_ptr(), state.data_ptr(), 1, stream)
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        for t in range(2, 2 + args.steps):
+            _lib.gpt_optimizer_step(m.h, oc, master.data_ptr(), state.data_ptr(), t, stream)
+        torch.cuda.synchronize()
+        out["optimizer_ms_per_step"] = round(1e3 * (time.perf_counter() - t2) / args.steps, 3)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg)
     print(json.dumps(out), flush=True)

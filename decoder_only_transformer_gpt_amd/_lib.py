@@ -42,6 +42,15 @@ class gpt_config(ctypes.Structure):
         return d
 
 
+class gpt_optim_config(ctypes.Structure):
+    _fields_ = [(k, ctypes.c_float) for k in ("lr_muon", "lr_embed", "lr_unembed", "lr_scalar", "momentum", "beta1",
+                                              "beta2", "eps", "wd_muon", "wd_adamw")] + [
+        ("ns_steps", ctypes.c_int32), ("ns_a", ctypes.c_float), ("ns_b", ctypes.c_float), ("ns_c", ctypes.c_float)]
+
+    def as_dict(self) -> dict:
+        return {k: getattr(self, k) for k, _ in self._fields_}
+
+
 class gpt_tensor_desc(ctypes.Structure):
     _fields_ = [("name", ctypes.c_char * 32), ("offset", ctypes.c_int64), ("rows", ctypes.c_int64),
                 ("cols", ctypes.c_int64)]
@@ -80,6 +89,8 @@ _SIGS = {
     "gpt_debug_buffer": (ctypes.c_int32, [_P, ctypes.c_char_p, ctypes.c_int32, ctypes.POINTER(_P),
                                           ctypes.POINTER(ctypes.c_size_t)]),
     "gpt_fp8_quantize": (ctypes.c_int32, [_P, ctypes.c_int64, ctypes.c_int64, _P, _P, ctypes.c_int64, _P, _P]),
+    "gpt_optimizer_state_elems": (ctypes.c_int32, [ctypes.POINTER(gpt_config), ctypes.POINTER(ctypes.c_int64)]),
+    "gpt_optimizer_step": (ctypes.c_int32, [_P, ctypes.POINTER(gpt_optim_config), _P, _P, ctypes.c_int32, _P]),
     "gpt_fp8_matmul": (ctypes.c_int32, [_P, ctypes.c_int64, _P, _P, ctypes.c_int64, _P, ctypes.c_int32, ctypes.c_int32,
                                         ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int64, ctypes.c_int32,
                                         ctypes.c_int32, _P, _P]),
@@ -221,3 +232,13 @@ def gpt_fp8_matmul(a_ptr, lda, amax_a_ptr, b_ptr, ldb, amax_b_ptr, M, N, K, out_
                    splits=1, partials_ptr=None, stream=0):
     _check(lib().gpt_fp8_matmul(a_ptr, lda, amax_a_ptr, b_ptr, ldb, amax_b_ptr, M, N, K, out_dtype, out_ptr, ldo,
                                 tile, splits, partials_ptr, stream), "gpt_fp8_matmul")
+
+
+def gpt_optimizer_state_elems(cfg: gpt_config) -> int:
+    n = ctypes.c_int64(0)
+    _check(lib().gpt_optimizer_state_elems(ctypes.byref(cfg), ctypes.byref(n)), "gpt_optimizer_state_elems")
+    return n.value
+
+
+def gpt_optimizer_step(h, oc: gpt_optim_config, master_ptr: int, state_ptr: int, t: int, stream: int):
+    _check(lib().gpt_optimizer_step(h, ctypes.byref(oc), master_ptr, state_ptr, t, stream), "gpt_optimizer_step")

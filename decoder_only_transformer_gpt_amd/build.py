@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libgpt_amd.so")
 OBJDIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["gemm.hip", "attention.hip", "norm.hip", "ce.hip", "embed_bwd.hip", "fp8.hip", "resid.hip", "gpt.cpp"]
+SOURCES = ["gemm.hip", "attention.hip", "norm.hip", "ce.hip", "embed_bwd.hip", "fp8.hip", "resid.hip", "optim.hip", "gpt.cpp"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -65,7 +65,7 @@ enum Tag : int {
   K_GEMM_LM, K_CE_LOSS, K_CE_BWD, K_GEMM_LM_DW, K_GEMM_LM_DX, K_RMSNORM_BWD, K_GEMM_W2_DW, K_GEMM_W2_DX,
   K_GEMM_W1_DW, K_GEMM_W1_DX, K_GEMM_O_DW, K_GEMM_O_DX, K_ATTN_BWD_PREP, K_ATTN_BWD_DQ, K_ATTN_BWD_DKV,
   K_ROPE_QKNORM_BWD, K_GEMM_QKV_DW, K_GEMM_QKV_DX, K_EMBED_BWD, K_WEIGHT_T, K_FP8_AMAX, K_FP8_QUANT,
-  K_FP8_WEIGHTS, K_EMBED_SORT, K_X0_MIX, K_X0_MIX_BWD, K_VE_ADD, K_VE_BWD, K_NUM_TAGS
+  K_FP8_WEIGHTS, K_EMBED_SORT, K_X0_MIX, K_X0_MIX_BWD, K_VE_ADD, K_VE_BWD, K_OPT_ADAMW, K_OPT_MUON, K_NUM_TAGS
 };
 
 // |max| slots per layer of an FP8 model (fp32, zeroed at every forward)
@@ -78,7 +78,7 @@ const char* kTagNames[K_NUM_TAGS] = {
   "rmsnorm_bwd", "gemm_w2_dw", "gemm_w2_dx", "gemm_w1_dw", "gemm_w1_dx_relu2bwd", "gemm_o_dw", "gemm_o_dx",
   "attn_bwd_prep", "attn_bwd_dq", "attn_bwd_dkv", "rope_qknorm_bwd", "gemm_qkv_dw", "gemm_qkv_dx", "embed_bwd",
   "weight_transpose", "fp8_amax", "fp8_quantize", "fp8_weights", "embed_sort", "x0_mix", "x0_mix_bwd", "ve_add",
-  "ve_bwd"};
+  "ve_bwd", "opt_adamw", "opt_muon"};
 
 struct Layout {  // byte offsets inside the workspace
   size_t flag, loss_rows, rope_cos, rope_sin;
@@ -99,6 +99,8 @@ struct Layout {  // byte offsets inside the workspace
   // the scalar gradients
   size_t x0, dx0acc, rpart;
   std::vector<size_t> xprev;
+  // optimiser scratch: Newton-Schulz iterates and products, norm partials
+  size_t ns_x, ns_xt, ns_a, ns_aa, ns_b, ns_part;
   size_t keys_a, vals_a, keys_b, vals_b, hist, coef, carry;
   size_t total;
   size_t split_elems;
@@ -243,6 +245,22 @@ Layout plan(const gpt_config& c, int maxB, int maxT) {
     for (int l = 0; l < c.n_layer; ++l) L.xprev.push_back(p.take(N * C * es));
   }
   L.rpart = (c.x0_lambdas || c.value_embeds) ? p.take(gk::resid_partials_elems() * 4) : p.take(0);
+  {
+    // the largest Muon matrix (elements) and its smaller side
+    const size_t mats[4][2] = {{QKV, C}, {C, H * kHeadDim}, {F, C}, {C, F}};
+    size_t big = 0, small2 = 0;
+    for (auto& mm : mats) {
+      big = std::max(big, mm[0] * mm[1]);
+      const size_t sm = std::min(mm[0], mm[1]);
+      small2 = std::max(small2, sm * sm);
+    }
+    L.ns_x = p.take(big * es);
+    L.ns_xt = p.take(big * es);
+    L.ns_a = p.take(small2 * es);
+    L.ns_aa = p.take(small2 * es);
+    L.ns_b = p.take(small2 * es);
+    L.ns_part = p.take(gk::muon_partials_elems() * 4);
+  }
   L.keys_a = p.take(N * 4);
   L.vals_a = p.take(N * 4);
   L.keys_b = p.take(N * 4);
@@ -1046,6 +1064,106 @@ gpt_status gpt_debug_buffer(gpt_model* m, const char* name, int32_t layer, void*
   if (s == "a") return set(L.a[layer], N * (size_t)c.mlp_dim * es);
   if (s == "amax" && c.dtype == GPT_FP8_E4M3) return set(L.amax + (size_t)layer * kAmaxSlots * 4, kAmaxSlots * 4);
   return fail(GPT_E_INVALID_ARG, "unknown buffer '%s'", name);
+}
+
+}  // extern "C"
+
+namespace {
+// Optimiser group of a parameter tensor: 0 Muon (blocks' matrix weights),
+// 1 embeddings (wte, value-embedding tables), 2 unembedding, 3 scalars.
+int optim_group(const std::string& nm) {
+  auto ends = [&](const char* suf) {
+    const size_t n = strlen(suf);
+    return nm.size() >= n && nm.compare(nm.size() - n, n, suf) == 0;
+  };
+  if (nm[0] == 'h' && (ends(".w_qkv") || ends(".w_o") || ends(".w_1") || ends(".w_2"))) return 0;
+  if (nm == "lm_head") return 2;
+  if (nm == "wte" || ends(".ve")) return 1;
+  return 3;
+}
+}  // namespace
+
+extern "C" {
+
+gpt_status gpt_optimizer_state_elems(const gpt_config* c, int64_t* elems) {
+  if (!elems) return fail(GPT_E_INVALID_ARG, "elems is NULL");
+  gpt_status s = gpt_config_validate(c);
+  if (s != GPT_OK) return s;
+  int32_t n = 0;
+  gpt_param_layout(c, nullptr, &n);
+  std::vector<gpt_tensor_desc> d(n);
+  gpt_param_layout(c, d.data(), &n);
+  int64_t tot = 0;
+  for (auto& t : d) tot += (optim_group(t.name) == 0 ? 1 : 2) * t.rows * t.cols;
+  *elems = tot;
+  return GPT_OK;
+}
+
+gpt_status gpt_optimizer_step(gpt_model* m, const gpt_optim_config* oc, float* master, float* state, int32_t t,
+                              void* stream_) {
+  if (!m || !oc || !master || !state) return fail(GPT_E_INVALID_ARG, "NULL argument");
+  if (t < 1) return fail(GPT_E_INVALID_ARG, "the step number t must be >= 1");
+  if (oc->ns_steps < 0 || oc->ns_steps > 100) return fail(GPT_E_INVALID_ARG, "ns_steps must be in [0, 100]");
+  if (!(oc->beta1 >= 0.f && oc->beta1 < 1.f && oc->beta2 >= 0.f && oc->beta2 < 1.f && oc->eps > 0.f))
+    return fail(GPT_E_INVALID_ARG, "need 0 <= beta1, beta2 < 1 and eps > 0");
+  if (((uintptr_t)master & 15) || ((uintptr_t)state & 15))
+    return fail(GPT_E_INVALID_ARG, "master and state must be 16-byte aligned");
+  hipStream_t stream = (hipStream_t)stream_;
+  const gpt_config& c = m->cfg;
+  const int dt = c.dtype == GPT_F32 ? GPT_F32 : GPT_BF16;  // the parameters' storage dtype
+  const Layout& L = m->L;
+  int32_t n = 0;
+  gpt_param_layout(&c, nullptr, &n);
+  std::vector<gpt_tensor_desc> d(n);
+  gpt_param_layout(&c, d.data(), &n);
+  char* params = reinterpret_cast<char*>(const_cast<void*>(m->params));
+  const double bc1 = 1.0 - std::pow((double)oc->beta1, (double)t);
+  const double bc2 = 1.0 - std::pow((double)oc->beta2, (double)t);
+  int64_t soff = 0;
+  for (const auto& td : d) {
+    const int grp = optim_group(td.name);
+    const int64_t ne = td.rows * td.cols;
+    if (grp == 0) {
+      RUN(K_OPT_MUON, {
+        gk::MuonArgs a;
+        a.w = master + td.offset;
+        a.g = m->grads + td.offset;
+        a.u = state + soff;
+        a.out = params + td.offset * (int64_t)esize(dt);
+        a.rows = (int)td.rows;
+        a.cols = (int)td.cols;
+        a.lr = oc->lr_muon;
+        a.mu = oc->momentum;
+        a.wd = oc->wd_muon;
+        a.steps = oc->ns_steps;
+        a.a = oc->ns_a; a.b = oc->ns_b; a.c = oc->ns_c;
+        a.X = m->ws + L.ns_x; a.XT = m->ws + L.ns_xt;
+        a.A = m->ws + L.ns_a; a.AA = m->ws + L.ns_aa; a.Bm = m->ws + L.ns_b;
+        a.partials = wsp<float>(m, L.ns_part);
+        a.inv = wsp<float>(m, L.ns_part) + gk::muon_partials_elems() - 16;
+        return gk::launch_muon(dt, a, stream);
+      });
+      soff += ne;
+    } else {
+      const float lr = grp == 1 ? oc->lr_embed : grp == 2 ? oc->lr_unembed : oc->lr_scalar;
+      RUN(K_OPT_ADAMW, {
+        gk::AdamwArgs a;
+        a.w = master + td.offset;
+        a.g = m->grads + td.offset;
+        a.m = state + soff;
+        a.v = state + soff + ne;
+        a.out = params + td.offset * (int64_t)esize(dt);
+        a.n = ne;
+        a.lr = lr;
+        a.beta1 = oc->beta1; a.beta2 = oc->beta2; a.eps = oc->eps; a.wd = oc->wd_adamw;
+        a.step_size = (float)(lr / bc1);
+        a.inv_sqrt_bc2 = (float)(1.0 / std::sqrt(bc2));
+        return gk::launch_adamw(dt, a, stream);
+      });
+      soff += 2 * ne;
+    }
+  }
+  return GPT_OK;
 }
 
 gpt_status gpt_fp8_matmul(const uint8_t* a, int64_t lda, const float* amax_a, const uint8_t* b, int64_t ldb,

@@ -180,4 +180,35 @@ hipError_t launch_fp8_quantize(const QuantDesc& d, hipStream_t s);
 hipError_t launch_fp8_amax_batched(const QuantDesc* table, int n, int64_t total_blocks, hipStream_t s);
 hipError_t launch_fp8_quantize_batched(const QuantDesc* table, int n, int64_t total_blocks, hipStream_t s);
 
+// Optimiser -------------------------------------------------------------------
+struct AdamwArgs {
+  float* w;            // fp32 master [n]
+  const float* g;      // fp32 gradient [n]
+  float* m;            // first moment [n]
+  float* v;            // second moment [n]
+  void* out;           // the model's copy (model dtype) [n]
+  int64_t n;
+  float lr, beta1, beta2, eps, wd;
+  float step_size;     // lr / (1 - beta1^t)
+  float inv_sqrt_bc2;  // 1 / sqrt(1 - beta2^t)
+};
+hipError_t launch_adamw(int dtype, const AdamwArgs& a, hipStream_t s);
+struct MuonArgs {
+  float* w;            // fp32 master [rows, cols]
+  const float* g;      // fp32 gradient
+  float* u;            // momentum
+  void* out;           // the model's copy (model dtype)
+  int rows, cols;
+  float lr, mu, wd;
+  int steps;           // Newton-Schulz steps
+  float a, b, c;       // X <- a X + (b A + c A^2) X
+  // scratch (model dtype unless noted): X and X^T [min*max], A, AA, Bm [min^2],
+  // partials (fp32, muon_partials_elems()), inv (fp32 scalar)
+  void *X, *XT, *A, *AA, *Bm;
+  float* partials;
+  float* inv;
+};
+size_t muon_partials_elems();
+hipError_t launch_muon(int dtype, const MuonArgs& a, hipStream_t s);
+
 }  // namespace gk

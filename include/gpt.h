@@ -251,6 +251,47 @@ gpt_status gpt_fp8_matmul(const uint8_t* a, int64_t lda, const float* amax_a, co
                           const float* amax_b, int32_t M, int32_t N, int32_t K, int32_t out_dtype, void* out,
                           int64_t ldo, int32_t tile, int32_t splits, float* partials, void* stream);
 
+/* ---- The optimiser step after the backward ------------------------------
+ * Muon for the blocks' matrix weights (w_qkv, w_o, w_1, w_2), AdamW for the
+ * embeddings (wte and the value-embedding tables), the unembedding (lm_head)
+ * and the scalars, on fp32 master weights whose cast to the config dtype
+ * (round to nearest even) becomes the model's parameters (atlas.blal.pro
+ * "nanochat — full-stack ChatGPT in ~8k lines", section "How it works", item
+ * "2. Pretrain"; aethryn.com "Nanochat: full-stack LLM training in 8,000 lines
+ * for $72", section "A Llama-class transformer with ten modern departures";
+ * energyai.berlin "nanochat vs GPT-OSS", section "Muon optimizer").
+ * AdamW: w <- w (1 - lr wd); m <- b1 m + (1 - b1) g; v <- b2 v + (1 - b2) g^2;
+ * w <- w - lr / (1 - b1^t) * m / (sqrt(v) / sqrt(1 - b2^t) + eps).
+ * Muon: u <- momentum u + g; X_0 = u / (||u||_F + 1e-7) in the orientation
+ * with fewer rows; ns_steps times X <- a X + (b A + c A^2) X with A = X X^T
+ * (products in the config dtype, fp32 accumulation); w <- w (1 - lr wd) -
+ * lr sqrt(max(1, rows / cols)) X. (a, b, c) = (1.5, -0.5, 0) is the cubic
+ * Newton-Schulz iteration towards the orthogonal polar factor of u. The
+ * caller applies its own schedules through the per-step values. */
+typedef struct gpt_optim_config {
+  float lr_muon, lr_embed, lr_unembed, lr_scalar;
+  float momentum;          /* Muon momentum of this step */
+  float beta1, beta2, eps; /* AdamW */
+  float wd_muon, wd_adamw; /* decoupled weight decay of each group */
+  int32_t ns_steps;        /* 0..100 */
+  float ns_a, ns_b, ns_c;
+} gpt_optim_config;
+
+/* fp32 elements of optimiser state: per parameter tensor in the canonical
+ * order, Muon tensors hold u [rows, cols], AdamW tensors m then v [rows, cols]
+ * each. Host only. */
+gpt_status gpt_optimizer_state_elems(const gpt_config* cfg, int64_t* elems);
+
+/* One optimiser step from the gradient buffer of the handle (as the last
+ * gpt_backward left it). master: device fp32 [param_count] master weights,
+ * updated in place; state: device fp32 [gpt_optimizer_state_elems], zero
+ * before the first step; t: the 1-based step number (bias correction).
+ * Writes the cast of the updated masters into the parameter buffer given to
+ * gpt_init (the only call that writes it). Uses the handle's workspace as
+ * scratch. Asynchronous on `stream`; GPT_E_INVALID_ARG on bad arguments. */
+gpt_status gpt_optimizer_step(gpt_model* m, const gpt_optim_config* oc, float* master, float* state, int32_t t,
+                              void* stream);
+
 #ifdef __cplusplus
 }
 #endif
