@@ -28,16 +28,34 @@ def d4_cfg():
     return c
 
 
+def vanishing(go: dict, k: str) -> bool:
+    """A gradient the mathematics makes exactly zero (e.g. W_q and W_k with
+    one-token rows, where the softmax is 1 whatever q and k are): its norm is
+    below 1e-12 of the whole gradient's. The GPU's value is then rounding
+    residue (dP - delta cancels), checked against the whole gradient's scale."""
+    total = np.sqrt(sum(float(np.sum(v * v)) for v in go.values()))
+    return float(np.linalg.norm(go[k])) <= 1e-12 * total
+
+
+def check_vanishing(gg, go, k, tol):
+    total = np.sqrt(sum(float(np.sum(v * v)) for v in go.values()))
+    assert float(np.linalg.norm(gg[k])) <= tol * total, k
+
+
 def check_fp32(case, gpu, loss, G, label):
     rel = abs(gpu["loss"] - loss) / abs(loss)
     U.log(f"[{label}] loss gpu={gpu['loss']:.9f} oracle={loss:.9f} rel={rel:.2e}")
     assert rel <= 1e-5
     gg = U.split_tensors(case, gpu["grads"])
     go = U.split_tensors(case, case.flat_grads(G))
-    worst = max((U.rel_l2(gg[k], go[k]), k) for k in go)
+    live = [k for k in go if not vanishing(go, k)]
+    worst = max((U.rel_l2(gg[k], go[k]), k) for k in live)
     U.log(f"[{label}] worst grad rel L2 {worst[0]:.2e} ({worst[1]})")
     for k in go:
-        assert U.rel_l2(gg[k], go[k]) <= 1e-4, k
+        if k in live:
+            assert U.rel_l2(gg[k], go[k]) <= 1e-4, k
+        else:
+            check_vanishing(gg, go, k, 1e-4)
 
 
 def check_bf16(case, gpu, loss, G, label):
@@ -46,10 +64,14 @@ def check_bf16(case, gpu, loss, G, label):
     assert rel <= 5e-3
     gg = U.split_tensors(case, gpu["grads"])
     go = U.split_tensors(case, case.flat_grads(G))
-    worst = min((U.cosine(gg[k], go[k]), k) for k in go)
+    live = [k for k in go if not vanishing(go, k)]
+    worst = min((U.cosine(gg[k], go[k]), k) for k in live)
     U.log(f"[{label}] worst grad cosine {worst[0]:.6f} ({worst[1]})")
     for k in go:
-        assert U.cosine(gg[k], go[k]) >= 0.999, k
+        if k in live:
+            assert U.cosine(gg[k], go[k]) >= 0.999, k
+        else:
+            check_vanishing(gg, go, k, 4.5e-2)
 
 
 @pytest.mark.parametrize("tile", [0, 1, 2, 3])
@@ -215,3 +237,32 @@ def test_d20_sssl_one_row():
     gpu = U.run_gpu(case)
     loss, rows, G = O.step(U.oracle_cfg(case.cfg), case.oracle_params(), case.idx, case.tgt)
     check_bf16(case, gpu, loss, G, "d20-sssl-B1")
+
+
+# ------------------------------------------------------- degenerate sizes ---
+
+@pytest.mark.parametrize("B,T", [(5, 1), (1, 2), (3, 65)])
+def test_tiny_fp32_degenerate_lengths(B, T):
+    """One-token rows (attention over the query itself only: the W_q and W_k
+    gradients vanish), two tokens, and one token past a 64-row tile; the
+    handle is built for a longer maximum."""
+    U.require_gpu()
+    case = U.Case(tiny_cfg(T=128), B=B, T=T, law="uniform", wseed=40 + T, tseed=41 + T)
+    U.log(f"case tiny fp32 B={B} T={T} (max 8 x 128)")
+    gpu = U.run_gpu(case, max_B=8, max_T=128)
+    assert gpu["status"] == _lib.GPT_OK
+    loss, rows, G = O.step(U.oracle_cfg(case.cfg), case.oracle_params(), case.idx, case.tgt)
+    np.testing.assert_allclose(gpu["row_loss"], rows.reshape(-1), rtol=2e-5)
+    check_fp32(case, gpu, loss, G, f"tiny-B{B}-T{T}")
+
+
+@pytest.mark.parametrize("B,T", [(7, 1), (2, 3)])
+def test_bf16_degenerate_lengths(B, T):
+    """bf16 d4 with one- and three-token rows (every GEMM's M far below a tile)."""
+    U.require_gpu()
+    case = U.Case(d4_cfg(), B=B, T=T, law="zipf", wseed=42 + T, tseed=43 + T)
+    U.log(f"case d4 bf16 B={B} T={T}")
+    gpu = U.run_gpu(case, max_B=8, max_T=512)
+    assert gpu["status"] == _lib.GPT_OK
+    loss, rows, G = O.step(U.oracle_cfg(case.cfg), case.oracle_params(), case.idx, case.tgt)
+    check_bf16(case, gpu, loss, G, f"d4-B{B}-T{T}")
