@@ -136,6 +136,22 @@ DEV void xcd_row_map(int id, int B, int per_row, int& b, int& r) {
   }
 }
 
+// Heavy-first order across every row an XCD holds, for kernels that run one
+// block per CU: XCD x (blocks id % 8 == x) holds rows x, x+8, ...; its j-th
+// block takes level j / rows (level 0 = most work) of row x + 8 (j % rows).
+// The greedy dispatcher then starts each light late block on the CU of an
+// early heavy one. Any B: level-major over all rows.
+DEV void xcd_level_map(int id, int B, int& b, int& level) {
+  if ((B & 7) == 0) {
+    const int x = id & 7, j = id >> 3, rows = B >> 3;
+    level = j / rows;
+    b = x + 8 * (j % rows);
+  } else {
+    level = id / B;
+    b = id % B;
+  }
+}
+
 DEV f32x16 zero16() {
   f32x16 z;
 #pragma unroll
@@ -584,9 +600,11 @@ __global__ __launch_bounds__(256) void attn_dkv_kernel(const T* __restrict__ qkv
 // lets the compiler prove the reads of the current stage independent of the
 // loads in flight, instead of waiting for all of them).
 //
-// Softmax: P = exp2(S * log2(e)/sqrt(D) - lse2) on v_exp_f32. Query
-// or key tiles that lie entirely on the allowed side of the diagonal skip the
-// mask; tiles entirely past it are skipped per wave.
+// Softmax: P = exp2(S * log2(e)/sqrt(D) - lse2) on v_exp_f32. Every tile
+// goes through the masked body (the causal / window test is a few VALU ops
+// per element; a second, unmasked body costs more in register spills and
+// accumulator copies than it saves); tiles entirely outside the band are
+// skipped per wave.
 
 constexpr int kRowB = 256;          // bytes per tile row (128 bf16)
 constexpr int kFwdStages = 2;       // 64 KiB of LDS: two blocks per CU
@@ -665,7 +683,6 @@ struct KvStage {
 // ---------------------------------------------------------- forward (bf16) --
 // Block: 128 queries of one (batch, head) = 4 waves x 32; key tiles of 64.
 // S^T = K Q^T puts each query on one lane (its row sum stays in the lane).
-template <bool MASK>
 DEV void fwd_tile(const KvStage& s, const RowFrag& rf, const TrFrag& tf, const u32x4 (&qf)[8], f32x16 (&acc)[4],
                   float& rsum, float sl2, float sh2, int krel, int Wl) {
   f32x16 sc[2];
@@ -695,10 +712,8 @@ DEV void fwd_tile(const KvStage& s, const RowFrag& rf, const TrFrag& tf, const u
     for (int i = 0; i < 16; ++i) {
       float p = fast_exp2(sc[kb2][i] * sl2 - sh2);
       // key (tile row kb2*32 + (i/4)*8 + 4g + i%4) <= query, within the window
-      if (MASK) {
-        const int dd = kb2 * 32 + (i >> 2) * 8 + (i & 3) + krel;  // key - query
-        p = (dd <= 0 && dd > -Wl) ? p : 0.f;
-      }
+      const int dd = kb2 * 32 + (i >> 2) * 8 + (i & 3) + krel;  // key - query
+      p = (dd <= 0 && dd > -Wl) ? p : 0.f;
       sc[kb2][i] = p;
       rsum += p;
     }
@@ -760,8 +775,8 @@ __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void attn_fwd_bf16_kernel(co
     issue(min(t + NST - 1, nt - 1), nxt);
     const int k0 = (t0 + t) * 64;
     if (k0 > qw + 31 || k0 + 63 <= qw - Wl) return;  // the tile misses every query's band
-    if (k0 + 63 <= qw && k0 >= qw + 32 - Wl) fwd_tile<false>(cur, rf, tf, qf, acc, rsum, sl2, sh2, 0, Wl);
-    else fwd_tile<true>(cur, rf, tf, qf, acc, rsum, sl2, sh2, k0 + 4 * g - q, Wl);
+    // one masked body for every tile (an unmasked twin spills registers)
+    fwd_tile(cur, rf, tf, qf, acc, rsum, sl2, sh2, k0 + 4 * g - q, Wl);
   };
   if constexpr (NST == 4) {
     issue(0, st0);
@@ -799,7 +814,6 @@ __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void attn_fwd_bf16_kernel(co
 
 // --------------------------------------------------------------- dQ (bf16) --
 // Block: 128 queries of one (batch, head) = 4 waves x 32; key tiles of 64.
-template <bool MASK>
 DEV void dq_tile(const KvStage& s, const RowFrag& rf, const TrFrag& tf, const u32x4 (&qf)[8], const u32x4 (&df)[8],
                  f32x16 (&acc)[4], float sl2, float l2, float dlt, int krel, int Wl) {
   f32x16 sc[2], dp[2];
@@ -818,10 +832,8 @@ DEV void dq_tile(const KvStage& s, const RowFrag& rf, const TrFrag& tf, const u3
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       float p = fast_exp2(sc[kb2][i] * sl2 - l2);
-      if (MASK) {
-        const int dd = kb2 * 32 + (i >> 2) * 8 + (i & 3) + krel;  // key - query
-        p = (dd <= 0 && dd > -Wl) ? p : 0.f;
-      }
+      const int dd = kb2 * 32 + (i >> 2) * 8 + (i & 3) + krel;  // key - query
+      p = (dd <= 0 && dd > -Wl) ? p : 0.f;
       dp[kb2][i] = p * (dp[kb2][i] - dlt);
     }
 #pragma unroll
@@ -885,8 +897,8 @@ __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void attn_dq_bf16_kernel(con
     issue(min(t + NST - 1, nt - 1), nxt);
     const int k0 = (t0 + t) * 64;
     if (k0 > qw + 31 || k0 + 63 <= qw - Wl) return;  // the tile misses every query's band
-    if (k0 + 63 <= qw && k0 >= qw + 32 - Wl) dq_tile<false>(cur, rf, tf, qf, df, acc, sl2, l2, dlt, 0, Wl);
-    else dq_tile<true>(cur, rf, tf, qf, df, acc, sl2, l2, dlt, k0 + 4 * g - q, Wl);
+    // one masked body for every tile (an unmasked twin spills registers)
+    dq_tile(cur, rf, tf, qf, df, acc, sl2, l2, dlt, k0 + 4 * g - q, Wl);
   };
   if constexpr (NST == 4) {
     issue(0, st0);
@@ -931,7 +943,6 @@ struct DkvStage {
   float e[4][64];  // delta
 };
 
-template <bool MASK>
 DEV void dkv_tile(const DkvStage& s, int wave, const RowFrag& rf, const TrFrag& tf, const u32x4 (&kf)[8],
                   const u32x4 (&vf)[8], f32x16 (&adk)[4], f32x16 (&adv)[4], float sl2, int qrel, int Wl, int g) {
   f32x16 sc[2], dp[2];
@@ -980,10 +991,8 @@ DEV void dkv_tile(const DkvStage& s, int wave, const RowFrag& rf, const TrFrag& 
         const int i = blk * 4 + r;
         float p = fast_exp2(sc[qb2][i] * sl2 - L[r]);
         // query (tile row qb2*32 + blk*8 + 4g + r) >= key, within the window
-        if (MASK) {
-          const int dd = qb2 * 32 + blk * 8 + r + qrel;  // query - key
-          p = (dd >= 0 && dd < Wl) ? p : 0.f;
-        }
+        const int dd = qb2 * 32 + blk * 8 + r + qrel;  // query - key
+        p = (dd >= 0 && dd < Wl) ? p : 0.f;
         sc[qb2][i] = p;
         dp[qb2][i] = p * (dp[qb2][i] - E[r]);
       }
@@ -1015,7 +1024,7 @@ __global__ __launch_bounds__(256, 1) void attn_dkv_bf16_kernel(const bf16* __res
   __shared__ __attribute__((aligned(1024))) DkvStage st0, st1, st2, st3;
   const int nkb = (T_ + 127) / 128;
   int b, kb;
-  xcd_row_map(blockIdx.x, gridDim.x / nkb, nkb, b, kb);  // key block 0 (most query tiles) first
+  xcd_level_map(blockIdx.x, gridDim.x / nkb, b, kb);  // key block 0 (most query tiles) first
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t ld = (int64_t)(H + 2) * D;
@@ -1061,8 +1070,10 @@ __global__ __launch_bounds__(256, 1) void attn_dkv_bf16_kernel(const bf16* __res
     issue(min(it + 3, total - 1), nxt);
     const int q0 = (nqt - 1 - it / H) * 64;
     if (q0 + 63 < kw || q0 - (kw + 31) >= Wl) return;  // the tile misses every key's band
-    if (q0 >= kw + 31 && q0 + 63 - kw < Wl) dkv_tile<false>(cur, wave, rf, tf, kf, vf, adk, adv, sl2, 0, Wl, g);
-    else dkv_tile<true>(cur, wave, rf, tf, kf, vf, adk, adv, sl2, q0 + 4 * g - key, Wl, g);
+    // One (masked) tile body for every tile: a second, unmasked body makes
+    // the register allocator shuffle the dK/dV accumulators between the two
+    // at every step.
+    dkv_tile(cur, wave, rf, tf, kf, vf, adk, adv, sl2, q0 + 4 * g - key, Wl, g);
   };
   issue(0, st0);
   issue(min(1, total - 1), st1);
