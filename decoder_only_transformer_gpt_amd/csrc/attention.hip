@@ -600,11 +600,9 @@ __global__ __launch_bounds__(256) void attn_dkv_kernel(const T* __restrict__ qkv
 // lets the compiler prove the reads of the current stage independent of the
 // loads in flight, instead of waiting for all of them).
 //
-// Softmax: P = exp2(S * log2(e)/sqrt(D) - lse2) on v_exp_f32. Every tile
-// goes through the masked body (the causal / window test is a few VALU ops
-// per element; a second, unmasked body costs more in register spills and
-// accumulator copies than it saves); tiles entirely outside the band are
-// skipped per wave.
+// Softmax: P = exp2(S * log2(e)/sqrt(D) - lse2) on v_exp_f32. Tiles that
+// lie inside the band of every row of the block skip the mask (a few VALU
+// ops per element); tiles entirely outside the band are skipped per wave.
 
 constexpr int kRowB = 256;          // bytes per tile row (128 bf16)
 constexpr int kFwdStages = 2;       // 64 KiB of LDS: two blocks per CU
@@ -683,6 +681,7 @@ struct KvStage {
 // ---------------------------------------------------------- forward (bf16) --
 // Block: 128 queries of one (batch, head) = 4 waves x 32; key tiles of 64.
 // S^T = K Q^T puts each query on one lane (its row sum stays in the lane).
+template <bool MASK>
 DEV void fwd_tile(const KvStage& s, const RowFrag& rf, const TrFrag& tf, const u32x4 (&qf)[8], f32x16 (&acc)[4],
                   float& rsum, float sl2, float sh2, int krel, int Wl) {
   f32x16 sc[2];
@@ -712,8 +711,10 @@ DEV void fwd_tile(const KvStage& s, const RowFrag& rf, const TrFrag& tf, const u
     for (int i = 0; i < 16; ++i) {
       float p = fast_exp2(sc[kb2][i] * sl2 - sh2);
       // key (tile row kb2*32 + (i/4)*8 + 4g + i%4) <= query, within the window
-      const int dd = kb2 * 32 + (i >> 2) * 8 + (i & 3) + krel;  // key - query
-      p = (dd <= 0 && dd > -Wl) ? p : 0.f;
+      if (MASK) {
+        const int dd = kb2 * 32 + (i >> 2) * 8 + (i & 3) + krel;  // key - query
+        p = (dd <= 0 && dd > -Wl) ? p : 0.f;
+      }
       sc[kb2][i] = p;
       rsum += p;
     }
@@ -733,8 +734,7 @@ __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void attn_fwd_bf16_kernel(co
                                                                               int H, int W, bf16* __restrict__ o,
                                                                               float* __restrict__ lse) {
   static_assert(NST == 2 || NST == 4, "two or four stages");
-  __shared__ __attribute__((aligned(1024))) KvStage st0, st1;
-  __shared__ __attribute__((aligned(1024))) std::conditional_t<NST == 4, KvStage, char[16]> st2, st3;
+  __shared__ __attribute__((aligned(1024))) KvStage st[NST];
   const int nqb = (T_ + 127) / 128;
   int b, r;
   xcd_row_map(blockIdx.x, gridDim.x / (nqb * H), nqb * H, b, r);
@@ -769,32 +769,28 @@ __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void attn_fwd_bf16_kernel(co
     tile_issue(uniform_rsrc(kp, rows * (int)ld_b), s.k, vo, wave);
     tile_issue(uniform_rsrc(kp + D, rows * (int)ld_b), s.v, vo, wave);
   };
-  auto step = [&](int t, const KvStage& cur, KvStage& nxt) {
+  auto step = [&](int t, auto masked) {
     wait_vmcnt<(NST - 2) * 8>();  // this wave's part of tile t has landed
     __builtin_amdgcn_s_barrier();
-    issue(min(t + NST - 1, nt - 1), nxt);
+    issue(min(t + NST - 1, nt - 1), st[(t + NST - 1) % NST]);
     const int k0 = (t0 + t) * 64;
     if (k0 > qw + 31 || k0 + 63 <= qw - Wl) return;  // the tile misses every query's band
-    // one masked body for every tile (an unmasked twin spills registers)
-    fwd_tile(cur, rf, tf, qf, acc, rsum, sl2, sh2, k0 + 4 * g - q, Wl);
+    fwd_tile<decltype(masked)::value>(st[t % NST], rf, tf, qf, acc, rsum, sl2, sh2, k0 + 4 * g - q, Wl);
   };
-  if constexpr (NST == 4) {
-    issue(0, st0);
-    issue(min(1, nt - 1), st1);
-    issue(min(2, nt - 1), st2);
-    for (int t = 0; t < nt; t += 4) {
-      step(t, st0, st3);
-      if (t + 1 < nt) step(t + 1, st1, st0);
-      if (t + 2 < nt) step(t + 2, st2, st1);
-      if (t + 3 < nt) step(t + 3, st3, st2);
-    }
-  } else {
-    issue(0, st0);
-    for (int t = 0; t < nt; t += 2) {
-      step(t, st0, st1);
-      if (t + 1 < nt) step(t + 1, st1, st0);
-    }
-  }
+  // Key tiles (ascending) fall into three runs: tiles that cross the far
+  // edge of some query's window, tiles inside the band of every query of the
+  // block (no mask), and tiles that cross the diagonal; one loop per run (see
+  // the dK/dV kernel for why).
+  const int lo_num = qb * 128 + 127 - Wl;  // first key tile with t - u < Wl for all its pairs
+  const int kt_lo = lo_num >= 0 ? lo_num / 64 + 1 : 0;
+  const int t_a = min(nt, max(0, kt_lo - t0));
+  const int t_b = min(nt, max(t_a, 2 * qb - t0));  // key tiles up to 2qb - 1 precede every query
+#pragma unroll
+  for (int i = 0; i < NST - 1; ++i) issue(min(i, nt - 1), st[i]);
+  int t = 0;
+  for (; t < t_a; ++t) step(t, std::true_type{});
+  for (; t < t_b; ++t) step(t, std::false_type{});
+  for (; t < nt; ++t) step(t, std::true_type{});
   wait_vmcnt<0>();
   rsum += __shfl_xor(rsum, 32, 64);
   if (q < T_) {
@@ -814,6 +810,7 @@ __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void attn_fwd_bf16_kernel(co
 
 // --------------------------------------------------------------- dQ (bf16) --
 // Block: 128 queries of one (batch, head) = 4 waves x 32; key tiles of 64.
+template <bool MASK>
 DEV void dq_tile(const KvStage& s, const RowFrag& rf, const TrFrag& tf, const u32x4 (&qf)[8], const u32x4 (&df)[8],
                  f32x16 (&acc)[4], float sl2, float l2, float dlt, int krel, int Wl) {
   f32x16 sc[2], dp[2];
@@ -832,8 +829,10 @@ DEV void dq_tile(const KvStage& s, const RowFrag& rf, const TrFrag& tf, const u3
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       float p = fast_exp2(sc[kb2][i] * sl2 - l2);
-      const int dd = kb2 * 32 + (i >> 2) * 8 + (i & 3) + krel;  // key - query
-      p = (dd <= 0 && dd > -Wl) ? p : 0.f;
+      if (MASK) {
+        const int dd = kb2 * 32 + (i >> 2) * 8 + (i & 3) + krel;  // key - query
+        p = (dd <= 0 && dd > -Wl) ? p : 0.f;
+      }
       dp[kb2][i] = p * (dp[kb2][i] - dlt);
     }
 #pragma unroll
@@ -851,8 +850,7 @@ __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void attn_dq_bf16_kernel(con
                                                                              const float* __restrict__ delta, int T_,
                                                                              int H, int W, bf16* __restrict__ dqkv) {
   static_assert(NST == 2 || NST == 4, "two or four stages");
-  __shared__ __attribute__((aligned(1024))) KvStage st0, st1;
-  __shared__ __attribute__((aligned(1024))) std::conditional_t<NST == 4, KvStage, char[16]> st2, st3;
+  __shared__ __attribute__((aligned(1024))) KvStage st[NST];
   const int nqb = (T_ + 127) / 128;
   int b, r;
   xcd_row_map(blockIdx.x, gridDim.x / (nqb * H), nqb * H, b, r);
@@ -891,32 +889,28 @@ __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void attn_dq_bf16_kernel(con
     tile_issue(uniform_rsrc(kp, rows * (int)ld_b), s.k, vo, wave);
     tile_issue(uniform_rsrc(kp + D, rows * (int)ld_b), s.v, vo, wave);
   };
-  auto step = [&](int t, const KvStage& cur, KvStage& nxt) {
+  auto step = [&](int t, auto masked) {
     wait_vmcnt<(NST - 2) * 8>();  // this wave's part of tile t has landed
     __builtin_amdgcn_s_barrier();
-    issue(min(t + NST - 1, nt - 1), nxt);
+    issue(min(t + NST - 1, nt - 1), st[(t + NST - 1) % NST]);
     const int k0 = (t0 + t) * 64;
     if (k0 > qw + 31 || k0 + 63 <= qw - Wl) return;  // the tile misses every query's band
-    // one masked body for every tile (an unmasked twin spills registers)
-    dq_tile(cur, rf, tf, qf, df, acc, sl2, l2, dlt, k0 + 4 * g - q, Wl);
+    dq_tile<decltype(masked)::value>(st[t % NST], rf, tf, qf, df, acc, sl2, l2, dlt, k0 + 4 * g - q, Wl);
   };
-  if constexpr (NST == 4) {
-    issue(0, st0);
-    issue(min(1, nt - 1), st1);
-    issue(min(2, nt - 1), st2);
-    for (int t = 0; t < nt; t += 4) {
-      step(t, st0, st3);
-      if (t + 1 < nt) step(t + 1, st1, st0);
-      if (t + 2 < nt) step(t + 2, st2, st1);
-      if (t + 3 < nt) step(t + 3, st3, st2);
-    }
-  } else {
-    issue(0, st0);
-    for (int t = 0; t < nt; t += 2) {
-      step(t, st0, st1);
-      if (t + 1 < nt) step(t + 1, st1, st0);
-    }
-  }
+  // Key tiles (ascending) fall into three runs: tiles that cross the far
+  // edge of some query's window, tiles inside the band of every query of the
+  // block (no mask), and tiles that cross the diagonal; one loop per run (see
+  // the dK/dV kernel for why).
+  const int lo_num = qb * 128 + 127 - Wl;  // first key tile with t - u < Wl for all its pairs
+  const int kt_lo = lo_num >= 0 ? lo_num / 64 + 1 : 0;
+  const int t_a = min(nt, max(0, kt_lo - t0));
+  const int t_b = min(nt, max(t_a, 2 * qb - t0));  // key tiles up to 2qb - 1 precede every query
+#pragma unroll
+  for (int i = 0; i < NST - 1; ++i) issue(min(i, nt - 1), st[i]);
+  int t = 0;
+  for (; t < t_a; ++t) step(t, std::true_type{});
+  for (; t < t_b; ++t) step(t, std::false_type{});
+  for (; t < nt; ++t) step(t, std::true_type{});
   wait_vmcnt<0>();
   if (qv) {
     bf16* outp = dqkv + ((int64_t)b * T_ + q) * ld + h * D;
@@ -943,6 +937,7 @@ struct DkvStage {
   float e[4][64];  // delta
 };
 
+template <bool MASK>
 DEV void dkv_tile(const DkvStage& s, int wave, const RowFrag& rf, const TrFrag& tf, const u32x4 (&kf)[8],
                   const u32x4 (&vf)[8], f32x16 (&adk)[4], f32x16 (&adv)[4], float sl2, int qrel, int Wl, int g) {
   f32x16 sc[2], dp[2];
@@ -991,8 +986,10 @@ DEV void dkv_tile(const DkvStage& s, int wave, const RowFrag& rf, const TrFrag& 
         const int i = blk * 4 + r;
         float p = fast_exp2(sc[qb2][i] * sl2 - L[r]);
         // query (tile row qb2*32 + blk*8 + 4g + r) >= key, within the window
-        const int dd = qb2 * 32 + blk * 8 + r + qrel;  // query - key
-        p = (dd >= 0 && dd < Wl) ? p : 0.f;
+        if (MASK) {
+          const int dd = qb2 * 32 + blk * 8 + r + qrel;  // query - key
+          p = (dd >= 0 && dd < Wl) ? p : 0.f;
+        }
         sc[qb2][i] = p;
         dp[qb2][i] = p * (dp[qb2][i] - E[r]);
       }
@@ -1021,7 +1018,7 @@ __global__ __launch_bounds__(256, 1) void attn_dkv_bf16_kernel(const bf16* __res
                                                                const float* __restrict__ lse,
                                                                const float* __restrict__ delta, int T_, int H,
                                                                int W, bf16* __restrict__ dqkv) {
-  __shared__ __attribute__((aligned(1024))) DkvStage st0, st1, st2, st3;
+  __shared__ __attribute__((aligned(1024))) DkvStage st[4];
   const int nkb = (T_ + 127) / 128;
   int b, kb;
   xcd_level_map(blockIdx.x, gridDim.x / nkb, b, kb);  // key block 0 (most query tiles) first
@@ -1064,26 +1061,34 @@ __global__ __launch_bounds__(256, 1) void attn_dkv_bf16_kernel(const bf16* __res
     lds_direct4(uniform_rsrc(lse + lo, rows * 4), &s.l[wave][0], (uint32_t)lane * 4u);
     lds_direct4(uniform_rsrc(delta + lo, rows * 4), &s.e[wave][0], (uint32_t)lane * 4u);
   };
-  auto step = [&](int it, const DkvStage& cur, DkvStage& nxt) {
+  // Step it consumes stage it % 4 and requests step it + 3 into stage
+  // (it + 3) % 4, last read in step it - 1, which every wave finished before
+  // this step's barrier.
+  auto step = [&](int it, auto masked) {
     wait_vmcnt<2 * 10>();  // this wave's part of step it's tiles has landed
     __builtin_amdgcn_s_barrier();
-    issue(min(it + 3, total - 1), nxt);
+    issue(min(it + 3, total - 1), st[(it + 3) & 3]);
     const int q0 = (nqt - 1 - it / H) * 64;
     if (q0 + 63 < kw || q0 - (kw + 31) >= Wl) return;  // the tile misses every key's band
-    // One (masked) tile body for every tile: a second, unmasked body makes
-    // the register allocator shuffle the dK/dV accumulators between the two
-    // at every step.
-    dkv_tile(cur, wave, rf, tf, kf, vf, adk, adv, sl2, q0 + 4 * g - key, Wl, g);
+    dkv_tile<decltype(masked)::value>(st[it & 3], wave, rf, tf, kf, vf, adk, adv, sl2, q0 + 4 * g - key, Wl, g);
   };
-  issue(0, st0);
-  issue(min(1, total - 1), st1);
-  issue(min(2, total - 1), st2);
-  for (int it = 0; it < total; it += 4) {
-    step(it, st0, st3);
-    if (it + 1 < total) step(it + 1, st1, st0);
-    if (it + 2 < total) step(it + 2, st2, st1);
-    if (it + 3 < total) step(it + 3, st3, st2);
-  }
+  // Query tiles (descending) fall into three runs: tiles that cross the far
+  // edge of some key's window, tiles inside the band of every key of the
+  // block (qt in [2kb + 2, qt_hi]: no mask), and tiles that cross the
+  // diagonal. Each run is its own loop, so the masked and unmasked bodies
+  // never meet at a branch join (where the register allocator would copy the
+  // dK/dV accumulators between their two register assignments every step).
+  const int hi_num = Wl + kb * 128 - 64;  // last tile with t - u < Wl for all its pairs
+  const int qt_hi = min(nqt - 1, hi_num >= 0 ? hi_num / 64 : -1);
+  const int it_a = min(total, max(0, (nqt - 1 - qt_hi) * H));
+  const int it_b = min(total, max(it_a, (nqt - (2 * kb + 2)) * H));
+  issue(0, st[0]);
+  issue(min(1, total - 1), st[1]);
+  issue(min(2, total - 1), st[2]);
+  int it = 0;
+  for (; it < it_a; ++it) step(it, std::true_type{});
+  for (; it < it_b; ++it) step(it, std::false_type{});
+  for (; it < total; ++it) step(it, std::true_type{});
   wait_vmcnt<0>();
   if (key < T_) {
     bf16* outk = dqkv + ((int64_t)b * T_ + key) * ld + H * D;
