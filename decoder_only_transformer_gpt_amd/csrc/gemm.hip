@@ -30,6 +30,7 @@ namespace gk {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kGroupM = 4;  // row panels per tile group (NT kernel)
 
 template <typename T>
 struct TileK {
@@ -491,8 +492,13 @@ struct Epilogue<T, Epi::LMHead> {
         v[r] = c * tanh_fast(v[r] * inv_c);
         sum += __builtin_amdgcn_exp2f((v[r] - c) * 1.4426950408889634f);
       }
+      // the target's column among the lane's 4: chosen from scalars by
+      // compares (a select chain over v[] is folded into an indexed load
+      // that puts v in scratch memory)
       const unsigned d = (unsigned)(tgt - n);
-      if (d < 4u) a.ztgt[m] = d == 0 ? v[0] : d == 1 ? v[1] : d == 2 ? v[2] : v[3];
+      const float v0 = v[0], v1 = v[1], v2 = v[2], v3 = v[3];
+      const float zt = d == 0u ? v0 : (d == 1u ? v1 : (d == 2u ? v2 : v3));
+      if (d < 4u) a.ztgt[m] = zt;
       if (mv) store4(Z + (int64_t)m * a.ldc + n, v);
 #pragma unroll
       for (int o = 8; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 16);
@@ -574,12 +580,19 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm_nt_lds_kernel(GemmArgs args
   const int M = args.M, N = args.N, K = args.K;
   const int tiles_n = (N + BN - 1) / BN, tiles = ((M + BM - 1) / BM) * tiles_n;
   // blocks are dealt round-robin to the 8 XCDs: remap so that each XCD takes
-  // a contiguous run of items (neighbouring tiles, whole split-K slices)
+  // a contiguous run of items (neighbouring tiles, whole split-K slices).
+  // Within a slice, tiles go in groups of kGroupM row panels, down the group
+  // first: the blocks an XCD runs side by side cover a few row panels and a
+  // few column panels, so both operands' K windows are shared in its L2
+  // (row-major order would stream every column panel of B once per row panel).
   int item = blockIdx.x;
   const int nb = gridDim.x;
   if ((nb & 7) == 0) item = (item & 7) * (nb >> 3) + (item >> 3);
   const int split = item / tiles, bid = item % tiles;
-  const int m0 = (bid / tiles_n) * BM, n0 = (bid % tiles_n) * BN;
+  const int tiles_m = tiles / tiles_n;
+  const int grp = bid / (kGroupM * tiles_n), first_m = grp * kGroupM;
+  const int gm = min(tiles_m - first_m, kGroupM), r = bid - grp * kGroupM * tiles_n;
+  const int m0 = (first_m + r % gm) * BM, n0 = (r / gm) * BN;
   const int kper = ((K + args.splits - 1) / args.splits + BK - 1) / BK * BK;
   const int kbeg = split * kper;
   const int kend = min(K, kbeg + kper);
