@@ -102,7 +102,8 @@ def kernel_bytes_per_launch(tag: str, cfg, B: int, T: int, es: int) -> float | N
     b = {"fp8_amax": 2 * q_elems, "fp8_quantize": 4 * q_elems,
          "embed_rmsnorm": N * (4 + 2 * C * es + 4), "rmsnorm": N * (2 * C * es + 4),
          "rope_qknorm": N * (2 * (H + 1) * 128 * es + 4 * (H + 1)),
-         "ce_bwd": N * (2 * V * es + 8), "rmsnorm_bwd": N * (2 * C * es + 8 * C + C * es + 4),
+         "ce_bwd": N * (2 * C * es + 16 + es),  # lse, z'_t, target, r; the target entry; h in, r*h out
+         "rmsnorm_bwd": N * (2 * C * es + 8 * C + C * es + 4),
          "rope_qknorm_bwd": N * (3 * (H + 1) * 128 * es + 4 * (H + 1)),
          # transposed copies: read and write each (V; then Q, K, dO) once, plus delta's
          # read of O and dO and its fp32 write

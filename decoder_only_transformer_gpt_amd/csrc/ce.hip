@@ -11,8 +11,15 @@
 //   loss      = mean over all B*T rows (fixed-order reduction: deterministic)
 //   backward  dz_nv = (exp(z'_nv - lse_n) - [v == target]) * dloss / N * (1 - (z'_nv / c)^2)
 //
-// The backward overwrites the stored logits in place with dz, which is what
-// the two LM-head backward GEMMs read.
+// The epilogue stores q_nv = exp(z'_nv - c) (1 - (z'_nv / c)^2) instead of z'.
+// With s_n = exp(lse_n - c) (the row's sum of exp(z' - c)) and
+// r_n = dloss / (N s_n), dz_nv = r_n q_nv except at the target, where
+// dz = r_n (q - (1 - (z'/c)^2) s_n). The backward therefore never makes a
+// pass over the N x V matrix: one wave per row rewrites the target entry
+// (from the fp32 z' at the target, with the same exp2 the epilogue used),
+// stores r_n, and writes the row of the final-norm output scaled by r_n; the
+// LM-head dW GEMM reads that scaled copy, and the dX GEMM's rows are scaled
+// by r_n in the final norm's backward.
 
 #include "common.h"
 #include "kernels.h"
@@ -65,29 +72,35 @@ __global__ __launch_bounds__(1024) void mean_kernel(const float* __restrict__ x,
   }
 }
 
+// One wave per row: the target-column fix of q, the row scale r, and the
+// final-norm output row h scaled by r (bf16 or fp32 like h).
 template <typename T>
-__global__ __launch_bounds__(256) void ce_bwd_kernel(T* __restrict__ z, const float* __restrict__ lse,
-                                                     const int32_t* __restrict__ targets, int N, int V, float c,
-                                                     float scale) {
-  const int64_t nvec = (int64_t)N * V / 8;
-  const float inv_c = 1.f / c;
-  for (int64_t q = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; q < nvec; q += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t e0 = q * 8;
-    const int row = (int)(e0 / V);
-    const int col = (int)(e0 % V);
-    const float l = lse[row];
+__global__ __launch_bounds__(256) void ce_grad_prep_kernel(T* __restrict__ q, const float* __restrict__ lse,
+                                                           const float* __restrict__ ztgt,
+                                                           const int32_t* __restrict__ targets, int N, int V,
+                                                           float c, float scale, const T* __restrict__ h, int C,
+                                                           T* __restrict__ hs, float* __restrict__ rscale) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= N) return;
+  const float s = expf(lse[row] - c);
+  const float r = scale / s;
+  if (lane == 0) {
+    rscale[row] = r;
     const int t = targets[row];
-    float v[8];
-    load8(z + e0, v);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float zc = v[e];
-      float p = __expf(zc - l);
-      if (col + e == t) p -= 1.f;
-      const float u = zc * inv_c;
-      v[e] = p * scale * (1.f - u * u);
+    if ((unsigned)t < (unsigned)V) {
+      const float z = ztgt[row], u = z / c;
+      const float e = __builtin_amdgcn_exp2f((z - c) * 1.4426950408889634f);
+      q[(int64_t)row * V + t] = from_f32<T>((1.f - u * u) * (e - s));
     }
-    store8(z + e0, v);
+  }
+  const int64_t off = (int64_t)row * C;
+  for (int k = lane * 8; k < C; k += 64 * 8) {
+    float v[8];
+    load8(h + off + k, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] *= r;
+    store8(hs + off + k, v);
   }
 }
 
@@ -104,16 +117,17 @@ hipError_t launch_ce_loss(const float* part, int nparts, const float* ztgt, cons
   return hipGetLastError();
 }
 
-hipError_t launch_ce_bwd(int dtype, void* logits, const float* lse, const int32_t* targets, int N, int V,
-                         float softcap, float scale, hipStream_t s) {
-  const int64_t nvec = (int64_t)N * V / 8;
-  const int blocks = (int)std::min<int64_t>((nvec + 255) / 256, 256 * 64);
+hipError_t launch_ce_grad_prep(int dtype, void* q, const float* lse, const float* ztgt, const int32_t* targets, int N,
+                               int V, float softcap, float scale, const void* h, int C, void* hs, float* rscale,
+                               hipStream_t s) {
+  if (C % 8 != 0) return hipErrorInvalidValue;
+  const dim3 grid((N + 3) / 4);
   if (dtype == 1)
-    hipLaunchKernelGGL(ce_bwd_kernel<bf16>, dim3(blocks), dim3(256), 0, s, (bf16*)logits, lse, targets, N, V,
-                       softcap, scale);
+    hipLaunchKernelGGL(ce_grad_prep_kernel<bf16>, grid, dim3(256), 0, s, (bf16*)q, lse, ztgt, targets, N, V, softcap,
+                       scale, (const bf16*)h, C, (bf16*)hs, rscale);
   else
-    hipLaunchKernelGGL(ce_bwd_kernel<float>, dim3(blocks), dim3(256), 0, s, (float*)logits, lse, targets, N, V,
-                       softcap, scale);
+    hipLaunchKernelGGL(ce_grad_prep_kernel<float>, grid, dim3(256), 0, s, (float*)q, lse, ztgt, targets, N, V,
+                       softcap, scale, (const float*)h, C, (float*)hs, rscale);
   return hipGetLastError();
 }
 

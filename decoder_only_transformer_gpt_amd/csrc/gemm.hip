@@ -467,14 +467,17 @@ struct Epilogue<T, Epi::Relu2Bwd> {
   }
 };
 
-// LM head with the logit softcap c*tanh(z/c), evaluated on the fp32
+// LM head with the logit softcap z' = c*tanh(z/c), evaluated on the fp32
 // accumulator (aethryn.com, section "A Llama-class transformer with ten modern
-// departures": softcap 15, in float32). Emits the capped logits in the
-// activation dtype, one fp32 partial sum of exp(z' - c) per row and 64
-// columns (terms lie in (e^-2c, 1], so partial sums add without rescaling),
-// and the fp32 capped logit at the row's target. Done on the staged rows: 64
-// columns of a row sit in 16 lanes (4 each), reduced with shuffles. The
-// row's target id is prefetched with the slab.
+// departures": softcap 15, in float32). Emits one fp32 partial sum of
+// exp(z' - c) per row and 64 columns (terms lie in (e^-2c, 1], so partial
+// sums add without rescaling), the fp32 z' at the row's target, and, in the
+// activation dtype, q = exp(z' - c) (1 - (z'/c)^2) for every entry: the
+// softmax numerator times the slope of the softcap, from which the backward
+// needs only a per-row scale and a fix at the target column (the cross-entropy
+// gradient dz = (exp(z' - lse) - [v == target]) (1 - (z'/c)^2) dloss / N).
+// Done on the staged rows: 64 columns of a row sit in 16 lanes (4 each),
+// reduced with shuffles. The row's target id is prefetched with the slab.
 template <typename T>
 struct Epilogue<T, Epi::LMHead> {
   template <int TM, int TN, int WN>
@@ -486,20 +489,22 @@ struct Epilogue<T, Epi::LMHead> {
     auto pre = [&](int m, int) { return m < a.M ? a.targets[m] : -1; };
     staged_store_pre<TM, TN, WN>(acc, lds, mbase, nbase, lane, pre, [&](int m, int n, float (&v)[4], int tgt) {
       const bool mv = m < a.M;
-      float sum = 0.f;
+      float sum = 0.f, z[4], q[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        v[r] = c * tanh_fast(v[r] * inv_c);
-        sum += __builtin_amdgcn_exp2f((v[r] - c) * 1.4426950408889634f);
+        z[r] = c * tanh_fast(v[r] * inv_c);
+        const float e = __builtin_amdgcn_exp2f((z[r] - c) * 1.4426950408889634f);
+        const float u = z[r] * inv_c;
+        sum += e;
+        q[r] = e * (1.f - u * u);
       }
       // the target's column among the lane's 4: chosen from scalars by
-      // compares (a select chain over v[] is folded into an indexed load
-      // that puts v in scratch memory)
+      // compares (a select chain over an array is folded into an indexed
+      // load that puts the array in scratch memory)
       const unsigned d = (unsigned)(tgt - n);
-      const float v0 = v[0], v1 = v[1], v2 = v[2], v3 = v[3];
-      const float zt = d == 0u ? v0 : (d == 1u ? v1 : (d == 2u ? v2 : v3));
+      const float zt = d == 0u ? z[0] : (d == 1u ? z[1] : (d == 2u ? z[2] : z[3]));
       if (d < 4u) a.ztgt[m] = zt;
-      if (mv) store4(Z + (int64_t)m * a.ldc + n, v);
+      if (mv) store4(Z + (int64_t)m * a.ldc + n, q);
 #pragma unroll
       for (int o = 8; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 16);
       if (mv && (lane & 15) == 0) a.part[(int64_t)m * nparts + n / kLMHeadPartCols] = sum;

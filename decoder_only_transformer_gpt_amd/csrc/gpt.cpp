@@ -82,7 +82,7 @@ const char* kTagNames[K_NUM_TAGS] = {
 
 struct Layout {  // byte offsets inside the workspace
   size_t flag, loss_rows, rope_cos, rope_sin;
-  size_t x, rstd0, hf, rstdf, logits, part, ztgt, lse_ce;
+  size_t x, rstd0, hf, rstdf, logits, part, ztgt, lse_ce, ce_rscale;
   std::vector<size_t> h1, rstd1, qkv, rstd_qk, o, lse, h2, rstd2, a;
   size_t dres, dres_lp, dh, du, dqkv, dout, delta, split;
   size_t qT, kT, vT, doT;  // attention's transposed copies [B, heads, 128, Tp]
@@ -188,6 +188,7 @@ Layout plan(const gpt_config& c, int maxB, int maxT) {
   L.part = p.take(N * (V / gk::kLMHeadPartCols) * 4);
   L.ztgt = p.take(N * 4);
   L.lse_ce = p.take(N * 4);
+  L.ce_rscale = p.take(N * 4);
   L.dres = p.take(N * C * 4);
   L.dres_lp = p.take(N * C * es);
   L.dh = p.take(N * C * es);
@@ -884,12 +885,17 @@ gpt_status gpt_backward(gpt_model* m, float dloss, int32_t accumulate, void* str
                                                  wsp<int32_t>(m, L.keys_b), wsp<int32_t>(m, L.vals_b),
                                                  wsp<int32_t>(m, L.hist), stream););
   if (c.x0_lambdas) RUN(K_X0_MIX_BWD, return gk::launch_fill_f32(wsp<float>(m, L.dx0acc), 0.f, (int64_t)N * C, stream););
-  RUN(K_CE_BWD, return gk::launch_ce_bwd(dt, m->ws + L.logits, wsp<float>(m, L.lse_ce), m->targets, N, V,
-                                         c.logit_softcap, dloss / (float)N, stream););
-  TRY(dw(K_GEMM_LM_DW, m->ws + L.logits, V, m->ws + L.hf, C, V, C, m->off_lm));
+  // dz = r_n q (target entries fixed in place), never formed: dW_lm = q^T (r h)
+  // with the scaled copy of h in dh's buffer (read before dX overwrites it),
+  // dX_lm = q W_lm with rows scaled by r in the final norm's backward
+  RUN(K_CE_BWD, return gk::launch_ce_grad_prep(dt, m->ws + L.logits, wsp<float>(m, L.lse_ce), wsp<float>(m, L.ztgt),
+                                               m->targets, N, V, c.logit_softcap, dloss / (float)N, m->ws + L.hf, C,
+                                               m->ws + L.dh, wsp<float>(m, L.ce_rscale), stream););
+  TRY(dw(K_GEMM_LM_DW, m->ws + L.logits, V, m->ws + L.dh, C, V, C, m->off_lm));
   TRY(dx(K_GEMM_LM_DX, gk::Epi::Store, m->ws + L.logits, V, m->off_lm, C, V, m->ws + L.dh, nullptr));
   RUN(K_RMSNORM_BWD, return gk::launch_rmsnorm_bwd(dt, m->ws + L.dh, m->ws + L.hf, wsp<float>(m, L.rstdf), N, C, 0,
-                                                   wsp<float>(m, L.dres), m->ws + L.dres_lp, stream););
+                                                   wsp<float>(m, L.dres), m->ws + L.dres_lp, stream,
+                                                   wsp<float>(m, L.ce_rscale)););
   for (int l = c.n_layer - 1; l >= 0; --l) {
     // MLP
     if (fp8) {

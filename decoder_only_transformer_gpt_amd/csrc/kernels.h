@@ -55,9 +55,11 @@ hipError_t launch_embed_rmsnorm(int dtype, const void* wte, const int32_t* idx, 
                                 float eps, void* x, float* rstd, int* flag, hipStream_t s);
 hipError_t launch_rmsnorm(int dtype, const void* x, int N, int C, float eps, void* y, float* rstd,
                           hipStream_t s);
-// dres = (accumulate ? dres : 0) + r * (dy - y * mean(dy*y)); dres_lp = dres in the activation dtype
+// dres = (accumulate ? dres : 0) + r * (dy - y * mean(dy*y)); dres_lp = dres in the activation dtype;
+// dy_row_scale (optional, fp32 [N]): dy of row n is multiplied by dy_row_scale[n] first
 hipError_t launch_rmsnorm_bwd(int dtype, const void* dy, const void* y, const float* rstd, int N, int C,
-                              int accumulate, float* dres, void* dres_lp, hipStream_t s);
+                              int accumulate, float* dres, void* dres_lp, hipStream_t s,
+                              const float* dy_row_scale = nullptr);
 hipError_t launch_rope_qknorm(int dtype, void* qkv, int B, int T, int H, float eps, const float* cos_t,
                               const float* sin_t, float* rstd_qk, hipStream_t s);
 hipError_t launch_rope_qknorm_bwd(int dtype, void* dqkv, const void* qkv, const float* rstd_qk, int B,
@@ -92,8 +94,9 @@ hipError_t launch_attn_bwd(int dtype, const AttnBwdArgs& a, int stage, hipStream
 hipError_t launch_ce_loss(const float* part, int nparts, const float* ztgt, const int32_t* targets, int N,
                           int V, float softcap, float* lse, float* row_loss, float* row_loss_out,
                           float* loss, int* flag, hipStream_t s);
-hipError_t launch_ce_bwd(int dtype, void* logits, const float* lse, const int32_t* targets, int N, int V,
-                         float softcap, float scale, hipStream_t s);
+hipError_t launch_ce_grad_prep(int dtype, void* q, const float* lse, const float* ztgt, const int32_t* targets, int N,
+                               int V, float softcap, float scale, const void* h, int C, void* hs, float* rscale,
+                               hipStream_t s);
 
 // Embedding backward ---------------------------------------------------------
 struct EmbedBwdArgs {

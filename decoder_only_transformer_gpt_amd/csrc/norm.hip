@@ -77,12 +77,14 @@ template <typename T>
 __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const T* __restrict__ dy, const T* __restrict__ y,
                                                           const float* __restrict__ rstd, int N, int C,
                                                           int accumulate, float* __restrict__ dres,
-                                                          T* __restrict__ dres_lp) {
+                                                          T* __restrict__ dres_lp,
+                                                          const float* __restrict__ dy_row_scale) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= N) return;
   const int64_t off = (int64_t)row * C;
   const int nch = C >> 3;
+  const float gs = dy_row_scale ? dy_row_scale[row] : 1.f;
   float g[kMaxChunks][8], yy[kMaxChunks][8];
   float dot = 0.f;
 #pragma unroll
@@ -92,7 +94,10 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const T* __restrict__ 
       load8(dy + off + ch * 8, g[j]);
       load8(y + off + ch * 8, yy[j]);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) dot += g[j][e] * yy[j][e];
+      for (int e = 0; e < 8; ++e) {
+        g[j][e] *= gs;
+        dot += g[j][e] * yy[j][e];
+      }
     }
   }
   dot = wave_sum(dot) / (float)C;
@@ -223,14 +228,14 @@ hipError_t launch_rmsnorm(int dtype, const void* x, int N, int C, float eps, voi
 }
 
 hipError_t launch_rmsnorm_bwd(int dtype, const void* dy, const void* y, const float* rstd, int N, int C,
-                              int accumulate, float* dres, void* dres_lp, hipStream_t s) {
+                              int accumulate, float* dres, void* dres_lp, hipStream_t s, const float* dy_row_scale) {
   dim3 grid((N + 3) / 4);
   if (dtype == 1)
     hipLaunchKernelGGL(rmsnorm_bwd_kernel<bf16>, grid, dim3(256), 0, s, (const bf16*)dy, (const bf16*)y, rstd, N,
-                       C, accumulate, dres, (bf16*)dres_lp);
+                       C, accumulate, dres, (bf16*)dres_lp, dy_row_scale);
   else
     hipLaunchKernelGGL(rmsnorm_bwd_kernel<float>, grid, dim3(256), 0, s, (const float*)dy, (const float*)y, rstd,
-                       N, C, accumulate, dres, (float*)dres_lp);
+                       N, C, accumulate, dres, (float*)dres_lp, dy_row_scale);
   return hipGetLastError();
 }
 

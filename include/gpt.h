@@ -214,7 +214,10 @@ const char* gpt_kernel_tag_name(int32_t tag);
  * "hf", "logits", "rstd0"; FP8 models also "amax") for `layer` (ignored by
  * non-layer buffers). The pointer aliases the workspace and is valid until
  * the next call. "lse" holds the attention log-sum-exp per (batch row, head,
- * position) in base 2, i.e. ln(sum) * log2(e), fp32 [B, H, T]. "amax" holds
+ * position) in base 2, i.e. ln(sum) * log2(e), fp32 [B, H, T]. "logits" holds
+ * what the LM head stores for the backward, q = exp(z' - c) (1 - (z'/c)^2)
+ * per row and vocabulary entry (z' = c tanh(z/c), c the softcap), activation
+ * dtype [B*T, V]; a backward overwrites the target entries. "amax" holds
  * the layer's 16 fp32 |max| slots of the FP8 operands: h1, o, h2, a (forward
  * inputs of the QKV, O, W1, W2 products), the output gradients of W2 and W1
  * (d(out) of the MLP, du), of O and of QKV, then W_qkv, W_o, W_1, W_2, then 4
