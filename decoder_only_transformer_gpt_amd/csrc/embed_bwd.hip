@@ -167,8 +167,22 @@ __global__ __launch_bounds__(256) void seg_partial_kernel(const int32_t* __restr
   }
 }
 
+// Last sorted position holding id v, searching from position `from` (whose
+// key is v): a binary search over the ascending keys.
+DEV int segment_last(const int32_t* __restrict__ keys, int N, int from, int v) {
+  int lo = from, hi = N;  // keys[lo] == v; keys[hi] != v (or hi == N)
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (keys[mid] == v) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
+
 // One block per chunk in which a boundary-crossing segment starts: adds the
-// partials of that segment in chunk order and finalises its row.
+// partials of that segment in chunk order and finalises its row. The chunk
+// holding the segment's last entry is found first (binary search), so the
+// partial rows are summed over a known range with many loads in flight.
 __global__ __launch_bounds__(256) void seg_fixup_kernel(const int32_t* __restrict__ keys, int N, int C, int nchunks,
                                                         const void* wte_raw, int wte_bf16,
                                                         const float* __restrict__ carry, float* __restrict__ dwte) {
@@ -182,25 +196,24 @@ __global__ __launch_bounds__(256) void seg_fixup_kernel(const int32_t* __restric
   int s = last;
   while (s > e0 && keys[s - 1] == v) --s;
   if (s == e0 && e0 > 0 && keys[e0 - 1] == v) return;  // began earlier: owned by an earlier chunk
-  for (int col = threadIdx.x; col <= C; col += 256) {
+  const int cend = min(nchunks - 1, segment_last(keys, N, e1, v) / kSegChunk);
+  // column C of a partial row carries the k sum
+  __shared__ float ks_sh;
+  if (threadIdx.x == 0) {
+    float ks = carry[((int64_t)c * 2 + 1) * (C + 1) + C];
+#pragma unroll 8
+    for (int cc = c + 1; cc <= cend; ++cc) ks += carry[((int64_t)cc * 2 + 0) * (C + 1) + C];
+    ks_sh = ks;
+  }
+  __syncthreads();
+  const float ks = ks_sh;
+  for (int col = threadIdx.x; col < C; col += 256) {
     float acc = carry[((int64_t)c * 2 + 1) * (C + 1) + col];
-    for (int cc = c + 1; cc < nchunks; ++cc) {
-      acc += carry[((int64_t)cc * 2 + 0) * (C + 1) + col];
-      const int l2 = min(N, (cc + 1) * kSegChunk) - 1;
-      if (keys[l2] != v || l2 + 1 >= N || keys[l2 + 1] != v) break;  // segment ends in chunk cc
-    }
-    if (col < C) {
-      // acc holds sum r*dres for this column; the k sum sits in column C.
-      float ks = carry[((int64_t)c * 2 + 1) * (C + 1) + C];
-      for (int cc = c + 1; cc < nchunks; ++cc) {
-        ks += carry[((int64_t)cc * 2 + 0) * (C + 1) + C];
-        const int l2 = min(N, (cc + 1) * kSegChunk) - 1;
-        if (keys[l2] != v || l2 + 1 >= N || keys[l2 + 1] != v) break;
-      }
-      const float w = wte_bf16 ? (float)((const bf16*)wte_raw)[(int64_t)v * C + col]
-                               : ((const float*)wte_raw)[(int64_t)v * C + col];
-      dwte[(int64_t)v * C + col] += acc - w * ks;
-    }
+#pragma unroll 8
+    for (int cc = c + 1; cc <= cend; ++cc) acc += carry[((int64_t)cc * 2 + 0) * (C + 1) + col];
+    const float w = wte_bf16 ? (float)((const bf16*)wte_raw)[(int64_t)v * C + col]
+                             : ((const float*)wte_raw)[(int64_t)v * C + col];
+    dwte[(int64_t)v * C + col] += acc - w * ks;
   }
 }
 
@@ -246,12 +259,10 @@ __global__ __launch_bounds__(128) void ve_seg_fixup_kernel(const int32_t* __rest
   int s = last;
   while (s > e0 && keys[s - 1] == v) --s;
   if (s == e0 && e0 > 0 && keys[e0 - 1] == v) return;
+  const int cend = min(nchunks - 1, segment_last(keys, N, e1, v) / kSegChunk);
   float acc = carry[((int64_t)c * 2 + 1) * 129 + col];
-  for (int cc = c + 1; cc < nchunks; ++cc) {
-    acc += carry[((int64_t)cc * 2 + 0) * 129 + col];
-    const int l2 = min(N, (cc + 1) * kSegChunk) - 1;
-    if (keys[l2] != v || l2 + 1 >= N || keys[l2 + 1] != v) break;
-  }
+#pragma unroll 8
+  for (int cc = c + 1; cc <= cend; ++cc) acc += carry[((int64_t)cc * 2 + 0) * 129 + col];
   dve[(int64_t)v * 128 + col] += to_f32(*gate) * acc;
 }
 
