@@ -593,6 +593,9 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm_nt_lds_kernel(GemmArgs args
   int item = blockIdx.x;
   const int nb = gridDim.x;
   if ((nb & 7) == 0) item = (item & 7) * (nb >> 3) + (item >> 3);
+  // batched products: product-major, then split-K slices, then tiles
+  const int bz = item / (tiles * args.splits);
+  item -= bz * tiles * args.splits;
   const int split = item / tiles, bid = item % tiles;
   const int tiles_m = tiles / tiles_n;
   const int grp = bid / (kGroupM * tiles_n), first_m = grp * kGroupM;
@@ -602,8 +605,8 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm_nt_lds_kernel(GemmArgs args
   const int kbeg = split * kper;
   const int kend = min(K, kbeg + kper);
   const int nk = kend > kbeg ? (kend - kbeg) / BK : 0;
-  const char* Ap = reinterpret_cast<const char*>(args.A) + ((int64_t)m0 * args.lda + kbeg) * ES;
-  const char* Bp = reinterpret_cast<const char*>(args.B) + ((int64_t)n0 * args.ldb + kbeg) * ES;
+  const char* Ap = reinterpret_cast<const char*>(args.A) + bz * args.stride_a + ((int64_t)m0 * args.lda + kbeg) * ES;
+  const char* Bp = reinterpret_cast<const char*>(args.B) + bz * args.stride_b + ((int64_t)n0 * args.ldb + kbeg) * ES;
   const uint32_t lda_b = (uint32_t)(args.lda * ES), ldb_b = (uint32_t)(args.ldb * ES);
   // record counts (bytes from the tile's first row), clamped to 1 GiB; plain
   // integer ternaries (a templated 64-bit min() would go through f64 VALU
@@ -754,6 +757,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm_nt_lds_kernel(GemmArgs args
   }
   GemmArgs ea = args;
   ea.zslice = split;
+  ea.C = reinterpret_cast<char*>(args.C) + bz * args.stride_c;
   Epilogue<T, E>::template run<TM, TN, WN>(ea, acc, slab, m0 + wm * WM, n0 + wn * WN, lane);
 }
 
@@ -1003,8 +1007,8 @@ hipError_t launch_nt_lds(const GemmArgs& a, hipStream_t s) {
   const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   GemmArgs g = a;
   g.splits = splits;
-  hipLaunchKernelGGL((gemm_nt_lds_kernel<BM, BN, NSTAGE, OCC, E, NW, BK, ES>), dim3(tiles * splits), dim3(NW * 64), 0,
-                     s, g);
+  hipLaunchKernelGGL((gemm_nt_lds_kernel<BM, BN, NSTAGE, OCC, E, NW, BK, ES>), dim3(tiles * splits * a.batch),
+                     dim3(NW * 64), 0, s, g);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || splits <= 1) return err;
   const int64_t total4 = (int64_t)a.M * a.N / 4;
@@ -1033,7 +1037,7 @@ hipError_t launch_tn_lds(const GemmArgs& a, hipStream_t s) {
 
 template <Epi E>
 hipError_t launch_nt_lds_tile(const GemmArgs& a, hipStream_t s) {
-  const int64_t t256 = (int64_t)((a.M + 255) / 256) * ((a.N + 255) / 256);
+  const int64_t t256 = (int64_t)((a.M + 255) / 256) * ((a.N + 255) / 256) * a.batch;
   // tile: 1 = 256x256 (8 waves, two per SIMD; 64-wide K tiles when K allows),
   // 2 = 256x128 (4 waves, two CTAs per CU), 3 = 128x128. By shape: 256x256
   // when there are at least two tiles per CU, else 128x128.
@@ -1134,7 +1138,22 @@ hipError_t launch_typed(Epi epi, const GemmArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_gemm(int dtype, Epi epi, const GemmArgs& a, hipStream_t s) {
-  if (a.M <= 0 || a.N <= 0) return hipSuccess;
+  if (a.M <= 0 || a.N <= 0 || a.batch <= 0) return hipSuccess;
+  if (a.batch > 1) {
+    if ((epi != Epi::Store && epi != Epi::Residual) || a.splits != 1) return hipErrorInvalidValue;
+    // one launch on the bf16 direct-to-LDS kernel; any other path, product by product
+    if (!(dtype == 1 && a.a_kcontig && a.b_kcontig && a.K % 64 == 0 && a.N % 4 == 0)) {
+      for (int j = 0; j < a.batch; ++j) {
+        GemmArgs g = a;
+        g.batch = 1;
+        g.A = reinterpret_cast<const char*>(a.A) + j * a.stride_a;
+        g.B = reinterpret_cast<const char*>(a.B) + j * a.stride_b;
+        g.C = reinterpret_cast<char*>(a.C) + j * a.stride_c;
+        if (hipError_t e = launch_gemm(dtype, epi, g, s); e != hipSuccess) return e;
+      }
+      return hipSuccess;
+    }
+  }
   // Shapes the tile loaders assume: a k-contiguous operand has K a multiple of
   // the 128-byte K tile; an mn-contiguous operand has its rows in whole
   // 16-byte vectors; the epilogue writes groups of 4 columns.

@@ -100,7 +100,8 @@ struct Layout {  // byte offsets inside the workspace
   size_t x0, dx0acc, rpart;
   std::vector<size_t> xprev;
   // optimiser scratch: Newton-Schulz iterates and products, norm partials
-  size_t ns_x, ns_xt, ns_a, ns_aa, ns_b, ns_part;
+  size_t ns_x, ns_xt, ns_a, ns_aa, ns_b, ns_part, ns_inv;
+  int ns_batch;  // Muon matrices per batched launch
   size_t keys_a, vals_a, keys_b, vals_b, hist, coef, carry;
   size_t total;
   size_t split_elems;
@@ -255,12 +256,16 @@ Layout plan(const gpt_config& c, int maxB, int maxT) {
       const size_t sm = std::min(mm[0], mm[1]);
       small2 = std::max(small2, sm * sm);
     }
-    L.ns_x = p.take(big * es);
-    L.ns_xt = p.take(big * es);
-    L.ns_a = p.take(small2 * es);
-    L.ns_aa = p.take(small2 * es);
-    L.ns_b = p.take(small2 * es);
-    L.ns_part = p.take(gk::muon_partials_elems() * 4);
+    // one matrix per layer has each shape: batches of up to kMuonBatch layers
+    const size_t nb = (size_t)std::max(1, std::min(gk::kMuonBatch, c.n_layer));
+    L.ns_batch = (int)nb;
+    L.ns_x = p.take(nb * big * es);
+    L.ns_xt = p.take(nb * big * es);
+    L.ns_a = p.take(nb * small2 * es);
+    L.ns_aa = p.take(nb * small2 * es);
+    L.ns_b = p.take(nb * small2 * es);
+    L.ns_part = p.take(nb * gk::muon_partials_elems() * 4);
+    L.ns_inv = p.take(nb * 4);
   }
   L.keys_a = p.take(N * 4);
   L.vals_a = p.take(N * 4);
@@ -1125,39 +1130,59 @@ gpt_status gpt_optimizer_step(gpt_model* m, const gpt_optim_config* oc, float* m
   char* params = reinterpret_cast<char*>(const_cast<void*>(m->params));
   const double bc1 = 1.0 - std::pow((double)oc->beta1, (double)t);
   const double bc2 = 1.0 - std::pow((double)oc->beta2, (double)t);
-  int64_t soff = 0;
-  for (const auto& td : d) {
+  // state offsets in parameter order (Muon: momentum; AdamW: m then v)
+  std::vector<int64_t> soff(d.size());
+  int64_t so = 0;
+  for (size_t i = 0; i < d.size(); ++i) {
+    soff[i] = so;
+    so += (optim_group(d[i].name) == 0 ? 1 : 2) * d[i].rows * d[i].cols;
+  }
+  std::vector<char> done(d.size(), 0);
+  for (size_t i = 0; i < d.size(); ++i) {
+    const auto& td = d[i];
     const int grp = optim_group(td.name);
     const int64_t ne = td.rows * td.cols;
     if (grp == 0) {
-      RUN(K_OPT_MUON, {
-        gk::MuonArgs a;
-        a.w = master + td.offset;
-        a.g = m->grads + td.offset;
-        a.u = state + soff;
-        a.out = params + td.offset * (int64_t)esize(dt);
-        a.rows = (int)td.rows;
-        a.cols = (int)td.cols;
-        a.lr = oc->lr_muon;
-        a.mu = oc->momentum;
-        a.wd = oc->wd_muon;
-        a.steps = oc->ns_steps;
-        a.a = oc->ns_a; a.b = oc->ns_b; a.c = oc->ns_c;
-        a.X = m->ws + L.ns_x; a.XT = m->ws + L.ns_xt;
-        a.A = m->ws + L.ns_a; a.AA = m->ws + L.ns_aa; a.Bm = m->ws + L.ns_b;
-        a.partials = wsp<float>(m, L.ns_part);
-        a.inv = wsp<float>(m, L.ns_part) + gk::muon_partials_elems() - 16;
-        return gk::launch_muon(dt, a, stream);
-      });
-      soff += ne;
+      if (done[i]) continue;
+      // this matrix and the later ones of its shape, in batches
+      std::vector<size_t> same;
+      for (size_t k = i; k < d.size(); ++k)
+        if (!done[k] && optim_group(d[k].name) == 0 && d[k].rows == td.rows && d[k].cols == td.cols) same.push_back(k);
+      for (size_t b0 = 0; b0 < same.size(); b0 += (size_t)L.ns_batch) {
+        const int cnt = (int)std::min(same.size() - b0, (size_t)L.ns_batch);
+        RUN(K_OPT_MUON, {
+          gk::MuonArgs a;
+          a.count = cnt;
+          for (int j = 0; j < cnt; ++j) {
+            const auto& tj = d[same[b0 + j]];
+            a.w[j] = master + tj.offset;
+            a.g[j] = m->grads + tj.offset;
+            a.u[j] = state + soff[same[b0 + j]];
+            a.out[j] = params + tj.offset * (int64_t)esize(dt);
+          }
+          a.rows = (int)td.rows;
+          a.cols = (int)td.cols;
+          a.lr = oc->lr_muon;
+          a.mu = oc->momentum;
+          a.wd = oc->wd_muon;
+          a.steps = oc->ns_steps;
+          a.a = oc->ns_a; a.b = oc->ns_b; a.c = oc->ns_c;
+          a.X = m->ws + L.ns_x; a.XT = m->ws + L.ns_xt;
+          a.A = m->ws + L.ns_a; a.AA = m->ws + L.ns_aa; a.Bm = m->ws + L.ns_b;
+          a.partials = wsp<float>(m, L.ns_part);
+          a.inv = wsp<float>(m, L.ns_inv);
+          return gk::launch_muon(dt, a, stream);
+        });
+      }
+      for (size_t k : same) done[k] = 1;
     } else {
       const float lr = grp == 1 ? oc->lr_embed : grp == 2 ? oc->lr_unembed : oc->lr_scalar;
       RUN(K_OPT_ADAMW, {
         gk::AdamwArgs a;
         a.w = master + td.offset;
         a.g = m->grads + td.offset;
-        a.m = state + soff;
-        a.v = state + soff + ne;
+        a.m = state + soff[i];
+        a.v = state + soff[i] + ne;
         a.out = params + td.offset * (int64_t)esize(dt);
         a.n = ne;
         a.lr = lr;
@@ -1166,7 +1191,6 @@ gpt_status gpt_optimizer_step(gpt_model* m, const gpt_optim_config* oc, float* m
         a.inv_sqrt_bc2 = (float)(1.0 / std::sqrt(bc2));
         return gk::launch_adamw(dt, a, stream);
       });
-      soff += 2 * ne;
     }
   }
   return GPT_OK;

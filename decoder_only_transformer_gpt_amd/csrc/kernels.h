@@ -42,6 +42,10 @@ struct GemmArgs {
   // fp8 operands (dtype 2): |max| slots of A and B; acc is scaled by 1/(s_a s_b)
   const float* amax_a = nullptr;
   const float* amax_b = nullptr;
+  // batched products (Store / Residual epilogues, no split-K): product j reads
+  // A + j*stride_a, B + j*stride_b and writes C + j*stride_c (bytes)
+  int batch = 1;
+  int64_t stride_a = 0, stride_b = 0, stride_c = 0;
 };
 
 // dtype: 0 = fp32, 1 = bf16 (gpt.h GPT_F32 / GPT_BF16), 2 = fp8 e4m3
@@ -196,17 +200,22 @@ struct AdamwArgs {
   float inv_sqrt_bc2;  // 1 / sqrt(1 - beta2^t)
 };
 hipError_t launch_adamw(int dtype, const AdamwArgs& a, hipStream_t s);
+// Muon on up to kMuonBatch matrices of one shape at once: every step of the
+// iteration is one launch for the whole batch.
+constexpr int kMuonBatch = 32;
 struct MuonArgs {
-  float* w;            // fp32 master [rows, cols]
-  const float* g;      // fp32 gradient
-  float* u;            // momentum
-  void* out;           // the model's copy (model dtype)
+  int count;                      // matrices in the batch, 1..kMuonBatch
+  float* w[kMuonBatch];           // fp32 masters [rows, cols]
+  const float* g[kMuonBatch];     // fp32 gradients
+  float* u[kMuonBatch];           // momenta
+  void* out[kMuonBatch];          // the model's copies (model dtype)
   int rows, cols;
   float lr, mu, wd;
   int steps;           // Newton-Schulz steps
   float a, b, c;       // X <- a X + (b A + c A^2) X
-  // scratch (model dtype unless noted): X and X^T [min*max], A, AA, Bm [min^2],
-  // partials (fp32, muon_partials_elems()), inv (fp32 scalar)
+  // scratch (model dtype unless noted), count copies each, contiguous: X and
+  // X^T [min*max], A, AA, Bm [min^2]; partials (fp32, count *
+  // muon_partials_elems()), inv (fp32, count)
   void *X, *XT, *A, *AA, *Bm;
   float* partials;
   float* inv;
