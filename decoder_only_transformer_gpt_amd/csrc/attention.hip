@@ -1013,15 +1013,21 @@ DEV void dkv_tile(const DkvStage& s, int wave, const RowFrag& rf, const TrFrag& 
   }
 }
 
+// With hsplit = 2 (grids too small for two rounds of blocks per CU) each key
+// block is split over two blocks by head halves, which write fp32 partial
+// dK/dV rows to `part`; attn_dkv_combine_kernel adds the halves in order.
 __global__ __launch_bounds__(256, 1) void attn_dkv_bf16_kernel(const bf16* __restrict__ qkv,
                                                                const bf16* __restrict__ dout,
                                                                const float* __restrict__ lse,
                                                                const float* __restrict__ delta, int T_, int H,
-                                                               int W, bf16* __restrict__ dqkv) {
+                                                               int W, int hsplit, bf16* __restrict__ dqkv,
+                                                               float* __restrict__ part) {
   __shared__ __attribute__((aligned(1024))) DkvStage st[4];
   const int nkb = (T_ + 127) / 128;
-  int b, kb;
-  xcd_level_map(blockIdx.x, gridDim.x / nkb, b, kb);  // key block 0 (most query tiles) first
+  int bh, kb;
+  xcd_level_map(blockIdx.x, gridDim.x / nkb, bh, kb);  // key block 0 (most query tiles) first
+  const int b = bh / hsplit, hs = bh % hsplit;
+  const int Hs = H / hsplit, h0 = hs * Hs;  // this block's heads
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t ld = (int64_t)(H + 2) * D;
@@ -1045,7 +1051,7 @@ __global__ __launch_bounds__(256, 1) void attn_dkv_bf16_kernel(const bf16* __res
   // any of its keys is visible from
   const int nqt = W > 0 ? min((T_ + 63) / 64, (kb * 128 + 127 + W - 1) / 64 + 1) : (T_ + 63) / 64;
   const int nq = nqt - 2 * kb;
-  const int total = H * nq;
+  const int total = Hs * nq;
   const int Wl = window_len(W);
 
   uint32_t voq[4], vod[4];
@@ -1054,7 +1060,7 @@ __global__ __launch_bounds__(256, 1) void attn_dkv_bf16_kernel(const bf16* __res
   const RowFrag rf(lane);
   const TrFrag tf(lane);
   auto issue = [&](int it, DkvStage& s) {
-    const int h = it % H, q0 = (nqt - 1 - it / H) * 64, rows = min(64, T_ - q0);
+    const int h = h0 + it % Hs, q0 = (nqt - 1 - it / Hs) * 64, rows = min(64, T_ - q0);
     tile_issue(uniform_rsrc(base + (int64_t)q0 * ld + h * D, rows * (int)ld_b), s.q, voq, wave);
     tile_issue(uniform_rsrc(dout + ((int64_t)b * T_ + q0) * H * D + h * D, rows * (int)ldo_b), s.d, vod, wave);
     const int64_t lo = ((int64_t)b * H + h) * T_ + q0;
@@ -1068,7 +1074,7 @@ __global__ __launch_bounds__(256, 1) void attn_dkv_bf16_kernel(const bf16* __res
     wait_vmcnt<2 * 10>();  // this wave's part of step it's tiles has landed
     __builtin_amdgcn_s_barrier();
     issue(min(it + 3, total - 1), st[(it + 3) & 3]);
-    const int q0 = (nqt - 1 - it / H) * 64;
+    const int q0 = (nqt - 1 - it / Hs) * 64;
     if (q0 + 63 < kw || q0 - (kw + 31) >= Wl) return;  // the tile misses every key's band
     dkv_tile<decltype(masked)::value>(st[it & 3], wave, rf, tf, kf, vf, adk, adv, sl2, q0 + 4 * g - key, Wl, g);
   };
@@ -1080,8 +1086,8 @@ __global__ __launch_bounds__(256, 1) void attn_dkv_bf16_kernel(const bf16* __res
   // dK/dV accumulators between their two register assignments every step).
   const int hi_num = Wl + kb * 128 - 64;  // last tile with t - u < Wl for all its pairs
   const int qt_hi = min(nqt - 1, hi_num >= 0 ? hi_num / 64 : -1);
-  const int it_a = min(total, max(0, (nqt - 1 - qt_hi) * H));
-  const int it_b = min(total, max(it_a, (nqt - (2 * kb + 2)) * H));
+  const int it_a = min(total, max(0, (nqt - 1 - qt_hi) * Hs));
+  const int it_b = min(total, max(it_a, (nqt - (2 * kb + 2)) * Hs));
   issue(0, st[0]);
   issue(min(1, total - 1), st[1]);
   issue(min(2, total - 1), st[2]);
@@ -1092,6 +1098,8 @@ __global__ __launch_bounds__(256, 1) void attn_dkv_bf16_kernel(const bf16* __res
   wait_vmcnt<0>();
   if (key < T_) {
     bf16* outk = dqkv + ((int64_t)b * T_ + key) * ld + H * D;
+    const int64_t N = (int64_t)(gridDim.x / (nkb * hsplit)) * T_;  // B * T
+    float* outp = hsplit == 1 ? nullptr : part + (hs * N + (int64_t)b * T_ + key) * (2 * D);
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -1100,10 +1108,30 @@ __global__ __launch_bounds__(256, 1) void attn_dkv_bf16_kernel(const bf16* __res
         float vk[4] = {adk[db][blk * 4] * scale, adk[db][blk * 4 + 1] * scale, adk[db][blk * 4 + 2] * scale,
                        adk[db][blk * 4 + 3] * scale};
         float vv[4] = {adv[db][blk * 4], adv[db][blk * 4 + 1], adv[db][blk * 4 + 2], adv[db][blk * 4 + 3]};
-        store4(outk + d, vk);
-        store4(outk + D + d, vv);
+        if (hsplit == 1) {
+          store4(outk + d, vk);
+          store4(outk + D + d, vv);
+        } else {
+          store4(outp + d, vk);
+          store4(outp + D + d, vv);
+        }
       }
   }
+}
+
+// dK, dV rows = the two head halves' fp32 partials added in order (bf16 out)
+__global__ __launch_bounds__(256) void attn_dkv_combine_kernel(const float* __restrict__ part, int64_t N, int H,
+                                                               bf16* __restrict__ dqkv) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // group of 8 values
+  if (i >= N * (2 * D / 8)) return;
+  const int64_t row = i / (2 * D / 8);
+  const int c = (int)(i % (2 * D / 8)) * 8;
+  float a[8], b[8];
+  load8(part + row * 2 * D + c, a);
+  load8(part + (N + row) * 2 * D + c, b);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) a[e] += b[e];
+  store8(dqkv + row * (int64_t)(H + 2) * D + H * D + c, a);
 }
 
 template <typename T>
@@ -1155,12 +1183,20 @@ hipError_t bwd_typed(const AttnBwdArgs& a, int stage, hipStream_t s) {
       hipLaunchKernelGGL(attn_dq_kernel<T>, grid, dim3(256), 0, s, (const T*)a.qkv, (const T*)a.kT,
                          (const T*)a.dout, a.lse, a.delta, T_, Tp, H, W, (T*)a.dqkv);
   } else {
-    const dim3 grid(((T_ + 127) / 128) * B);
-    if constexpr (kBf16)
-      hipLaunchKernelGGL(attn_dkv_bf16_kernel, grid, dim3(256), 0, s, (const bf16*)a.qkv, (const bf16*)a.dout,
-                         a.lse, a.delta, T_, H, W, (bf16*)a.dqkv);
-    else
-      hipLaunchKernelGGL(attn_dkv_kernel<T>, grid, dim3(256), 0, s, (const T*)a.qkv, (const T*)a.qT,
+    if constexpr (kBf16) {
+      // one block per CU: below two rounds of blocks, split each key block
+      // over two head halves (dK/dV partials added by the combine kernel)
+      const int nkb = (T_ + 127) / 128;
+      const int hsplit = (a.dkv_part && H % 2 == 0 && (int64_t)nkb * B < 512) ? 2 : 1;
+      hipLaunchKernelGGL(attn_dkv_bf16_kernel, dim3(nkb * B * hsplit), dim3(256), 0, s, (const bf16*)a.qkv,
+                         (const bf16*)a.dout, a.lse, a.delta, T_, H, W, hsplit, (bf16*)a.dqkv, a.dkv_part);
+      if (hsplit == 1) return hipGetLastError();
+      if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+      const int64_t N = (int64_t)B * T_, groups = N * (2 * D / 8);
+      hipLaunchKernelGGL(attn_dkv_combine_kernel, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, s,
+                         a.dkv_part, N, H, (bf16*)a.dqkv);
+    } else
+      hipLaunchKernelGGL(attn_dkv_kernel<T>, dim3(((T_ + 127) / 128) * B), dim3(256), 0, s, (const T*)a.qkv, (const T*)a.qT,
                          (const T*)a.dout, (const T*)a.doT, a.lse, a.delta, T_, Tp, H, W, (T*)a.dqkv);
   }
   return hipGetLastError();

@@ -84,7 +84,7 @@ struct Layout {  // byte offsets inside the workspace
   size_t flag, loss_rows, rope_cos, rope_sin;
   size_t x, rstd0, hf, rstdf, logits, part, ztgt, lse_ce, ce_rscale;
   std::vector<size_t> h1, rstd1, qkv, rstd_qk, o, lse, h2, rstd2, a;
-  size_t dres, dres_lp, dh, du, dqkv, dout, delta, split;
+  size_t dres, dres_lp, dh, du, dqkv, dout, delta, dkv_part, split;
   size_t qT, kT, vT, doT;  // attention's transposed copies [B, heads, 128, Tp]
   size_t wT, tdesc;        // transposed weights (bf16 models) and their descriptor table
   // FP8 models: amax slots; e4m3 codes of the layer weights (row-major and
@@ -197,6 +197,7 @@ Layout plan(const gpt_config& c, int maxB, int maxT) {
   L.dqkv = p.take(N * QKV * es);
   L.dout = p.take(N * H * kHeadDim * es);
   L.delta = p.take(N * H * 4);
+  L.dkv_part = p.take(2 * N * 2 * kHeadDim * 4);
   {
     const size_t Tp = (size_t)gk::attn_padded_len(maxT), BT = (size_t)maxB * Tp * kHeadDim;
     L.qT = p.take(BT * H * es);
@@ -940,6 +941,7 @@ gpt_status gpt_backward(gpt_model* m, float dloss, int32_t accumulate, void* str
     ab.kT = m->ws + L.kT;
     ab.doT = m->ws + L.doT;
     ab.dqkv = m->ws + L.dqkv;
+    ab.dkv_part = wsp<float>(m, L.dkv_part);
     RUN(K_ATTN_BWD_PREP, return gk::launch_attn_bwd(dt, ab, 0, stream););
     RUN(K_ATTN_BWD_DQ, return gk::launch_attn_bwd(dt, ab, 1, stream););
     RUN(K_ATTN_BWD_DKV, return gk::launch_attn_bwd(dt, ab, 2, stream););

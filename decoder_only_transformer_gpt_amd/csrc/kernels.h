@@ -90,6 +90,7 @@ struct AttnBwdArgs {
   void* kT;          // [B, 1, 128, Tp] scratch
   void* doT;         // [B, H, 128, Tp] scratch
   void* dqkv;        // [N, (H+2)*128] output
+  float* dkv_part;   // [2, N, 256] fp32 scratch (bf16 dK/dV split over two head halves), or null
 };
 // Stage 0: transposed copies + delta; stage 1: dQ; stage 2: dK and dV.
 hipError_t launch_attn_bwd(int dtype, const AttnBwdArgs& a, int stage, hipStream_t s);
