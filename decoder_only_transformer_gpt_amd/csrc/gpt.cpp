@@ -1068,6 +1068,8 @@ gpt_status gpt_debug_buffer(gpt_model* m, const char* name, int32_t layer, void*
   if (s == "hf") return set(L.hf, N * C * es);
   if (s == "rstd0") return set(L.rstd0, N * 4);
   if (s == "logits") return set(L.logits, N * (size_t)c.vocab_size * es);
+  if (s == "du") return set(L.du, N * (size_t)c.mlp_dim * es);
+  if (s == "dqkv") return set(L.dqkv, N * (H + 2) * kHeadDim * es);
   if (!lv) return fail(GPT_E_INVALID_ARG, "unknown buffer '%s' or layer %d out of range", name, layer);
   if (s == "h1") return set(L.h1[layer], N * C * es);
   if (s == "qkv") return set(L.qkv[layer], N * (H + 2) * kHeadDim * es);

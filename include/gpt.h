@@ -217,7 +217,10 @@ const char* gpt_kernel_tag_name(int32_t tag);
  * position) in base 2, i.e. ln(sum) * log2(e), fp32 [B, H, T]. "logits" holds
  * what the LM head stores for the backward, q = exp(z' - c) (1 - (z'/c)^2)
  * per row and vocabulary entry (z' = c tanh(z/c), c the softcap), activation
- * dtype [B*T, V]; a backward overwrites the target entries. "amax" holds
+ * dtype [B*T, V]; a backward overwrites the target entries. "du" and "dqkv"
+ * (no layer) hold the last backward's gradients at the MLP's hidden
+ * activation [B*T, mlp_dim] and at the QKV projection's output
+ * [B*T, (H+2)*128] of layer 0 (scratch reused layer by layer). "amax" holds
  * the layer's 16 fp32 |max| slots of the FP8 operands: h1, o, h2, a (forward
  * inputs of the QKV, O, W1, W2 products), the output gradients of W2 and W1
  * (d(out) of the MLP, du), of O and of QKV, then W_qkv, W_o, W_1, W_2, then 4

@@ -200,24 +200,35 @@ def test_fp8_ragged_zipf_accumulate(tile):
     check_fp8(case, gpu, l8, G8, G0, "d4-fp8-ragged", cos_bar=FP8_COS_D4)
 
 
-def test_fp8_amax_slots_and_differs_from_bf16():
-    """The stashed |max| slots hold exactly the maxima of the bf16 operands
-    (activations from the debug buffers, weights from the seeded values), and
-    FP8 changes the result relative to the bf16 model on the same inputs."""
+@pytest.mark.parametrize("B,T", [(2, 256), (128, 512)])
+def test_fp8_amax_slots_and_differs_from_bf16(B, T):
+    """The |max| slots hold exactly the maxima of the bf16 operands: the
+    activations against the debug buffers, the layer-0 gradients du and dqkv
+    after the backward, and the weights against the seeded values. B = 128
+    gives the dK/dV kernel one key block per block, B = 2 the head-split form
+    (dV through the combine pass). At B = 2, FP8 also changes the result
+    relative to the bf16 model on the same inputs."""
     torch = U.require_gpu()
-    case = U.Case(fp8_cfg(), B=2, T=256, law="uniform", wseed=4, tseed=5)
-    gpu = U.run_gpu(case)
+    case = U.Case(fp8_cfg(), B=B, T=T, law="uniform", wseed=4, tseed=5)
+    gpu = U.run_gpu(case, max_B=B, max_T=T)
     m = gpu["model"]
-    C, F, N = case.cfg.model_dim, case.cfg.mlp_dim, 2 * 256
+    C, F, N = case.cfg.model_dim, case.cfg.mlp_dim, B * T
+    HD, QKV = case.cfg.n_head * 128, (case.cfg.n_head + 2) * 128
     P = case.oracle_params()
     for l in range(case.cfg.n_layer):
         am = m.debug_tensor("amax", l, (16,), torch.float32).cpu().numpy()
-        h1 = m.debug_tensor("h1", l, (N, C), torch.bfloat16).float().cpu().numpy()
-        a = m.debug_tensor("a", l, (N, F), torch.bfloat16).float().cpu().numpy()
-        assert am[0] == np.abs(h1).max() and am[3] == np.abs(a).max()
+        for k, (nm, cols) in enumerate([("h1", C), ("o", HD), ("h2", C), ("a", F)]):
+            x = m.debug_tensor(nm, l, (N, cols), torch.bfloat16).float().cpu().numpy()
+            assert am[k] == np.abs(x).max(), (l, nm)
+        if l == 0:  # the gradients of the last layer the backward processed
+            du = m.debug_tensor("du", 0, (N, F), torch.bfloat16).float().cpu().numpy()
+            dqkv = m.debug_tensor("dqkv", 0, (N, QKV), torch.bfloat16).float().cpu().numpy()
+            assert am[5] == np.abs(du).max() and am[7] == np.abs(dqkv).max()
         for k, w in enumerate(["w_qkv", "w_o", "w_1", "w_2"]):
             assert am[8 + k] == np.abs(P[f"h{l}.{w}"]).max()
         assert np.all(am[:12] > 0) and np.all(np.isfinite(am))
+    if B != 2:
+        return
     bf = U.Case(_lib.gpt_config_from_depth(4, _lib.GPT_BF16), B=2, T=256, law="uniform", wseed=4, tseed=5)
     g_bf = U.run_gpu(bf)
     assert gpu["loss"] != g_bf["loss"] and abs(gpu["loss"] - g_bf["loss"]) / g_bf["loss"] < 1e-2
