@@ -732,7 +732,7 @@ DEV void fwd_tile(const KvStage& s, const RowFrag& rf, const TrFrag& tf, const u
 template <int NST>
 __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void attn_fwd_bf16_kernel(const bf16* __restrict__ qkv, int T_,
                                                                               int H, int W, bf16* __restrict__ o,
-                                                                              float* __restrict__ lse) {
+                                                                              float* __restrict__ lse, float* amax) {
   static_assert(NST == 2 || NST == 4, "two or four stages");
   __shared__ __attribute__((aligned(1024))) KvStage st[NST];
   const int nqb = (T_ + 127) / 128;
@@ -793,6 +793,7 @@ __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void attn_fwd_bf16_kernel(co
   for (; t < nt; ++t) step(t, std::true_type{});
   wait_vmcnt<0>();
   rsum += __shfl_xor(rsum, 32, 64);
+  float mx = 0.f;
   if (q < T_) {
     const float inv = 1.f / rsum;
     bf16* op = o + ((int64_t)b * T_ + q) * H * D + h * D;
@@ -802,10 +803,13 @@ __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void attn_fwd_bf16_kernel(co
       for (int blk = 0; blk < 4; ++blk) {
         float v[4] = {acc[db][blk * 4] * inv, acc[db][blk * 4 + 1] * inv, acc[db][blk * 4 + 2] * inv,
                       acc[db][blk * 4 + 3] * inv};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, fabsf(v[e]));
         store4(op + db * 32 + blk * 8 + g * 4, v);
       }
     if (g == 0) lse[((int64_t)b * H + h) * T_ + q] = sh2 + log2f(rsum);
   }
+  if (amax) amax_fold_block<bf16>(mx, amax);  // every wave gets here
 }
 
 // --------------------------------------------------------------- dQ (bf16) --
@@ -1143,13 +1147,13 @@ hipError_t transpose(const void* src, int64_t ld, int col0, int nh, int B, int T
 
 template <typename T>
 hipError_t fwd_typed(const void* qkv, int B, int T_, int H, int W, void* o, float* lse, void* vT, int stage,
-                     hipStream_t s) {
+                     hipStream_t s, float* amax) {
   const int Tp = attn_padded_len(T_);
   dim3 grid(((T_ + 127) / 128) * H * B);
   if constexpr (sizeof(T) == 2) {
     if (stage == 0) return hipSuccess;  // no transposed copy on this path
     hipLaunchKernelGGL(attn_fwd_bf16_kernel<kFwdStages>, grid, dim3(256), 0, s, (const bf16*)qkv, T_, H, W, (bf16*)o,
-                       lse);
+                       lse, amax);
     return hipGetLastError();
   }
   if (stage == 0) return transpose<T>(qkv, (int64_t)(H + 2) * D, (H + 1) * D, 1, B, T_, Tp, vT, s);
@@ -1207,10 +1211,10 @@ hipError_t bwd_typed(const AttnBwdArgs& a, int stage, hipStream_t s) {
 int attn_padded_len(int T) { return (T + 63) / 64 * 64; }
 
 hipError_t launch_attn_fwd(int dtype, const void* qkv, int B, int T, int H, int window, void* o, float* lse, void* vT,
-                           int stage, hipStream_t s) {
+                           int stage, hipStream_t s, float* amax) {
   const int W = window > 0 && window < T ? window : 0;
-  return dtype == 1 ? fwd_typed<bf16>(qkv, B, T, H, W, o, lse, vT, stage, s)
-                    : fwd_typed<float>(qkv, B, T, H, W, o, lse, vT, stage, s);
+  return dtype == 1 ? fwd_typed<bf16>(qkv, B, T, H, W, o, lse, vT, stage, s, amax)
+                    : fwd_typed<float>(qkv, B, T, H, W, o, lse, vT, stage, s, nullptr);
 }
 
 hipError_t launch_attn_bwd(int dtype, const AttnBwdArgs& a, int stage, hipStream_t s) {

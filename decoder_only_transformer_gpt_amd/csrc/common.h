@@ -103,6 +103,27 @@ DEV float wave_max(float v) {
   return v;
 }
 
+// Folds the threads' running |max| of values a kernel stores as T into a
+// float slot: the block's maximum, rounded to T (rounding is monotonic, so
+// this is the maximum of the stored values), by one atomic max of the bit
+// pattern per block (non-negative floats order like their bits; the slot
+// starts at 0). Every thread of the block must call it (it has a barrier);
+// at most 16 waves per block. Meant for kernels with few, long-running
+// blocks: the atomics of many short blocks on one address serialise.
+template <typename T>
+DEV void amax_fold_block(float m, float* slot) {
+  __shared__ float red[16];
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float v = red[0];
+    for (int w = 1; w < (int)(blockDim.x >> 6); ++w) v = fmaxf(v, red[w]);
+    if constexpr (sizeof(T) == 2) v = (float)(bf16)v;
+    atomicMax(reinterpret_cast<unsigned*>(slot), __float_as_uint(v));
+  }
+}
+
 // ------------------------------------------------------------- MFMA -------
 // Lane layout (checked on gfx950): for the 32x32 shapes, lane l feeds row
 // (l % 32) of the A operand and column (l % 32) of the B operand with the

@@ -424,13 +424,19 @@ struct Epilogue<T, Epi::Relu2> {
   template <int TM, int TN, int WN>
   static DEV void run(const GemmArgs& a, f32x16 (&acc)[TM][TN], float* lds, int mbase, int nbase, int lane) {
     T* A2 = reinterpret_cast<T*>(a.C);
+    float mx = 0.f;
     staged_store<TM, TN, WN>(acc, lds, mbase, nbase, lane, [&](int m, int n, float (&v)[4]) {
       if (m < a.M && n < a.N) {
         float s[4];
-        for (int r = 0; r < 4; ++r) { const float p = fmaxf(v[r], 0.f); s[r] = p * p; }
+        for (int r = 0; r < 4; ++r) {
+          const float p = fmaxf(v[r], 0.f);
+          s[r] = p * p;
+          mx = fmaxf(mx, s[r]);
+        }
         store4(A2 + (int64_t)m * a.ldc + n, s);
       }
     });
+    if (a.amax_out) amax_fold_block<T>(mx, a.amax_out);  // the whole block runs the epilogue
   }
 };
 
@@ -442,6 +448,7 @@ struct Epilogue<T, Epi::Relu2Bwd> {
   static DEV void run(const GemmArgs& a, f32x16 (&acc)[TM][TN], float* lds, int mbase, int nbase, int lane) {
     T* Dp = reinterpret_cast<T*>(a.C);
     const T* A2 = reinterpret_cast<const T*>(a.C2);
+    float mx = 0.f;
     // a is prefetched raw (4 bf16 in two dwords) for the whole tile
     auto pre = [&](int m, int n) {
       u32x2 r = {0u, 0u};
@@ -460,10 +467,14 @@ struct Epilogue<T, Epi::Relu2Bwd> {
         } else {
           load4(A2 + (int64_t)m * a.ldc2 + n, x);
         }
-        for (int q = 0; q < 4; ++q) v[q] *= 2.f * sqrtf(x[q]);
+        for (int q = 0; q < 4; ++q) {
+          v[q] *= 2.f * sqrtf(x[q]);
+          mx = fmaxf(mx, fabsf(v[q]));
+        }
         store4(Dp + (int64_t)m * a.ldc + n, v);
       }
     });
+    if (a.amax_out) amax_fold_block<T>(mx, a.amax_out);
   }
 };
 

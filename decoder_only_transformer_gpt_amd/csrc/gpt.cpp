@@ -366,8 +366,9 @@ gpt_status run(gpt_model* m, int tag, hipStream_t s, Fn&& fn) {
 
 // FP8: amax pass then quantise pass of one bf16 operand [rows, cols]
 // (contiguous) into row-major codes q and/or token-major codes qT [cols, ldT].
+// amax_ready: the producer of src folded its |max| into amax as it wrote it
 gpt_status quantize_operand(gpt_model* m, hipStream_t stream, const void* src, int rows, int cols, uint8_t* q,
-                            uint8_t* qT, int64_t ldT, float* amax) {
+                            uint8_t* qT, int64_t ldT, float* amax, bool amax_ready = false) {
   gk::QuantDesc d;
   d.src = src;
   d.ld = cols;
@@ -377,7 +378,7 @@ gpt_status quantize_operand(gpt_model* m, hipStream_t stream, const void* src, i
   d.qT = qT;
   d.ldT = (int32_t)ldT;
   d.amax = amax;
-  RUN(K_FP8_AMAX, return gk::launch_fp8_amax(d, stream););
+  if (!amax_ready) RUN(K_FP8_AMAX, return gk::launch_fp8_amax(d, stream););
   RUN(K_FP8_QUANT, return gk::launch_fp8_quantize(d, stream););
   return GPT_OK;
 }
@@ -727,9 +728,14 @@ gpt_status gpt_forward_loss(gpt_model* m, const int32_t* idx, const int32_t* tar
     const int win = layer_window(c, l);
     RUN(K_ATTN_FWD_PREP, return gk::launch_attn_fwd(dt, m->ws + L.qkv[l], B, T, H, win, m->ws + L.o[l],
                                                     wsp<float>(m, L.lse[l]), m->ws + L.vT, 0, stream););
+    // FP8: the attention forward and the W1 / W2-dX epilogues (few long
+    // blocks) fold the |max| of what they store, so those operands skip the
+    // separate |max| pass; the row kernels' operands keep it
     RUN(K_ATTN_FWD, return gk::launch_attn_fwd(dt, m->ws + L.qkv[l], B, T, H, win, m->ws + L.o[l],
-                                               wsp<float>(m, L.lse[l]), m->ws + L.vT, 1, stream););
-    if (fp8) TRY(quantize_operand(m, stream, m->ws + L.o[l], N, HD, xq, wsp<uint8_t>(m, L.oqT[l]), Np, slot(l, A_O)));
+                                               wsp<float>(m, L.lse[l]), m->ws + L.vT, 1, stream,
+                                               fp8 ? slot(l, A_O) : nullptr););
+    if (fp8)
+      TRY(quantize_operand(m, stream, m->ws + L.o[l], N, HD, xq, wsp<uint8_t>(m, L.oqT[l]), Np, slot(l, A_O), true));
     RUN(K_GEMM_O, {
       gk::GemmArgs a;
       a.tile = m->gemm_tile;
@@ -749,9 +755,11 @@ gpt_status gpt_forward_loss(gpt_model* m, const int32_t* idx, const int32_t* tar
       a.lda = C; a.ldb = C;
       a.M = N; a.N = F; a.K = C;
       a.C = m->ws + L.a[l]; a.ldc = F;
+      if (fp8) a.amax_out = slot(l, A_A);
       return gk::launch_gemm(gdt, gk::Epi::Relu2, a, stream);
     });
-    if (fp8) TRY(quantize_operand(m, stream, m->ws + L.a[l], N, F, xq, wsp<uint8_t>(m, L.aqT[l]), Np, slot(l, A_A)));
+    if (fp8)
+      TRY(quantize_operand(m, stream, m->ws + L.a[l], N, F, xq, wsp<uint8_t>(m, L.aqT[l]), Np, slot(l, A_A), true));
     RUN(K_GEMM_W2, {
       gk::GemmArgs a;
       a.tile = m->gemm_tile;
@@ -870,7 +878,7 @@ gpt_status gpt_backward(gpt_model* m, float dloss, int32_t accumulate, void* str
     return GPT_OK;
   };
   auto dx8 = [&](int tag, gk::Epi epi, int l, int dy_slot, int w_slot, int64_t woff, int Nn, int K, void* out,
-                 const void* aux) -> gpt_status {
+                 const void* aux, float* amax_out = nullptr) -> gpt_status {
     RUN(tag, {
       gk::GemmArgs a;
       a.tile = m->gemm_tile;
@@ -881,6 +889,7 @@ gpt_status gpt_backward(gpt_model* m, float dloss, int32_t accumulate, void* str
       a.C2 = const_cast<void*>(aux); a.ldc2 = Nn;
       a.amax_a = slot(l, dy_slot);
       a.amax_b = slot(l, w_slot);
+      a.amax_out = amax_out;
       return gk::launch_gemm(2, epi, a, stream);
     });
     return GPT_OK;
@@ -907,8 +916,9 @@ gpt_status gpt_backward(gpt_model* m, float dloss, int32_t accumulate, void* str
     if (fp8) {
       TRY(quantize_operand(m, stream, m->ws + L.dres_lp, N, C, dyq, dyqT, Np, slot(l, A_DY_MLP)));
       TRY(dw8(K_GEMM_W2_DW, L.aqT[l], l, A_DY_MLP, A_A, C, F, m->off_w2[l]));
-      TRY(dx8(K_GEMM_W2_DX, gk::Epi::Relu2Bwd, l, A_DY_MLP, A_W_2, m->off_w2[l], F, C, m->ws + L.du, m->ws + L.a[l]));
-      TRY(quantize_operand(m, stream, m->ws + L.du, N, F, dyq, dyqT, Np, slot(l, A_DU)));
+      TRY(dx8(K_GEMM_W2_DX, gk::Epi::Relu2Bwd, l, A_DY_MLP, A_W_2, m->off_w2[l], F, C, m->ws + L.du, m->ws + L.a[l],
+              slot(l, A_DU)));
+      TRY(quantize_operand(m, stream, m->ws + L.du, N, F, dyq, dyqT, Np, slot(l, A_DU), true));
       TRY(dw8(K_GEMM_W1_DW, L.h2qT[l], l, A_DU, A_H2, F, C, m->off_w1[l]));
       TRY(dx8(K_GEMM_W1_DX, gk::Epi::Store, l, A_DU, A_W_1, m->off_w1[l], C, F, m->ws + L.dh, nullptr));
     } else {

@@ -42,6 +42,9 @@ struct GemmArgs {
   // fp8 operands (dtype 2): |max| slots of A and B; acc is scaled by 1/(s_a s_b)
   const float* amax_a = nullptr;
   const float* amax_b = nullptr;
+  // Relu2 / Relu2Bwd: optional slot for the |max| of the stored output, one
+  // atomic max per block (the slot must start at 0)
+  float* amax_out = nullptr;
   // batched products (Store / Residual epilogues, no split-K): product j reads
   // A + j*stride_a, B + j*stride_b and writes C + j*stride_c (bytes)
   int batch = 1;
@@ -77,7 +80,8 @@ int attn_padded_len(int T);
 // window: sliding-window length (keys u with 0 <= t - u < window); 0 or >= T
 // means the full causal prefix.
 hipError_t launch_attn_fwd(int dtype, const void* qkv, int B, int T, int H, int window, void* o, float* lse, void* vT,
-                           int stage, hipStream_t s);
+                           int stage, hipStream_t s,
+                           float* amax = nullptr);  // optional: |max| of o, one atomic max per block
 struct AttnBwdArgs {
   const void* qkv;   // [N, (H+2)*128] normalised q, k and v
   const void* o;     // [N, H*128]
