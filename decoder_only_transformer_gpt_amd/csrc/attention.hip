@@ -1188,10 +1188,12 @@ hipError_t bwd_typed(const AttnBwdArgs& a, int stage, hipStream_t s) {
                          (const T*)a.dout, a.lse, a.delta, T_, Tp, H, W, (T*)a.dqkv);
   } else {
     if constexpr (kBf16) {
-      // one block per CU: below two rounds of blocks, split each key block
-      // over two head halves (dK/dV partials added by the combine kernel)
+      // one block per CU: below two rounds of blocks, or with a sliding
+      // window (equal work for most key blocks, so two rounds of blocks pair
+      // up unevenly), split each key block over two head halves (dK/dV
+      // partials added by the combine kernel)
       const int nkb = (T_ + 127) / 128;
-      const int hsplit = (a.dkv_part && H % 2 == 0 && (int64_t)nkb * B < 512) ? 2 : 1;
+      const int hsplit = (a.dkv_part && H % 2 == 0 && ((int64_t)nkb * B < 512 || W > 0)) ? 2 : 1;
       hipLaunchKernelGGL(attn_dkv_bf16_kernel, dim3(nkb * B * hsplit), dim3(256), 0, s, (const bf16*)a.qkv,
                          (const bf16*)a.dout, a.lse, a.delta, T_, H, W, hsplit, (bf16*)a.dqkv, a.dkv_part);
       if (hsplit == 1) return hipGetLastError();
