@@ -376,7 +376,7 @@ DEV float tanh_fast(float y) {
 
 template <typename T>
 struct Epilogue<T, Epi::Store> {
-  template <int TM, int TN, int WN>
+  template <int TM, int TN, int WN, bool FOLD = false>
   static DEV void run(const GemmArgs& a, f32x16 (&acc)[TM][TN], float* lds, int mbase, int nbase, int lane) {
     T* C = reinterpret_cast<T*>(a.C);
     staged_store<TM, TN, WN>(acc, lds, mbase, nbase, lane, [&](int m, int n, float (&v)[4]) {
@@ -387,7 +387,7 @@ struct Epilogue<T, Epi::Store> {
 
 template <typename T>
 struct Epilogue<T, Epi::Residual> {
-  template <int TM, int TN, int WN>
+  template <int TM, int TN, int WN, bool FOLD = false>
   static DEV void run(const GemmArgs& a, f32x16 (&acc)[TM][TN], float* lds, int mbase, int nbase, int lane) {
     T* C = reinterpret_cast<T*>(a.C);
     // bf16: the residual is requested for the whole tile up front (raw, 4
@@ -421,7 +421,7 @@ struct Epilogue<T, Epi::Residual> {
 // max(u, 0) as sqrt(a).
 template <typename T>
 struct Epilogue<T, Epi::Relu2> {
-  template <int TM, int TN, int WN>
+  template <int TM, int TN, int WN, bool FOLD = false>
   static DEV void run(const GemmArgs& a, f32x16 (&acc)[TM][TN], float* lds, int mbase, int nbase, int lane) {
     T* A2 = reinterpret_cast<T*>(a.C);
     float mx = 0.f;
@@ -436,7 +436,8 @@ struct Epilogue<T, Epi::Relu2> {
         store4(A2 + (int64_t)m * a.ldc + n, s);
       }
     });
-    if (a.amax_out) amax_fold_block<T>(mx, a.amax_out);  // the whole block runs the epilogue
+    if constexpr (FOLD)  // the whole block runs the epilogue
+      if (a.amax_out) amax_fold_block<T>(mx, a.amax_out);
   }
 };
 
@@ -444,7 +445,7 @@ struct Epilogue<T, Epi::Relu2> {
 // (prefetched per slab)
 template <typename T>
 struct Epilogue<T, Epi::Relu2Bwd> {
-  template <int TM, int TN, int WN>
+  template <int TM, int TN, int WN, bool FOLD = false>
   static DEV void run(const GemmArgs& a, f32x16 (&acc)[TM][TN], float* lds, int mbase, int nbase, int lane) {
     T* Dp = reinterpret_cast<T*>(a.C);
     const T* A2 = reinterpret_cast<const T*>(a.C2);
@@ -474,7 +475,8 @@ struct Epilogue<T, Epi::Relu2Bwd> {
         store4(Dp + (int64_t)m * a.ldc + n, v);
       }
     });
-    if (a.amax_out) amax_fold_block<T>(mx, a.amax_out);
+    if constexpr (FOLD)
+      if (a.amax_out) amax_fold_block<T>(mx, a.amax_out);
   }
 };
 
@@ -491,7 +493,7 @@ struct Epilogue<T, Epi::Relu2Bwd> {
 // reduced with shuffles. The row's target id is prefetched with the slab.
 template <typename T>
 struct Epilogue<T, Epi::LMHead> {
-  template <int TM, int TN, int WN>
+  template <int TM, int TN, int WN, bool FOLD = false>
   static DEV void run(const GemmArgs& a, f32x16 (&acc)[TM][TN], float* lds, int mbase, int nbase, int lane) {
     static_assert(WN % kLMHeadPartCols == 0 && kLMHeadPartCols == 64, "16 lanes per partial");
     const float c = a.softcap, inv_c = 1.f / a.softcap;
@@ -525,7 +527,7 @@ struct Epilogue<T, Epi::LMHead> {
 
 template <typename T>
 struct Epilogue<T, Epi::GradF32> {
-  template <int TM, int TN, int WN>
+  template <int TM, int TN, int WN, bool FOLD = false>
   static DEV void run(const GemmArgs& a, f32x16 (&acc)[TM][TN], float* lds, int mbase, int nbase, int lane) {
     if (a.splits > 1) {
       const int z = a.zslice >= 0 ? a.zslice : (int)blockIdx.z;
@@ -769,7 +771,8 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm_nt_lds_kernel(GemmArgs args
   GemmArgs ea = args;
   ea.zslice = split;
   ea.C = reinterpret_cast<char*>(args.C) + bz * args.stride_c;
-  Epilogue<T, E>::template run<TM, TN, WN>(ea, acc, slab, m0 + wm * WM, n0 + wn * WN, lane);
+  // FP8 products (ES = 1) fold the |max| of a relu^2 / relu^2-backward output
+  Epilogue<T, E>::template run<TM, TN, WN, ES == 1>(ea, acc, slab, m0 + wm * WM, n0 + wn * WN, lane);
 }
 
 // bf16 GEMM with both operands mn-contiguous (dW = dy^T x: A = dy [K, M] and

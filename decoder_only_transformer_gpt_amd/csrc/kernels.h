@@ -42,8 +42,8 @@ struct GemmArgs {
   // fp8 operands (dtype 2): |max| slots of A and B; acc is scaled by 1/(s_a s_b)
   const float* amax_a = nullptr;
   const float* amax_b = nullptr;
-  // Relu2 / Relu2Bwd: optional slot for the |max| of the stored output, one
-  // atomic max per block (the slot must start at 0)
+  // Relu2 / Relu2Bwd on fp8 operands: optional slot for the |max| of the
+  // stored output, one atomic max per block (the slot must start at 0)
   float* amax_out = nullptr;
   // batched products (Store / Residual epilogues, no split-K): product j reads
   // A + j*stride_a, B + j*stride_b and writes C + j*stride_c (bytes)
