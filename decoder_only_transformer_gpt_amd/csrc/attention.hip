@@ -853,10 +853,13 @@ DEV void dq_tile(const KvStage& s, const RowFrag& rf, const TrFrag& tf, const u3
 }
 
 template <int NST>
+// Also forms delta = rowsum(dO * O) for its queries (from the dO fragments it
+// holds and O's matching ones) and stores it for the dK/dV kernel.
 __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void attn_dq_bf16_kernel(const bf16* __restrict__ qkv,
                                                                              const bf16* __restrict__ dout,
+                                                                             const bf16* __restrict__ o,
                                                                              const float* __restrict__ lse,
-                                                                             const float* __restrict__ delta, int T_,
+                                                                             float* __restrict__ delta, int T_,
                                                                              int H, int W, bf16* __restrict__ dqkv) {
   static_assert(NST == 2 || NST == 4, "two or four stages");
   __shared__ __attribute__((aligned(1024))) KvStage st[NST];
@@ -878,7 +881,23 @@ __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void attn_dq_bf16_kernel(con
   load_row_frags(df, dout + ((int64_t)b * T_ + qw) * H * D + h * D, T_ - qw, (uint32_t)H * D * 2u, l32, g);
   const int64_t si = ((int64_t)b * H + h) * T_ + q;
   const float l2 = qv ? lse[si] : 0.f;
-  const float dlt = qv ? delta[si] : 0.f;
+  float dlt;
+  {  // delta: this lane's 64 products of the query's row (chunks 2ks + g), then its partner's
+    u32x4 of[8];
+    load_row_frags(of, o + ((int64_t)b * T_ + qw) * H * D + h * D, T_ - qw, (uint32_t)H * D * 2u, l32, g);
+    float s = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t x = df[ks][e], y = of[ks][e];
+        s += __uint_as_float(x << 16) * __uint_as_float(y << 16) +
+             __uint_as_float(x & 0xffff0000u) * __uint_as_float(y & 0xffff0000u);
+      }
+    s += __shfl_xor(s, 32, 64);
+    dlt = qv ? s : 0.f;
+    if (qv && g == 0) delta[si] = s;
+  }
   const float scale = rsqrtf((float)D);
   const float sl2 = kLog2e * scale;
   f32x16 acc[4];
@@ -1184,14 +1203,16 @@ hipError_t bwd_typed(const AttnBwdArgs& a, int stage, hipStream_t s) {
       if ((e = transpose<T>(a.qkv, ld, H * D, 1, B, T_, Tp, a.kT, s)) != hipSuccess) return e;
       if ((e = transpose<T>(a.dout, (int64_t)H * D, 0, H, B, T_, Tp, a.doT, s)) != hipSuccess) return e;
     }
-    const int64_t groups = (int64_t)B * T_ * H;
-    hipLaunchKernelGGL(attn_delta_kernel<T>, dim3((unsigned)((groups * 16 + 255) / 256)), dim3(256), 0, s,
-                       (const T*)a.o, (const T*)a.dout, B * T_, T_, H, a.delta);
+    if (!kBf16) {  // the bf16 dQ kernel forms delta itself
+      const int64_t groups = (int64_t)B * T_ * H;
+      hipLaunchKernelGGL(attn_delta_kernel<T>, dim3((unsigned)((groups * 16 + 255) / 256)), dim3(256), 0, s,
+                         (const T*)a.o, (const T*)a.dout, B * T_, T_, H, a.delta);
+    }
   } else if (stage == 1) {
     const dim3 grid(((T_ + 127) / 128) * H * B);
     if constexpr (kBf16)
       hipLaunchKernelGGL(attn_dq_bf16_kernel<kDqStages>, grid, dim3(256), 0, s, (const bf16*)a.qkv,
-                         (const bf16*)a.dout, a.lse, a.delta, T_, H, W, (bf16*)a.dqkv);
+                         (const bf16*)a.dout, (const bf16*)a.o, a.lse, a.delta, T_, H, W, (bf16*)a.dqkv);
     else
       hipLaunchKernelGGL(attn_dq_kernel<T>, grid, dim3(256), 0, s, (const T*)a.qkv, (const T*)a.kT,
                          (const T*)a.dout, a.lse, a.delta, T_, Tp, H, W, (T*)a.dqkv);

@@ -952,7 +952,8 @@ gpt_status gpt_backward(gpt_model* m, float dloss, int32_t accumulate, void* str
     ab.doT = m->ws + L.doT;
     ab.dqkv = m->ws + L.dqkv;
     ab.dkv_part = wsp<float>(m, L.dkv_part);
-    RUN(K_ATTN_BWD_PREP, return gk::launch_attn_bwd(dt, ab, 0, stream););
+    // fp32: transposed copies and delta (the bf16 dQ kernel forms delta itself)
+    if (dt == GPT_F32) RUN(K_ATTN_BWD_PREP, return gk::launch_attn_bwd(dt, ab, 0, stream););
     RUN(K_ATTN_BWD_DQ, return gk::launch_attn_bwd(dt, ab, 1, stream););
     RUN(K_ATTN_BWD_DKV, return gk::launch_attn_bwd(dt, ab, 2, stream););
     RUN(K_ROPE_QKNORM_BWD, return gk::launch_rope_qknorm_bwd(dt, m->ws + L.dqkv, m->ws + L.qkv[l],
