@@ -366,14 +366,6 @@ DEV void staged_store_pre(f32x16 (&acc)[TM][TN], float* st, int mbase, int nbase
   }
 }
 
-// tanh(y) = 1 - 2 / (exp(2y) + 1) on v_exp_f32 and v_rcp_f32; saturates to
-// +-1 through exp's overflow to inf and underflow to 0. Absolute error a few
-// 1e-7 (cancellation near 0 bounds it in absolute, not relative, terms).
-DEV float tanh_fast(float y) {
-  const float e = __builtin_amdgcn_exp2f(y * 2.8853900817779268f);  // 2 log2(e)
-  return 1.f - 2.f * __builtin_amdgcn_rcpf(e + 1.f);
-}
-
 template <typename T>
 struct Epilogue<T, Epi::Store> {
   template <int TM, int TN, int WN, bool FOLD = false>
@@ -468,8 +460,11 @@ struct Epilogue<T, Epi::Relu2Bwd> {
         } else {
           load4(A2 + (int64_t)m * a.ldc2 + n, x);
         }
+        // v_sqrt_f32 alone, not correctly rounded: sqrtf's correctly rounded
+        // expansion costs about fifteen instructions per element here, and the
+        // product is rounded to the activation dtype anyway
         for (int q = 0; q < 4; ++q) {
-          v[q] *= 2.f * sqrtf(x[q]);
+          v[q] *= 2.f * __builtin_amdgcn_sqrtf(x[q]);
           mx = fmaxf(mx, fabsf(v[q]));
         }
         store4(Dp + (int64_t)m * a.ldc + n, v);
@@ -489,6 +484,10 @@ struct Epilogue<T, Epi::Relu2Bwd> {
 // softmax numerator times the slope of the softcap, from which the backward
 // needs only a per-row scale and a fix at the target column (the cross-entropy
 // gradient dz = (exp(z' - lse) - [v == target]) (1 - (z'/c)^2) dloss / N).
+// All three come from R = 1 / (exp(2z/c) + 1): tanh(z/c) = 1 - 2R, so
+// z' - c = -2cR and 1 - (z'/c)^2 = 4R(1 - R), free of the cancellation of
+// the plain forms near tanh = +-1; three transcendentals and six other
+// instructions per entry (exp overflow to inf gives R = 0, underflow R = 1).
 // Done on the staged rows: 64 columns of a row sit in 16 lanes (4 each),
 // reduced with shuffles. The row's target id is prefetched with the slab.
 template <typename T>
@@ -496,28 +495,31 @@ struct Epilogue<T, Epi::LMHead> {
   template <int TM, int TN, int WN, bool FOLD = false>
   static DEV void run(const GemmArgs& a, f32x16 (&acc)[TM][TN], float* lds, int mbase, int nbase, int lane) {
     static_assert(WN % kLMHeadPartCols == 0 && kLMHeadPartCols == 64, "16 lanes per partial");
-    const float c = a.softcap, inv_c = 1.f / a.softcap;
+    constexpr float kLog2e = 1.4426950408889634f;
+    const float c = a.softcap;
+    const float k2 = 2.f * kLog2e / c;   // exp(2z/c) as exp2(z * k2)
+    const float kq = -2.f * c * kLog2e;  // 4 exp(-2cR) as exp2(R * kq + 2)
     const int nparts = a.N / kLMHeadPartCols;
     T* Z = reinterpret_cast<T*>(a.C);
     auto pre = [&](int m, int) { return m < a.M ? a.targets[m] : -1; };
     staged_store_pre<TM, TN, WN>(acc, lds, mbase, nbase, lane, pre, [&](int m, int n, float (&v)[4], int tgt) {
       const bool mv = m < a.M;
-      float sum = 0.f, z[4], q[4];
+      float sum4 = 0.f, R[4], q[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        z[r] = c * tanh_fast(v[r] * inv_c);
-        const float e = __builtin_amdgcn_exp2f((z[r] - c) * 1.4426950408889634f);
-        const float u = z[r] * inv_c;
-        sum += e;
-        q[r] = e * (1.f - u * u);
+        R[r] = __builtin_amdgcn_rcpf(__builtin_amdgcn_exp2f(v[r] * k2) + 1.f);
+        const float e4 = __builtin_amdgcn_exp2f(fmaf(R[r], kq, 2.f));  // 4 exp(z' - c)
+        sum4 += e4;
+        q[r] = e4 * fmaf(-R[r], R[r], R[r]);
       }
       // the target's column among the lane's 4: chosen from scalars by
       // compares (a select chain over an array is folded into an indexed
       // load that puts the array in scratch memory)
       const unsigned d = (unsigned)(tgt - n);
-      const float zt = d == 0u ? z[0] : (d == 1u ? z[1] : (d == 2u ? z[2] : z[3]));
-      if (d < 4u) a.ztgt[m] = zt;
+      const float Rt = d == 0u ? R[0] : (d == 1u ? R[1] : (d == 2u ? R[2] : R[3]));
+      if (d < 4u) a.ztgt[m] = fmaf(-2.f * c, Rt, c);
       if (mv) store4(Z + (int64_t)m * a.ldc + n, q);
+      float sum = 0.25f * sum4;
 #pragma unroll
       for (int o = 8; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 16);
       if (mv && (lane & 15) == 0) a.part[(int64_t)m * nparts + n / kLMHeadPartCols] = sum;
