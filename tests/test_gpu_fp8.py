@@ -130,7 +130,9 @@ def _codes(torch, vals_bits, ldT=16):
 @pytest.mark.parametrize("M,N,K,out,tile,splits", [
     (999, 1536, 1024, "bf16", 0, 1), (999, 1536, 1024, "bf16", 1, 1), (999, 1536, 1024, "bf16", 2, 1),
     (999, 1536, 1024, "bf16", 3, 1), (300, 260, 384, "f32", 3, 1), (1536, 768, 4096, "f32", 1, 4),
-    (640, 512, 2048, "f32", 0, 3), (33, 64, 128, "bf16", 0, 1)])
+    (640, 512, 2048, "f32", 0, 3), (33, 64, 128, "bf16", 0, 1),
+    # more 256x256 tiles than compute units, an odd K tile count
+    (4500, 4224, 384, "bf16", 1, 1), (2100, 8448, 640, "f32", 1, 1)])
 def test_fp8_matmul_on_identical_codes(M, N, K, out, tile, splits):
     """The e4m3 GEMM against the float64 product of the same dequantised codes
     (the oracle's codes equal the GPU's: checked bit for bit above), ragged M
