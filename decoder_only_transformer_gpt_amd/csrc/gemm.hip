@@ -354,6 +354,11 @@ DEV void staged_store_pre(f32x16 (&acc)[TM][TN], float* st, int mbase, int nbase
         float v[4] = {acc[i][j][blk * 4], acc[i][j][blk * 4 + 1], acc[i][j][blk * 4 + 2], acc[i][j][blk * 4 + 3]};
         store4(st + l32 * P + j * 32 + blk * 8 + g * 4, v);
       }
+    // ALL: every prefetch has landed before the first store goes out. (Left
+    // to itself the compiler waits per item, inside the item's bounds test,
+    // and once stores are in flight a wait for a load is a wait for all
+    // outstanding accesses: each item would wait for the previous store.)
+    if (ALL && i == 0) wait_vmcnt<0>();
     slab_sync();
 #pragma unroll
     for (int q = 0; q < NP; ++q) {
@@ -366,13 +371,36 @@ DEV void staged_store_pre(f32x16 (&acc)[TM][TN], float* st, int mbase, int nbase
   }
 }
 
+// Output addressing of a wave's (TM*32) x WN tile at (mbase, nbase) in a
+// row-major matrix of leading dimension ld: one 64-bit base per wave and
+// 32-bit element offsets from it (the launcher bounds ld by 2^22 so that the
+// tile's rows fit), and no per-item bounds test when the whole tile lies
+// inside M x N. (64-bit index arithmetic and the bounds test per 4-column
+// item were half the instructions of the store path.) Used where it measured
+// faster: the residual and fp32-gradient epilogues keep the 64-bit form
+// (the residual one, which reads and writes the same positions, ran 17 %
+// slower with this).
+template <int TM, int WN>
+struct TileAddr {
+  static_assert(TM * 32 <= 256, "32-bit offsets: at most 256 rows of at most 2^22 elements");
+  int64_t base;
+  int ld, mbase, nbase, M, N;
+  bool full;
+  DEV TileAddr(int64_t ld_, int mb, int nb, int M_, int N_)
+      : base((int64_t)mb * ld_ + nb), ld((int)ld_), mbase(mb), nbase(nb), M(M_), N(N_),
+        full(mb + TM * 32 <= M_ && nb + WN <= N_) {}
+  DEV bool in(int m, int n) const { return full || (m < M && n < N); }
+  DEV int off(int m, int n) const { return (m - mbase) * ld + (n - nbase); }
+};
+
 template <typename T>
 struct Epilogue<T, Epi::Store> {
   template <int TM, int TN, int WN, bool FOLD = false>
   static DEV void run(const GemmArgs& a, f32x16 (&acc)[TM][TN], float* lds, int mbase, int nbase, int lane) {
-    T* C = reinterpret_cast<T*>(a.C);
+    const TileAddr<TM, WN> t(a.ldc, mbase, nbase, a.M, a.N);
+    T* C = reinterpret_cast<T*>(a.C) + t.base;
     staged_store<TM, TN, WN>(acc, lds, mbase, nbase, lane, [&](int m, int n, float (&v)[4]) {
-      if (m < a.M && n < a.N) store4(C + (int64_t)m * a.ldc + n, v);
+      if (t.in(m, n)) store4(C + t.off(m, n), v);
     });
   }
 };
@@ -415,17 +443,18 @@ template <typename T>
 struct Epilogue<T, Epi::Relu2> {
   template <int TM, int TN, int WN, bool FOLD = false>
   static DEV void run(const GemmArgs& a, f32x16 (&acc)[TM][TN], float* lds, int mbase, int nbase, int lane) {
-    T* A2 = reinterpret_cast<T*>(a.C);
+    const TileAddr<TM, WN> t(a.ldc, mbase, nbase, a.M, a.N);
+    T* A2 = reinterpret_cast<T*>(a.C) + t.base;
     float mx = 0.f;
     staged_store<TM, TN, WN>(acc, lds, mbase, nbase, lane, [&](int m, int n, float (&v)[4]) {
-      if (m < a.M && n < a.N) {
+      if (t.in(m, n)) {
         float s[4];
         for (int r = 0; r < 4; ++r) {
           const float p = fmaxf(v[r], 0.f);
           s[r] = p * p;
           mx = fmaxf(mx, s[r]);
         }
-        store4(A2 + (int64_t)m * a.ldc + n, s);
+        store4(A2 + t.off(m, n), s);
       }
     });
     if constexpr (FOLD)  // the whole block runs the epilogue
@@ -439,26 +468,27 @@ template <typename T>
 struct Epilogue<T, Epi::Relu2Bwd> {
   template <int TM, int TN, int WN, bool FOLD = false>
   static DEV void run(const GemmArgs& a, f32x16 (&acc)[TM][TN], float* lds, int mbase, int nbase, int lane) {
-    T* Dp = reinterpret_cast<T*>(a.C);
-    const T* A2 = reinterpret_cast<const T*>(a.C2);
+    const TileAddr<TM, WN> t(a.ldc, mbase, nbase, a.M, a.N), t2(a.ldc2, mbase, nbase, a.M, a.N);
+    T* Dp = reinterpret_cast<T*>(a.C) + t.base;
+    const T* A2 = reinterpret_cast<const T*>(a.C2) + t2.base;
     float mx = 0.f;
     // a is prefetched raw (4 bf16 in two dwords) for the whole tile
     auto pre = [&](int m, int n) {
       u32x2 r = {0u, 0u};
       if constexpr (sizeof(T) == 2) {
-        if (m < a.M && n < a.N) r = ld8(A2 + (int64_t)m * a.ldc2 + n);
+        if (t.in(m, n)) r = ld8(A2 + t2.off(m, n));
       }
       return r;
     };
     staged_store_pre<TM, TN, WN, sizeof(T) == 2>(acc, lds, mbase, nbase, lane, pre,
                                                  [&](int m, int n, float (&v)[4], u32x2 r) {
-      if (m < a.M && n < a.N) {
+      if (t.in(m, n)) {
         float x[4];
         if constexpr (sizeof(T) == 2) {
           x[0] = __uint_as_float(r[0] << 16); x[1] = __uint_as_float(r[0] & 0xffff0000u);
           x[2] = __uint_as_float(r[1] << 16); x[3] = __uint_as_float(r[1] & 0xffff0000u);
         } else {
-          load4(A2 + (int64_t)m * a.ldc2 + n, x);
+          load4(A2 + t2.off(m, n), x);
         }
         // v_sqrt_f32 alone, not correctly rounded: sqrtf's correctly rounded
         // expansion costs about fifteen instructions per element here, and the
@@ -467,7 +497,7 @@ struct Epilogue<T, Epi::Relu2Bwd> {
           v[q] *= 2.f * __builtin_amdgcn_sqrtf(x[q]);
           mx = fmaxf(mx, fabsf(v[q]));
         }
-        store4(Dp + (int64_t)m * a.ldc + n, v);
+        store4(Dp + t.off(m, n), v);
       }
     });
     if constexpr (FOLD)
@@ -500,10 +530,12 @@ struct Epilogue<T, Epi::LMHead> {
     const float k2 = 2.f * kLog2e / c;   // exp(2z/c) as exp2(z * k2)
     const float kq = -2.f * c * kLog2e;  // 4 exp(-2cR) as exp2(R * kq + 2)
     const int nparts = a.N / kLMHeadPartCols;
-    T* Z = reinterpret_cast<T*>(a.C);
+    const TileAddr<TM, WN> t(a.ldc, mbase, nbase, a.M, a.N);
+    T* Z = reinterpret_cast<T*>(a.C) + t.base;
+    float* part = a.part + ((int64_t)mbase * nparts + nbase / kLMHeadPartCols);
     auto pre = [&](int m, int) { return m < a.M ? a.targets[m] : -1; };
     staged_store_pre<TM, TN, WN>(acc, lds, mbase, nbase, lane, pre, [&](int m, int n, float (&v)[4], int tgt) {
-      const bool mv = m < a.M;
+      const bool mv = t.full || m < a.M;
       float sum4 = 0.f, R[4], q[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -518,11 +550,11 @@ struct Epilogue<T, Epi::LMHead> {
       const unsigned d = (unsigned)(tgt - n);
       const float Rt = d == 0u ? R[0] : (d == 1u ? R[1] : (d == 2u ? R[2] : R[3]));
       if (d < 4u) a.ztgt[m] = fmaf(-2.f * c, Rt, c);
-      if (mv) store4(Z + (int64_t)m * a.ldc + n, q);
+      if (mv) store4(Z + t.off(m, n), q);
       float sum = 0.25f * sum4;
 #pragma unroll
       for (int o = 8; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 16);
-      if (mv && (lane & 15) == 0) a.part[(int64_t)m * nparts + n / kLMHeadPartCols] = sum;
+      if (mv && (lane & 15) == 0) part[(m - mbase) * nparts + (n - nbase) / kLMHeadPartCols] = sum;
     });
   }
 };
@@ -1155,6 +1187,9 @@ hipError_t launch_typed(Epi epi, const GemmArgs& a, hipStream_t s) {
 
 hipError_t launch_gemm(int dtype, Epi epi, const GemmArgs& a, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0 || a.batch <= 0) return hipSuccess;
+  // epilogues address a wave's output tile (at most 256 rows) with 32-bit
+  // element offsets
+  if (a.ldc > (1 << 22) || a.ldc2 > (1 << 22) || a.N > (1 << 22)) return hipErrorInvalidValue;
   if (a.batch > 1) {
     if ((epi != Epi::Store && epi != Epi::Residual) || a.splits != 1) return hipErrorInvalidValue;
     // one launch on the bf16 direct-to-LDS kernel; any other path, product by product
