@@ -23,9 +23,17 @@ namespace {
 
 constexpr int kMaxChunks = 8;  // 8-element chunks per lane: C <= 64 * 8 * 8 = 4096
 
+// A wave owns a row; lane L holds the 8-element chunks L + 64 j, j < J, with
+// J = ceil(C / 512) a template argument (register arrays sized to the row).
+// Where the last round has no chunk for a lane, the lane loads the row's last
+// chunk again and drops it: every load is issued unconditionally, back to
+// back, before the first use. (A load under a per-lane test is waited for
+// inside the test, so the rounds' loads would go out one round at a time.)
+DEV int chunk_of(int lane, int j, int nch) { return min(lane + j * 64, nch - 1); }
+
 // --------------------------------------------------------------- RMSNorm --
 
-template <typename T, bool GATHER>
+template <typename T, bool GATHER, int J>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const T* __restrict__ src, const int32_t* __restrict__ idx,
                                                       int N, int C, int V, float eps, T* __restrict__ y,
                                                       float* __restrict__ rstd, int* flag) {
@@ -41,16 +49,16 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const T* __restrict__ src,
   }
   const T* s = src + srow * C;
   const int nch = C >> 3;
-  float v[kMaxChunks][8];
+  float v[J][8];
+#pragma unroll
+  for (int j = 0; j < J; ++j) load8(s + chunk_of(lane, j, nch) * 8, v[j]);
   float ss = 0.f;
 #pragma unroll
-  for (int j = 0; j < kMaxChunks; ++j) {
-    const int ch = lane + j * 64;
-    if (ch < nch) {
-      load8(s + ch * 8, v[j]);
+  for (int j = 0; j < J; ++j) {
+    float t = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) ss += v[j][e] * v[j][e];
-    }
+    for (int e = 0; e < 8; ++e) t += v[j][e] * v[j][e];
+    ss += lane + j * 64 < nch ? t : 0.f;
   }
   ss = wave_sum(ss);
   float r = rsqrtf(ss / (float)C + eps);
@@ -60,7 +68,7 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const T* __restrict__ src,
   }
   T* d = y + (int64_t)row * C;
 #pragma unroll
-  for (int j = 0; j < kMaxChunks; ++j) {
+  for (int j = 0; j < J; ++j) {
     const int ch = lane + j * 64;
     if (ch < nch) {
       float o[8];
@@ -73,7 +81,7 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const T* __restrict__ src,
 }
 
 // dres = (accumulate ? dres : 0) + r * (dy - y * mean(dy * y)); dres_lp = dres (activation dtype)
-template <typename T>
+template <typename T, int J>
 __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const T* __restrict__ dy, const T* __restrict__ y,
                                                           const float* __restrict__ rstd, int N, int C,
                                                           int accumulate, float* __restrict__ dres,
@@ -85,36 +93,42 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const T* __restrict__ 
   const int64_t off = (int64_t)row * C;
   const int nch = C >> 3;
   const float gs = dy_row_scale ? dy_row_scale[row] : 1.f;
-  float g[kMaxChunks][8], yy[kMaxChunks][8];
+  const float r = rstd[row];
+  float g[J][8], yy[J][8], o[J][8];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int ch = chunk_of(lane, j, nch);
+    load8(dy + off + ch * 8, g[j]);
+    load8(y + off + ch * 8, yy[j]);
+  }
+  if (accumulate) {
+#pragma unroll
+    for (int j = 0; j < J; ++j) load8(dres + off + chunk_of(lane, j, nch) * 8, o[j]);
+  }
   float dot = 0.f;
 #pragma unroll
-  for (int j = 0; j < kMaxChunks; ++j) {
-    const int ch = lane + j * 64;
-    if (ch < nch) {
-      load8(dy + off + ch * 8, g[j]);
-      load8(y + off + ch * 8, yy[j]);
+  for (int j = 0; j < J; ++j) {
+    float t = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        g[j][e] *= gs;
-        dot += g[j][e] * yy[j][e];
-      }
+    for (int e = 0; e < 8; ++e) {
+      g[j][e] *= gs;
+      t += g[j][e] * yy[j][e];
     }
+    dot += lane + j * 64 < nch ? t : 0.f;
   }
   dot = wave_sum(dot) / (float)C;
-  const float r = rstd[row];
 #pragma unroll
-  for (int j = 0; j < kMaxChunks; ++j) {
+  for (int j = 0; j < J; ++j) {
     const int ch = lane + j * 64;
     if (ch < nch) {
-      float o[8];
-      if (accumulate) load8(dres + off + ch * 8, o);
+      float out[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float dx = r * (g[j][e] - yy[j][e] * dot);
-        o[e] = accumulate ? o[e] + dx : dx;
+        out[e] = accumulate ? o[j][e] + dx : dx;
       }
-      store8(dres + off + ch * 8, o);
-      store8(dres_lp + off + ch * 8, o);
+      store8(dres + off + ch * 8, out);
+      store8(dres_lp + off + ch * 8, out);
     }
   }
 }
@@ -202,41 +216,67 @@ __global__ void fill_kernel(float* p, float v, int64_t n) {
     p[i] = v;
 }
 
+// Launch a row kernel instance with J = ceil(C / 512) chunks per lane.
+template <template <int> class K, typename... Args>
+hipError_t launch_rows(int C, dim3 grid, hipStream_t s, Args... args) {
+  switch ((C / 8 + 63) / 64) {
+    case 1: hipLaunchKernelGGL(K<1>::fn, grid, dim3(256), 0, s, args...); break;
+    case 2: hipLaunchKernelGGL(K<2>::fn, grid, dim3(256), 0, s, args...); break;
+    case 3: hipLaunchKernelGGL(K<3>::fn, grid, dim3(256), 0, s, args...); break;
+    case 4: hipLaunchKernelGGL(K<4>::fn, grid, dim3(256), 0, s, args...); break;
+    case 5: hipLaunchKernelGGL(K<5>::fn, grid, dim3(256), 0, s, args...); break;
+    case 6: hipLaunchKernelGGL(K<6>::fn, grid, dim3(256), 0, s, args...); break;
+    case 7: hipLaunchKernelGGL(K<7>::fn, grid, dim3(256), 0, s, args...); break;
+    case 8: hipLaunchKernelGGL(K<8>::fn, grid, dim3(256), 0, s, args...); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+template <typename T, bool GATHER>
+struct RmsK {
+  template <int J>
+  struct At {
+    static constexpr auto fn = rmsnorm_kernel<T, GATHER, J>;
+  };
+};
+template <typename T>
+struct RmsBwdK {
+  template <int J>
+  struct At {
+    static constexpr auto fn = rmsnorm_bwd_kernel<T, J>;
+  };
+};
+
 }  // namespace
 
 hipError_t launch_embed_rmsnorm(int dtype, const void* wte, const int32_t* idx, int N, int C, int V, float eps,
                                 void* x, float* rstd, int* flag, hipStream_t s) {
+  if (C <= 0 || C % 8 != 0 || C > 64 * 8 * kMaxChunks) return hipErrorInvalidValue;
   dim3 grid((N + 3) / 4);
   if (dtype == 1)
-    hipLaunchKernelGGL((rmsnorm_kernel<bf16, true>), grid, dim3(256), 0, s, (const bf16*)wte, idx, N, C, V, eps,
-                       (bf16*)x, rstd, flag);
-  else
-    hipLaunchKernelGGL((rmsnorm_kernel<float, true>), grid, dim3(256), 0, s, (const float*)wte, idx, N, C, V, eps,
-                       (float*)x, rstd, flag);
-  return hipGetLastError();
+    return launch_rows<RmsK<bf16, true>::At>(C, grid, s, (const bf16*)wte, idx, N, C, V, eps, (bf16*)x, rstd, flag);
+  return launch_rows<RmsK<float, true>::At>(C, grid, s, (const float*)wte, idx, N, C, V, eps, (float*)x, rstd, flag);
 }
 
 hipError_t launch_rmsnorm(int dtype, const void* x, int N, int C, float eps, void* y, float* rstd, hipStream_t s) {
+  if (C <= 0 || C % 8 != 0 || C > 64 * 8 * kMaxChunks) return hipErrorInvalidValue;
   dim3 grid((N + 3) / 4);
   if (dtype == 1)
-    hipLaunchKernelGGL((rmsnorm_kernel<bf16, false>), grid, dim3(256), 0, s, (const bf16*)x, nullptr, N, C, 0,
-                       eps, (bf16*)y, rstd, nullptr);
-  else
-    hipLaunchKernelGGL((rmsnorm_kernel<float, false>), grid, dim3(256), 0, s, (const float*)x, nullptr, N, C, 0,
-                       eps, (float*)y, rstd, nullptr);
-  return hipGetLastError();
+    return launch_rows<RmsK<bf16, false>::At>(C, grid, s, (const bf16*)x, (const int32_t*)nullptr, N, C, 0, eps,
+                                              (bf16*)y, rstd, (int*)nullptr);
+  return launch_rows<RmsK<float, false>::At>(C, grid, s, (const float*)x, (const int32_t*)nullptr, N, C, 0, eps,
+                                             (float*)y, rstd, (int*)nullptr);
 }
 
 hipError_t launch_rmsnorm_bwd(int dtype, const void* dy, const void* y, const float* rstd, int N, int C,
                               int accumulate, float* dres, void* dres_lp, hipStream_t s, const float* dy_row_scale) {
+  if (C <= 0 || C % 8 != 0 || C > 64 * 8 * kMaxChunks) return hipErrorInvalidValue;
   dim3 grid((N + 3) / 4);
   if (dtype == 1)
-    hipLaunchKernelGGL(rmsnorm_bwd_kernel<bf16>, grid, dim3(256), 0, s, (const bf16*)dy, (const bf16*)y, rstd, N,
-                       C, accumulate, dres, (bf16*)dres_lp, dy_row_scale);
-  else
-    hipLaunchKernelGGL(rmsnorm_bwd_kernel<float>, grid, dim3(256), 0, s, (const float*)dy, (const float*)y, rstd,
-                       N, C, accumulate, dres, (float*)dres_lp, dy_row_scale);
-  return hipGetLastError();
+    return launch_rows<RmsBwdK<bf16>::At>(C, grid, s, (const bf16*)dy, (const bf16*)y, rstd, N, C, accumulate, dres,
+                                          (bf16*)dres_lp, dy_row_scale);
+  return launch_rows<RmsBwdK<float>::At>(C, grid, s, (const float*)dy, (const float*)y, rstd, N, C, accumulate,
+                                         dres, (float*)dres_lp, dy_row_scale);
 }
 
 hipError_t launch_rope_qknorm(int dtype, void* qkv, int B, int T, int H, float eps, const float* cos_t,
