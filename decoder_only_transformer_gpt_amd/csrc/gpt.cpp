@@ -122,12 +122,14 @@ struct Planner {
 };
 
 // Split-K slices for a dW GEMM [M, N] reduced over K tokens (256x256 tiles,
-// one CTA per CU, 256 CUs). Candidates give at least two rounds of CTAs (at
-// least 1024 k per slice, at most 32 slices). Score of a slice count t: the
-// busy fraction of the rounds, with a 10 % handicap when tiles * t is not a
-// multiple of 8 (the kernel then cannot hand each XCD whole slices, whose K
-// windows share its L2). The fewest slices scoring at least 0.93 (each slice
-// adds an M x N fp32 partial), else the best score.
+// one CTA per CU, 256 CUs). Candidates give at least one full round of CTAs
+// (at least 1024 k per slice, at most 32 slices; requiring two rounds had
+// cost the QKV and O dW 24 and 30 slices of partial traffic). Score of a
+// slice count t: the busy fraction of the rounds. The fewest slices scoring
+// at least 0.93 (each slice adds an M x N fp32 partial that is written and
+// read back), else the best score. (A handicap for tiles * t not a multiple
+// of 8, meant to keep whole slices on one XCD, doubled the MLP dW slices to
+// 10 and cost each of them about 1 ms per d20 step.)
 int dw_splits(int M, int N, int K) {
   const int64_t tiles = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
   const int cap = std::min(32, std::max(1, K / 1024));
@@ -135,10 +137,9 @@ int dw_splits(int M, int N, int K) {
   double best_score = -1.0;
   for (int t = 1; t <= cap; ++t) {
     const int64_t blocks = tiles * t;
-    if (blocks < 512 && t < cap) continue;
+    if (blocks < 256 && t < cap) continue;
     const int64_t rounds = (blocks + 255) / 256;
     double score = (double)blocks / (double)(rounds * 256);
-    if (blocks % 8 != 0) score *= 0.9;
     if (score >= 0.93) return t;
     if (score > best_score + 1e-9) {
       best_score = score;
