@@ -321,7 +321,8 @@ namespace {
 
 // Batched 2-D transpose of activation-dtype matrices: for every tensor t,
 // dst[t][c][r] = src[t][r][c]. One 64x64 tile per block, staged through LDS
-// (+1 column of padding against bank conflicts); tiles of all tensors are
+// (+1 column of padding against bank conflicts; 16-element vector accesses
+// for whole tiles, element by element at ragged edges); tiles of all tensors are
 // numbered consecutively and a block finds its tensor by a linear scan of
 // the (few dozen) tile-start offsets.
 template <typename T>
@@ -336,6 +337,30 @@ __global__ __launch_bounds__(256) void transpose_batched_kernel(const T* __restr
   const int r0 = (int)(local / tiles_c) * 64, c0 = (int)(local % tiles_c) * 64;
   const T* s = src + d.offset;
   T* o = dst + d.offset;
+  // whole tiles of 16-byte-aligned rows: each lane reads 16 consecutive
+  // elements of one row and writes 16 consecutive elements of one output row
+  // (element-wise accesses under per-element bounds tests had run at a
+  // fraction of the HBM rate)
+  const bool whole = r0 + 64 <= d.rows && c0 + 64 <= d.cols && d.rows % 16 == 0 && d.cols % 16 == 0 &&
+                     (d.offset * (int64_t)sizeof(T)) % 16 == 0;
+  if (whole) {  // uniform per block
+    const int q = threadIdx.x & 3, rc = threadIdx.x >> 2;
+    float v[2][8];
+    const T* sp = s + (int64_t)(r0 + rc) * d.cols + c0 + q * 16;
+    load8(sp, v[0]);
+    load8(sp + 8, v[1]);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) tile[rc][q * 16 + k] = v[k >> 3][k & 7];
+    __syncthreads();
+    // lane (rc, q) writes output row c0 + rc, columns r0 + 16q ..: for a fixed
+    // k the 64 lanes read banks (16q + rc) mod 64 of the padded tile
+#pragma unroll
+    for (int k = 0; k < 16; ++k) v[k >> 3][k & 7] = tile[q * 16 + k][rc];
+    T* op = o + (int64_t)(c0 + rc) * d.rows + r0 + q * 16;
+    store8(op, v[0]);
+    store8(op + 8, v[1]);
+    return;
+  }
   for (int i = threadIdx.x; i < 64 * 64; i += 256) {
     const int r = i / 64, c = i % 64;
     if (r0 + r < d.rows && c0 + c < d.cols) tile[r][c] = to_f32(s[(int64_t)(r0 + r) * d.cols + c0 + c]);
