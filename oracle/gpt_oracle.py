@@ -518,10 +518,13 @@ def backward(cfg: dict, params: dict, idx: np.ndarray, targets: np.ndarray, cach
     return G
 
 
-def step(cfg: dict, params: dict, idx: np.ndarray, targets: np.ndarray, dloss: float = 1.0):
-    """One forward + backward. Returns (loss, row_loss [B, T], grads dict)."""
-    loss, row_loss, cache = forward(cfg, params, idx, targets)
-    grads = backward(cfg, params, idx, targets, cache, dloss)
+def step(cfg: dict, params: dict, idx: np.ndarray, targets: np.ndarray, dloss: float = 1.0,
+         row_chunk: int = 4096):
+    """One forward + backward. Returns (loss, row_loss [B, T], grads dict).
+    `row_chunk` bounds the rows of the LM head and cross-entropy held at once;
+    it changes memory use only, not what is computed."""
+    loss, row_loss, cache = forward(cfg, params, idx, targets, row_chunk)
+    grads = backward(cfg, params, idx, targets, cache, dloss, row_chunk)
     return loss, row_loss, grads
 
 

@@ -385,6 +385,26 @@ def test_whole_step_matches_torch_autograd_float64(H):
         np.testing.assert_allclose(G[k], TG[k], rtol=1e-9, atol=1e-13, err_msg=k)
 
 
+def test_lm_head_row_chunks_match_torch_autograd():
+    """The LM head and cross-entropy run over row chunks (to bound memory at
+    d12/d20). With chunks of 5 rows over N = 42 positions (eight whole chunks
+    and a ragged one), the loss and every gradient still equal the independent
+    torch-autograd step's: a chunk that read another chunk's log-sum-exp,
+    targets or rows would fail here."""
+    pytest.importorskip("torch")
+    cfg = tiny_cfg(n_layer=1, vocab_size=96)
+    P = rand_params(cfg, seed=23, std=0.1)
+    rng = np.random.default_rng(24)
+    idx = rng.integers(0, 96, (2, 21))
+    tg = rng.integers(0, 96, (2, 21))
+    tl, TG = _torch_step(cfg, P, idx, tg)
+    for chunk in (5, 7, 41):
+        loss, _, G = O.step(cfg, P, idx, tg, row_chunk=chunk)
+        assert loss == pytest.approx(tl, rel=1e-13), chunk
+        for k in G:
+            np.testing.assert_allclose(G[k], TG[k], rtol=1e-9, atol=1e-13, err_msg=f"{k} chunk {chunk}")
+
+
 def test_causality_and_row_independence():
     cfg = tiny_cfg(n_layer=1, vocab_size=128)
     P = rand_params(cfg, seed=19, std=0.1)
@@ -778,6 +798,78 @@ def test_newton_schulz_reaches_the_polar_factor():
     # a few steps only approach it, monotonically in the singular values
     s5 = np.linalg.svd(O.newton_schulz(M, 5), compute_uv=False)
     assert np.all(s5 < 1.0 + 1e-12) and np.all(s5 > 0.2)
+
+
+def _with_singular_values(rng, rows, cols, s):
+    """A rows x cols matrix U diag(s) V^T with random orthonormal U, V."""
+    r = min(rows, cols)
+    U_, _ = np.linalg.qr(rng.standard_normal((rows, r)))
+    V_, _ = np.linalg.qr(rng.standard_normal((cols, r)))
+    return U_, V_, U_ @ np.diag(s) @ V_.T
+
+
+def test_newton_schulz_one_step_closed_form_and_quintic_convergence():
+    """One step X <- a X + (b A + c A^2) X with A = X X^T keeps the singular
+    vectors of X0 = M / (||M||_F + 1e-7) and maps each singular value s to
+    a s + b s^3 + c s^5 (A has eigenvalues s^2, A^2 has s^4), in both
+    orientations: a wrong power in the c term or a dropped term fails here.
+    The quintic coefficients (1.875, -1.25, 0.375) (p(1) = 1, p'(1) = p''(1) = 0)
+    also converge to the polar factor U V^T of the SVD."""
+    rng = np.random.default_rng(63)
+    s = np.linspace(0.5, 4.0, 9)
+    U_, V_, M = _with_singular_values(rng, 9, 25, s)
+    s0 = s / (np.linalg.norm(M) + 1e-7)
+    for a, b, c in [(1.875, -1.25, 0.375), (2.0, -1.5, 0.5), (0.0, 0.0, 1.0), (0.0, 1.0, 0.0)]:
+        want = U_ @ np.diag(a * s0 + b * s0 ** 3 + c * s0 ** 5) @ V_.T
+        np.testing.assert_allclose(O.newton_schulz(M, 1, a, b, c), want, atol=1e-14)
+        np.testing.assert_allclose(O.newton_schulz(M.T, 1, a, b, c), want.T, atol=1e-14)
+    # two steps compose the scalar map
+    p = lambda x: 1.875 * x - 1.25 * x ** 3 + 0.375 * x ** 5  # noqa: E731
+    np.testing.assert_allclose(O.newton_schulz(M, 2, 1.875, -1.25, 0.375), U_ @ np.diag(p(p(s0))) @ V_.T,
+                               atol=1e-14)
+    X = O.newton_schulz(M, 40, 1.875, -1.25, 0.375)
+    np.testing.assert_allclose(X, U_ @ V_.T, atol=1e-10)
+
+
+def test_optimizer_step_gives_each_group_its_own_learning_rate():
+    """A first step with four distinct learning rates: every AdamW-group tensor
+    equals torch.optim.AdamW run with its own group's rate (embeddings incl.
+    value-embedding tables, unembedding, scalars), and every block matrix the
+    converged Muon step w (1 - lr wd) - lr sqrt(max(1, rows/cols)) U V^T of its
+    gradient (the momentum buffer is the gradient on the first step). Swapping
+    any two groups' rates, or sending a tensor to the wrong group, fails here."""
+    torch = pytest.importorskip("torch")
+    cfg = tiny_cfg(n_layer=2, vocab_size=64, x0_lambdas=True, value_embeds=True)
+    oc = dict(lr_embed=0.3, lr_unembed=0.004, lr_scalar=0.05, lr_muon=0.02, momentum=0.9,
+              beta1=0.8, beta2=0.95, eps=1e-10, wd_muon=0.1, wd_adamw=0.01, ns_steps=60)
+    rng = np.random.default_rng(64)
+    master = {n: rng.standard_normal((r, c)) * 0.02 for n, r, c in O.param_shapes(cfg)}
+    grads, polar = {}, {}
+    for n, r, c in O.param_shapes(cfg):
+        if O.optimizer_group(n) == "muon":
+            U_, V_, grads[n] = _with_singular_values(rng, r, c, np.linspace(1.0, 3.0, min(r, c)))
+            polar[n] = U_ @ V_.T
+        else:
+            grads[n] = rng.standard_normal((r, c))
+    new_w, new_s = O.optimizer_step(cfg, oc, master, grads, {}, 1)
+    lr = dict(embed=oc["lr_embed"], unembed=oc["lr_unembed"], scalar=oc["lr_scalar"])
+    seen = set()
+    for n, w in master.items():
+        grp = O.optimizer_group(n)
+        seen.add(grp)
+        if grp == "muon":
+            scale = math.sqrt(max(1.0, w.shape[0] / w.shape[1]))
+            want = w * (1 - oc["lr_muon"] * oc["wd_muon"]) - oc["lr_muon"] * scale * polar[n]
+            np.testing.assert_allclose(new_w[n], want, rtol=0, atol=1e-11, err_msg=n)
+            np.testing.assert_array_equal(new_s[n]["u"], grads[n])
+        else:
+            p = torch.tensor(w, requires_grad=True)
+            opt = torch.optim.AdamW([p], lr=lr[grp], betas=(oc["beta1"], oc["beta2"]), eps=oc["eps"],
+                                    weight_decay=oc["wd_adamw"])
+            p.grad = torch.tensor(grads[n])
+            opt.step()
+            np.testing.assert_allclose(new_w[n], p.detach().numpy(), rtol=1e-13, atol=1e-15, err_msg=n)
+    assert seen == {"muon", "embed", "unembed", "scalar"}
 
 
 def test_muon_step_momentum_and_scale():
