@@ -112,6 +112,69 @@ def kernel_bytes_per_launch(tag: str, cfg, B: int, T: int, es: int) -> float | N
     return b.get(tag)
 
 
+def environment(torch) -> dict:
+    """GPU name and architecture, HIP/ROCm versions, engine clock, measured
+    device copy bandwidth and the host CPU model."""
+    import glob
+    import subprocess
+    props = torch.cuda.get_device_properties(0)
+    env = {"gpu": props.name, "arch": getattr(props, "gcnArchName", ""), "cus": props.multi_processor_count,
+           "hbm_gib": round(props.total_memory / 2**30, 1), "hip": torch.version.hip, "torch": torch.__version__}
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            env["rocm"] = f.read().strip()
+    except OSError:
+        env["rocm"] = None
+    sclk = None
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
+        d = json.loads(r.stdout[r.stdout.index("{"):]) if "{" in r.stdout else {}
+        for card in d.values():
+            if isinstance(card, dict):
+                for k, v in card.items():
+                    if "sclk" in k.lower():
+                        sclk = v
+                        break
+            if sclk:
+                break
+    except Exception:
+        pass
+    if sclk is None:
+        for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+            try:
+                with open(path) as f:
+                    lines = f.read().split("\n")
+                sclk = next((ln.split(":", 1)[1].replace("*", "").strip() for ln in lines if ln.endswith("*")), None)
+                if sclk:
+                    break
+            except OSError:
+                pass
+    env["sclk"] = sclk
+    # device copy bandwidth: 1 GiB read + 1 GiB written, best of 6 copies, HIP events
+    n = 1 << 28
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    best = float("inf")
+    for _ in range(6):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        e1.synchronize()
+        best = min(best, e0.elapsed_time(e1))
+    env["copy_gbs"] = round(2 * 4 * n / (best * 1e-3) / 1e9, 1)
+    del src, dst
+    cpu = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+    except OSError:
+        pass
+    env["cpu"] = cpu
+    env["host_cores"] = len(os.sched_getaffinity(0))
+    return env
+
+
 def cpu_baseline(cfg_lib, seconds_hint: float = 20.0) -> dict:
     """The float64 oracle, as it stands, on a bounded sample of the workload."""
     import numpy as np
@@ -226,16 +289,21 @@ def main():
             print(f"[bench] {t:24s} {ms:9.3f} ms {n:4d} launches {100 * ms / tot:5.1f}% {rate}",
                   file=sys.stderr, flush=True)
 
-    # timed region: K steps, the dominant kernel's launches timed with HIP events on its stream
+    # timed region: K steps, the dominant kernel's launches timed with HIP events
+    # on its stream, and every step bracketed by HIP events on the same stream
     dom_tag = tags.index(dominant)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     _lib.gpt_profile_begin(m.h, dom_tag)
-    for _ in range(args.steps):
+    evs[0].record()
+    for i in range(args.steps):
         step()
+        evs[i + 1].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     dom_ms, dom_n = _lib.gpt_profile_end(m.h)
+    step_ms = [evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]
     if m.sync_status() != _lib.GPT_OK:
         raise RuntimeError("device flag raised")
     loss = float(m.loss.item())
@@ -279,6 +347,9 @@ def main():
                    "global_batch": B, "seq_len": T, "tokens": wl.tokens, "parallelism": "single GPU"},
         "mfu_bf16": round(mfu, 4), "mfu_palm_convention": round(fl["palm"] * tok_s / (PEAK_BF16_TFLOPS * 1e12), 4),
         "loss": round(loss, 5), "roofline": roof,
+        "step_ms_events": {"median": round(float(np.median(step_ms)), 3), "mean": round(float(np.mean(step_ms)), 3),
+                           "min": round(min(step_ms), 3), "max": round(max(step_ms), 3)},
+        "env": environment(torch),
     }
     if args.optimizer:
         oc = _lib.gpt_optim_config()

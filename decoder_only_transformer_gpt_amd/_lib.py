@@ -24,6 +24,7 @@ GPT_F32 = 0
 GPT_BF16 = 1
 GPT_FP8_E4M3 = 2
 GPT_OPT_GEMM_TILE = 1
+GPT_OPT_DKV_HSPLIT = 2
 
 
 class gpt_config(ctypes.Structure):

@@ -1223,7 +1223,10 @@ hipError_t bwd_typed(const AttnBwdArgs& a, int stage, hipStream_t s) {
       // up unevenly), split each key block over two head halves (dK/dV
       // partials added by the combine kernel)
       const int nkb = (T_ + 127) / 128;
-      const int hsplit = (a.dkv_part && H % 2 == 0 && ((int64_t)nkb * B < 512 || W > 0)) ? 2 : 1;
+      const bool can2 = a.dkv_part && H % 2 == 0;
+      const int hsplit = a.hsplit == 1 ? 1
+                         : a.hsplit == 2 ? (can2 ? 2 : 1)
+                                         : (can2 && ((int64_t)nkb * B < 512 || W > 0)) ? 2 : 1;
       hipLaunchKernelGGL(attn_dkv_bf16_kernel, dim3(nkb * B * hsplit), dim3(256), 0, s, (const bf16*)a.qkv,
                          (const bf16*)a.dout, a.lse, a.delta, T_, H, W, hsplit, (bf16*)a.dqkv, a.dkv_part);
       if (hsplit == 1) return hipGetLastError();

@@ -313,6 +313,7 @@ struct gpt_model {
   std::vector<int64_t> off_ve;                      // per layer, -1 without a value embedding
   int64_t off_resid = -1, off_x0lam = -1, off_gates = -1;
   int gemm_tile = 0;      // GPT_OPT_GEMM_TILE
+  int dkv_hsplit = 0;     // GPT_OPT_DKV_HSPLIT
   int ntdesc = 0;
   int64_t wt_tiles = 0;   // total 64x64 tiles of the batched weight transpose
   int nqdesc = 0;                         // FP8: layer-weight quantisation table
@@ -953,6 +954,7 @@ gpt_status gpt_backward(gpt_model* m, float dloss, int32_t accumulate, void* str
     ab.doT = m->ws + L.doT;
     ab.dqkv = m->ws + L.dqkv;
     ab.dkv_part = wsp<float>(m, L.dkv_part);
+    ab.hsplit = m->dkv_hsplit;
     // fp32: transposed copies and delta (the bf16 dQ kernel forms delta itself)
     if (dt == GPT_F32) RUN(K_ATTN_BWD_PREP, return gk::launch_attn_bwd(dt, ab, 0, stream););
     RUN(K_ATTN_BWD_DQ, return gk::launch_attn_bwd(dt, ab, 1, stream););
@@ -1057,6 +1059,10 @@ gpt_status gpt_set_option(gpt_model* m, int32_t option, int32_t value) {
     case GPT_OPT_GEMM_TILE:
       if (value < 0 || value > 3) return fail(GPT_E_INVALID_ARG, "GEMM tile option %d not in 0..3", value);
       m->gemm_tile = value;
+      return GPT_OK;
+    case GPT_OPT_DKV_HSPLIT:
+      if (value < 0 || value > 2) return fail(GPT_E_INVALID_ARG, "dK/dV head-split option %d not in 0..2", value);
+      m->dkv_hsplit = value;
       return GPT_OK;
     default:
       return fail(GPT_E_INVALID_ARG, "unknown option %d", option);

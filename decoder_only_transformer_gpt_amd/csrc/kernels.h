@@ -95,6 +95,7 @@ struct AttnBwdArgs {
   void* doT;         // [B, H, 128, Tp] scratch
   void* dqkv;        // [N, (H+2)*128] output
   float* dkv_part;   // [2, N, 256] fp32 scratch (bf16 dK/dV split over two head halves), or null
+  int hsplit = 0;    // bf16 dK/dV: 0 picks by grid size, 1 or 2 forces that many head groups per key block
 };
 // Stage 0: transposed copies + delta; stage 1: dQ; stage 2: dK and dV.
 hipError_t launch_attn_bwd(int dtype, const AttnBwdArgs& a, int stage, hipStream_t s);

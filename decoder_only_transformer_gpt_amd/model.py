@@ -65,6 +65,9 @@ class GPT:
     def set_gemm_tile(self, tile: int):
         _lib.gpt_set_option(self.h, _lib.GPT_OPT_GEMM_TILE, tile)
 
+    def set_dkv_hsplit(self, hsplit: int):
+        _lib.gpt_set_option(self.h, _lib.GPT_OPT_DKV_HSPLIT, hsplit)
+
     def close(self):
         if self.h is not None:
             _lib.gpt_destroy(self.h)

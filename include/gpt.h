@@ -202,8 +202,16 @@ gpt_status gpt_profile_end(gpt_model* m, double* total_ms, int64_t* launches);
  * 1..3 force one tile variant for every GEMM, largest first (bf16
  * k-contiguous GEMMs: 256x256, 256x128 with two workgroups per CU, 128x128;
  * others: 256x256, 128x128, 64x64). Results are the same up to rounding
- * order; the option exists to measure and test every variant. */
-enum { GPT_OPT_GEMM_TILE = 1 };
+ * order; the option exists to measure and test every variant.
+ * GPT_OPT_DKV_HSPLIT: bf16 attention backward, dK/dV kernel. 0 (default)
+ * picks by grid size: each 128-key block of a batch row sums dK and dV over
+ * all H query heads in one workgroup (1), or, when that grid would give
+ * fewer than two rounds of workgroups per compute unit or the layer has a
+ * sliding window, over two workgroups of H/2 heads each whose fp32 partial
+ * rows a combine kernel adds in order (2). 1 or 2 force that form (2 needs
+ * an even H, else 1 is used). Same result up to rounding order; the option
+ * exists to test both forms at any size. */
+enum { GPT_OPT_GEMM_TILE = 1, GPT_OPT_DKV_HSPLIT = 2 };
 gpt_status gpt_set_option(gpt_model* m, int32_t option, int32_t value);
 
 /* Name of a kernel tag (NULL past the last tag); tags run 0..n-1. */
