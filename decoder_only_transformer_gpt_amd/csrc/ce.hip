@@ -3,7 +3,7 @@
 // The LM head GEMM epilogue has already squashed the logits to
 // z' = c * tanh(z / c) (c = 15, in fp32; aethryn.com "Nanochat: full-stack LLM
 // training in 8,000 lines for $72", section "A Llama-class transformer with
-// ten modern departures") and emitted, per row and 128 columns, the partial
+// ten modern departures") and emitted, per row and 64 columns, the partial
 // sums of exp(z' - c). Because |z'| < c every term lies in (e^-2c, 1], so the
 // log-sum-exp is c + log(sum of partials) with no running maximum.
 //
@@ -38,8 +38,25 @@ __global__ __launch_bounds__(256) void ce_rows_kernel(const float* __restrict__ 
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= N) return;
   const float* p = part + (int64_t)row * nparts;
+  // 16-byte loads, four per lane in flight per round (nparts = V / 64 is a
+  // multiple of 4), then a fixed butterfly over the lanes
   float s = 0.f;
-  for (int i = lane; i < nparts; i += 64) s += p[i];
+  if ((nparts & 3) == 0) {
+    const int n4 = nparts >> 2;
+    int i = lane;
+    for (; i + 192 < n4; i += 256) {
+      f32x4 a = *reinterpret_cast<const f32x4*>(p + 4 * i), b = *reinterpret_cast<const f32x4*>(p + 4 * (i + 64));
+      f32x4 c2 = *reinterpret_cast<const f32x4*>(p + 4 * (i + 128)), d = *reinterpret_cast<const f32x4*>(p + 4 * (i + 192));
+      s += ((a[0] + a[1]) + (a[2] + a[3])) + ((b[0] + b[1]) + (b[2] + b[3])) + ((c2[0] + c2[1]) + (c2[2] + c2[3])) +
+           ((d[0] + d[1]) + (d[2] + d[3]));
+    }
+    for (; i < n4; i += 64) {
+      f32x4 a = *reinterpret_cast<const f32x4*>(p + 4 * i);
+      s += (a[0] + a[1]) + (a[2] + a[3]);
+    }
+  } else {
+    for (int i = lane; i < nparts; i += 64) s += p[i];
+  }
   s = wave_sum(s);
   if (lane == 0) {
     const float l = c + logf(s);
@@ -57,11 +74,24 @@ __global__ __launch_bounds__(256) void ce_rows_kernel(const float* __restrict__ 
   }
 }
 
-// Single block: mean of N row losses in a fixed order.
+// Single block: mean of N row losses in a fixed order (16-byte loads, four
+// in flight per thread).
 __global__ __launch_bounds__(1024) void mean_kernel(const float* __restrict__ x, int N, float* __restrict__ out) {
   __shared__ float red[16];
   float s = 0.f;
-  for (int i = threadIdx.x; i < N; i += 1024) s += x[i];
+  const int n4 = N >> 2;
+  int i = threadIdx.x;
+  for (; i + 3072 < n4; i += 4096) {
+    const f32x4 a = reinterpret_cast<const f32x4*>(x)[i], b = reinterpret_cast<const f32x4*>(x)[i + 1024];
+    const f32x4 c = reinterpret_cast<const f32x4*>(x)[i + 2048], d = reinterpret_cast<const f32x4*>(x)[i + 3072];
+    s += ((a[0] + a[1]) + (a[2] + a[3])) + ((b[0] + b[1]) + (b[2] + b[3])) + ((c[0] + c[1]) + (c[2] + c[3])) +
+         ((d[0] + d[1]) + (d[2] + d[3]));
+  }
+  for (; i < n4; i += 1024) {
+    const f32x4 a = reinterpret_cast<const f32x4*>(x)[i];
+    s += (a[0] + a[1]) + (a[2] + a[3]);
+  }
+  for (int j = 4 * n4 + (int)threadIdx.x; j < N; j += 1024) s += x[j];
   s = wave_sum(s);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
   __syncthreads();

@@ -90,6 +90,26 @@ DEV void store4(float* p, const float (&v)[4]) {
   st16(p, r);
 }
 
+// Non-temporal (streaming) variants: for outputs and operands touched once,
+// so that they do not evict data other workgroups still reuse from the L2
+// (the GEMM operand panels).
+DEV void st8_nt(void* p, u32x2 v) { __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(p)); }
+DEV void st16_nt(void* p, u32x4 v) { __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p)); }
+DEV u32x2 ld8_nt(const void* p) { return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p)); }
+DEV u32x4 ld16_nt(const void* p) { return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)); }
+DEV void store4_nt(bf16* p, const float (&v)[4]) {
+  u32x2 r; r[0] = pack_bf16x2(v[0], v[1]); r[1] = pack_bf16x2(v[2], v[3]);
+  st8_nt(p, r);
+}
+DEV void store4_nt(float* p, const float (&v)[4]) {
+  u32x4 r; for (int i = 0; i < 4; ++i) r[i] = __float_as_uint(v[i]);
+  st16_nt(p, r);
+}
+DEV void load4_nt(const float* p, float (&v)[4]) {
+  u32x4 r = ld16_nt(p);
+  for (int i = 0; i < 4; ++i) v[i] = __uint_as_float(r[i]);
+}
+
 // ---------------------------------------------------------- reductions -----
 
 DEV float wave_sum(float v) {

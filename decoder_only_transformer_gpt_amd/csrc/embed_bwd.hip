@@ -5,15 +5,20 @@
 //
 // With y = wte[v] * r_n the norm backward is r_n * dres_n - wte[v] * k_n where
 // k_n = r_n^3 / C * <dres_n, wte[v]>, so
-//   dwte[v] += sum_n r_n * dres_n  -  wte[v] * sum_n k_n.
+//   dwte[v] += sum_n r_n * dres_n  -  wte[v] * sum_n k_n,
+// and by linearity sum_n k_n = <sum_n (r_n^3 / C) dres_n, wte[v]>: one pass
+// over the gradient rows accumulates two C-vectors per id, and one dot
+// product per id (or per part of an id's run) gives the k sum.
 //
 // Token ids follow a skewed (Zipf-like) law, so a scatter with float atomics
 // would serialise on the frequent rows and make the result depend on timing.
-// Instead: (1) per-token k_n, (2) a stable LSD radix sort of the ids
-// (2 passes of 8 bits, V <= 65536) carrying the token index, (3) segment sums
-// over fixed chunks of the sorted list, where runs that cross a chunk boundary
-// leave partial rows that (4) one block per crossing segment adds up in chunk
-// order. Every sum has a fixed order, so the result is bitwise reproducible.
+// Instead: (1) a stable LSD radix sort of the ids (2 passes of 8 bits,
+// V <= 65536) carrying the token index; (2) one wave per chunk of 32 sorted
+// entries sums each run of equal ids over whole rows, finishing runs that
+// lie inside the chunk and leaving a partial row plus its k sum for the two
+// runs that cross the chunk's edges; (3) one wave per (chunk where a crossing
+// run starts, 512 columns) adds those partials in chunk order. Every sum has a
+// fixed order, so the result is bitwise reproducible.
 
 #include "common.h"
 #include "kernels.h"
@@ -36,34 +41,6 @@ __global__ __launch_bounds__(256) void sort_init_kernel(const int32_t* __restric
   vals[n] = ok ? n : -1 - n;
 }
 
-template <typename T>
-__global__ __launch_bounds__(256) void embed_coef_kernel(const T* __restrict__ wte, const int32_t* __restrict__ idx,
-                                                         const float* __restrict__ dres,
-                                                         const float* __restrict__ rstd0, int N, int C, int V,
-                                                         float* __restrict__ coef) {
-  const int lane = threadIdx.x & 63;
-  const int n = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (n >= N) return;
-  const int id = idx[n];
-  const bool ok = (unsigned)id < (unsigned)V;
-  const T* w = wte + (int64_t)(ok ? id : 0) * C;
-  const float* g = dres + (int64_t)n * C;
-  float dot = 0.f;
-  for (int ch = lane; ch < (C >> 3); ch += 64) {
-    float a[8], b[8];
-    load8(w + ch * 8, a);
-    load8(g + ch * 8, b);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) dot += a[e] * b[e];
-  }
-  dot = wave_sum(dot);
-  if (lane == 0) {
-    const float r = rstd0[n];
-    // An invalid id (the forward already raised the device flag) contributes nothing.
-    coef[n] = ok ? r * r * r * dot / (float)C : 0.f;
-  }
-}
-
 // Per-chunk digit histogram, stored digit-major: hist[d * nchunks + chunk].
 __global__ __launch_bounds__(kSortChunk) void radix_hist_kernel(const int32_t* __restrict__ keys, int N, int shift,
                                                                 int nchunks, int32_t* __restrict__ hist) {
@@ -76,36 +53,57 @@ __global__ __launch_bounds__(kSortChunk) void radix_hist_kernel(const int32_t* _
   hist[threadIdx.x * nchunks + blockIdx.x] = cnt[threadIdx.x];
 }
 
-// Exclusive scan of n ints in place, one block of 1024 threads.
-__global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ a, int n) {
-  __shared__ int part[1024];
-  const int per = (n + 1023) / 1024;
-  const int beg = min(n, threadIdx.x * per), end = min(n, beg + per);
-  int s = 0;
-  for (int i = beg; i < end; ++i) s += a[i];
-  part[threadIdx.x] = s;
+// Block-wide inclusive scan of one int per thread (256 threads).
+DEV int block_scan256(int v, int* sh) {
+  sh[threadIdx.x] = v;
   __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {  // Hillis-Steele inclusive scan
-    int v = threadIdx.x >= o ? part[threadIdx.x - o] : 0;
+  for (int o = 1; o < 256; o <<= 1) {  // Hillis-Steele
+    const int u = threadIdx.x >= o ? sh[threadIdx.x - o] : 0;
     __syncthreads();
-    part[threadIdx.x] += v;
+    sh[threadIdx.x] += u;
     __syncthreads();
   }
-  int run = threadIdx.x ? part[threadIdx.x - 1] : 0;
-  for (int i = beg; i < end; ++i) {
-    const int v = a[i];
-    a[i] = run;
-    run += v;
-  }
+  return sh[threadIdx.x];
 }
 
-// Stable scatter: rank within the chunk among equal digits = earlier equal items.
+// One block per digit d: exclusive scan of the digit's per-chunk counts
+// hist[d * nchunks + c] in place, and the digit's total count.
+__global__ __launch_bounds__(256) void digit_scan_kernel(int32_t* __restrict__ hist, int nchunks,
+                                                         int32_t* __restrict__ total) {
+  __shared__ int sh[256];
+  int32_t* h = hist + (int64_t)blockIdx.x * nchunks;
+  const int per = (nchunks + 255) / 256;
+  const int beg = min(nchunks, (int)threadIdx.x * per), end = min(nchunks, beg + per);
+  int s = 0;
+  for (int i = beg; i < end; ++i) s += h[i];
+  const int incl = block_scan256(s, sh);
+  int run = incl - s;
+  for (int i = beg; i < end; ++i) {
+    const int v = h[i];
+    h[i] = run;
+    run += v;
+  }
+  if (threadIdx.x == 255) total[blockIdx.x] = incl;
+}
+
+// Stable scatter: position = start of the digit (exclusive scan of the digit
+// totals) + the chunk's offset within the digit + the rank within the chunk
+// among equal digits (earlier equal items).
 __global__ __launch_bounds__(kSortChunk) void radix_scatter_kernel(const int32_t* __restrict__ kin,
                                                                    const int32_t* __restrict__ vin, int N, int shift,
                                                                    int nchunks, const int32_t* __restrict__ hist,
+                                                                   const int32_t* __restrict__ total,
                                                                    int32_t* __restrict__ kout,
                                                                    int32_t* __restrict__ vout) {
+  static_assert(kSortChunk == 256, "one thread per digit");
   __shared__ int dig[kSortChunk];
+  __shared__ int base[256];
+  {
+    const int t = total[threadIdx.x];
+    const int incl = block_scan256(t, base);
+    __syncthreads();
+    base[threadIdx.x] = incl - t;
+  }
   const int i = blockIdx.x * kSortChunk + threadIdx.x;
   const bool valid = i < N;
   const int key = valid ? kin[i] : 0;
@@ -115,55 +113,124 @@ __global__ __launch_bounds__(kSortChunk) void radix_scatter_kernel(const int32_t
   if (!valid) return;
   int rank = 0;
   for (int j = 0; j < (int)threadIdx.x; ++j) rank += (dig[j] == d);
-  const int pos = hist[d * nchunks + blockIdx.x] + rank;
+  const int pos = base[d] + hist[d * nchunks + blockIdx.x] + rank;
   kout[pos] = key;
   vout[pos] = vin[i];
 }
 
-// Segment sums over chunks of kSegChunk sorted entries. Complete runs are
-// added to dwte directly; a run cut by a chunk boundary leaves a partial row
-// (C values + the k sum) in carry slot 0 (run began before this chunk) or 1
-// (run begins in this chunk and continues after it).
-__global__ __launch_bounds__(256) void seg_partial_kernel(const int32_t* __restrict__ keys,
-                                                          const int32_t* __restrict__ vals,
-                                                          const float* __restrict__ dres,
-                                                          const float* __restrict__ rstd0,
-                                                          const float* __restrict__ coef, const void* wte_raw,
-                                                          int wte_bf16, int N, int C, float* __restrict__ dwte,
-                                                          float* __restrict__ carry) {
-  const int c = blockIdx.x;
-  const int e0 = c * kSegChunk, e1 = min(N, e0 + kSegChunk);
-  for (int col0 = 0; col0 < C; col0 += 256) {
-    const int col = col0 + threadIdx.x;
-    const bool cv = col < C;
-    float acc = 0.f, ks = 0.f;
-    int rs = e0;  // run start
-    for (int e = e0; e < e1; ++e) {
-      const int v = keys[e];
-      const int n = vals[e];
-      if (n >= 0) {
-        if (cv) acc += rstd0[n] * dres[(int64_t)n * C + col];
-        ks += coef[n];
-      }
-      const bool run_end = (e + 1 == e1) || keys[e + 1] != v;
-      if (!run_end) continue;
-      const bool seg_start = (rs == 0) || keys[rs - 1] != v;
-      const bool seg_end = (e + 1 == N) || keys[e + 1] != v;
-      if (seg_start && seg_end) {
-        if (cv) {
-          const float w = wte_bf16 ? (float)((const bf16*)wte_raw)[(int64_t)v * C + col]
-                                   : ((const float*)wte_raw)[(int64_t)v * C + col];
-          dwte[(int64_t)v * C + col] += acc - w * ks;
+// 8 consecutive fp32 values of a gradient row / bf16 or fp32 embedding row.
+DEV void ld8f(const float* p, float (&v)[8]) { load8(p, v); }
+template <typename T>
+DEV void ld8w(const T* p, float (&v)[8]) { load8(p, v); }
+
+// One wave per chunk of kSegChunk sorted entries; lane l holds columns
+// j * 512 + 8l .. +8 of every row (J = ceil(C / 512) groups). For each run of
+// equal ids in the chunk the wave accumulates a1 = sum r_n dres_n and
+// a2 = sum (r_n^3 / C) dres_n, the next entry's row in flight while the
+// current one is added. At a run's end, ks = <a2, wte[v]> (a wave
+// reduction); a run that starts and ends inside the chunk adds
+// a1 - wte[v] * ks to dwte[v]; a run cut by the chunk's first (last) edge
+// stores a1 and ks in carry slot 0 (1) of the chunk instead (slots of C + 8
+// floats: the row, then ks).
+template <typename T, int J>
+__global__ __launch_bounds__(256) void embed_seg_kernel(const int32_t* __restrict__ keys,
+                                                        const int32_t* __restrict__ vals,
+                                                        const float* __restrict__ dres,
+                                                        const float* __restrict__ rstd0, const T* __restrict__ wte,
+                                                        int N, int C, float* __restrict__ dwte,
+                                                        float* __restrict__ carry) {
+  static_assert(kSegChunk <= 64, "one entry per lane");
+  const int lane = threadIdx.x & 63;
+  const int c = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int nseg = (N + kSegChunk - 1) / kSegChunk;
+  if (c >= nseg) return;
+  const int e0 = c * kSegChunk, e1 = min(N, e0 + kSegChunk), ne = e1 - e0;
+  // the chunk's entries, one per lane, and the ids just outside it
+  const int me = e0 + (lane < ne ? lane : 0);
+  const int key_l = keys[me];
+  const int val_l = vals[me];
+  const float r_l = val_l >= 0 ? rstd0[val_l] : 0.f;
+  const int prev_key = e0 > 0 ? keys[e0 - 1] : -1;
+  const int next_key = e1 < N ? keys[e1] : -1;
+  const float invC = 1.f / (float)C;
+  int col[J];
+  bool cv[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    col[j] = j * 512 + lane * 8;
+    cv[j] = col[j] < C;
+  }
+  float a1[J][8], a2[J][8], cur[J][8], nxt[J][8];
+  auto load_row = [&](float (&dst)[J][8], int n) {
+    const float* row = dres + (int64_t)(n < 0 ? 0 : n) * C;
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+      if (cv[j]) ld8f(row + col[j], dst[j]);
+  };
+#pragma unroll
+  for (int j = 0; j < J; ++j)
+#pragma unroll
+    for (int q = 0; q < 8; ++q) a1[j][q] = a2[j][q] = 0.f;
+  load_row(cur, __builtin_amdgcn_readlane(val_l, 0));
+  int rs = 0;  // run start (entry index within the chunk)
+  for (int e = 0; e < ne; ++e) {
+    const int v = __builtin_amdgcn_readlane(key_l, e);
+    const int n = __builtin_amdgcn_readlane(val_l, e);
+    const float r = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, r_l), e));
+    if (e + 1 < ne) load_row(nxt, __builtin_amdgcn_readlane(val_l, e + 1));
+    if (n >= 0) {  // an invalid id (the forward raised the device flag) adds nothing
+      const float r3 = r * r * r * invC;
+#pragma unroll
+      for (int j = 0; j < J; ++j)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          a1[j][q] = fmaf(r, cur[j][q], a1[j][q]);
+          a2[j][q] = fmaf(r3, cur[j][q], a2[j][q]);
         }
+    }
+    const int vn = e + 1 < ne ? __builtin_amdgcn_readlane(key_l, e + 1) : next_key;
+    if (vn != v || e + 1 == ne) {
+      // end of a run inside this chunk (it may continue in the next chunk)
+      const bool starts_here = rs > 0 || prev_key != v;
+      const bool ends_here = vn != v;
+      float w[J][8];
+      float dot = 0.f;
+#pragma unroll
+      for (int j = 0; j < J; ++j)
+        if (cv[j]) {
+          ld8w(wte + (int64_t)v * C + col[j], w[j]);
+#pragma unroll
+          for (int q = 0; q < 8; ++q) dot = fmaf(a2[j][q], w[j][q], dot);
+        }
+      const float ks = wave_sum(dot);
+      if (starts_here && ends_here) {
+        float* drow = dwte + (int64_t)v * C;
+#pragma unroll
+        for (int j = 0; j < J; ++j)
+          if (cv[j]) {
+            float o[8];
+            ld8f(drow + col[j], o);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) o[q] += a1[j][q] - w[j][q] * ks;
+            store8(drow + col[j], o);
+          }
       } else {
-        float* slot = carry + ((int64_t)c * 2 + (seg_start ? 1 : 0)) * (C + 1);
-        if (cv) slot[col] = acc;
-        if (threadIdx.x == 0) slot[C] = ks;
+        float* slot = carry + ((int64_t)c * 2 + (starts_here ? 1 : 0)) * (C + 8);
+#pragma unroll
+        for (int j = 0; j < J; ++j)
+          if (cv[j]) store8(slot + col[j], a1[j]);
+        if (lane == 0) slot[C] = ks;
       }
-      acc = 0.f;
-      ks = 0.f;
+#pragma unroll
+      for (int j = 0; j < J; ++j)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) a1[j][q] = a2[j][q] = 0.f;
       rs = e + 1;
     }
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) cur[j][q] = nxt[j][q];
   }
 }
 
@@ -179,42 +246,61 @@ DEV int segment_last(const int32_t* __restrict__ keys, int N, int from, int v) {
   return lo;
 }
 
-// One block per chunk in which a boundary-crossing segment starts: adds the
-// partials of that segment in chunk order and finalises its row. The chunk
-// holding the segment's last entry is found first (binary search), so the
-// partial rows are summed over a known range with many loads in flight.
+// One wave per (chunk in which a boundary-crossing run starts, 512 columns):
+// adds that run's partial rows (slot 1 of its first chunk, then slot 0 of
+// every later chunk it reaches, in chunk order) and their k sums, and adds
+// a1 - wte[v] * ks to dwte[v]. The chunk holding the run's last entry is found
+// by a binary search, so the partials are summed over a known range with
+// many loads in flight.
+template <typename T>
 __global__ __launch_bounds__(256) void seg_fixup_kernel(const int32_t* __restrict__ keys, int N, int C, int nchunks,
-                                                        const void* wte_raw, int wte_bf16,
-                                                        const float* __restrict__ carry, float* __restrict__ dwte) {
-  const int c = blockIdx.x;
+                                                        const T* __restrict__ wte, const float* __restrict__ carry,
+                                                        float* __restrict__ dwte) {
+  const int lane = threadIdx.x & 63;
+  const int ngrp = (C + 511) / 512;
+  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int c = item / ngrp, grp = item % ngrp;
+  if (c >= nchunks) return;
   const int e0 = c * kSegChunk, e1 = min(N, e0 + kSegChunk);
   const int last = e1 - 1;
   if (e1 >= N) return;                      // nothing continues past the end
   const int v = keys[last];
   if (keys[e1] != v) return;                // last run does not continue
-  // did the segment start inside this chunk?
-  int s = last;
-  while (s > e0 && keys[s - 1] == v) --s;
-  if (s == e0 && e0 > 0 && keys[e0 - 1] == v) return;  // began earlier: owned by an earlier chunk
+  // did the run start inside this chunk?
+  if (keys[e0] == v && e0 > 0 && keys[e0 - 1] == v) return;  // began earlier: owned by an earlier chunk
   const int cend = min(nchunks - 1, segment_last(keys, N, e1, v) / kSegChunk);
-  // column C of a partial row carries the k sum
-  __shared__ float ks_sh;
-  if (threadIdx.x == 0) {
-    float ks = carry[((int64_t)c * 2 + 1) * (C + 1) + C];
-#pragma unroll 8
-    for (int cc = c + 1; cc <= cend; ++cc) ks += carry[((int64_t)cc * 2 + 0) * (C + 1) + C];
-    ks_sh = ks;
+  // k sums: slot 1 of chunk c, then slot 0 of chunks c+1..cend, lane-strided
+  // partial sums combined by a fixed butterfly
+  float ks = 0.f;
+  for (int cc = c + 1 + lane; cc <= cend; cc += 64) ks += carry[((int64_t)cc * 2 + 0) * (C + 8) + C];
+  ks = wave_sum(ks) + carry[((int64_t)c * 2 + 1) * (C + 8) + C];
+  const int col = grp * 512 + lane * 8;
+  if (col >= C) return;
+  float acc[8];
+  load8(carry + ((int64_t)c * 2 + 1) * (C + 8) + col, acc);
+  int cc = c + 1;
+  for (; cc + 7 <= cend; cc += 8) {
+    float x[8][8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) load8(carry + ((int64_t)(cc + u) * 2 + 0) * (C + 8) + col, x[u]);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[q] += x[u][q];
   }
-  __syncthreads();
-  const float ks = ks_sh;
-  for (int col = threadIdx.x; col < C; col += 256) {
-    float acc = carry[((int64_t)c * 2 + 1) * (C + 1) + col];
-#pragma unroll 8
-    for (int cc = c + 1; cc <= cend; ++cc) acc += carry[((int64_t)cc * 2 + 0) * (C + 1) + col];
-    const float w = wte_bf16 ? (float)((const bf16*)wte_raw)[(int64_t)v * C + col]
-                             : ((const float*)wte_raw)[(int64_t)v * C + col];
-    dwte[(int64_t)v * C + col] += acc - w * ks;
+  for (; cc <= cend; ++cc) {
+    float x[8];
+    load8(carry + ((int64_t)cc * 2 + 0) * (C + 8) + col, x);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[q] += x[q];
   }
+  float w[8], o[8];
+  load8(wte + (int64_t)v * C + col, w);
+  float* drow = dwte + (int64_t)v * C + col;
+  load8(drow, o);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) o[q] += acc[q] - w[q] * ks;
+  store8(drow, o);
 }
 
 // Value-embedding gradient: dve[v] += gate * sum over positions n with
@@ -277,10 +363,11 @@ hipError_t launch_embed_sort(const int32_t* idx, int N, int V, int32_t* keys_a, 
   const int nchunks = (N + kSortChunk - 1) / kSortChunk;
   int32_t *kin = keys_a, *vin = vals_a, *kout = keys_b, *vout = vals_b;
   for (int shift = 0; shift < 16; shift += 8) {
+    int32_t* total = hist + (size_t)256 * nchunks;
     hipLaunchKernelGGL(radix_hist_kernel, dim3(nchunks), dim3(kSortChunk), 0, s, kin, N, shift, nchunks, hist);
-    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, hist, 256 * nchunks);
+    hipLaunchKernelGGL(digit_scan_kernel, dim3(256), dim3(256), 0, s, hist, nchunks, total);
     hipLaunchKernelGGL(radix_scatter_kernel, dim3(nchunks), dim3(kSortChunk), 0, s, kin, vin, N, shift, nchunks, hist,
-                       kout, vout);
+                       total, kout, vout);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     std::swap(kin, kout);
     std::swap(vin, vout);
@@ -309,31 +396,55 @@ hipError_t launch_ve_scatter(int dtype, const int32_t* keys, const int32_t* vals
   return hipGetLastError();
 }
 
-size_t embed_bwd_hist_elems(int N) { return (size_t)256 * ((N + kSortChunk - 1) / kSortChunk); }
-size_t embed_bwd_carry_elems(int N, int C) { return (size_t)2 * ((N + kSegChunk - 1) / kSegChunk) * (C + 1); }
+// per-chunk digit counts, then the 256 digit totals
+size_t embed_bwd_hist_elems(int N) { return (size_t)256 * ((N + kSortChunk - 1) / kSortChunk) + 256; }
+// two partial-row slots of C + 8 floats per chunk of sorted entries (the
+// value-embedding sums use slots of 129 floats in the same buffer)
+size_t embed_bwd_carry_elems(int N, int C) {
+  return (size_t)2 * ((N + kSegChunk - 1) / kSegChunk) * (size_t)(C + 8 > 129 ? C + 8 : 129);
+}
+
+template <typename T, int J>
+hipError_t embed_seg(const EmbedBwdArgs& a, int nseg, hipStream_t s) {
+  hipLaunchKernelGGL((embed_seg_kernel<T, J>), dim3((nseg + 3) / 4), dim3(256), 0, s, a.keys_a, a.vals_a, a.dres,
+                     a.rstd0, (const T*)a.wte, a.N, a.C, a.dwte, a.carry);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t embed_seg_j(const EmbedBwdArgs& a, int nseg, hipStream_t s) {
+  switch ((a.C + 511) / 512) {
+    case 1: return embed_seg<T, 1>(a, nseg, s);
+    case 2: return embed_seg<T, 2>(a, nseg, s);
+    case 3: return embed_seg<T, 3>(a, nseg, s);
+    case 4: return embed_seg<T, 4>(a, nseg, s);
+    case 5: return embed_seg<T, 5>(a, nseg, s);
+    case 6: return embed_seg<T, 6>(a, nseg, s);
+    case 7: return embed_seg<T, 7>(a, nseg, s);
+    case 8: return embed_seg<T, 8>(a, nseg, s);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 hipError_t launch_embed_bwd(const EmbedBwdArgs& a, hipStream_t s) {
   const int N = a.N, C = a.C;
+  if (C % 8 != 0 || C > 4096) return hipErrorInvalidValue;
   hipError_t e;
   if (!a.accumulate) {
     if ((e = launch_fill_f32(a.dwte, 0.f, (int64_t)a.V * C, s)) != hipSuccess) return e;
   }
   if (N <= 0) return hipSuccess;
-  if (a.dtype == 1)
-    hipLaunchKernelGGL(embed_coef_kernel<bf16>, dim3((N + 3) / 4), dim3(256), 0, s, (const bf16*)a.wte, a.idx,
-                       a.dres, a.rstd0, N, C, a.V, a.coef);
-  else
-    hipLaunchKernelGGL(embed_coef_kernel<float>, dim3((N + 3) / 4), dim3(256), 0, s, (const float*)a.wte, a.idx,
-                       a.dres, a.rstd0, N, C, a.V, a.coef);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
   // the ids were sorted by launch_embed_sort into keys_a / vals_a
-  const int32_t* kin = a.keys_a;
-  const int32_t* vin = a.vals_a;
   const int nseg = (N + kSegChunk - 1) / kSegChunk;
-  hipLaunchKernelGGL(seg_partial_kernel, dim3(nseg), dim3(256), 0, s, kin, vin, a.dres, a.rstd0, a.coef, a.wte,
-                     a.dtype == 1, N, C, a.dwte, a.carry);
-  hipLaunchKernelGGL(seg_fixup_kernel, dim3(nseg), dim3(256), 0, s, kin, N, C, nseg, a.wte, a.dtype == 1, a.carry,
-                     a.dwte);
+  e = a.dtype == 1 ? embed_seg_j<bf16>(a, nseg, s) : embed_seg_j<float>(a, nseg, s);
+  if (e != hipSuccess) return e;
+  const int waves = nseg * ((C + 511) / 512);
+  if (a.dtype == 1)
+    hipLaunchKernelGGL(seg_fixup_kernel<bf16>, dim3((waves + 3) / 4), dim3(256), 0, s, a.keys_a, N, C, nseg,
+                       (const bf16*)a.wte, a.carry, a.dwte);
+  else
+    hipLaunchKernelGGL(seg_fixup_kernel<float>, dim3((waves + 3) / 4), dim3(256), 0, s, a.keys_a, N, C, nseg,
+                       (const float*)a.wte, a.carry, a.dwte);
   return hipGetLastError();
 }
 

@@ -400,7 +400,7 @@ struct Epilogue<T, Epi::Store> {
     const TileAddr<TM, WN> t(a.ldc, mbase, nbase, a.M, a.N);
     T* C = reinterpret_cast<T*>(a.C) + t.base;
     staged_store<TM, TN, WN>(acc, lds, mbase, nbase, lane, [&](int m, int n, float (&v)[4]) {
-      if (t.in(m, n)) store4(C + t.off(m, n), v);
+      if (t.in(m, n)) store4_nt(C + t.off(m, n), v);
     });
   }
 };
@@ -415,7 +415,7 @@ struct Epilogue<T, Epi::Residual> {
     auto pre = [&](int m, int n) {
       u32x2 r = {0u, 0u};
       if constexpr (sizeof(T) == 2) {
-        if (m < a.M && n < a.N) r = ld8(C + (int64_t)m * a.ldc + n);
+        if (m < a.M && n < a.N) r = ld8_nt(C + (int64_t)m * a.ldc + n);
       }
       return r;
     };
@@ -430,7 +430,7 @@ struct Epilogue<T, Epi::Residual> {
           load4(C + (int64_t)m * a.ldc + n, x);
         }
         for (int q = 0; q < 4; ++q) x[q] += v[q];
-        store4(C + (int64_t)m * a.ldc + n, x);
+        store4_nt(C + (int64_t)m * a.ldc + n, x);
       }
     });
   }
@@ -454,7 +454,7 @@ struct Epilogue<T, Epi::Relu2> {
           s[r] = p * p;
           mx = fmaxf(mx, s[r]);
         }
-        store4(A2 + t.off(m, n), s);
+        store4_nt(A2 + t.off(m, n), s);
       }
     });
     if constexpr (FOLD)  // the whole block runs the epilogue
@@ -476,7 +476,7 @@ struct Epilogue<T, Epi::Relu2Bwd> {
     auto pre = [&](int m, int n) {
       u32x2 r = {0u, 0u};
       if constexpr (sizeof(T) == 2) {
-        if (t.in(m, n)) r = ld8(A2 + t2.off(m, n));
+        if (t.in(m, n)) r = ld8_nt(A2 + t2.off(m, n));
       }
       return r;
     };
@@ -497,7 +497,7 @@ struct Epilogue<T, Epi::Relu2Bwd> {
           v[q] *= 2.f * __builtin_amdgcn_sqrtf(x[q]);
           mx = fmaxf(mx, fabsf(v[q]));
         }
-        store4(Dp + t.off(m, n), v);
+        store4_nt(Dp + t.off(m, n), v);
       }
     });
     if constexpr (FOLD)
@@ -550,7 +550,7 @@ struct Epilogue<T, Epi::LMHead> {
       const unsigned d = (unsigned)(tgt - n);
       const float Rt = d == 0u ? R[0] : (d == 1u ? R[1] : (d == 2u ? R[2] : R[3]));
       if (d < 4u) a.ztgt[m] = fmaf(-2.f * c, Rt, c);
-      if (mv) store4(Z + t.off(m, n), q);
+      if (mv) store4_nt(Z + t.off(m, n), q);
       float sum = 0.25f * sum4;
 #pragma unroll
       for (int o = 8; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 16);
@@ -567,7 +567,7 @@ struct Epilogue<T, Epi::GradF32> {
       const int z = a.zslice >= 0 ? a.zslice : (int)blockIdx.z;
       float* P = a.split_buf + (int64_t)z * a.M * a.N;
       staged_store<TM, TN, WN>(acc, lds, mbase, nbase, lane, [&](int m, int n, float (&v)[4]) {
-        if (m < a.M && n < a.N) store4(P + (int64_t)m * a.N + n, v);
+        if (m < a.M && n < a.N) store4_nt(P + (int64_t)m * a.N + n, v);
       });
     } else {
       float* G = reinterpret_cast<float*>(a.C);
@@ -577,10 +577,10 @@ struct Epilogue<T, Epi::GradF32> {
           float* p = G + (int64_t)m * a.ldc + n;
           if (accum) {
             float x[4];
-            load4(p, x);
+            load4_nt(p, x);
             for (int r = 0; r < 4; ++r) v[r] += x[r];
           }
-          store4(p, v);
+          store4_nt(p, v);
         }
       });
     }
@@ -1000,16 +1000,16 @@ __global__ __launch_bounds__(256) void splitk_reduce(const float* __restrict__ P
     float s[4] = {0.f, 0.f, 0.f, 0.f};
     for (int z = 0; z < splits; ++z) {
       float x[4];
-      load4(P + (int64_t)z * M * N + e, x);
+      load4_nt(P + (int64_t)z * M * N + e, x);
       for (int r = 0; r < 4; ++r) s[r] += x[r];
     }
     float* gp = G + (int64_t)m * ldg + n;
     if (accumulate) {
       float x[4];
-      load4(gp, x);
+      load4_nt(gp, x);
       for (int r = 0; r < 4; ++r) s[r] += x[r];
     }
-    store4(gp, s);
+    store4_nt(gp, s);
   }
 }
 

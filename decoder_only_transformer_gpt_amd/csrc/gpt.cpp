@@ -102,7 +102,7 @@ struct Layout {  // byte offsets inside the workspace
   // optimiser scratch: Newton-Schulz iterates and products, norm partials
   size_t ns_x, ns_xt, ns_a, ns_aa, ns_b, ns_part, ns_inv;
   int ns_batch;  // Muon matrices per batched launch
-  size_t keys_a, vals_a, keys_b, vals_b, hist, coef, carry;
+  size_t keys_a, vals_a, keys_b, vals_b, hist, carry;
   size_t total;
   size_t split_elems;
 };
@@ -274,7 +274,6 @@ Layout plan(const gpt_config& c, int maxB, int maxT) {
   L.keys_b = p.take(N * 4);
   L.vals_b = p.take(N * 4);
   L.hist = p.take(gk::embed_bwd_hist_elems((int)N) * 4);
-  L.coef = p.take(N * 4);
   L.carry = p.take(gk::embed_bwd_carry_elems((int)N, (int)C) * 4);
   L.total = p.off;
   return L;
@@ -1003,7 +1002,6 @@ gpt_status gpt_backward(gpt_model* m, float dloss, int32_t accumulate, void* str
     a.keys_b = wsp<int32_t>(m, L.keys_b);
     a.vals_b = wsp<int32_t>(m, L.vals_b);
     a.hist = wsp<int32_t>(m, L.hist);
-    a.coef = wsp<float>(m, L.coef);
     a.carry = wsp<float>(m, L.carry);
     return gk::launch_embed_bwd(a, stream);
   });

@@ -120,9 +120,8 @@ struct EmbedBwdArgs {
   float* dwte;           // [V, C] fp32
   // scratch (inside the workspace); keys_a / vals_a hold the ids sorted by launch_embed_sort
   int32_t* keys_a; int32_t* vals_a; int32_t* keys_b; int32_t* vals_b;  // [N] each
-  int32_t* hist;         // [256 * nchunks]
-  float* coef;           // [N]
-  float* carry;          // [2 * nseg_chunks * (C + 1)]
+  int32_t* hist;         // embed_bwd_hist_elems(N)
+  float* carry;          // embed_bwd_carry_elems(N, C)
 };
 // Stable sort of the token ids (key = id, value = position) into keys_a /
 // vals_a (keys_b / vals_b scratch); launch_embed_bwd and launch_ve_scatter

@@ -127,7 +127,13 @@ const char* gpt_status_string(gpt_status s);
 /* Thread-local detail of the last error raised on this thread ("" if none). */
 const char* gpt_last_error_message(void);
 
-/* Shapes from the depth dial: C = 64*depth, H = C/128, n_kv_head = 1, D = 128,
+/* The depth dial (aethryn.com "Nanochat: full-stack LLM training in 8,000
+ * lines for $72", section "One dial controls everything": width = 64 x depth,
+ * heads = width / 128; atlas.blal.pro "nanochat — full-stack ChatGPT in ~8k
+ * lines", section "How it works": heads of dim 128, separate query and K/V
+ * head counts (item 0), vocabulary 65,536 (item 1); energyai.berlin "nanochat
+ * vs GPT-OSS", section "Context window and scaling": 2,048-token context).
+ * Shapes from the depth dial: C = 64*depth, H = C/128, n_kv_head = 1, D = 128,
  * F = 4C, V = 65536, max_seq_len = 2048, theta = 1e4, softcap 15, eps = 2^-23,
  * every layer full causal attention (window_short 0, window_pattern "").
  * Host only. GPT_E_INVALID_ARG for depth < 2 (C must hold one 128-wide head
@@ -156,7 +162,12 @@ gpt_status gpt_param_layout(const gpt_config* cfg, gpt_tensor_desc* out, int32_t
  * Host only. */
 gpt_status gpt_workspace_bytes(const gpt_config* cfg, int32_t max_B, int32_t max_T, size_t* bytes);
 
-/* Creates a handle. `params` is the flat parameter buffer in the config dtype
+/* Sets up one model for training steps on the caller's memory: fp32 gradients
+ * beside parameters in the compute dtype (aimarketly.com "nanochat-train"
+ * README, section "Precision / dtype": bf16 compute, fp32 master weights and
+ * gradients), RoPE tables with base 10,000 (aethryn.com, section "A
+ * Llama-class transformer with ten modern departures").
+ * Creates a handle. `params` is the flat parameter buffer in the config dtype
  * (read only, never written); `grads` the flat fp32 gradient buffer with the
  * same offsets; `workspace` a device buffer of at least
  * gpt_workspace_bytes(cfg, max_B, max_T) bytes, 256-byte aligned. All three are
@@ -165,7 +176,14 @@ gpt_status gpt_workspace_bytes(const gpt_config* cfg, int32_t max_B, int32_t max
 gpt_status gpt_init(const gpt_config* cfg, const void* params, float* grads, void* workspace,
                     size_t ws_bytes, int32_t max_B, int32_t max_T, void* stream, gpt_model** out);
 
-/* Forward pass and mean cross-entropy loss over all B*T positions.
+/* The forward pass of one pretraining step (aethryn.com "Nanochat: full-stack
+ * LLM training in 8,000 lines for $72", section "A Llama-class transformer
+ * with ten modern departures": embedding, RMSNorm before every block and the
+ * head, RoPE then QK-norm, causal attention, relu^2 MLP, untied head with the
+ * 15*tanh(z/15) softcap in fp32; energyai.berlin "nanochat vs GPT-OSS",
+ * section "Architectural decisions": multi-query attention) and its loss,
+ * the mean cross-entropy of the next token.
+ * Forward pass and mean cross-entropy loss over all B*T positions.
  * idx, targets: device int32 [B, T] row-major; targets are the next tokens,
  * each in [0, V). loss: device fp32 scalar. row_loss: optional device fp32
  * [B*T] per-position losses (may be NULL). need_grad = 1 keeps the stash that
@@ -176,7 +194,11 @@ gpt_status gpt_init(const gpt_config* cfg, const void* params, float* grads, voi
 gpt_status gpt_forward_loss(gpt_model* m, const int32_t* idx, const int32_t* targets, int32_t B,
                             int32_t T, int32_t need_grad, float* loss, float* row_loss, void* stream);
 
-/* Backward of the last need_grad forward: grads = dloss * d(loss)/d(theta).
+/* The backward pass of the same step, written as dloss times the gradient so
+ * that a caller can average micro-batches, and with `accumulate` for the
+ * gradient accumulation a single GPU runs in place of eight (aimarketly.com
+ * "nanochat-train" README, section "Getting started").
+ * Backward of the last need_grad forward: grads = dloss * d(loss)/d(theta).
  * accumulate = 1 adds into the gradient buffer; 0 overwrites all of it
  * (including embedding rows no token touched). GPT_E_STATE if no forward is
  * pending. Asynchronous. */
