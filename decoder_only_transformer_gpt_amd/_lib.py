@@ -95,6 +95,9 @@ _SIGS = {
     "gpt_fp8_matmul": (ctypes.c_int32, [_P, ctypes.c_int64, _P, _P, ctypes.c_int64, _P, ctypes.c_int32, ctypes.c_int32,
                                         ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int64, ctypes.c_int32,
                                         ctypes.c_int32, _P, _P]),
+    "gpt_fp8_matmul_noalloc": (ctypes.c_int32, [_P, ctypes.c_int64, _P, _P, ctypes.c_int64, _P, ctypes.c_int32,
+                                                ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int64,
+                                                ctypes.c_int32, ctypes.c_int32, _P]),
 }
 
 
@@ -233,6 +236,12 @@ def gpt_fp8_matmul(a_ptr, lda, amax_a_ptr, b_ptr, ldb, amax_b_ptr, M, N, K, out_
                    splits=1, partials_ptr=None, stream=0):
     _check(lib().gpt_fp8_matmul(a_ptr, lda, amax_a_ptr, b_ptr, ldb, amax_b_ptr, M, N, K, out_dtype, out_ptr, ldo,
                                 tile, splits, partials_ptr, stream), "gpt_fp8_matmul")
+
+
+def gpt_fp8_matmul_noalloc(a_ptr, lda, amax_a_ptr, b_ptr, ldb, amax_b_ptr, M, N, K, out_dtype, out_ptr, ldo, tile=0,
+                           splits=1, stream=0):
+    _check(lib().gpt_fp8_matmul_noalloc(a_ptr, lda, amax_a_ptr, b_ptr, ldb, amax_b_ptr, M, N, K, out_dtype, out_ptr,
+                                        ldo, tile, splits, stream), "gpt_fp8_matmul_noalloc")
 
 
 def gpt_optimizer_state_elems(cfg: gpt_config) -> int:

@@ -21,6 +21,7 @@
 // holding 4 consecutive output columns of one output row: the epilogue writes
 // 8- or 16-byte vectors and row-wise epilogue reductions stay inside a lane.
 
+#include <mutex>
 #include <type_traits>
 
 #include "common.h"
@@ -1184,6 +1185,31 @@ hipError_t launch_typed(Epi epi, const GemmArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+// Split-K partials for callers that cannot allocate (gpt_fp8_matmul_noalloc):
+// a fixed device array, one copy per GPU for the life of the process. Host
+// code never passes the array's name to a kernel: each device's address is
+// looked up once, with that device current, and cached.
+namespace {
+__device__ __align__(256) float scratch[kNoAllocScratchFloats];
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t noalloc_scratch(float** out) {
+  *out = nullptr;
+  int dev = 0;
+  if (hipError_t e = hipGetDevice(&dev); e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)); e != hipSuccess) return e;
+    g_scratch_ptr[dev] = static_cast<float*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_gemm(int dtype, Epi epi, const GemmArgs& a, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0 || a.batch <= 0) return hipSuccess;

@@ -1248,6 +1248,23 @@ gpt_status gpt_fp8_matmul(const uint8_t* a, int64_t lda, const float* amax_a, co
   return GPT_OK;
 }
 
+gpt_status gpt_fp8_matmul_noalloc(const uint8_t* a, int64_t lda, const float* amax_a, const uint8_t* b,
+                                  int64_t ldb, const float* amax_b, int32_t M, int32_t N, int32_t K,
+                                  int32_t out_dtype, void* out, int64_t ldo, int32_t tile, int32_t splits,
+                                  void* stream) {
+  float* part = nullptr;
+  if (splits > 1) {
+    if (M < 0 || N < 0 || splits > 64)
+      return fail(GPT_E_INVALID_ARG, "need M, N >= 0 and splits 1..64");
+    const uint64_t need = (uint64_t)splits * (uint64_t)M * (uint64_t)N;
+    if (need > gk::kNoAllocScratchFloats)
+      return fail(GPT_E_INVALID_ARG, "splits * M * N = %llu exceeds the fixed partial buffer of %llu floats",
+                  (unsigned long long)need, (unsigned long long)gk::kNoAllocScratchFloats);
+    HIP_TRY(gk::noalloc_scratch(&part));
+  }
+  return gpt_fp8_matmul(a, lda, amax_a, b, ldb, amax_b, M, N, K, out_dtype, out, ldo, tile, splits, part, stream);
+}
+
 gpt_status gpt_fp8_quantize(const void* x, int64_t rows, int64_t cols, uint8_t* q, uint8_t* qT, int64_t ldT,
                             float* amax, void* stream_) {
   if (!x || !amax || (!q && !qT)) return fail(GPT_E_INVALID_ARG, "x, amax and one of q, qT must be non-NULL");

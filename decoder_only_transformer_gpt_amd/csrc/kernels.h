@@ -54,6 +54,12 @@ struct GemmArgs {
 // dtype: 0 = fp32, 1 = bf16 (gpt.h GPT_F32 / GPT_BF16), 2 = fp8 e4m3
 // operands (k-contiguous, K a multiple of 128) with bf16 / fp32 outputs
 hipError_t launch_gemm(int dtype, Epi epi, const GemmArgs& a, hipStream_t s);
+// Fixed device array for split-K partials of gpt_fp8_matmul_noalloc (floats,
+// 16 MiB per GPU), and the address of the current device's copy (looked up
+// once per device with hipGetSymbolAddress).
+constexpr size_t kNoAllocScratchFloats = (size_t)4 << 20;
+constexpr int kMaxDevices = 64;
+hipError_t noalloc_scratch(float** out);
 // Partial-column width of the LMHead epilogue (exp-sum partials per row).
 constexpr int kLMHeadPartCols = 64;
 

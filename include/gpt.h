@@ -287,6 +287,21 @@ gpt_status gpt_fp8_matmul(const uint8_t* a, int64_t lda, const float* amax_a, co
                           const float* amax_b, int32_t M, int32_t N, int32_t K, int32_t out_dtype, void* out,
                           int64_t ldo, int32_t tile, int32_t splits, float* partials, void* stream);
 
+/* gpt_fp8_matmul for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments and result, but split-K partials (splits > 1) go to a
+ * fixed device array inside the library instead of a caller buffer. The array
+ * holds 4,194,304 floats (16 MiB) on each GPU the library runs on, kept until
+ * the process ends; splits * M * N above that is GPT_E_INVALID_ARG. Nothing
+ * is allocated: the array's address on the current device is looked up on
+ * the first call made on that device. Every call on one GPU shares that GPU's
+ * array, so calls with splits > 1 that overlap on one GPU (other streams or
+ * threads) race and must be serialised by the caller. */
+gpt_status gpt_fp8_matmul_noalloc(const uint8_t* a, int64_t lda, const float* amax_a, const uint8_t* b,
+                                  int64_t ldb, const float* amax_b, int32_t M, int32_t N, int32_t K,
+                                  int32_t out_dtype, void* out, int64_t ldo, int32_t tile, int32_t splits,
+                                  void* stream);
+
 /* ---- The optimiser step after the backward ------------------------------
  * Muon for the blocks' matrix weights (w_qkv, w_o, w_1, w_2), AdamW for the
  * embeddings (wte and the value-embedding tables), the unembedding (lm_head)
