@@ -12,8 +12,16 @@ Two reports, both plain text:
   units. The report carries a digest of the kernel's sources; ``bench.py``
   reports the figure only while that digest still matches.
 
+* ``mfma``: per kernel, from one ``--pmc`` run with
+  ``SQ_INSTS_VALU_MFMA_MOPS_BF16`` (bf16 MFMA operations / 512),
+  ``SQ_VALU_MFMA_BUSY_CYCLES`` and ``SQ_BUSY_CYCLES``: the MFMA FLOPs each
+  dispatch executed (recomputation included), its duration from the
+  dispatch's own timestamps, the executed TFLOP/s, and the MFMA-busy share
+  busy_cycles / (SIMDs x duration x clock) at the given engine clock.
+
 Usage:
   python -m decoder_only_transformer_gpt_amd.profsum stats CSV --command CMD [--top N]
+  python -m decoder_only_transformer_gpt_amd.profsum mfma DIR --command CMD --clock-mhz F [--simds 1024]
   python -m decoder_only_transformer_gpt_amd.profsum traffic --fetch DIR --write DIR --kernel SUBSTR
          --tag TAG --copy-bytes N --command-fetch CMD --command-write CMD
 """
@@ -140,6 +148,39 @@ def traffic_report(fetch_dir: str, write_dir: str, kernel: str, tag: str, copy_b
     return "\n".join(out) + "\n"
 
 
+def mfma_report(d: str, command: str, clock_mhz: float, simds: int = 1024, top: int = 40) -> str:
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no counter_collection.csv under {d}")
+    disp: dict = {}
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            key = (f, r["Dispatch_Id"])
+            e = disp.setdefault(key, {"name": r["Kernel_Name"],
+                                      "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+            e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    per: dict = {}
+    for e in disp.values():
+        k = short_name(e["name"])
+        a = per.setdefault(k, {"n": 0, "ns": 0.0, "mops": 0.0, "busy": 0.0})
+        a["n"] += 1
+        a["ns"] += e["ns"]
+        a["mops"] += e.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0)
+        a["busy"] += e.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
+    rows = sorted(((k, a) for k, a in per.items() if a["mops"] > 0), key=lambda kv: -kv[1]["ns"])
+    out = [f"command: {command}",
+           f"MFMA-busy share = SQ_VALU_MFMA_BUSY_CYCLES / ({simds} SIMDs x duration x {clock_mhz:.0f} MHz); "
+           "executed FLOPs = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 (recomputation included); durations are the "
+           "profiled dispatches' own timestamps", "",
+           f"{'calls':>5} {'avg ms':>8} {'GFLOP/call':>11} {'TFLOP/s':>8} {'MFMA busy':>9}  kernel"]
+    for k, a in rows[:top]:
+        avg_ms = a["ns"] / a["n"] / 1e6
+        fl = a["mops"] * 512 / a["n"]
+        busy = a["busy"] / (simds * (a["ns"] * 1e-9) * clock_mhz * 1e6)
+        out.append(f"{a['n']:5d} {avg_ms:8.4f} {fl / 1e9:11.1f} {fl / (avg_ms * 1e-3) / 1e12:8.1f} {busy:9.3f}  {k}")
+    return "\n".join(out) + "\n"
+
+
 def read_traffic(path: str, tag: str) -> float | None:
     """Traffic per launch from a report, or None if absent or its sources changed."""
     if not os.path.exists(path):
@@ -172,8 +213,15 @@ def main():
     t.add_argument("--copy-bytes", type=int, required=True)
     t.add_argument("--command-fetch", required=True)
     t.add_argument("--command-write", required=True)
+    m = sub.add_parser("mfma")
+    m.add_argument("dir")
+    m.add_argument("--command", required=True)
+    m.add_argument("--clock-mhz", type=float, required=True)
+    m.add_argument("--simds", type=int, default=1024)
     a = ap.parse_args()
-    if a.mode == "stats":
+    if a.mode == "mfma":
+        print(mfma_report(a.dir, a.command, a.clock_mhz, a.simds), end="")
+    elif a.mode == "stats":
         print(stats_report(a.csv, a.command, a.top), end="")
     else:
         print(traffic_report(a.fetch, a.write, a.kernel, a.tag, a.copy_bytes, a.command_fetch, a.command_write),
