@@ -60,12 +60,15 @@ closed form, an invariant, a library routine or finite differences; none is
 from __future__ import annotations
 
 import math
+import os
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
 EPS = 2.0 ** -23          # RMSNorm epsilon (reading: float32 machine epsilon)
 ROPE_THETA = 10000.0      # [P1] "A Llama-class transformer..."; RoPE base
 SOFTCAP = 15.0            # [P1] same section; logits = 15 * tanh(z / 15)
+_WORKERS = max(1, min(16, len(os.sched_getaffinity(0))))  # threads for independent attention heads
 
 
 # ---------------------------------------------------------------------------
@@ -193,6 +196,21 @@ def layer_window(cfg: dict, layer: int) -> int | None:
     return short if pattern[layer % len(pattern)] == "S" else None
 
 
+def _each(fn, items):
+    """Runs fn on every item. The items (batch rows and heads of attention) are
+    independent and each writes only its own output slice, so they run on a
+    thread pool: NumPy's elementwise kernels release the GIL, and the softmax
+    work of different heads proceeds side by side. Nothing about the result
+    depends on the order."""
+    items = list(items)
+    if len(items) <= 1 or _WORKERS <= 1:
+        for it in items:
+            fn(it)
+        return
+    with ThreadPoolExecutor(min(len(items), _WORKERS)) as ex:
+        list(ex.map(fn, items))
+
+
 def causal_mqa_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, window: int | None = None):
     """Causal attention where all query heads share one K/V head
     ([P5] "Multi-Query Attention"; [P1] causal decoder).
@@ -206,16 +224,18 @@ def causal_mqa_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, window: in
     mask = attention_mask(T, window)
     o = np.empty_like(q)
     lse = np.empty((B, H, T))
-    for b in range(B):
-        qh = q[b].transpose(1, 0, 2)                      # [H, T, D]
-        s = (qh @ k[b].T) * scale                          # [H, T(query), T(key)]
-        s = np.where(mask[None], s, -np.inf)
+
+    def one(bh):
+        b, h = bh
+        s = (q[b, :, h, :] @ k[b].T) * scale               # [T(query), T(key)]
+        s = np.where(mask, s, -np.inf)
         m = s.max(axis=-1, keepdims=True)
         e = np.exp(s - m)
         z = e.sum(axis=-1, keepdims=True)
-        p = e / z
-        o[b] = (p @ v[b]).transpose(1, 0, 2)
-        lse[b] = (m + np.log(z))[..., 0]
+        o[b, :, h, :] = (e / z) @ v[b]
+        lse[b, h] = (m + np.log(z))[:, 0]
+
+    _each(one, [(b, h) for b in range(B) for h in range(H)])
     return o, lse
 
 
@@ -229,20 +249,24 @@ def causal_mqa_attention_bwd(do, q, k, v, window: int | None = None):
     scale = 1.0 / math.sqrt(D)
     mask = attention_mask(T, window)
     dq = np.empty_like(q)
-    dk = np.empty_like(k)
-    dv = np.empty_like(v)
-    for b in range(B):
-        qh, doh = q[b].transpose(1, 0, 2), do[b].transpose(1, 0, 2)   # [H, T, D]
+    dk_h = np.empty((B, H, T, D))     # per-head terms of dk and dv, summed over heads below
+    dv_h = np.empty((B, H, T, D))
+
+    def one(bh):
+        b, h = bh
+        qh, doh = q[b, :, h, :], do[b, :, h, :]            # [T, D]
         s = (qh @ k[b].T) * scale
-        s = np.where(mask[None], s, -np.inf)
+        s = np.where(mask, s, -np.inf)
         e = np.exp(s - s.max(axis=-1, keepdims=True))
         p = e / e.sum(axis=-1, keepdims=True)
         dp = doh @ v[b].T
         ds = p * (dp - (p * dp).sum(axis=-1, keepdims=True))
-        dq[b] = (ds @ k[b]).transpose(1, 0, 2) * scale
-        dk[b] = (ds.transpose(0, 2, 1) @ qh).sum(axis=0) * scale
-        dv[b] = (p.transpose(0, 2, 1) @ doh).sum(axis=0)
-    return dq, dk, dv
+        dq[b, :, h, :] = (ds @ k[b]) * scale
+        dk_h[b, h] = ds.T @ qh
+        dv_h[b, h] = p.T @ doh
+
+    _each(one, [(b, h) for b in range(B) for h in range(H)])
+    return dq, dk_h.sum(axis=1) * scale, dv_h.sum(axis=1)
 
 
 def softcap(z: np.ndarray, c: float = SOFTCAP) -> np.ndarray:

@@ -33,6 +33,21 @@ def oracle_cfg(c: _lib.gpt_config) -> dict:
     return d
 
 
+_WEIGHTS: dict = {}
+
+
+def seeded_weights(shapes, seed: int, dtype: str):
+    """synthetic.make_weights, kept for the next test that asks for the same
+    draw (the d20 draw takes seconds). The arrays are shared: callers copy
+    before changing them."""
+    key = (tuple(shapes), seed, dtype)
+    if key not in _WEIGHTS:
+        while len(_WEIGHTS) >= 2:
+            _WEIGHTS.pop(next(iter(_WEIGHTS)))
+        _WEIGHTS[key] = synthetic.make_weights(shapes, seed=seed, dtype=dtype)
+    return _WEIGHTS[key]
+
+
 class Case:
     """One configuration with seeded weights and tokens."""
 
@@ -40,7 +55,7 @@ class Case:
         self.cfg, self.B, self.T, self.law = cfg, B, T, law
         self.shapes = [(n, r, c) for n, _, r, c in _lib.gpt_param_layout(cfg)]
         dt = "f32" if cfg.dtype == _lib.GPT_F32 else "bf16"  # FP8 models keep bf16 parameters
-        self.storage, self.values = synthetic.make_weights(self.shapes, seed=wseed, dtype=dt)
+        self.storage, self.values = seeded_weights(self.shapes, wseed, dt)
         self.idx, self.tgt = synthetic.make_tokens(B, T, cfg.vocab_size, law, seed=tseed)
 
     def oracle_params(self) -> dict:

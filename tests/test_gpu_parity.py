@@ -218,9 +218,9 @@ def test_d20_bf16_gradients(form):
 @pytest.mark.timeout(900)
 def test_d20_full_batch_sampled_rows():
     """The benchmarked launch (d20, B=32, T=2048) on 32 distinct rows: the
-    per-position losses of two seeded batch rows against an oracle forward of
-    just those rows (rows are independent), every position within the loss
-    tolerance, and finite gradients."""
+    per-position losses of three batch rows (the first two and the last)
+    against the oracle on just those rows (rows are independent), every
+    position within the loss tolerance, and finite gradients."""
     U.require_gpu()
     c = _lib.gpt_config_from_depth(20, _lib.GPT_BF16)
     case = U.Case(c, B=32, T=2048, law="zipf")
@@ -230,9 +230,15 @@ def test_d20_full_batch_sampled_rows():
     assert np.all(np.isfinite(gpu["grads"]))
     rows_gpu = gpu["row_loss"].reshape(32, 2048)
     assert gpu["loss"] == pytest.approx(rows_gpu.mean(), rel=1e-5)
+    # rows 0 and 1 of this seeded draw are the two rows of the d20 B=2 case
+    # (one [B, T+1] draw, row by row), whose oracle step the gradient tests
+    # already ran; the last row gets an oracle forward of its own
+    two = U.Case(c, B=2, T=2048, law="zipf")
+    assert np.array_equal(two.idx, case.idx[:2]) and np.array_equal(two.tgt, case.tgt[:2])
+    _, rows2, _ = oracle_step("d20-b2", two)
     P = case.oracle_params()
-    for b in (int(np.random.default_rng(7).integers(0, 32)), 31):
-        r = O.forward_rows(U.oracle_cfg(c), P, case.idx[b:b + 1], case.tgt[b:b + 1])[0]
+    for b in (0, 1, 31):
+        r = rows2[b] if b < 2 else O.forward_rows(U.oracle_cfg(c), P, case.idx[b:b + 1], case.tgt[b:b + 1])[0]
         rel = abs(rows_gpu[b].mean() - r.mean()) / r.mean()
         err = np.abs(rows_gpu[b] - r) / r
         U.log(f"[d20-B32] row {b}: mean loss gpu={rows_gpu[b].mean():.5f} oracle={r.mean():.5f} rel={rel:.2e} "
