@@ -126,18 +126,20 @@ DEV void ld8w(const T* p, float (&v)[8]) { load8(p, v); }
 // One wave per chunk of kSegChunk sorted entries; lane l holds columns
 // j * 512 + 8l .. +8 of every row (J = ceil(C / 512) groups). For each run of
 // equal ids in the chunk the wave accumulates a1 = sum r_n dres_n and
-// a2 = sum (r_n^3 / C) dres_n, the next entry's row in flight while the
-// current one is added. At a run's end, ks = <a2, wte[v]> (a wave
-// reduction); a run that starts and ends inside the chunk adds
-// a1 - wte[v] * ks to dwte[v]; a run cut by the chunk's first (last) edge
-// stores a1 and ks in carry slot 0 (1) of the chunk instead (slots of C + 8
-// floats: the row, then ks).
+// a2 = sum (r_n^3 / C) dres_n; the next entry's row is in flight while the
+// current one is added (two row buffers in alternate roles), and a run's
+// embedding row is requested when the run starts. At a run's end,
+// ks = <a2, wte[v]> (a wave reduction); a run that starts and ends inside the
+// chunk adds a1 - wte[v] * ks to dwte[v] (stores it when the backward
+// overwrites: dwte was zeroed first); a run cut by the chunk's first (last)
+// edge stores a1 and ks in carry slot 0 (1) of the chunk instead (slots of
+// C + 8 floats: the row, then ks).
 template <typename T, int J>
 __global__ __launch_bounds__(256) void embed_seg_kernel(const int32_t* __restrict__ keys,
                                                         const int32_t* __restrict__ vals,
                                                         const float* __restrict__ dres,
                                                         const float* __restrict__ rstd0, const T* __restrict__ wte,
-                                                        int N, int C, float* __restrict__ dwte,
+                                                        int N, int C, int accumulate, float* __restrict__ dwte,
                                                         float* __restrict__ carry) {
   static_assert(kSegChunk <= 64, "one entry per lane");
   const int lane = threadIdx.x & 63;
@@ -160,20 +162,27 @@ __global__ __launch_bounds__(256) void embed_seg_kernel(const int32_t* __restric
     col[j] = j * 512 + lane * 8;
     cv[j] = col[j] < C;
   }
-  float a1[J][8], a2[J][8], cur[J][8], nxt[J][8];
-  auto load_row = [&](float (&dst)[J][8], int n) {
+  float a1[J][8], a2[J][8], ra[J][8], rb[J][8], w[J][8];
+  auto load_row = [&](float (&dst)[J][8], int n) __attribute__((always_inline)) {
     const float* row = dres + (int64_t)(n < 0 ? 0 : n) * C;
 #pragma unroll
     for (int j = 0; j < J; ++j)
       if (cv[j]) ld8f(row + col[j], dst[j]);
   };
+  auto load_w = [&](int v) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+      if (cv[j]) ld8w(wte + (int64_t)v * C + col[j], w[j]);
+  };
 #pragma unroll
   for (int j = 0; j < J; ++j)
 #pragma unroll
     for (int q = 0; q < 8; ++q) a1[j][q] = a2[j][q] = 0.f;
-  load_row(cur, __builtin_amdgcn_readlane(val_l, 0));
+  load_row(ra, __builtin_amdgcn_readlane(val_l, 0));
+  load_w(__builtin_amdgcn_readlane(key_l, 0));
   int rs = 0;  // run start (entry index within the chunk)
-  for (int e = 0; e < ne; ++e) {
+  // entry e: row in `cur`; the next entry's row goes to `nxt`
+  auto step = [&](int e, float (&cur)[J][8], float (&nxt)[J][8]) __attribute__((always_inline)) {
     const int v = __builtin_amdgcn_readlane(key_l, e);
     const int n = __builtin_amdgcn_readlane(val_l, e);
     const float r = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, r_l), e));
@@ -193,12 +202,10 @@ __global__ __launch_bounds__(256) void embed_seg_kernel(const int32_t* __restric
       // end of a run inside this chunk (it may continue in the next chunk)
       const bool starts_here = rs > 0 || prev_key != v;
       const bool ends_here = vn != v;
-      float w[J][8];
       float dot = 0.f;
 #pragma unroll
       for (int j = 0; j < J; ++j)
         if (cv[j]) {
-          ld8w(wte + (int64_t)v * C + col[j], w[j]);
 #pragma unroll
           for (int q = 0; q < 8; ++q) dot = fmaf(a2[j][q], w[j][q], dot);
         }
@@ -209,9 +216,9 @@ __global__ __launch_bounds__(256) void embed_seg_kernel(const int32_t* __restric
         for (int j = 0; j < J; ++j)
           if (cv[j]) {
             float o[8];
-            ld8f(drow + col[j], o);
+            if (accumulate) ld8f(drow + col[j], o);
 #pragma unroll
-            for (int q = 0; q < 8; ++q) o[q] += a1[j][q] - w[j][q] * ks;
+            for (int q = 0; q < 8; ++q) o[q] = (accumulate ? o[q] : 0.f) + a1[j][q] - w[j][q] * ks;
             store8(drow + col[j], o);
           }
       } else {
@@ -226,12 +233,15 @@ __global__ __launch_bounds__(256) void embed_seg_kernel(const int32_t* __restric
 #pragma unroll
         for (int q = 0; q < 8; ++q) a1[j][q] = a2[j][q] = 0.f;
       rs = e + 1;
+      if (e + 1 < ne) load_w(vn);  // the next run's embedding row
     }
-#pragma unroll
-    for (int j = 0; j < J; ++j)
-#pragma unroll
-      for (int q = 0; q < 8; ++q) cur[j][q] = nxt[j][q];
+  };
+  int e = 0;
+  for (; e + 1 < ne; e += 2) {
+    step(e, ra, rb);
+    step(e + 1, rb, ra);
   }
+  if (e < ne) step(e, ra, rb);
 }
 
 // Last sorted position holding id v, searching from position `from` (whose
@@ -407,7 +417,7 @@ size_t embed_bwd_carry_elems(int N, int C) {
 template <typename T, int J>
 hipError_t embed_seg(const EmbedBwdArgs& a, int nseg, hipStream_t s) {
   hipLaunchKernelGGL((embed_seg_kernel<T, J>), dim3((nseg + 3) / 4), dim3(256), 0, s, a.keys_a, a.vals_a, a.dres,
-                     a.rstd0, (const T*)a.wte, a.N, a.C, a.dwte, a.carry);
+                     a.rstd0, (const T*)a.wte, a.N, a.C, a.accumulate, a.dwte, a.carry);
   return hipGetLastError();
 }
 

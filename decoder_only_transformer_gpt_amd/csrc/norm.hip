@@ -323,14 +323,20 @@ namespace {
 // dst[t][c][r] = src[t][r][c]. One 64x64 tile per block, staged through LDS
 // (+1 column of padding against bank conflicts; 16-element vector accesses
 // for whole tiles, element by element at ragged edges); tiles of all tensors are
-// numbered consecutively and a block finds its tensor by a linear scan of
-// the (few dozen) tile-start offsets.
+// numbered consecutively and a block finds its tensor by a binary search of
+// the (few dozen) tile-start offsets (a linear scan, one dependent scalar load
+// per tensor, had cost more than the block's own 16 KiB of traffic).
 template <typename T>
 __global__ __launch_bounds__(256) void transpose_batched_kernel(const T* __restrict__ src, T* __restrict__ dst,
                                                                 const TransposeDesc* __restrict__ desc, int ndesc) {
   __shared__ float tile[64][65];
-  int t = 0;
-  while (t + 1 < ndesc && (int64_t)blockIdx.x >= desc[t + 1].tile0) ++t;
+  int lo = 0, hi = ndesc;  // desc[lo].tile0 <= blockIdx.x < desc[hi].tile0 (desc[ndesc] past the end)
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if ((int64_t)blockIdx.x >= desc[mid].tile0) lo = mid;
+    else hi = mid;
+  }
+  const int t = lo;
   const TransposeDesc d = desc[t];
   const int64_t local = blockIdx.x - d.tile0;
   const int tiles_c = (d.cols + 63) / 64;

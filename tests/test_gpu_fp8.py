@@ -168,6 +168,53 @@ def test_fp8_matmul_on_identical_codes(M, N, K, out, tile, splits):
     assert np.all(err <= bound)
 
 
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("M,N,K,out,splits", [
+    (32768, 1792, 1536, "bf16", 1),     # d24 QKV forward (B=16 x T=2048 tokens)
+    (32768, 1536, 6144, "bf16", 1),     # d24 W2 forward / W1 dX
+    (6144, 1536, 32768, "f32", 4)])     # d24 W1 dW: tokens on K, split-K
+def test_fp8_d24_shapes_quantise_and_matmul(M, N, K, out, splits):
+    """Quantise -> e4m3 GEMM at the d24 FP8 model's own shapes, under the
+    kernel-level bars: the GPU's codes of both operands equal the oracle's bit
+    for bit (checked on 256 seeded rows of A and all of B), and 256 seeded
+    output rows lie within the fp32-accumulation bound of the float64 product
+    of the same dequantised codes (plus half a bf16 ulp for bf16 output).
+    These bars hold at any depth; the whole-step d24 comparison below is a
+    sanity check of the assembled step."""
+    torch = U.require_gpu()
+    rng = np.random.default_rng(M + 3 * N + 7 * K)
+    U.log(f"case fp8 d24 shape M={M} N={N} K={K} out={out} splits={splits}")
+    ab, av = _bf16_tensor(rng, M, K, 1.0)
+    bb, bv = _bf16_tensor(rng, N, K, 0.05)
+    qa, am_a = _codes(torch, ab)
+    qb, am_b = _codes(torch, bb)
+    odt = torch.float32 if out == "f32" else torch.bfloat16
+    o = torch.full((M, N), float("nan"), dtype=odt, device="cuda")
+    part = torch.empty((splits, M, N), dtype=torch.float32, device="cuda") if splits > 1 else None
+    _lib.gpt_fp8_matmul(qa.data_ptr(), K, am_a.data_ptr(), qb.data_ptr(), K, am_b.data_ptr(), M, N, K,
+                        _lib.GPT_F32 if out == "f32" else _lib.GPT_BF16, o.data_ptr(), N, 0, splits,
+                        None if part is None else part.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    rows = np.sort(rng.choice(M, size=256, replace=False))
+    # the oracle's scale from the whole tensor's |max|, its codes on the sampled rows
+    sa = np.float32(448.0) / np.float32(np.abs(av).max())
+    sb = np.float32(448.0) / np.float32(np.abs(bv).max())
+    assert float(am_a.item()) == float(np.abs(av).max()) and float(am_b.item()) == float(np.abs(bv).max())
+    ca = O.e4m3_encode((av[rows] * sa).astype(np.float32))
+    cb, sb_o = O.fp8_quantize(bv)
+    assert np.float32(sb_o) == sb
+    np.testing.assert_array_equal(qa.cpu().numpy()[rows], ca)
+    np.testing.assert_array_equal(qb.cpu().numpy(), cb)
+    da, db = O.fp8_dequantize(ca, sa), O.fp8_dequantize(cb, sb)
+    ref = da @ db.T
+    mag = np.abs(da) @ np.abs(db).T
+    got = o.float().cpu().numpy()[rows].astype(np.float64)
+    bound = 2.0 ** -16 * mag + (2.0 ** -8 * np.abs(ref) if out == "bf16" else 0.0)
+    err = np.abs(got - ref)
+    U.log(f"[fp8-d24] max err / bound = {np.max(err / np.maximum(bound, 1e-300)):.3f}")
+    assert np.all(err <= bound)
+
+
 @pytest.mark.parametrize("tile", [0, 1, 2, 3])
 def test_d4_fp8_full_step(tile):
     U.require_gpu()

@@ -28,17 +28,21 @@ def d4_cfg():
     return c
 
 
-def vanishing(go: dict, k: str) -> bool:
+def grad_norm(go: dict) -> float:
+    """L2 norm of the whole gradient (all tensors)."""
+    return float(np.sqrt(sum(float(np.dot(v.ravel(), v.ravel())) for v in go.values())))
+
+
+def vanishing(go: dict, k: str, total: float) -> bool:
     """A gradient the mathematics makes exactly zero (e.g. W_q and W_k with
     one-token rows, where the softmax is 1 whatever q and k are): its norm is
-    below 1e-12 of the whole gradient's. The GPU's value is then rounding
-    residue (dP - delta cancels), checked against the whole gradient's scale."""
-    total = np.sqrt(sum(float(np.sum(v * v)) for v in go.values()))
+    below 1e-12 of the whole gradient's (`total`). The GPU's value is then
+    rounding residue (dP - delta cancels), checked against the whole
+    gradient's scale."""
     return float(np.linalg.norm(go[k])) <= 1e-12 * total
 
 
-def check_vanishing(gg, go, k, tol):
-    total = np.sqrt(sum(float(np.sum(v * v)) for v in go.values()))
+def check_vanishing(gg, k, tol, total):
     assert float(np.linalg.norm(gg[k])) <= tol * total, k
 
 
@@ -48,14 +52,15 @@ def check_fp32(case, gpu, loss, G, label):
     assert rel <= 1e-5
     gg = U.split_tensors(case, gpu["grads"])
     go = U.split_tensors(case, case.flat_grads(G))
-    live = [k for k in go if not vanishing(go, k)]
+    total = grad_norm(go)
+    live = [k for k in go if not vanishing(go, k, total)]
     worst = max((U.rel_l2(gg[k], go[k]), k) for k in live)
     U.log(f"[{label}] worst grad rel L2 {worst[0]:.2e} ({worst[1]})")
     for k in go:
         if k in live:
             assert U.rel_l2(gg[k], go[k]) <= 1e-4, k
         else:
-            check_vanishing(gg, go, k, 1e-4)
+            check_vanishing(gg, k, 1e-4, total)
 
 
 def check_bf16(case, gpu, loss, G, label):
@@ -64,14 +69,15 @@ def check_bf16(case, gpu, loss, G, label):
     assert rel <= 5e-3
     gg = U.split_tensors(case, gpu["grads"])
     go = U.split_tensors(case, case.flat_grads(G))
-    live = [k for k in go if not vanishing(go, k)]
+    total = grad_norm(go)
+    live = [k for k in go if not vanishing(go, k, total)]
     worst = min((U.cosine(gg[k], go[k]), k) for k in live)
     U.log(f"[{label}] worst grad cosine {worst[0]:.6f} ({worst[1]})")
     for k in go:
         if k in live:
             assert U.cosine(gg[k], go[k]) >= 0.999, k
         else:
-            check_vanishing(gg, go, k, 4.5e-2)
+            check_vanishing(gg, k, 4.5e-2, total)
 
 
 @pytest.mark.parametrize("tile", [0, 1, 2, 3])
