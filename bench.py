@@ -126,29 +126,29 @@ def environment(torch) -> dict:
     except OSError:
         env["rocm"] = None
     sclk = None
-    try:
-        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
-        d = json.loads(r.stdout[r.stdout.index("{"):]) if "{" in r.stdout else {}
-        for card in d.values():
-            if isinstance(card, dict):
-                for k, v in card.items():
-                    if "sclk" in k.lower():
-                        sclk = v
-                        break
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            with open(path) as f:
+                lines = f.read().split("\n")
+            sclk = next((ln.split(":", 1)[1].replace("*", "").strip() for ln in lines if ln.endswith("*")), None)
             if sclk:
                 break
-    except Exception:
-        pass
-    if sclk is None:
-        for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
-            try:
-                with open(path) as f:
-                    lines = f.read().split("\n")
-                sclk = next((ln.split(":", 1)[1].replace("*", "").strip() for ln in lines if ln.endswith("*")), None)
+        except OSError:
+            pass
+    # rocm-smi is a Python script started through env: under a profiler whose
+    # library is preloaded into every child, that hop is an exec after GPU
+    # initialisation, so it is only asked when nothing is preloaded.
+    if sclk is None and "rocprof" not in os.environ.get("LD_PRELOAD", ""):
+        try:
+            r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
+            d = json.loads(r.stdout[r.stdout.index("{"):]) if "{" in r.stdout else {}
+            for card in d.values():
+                if isinstance(card, dict):
+                    sclk = next((v for k, v in card.items() if "sclk" in k.lower()), None)
                 if sclk:
                     break
-            except OSError:
-                pass
+        except Exception:
+            pass
     env["sclk"] = sclk
     # device copy bandwidth: 1 GiB read + 1 GiB written, best of 6 copies, HIP events
     n = 1 << 28

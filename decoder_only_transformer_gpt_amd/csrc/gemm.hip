@@ -520,7 +520,7 @@ struct Epilogue<T, Epi::Relu2Bwd> {
 // the plain forms near tanh = +-1; three transcendentals and six other
 // instructions per entry (exp overflow to inf gives R = 0, underflow R = 1).
 // Done on the staged rows: 64 columns of a row sit in 16 lanes (4 each),
-// reduced with shuffles. The row's target id is prefetched with the slab.
+// reduced by DPP row rotations. The row's target id is prefetched with the slab.
 template <typename T>
 struct Epilogue<T, Epi::LMHead> {
   template <int TM, int TN, int WN, bool FOLD = false>
@@ -552,9 +552,7 @@ struct Epilogue<T, Epi::LMHead> {
       const float Rt = d == 0u ? R[0] : (d == 1u ? R[1] : (d == 2u ? R[2] : R[3]));
       if (d < 4u) a.ztgt[m] = fmaf(-2.f * c, Rt, c);
       if (mv) store4_nt(Z + t.off(m, n), q);
-      float sum = 0.25f * sum4;
-#pragma unroll
-      for (int o = 8; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 16);
+      const float sum = row16_sum(0.25f * sum4);  // the row's 64 columns sit in 16 lanes
       if (mv && (lane & 15) == 0) part[(m - mbase) * nparts + (n - nbase) / kLMHeadPartCols] = sum;
     });
   }
