@@ -91,9 +91,11 @@ def kernel_flops_per_launch(tag: str, cfg, B: int, T: int) -> float | None:
     return None
 
 
-def kernel_bytes_per_launch(tag: str, cfg, B: int, T: int, es: int) -> float | None:
-    """Algorithmic HBM bytes of one launch of a memory-bound kernel."""
+def kernel_bytes_per_launch(tag: str, cfg, B: int, T: int, es: int, distinct: int = 0) -> float | None:
+    """Algorithmic HBM bytes of one launch of a memory-bound kernel (distinct:
+    the number of distinct token ids in the batch)."""
     N, C, H, V, F = B * T, cfg.model_dim, cfg.n_head, cfg.vocab_size, cfg.mlp_dim
+    L, QKV = cfg.n_layer, (H + 2) * 128
     # FP8 operand passes: per layer the forward quantises h1, o, h2, a and the
     # backward dy (twice), du, dqkv -- 8 tensors, N (4C + 2F + (H+2)128)
     # elements in all; per launch the mean. amax reads each element (bf16),
@@ -108,7 +110,16 @@ def kernel_bytes_per_launch(tag: str, cfg, B: int, T: int, es: int) -> float | N
          # transposed copies: read and write each (V; then Q, K, dO) once, plus delta's
          # read of O and dO and its fp32 write
          "attn_fwd_transpose": N * 128 * es * 2,
-         "attn_bwd_prep": N * (2 * (2 * H + 1) * 128 * es + 2 * H * 128 * es + 4 * H)}
+         "attn_bwd_prep": N * (2 * (2 * H + 1) * 128 * es + 2 * H * 128 * es + 4 * H),
+         # per row: the V/64 fp32 exp partials and z'_t in, lse and the row loss out, the mean's read
+         "ce_loss": N * (V // 64 * 4 + 16),
+         # the fp32 residual-gradient rows, rstd and the sorted (id, position) pairs in; every
+         # dwte row written once (zeros included); one embedding row per distinct id
+         "embed_bwd": N * (4 * C + 12) + V * C * 4 + distinct * C * es,
+         # two radix passes over (id, position) pairs plus the initial pairs
+         "embed_sort": N * (4 + 8 + 2 * 16),
+         # every weight the dX products read transposed: read and written once
+         "weight_transpose": 2 * es * (L * (QKV * C + C * H * 128 + 2 * F * C) + V * C)}
     return b.get(tag)
 
 
@@ -282,9 +293,10 @@ def main():
     dominant = args.dominant or max(per_tag, key=lambda t: per_tag[t][0])
     if args.kernel_table:
         tot = sum(v[0] for v in per_tag.values())
+        distinct = int(np.unique(idx_np).size)
         for t, (ms, n) in sorted(per_tag.items(), key=lambda kv: -kv[1][0]):
             f = kernel_flops_per_launch(t, cfg, B, T)
-            kb = kernel_bytes_per_launch(t, cfg, B, T, 4 if wl.dtype == "f32" else 2)
+            kb = kernel_bytes_per_launch(t, cfg, B, T, 4 if wl.dtype == "f32" else 2, distinct)
             rate = f"{f * n / ms / 1e9:8.1f} TFLOP/s" if f else (f"{kb * n / ms / 1e6:8.1f} GB/s" if kb else "")
             print(f"[bench] {t:24s} {ms:9.3f} ms {n:4d} launches {100 * ms / tot:5.1f}% {rate}",
                   file=sys.stderr, flush=True)

@@ -5,10 +5,10 @@
 //
 // With y = wte[v] * r_n the norm backward is r_n * dres_n - wte[v] * k_n where
 // k_n = r_n^3 / C * <dres_n, wte[v]>, so
-//   dwte[v] += sum_n r_n * dres_n  -  wte[v] * sum_n k_n,
-// and by linearity sum_n k_n = <sum_n (r_n^3 / C) dres_n, wte[v]>: one pass
-// over the gradient rows accumulates two C-vectors per id, and one dot
-// product per id (or per part of an id's run) gives the k sum.
+//   dwte[v] += sum_n r_n * dres_n  -  wte[v] * sum_n k_n:
+// one pass over the gradient rows accumulates one C-vector and, per lane, the
+// k terms of each id (the embedding row travels with every gradient row), and
+// one wave reduction per id (or per part of an id's run) gives the k sum.
 //
 // Token ids follow a skewed (Zipf-like) law, so a scatter with float atomics
 // would serialise on the frequent rows and make the result depend on timing.
@@ -16,9 +16,12 @@
 // V <= 65536) carrying the token index; (2) one wave per chunk of 32 sorted
 // entries sums each run of equal ids over whole rows, finishing runs that
 // lie inside the chunk and leaving a partial row plus its k sum for the two
-// runs that cross the chunk's edges; (3) one wave per (chunk where a crossing
-// run starts, 512 columns) adds those partials in chunk order. Every sum has a
+// runs that cross the chunk's edges; (3) one block per (chunk where a crossing
+// run starts, 512 columns) adds those partials (four waves over contiguous
+// quarters of the run's chunks, then the quarters in order). Every sum has a
 // fixed order, so the result is bitwise reproducible.
+
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -118,32 +121,63 @@ __global__ __launch_bounds__(kSortChunk) void radix_scatter_kernel(const int32_t
   vout[pos] = vin[i];
 }
 
-// 8 consecutive fp32 values of a gradient row / bf16 or fp32 embedding row.
-DEV void ld8f(const float* p, float (&v)[8]) { load8(p, v); }
+// 8 consecutive values of an embedding row, kept raw while the load is in
+// flight and widened to fp32 when used.
 template <typename T>
-DEV void ld8w(const T* p, float (&v)[8]) { load8(p, v); }
+struct Raw8;
+template <>
+struct Raw8<bf16> {
+  u32x4 r;
+  DEV void load(const bf16* p) { r = ld16(p); }
+  DEV void get(float (&v)[8]) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(r[i] << 16);
+      v[2 * i + 1] = __uint_as_float(r[i] & 0xffff0000u);
+    }
+  }
+};
+template <>
+struct Raw8<float> {
+  u32x4 a, b;
+  DEV void load(const float* p) {
+    a = ld16(p);
+    b = ld16(p + 4);
+  }
+  DEV void get(float (&v)[8]) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] = __uint_as_float(a[i]);
+      v[4 + i] = __uint_as_float(b[i]);
+    }
+  }
+};
 
 // One wave per chunk of kSegChunk sorted entries; lane l holds columns
 // j * 512 + 8l .. +8 of every row (J = ceil(C / 512) groups). For each run of
-// equal ids in the chunk the wave accumulates a1 = sum r_n dres_n and
-// a2 = sum (r_n^3 / C) dres_n; the next entry's row is in flight while the
-// current one is added (two row buffers in alternate roles), and a run's
-// embedding row is requested when the run starts. At a run's end,
-// ks = <a2, wte[v]> (a wave reduction); a run that starts and ends inside the
-// chunk adds a1 - wte[v] * ks to dwte[v] (stores it when the backward
-// overwrites: dwte was zeroed first); a run cut by the chunk's first (last)
-// edge stores a1 and ks in carry slot 0 (1) of the chunk instead (slots of
-// C + 8 floats: the row, then ks).
-template <typename T, int J>
+// equal ids in the chunk the wave accumulates a1 = sum r_n dres_n and, per
+// lane, the run's part of ks = sum_n (r_n^3 / C) <dres_n, wte[v]>. The
+// gradient rows and embedding rows of the next R - 1 entries are in flight
+// while the current one is added (rings of R row buffers, the loop unrolled
+// by R so every slot is a fixed register set; the embedding row is requested
+// for every entry so that no load is conditional, repeats of an id hitting
+// the cache). At a run's end ks is a wave reduction; a run that starts and
+// ends inside the chunk adds a1 - wte[v] * ks to dwte[v] (stores it when the
+// backward overwrites: dwte was zeroed first); a run cut by the chunk's first
+// (last) edge stores a1 and ks in carry slot 0 (1) of the chunk instead
+// (slots of C + 8 floats: the row, then ks).
+template <typename T, int J, int R, bool ACC>
 __global__ __launch_bounds__(256) void embed_seg_kernel(const int32_t* __restrict__ keys,
                                                         const int32_t* __restrict__ vals,
                                                         const float* __restrict__ dres,
                                                         const float* __restrict__ rstd0, const T* __restrict__ wte,
-                                                        int N, int C, int accumulate, float* __restrict__ dwte,
+                                                        int N, int C, float* __restrict__ dwte,
                                                         float* __restrict__ carry) {
   static_assert(kSegChunk <= 64, "one entry per lane");
+  static_assert(R >= 2 && R <= 4, "one to three rows in flight");
   const int lane = threadIdx.x & 63;
-  const int c = blockIdx.x * 4 + (threadIdx.x >> 6);
+  // wave-uniform (scalar) chunk index, so the entry loop and its tests are scalar
+  const int c = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int nseg = (N + kSegChunk - 1) / kSegChunk;
   if (c >= nseg) return;
   const int e0 = c * kSegChunk, e1 = min(N, e0 + kSegChunk), ne = e1 - e0;
@@ -151,74 +185,87 @@ __global__ __launch_bounds__(256) void embed_seg_kernel(const int32_t* __restric
   const int me = e0 + (lane < ne ? lane : 0);
   const int key_l = keys[me];
   const int val_l = vals[me];
-  const float r_l = val_l >= 0 ? rstd0[val_l] : 0.f;
+  const float r_l = rstd0[val_l >= 0 ? val_l : 0];  // unused for an invalid id
   const int prev_key = e0 > 0 ? keys[e0 - 1] : -1;
   const int next_key = e1 < N ? keys[e1] : -1;
+  // retire these loads on every path, so the entry loop's reads of them need
+  // no wait (otherwise its header, reachable before any row request, waits
+  // for every load in flight)
+  wait_vmcnt<0>();
   const float invC = 1.f / (float)C;
-  int col[J];
+  int col[J], colc[J];
   bool cv[J];
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     col[j] = j * 512 + lane * 8;
     cv[j] = col[j] < C;
+    colc[j] = cv[j] ? col[j] : C - 8;
   }
-  float a1[J][8], a2[J][8], ra[J][8], rb[J][8], w[J][8];
-  auto load_row = [&](float (&dst)[J][8], int n) __attribute__((always_inline)) {
+  float a1[J][8], rows[R][J][8], dk = 0.f;
+  Raw8<T> wring[R][J];
+  auto key_at = [&](int e) { return __builtin_amdgcn_readlane(key_l, e); };
+  // entry f's gradient row and embedding row into slot u (lanes past the row
+  // re-read its last 8 columns, so every load is unconditional and the
+  // compiler's waits count exactly the loads issued since)
+  auto request = [&](int f, int u) __attribute__((always_inline)) {
+    const int n = __builtin_amdgcn_readlane(val_l, f);
     const float* row = dres + (int64_t)(n < 0 ? 0 : n) * C;
+    const T* w = wte + (int64_t)key_at(f) * C;
 #pragma unroll
-    for (int j = 0; j < J; ++j)
-      if (cv[j]) ld8f(row + col[j], dst[j]);
-  };
-  auto load_w = [&](int v) __attribute__((always_inline)) {
-#pragma unroll
-    for (int j = 0; j < J; ++j)
-      if (cv[j]) ld8w(wte + (int64_t)v * C + col[j], w[j]);
+    for (int j = 0; j < J; ++j) {
+      load8(row + colc[j], rows[u][j]);
+      wring[u][j].load(w + colc[j]);
+    }
   };
 #pragma unroll
   for (int j = 0; j < J; ++j)
 #pragma unroll
-    for (int q = 0; q < 8; ++q) a1[j][q] = a2[j][q] = 0.f;
-  load_row(ra, __builtin_amdgcn_readlane(val_l, 0));
-  load_w(__builtin_amdgcn_readlane(key_l, 0));
+    for (int q = 0; q < 8; ++q) a1[j][q] = 0.f;
+  // requests past the chunk's last entry repeat that entry: every path then
+  // issues the same loads, and the compiler's waits stay exact
+#pragma unroll
+  for (int u = 0; u + 1 < R; ++u) request(min(u, ne - 1), u);
   int rs = 0;  // run start (entry index within the chunk)
-  // entry e: row in `cur`; the next entry's row goes to `nxt`
-  auto step = [&](int e, float (&cur)[J][8], float (&nxt)[J][8]) __attribute__((always_inline)) {
-    const int v = __builtin_amdgcn_readlane(key_l, e);
+  // entry e sits in slot u = e % R; entry e + R - 1 goes to slot (u + R - 1) % R
+  auto step = [&](int e, auto slot) __attribute__((always_inline)) {
+    constexpr int u = decltype(slot)::value;
+    const int v = key_at(e);
     const int n = __builtin_amdgcn_readlane(val_l, e);
     const float r = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, r_l), e));
-    if (e + 1 < ne) load_row(nxt, __builtin_amdgcn_readlane(val_l, e + 1));
+    request(min(e + R - 1, ne - 1), (u + R - 1) % R);
+    float w[J][8];
+#pragma unroll
+    for (int j = 0; j < J; ++j) wring[u][j].get(w[j]);
     if (n >= 0) {  // an invalid id (the forward raised the device flag) adds nothing
       const float r3 = r * r * r * invC;
+      float d = 0.f;
 #pragma unroll
-      for (int j = 0; j < J; ++j)
+      for (int j = 0; j < J; ++j) {
+        float dj = 0.f;
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
-          a1[j][q] = fmaf(r, cur[j][q], a1[j][q]);
-          a2[j][q] = fmaf(r3, cur[j][q], a2[j][q]);
+          a1[j][q] = fmaf(r, rows[u][j][q], a1[j][q]);
+          dj = fmaf(rows[u][j][q], w[j][q], dj);
         }
+        d += cv[j] ? dj : 0.f;
+      }
+      dk = fmaf(r3, d, dk);
     }
-    const int vn = e + 1 < ne ? __builtin_amdgcn_readlane(key_l, e + 1) : next_key;
+    const int vn = e + 1 < ne ? key_at(e + 1) : next_key;
     if (vn != v || e + 1 == ne) {
       // end of a run inside this chunk (it may continue in the next chunk)
       const bool starts_here = rs > 0 || prev_key != v;
       const bool ends_here = vn != v;
-      float dot = 0.f;
-#pragma unroll
-      for (int j = 0; j < J; ++j)
-        if (cv[j]) {
-#pragma unroll
-          for (int q = 0; q < 8; ++q) dot = fmaf(a2[j][q], w[j][q], dot);
-        }
-      const float ks = wave_sum(dot);
+      const float ks = wave_sum(dk);
       if (starts_here && ends_here) {
         float* drow = dwte + (int64_t)v * C;
 #pragma unroll
         for (int j = 0; j < J; ++j)
           if (cv[j]) {
             float o[8];
-            if (accumulate) ld8f(drow + col[j], o);
+            if constexpr (ACC) load8(drow + col[j], o);
 #pragma unroll
-            for (int q = 0; q < 8; ++q) o[q] = (accumulate ? o[q] : 0.f) + a1[j][q] - w[j][q] * ks;
+            for (int q = 0; q < 8; ++q) o[q] = (ACC ? o[q] : 0.f) + a1[j][q] - w[j][q] * ks;
             store8(drow + col[j], o);
           }
       } else {
@@ -231,17 +278,17 @@ __global__ __launch_bounds__(256) void embed_seg_kernel(const int32_t* __restric
 #pragma unroll
       for (int j = 0; j < J; ++j)
 #pragma unroll
-        for (int q = 0; q < 8; ++q) a1[j][q] = a2[j][q] = 0.f;
+        for (int q = 0; q < 8; ++q) a1[j][q] = 0.f;
+      dk = 0.f;
       rs = e + 1;
-      if (e + 1 < ne) load_w(vn);  // the next run's embedding row
     }
   };
-  int e = 0;
-  for (; e + 1 < ne; e += 2) {
-    step(e, ra, rb);
-    step(e + 1, rb, ra);
+  for (int e = 0; e < ne; e += R) {
+    step(e, std::integral_constant<int, 0>{});
+    if (e + 1 < ne) step(e + 1, std::integral_constant<int, 1 % R>{});
+    if constexpr (R > 2) if (e + 2 < ne) step(e + 2, std::integral_constant<int, 2 % R>{});
+    if constexpr (R > 3) if (e + 3 < ne) step(e + 3, std::integral_constant<int, 3 % R>{});
   }
-  if (e < ne) step(e, ra, rb);
 }
 
 // Last sorted position holding id v, searching from position `from` (whose
@@ -256,20 +303,24 @@ DEV int segment_last(const int32_t* __restrict__ keys, int N, int from, int v) {
   return lo;
 }
 
-// One wave per (chunk in which a boundary-crossing run starts, 512 columns):
-// adds that run's partial rows (slot 1 of its first chunk, then slot 0 of
-// every later chunk it reaches, in chunk order) and their k sums, and adds
+// One block of four waves per (chunk in which a boundary-crossing run starts,
+// 512 columns): adds that run's partial rows (slot 1 of its first chunk and
+// slot 0 of every later chunk it reaches) and their k sums, and adds
 // a1 - wte[v] * ks to dwte[v]. The chunk holding the run's last entry is found
-// by a binary search, so the partials are summed over a known range with
-// many loads in flight.
+// by a binary search; each wave sums a contiguous quarter of the slot-0 range
+// (eight rows in flight per lane), and wave 0 adds slot 1 and the quarters in
+// order, so the frequent ids' long runs are summed by four waves in a fixed
+// order.
 template <typename T>
 __global__ __launch_bounds__(256) void seg_fixup_kernel(const int32_t* __restrict__ keys, int N, int C, int nchunks,
                                                         const T* __restrict__ wte, const float* __restrict__ carry,
                                                         float* __restrict__ dwte) {
+  __shared__ float part[4][512];
+  __shared__ float kpart[4];
   const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int ngrp = (C + 511) / 512;
-  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int c = item / ngrp, grp = item % ngrp;
+  const int c = blockIdx.x / ngrp, grp = blockIdx.x % ngrp;
   if (c >= nchunks) return;
   const int e0 = c * kSegChunk, e1 = min(N, e0 + kSegChunk);
   const int last = e1 - 1;
@@ -279,37 +330,54 @@ __global__ __launch_bounds__(256) void seg_fixup_kernel(const int32_t* __restric
   // did the run start inside this chunk?
   if (keys[e0] == v && e0 > 0 && keys[e0 - 1] == v) return;  // began earlier: owned by an earlier chunk
   const int cend = min(nchunks - 1, segment_last(keys, N, e1, v) / kSegChunk);
-  // k sums: slot 1 of chunk c, then slot 0 of chunks c+1..cend, lane-strided
-  // partial sums combined by a fixed butterfly
+  const int n = cend - c;  // slot-0 partials: chunks c+1 .. cend
+  const int q0 = c + 1 + (int)((int64_t)n * wave / 4), q1 = c + 1 + (int)((int64_t)n * (wave + 1) / 4);
+  // this wave's k sums: lane-strided partial sums combined by a fixed butterfly
   float ks = 0.f;
-  for (int cc = c + 1 + lane; cc <= cend; cc += 64) ks += carry[((int64_t)cc * 2 + 0) * (C + 8) + C];
-  ks = wave_sum(ks) + carry[((int64_t)c * 2 + 1) * (C + 8) + C];
+  for (int cc = q0 + lane; cc < q1; cc += 64) ks += carry[((int64_t)cc * 2 + 0) * (C + 8) + C];
+  ks = wave_sum(ks);
   const int col = grp * 512 + lane * 8;
-  if (col >= C) return;
+  const bool valid = col < C;
+  const int colc = valid ? col : C - 8;  // lanes past the row re-read its last 8 columns
   float acc[8];
-  load8(carry + ((int64_t)c * 2 + 1) * (C + 8) + col, acc);
-  int cc = c + 1;
-  for (; cc + 7 <= cend; cc += 8) {
+#pragma unroll
+  for (int q = 0; q < 8; ++q) acc[q] = 0.f;
+  int cc = q0;
+  for (; cc + 7 < q1; cc += 8) {
     float x[8][8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) load8(carry + ((int64_t)(cc + u) * 2 + 0) * (C + 8) + col, x[u]);
+    for (int u = 0; u < 8; ++u) load8(carry + ((int64_t)(cc + u) * 2 + 0) * (C + 8) + colc, x[u]);
 #pragma unroll
     for (int u = 0; u < 8; ++u)
 #pragma unroll
       for (int q = 0; q < 8; ++q) acc[q] += x[u][q];
   }
-  for (; cc <= cend; ++cc) {
+  for (; cc < q1; ++cc) {
     float x[8];
-    load8(carry + ((int64_t)cc * 2 + 0) * (C + 8) + col, x);
+    load8(carry + ((int64_t)cc * 2 + 0) * (C + 8) + colc, x);
 #pragma unroll
     for (int q = 0; q < 8; ++q) acc[q] += x[q];
   }
-  float w[8], o[8];
-  load8(wte + (int64_t)v * C + col, w);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) part[wave][lane * 8 + q] = acc[q];
+  if (lane == 0) kpart[wave] = ks;
+  __syncthreads();
+  if (wave != 0 || !valid) return;
+  float tot[8];
+  load8(carry + ((int64_t)c * 2 + 1) * (C + 8) + col, tot);
+  float kt = carry[((int64_t)c * 2 + 1) * (C + 8) + C];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) tot[q] += part[w][lane * 8 + q];
+    kt += kpart[w];
+  }
+  float wv[8], o[8];
+  load8(wte + (int64_t)v * C + col, wv);
   float* drow = dwte + (int64_t)v * C + col;
   load8(drow, o);
 #pragma unroll
-  for (int q = 0; q < 8; ++q) o[q] += acc[q] - w[q] * ks;
+  for (int q = 0; q < 8; ++q) o[q] += tot[q] - wv[q] * kt;
   store8(drow, o);
 }
 
@@ -416,8 +484,16 @@ size_t embed_bwd_carry_elems(int N, int C) {
 
 template <typename T, int J>
 hipError_t embed_seg(const EmbedBwdArgs& a, int nseg, hipStream_t s) {
-  hipLaunchKernelGGL((embed_seg_kernel<T, J>), dim3((nseg + 3) / 4), dim3(256), 0, s, a.keys_a, a.vals_a, a.dres,
-                     a.rstd0, (const T*)a.wte, a.N, a.C, a.accumulate, a.dwte, a.carry);
+  // rows in flight per wave: about J * ((8 + 4 or 8) R + 16) registers must
+  // stay within ~220 (two waves per SIMD)
+  constexpr int per = sizeof(T) == 2 ? 12 : 16;
+  constexpr int R = (220 / J - 16) / per >= 4 ? 4 : (220 / J - 16) / per >= 3 ? 3 : 2;
+  if (a.accumulate)
+    hipLaunchKernelGGL((embed_seg_kernel<T, J, R, true>), dim3((nseg + 3) / 4), dim3(256), 0, s, a.keys_a, a.vals_a,
+                       a.dres, a.rstd0, (const T*)a.wte, a.N, a.C, a.dwte, a.carry);
+  else
+    hipLaunchKernelGGL((embed_seg_kernel<T, J, R, false>), dim3((nseg + 3) / 4), dim3(256), 0, s, a.keys_a, a.vals_a,
+                       a.dres, a.rstd0, (const T*)a.wte, a.N, a.C, a.dwte, a.carry);
   return hipGetLastError();
 }
 
@@ -448,12 +524,12 @@ hipError_t launch_embed_bwd(const EmbedBwdArgs& a, hipStream_t s) {
   const int nseg = (N + kSegChunk - 1) / kSegChunk;
   e = a.dtype == 1 ? embed_seg_j<bf16>(a, nseg, s) : embed_seg_j<float>(a, nseg, s);
   if (e != hipSuccess) return e;
-  const int waves = nseg * ((C + 511) / 512);
+  const int items = nseg * ((C + 511) / 512);  // one block per (chunk, 512 columns)
   if (a.dtype == 1)
-    hipLaunchKernelGGL(seg_fixup_kernel<bf16>, dim3((waves + 3) / 4), dim3(256), 0, s, a.keys_a, N, C, nseg,
+    hipLaunchKernelGGL(seg_fixup_kernel<bf16>, dim3(items), dim3(256), 0, s, a.keys_a, N, C, nseg,
                        (const bf16*)a.wte, a.carry, a.dwte);
   else
-    hipLaunchKernelGGL(seg_fixup_kernel<float>, dim3((waves + 3) / 4), dim3(256), 0, s, a.keys_a, N, C, nseg,
+    hipLaunchKernelGGL(seg_fixup_kernel<float>, dim3(items), dim3(256), 0, s, a.keys_a, N, C, nseg,
                        (const float*)a.wte, a.carry, a.dwte);
   return hipGetLastError();
 }
