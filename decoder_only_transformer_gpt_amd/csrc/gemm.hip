@@ -604,7 +604,7 @@ struct Epilogue<T, Epi::GradF32> {
 // once: rows in one 256-byte bank line differ in their row offset, rows RP
 // apart in the chunk position. Rows past M read as zero (buffer record count).
 // One explicit vmcnt wait and one barrier per K tile.
-template <int BM, int BN, int NSTAGE, int OCC, Epi E, int NW = 4, int BK = 32, int ES = 2>
+template <int BM, int BN, int NSTAGE, int OCC, Epi E, int NW = 4, int BK = 32, int ES = 2, bool PP = false>
 __global__ __launch_bounds__(NW * 64, OCC) void gemm_nt_lds_kernel(GemmArgs args) {
   using T = bf16;  // output (epilogue) type
   constexpr int ROWB = BK * ES, CH = ROWB / 16, RP = 256 / ROWB, RPK = 1024 / ROWB;
@@ -705,6 +705,89 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm_nt_lds_kernel(GemmArgs args
   for (int ks = 0; ks < KSTEPS; ++ks) fo[ks] = l32 * ROWB + ((ks * 2 + g) ^ swz) * 16;
 
   issue(0, st0);
+  if constexpr (PP) {
+    // Ping-pong: the waves of rows 0..WM-1 (group 0, one per SIMD) and of
+    // rows WM.. (group 1) take turns. A K tile is NP parts of two MFMA
+    // k-steps, and every wave runs the same sequence per tile: read the
+    // fragments of a part, multiply them, one phase each, a barrier starting
+    // every phase. Group 1 runs one phase behind group 0, so in every phase
+    // one wave per SIMD feeds the matrix core while the other waits on LDS.
+    // A wave requests its part of tile m + NSTAGE - 1 when it starts reading
+    // tile m (that stage was last read by group 1 in the phase before group 0
+    // starts tile m) and waits for its part of tile m + 1 before its last
+    // phase of tile m, which ends before group 0 reads tile m + 1.
+    static_assert(NW == 8 && KSTEPS % 2 == 0, "two groups of four waves, k-step pairs");
+    constexpr int NP = KSTEPS / 2;
+    u32x4 af[2][TM], bfr[2][TN];
+    auto readf = [&](const char* cur, int part) __attribute__((always_inline)) {
+      const char* As = cur + wm * WM * ROWB;
+      const char* Bs = cur + BM * ROWB + wn * WN * ROWB;
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int ks = part * 2 + k;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) af[k][i] = ld16(As + i * 32 * ROWB + fo[ks]);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) bfr[k][j] = ld16(Bs + j * 32 * ROWB + fo[ks]);
+      }
+    };
+    auto mma = [&]() __attribute__((always_inline)) {
+      if constexpr (ES == 2) {
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) acc[i][j] = mfma16(bfr[k][j], af[k][i], acc[i][j], (T*)nullptr);
+      } else {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j) acc[i][j] = mfma_fp8(bfr[0][j], bfr[1][j], af[0][i], af[1][i], acc[i][j]);
+      }
+    };
+    auto phase = [&]() __attribute__((always_inline)) {
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    constexpr int YOUNG = NLOAD * (NSTAGE - 2);  // loads of the tiles after the one awaited
+    auto tile_pp = [&](int m, const char* cur, char* nxt) __attribute__((always_inline)) {
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        phase();
+        if (p == 0) issue(min(m + NSTAGE - 1, nk - 1), nxt);  // past the end: a harmless re-read into a free stage
+        readf(cur, p);
+        if (p == NP - 1) wait_vmcnt<YOUNG>();  // this wave's part of tile m + 1 has landed
+        phase();
+        mma();
+      }
+    };
+    if (NSTAGE >= 3) issue(min(1, nk - 1), st1);
+    if (NSTAGE == 4) issue(min(2, nk - 1), st2);
+    wait_vmcnt<YOUNG>();   // tile 0
+    if (wm == 1) phase();  // group 1 starts one phase later
+    if constexpr (NSTAGE == 4) {
+      for (int m = 0; m < nk; m += 4) {
+        tile_pp(m, st0, st3);
+        if (m + 1 < nk) tile_pp(m + 1, st1, st0);
+        if (m + 2 < nk) tile_pp(m + 2, st2, st1);
+        if (m + 3 < nk) tile_pp(m + 3, st3, st2);
+      }
+    } else if constexpr (NSTAGE == 3) {
+      for (int m = 0; m < nk; m += 3) {
+        tile_pp(m, st0, st2);
+        if (m + 1 < nk) tile_pp(m + 1, st1, st0);
+        if (m + 2 < nk) tile_pp(m + 2, st2, st1);
+      }
+    } else {
+      for (int m = 0; m < nk; m += 2) {
+        tile_pp(m, st0, st1);
+        if (m + 1 < nk) tile_pp(m + 1, st1, st0);
+      }
+    }
+    if (wm == 0) phase();  // and group 0 ends one phase later
+  } else {
   if (NSTAGE >= 3) issue(max(0, min(1, nk - 1)), st1);
   if (NSTAGE == 4) issue(max(0, min(2, nk - 1)), st2);
   // tile kt sits in stage kt % NSTAGE; the loop is unrolled by NSTAGE so
@@ -781,6 +864,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm_nt_lds_kernel(GemmArgs args
       tile(kt, st0, st1);
       if (kt + 1 < nk) tile(kt + 1, st1, st0);
     }
+  }
   }
   __builtin_amdgcn_s_waitcnt(0);  // no LDS-direct load may land during the epilogue
   __syncthreads();
@@ -1047,14 +1131,14 @@ hipError_t launch_layout(const GemmArgs& a, hipStream_t s) {
   }
 }
 
-template <int BM, int BN, int NSTAGE, int OCC, Epi E, int NW = 4, int BK = 32, int ES = 2>
+template <int BM, int BN, int NSTAGE, int OCC, Epi E, int NW = 4, int BK = 32, int ES = 2, bool PP = false>
 hipError_t launch_nt_lds(const GemmArgs& a, hipStream_t s) {
   if (a.K % BK != 0) return hipErrorInvalidValue;
   const int splits = E == Epi::GradF32 ? a.splits : 1;
   const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   GemmArgs g = a;
   g.splits = splits;
-  hipLaunchKernelGGL((gemm_nt_lds_kernel<BM, BN, NSTAGE, OCC, E, NW, BK, ES>), dim3(tiles * splits * a.batch),
+  hipLaunchKernelGGL((gemm_nt_lds_kernel<BM, BN, NSTAGE, OCC, E, NW, BK, ES, PP>), dim3(tiles * splits * a.batch),
                      dim3(NW * 64), 0, s, g);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || splits <= 1) return err;
@@ -1085,18 +1169,19 @@ hipError_t launch_tn_lds(const GemmArgs& a, hipStream_t s) {
 template <Epi E>
 hipError_t launch_nt_lds_tile(const GemmArgs& a, hipStream_t s) {
   const int64_t t256 = (int64_t)((a.M + 255) / 256) * ((a.N + 255) / 256) * a.batch;
-  // tile: 1 = 256x256 (8 waves, two per SIMD; 64-wide K tiles when K allows),
+  // tile: 1 = 256x256 (8 waves, two per SIMD; 64-wide K tiles, with the
+  // ping-pong main loop, when K allows),
   // 2 = 256x128 (4 waves, two CTAs per CU), 3 = 128x128. By shape: 256x256
   // when there are at least two tiles per CU, else 128x128.
   int tile = a.tile;
   if (tile == 0) tile = (t256 >= 512 && a.N % 256 == 0) ? 1 : 3;
   if constexpr (E == Epi::LMHead) {  // exp-sum partials per 64 columns: BN a multiple of 128
-    if (tile == 1 && a.K % 64 == 0) return launch_nt_lds<256, 256, 2, 1, E, 8, 64>(a, s);
+    if (tile == 1 && a.K % 64 == 0) return launch_nt_lds<256, 256, 2, 1, E, 8, 64, 2, true>(a, s);
     if (tile == 1) return launch_nt_lds<256, 256, 4, 1, E>(a, s);
     if (tile == 2) return launch_nt_lds<256, 128, 3, 2, E>(a, s);
     return launch_nt_lds<128, 256, 4, 1, E>(a, s);
   } else {
-    if (tile == 1 && a.K % 64 == 0) return launch_nt_lds<256, 256, 2, 1, E, 8, 64>(a, s);
+    if (tile == 1 && a.K % 64 == 0) return launch_nt_lds<256, 256, 2, 1, E, 8, 64, 2, true>(a, s);
     if (tile == 1) return launch_nt_lds<256, 256, 4, 1, E, 8>(a, s);
     if (tile == 2) return launch_nt_lds<256, 128, 3, 2, E>(a, s);
     return launch_nt_lds<128, 128, 4, 1, E>(a, s);
