@@ -904,7 +904,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm_nt_lds_kernel(GemmArgs args
 // transposing read delivers (rows 4g+e, then 8+4g+e, of each 16-row step),
 // the same for both operands. Pipeline and epilogue as in the NT kernel;
 // split-K slices are whole K tiles.
-template <int BM, int BN, int NSTAGE, int OCC, Epi E, int NW = 4, int BK = 32>
+template <int BM, int BN, int NSTAGE, int OCC, Epi E, int NW = 4, int BK = 32, bool PP = false>
 __global__ __launch_bounds__(NW * 64, OCC) void gemm_tn_lds_kernel(GemmArgs args) {
   using T = bf16;
   constexpr int KK = BK / 16;                   // MFMA k-steps per K tile
@@ -1004,6 +1004,71 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm_tn_lds_kernel(GemmArgs args
   issue(0, st0);
   if (NSTAGE >= 3) issue(max(0, min(1, nk - 1)), st1);
   if (NSTAGE == 4) issue(max(0, min(2, nk - 1)), st2);
+  if constexpr (PP) {
+    // Ping-pong as in the k-contiguous kernel: the two row-half wave groups
+    // (one wave per SIMD each) alternate between reading a K tile's
+    // fragments (transposing reads) and multiplying them, group 1 one phase
+    // behind, a barrier starting every phase. A wave requests its part of
+    // tile m + NSTAGE - 1 when it starts reading tile m and waits for its
+    // part of tile m + 1 before it multiplies tile m.
+    static_assert(NW == 8, "two groups of four waves");
+    constexpr int YOUNG = NLOAD * (NSTAGE - 2);
+    u32x4 af[KK][TM], bfr[KK][TN];
+    auto readf = [&](const char* cur) __attribute__((always_inline)) {
+      const char* As = cur;
+      const char* Bs = cur + BK * ROWA;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) af[kk][i] = frag(As + kk * 16 * ROWA, ofa[i], ROWA);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) bfr[kk][j] = frag(Bs + kk * 16 * ROWB, ofb[j], ROWB);
+      }
+    };
+    auto mma = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j) acc[i][j] = mfma16(bfr[kk][j], af[kk][i], acc[i][j], (T*)nullptr);
+    };
+    auto phase = [&]() __attribute__((always_inline)) {
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    auto tile_pp = [&](int m, const char* cur, char* nxt) __attribute__((always_inline)) {
+      phase();
+      issue(min(m + NSTAGE - 1, nk - 1), nxt);  // past the end: a harmless re-read into a free stage
+      readf(cur);
+      wait_vmcnt<YOUNG>();  // this wave's part of tile m + 1 has landed
+      phase();
+      mma();
+    };
+    wait_vmcnt<YOUNG>();   // tile 0
+    if (wm == 1) phase();  // group 1 starts one phase later
+    if constexpr (NSTAGE == 4) {
+      for (int m = 0; m < nk; m += 4) {
+        tile_pp(m, st0, st3);
+        if (m + 1 < nk) tile_pp(m + 1, st1, st0);
+        if (m + 2 < nk) tile_pp(m + 2, st2, st1);
+        if (m + 3 < nk) tile_pp(m + 3, st3, st2);
+      }
+    } else if constexpr (NSTAGE == 3) {
+      for (int m = 0; m < nk; m += 3) {
+        tile_pp(m, st0, st2);
+        if (m + 1 < nk) tile_pp(m + 1, st1, st0);
+        if (m + 2 < nk) tile_pp(m + 2, st2, st1);
+      }
+    } else {
+      for (int m = 0; m < nk; m += 2) {
+        tile_pp(m, st0, st1);
+        if (m + 1 < nk) tile_pp(m + 1, st1, st0);
+      }
+    }
+    if (wm == 0) phase();  // and group 0 ends one phase later
+  } else {
   auto tile = [&](int kt, const char* cur, char* nxt) {
     constexpr int YOUNG = NLOAD * (NSTAGE - 2);
     __builtin_amdgcn_s_waitcnt(((YOUNG >> 4) << 14) | (0x7 << 4) | (0xF << 8) | (YOUNG & 15));
@@ -1060,6 +1125,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm_tn_lds_kernel(GemmArgs args
       tile(kt, st0, st1);
       if (kt + 1 < nk) tile(kt + 1, st1, st0);
     }
+  }
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -1150,12 +1216,12 @@ hipError_t launch_nt_lds(const GemmArgs& a, hipStream_t s) {
 }
 
 
-template <int BM, int BN, int NSTAGE, int OCC, Epi E, int NW = 4, int BK = 32>
+template <int BM, int BN, int NSTAGE, int OCC, Epi E, int NW = 4, int BK = 32, bool PP = false>
 hipError_t launch_tn_lds(const GemmArgs& a, hipStream_t s) {
   // split-K slices are whole K tiles and K itself a whole number of them
   if (a.K % BK != 0) return hipErrorInvalidValue;
   const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_tn_lds_kernel<BM, BN, NSTAGE, OCC, E, NW, BK>), dim3(tiles * a.splits), dim3(NW * 64), 0,
+  hipLaunchKernelGGL((gemm_tn_lds_kernel<BM, BN, NSTAGE, OCC, E, NW, BK, PP>), dim3(tiles * a.splits), dim3(NW * 64), 0,
                      s, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.splits <= 1) return err;
@@ -1236,7 +1302,8 @@ hipError_t launch_typed(Epi epi, const GemmArgs& a, hipStream_t s) {
       const int64_t t256 = (int64_t)((a.M + 255) / 256) * ((a.N + 255) / 256) * a.splits;
       int tile = a.tile;
       if (tile == 0) tile = (t256 >= 256 && a.M % 256 == 0 && a.N % 256 == 0) ? 1 : 2;
-      if (tile == 1 && a.M % 256 == 0 && a.N % 256 == 0) return launch_tn_lds<256, 256, 4, 1, Epi::GradF32, 8>(a, s);
+      if (tile == 1 && a.M % 256 == 0 && a.N % 256 == 0)
+        return launch_tn_lds<256, 256, 4, 1, Epi::GradF32, 8, 32, true>(a, s);
       return launch_tn_lds<128, 128, 4, 1, Epi::GradF32>(a, s);
     }
   }
