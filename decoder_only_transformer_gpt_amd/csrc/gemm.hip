@@ -1264,7 +1264,7 @@ hipError_t launch_nt_fp8_tile(const GemmArgs& a, hipStream_t s) {
   const int64_t t256 = (int64_t)((a.M + 255) / 256) * ((a.N + 255) / 256) * splits;
   int tile = a.tile;
   if (tile == 0) tile = (t256 >= 512 && a.N % 256 == 0) ? 1 : 3;
-  if (tile == 1) return launch_nt_lds<256, 256, 2, 1, E, 8, 128, 1>(a, s);
+  if (tile == 1) return launch_nt_lds<256, 256, 2, 1, E, 8, 128, 1, true>(a, s);
   if (tile == 2) return launch_nt_lds<256, 128, 3, 2, E, 4, 64, 1>(a, s);
   return launch_nt_lds<128, 128, 4, 1, E, 4, 64, 1>(a, s);
 }
