@@ -33,6 +33,15 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kGroupM = 4;  // row panels per tile group (NT kernel)
 
+// Blocks are dealt round-robin to the 8 XCDs (block b runs on XCD b mod 8).
+// Map block b to an item index so that each XCD takes one contiguous run of
+// items: XCD x's j-th block gets item start(x) + j, the runs sized by how
+// many blocks each XCD receives (any grid size; a bijection on [0, nb)).
+DEV int xcd_contiguous(int b, int nb) {
+  const int x = b & 7, j = b >> 3, q = nb >> 3, r = nb & 7;
+  return x * q + (x < r ? x : r) + j;
+}
+
 template <typename T>
 struct TileK {
   static constexpr int V = Vec<T>::N;        // elements per 16 bytes
@@ -638,7 +647,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm_nt_lds_kernel(GemmArgs args
   // (row-major order would stream every column panel of B once per row panel).
   int item = blockIdx.x;
   const int nb = gridDim.x;
-  if ((nb & 7) == 0) item = (item & 7) * (nb >> 3) + (item >> 3);
+  item = xcd_contiguous(item, nb);
   // batched products: product-major, then split-K slices, then tiles
   const int bz = item / (tiles * args.splits);
   item -= bz * tiles * args.splits;
@@ -934,7 +943,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm_tn_lds_kernel(GemmArgs args
   // same K window together and share it in that XCD's L2.
   int item = blockIdx.x;
   const int nb = gridDim.x;
-  if ((nb & 7) == 0) item = (item & 7) * (nb >> 3) + (item >> 3);
+  item = xcd_contiguous(item, nb);
   const int split = item / tiles, bid = item % tiles;
   const int m0 = (bid / tiles_n) * BM, n0 = (bid % tiles_n) * BN;
   const int kper = ((K + args.splits - 1) / args.splits + BK - 1) / BK * BK;
