@@ -91,9 +91,11 @@ def kernel_flops_per_launch(tag: str, cfg, B: int, T: int) -> float | None:
     return None
 
 
-def kernel_bytes_per_launch(tag: str, cfg, B: int, T: int, es: int, distinct: int = 0) -> float | None:
+def kernel_bytes_per_launch(tag: str, cfg, B: int, T: int, es: int, distinct: int = 0,
+                            fp8: bool = False) -> float | None:
     """Algorithmic HBM bytes of one launch of a memory-bound kernel (distinct:
-    the number of distinct token ids in the batch)."""
+    the number of distinct token ids in the batch; fp8: an FP8 model, whose
+    layer weights get e4m3 copies instead of bf16 transposes)."""
     N, C, H, V, F = B * T, cfg.model_dim, cfg.n_head, cfg.vocab_size, cfg.mlp_dim
     L, QKV = cfg.n_layer, (H + 2) * 128
     # FP8 operand passes: per layer the forward quantises h1, o, h2, a and the
@@ -118,8 +120,9 @@ def kernel_bytes_per_launch(tag: str, cfg, B: int, T: int, es: int, distinct: in
          "embed_bwd": N * (4 * C + 12) + V * C * 4 + distinct * C * es,
          # two radix passes over (id, position) pairs plus the initial pairs
          "embed_sort": N * (4 + 8 + 2 * 16),
-         # every weight the dX products read transposed: read and written once
-         "weight_transpose": 2 * es * (L * (QKV * C + C * H * 128 + 2 * F * C) + V * C)}
+         # every weight the dX products read transposed (FP8 models: the LM head only):
+         # read and written once
+         "weight_transpose": 2 * es * ((0 if fp8 else L * (QKV * C + C * H * 128 + 2 * F * C)) + V * C)}
     return b.get(tag)
 
 
@@ -296,7 +299,7 @@ def main():
         distinct = int(np.unique(idx_np).size)
         for t, (ms, n) in sorted(per_tag.items(), key=lambda kv: -kv[1][0]):
             f = kernel_flops_per_launch(t, cfg, B, T)
-            kb = kernel_bytes_per_launch(t, cfg, B, T, 4 if wl.dtype == "f32" else 2, distinct)
+            kb = kernel_bytes_per_launch(t, cfg, B, T, 4 if wl.dtype == "f32" else 2, distinct, wl.dtype == "fp8")
             rate = f"{f * n / ms / 1e9:8.1f} TFLOP/s" if f else (f"{kb * n / ms / 1e6:8.1f} GB/s" if kb else "")
             print(f"[bench] {t:24s} {ms:9.3f} ms {n:4d} launches {100 * ms / tot:5.1f}% {rate}",
                   file=sys.stderr, flush=True)

@@ -736,8 +736,13 @@ template <int NST, bool AMAX>
 __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void attn_fwd_bf16_kernel(const bf16* __restrict__ qkv, int T_,
                                                                               int H, int W, bf16* __restrict__ o,
                                                                               float* __restrict__ lse, float* amax) {
-  static_assert(NST == 2 || NST == 4, "two or four stages");
-  __shared__ __attribute__((aligned(1024))) KvStage st[NST];
+  static_assert(NST == 2, "two stages");
+  // one object per stage, and the loops unrolled by two so that each step
+  // names its stages statically: with one runtime-indexed array the compiler
+  // cannot tell the stages' direct-to-LDS loads apart, and it waited for the
+  // next tile's loads (issued at the start of the step) before reading V
+  __shared__ __attribute__((aligned(1024))) KvStage st0;
+  __shared__ __attribute__((aligned(1024))) KvStage st1;
   const int nqb = (T_ + 127) / 128;
   int b, r;
   xcd_row_map(blockIdx.x, gridDim.x / (nqb * H), nqb * H, b, r);
@@ -772,13 +777,29 @@ __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void attn_fwd_bf16_kernel(co
     tile_issue(uniform_rsrc(kp, rows * (int)ld_b), s.k, vo, wave);
     tile_issue(uniform_rsrc(kp + D, rows * (int)ld_b), s.v, vo, wave);
   };
-  auto step = [&](int t, auto masked) {
-    wait_vmcnt<(NST - 2) * 8>();  // this wave's part of tile t has landed
+  // tile t sits in stage t % 2 (st0 for even t)
+  auto step = [&](int t, const KvStage& cur, KvStage& nxt, auto masked) __attribute__((always_inline)) {
+    wait_vmcnt<0>();  // this wave's part of tile t has landed
     __builtin_amdgcn_s_barrier();
-    issue(min(t + NST - 1, nt - 1), st[(t + NST - 1) % NST]);
+    issue(min(t + 1, nt - 1), nxt);
     const int k0 = (t0 + t) * 64;
     if (k0 > qw + 31 || k0 + 63 <= qw - Wl) return;  // the tile misses every query's band
-    fwd_tile<decltype(masked)::value>(st[t % NST], rf, tf, qf, acc, rsum, sl2, sh2, k0 + 4 * g - q, Wl);
+    fwd_tile<decltype(masked)::value>(cur, rf, tf, qf, acc, rsum, sl2, sh2, k0 + 4 * g - q, Wl);
+  };
+  // tiles [t, end) with the stages alternating, two tiles per iteration
+  auto run = [&](int& t, int end, auto masked) __attribute__((always_inline)) {
+    if ((t & 1) && t < end) {
+      step(t, st1, st0, masked);
+      ++t;
+    }
+    for (; t + 1 < end; t += 2) {
+      step(t, st0, st1, masked);
+      step(t + 1, st1, st0, masked);
+    }
+    if (t < end) {
+      step(t, st0, st1, masked);
+      ++t;
+    }
   };
   // Key tiles (ascending) fall into three runs: tiles that cross the far
   // edge of some query's window, tiles inside the band of every query of the
@@ -788,12 +809,11 @@ __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void attn_fwd_bf16_kernel(co
   const int kt_lo = lo_num >= 0 ? lo_num / 64 + 1 : 0;
   const int t_a = min(nt, max(0, kt_lo - t0));
   const int t_b = min(nt, max(t_a, 2 * qb - t0));  // key tiles up to 2qb - 1 precede every query
-#pragma unroll
-  for (int i = 0; i < NST - 1; ++i) issue(min(i, nt - 1), st[i]);
+  issue(0, st0);
   int t = 0;
-  for (; t < t_a; ++t) step(t, std::true_type{});
-  for (; t < t_b; ++t) step(t, std::false_type{});
-  for (; t < nt; ++t) step(t, std::true_type{});
+  run(t, t_a, std::true_type{});
+  run(t, t_b, std::false_type{});
+  run(t, nt, std::true_type{});
   wait_vmcnt<0>();
   rsum += __shfl_xor(rsum, 32, 64);
   [[maybe_unused]] float mx = 0.f;
@@ -861,8 +881,13 @@ __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void attn_dq_bf16_kernel(con
                                                                              const float* __restrict__ lse,
                                                                              float* __restrict__ delta, int T_,
                                                                              int H, int W, bf16* __restrict__ dqkv) {
-  static_assert(NST == 2 || NST == 4, "two or four stages");
-  __shared__ __attribute__((aligned(1024))) KvStage st[NST];
+  static_assert(NST == 2, "two stages");
+  // one object per stage, and the loops unrolled by two so that each step
+  // names its stages statically: with one runtime-indexed array the compiler
+  // cannot tell the stages' direct-to-LDS loads apart, and it waited for the
+  // next tile's loads (issued at the start of the step) before reading V
+  __shared__ __attribute__((aligned(1024))) KvStage st0;
+  __shared__ __attribute__((aligned(1024))) KvStage st1;
   const int nqb = (T_ + 127) / 128;
   int b, r;
   xcd_row_map(blockIdx.x, gridDim.x / (nqb * H), nqb * H, b, r);
@@ -917,13 +942,29 @@ __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void attn_dq_bf16_kernel(con
     tile_issue(uniform_rsrc(kp, rows * (int)ld_b), s.k, vo, wave);
     tile_issue(uniform_rsrc(kp + D, rows * (int)ld_b), s.v, vo, wave);
   };
-  auto step = [&](int t, auto masked) {
-    wait_vmcnt<(NST - 2) * 8>();  // this wave's part of tile t has landed
+  // tile t sits in stage t % 2 (st0 for even t)
+  auto step = [&](int t, const KvStage& cur, KvStage& nxt, auto masked) __attribute__((always_inline)) {
+    wait_vmcnt<0>();  // this wave's part of tile t has landed
     __builtin_amdgcn_s_barrier();
-    issue(min(t + NST - 1, nt - 1), st[(t + NST - 1) % NST]);
+    issue(min(t + 1, nt - 1), nxt);
     const int k0 = (t0 + t) * 64;
     if (k0 > qw + 31 || k0 + 63 <= qw - Wl) return;  // the tile misses every query's band
-    dq_tile<decltype(masked)::value>(st[t % NST], rf, tf, qf, df, acc, sl2, l2, dlt, k0 + 4 * g - q, Wl);
+    dq_tile<decltype(masked)::value>(cur, rf, tf, qf, df, acc, sl2, l2, dlt, k0 + 4 * g - q, Wl);
+  };
+  // tiles [t, end) with the stages alternating, two tiles per iteration
+  auto run = [&](int& t, int end, auto masked) __attribute__((always_inline)) {
+    if ((t & 1) && t < end) {
+      step(t, st1, st0, masked);
+      ++t;
+    }
+    for (; t + 1 < end; t += 2) {
+      step(t, st0, st1, masked);
+      step(t + 1, st1, st0, masked);
+    }
+    if (t < end) {
+      step(t, st0, st1, masked);
+      ++t;
+    }
   };
   // Key tiles (ascending) fall into three runs: tiles that cross the far
   // edge of some query's window, tiles inside the band of every query of the
@@ -933,12 +974,11 @@ __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void attn_dq_bf16_kernel(con
   const int kt_lo = lo_num >= 0 ? lo_num / 64 + 1 : 0;
   const int t_a = min(nt, max(0, kt_lo - t0));
   const int t_b = min(nt, max(t_a, 2 * qb - t0));  // key tiles up to 2qb - 1 precede every query
-#pragma unroll
-  for (int i = 0; i < NST - 1; ++i) issue(min(i, nt - 1), st[i]);
+  issue(0, st0);
   int t = 0;
-  for (; t < t_a; ++t) step(t, std::true_type{});
-  for (; t < t_b; ++t) step(t, std::false_type{});
-  for (; t < nt; ++t) step(t, std::true_type{});
+  run(t, t_a, std::true_type{});
+  run(t, t_b, std::false_type{});
+  run(t, nt, std::true_type{});
   wait_vmcnt<0>();
   if (qv) {
     bf16* outp = dqkv + ((int64_t)b * T_ + q) * ld + h * D;
