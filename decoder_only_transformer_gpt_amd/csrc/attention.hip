@@ -1090,7 +1090,15 @@ __global__ __launch_bounds__(256, 1) void attn_dkv_bf16_kernel(const bf16* __res
                                                                const float* __restrict__ delta, int T_, int H,
                                                                int W, int hsplit, bf16* __restrict__ dqkv,
                                                                float* __restrict__ part) {
-  __shared__ __attribute__((aligned(1024))) DkvStage st[4];
+  // four stage objects: the unmasked main loop names them statically (the
+  // compiler then tells their direct-to-LDS loads apart and folds each stage's
+  // base into the read offsets); the short masked runs and the ends of the
+  // unmasked run select them at run time
+  __shared__ __attribute__((aligned(1024))) DkvStage s0;
+  __shared__ __attribute__((aligned(1024))) DkvStage s1;
+  __shared__ __attribute__((aligned(1024))) DkvStage s2;
+  __shared__ __attribute__((aligned(1024))) DkvStage s3;
+  auto st = [&](int q) -> DkvStage& { return q == 0 ? s0 : q == 1 ? s1 : q == 2 ? s2 : s3; };
   const int nkb = (T_ + 127) / 128;
   int bh, kb;
   xcd_level_map(blockIdx.x, gridDim.x / nkb, bh, kb);  // key block 0 (most query tiles) first
@@ -1138,13 +1146,21 @@ __global__ __launch_bounds__(256, 1) void attn_dkv_bf16_kernel(const bf16* __res
   // Step it consumes stage it % 4 and requests step it + 3 into stage
   // (it + 3) % 4, last read in step it - 1, which every wave finished before
   // this step's barrier.
+  auto step_s = [&](int it, const DkvStage& cur, DkvStage& nxt, auto masked) __attribute__((always_inline)) {
+    wait_vmcnt<2 * 10>();  // this wave's part of step it's tiles has landed
+    __builtin_amdgcn_s_barrier();
+    issue(min(it + 3, total - 1), nxt);
+    const int q0 = (nqt - 1 - it / Hs) * 64;
+    if (q0 + 63 < kw || q0 - (kw + 31) >= Wl) return;  // the tile misses every key's band
+    dkv_tile<decltype(masked)::value>(cur, wave, rf, tf, kf, vf, adk, adv, sl2, q0 + 4 * g - key, Wl, g);
+  };
   auto step = [&](int it, auto masked) {
     wait_vmcnt<2 * 10>();  // this wave's part of step it's tiles has landed
     __builtin_amdgcn_s_barrier();
-    issue(min(it + 3, total - 1), st[(it + 3) & 3]);
+    issue(min(it + 3, total - 1), st((it + 3) & 3));
     const int q0 = (nqt - 1 - it / Hs) * 64;
     if (q0 + 63 < kw || q0 - (kw + 31) >= Wl) return;  // the tile misses every key's band
-    dkv_tile<decltype(masked)::value>(st[it & 3], wave, rf, tf, kf, vf, adk, adv, sl2, q0 + 4 * g - key, Wl, g);
+    dkv_tile<decltype(masked)::value>(st(it & 3), wave, rf, tf, kf, vf, adk, adv, sl2, q0 + 4 * g - key, Wl, g);
   };
   // Query tiles (descending) fall into three runs: tiles that cross the far
   // edge of some key's window, tiles inside the band of every key of the
@@ -1156,11 +1172,18 @@ __global__ __launch_bounds__(256, 1) void attn_dkv_bf16_kernel(const bf16* __res
   const int qt_hi = min(nqt - 1, hi_num >= 0 ? hi_num / 64 : -1);
   const int it_a = min(total, max(0, (nqt - 1 - qt_hi) * Hs));
   const int it_b = min(total, max(it_a, (nqt - (2 * kb + 2)) * Hs));
-  issue(0, st[0]);
-  issue(min(1, total - 1), st[1]);
-  issue(min(2, total - 1), st[2]);
+  issue(0, s0);
+  issue(min(1, total - 1), s1);
+  issue(min(2, total - 1), s2);
   int it = 0;
   for (; it < it_a; ++it) step(it, std::true_type{});
+  for (; it < it_b && (it & 3); ++it) step(it, std::false_type{});
+  for (; it + 3 < it_b; it += 4) {
+    step_s(it, s0, s3, std::false_type{});
+    step_s(it + 1, s1, s0, std::false_type{});
+    step_s(it + 2, s2, s1, std::false_type{});
+    step_s(it + 3, s3, s2, std::false_type{});
+  }
   for (; it < it_b; ++it) step(it, std::false_type{});
   for (; it < total; ++it) step(it, std::true_type{});
   wait_vmcnt<0>();
