@@ -104,15 +104,24 @@ __global__ __launch_bounds__(1024) void mean_kernel(const float* __restrict__ x,
 
 // One wave per row: the target-column fix of q, the row scale r, and the
 // final-norm output row h scaled by r (bf16 or fp32 like h).
-template <typename T>
+template <typename T, int J>
 __global__ __launch_bounds__(256) void ce_grad_prep_kernel(T* __restrict__ q, const float* __restrict__ lse,
                                                            const float* __restrict__ ztgt,
                                                            const int32_t* __restrict__ targets, int N, int V,
                                                            float c, float scale, const T* __restrict__ h, int C,
                                                            T* __restrict__ hs, float* __restrict__ rscale) {
   const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int row = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   if (row >= N) return;
+  // the row of h is requested before r is known (J groups of 512 columns;
+  // lanes past the row re-read its last 8 columns, so no load is conditional)
+  const int64_t off = (int64_t)row * C;
+  float v[J][8];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int k = j * 512 + lane * 8;
+    load8(h + off + (k < C ? k : C - 8), v[j]);
+  }
   const float s = expf(lse[row] - c);
   const float r = scale / s;
   if (lane == 0) {
@@ -124,13 +133,12 @@ __global__ __launch_bounds__(256) void ce_grad_prep_kernel(T* __restrict__ q, co
       q[(int64_t)row * V + t] = from_f32<T>((1.f - u * u) * (e - s));
     }
   }
-  const int64_t off = (int64_t)row * C;
-  for (int k = lane * 8; k < C; k += 64 * 8) {
-    float v[8];
-    load8(h + off + k, v);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] *= r;
-    store8(hs + off + k, v);
+  for (int j = 0; j < J; ++j) {
+    const int k = j * 512 + lane * 8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[j][e] *= r;
+    if (k < C) store8(hs + off + k, v[j]);
   }
 }
 
@@ -147,18 +155,36 @@ hipError_t launch_ce_loss(const float* part, int nparts, const float* ztgt, cons
   return hipGetLastError();
 }
 
+template <typename T, int J>
+hipError_t ce_grad_prep_j(void* q, const float* lse, const float* ztgt, const int32_t* targets, int N, int V,
+                          float softcap, float scale, const void* h, int C, void* hs, float* rscale, hipStream_t s) {
+  hipLaunchKernelGGL((ce_grad_prep_kernel<T, J>), dim3((N + 3) / 4), dim3(256), 0, s, (T*)q, lse, ztgt, targets, N, V,
+                     softcap, scale, (const T*)h, C, (T*)hs, rscale);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t ce_grad_prep_t(void* q, const float* lse, const float* ztgt, const int32_t* targets, int N, int V,
+                          float softcap, float scale, const void* h, int C, void* hs, float* rscale, hipStream_t s) {
+  switch ((C + 511) / 512) {  // 512-column groups per row
+    case 1: return ce_grad_prep_j<T, 1>(q, lse, ztgt, targets, N, V, softcap, scale, h, C, hs, rscale, s);
+    case 2: return ce_grad_prep_j<T, 2>(q, lse, ztgt, targets, N, V, softcap, scale, h, C, hs, rscale, s);
+    case 3: return ce_grad_prep_j<T, 3>(q, lse, ztgt, targets, N, V, softcap, scale, h, C, hs, rscale, s);
+    case 4: return ce_grad_prep_j<T, 4>(q, lse, ztgt, targets, N, V, softcap, scale, h, C, hs, rscale, s);
+    case 5: return ce_grad_prep_j<T, 5>(q, lse, ztgt, targets, N, V, softcap, scale, h, C, hs, rscale, s);
+    case 6: return ce_grad_prep_j<T, 6>(q, lse, ztgt, targets, N, V, softcap, scale, h, C, hs, rscale, s);
+    case 7: return ce_grad_prep_j<T, 7>(q, lse, ztgt, targets, N, V, softcap, scale, h, C, hs, rscale, s);
+    case 8: return ce_grad_prep_j<T, 8>(q, lse, ztgt, targets, N, V, softcap, scale, h, C, hs, rscale, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 hipError_t launch_ce_grad_prep(int dtype, void* q, const float* lse, const float* ztgt, const int32_t* targets, int N,
                                int V, float softcap, float scale, const void* h, int C, void* hs, float* rscale,
                                hipStream_t s) {
-  if (C % 8 != 0) return hipErrorInvalidValue;
-  const dim3 grid((N + 3) / 4);
-  if (dtype == 1)
-    hipLaunchKernelGGL(ce_grad_prep_kernel<bf16>, grid, dim3(256), 0, s, (bf16*)q, lse, ztgt, targets, N, V, softcap,
-                       scale, (const bf16*)h, C, (bf16*)hs, rscale);
-  else
-    hipLaunchKernelGGL(ce_grad_prep_kernel<float>, grid, dim3(256), 0, s, (float*)q, lse, ztgt, targets, N, V,
-                       softcap, scale, (const float*)h, C, (float*)hs, rscale);
-  return hipGetLastError();
+  if (C % 8 != 0 || C < 8 || C > 4096) return hipErrorInvalidValue;
+  return dtype == 1 ? ce_grad_prep_t<bf16>(q, lse, ztgt, targets, N, V, softcap, scale, h, C, hs, rscale, s)
+                    : ce_grad_prep_t<float>(q, lse, ztgt, targets, N, V, softcap, scale, h, C, hs, rscale, s);
 }
 
 }  // namespace gk
