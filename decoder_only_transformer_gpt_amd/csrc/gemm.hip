@@ -334,6 +334,45 @@ DEV void staged_store(f32x16 (&acc)[TM][TN], float* st, int mbase, int nbase, in
   }
 }
 
+// staged_store for bf16 outputs that depend on the accumulator alone:
+// f(m, n, v) maps the 4 consecutive columns n .. n+3 of row m in place while
+// they are still in accumulator order, the results are rounded to bf16
+// before they go to the slab (a
+// [32][WN+8] bf16 region: half the LDS bytes of the fp32 slab), and each lane
+// then hands 8 consecutive bf16 of a row to out(m, n, 16 bytes). The values
+// and their single rounding are those of staged_store + a bf16 store.
+template <int TM, int TN, int WN>
+constexpr bool kBf16Slab = WN % 16 == 0 && 64 % (WN / 8) == 0 && 32 % (64 / (WN / 8)) == 0;
+
+template <int TM, int TN, int WN, class F, class Out>
+DEV void staged_store_bf16(f32x16 (&acc)[TM][TN], float* stf, int mbase, int nbase, int lane, F f, Out out) {
+  static_assert(kBf16Slab<TM, TN, WN>, "slab rows of whole 16-byte chunks");
+  constexpr int PB = WN + 8, LPR = WN / 8, RPP = 64 / LPR;
+  bf16* st = reinterpret_cast<bf16*>(stf);
+  const int g = lane >> 5, l32 = lane & 31;
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk) {
+        float v[4] = {acc[i][j][blk * 4], acc[i][j][blk * 4 + 1], acc[i][j][blk * 4 + 2], acc[i][j][blk * 4 + 3]};
+        f(mbase + i * 32 + l32, nbase + j * 32 + blk * 8 + g * 4, v);
+        u32x2 pk;
+        pk[0] = pack_bf16x2(v[0], v[1]);
+        pk[1] = pack_bf16x2(v[2], v[3]);
+        *reinterpret_cast<u32x2*>(st + l32 * PB + j * 32 + blk * 8 + g * 4) = pk;
+      }
+    slab_sync();
+#pragma unroll
+    for (int r0 = 0; r0 < 32; r0 += RPP) {
+      const int row = r0 + lane / LPR, col = (lane % LPR) * 8;
+      out(mbase + i * 32 + row, nbase + col, ld16(st + row * PB + col));
+    }
+    slab_sync();
+  }
+}
+
 // staged_store with a prefetch: pre(m, n) is issued for every (row, 4
 // columns) item before the accumulators go to LDS, so those global loads are
 // in flight during the staging; op(m, n, v, pre_value). ALL: every slab's
@@ -409,6 +448,15 @@ struct Epilogue<T, Epi::Store> {
   static DEV void run(const GemmArgs& a, f32x16 (&acc)[TM][TN], float* lds, int mbase, int nbase, int lane) {
     const TileAddr<TM, WN> t(a.ldc, mbase, nbase, a.M, a.N);
     T* C = reinterpret_cast<T*>(a.C) + t.base;
+    if constexpr (sizeof(T) == 2 && kBf16Slab<TM, TN, WN>) {
+      if (a.N % 8 == 0) {  // 8-column items never straddle the last column
+        staged_store_bf16<TM, TN, WN>(acc, lds, mbase, nbase, lane, [](int, int, float (&)[4]) {},
+                                      [&](int m, int n, u32x4 v) {
+                                        if (t.in(m, n)) st16_nt(C + t.off(m, n), v);
+                                      });
+        return;
+      }
+    }
     staged_store<TM, TN, WN>(acc, lds, mbase, nbase, lane, [&](int m, int n, float (&v)[4]) {
       if (t.in(m, n)) store4_nt(C + t.off(m, n), v);
     });
@@ -456,6 +504,25 @@ struct Epilogue<T, Epi::Relu2> {
     const TileAddr<TM, WN> t(a.ldc, mbase, nbase, a.M, a.N);
     T* A2 = reinterpret_cast<T*>(a.C) + t.base;
     float mx = 0.f;
+    if constexpr (sizeof(T) == 2 && kBf16Slab<TM, TN, WN>) {
+      if (a.N % 8 == 0) {
+        staged_store_bf16<TM, TN, WN>(acc, lds, mbase, nbase, lane,
+                                      [&](int m, int n, float (&v)[4]) {
+                                        for (int r = 0; r < 4; ++r) {
+                                          const float p = fmaxf(v[r], 0.f);
+                                          v[r] = p * p;
+                                        }
+                                        if (FOLD && t.in(m, n))
+                                          for (int r = 0; r < 4; ++r) mx = fmaxf(mx, v[r]);
+                                      },
+                                      [&](int m, int n, u32x4 v) {
+                                        if (t.in(m, n)) st16_nt(A2 + t.off(m, n), v);
+                                      });
+        if constexpr (FOLD)
+          if (a.amax_out) amax_fold_block<T>(mx, a.amax_out);
+        return;
+      }
+    }
     staged_store<TM, TN, WN>(acc, lds, mbase, nbase, lane, [&](int m, int n, float (&v)[4]) {
       if (t.in(m, n)) {
         float s[4];
