@@ -420,6 +420,51 @@ DEV void staged_store_pre(f32x16 (&acc)[TM][TN], float* st, int mbase, int nbase
   }
 }
 
+// staged_store_pre for bf16 outputs, 8 columns per lane: pre(m, n) returns
+// the 16 bytes of operand at (m, n .. n+7) (every item requested up front,
+// all landed before the first store), op(m, n, v[8], pre_value). Half the
+// load and store instructions of the 4-column form for the same bytes.
+template <int TM, int TN, int WN>
+constexpr bool kPre8 = WN % 32 == 0 && 64 % (WN / 8) == 0 && 32 % (64 / (WN / 8)) == 0;
+
+template <int TM, int TN, int WN, class Pre, class Op>
+DEV void staged_store_pre8(f32x16 (&acc)[TM][TN], float* st, int mbase, int nbase, int lane, Pre pre, Op op) {
+  static_assert(kPre8<TM, TN, WN>, "8-column items");
+  constexpr int P = WN + 4, LPR = WN / 8, RPP = 64 / LPR, NP = 32 / RPP;
+  const int g = lane >> 5, l32 = lane & 31;
+  const int prow = lane / LPR, pcol = (lane % LPR) * 8;
+  u32x4 pall[TM][NP];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int q = 0; q < NP; ++q) pall[i][q] = pre(mbase + i * 32 + q * RPP + prow, nbase + pcol);
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk) {
+        float v[4] = {acc[i][j][blk * 4], acc[i][j][blk * 4 + 1], acc[i][j][blk * 4 + 2], acc[i][j][blk * 4 + 3]};
+        store4(st + l32 * P + j * 32 + blk * 8 + g * 4, v);
+      }
+    if (i == 0) wait_vmcnt<0>();  // as in staged_store_pre (ALL)
+    slab_sync();
+#pragma unroll
+    for (int q = 0; q < NP; ++q) {
+      const int row = q * RPP + prow;
+      float v[8], w[4];
+      load4(st + row * P + pcol, w);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = w[e];
+      load4(st + row * P + pcol + 4, w);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[4 + e] = w[e];
+      op(mbase + i * 32 + row, nbase + pcol, v, pall[i][q]);
+    }
+    slab_sync();
+  }
+}
+
 // Output addressing of a wave's (TM*32) x WN tile at (mbase, nbase) in a
 // row-major matrix of leading dimension ld: one 64-bit base per wave and
 // 32-bit element offsets from it (the launcher bounds ld by 2^22 so that the
@@ -468,6 +513,27 @@ struct Epilogue<T, Epi::Residual> {
   template <int TM, int TN, int WN, bool FOLD = false>
   static DEV void run(const GemmArgs& a, f32x16 (&acc)[TM][TN], float* lds, int mbase, int nbase, int lane) {
     T* C = reinterpret_cast<T*>(a.C);
+    if constexpr (sizeof(T) == 2 && kPre8<TM, TN, WN>) {
+      if (a.N % 8 == 0) {
+        auto pre8 = [&](int m, int n) {
+          u32x4 r = {0u, 0u, 0u, 0u};
+          if (m < a.M && n < a.N) r = ld16_nt(C + (int64_t)m * a.ldc + n);
+          return r;
+        };
+        staged_store_pre8<TM, TN, WN>(acc, lds, mbase, nbase, lane, pre8,
+                                      [&](int m, int n, float (&v)[8], u32x4 r) {
+          if (m < a.M && n < a.N) {
+            u32x4 o;
+#pragma unroll
+            for (int h = 0; h < 4; ++h)
+              o[h] = pack_bf16x2(__uint_as_float(r[h] << 16) + v[2 * h],
+                                 __uint_as_float(r[h] & 0xffff0000u) + v[2 * h + 1]);
+            st16_nt(C + (int64_t)m * a.ldc + n, o);
+          }
+        });
+        return;
+      }
+    }
     // bf16: the residual is requested for the whole tile up front (raw, 4
     // values in two dwords); fp32 loads it per item
     auto pre = [&](int m, int n) {
