@@ -334,6 +334,13 @@ DEV void staged_store(f32x16 (&acc)[TM][TN], float* st, int mbase, int nbase, in
   }
 }
 
+// 8-column (16-byte) items of a bf16 output (and, for the residual, of its
+// operand C): the columns, the row pitch and the base keep every item whole
+// and 16-byte aligned
+DEV bool row16_aligned(const GemmArgs& a) {
+  return a.N % 8 == 0 && a.ldc % 8 == 0 && (reinterpret_cast<uintptr_t>(a.C) & 15) == 0;
+}
+
 // staged_store for bf16 outputs that depend on the accumulator alone:
 // f(m, n, v) maps the 4 consecutive columns n .. n+3 of row m in place while
 // they are still in accumulator order, the results are rounded to bf16
@@ -494,7 +501,7 @@ struct Epilogue<T, Epi::Store> {
     const TileAddr<TM, WN> t(a.ldc, mbase, nbase, a.M, a.N);
     T* C = reinterpret_cast<T*>(a.C) + t.base;
     if constexpr (sizeof(T) == 2 && kBf16Slab<TM, TN, WN>) {
-      if (a.N % 8 == 0) {  // 8-column items never straddle the last column
+      if (row16_aligned(a)) {  // 8-column items: whole 16-byte chunks inside the rows
         staged_store_bf16<TM, TN, WN>(acc, lds, mbase, nbase, lane, [](int, int, float (&)[4]) {},
                                       [&](int m, int n, u32x4 v) {
                                         if (t.in(m, n)) st16_nt(C + t.off(m, n), v);
@@ -514,7 +521,7 @@ struct Epilogue<T, Epi::Residual> {
   static DEV void run(const GemmArgs& a, f32x16 (&acc)[TM][TN], float* lds, int mbase, int nbase, int lane) {
     T* C = reinterpret_cast<T*>(a.C);
     if constexpr (sizeof(T) == 2 && kPre8<TM, TN, WN>) {
-      if (a.N % 8 == 0) {
+      if (row16_aligned(a)) {
         auto pre8 = [&](int m, int n) {
           u32x4 r = {0u, 0u, 0u, 0u};
           if (m < a.M && n < a.N) r = ld16_nt(C + (int64_t)m * a.ldc + n);
@@ -571,7 +578,7 @@ struct Epilogue<T, Epi::Relu2> {
     T* A2 = reinterpret_cast<T*>(a.C) + t.base;
     float mx = 0.f;
     if constexpr (sizeof(T) == 2 && kBf16Slab<TM, TN, WN>) {
-      if (a.N % 8 == 0) {
+      if (row16_aligned(a)) {
         staged_store_bf16<TM, TN, WN>(acc, lds, mbase, nbase, lane,
                                       [&](int m, int n, float (&v)[4]) {
                                         for (int r = 0; r < 4; ++r) {

@@ -131,6 +131,9 @@ def _codes(torch, vals_bits, ldT=16):
     (999, 1536, 1024, "bf16", 0, 1), (999, 1536, 1024, "bf16", 1, 1), (999, 1536, 1024, "bf16", 2, 1),
     (999, 1536, 1024, "bf16", 3, 1), (300, 260, 384, "f32", 3, 1), (1536, 768, 4096, "f32", 1, 4),
     (640, 512, 2048, "f32", 0, 3), (33, 64, 128, "bf16", 0, 1),
+    # bf16 output with N % 8 == 4: the epilogue's 4-column form (8-column
+    # items would straddle the last column)
+    (300, 260, 384, "bf16", 3, 1), (999, 1540, 1024, "bf16", 1, 1),
     # more 256x256 tiles than compute units, an odd K tile count
     (4500, 4224, 384, "bf16", 1, 1), (2100, 8448, 640, "f32", 1, 1)])
 def test_fp8_matmul_on_identical_codes(M, N, K, out, tile, splits):
