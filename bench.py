@@ -107,7 +107,9 @@ def kernel_bytes_per_launch(tag: str, cfg, B: int, T: int, es: int, distinct: in
          "embed_rmsnorm": N * (4 + 2 * C * es + 4), "rmsnorm": N * (2 * C * es + 4),
          "rope_qknorm": N * (2 * (H + 1) * 128 * es + 4 * (H + 1)),
          "ce_bwd": N * (2 * C * es + 16 + es),  # lse, z'_t, target, r; the target entry; h in, r*h out
-         "rmsnorm_bwd": N * (2 * C * es + 8 * C + C * es + 4),
+         # dy and y in, the fp32 residual gradient in and out, rstd (the kernel also
+         # writes the bf16 copy of that gradient the next GEMMs read: not counted)
+         "rmsnorm_bwd": N * (2 * C * es + 8 * C + 4),
          "rope_qknorm_bwd": N * (3 * (H + 1) * 128 * es + 4 * (H + 1)),
          # transposed copies: read and write each (V; then Q, K, dO) once, plus delta's
          # read of O and dO and its fp32 write

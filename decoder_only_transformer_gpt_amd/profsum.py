@@ -40,7 +40,10 @@ CSRC = os.path.join(HERE, "csrc")
 # Source files whose text decides each kernel tag's code.
 TAG_SOURCES = {
     "attn": ["attention.hip"], "gemm": ["gemm.hip"], "rmsnorm": ["norm.hip"], "rope": ["norm.hip"],
-    "embed_rmsnorm": ["norm.hip"], "ce": ["ce.hip"], "embed_bwd": ["embed_bwd.hip"], "weight": ["norm.hip"],
+    "embed_rmsnorm": ["norm.hip"], "ce": ["ce.hip"], "embed_bwd": ["embed_bwd.hip"],
+    "embed_sort": ["embed_bwd.hip"], "weight": ["norm.hip"], "fp8": ["fp8.hip"], "x0_mix": ["resid.hip"],
+    "ve_add": ["resid.hip"], "ve_bwd": ["resid.hip", "embed_bwd.hip"], "opt_adamw": ["optim.hip"],
+    "opt_muon": ["optim.hip", "gemm.hip"],
 }
 COMMON = ["common.h", "kernels.h"]
 
