@@ -107,9 +107,9 @@ def kernel_bytes_per_launch(tag: str, cfg, B: int, T: int, es: int, distinct: in
          "embed_rmsnorm": N * (4 + 2 * C * es + 4), "rmsnorm": N * (2 * C * es + 4),
          "rope_qknorm": N * (2 * (H + 1) * 128 * es + 4 * (H + 1)),
          "ce_bwd": N * (2 * C * es + 16 + es),  # lse, z'_t, target, r; the target entry; h in, r*h out
-         # dy and y in, the fp32 residual gradient in and out, rstd (the kernel also
-         # writes the bf16 copy of that gradient the next GEMMs read: not counted)
-         "rmsnorm_bwd": N * (2 * C * es + 8 * C + 4),
+         # dy and y in, the residual-stream gradient in and out (kept in the
+         # activation dtype by default), rstd
+         "rmsnorm_bwd": N * (4 * C * es + 4),
          "rope_qknorm_bwd": N * (3 * (H + 1) * 128 * es + 4 * (H + 1)),
          # transposed copies: read and write each (V; then Q, K, dO) once, plus delta's
          # read of O and dO and its fp32 write
@@ -117,9 +117,10 @@ def kernel_bytes_per_launch(tag: str, cfg, B: int, T: int, es: int, distinct: in
          "attn_bwd_prep": N * (2 * (2 * H + 1) * 128 * es + 2 * H * 128 * es + 4 * H),
          # per row: the V/64 fp32 exp partials and z'_t in, lse and the row loss out, the mean's read
          "ce_loss": N * (V // 64 * 4 + 16),
-         # the fp32 residual-gradient rows, rstd and the sorted (id, position) pairs in; every
-         # dwte row written once (zeros included); one embedding row per distinct id
-         "embed_bwd": N * (4 * C + 12) + V * C * 4 + distinct * C * es,
+         # the residual-gradient rows (activation dtype), rstd and the sorted (id, position)
+         # pairs in; every dwte row written once (zeros included); one embedding row per
+         # distinct id
+         "embed_bwd": N * (C * es + 12) + V * C * 4 + distinct * C * es,
          # two radix passes over (id, position) pairs plus the initial pairs
          "embed_sort": N * (4 + 8 + 2 * 16),
          # every weight the dX products read transposed (FP8 models: the LM head only):
@@ -233,6 +234,8 @@ def main():
                     help="also time the optimiser step (Muon + AdamW) after the timed region; reported apart")
     ap.add_argument("--gemm-tile", type=int, default=0, choices=[0, 1, 2, 3],
                     help="force one GEMM tile variant (0 = by shape)")
+    ap.add_argument("--resid-grad-f32", action="store_true",
+                    help="keep the residual-stream gradient in fp32 (default for bf16 models: bf16)")
     ap.add_argument("--kernel-table", action="store_true", help="print per-tag timings to stderr")
     ap.add_argument("--dominant", default=None,
                     help="kernel tag to report in the roofline (skips the one-step-per-tag scan)")
@@ -262,6 +265,8 @@ def main():
     m = GPT(cfg, GPT.params_from_numpy(storage, cfg), B, T)
     if args.gemm_tile:
         m.set_gemm_tile(args.gemm_tile)
+    if args.resid_grad_f32:
+        m.set_resid_grad_f32(True)
     idx = torch.from_numpy(idx_np).cuda()
     tgt = torch.from_numpy(tgt_np).cuda()
     print(f"[bench] workload {wl.name}: B={B} T={T} params={_lib.gpt_param_count(cfg)} "

@@ -25,6 +25,7 @@ GPT_BF16 = 1
 GPT_FP8_E4M3 = 2
 GPT_OPT_GEMM_TILE = 1
 GPT_OPT_DKV_HSPLIT = 2
+GPT_OPT_RESID_GRAD = 3
 
 
 class gpt_config(ctypes.Structure):

@@ -166,10 +166,10 @@ struct Raw8<float> {
 // backward overwrites: dwte was zeroed first); a run cut by the chunk's first
 // (last) edge stores a1 and ks in carry slot 0 (1) of the chunk instead
 // (slots of C + 8 floats: the row, then ks).
-template <typename T, int J, int R, bool ACC>
+template <typename T, typename DR, int J, int R, bool ACC>
 __global__ __launch_bounds__(256) void embed_seg_kernel(const int32_t* __restrict__ keys,
                                                         const int32_t* __restrict__ vals,
-                                                        const float* __restrict__ dres,
+                                                        const DR* __restrict__ dres,
                                                         const float* __restrict__ rstd0, const T* __restrict__ wte,
                                                         int N, int C, float* __restrict__ dwte,
                                                         float* __restrict__ carry) {
@@ -209,7 +209,7 @@ __global__ __launch_bounds__(256) void embed_seg_kernel(const int32_t* __restric
   // compiler's waits count exactly the loads issued since)
   auto request = [&](int f, int u) __attribute__((always_inline)) {
     const int n = __builtin_amdgcn_readlane(val_l, f);
-    const float* row = dres + (int64_t)(n < 0 ? 0 : n) * C;
+    const DR* row = dres + (int64_t)(n < 0 ? 0 : n) * C;
     const T* w = wte + (int64_t)key_at(f) * C;
 #pragma unroll
     for (int j = 0; j < J; ++j) {
@@ -488,12 +488,22 @@ hipError_t embed_seg(const EmbedBwdArgs& a, int nseg, hipStream_t s) {
   // stay within ~220 (two waves per SIMD)
   constexpr int per = sizeof(T) == 2 ? 12 : 16;
   constexpr int R = (220 / J - 16) / per >= 4 ? 4 : (220 / J - 16) / per >= 3 ? 3 : 2;
-  if (a.accumulate)
-    hipLaunchKernelGGL((embed_seg_kernel<T, J, R, true>), dim3((nseg + 3) / 4), dim3(256), 0, s, a.keys_a, a.vals_a,
-                       a.dres, a.rstd0, (const T*)a.wte, a.N, a.C, a.dwte, a.carry);
-  else
-    hipLaunchKernelGGL((embed_seg_kernel<T, J, R, false>), dim3((nseg + 3) / 4), dim3(256), 0, s, a.keys_a, a.vals_a,
-                       a.dres, a.rstd0, (const T*)a.wte, a.N, a.C, a.dwte, a.carry);
+  const dim3 grid((nseg + 3) / 4);
+  if (a.dres) {  // fp32 gradient rows
+    if (a.accumulate)
+      hipLaunchKernelGGL((embed_seg_kernel<T, float, J, R, true>), grid, dim3(256), 0, s, a.keys_a, a.vals_a, a.dres,
+                         a.rstd0, (const T*)a.wte, a.N, a.C, a.dwte, a.carry);
+    else
+      hipLaunchKernelGGL((embed_seg_kernel<T, float, J, R, false>), grid, dim3(256), 0, s, a.keys_a, a.vals_a, a.dres,
+                         a.rstd0, (const T*)a.wte, a.N, a.C, a.dwte, a.carry);
+  } else {  // gradient rows in the activation dtype
+    if (a.accumulate)
+      hipLaunchKernelGGL((embed_seg_kernel<T, T, J, R, true>), grid, dim3(256), 0, s, a.keys_a, a.vals_a,
+                         (const T*)a.dres_lp, a.rstd0, (const T*)a.wte, a.N, a.C, a.dwte, a.carry);
+    else
+      hipLaunchKernelGGL((embed_seg_kernel<T, T, J, R, false>), grid, dim3(256), 0, s, a.keys_a, a.vals_a,
+                         (const T*)a.dres_lp, a.rstd0, (const T*)a.wte, a.N, a.C, a.dwte, a.carry);
+  }
   return hipGetLastError();
 }
 
@@ -514,7 +524,7 @@ hipError_t embed_seg_j(const EmbedBwdArgs& a, int nseg, hipStream_t s) {
 
 hipError_t launch_embed_bwd(const EmbedBwdArgs& a, hipStream_t s) {
   const int N = a.N, C = a.C;
-  if (C % 8 != 0 || C > 4096) return hipErrorInvalidValue;
+  if (C % 8 != 0 || C > 4096 || (!a.dres && !a.dres_lp)) return hipErrorInvalidValue;
   hipError_t e;
   if (!a.accumulate) {
     if ((e = launch_fill_f32(a.dwte, 0.f, (int64_t)a.V * C, s)) != hipSuccess) return e;

@@ -313,6 +313,7 @@ struct gpt_model {
   int64_t off_resid = -1, off_x0lam = -1, off_gates = -1;
   int gemm_tile = 0;      // GPT_OPT_GEMM_TILE
   int dkv_hsplit = 0;     // GPT_OPT_DKV_HSPLIT
+  int resid_grad_f32 = 0; // GPT_OPT_RESID_GRAD
   int ntdesc = 0;
   int64_t wt_tiles = 0;   // total 64x64 tiles of the batched weight transpose
   int nqdesc = 0;                         // FP8: layer-weight quantisation table
@@ -904,13 +905,18 @@ gpt_status gpt_backward(gpt_model* m, float dloss, int32_t accumulate, void* str
   // dz = r_n q (target entries fixed in place), never formed: dW_lm = q^T (r h)
   // with the scaled copy of h in dh's buffer (read before dX overwrites it),
   // dX_lm = q W_lm with rows scaled by r in the final norm's backward
+  // the residual-stream gradient: fp32 in dres for fp32 models, by option, and
+  // with residual scalars (their gradients are dot products of this gradient
+  // with the stream, which its bf16 rounding moves measurably); else in the
+  // activation dtype in dres_lp alone
+  float* const dres32 = (dt == GPT_F32 || m->resid_grad_f32 || c.x0_lambdas) ? wsp<float>(m, L.dres) : nullptr;
   RUN(K_CE_BWD, return gk::launch_ce_grad_prep(dt, m->ws + L.logits, wsp<float>(m, L.lse_ce), wsp<float>(m, L.ztgt),
                                                m->targets, N, V, c.logit_softcap, dloss / (float)N, m->ws + L.hf, C,
                                                m->ws + L.dh, wsp<float>(m, L.ce_rscale), stream););
   TRY(dw(K_GEMM_LM_DW, m->ws + L.logits, V, m->ws + L.dh, C, V, C, m->off_lm));
   TRY(dx(K_GEMM_LM_DX, gk::Epi::Store, m->ws + L.logits, V, m->off_lm, C, V, m->ws + L.dh, nullptr));
   RUN(K_RMSNORM_BWD, return gk::launch_rmsnorm_bwd(dt, m->ws + L.dh, m->ws + L.hf, wsp<float>(m, L.rstdf), N, C, 0,
-                                                   wsp<float>(m, L.dres), m->ws + L.dres_lp, stream,
+                                                   dres32, m->ws + L.dres_lp, stream,
                                                    wsp<float>(m, L.ce_rscale)););
   for (int l = c.n_layer - 1; l >= 0; --l) {
     // MLP
@@ -930,7 +936,7 @@ gpt_status gpt_backward(gpt_model* m, float dloss, int32_t accumulate, void* str
       TRY(dx(K_GEMM_W1_DX, gk::Epi::Store, m->ws + L.du, F, m->off_w1[l], C, F, m->ws + L.dh, nullptr));
     }
     RUN(K_RMSNORM_BWD, return gk::launch_rmsnorm_bwd(dt, m->ws + L.dh, m->ws + L.h2[l], wsp<float>(m, L.rstd2[l]),
-                                                     N, C, 1, wsp<float>(m, L.dres), m->ws + L.dres_lp, stream););
+                                                     N, C, 1, dres32, m->ws + L.dres_lp, stream););
     // attention
     if (fp8) {
       TRY(quantize_operand(m, stream, m->ws + L.dres_lp, N, C, dyq, dyqT, Np, slot(l, A_DY_ATTN)));
@@ -979,9 +985,9 @@ gpt_status gpt_backward(gpt_model* m, float dloss, int32_t accumulate, void* str
       TRY(dx(K_GEMM_QKV_DX, gk::Epi::Store, m->ws + L.dqkv, QKV, m->off_qkv[l], C, QKV, m->ws + L.dh, nullptr));
     }
     RUN(K_RMSNORM_BWD, return gk::launch_rmsnorm_bwd(dt, m->ws + L.dh, m->ws + L.h1[l], wsp<float>(m, L.rstd1[l]),
-                                                     N, C, 1, wsp<float>(m, L.dres), m->ws + L.dres_lp, stream););
+                                                     N, C, 1, dres32, m->ws + L.dres_lp, stream););
     if (c.x0_lambdas)  // x_in = resid_lambdas[l] x_prev + x0_lambdas[l] x0
-      RUN(K_X0_MIX_BWD, return gk::launch_x0_mix_bwd(dt, wsp<float>(m, L.dres), m->ws + L.dres_lp, m->ws + L.xprev[l],
+      RUN(K_X0_MIX_BWD, return gk::launch_x0_mix_bwd(dt, dres32, m->ws + L.dres_lp, m->ws + L.xprev[l],
                                                      m->ws + L.x0, wsp<float>(m, L.dx0acc),
                                                      pbase(m, m->off_resid + l), pbase(m, m->off_x0lam + l), l == 0,
                                                      (int64_t)N * C, wsp<float>(m, L.rpart), G + m->off_resid + l,
@@ -992,7 +998,8 @@ gpt_status gpt_backward(gpt_model* m, float dloss, int32_t accumulate, void* str
     a.dtype = dt;
     a.wte = pbase(m, m->off_wte);
     a.idx = m->idx;
-    a.dres = wsp<float>(m, L.dres);
+    a.dres = dres32;
+    a.dres_lp = m->ws + L.dres_lp;
     a.rstd0 = wsp<float>(m, L.rstd0);
     a.N = N; a.C = C; a.V = V;
     a.accumulate = acc;
@@ -1061,6 +1068,10 @@ gpt_status gpt_set_option(gpt_model* m, int32_t option, int32_t value) {
     case GPT_OPT_DKV_HSPLIT:
       if (value < 0 || value > 2) return fail(GPT_E_INVALID_ARG, "dK/dV head-split option %d not in 0..2", value);
       m->dkv_hsplit = value;
+      return GPT_OK;
+    case GPT_OPT_RESID_GRAD:
+      if (value < 0 || value > 1) return fail(GPT_E_INVALID_ARG, "residual-gradient option %d not in 0..1", value);
+      m->resid_grad_f32 = value;
       return GPT_OK;
     default:
       return fail(GPT_E_INVALID_ARG, "unknown option %d", option);

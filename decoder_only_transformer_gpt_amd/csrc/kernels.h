@@ -69,6 +69,7 @@ hipError_t launch_embed_rmsnorm(int dtype, const void* wte, const int32_t* idx, 
 hipError_t launch_rmsnorm(int dtype, const void* x, int N, int C, float eps, void* y, float* rstd,
                           hipStream_t s);
 // dres = (accumulate ? dres : 0) + r * (dy - y * mean(dy*y)); dres_lp = dres in the activation dtype;
+// with dres null the gradient is kept in dres_lp alone (read there when accumulating);
 // dy_row_scale (optional, fp32 [N]): dy of row n is multiplied by dy_row_scale[n] first
 hipError_t launch_rmsnorm_bwd(int dtype, const void* dy, const void* y, const float* rstd, int N, int C,
                               int accumulate, float* dres, void* dres_lp, hipStream_t s,
@@ -119,7 +120,8 @@ struct EmbedBwdArgs {
   int dtype;
   const void* wte;       // [V, C]
   const int32_t* idx;    // [N]
-  const float* dres;     // [N, C] gradient w.r.t. x0 (the normalised embedding)
+  const float* dres;     // [N, C] gradient w.r.t. x0 (the normalised embedding), fp32; or null:
+  const void* dres_lp = nullptr;  // then this one, [N, C] in the activation dtype
   const float* rstd0;    // [N]
   int N, C, V;
   int accumulate;
@@ -148,6 +150,7 @@ hipError_t launch_x0_mix(int dtype, void* x, const void* x0, void* xprev, const 
                          int64_t n, hipStream_t s);
 // backward of the mix: scalar gradients (+)= <dres, xprev>, <dres, x0>; dres
 // becomes the gradient of xprev (first: of x0, dx0acc included); dres_lp = dres
+// (dres null: the gradient is read from and written to dres_lp alone)
 hipError_t launch_x0_mix_bwd(int dtype, float* dres, void* dres_lp, const void* xprev, const void* x0, float* dx0acc,
                              const void* lam_r, const void* lam_0, int first, int64_t n, float* partials,
                              float* g_lam_r, float* g_lam_0, int accumulate, hipStream_t s);

@@ -80,7 +80,9 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const T* __restrict__ src,
   if (lane == 0) rstd[row] = r;
 }
 
-// dres = (accumulate ? dres : 0) + r * (dy - y * mean(dy * y)); dres_lp = dres (activation dtype)
+// dres = (accumulate ? dres : 0) + r * (dy - y * mean(dy * y)); dres_lp = dres (activation dtype).
+// With dres null the residual gradient lives in dres_lp alone (activation
+// dtype, accumulated in fp32 inside the kernel and rounded once per call).
 template <typename T, int J>
 __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const T* __restrict__ dy, const T* __restrict__ y,
                                                           const float* __restrict__ rstd, int N, int C,
@@ -103,7 +105,12 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const T* __restrict__ 
   }
   if (accumulate) {
 #pragma unroll
-    for (int j = 0; j < J; ++j) load8(dres + off + chunk_of(lane, j, nch) * 8, o[j]);
+    for (int j = 0; j < J; ++j) {
+      if (dres)
+        load8(dres + off + chunk_of(lane, j, nch) * 8, o[j]);
+      else
+        load8(dres_lp + off + chunk_of(lane, j, nch) * 8, o[j]);
+    }
   }
   float dot = 0.f;
 #pragma unroll
@@ -127,7 +134,7 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const T* __restrict__ 
         const float dx = r * (g[j][e] - yy[j][e] * dot);
         out[e] = accumulate ? o[j][e] + dx : dx;
       }
-      store8(dres + off + ch * 8, out);
+      if (dres) store8(dres + off + ch * 8, out);
       store8(dres_lp + off + ch * 8, out);
     }
   }

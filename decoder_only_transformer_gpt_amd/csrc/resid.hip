@@ -50,7 +50,8 @@ __global__ __launch_bounds__(256) void x0_mix_kernel(T* __restrict__ x, const T*
   }
 }
 
-// Backward of the mix at layer l, d = dL/dx_in (fp32):
+// Backward of the mix at layer l, d = dL/dx_in (fp32 in dres, or in the
+// activation dtype in dres_lp alone when dres is null):
 //   partials: sum d * x_prev, sum d * x0 (for the two scalars' gradients);
 //   l > 0: dx0acc += l0 * d, d <- lr * d;  l == 0 (x_prev is x0 itself):
 //   d <- lr * d + l0 * d + dx0acc, the whole gradient reaching x0.
@@ -65,7 +66,10 @@ __global__ __launch_bounds__(256) void x0_mix_bwd_kernel(float* __restrict__ dre
   float pr = 0.f, p0 = 0.f;
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n8; i += (int64_t)gridDim.x * blockDim.x) {
     float d[8], xp[8], z[8], acc[8];
-    load8(dres + i * 8, d);
+    if (dres)
+      load8(dres + i * 8, d);
+    else
+      load8(dres_lp + i * 8, d);
     load8(xprev + i * 8, xp);
     load8(x0 + i * 8, z);
     load8(dx0acc + i * 8, acc);
@@ -85,7 +89,7 @@ __global__ __launch_bounds__(256) void x0_mix_bwd_kernel(float* __restrict__ dre
       }
       store8(dx0acc + i * 8, acc);
     }
-    store8(dres + i * 8, d);
+    if (dres) store8(dres + i * 8, d);
     store8(dres_lp + i * 8, d);
   }
   pr = block_sum256(pr, red);

@@ -68,6 +68,9 @@ class GPT:
     def set_dkv_hsplit(self, hsplit: int):
         _lib.gpt_set_option(self.h, _lib.GPT_OPT_DKV_HSPLIT, hsplit)
 
+    def set_resid_grad_f32(self, on: bool):
+        _lib.gpt_set_option(self.h, _lib.GPT_OPT_RESID_GRAD, 1 if on else 0)
+
     def close(self):
         if self.h is not None:
             _lib.gpt_destroy(self.h)

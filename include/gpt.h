@@ -232,8 +232,14 @@ gpt_status gpt_profile_end(gpt_model* m, double* total_ms, int64_t* launches);
  * sliding window, over two workgroups of H/2 heads each whose fp32 partial
  * rows a combine kernel adds in order (2). 1 or 2 force that form (2 needs
  * an even H, else 1 is used). Same result up to rounding order; the option
- * exists to test both forms at any size. */
-enum { GPT_OPT_GEMM_TILE = 1, GPT_OPT_DKV_HSPLIT = 2 };
+ * exists to test both forms at any size.
+ * GPT_OPT_RESID_GRAD: where a bf16 model keeps the gradient of the residual
+ * stream through the backward. 0 (default): in bf16, as for any gradient of
+ * a bf16 activation (each kernel adds in fp32 and rounds once); 1: in fp32
+ * (the bf16 copy the weight-gradient and dX products read is still made).
+ * fp32 models, and models with the residual scalars (x0_lambdas), keep it in
+ * fp32 either way. */
+enum { GPT_OPT_GEMM_TILE = 1, GPT_OPT_DKV_HSPLIT = 2, GPT_OPT_RESID_GRAD = 3 };
 gpt_status gpt_set_option(gpt_model* m, int32_t option, int32_t value);
 
 /* Name of a kernel tag (NULL past the last tag); tags run 0..n-1. */

@@ -71,7 +71,7 @@ class Case:
 
 def run_gpu(case: Case, dloss: float = 1.0, accumulate: bool = False, row_loss: bool = True, backward: bool = True,
             max_B: int | None = None, max_T: int | None = None, params_override=None, tile: int = 0,
-            hsplit: int = 0):
+            hsplit: int = 0, resid_grad_f32: bool = False):
     torch = require_gpu()
     from decoder_only_transformer_gpt_amd.model import GPT
     params = GPT.params_from_numpy(case.storage if params_override is None else params_override, case.cfg)
@@ -80,6 +80,8 @@ def run_gpu(case: Case, dloss: float = 1.0, accumulate: bool = False, row_loss: 
         m.set_gemm_tile(tile)
     if hsplit:
         m.set_dkv_hsplit(hsplit)
+    if resid_grad_f32:
+        m.set_resid_grad_f32(True)
     idx = torch.from_numpy(case.idx).cuda()
     tgt = torch.from_numpy(case.tgt).cuda()
     rl = torch.zeros(case.B * case.T, dtype=torch.float32, device="cuda") if row_loss else None

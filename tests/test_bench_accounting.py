@@ -86,21 +86,21 @@ def test_layer_windows_follow_the_pattern_and_keep_the_last_layer_full():
 
 def test_row_kernel_bytes_per_token():
     """The algorithmic bytes of the row kernels per token, bf16 activations
-    (a = 2 bytes), fp32 statistics and residual gradient."""
+    (a = 2 bytes), fp32 statistics."""
     cfg = WORKLOADS["d20"].config()
     C, H = cfg.model_dim, cfg.n_head
     per = {t: bench.kernel_bytes_per_launch(t, cfg, 1, 1, 2) for t in
            ("rmsnorm", "rmsnorm_bwd", "embed_rmsnorm", "rope_qknorm", "rope_qknorm_bwd", "attn_fwd_transpose")}
     assert per["rmsnorm"] == 4 * C + 4
-    assert per["rmsnorm_bwd"] == 12 * C + 4
+    assert per["rmsnorm_bwd"] == 8 * C + 4    # the residual gradient kept in bf16
     assert per["embed_rmsnorm"] == 4 + 4 * C + 4
     assert per["rope_qknorm"] == 4 * (H + 1) * D + 4 * (H + 1)
     assert per["rope_qknorm_bwd"] == 6 * (H + 1) * D + 4 * (H + 1)
     assert per["attn_fwd_transpose"] == 4 * D
-    # embedding backward: per token the fp32 gradient row and 12 bytes, every
-    # dwte row once, one embedding row per distinct id
+    # embedding backward: per token the bf16 gradient row and 12 bytes, every
+    # dwte row once (fp32), one embedding row per distinct id
     V = cfg.vocab_size
-    assert bench.kernel_bytes_per_launch("embed_bwd", cfg, 2, 3, 2, distinct=5) == 6 * (4 * C + 12) + V * C * 4 + 5 * C * 2
+    assert bench.kernel_bytes_per_launch("embed_bwd", cfg, 2, 3, 2, distinct=5) == 6 * (2 * C + 12) + V * C * 4 + 5 * C * 2
     assert bench.kernel_bytes_per_launch("gemm_qkv", cfg, 2, 3, 2) is None
 
 

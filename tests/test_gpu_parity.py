@@ -123,6 +123,25 @@ def test_d4_bf16_full_step(tile):
     check_bf16(case, gpu, loss, G, "d4")
 
 
+def test_d4_bf16_fp32_residual_gradient_option():
+    """GPT_OPT_RESID_GRAD = 1 keeps a bf16 model's residual-stream gradient in
+    fp32: the same bar against the oracle, the same loss bit for bit (the
+    forward is untouched), gradients close to the default bf16-kept ones;
+    values outside 0..1 are rejected."""
+    U.require_gpu()
+    case = U.Case(d4_cfg(), B=4, T=512, law="zipf")
+    U.log("case d4 bf16 B=4 T=512 zipf, residual gradient fp32 vs bf16")
+    g32 = U.run_gpu(case, resid_grad_f32=True)
+    g16 = U.run_gpu(case)
+    assert g32["status"] == _lib.GPT_OK and g16["status"] == _lib.GPT_OK
+    loss, rows, G = O.step(U.oracle_cfg(case.cfg), case.oracle_params(), case.idx, case.tgt)
+    check_bf16(case, g32, loss, G, "d4-resid-f32")
+    assert g32["loss"] == g16["loss"]
+    assert U.cosine(g32["grads"], g16["grads"]) >= 0.9999
+    with pytest.raises(RuntimeError):
+        _lib.gpt_set_option(g16["model"].h, _lib.GPT_OPT_RESID_GRAD, 2)
+
+
 @pytest.mark.parametrize("tile", [0, 1, 2, 3])
 def test_bf16_ragged_zipf(tile):
     """bf16, Zipf ids (heavy repeats in the embedding backward), ragged T and M

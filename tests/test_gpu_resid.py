@@ -61,7 +61,8 @@ def test_bf16_lambdas_and_value_embeds_zipf_ragged(tile):
 def test_neutral_scalars_and_zero_gates_equal_the_plain_model():
     """resid_lambdas = 1, x0_lambdas = 0 and zero gates reproduce the plain
     model bit for bit (loss and every shared gradient), and leave the tables'
-    gradients at zero."""
+    gradients at zero. A model with the residual scalars keeps the residual
+    gradient in fp32, so the plain model runs with that option too."""
     U.require_gpu()
     plain = U.Case(d4_cfg(), B=2, T=256, law="zipf", wseed=25, tseed=26)
     opt = U.Case(with_options(d4_cfg()), B=2, T=256, law="zipf", wseed=25, tseed=26)
@@ -76,7 +77,7 @@ def test_neutral_scalars_and_zero_gates_equal_the_plain_model():
     for k, (o, n) in p_names.items():
         storage[names[k][0]:names[k][0] + n] = plain.storage[o:o + n]
     g_opt = U.run_gpu(opt, params_override=storage)
-    g_plain = U.run_gpu(plain)
+    g_plain = U.run_gpu(plain, resid_grad_f32=True)
     assert g_opt["loss"] == g_plain["loss"]
     for k, (o, n) in p_names.items():
         np.testing.assert_array_equal(g_opt["grads"][names[k][0]:names[k][0] + n], g_plain["grads"][o:o + n],
