@@ -91,6 +91,10 @@ def kernel_flops_per_launch(tag: str, cfg, B: int, T: int) -> float | None:
     return None
 
 
+# tags whose byte figure below covers all of the tag's launches in a step
+STEP_BYTE_TAGS = {"embed_bwd"}
+
+
 def kernel_bytes_per_launch(tag: str, cfg, B: int, T: int, es: int, distinct: int = 0,
                             fp8: bool = False) -> float | None:
     """Algorithmic HBM bytes of one launch of a memory-bound kernel (distinct:
@@ -119,7 +123,7 @@ def kernel_bytes_per_launch(tag: str, cfg, B: int, T: int, es: int, distinct: in
          "ce_loss": N * (V // 64 * 4 + 16),
          # the residual-gradient rows (activation dtype), rstd and the sorted (id, position)
          # pairs in; every dwte row written once (zeros included); one embedding row per
-         # distinct id
+         # distinct id (for the step: the zeroing and the segment sums together)
          "embed_bwd": N * (C * es + 12) + V * C * 4 + distinct * C * es,
          # two radix passes over (id, position) pairs plus the initial pairs
          "embed_sort": N * (4 + 8 + 2 * 16),
@@ -307,7 +311,10 @@ def main():
         for t, (ms, n) in sorted(per_tag.items(), key=lambda kv: -kv[1][0]):
             f = kernel_flops_per_launch(t, cfg, B, T)
             kb = kernel_bytes_per_launch(t, cfg, B, T, 4 if wl.dtype == "f32" else 2, distinct, wl.dtype == "fp8")
-            rate = f"{f * n / ms / 1e9:8.1f} TFLOP/s" if f else (f"{kb * n / ms / 1e6:8.1f} GB/s" if kb else "")
+            # the embedding backward's bytes are the step's: its zeroing of dwte
+            # and its segment sums are two launches of the one tag
+            nb = 1 if t in STEP_BYTE_TAGS else n
+            rate = f"{f * n / ms / 1e9:8.1f} TFLOP/s" if f else (f"{kb * nb / ms / 1e6:8.1f} GB/s" if kb else "")
             print(f"[bench] {t:24s} {ms:9.3f} ms {n:4d} launches {100 * ms / tot:5.1f}% {rate}",
                   file=sys.stderr, flush=True)
 

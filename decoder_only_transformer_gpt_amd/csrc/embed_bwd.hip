@@ -347,6 +347,9 @@ __global__ __launch_bounds__(256) void seg_fixup_kernel(const int32_t* __restric
     float x[8][8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) load8(carry + ((int64_t)(cc + u) * 2 + 0) * (C + 8) + colc, x[u]);
+    // all eight rows requested before the first add (left to itself the
+    // scheduler interleaves each load with its add, two or three in flight)
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < 8; ++u)
 #pragma unroll
@@ -526,7 +529,7 @@ hipError_t launch_embed_bwd(const EmbedBwdArgs& a, hipStream_t s) {
   const int N = a.N, C = a.C;
   if (C % 8 != 0 || C > 4096 || (!a.dres && !a.dres_lp)) return hipErrorInvalidValue;
   hipError_t e;
-  if (!a.accumulate) {
+  if (!a.accumulate && !a.dwte_zeroed) {
     if ((e = launch_fill_f32(a.dwte, 0.f, (int64_t)a.V * C, s)) != hipSuccess) return e;
   }
   if (N <= 0) return hipSuccess;

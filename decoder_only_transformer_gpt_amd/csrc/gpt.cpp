@@ -913,6 +913,12 @@ gpt_status gpt_backward(gpt_model* m, float dloss, int32_t accumulate, void* str
   RUN(K_CE_BWD, return gk::launch_ce_grad_prep(dt, m->ws + L.logits, wsp<float>(m, L.lse_ce), wsp<float>(m, L.ztgt),
                                                m->targets, N, V, c.logit_softcap, dloss / (float)N, m->ws + L.hf, C,
                                                m->ws + L.dh, wsp<float>(m, L.ce_rscale), stream););
+  // The embedding gradient is zeroed here, ahead of the LM-head products,
+  // rather than just before its segment sums: the zeros (4VC bytes) land in
+  // the caches, and their write-back to HBM then drains under these
+  // MFMA-bound GEMMs instead of under the segment sums' reads.
+  if (!acc)
+    RUN(K_EMBED_BWD, return gk::launch_fill_f32(G + m->off_wte, 0.f, (int64_t)V * C, stream););
   TRY(dw(K_GEMM_LM_DW, m->ws + L.logits, V, m->ws + L.dh, C, V, C, m->off_lm));
   TRY(dx(K_GEMM_LM_DX, gk::Epi::Store, m->ws + L.logits, V, m->off_lm, C, V, m->ws + L.dh, nullptr));
   RUN(K_RMSNORM_BWD, return gk::launch_rmsnorm_bwd(dt, m->ws + L.dh, m->ws + L.hf, wsp<float>(m, L.rstdf), N, C, 0,
@@ -1003,6 +1009,7 @@ gpt_status gpt_backward(gpt_model* m, float dloss, int32_t accumulate, void* str
     a.rstd0 = wsp<float>(m, L.rstd0);
     a.N = N; a.C = C; a.V = V;
     a.accumulate = acc;
+    a.dwte_zeroed = 1;  // zeroed before the LM-head products (without accumulate)
     a.dwte = G + m->off_wte;
     a.keys_a = wsp<int32_t>(m, L.keys_a);
     a.vals_a = wsp<int32_t>(m, L.vals_a);

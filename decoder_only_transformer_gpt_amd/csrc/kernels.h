@@ -125,6 +125,7 @@ struct EmbedBwdArgs {
   const float* rstd0;    // [N]
   int N, C, V;
   int accumulate;
+  int dwte_zeroed = 0;   // without accumulate: dwte was zeroed earlier by the caller (no fill here)
   float* dwte;           // [V, C] fp32
   // scratch (inside the workspace); keys_a / vals_a hold the ids sorted by launch_embed_sort
   int32_t* keys_a; int32_t* vals_a; int32_t* keys_b; int32_t* vals_b;  // [N] each

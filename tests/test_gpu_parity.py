@@ -361,3 +361,66 @@ def test_bf16_degenerate_lengths(B, T):
     assert gpu["status"] == _lib.GPT_OK
     loss, rows, G = O.step(U.oracle_cfg(case.cfg), case.oracle_params(), case.idx, case.tgt)
     check_bf16(case, gpu, loss, G, f"d4-B{B}-T{T}")
+
+
+# ------------------------------------------------- embedding gradient rows ---
+
+def wide_one_layer_cfg(V=2048):
+    """One layer at the d20 width (1280 columns: the embedding backward's
+    three 512-column groups per lane, as in the benchmarked step) with a
+    small vocabulary, so that Zipf ids give long runs of one id across many
+    chunks of sorted entries as well as ids seen once."""
+    c = _lib.gpt_config_from_depth(20, _lib.GPT_BF16)
+    c.n_layer = 1
+    c.vocab_size = V
+    return c
+
+
+def check_embedding_rows(case, gpu, G, label):
+    """The embedding gradient row by row: rows of ids absent from the batch
+    exactly zero, every present id's row within cosine 0.99 of the oracle
+    (rows of ids seen once carry one position's contribution, so a lost,
+    doubled or misplaced entry of the sorted sums fails here even where the
+    whole tensor's cosine would hide it)."""
+    gg = U.split_tensors(case, gpu["grads"])["wte"]
+    go = U.split_tensors(case, case.flat_grads(G))["wte"]
+    present = np.zeros(case.cfg.vocab_size, dtype=bool)
+    present[case.idx.ravel()] = True
+    assert np.all(go[~present] == 0.0)
+    assert np.all(gg[~present] == 0.0), f"{label}: nonzero rows for absent ids"
+    na = np.linalg.norm(gg[present], axis=1)
+    nb = np.linalg.norm(go[present], axis=1)
+    cos = np.einsum("ij,ij->i", gg[present], go[present]) / np.maximum(na * nb, 1e-300)
+    U.log(f"[{label}] {present.sum()} present ids, worst row cosine {cos.min():.5f}")
+    assert cos.min() >= 0.99
+
+
+@pytest.mark.parametrize("T", [333, 512])
+def test_embedding_gradient_rows_zipf(T):
+    """The embedding backward at the d20 width on Zipf ids, row by row
+    against the oracle: a ragged count of sorted entries (T = 333, B = 3:
+    999 entries, the last chunk partly filled) and a whole number of chunks
+    (T = 512); then a second step on the same model with other ids, whose
+    absent rows must come back zero (nothing kept from the first step)."""
+    U.require_gpu()
+    import torch
+    c = wide_one_layer_cfg()
+    case = U.Case(c, B=3, T=T, law="zipf", wseed=21, tseed=22)
+    U.log(f"case 1-layer width 1280 V=2048 bf16 B=3 T={T} zipf: embedding rows")
+    gpu = U.run_gpu(case)
+    assert gpu["status"] == _lib.GPT_OK
+    loss, rows, G = O.step(U.oracle_cfg(c), case.oracle_params(), case.idx, case.tgt)
+    check_bf16(case, gpu, loss, G, f"emb-rows-T{T}")
+    check_embedding_rows(case, gpu, G, f"emb-rows-T{T}")
+    # second step, same model, uniform ids over the upper half of the vocabulary
+    rng = np.random.default_rng(23)
+    seq = rng.integers(c.vocab_size // 2, c.vocab_size, size=(3, T + 1)).astype(np.int32)
+    case.idx, case.tgt = np.ascontiguousarray(seq[:, :T]), np.ascontiguousarray(seq[:, 1:])
+    m = gpu["model"]
+    m.forward_loss(torch.from_numpy(case.idx).cuda(), torch.from_numpy(case.tgt).cuda(), need_grad=True)
+    m.backward(1.0, False)
+    torch.cuda.synchronize()
+    assert m.sync_status() == _lib.GPT_OK
+    gpu2 = dict(grads=m.grads.cpu().numpy().astype(np.float64))
+    _, _, G2 = O.step(U.oracle_cfg(c), case.oracle_params(), case.idx, case.tgt)
+    check_embedding_rows(case, gpu2, G2, f"emb-rows-T{T}-second")
