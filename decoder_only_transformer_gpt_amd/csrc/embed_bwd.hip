@@ -291,23 +291,35 @@ __global__ __launch_bounds__(256) void embed_seg_kernel(const int32_t* __restric
   }
 }
 
-// Last sorted position holding id v, searching from position `from` (whose
-// key is v): a binary search over the ascending keys.
-DEV int segment_last(const int32_t* __restrict__ keys, int N, int from, int v) {
-  int lo = from, hi = N;  // keys[lo] == v; keys[hi] != v (or hi == N)
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (keys[mid] == v) lo = mid;
-    else hi = mid;
+// Last chunk that a run of id v reaches, for a run that begins in chunk c and
+// goes on past it (keys ascending, so the run's chunks are those whose first
+// entry holds v). The wave's lanes probe the first entries of chunks S apart
+// (lane 0 at a chunk known to start inside the run); the first probe outside
+// bounds the run, and one more round probes the S chunks before it: two
+// rounds of loads per 63 S chunks of run, where a binary search over the
+// entries takes one dependent load per halving.
+DEV int run_last_chunk(const int32_t* __restrict__ keys, int nchunks, int c, int v, int lane) {
+  constexpr int S = 16;
+  int in = c + 1;  // starts inside the run: the run goes on past chunk c
+  for (;;) {
+    const int p = in + lane * S;
+    const uint64_t out = __ballot(p >= nchunks || keys[p * kSegChunk] != v);
+    if (out == 0) {  // every probe inside: lane 63's chunk starts inside
+      in += 63 * S;
+      continue;
+    }
+    const int lo = in + (__builtin_ctzll(out) - 1) * S;  // inside; lo + S is outside or past the end
+    const int q = lo + lane;
+    const uint64_t out2 = __ballot(lane >= S || q >= nchunks || keys[q * kSegChunk] != v);
+    return lo + __builtin_ctzll(out2) - 1;  // out2 has a bit at or below S, and none at 0
   }
-  return lo;
 }
 
 // One block of four waves per (chunk in which a boundary-crossing run starts,
 // 512 columns): adds that run's partial rows (slot 1 of its first chunk and
 // slot 0 of every later chunk it reaches) and their k sums, and adds
 // a1 - wte[v] * ks to dwte[v]. The chunk holding the run's last entry is found
-// by a binary search; each wave sums a contiguous quarter of the slot-0 range
+// by probing chunk starts across the wave's lanes; each wave sums a contiguous quarter of the slot-0 range
 // (eight rows in flight per lane), and wave 0 adds slot 1 and the quarters in
 // order, so the frequent ids' long runs are summed by four waves in a fixed
 // order.
@@ -329,7 +341,7 @@ __global__ __launch_bounds__(256) void seg_fixup_kernel(const int32_t* __restric
   if (keys[e1] != v) return;                // last run does not continue
   // did the run start inside this chunk?
   if (keys[e0] == v && e0 > 0 && keys[e0 - 1] == v) return;  // began earlier: owned by an earlier chunk
-  const int cend = min(nchunks - 1, segment_last(keys, N, e1, v) / kSegChunk);
+  const int cend = run_last_chunk(keys, nchunks, c, v, lane);
   const int n = cend - c;  // slot-0 partials: chunks c+1 .. cend
   const int q0 = c + 1 + (int)((int64_t)n * wave / 4), q1 = c + 1 + (int)((int64_t)n * (wave + 1) / 4);
   // this wave's k sums: lane-strided partial sums combined by a fixed butterfly
@@ -426,7 +438,7 @@ __global__ __launch_bounds__(128) void ve_seg_fixup_kernel(const int32_t* __rest
   int s = last;
   while (s > e0 && keys[s - 1] == v) --s;
   if (s == e0 && e0 > 0 && keys[e0 - 1] == v) return;
-  const int cend = min(nchunks - 1, segment_last(keys, N, e1, v) / kSegChunk);
+  const int cend = run_last_chunk(keys, nchunks, c, v, col & 63);
   float acc = carry[((int64_t)c * 2 + 1) * 129 + col];
 #pragma unroll 8
   for (int cc = c + 1; cc <= cend; ++cc) acc += carry[((int64_t)cc * 2 + 0) * 129 + col];
