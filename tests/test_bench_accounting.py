@@ -101,6 +101,9 @@ def test_row_kernel_bytes_per_token():
     # dwte row once (fp32), one embedding row per distinct id
     V = cfg.vocab_size
     assert bench.kernel_bytes_per_launch("embed_bwd", cfg, 2, 3, 2, distinct=5) == 6 * (2 * C + 12) + V * C * 4 + 5 * C * 2
+    # ...for the whole step: the zeroing of dwte and the segment sums are two
+    # launches of that tag, counted once between them
+    assert bench.STEP_BYTE_TAGS == {"embed_bwd"}
     assert bench.kernel_bytes_per_launch("gemm_qkv", cfg, 2, 3, 2) is None
 
 
