@@ -319,10 +319,10 @@ DEV int run_last_chunk(const int32_t* __restrict__ keys, int nchunks, int c, int
 // 512 columns): adds that run's partial rows (slot 1 of its first chunk and
 // slot 0 of every later chunk it reaches) and their k sums, and adds
 // a1 - wte[v] * ks to dwte[v]. The chunk holding the run's last entry is found
-// by probing chunk starts across the wave's lanes; each wave sums a contiguous quarter of the slot-0 range
-// (eight rows in flight per lane), and wave 0 adds slot 1 and the quarters in
-// order, so the frequent ids' long runs are summed by four waves in a fixed
-// order.
+// by probing chunk starts across the wave's lanes; each wave sums a contiguous
+// quarter of the slot-0 range (eight rows in flight per lane), and wave 0 adds
+// slot 1 and the quarters in order, so the frequent ids' long runs are summed
+// by four waves in a fixed order.
 template <typename T>
 __global__ __launch_bounds__(256) void seg_fixup_kernel(const int32_t* __restrict__ keys, int N, int C, int nchunks,
                                                         const T* __restrict__ wte, const float* __restrict__ carry,
