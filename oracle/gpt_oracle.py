@@ -558,16 +558,6 @@ def forward_rows(cfg: dict, params: dict, idx: np.ndarray, targets: np.ndarray) 
     return row_loss
 
 
-def flops_per_token(cfg: dict, T: int) -> dict:
-    """Algorithmic FLOPs per token for fwd+bwd: 6 * (matmul params) plus causal
-    attention counted over the T(T+1)/2 needed (query, key) pairs."""
-    C, H, D, F, V, Lyr = (cfg["model_dim"], cfg["n_head"], cfg["head_dim"],
-                          cfg["mlp_dim"], cfg["vocab_size"], cfg["n_layer"])
-    n_mm = Lyr * ((H + 2) * D * C + C * H * D + 2 * F * C) + V * C
-    attn = 6.0 * Lyr * H * D * (T + 1)
-    return dict(matmul=6.0 * n_mm, attention=attn, total=6.0 * n_mm + attn)
-
-
 # ---------------------------------------------------------------------------
 # The optimiser step that follows the backward
 # ---------------------------------------------------------------------------

@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 from decoder_only_transformer_gpt_amd import _lib
@@ -66,6 +67,27 @@ def test_layout_matches_oracle_order():
         assert o == off
         off += r * cc
     assert off == _lib.gpt_param_count(c)
+
+
+def test_oracle_unflatten_reads_the_documented_row_major_layout():
+    """The oracle's view of a flat parameter (or gradient) buffer: element
+    (i, j) of each tensor sits at the library's offset + i * cols + j, the
+    row-major layout gpt_tensor_desc documents (every tensor kind, the
+    optional ones included, at a small vocabulary)."""
+    c = _lib.gpt_config_from_depth(4, _lib.GPT_BF16)
+    c.n_layer, c.vocab_size = 3, 512
+    c.x0_lambdas, c.value_embeds = 1, 1
+    assert _lib.gpt_config_validate(c) == _lib.GPT_OK
+    n = _lib.gpt_param_count(c)
+    flat = np.arange(n, dtype=np.int64)
+    got = O.unflatten(c.as_dict(), flat)
+    lay = _lib.gpt_param_layout(c)
+    assert list(got) == [name for name, _, _, _ in lay]
+    for name, off, r, cc in lay:
+        t = got[name]
+        assert t.shape == (r, cc), name
+        i, j = np.meshgrid(np.arange(r), np.arange(cc), indexing="ij")
+        assert np.array_equal(t, off + i * cc + j), name
 
 
 def test_validation_errors():
