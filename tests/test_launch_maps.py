@@ -12,30 +12,13 @@ every grid size the library can launch (and many more) for:
 No GPU is needed, and the test fails if a map's text can no longer be found.
 """
 import ctypes
-import os
-import re
 import shutil
 import subprocess
 
 import numpy as np
 import pytest
 
-ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-CSRC = os.path.join(ROOT, "decoder_only_transformer_gpt_amd", "csrc")
-
-
-def device_function(path, name):
-    """The full text of `DEV <type> name(...) { ... }` in a kernel source."""
-    src = open(os.path.join(CSRC, path)).read()
-    m = re.search(r"^DEV\s+\w+\s+" + name + r"\s*\(", src, flags=re.M)
-    assert m, f"{name} not found in {path}"
-    i = src.index("{", m.end())
-    depth = 0
-    for j in range(i, len(src)):
-        depth += {"{": 1, "}": -1}.get(src[j], 0)
-        if depth == 0:
-            return src[m.start():j + 1]
-    raise AssertionError(f"unbalanced braces after {name}")
+from host_src import device_function
 
 
 HARNESS = r"""
