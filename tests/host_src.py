@@ -27,3 +27,17 @@ def int_constant(path, name):
     m = re.search(r"constexpr\s+int\s+" + name + r"\s*=\s*(\d+)\s*;", src)
     assert m, f"{name} not found in {path}"
     return int(m.group(1))
+
+
+def kernel_function(path, name):
+    """The full text of a kernel `[template <...>] __global__ ... name(...) { ... }`."""
+    src = open(os.path.join(CSRC, path)).read()
+    m = re.search(r"^(template\s*<[^>]*>\s*\n)?__global__[^\n]*\b" + name + r"\s*\(", src, flags=re.M)
+    assert m, f"{name} not found in {path}"
+    i = src.index("{", m.end())
+    depth = 0
+    for j in range(i, len(src)):
+        depth += {"{": 1, "}": -1}.get(src[j], 0)
+        if depth == 0:
+            return src[m.start():j + 1]
+    raise AssertionError(f"unbalanced braces after {name}")
