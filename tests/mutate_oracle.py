@@ -51,6 +51,7 @@ MUTS = [
  ("fwd_qknorm_order", "qr, kr = rope(q, cos, sin), rope(k, cos, sin)\n        qn, rq = rmsnorm(qr, eps)", "qr, kr = rope(q, cos, sin), rope(k, cos, sin)\n        qn, rq = rmsnorm(q, eps)"),
  ("fwd_ve_gate", "v = v + W[\"ve_gates\"][0, vel.index(l)] * W[f\"h{l}.ve\"][idx][:, :, None, :]", "v = v + W[f\"h{l}.ve\"][idx][:, :, None, :]"),
  ("fwd_x0mix", "x = W[\"resid_lambdas\"][0, l] * x + W[\"x0_lambdas\"][0, l] * x0", "x = W[\"resid_lambdas\"][0, l] * x + W[\"x0_lambdas\"][0, l] * xprev"),
+ ("fwd_lse_chunk", "row_loss[s0:s1] = lse_rows[s0:s1] - zc[np.arange(s1 - s0), tg[s0:s1]]", "row_loss[s0:s1] = lse_rows[0:s1 - s0] - zc[np.arange(s1 - s0), tg[s0:s1]]"),
  ("fwd_tgt", "row_loss[s0:s1] = lse_rows[s0:s1] - zc[np.arange(s1 - s0), tg[s0:s1]]", "row_loss[s0:s1] = lse_rows[s0:s1] - zc[np.arange(s1 - s0), tg[s0]]"),
  ("bwd_relu2", "du = da * 2.0 * np.maximum(L[\"u\"], 0.0)", "du = da * np.maximum(L[\"u\"], 0.0)"),
  ("bwd_w2_unq", "G[f\"h{l}.w_2\"] += dy.reshape(N, C).T @ L[\"am\"].reshape(N, -1)", "G[f\"h{l}.w_2\"] += dy.reshape(N, C).T @ L[\"a\"].reshape(N, -1)"),
