@@ -51,6 +51,9 @@ MUTS = [
  ("fwd_qknorm_order", "qr, kr = rope(q, cos, sin), rope(k, cos, sin)\n        qn, rq = rmsnorm(qr, eps)", "qr, kr = rope(q, cos, sin), rope(k, cos, sin)\n        qn, rq = rmsnorm(q, eps)"),
  ("fwd_ve_gate", "v = v + W[\"ve_gates\"][0, vel.index(l)] * W[f\"h{l}.ve\"][idx][:, :, None, :]", "v = v + W[f\"h{l}.ve\"][idx][:, :, None, :]"),
  ("fwd_x0mix", "x = W[\"resid_lambdas\"][0, l] * x + W[\"x0_lambdas\"][0, l] * x0", "x = W[\"resid_lambdas\"][0, l] * x + W[\"x0_lambdas\"][0, l] * xprev"),
+ ("ns_c_term", "X = a * X + (b * A + c * (A @ A)) @ X", "X = a * X + (b * A + c * A) @ X"),
+ ("bwd_lse_chunk", 'p = np.exp(zc - cache["lse_rows"][s0:s1, None])', 'p = np.exp(zc - cache["lse_rows"][0:s1 - s0, None])'),
+ ("lr_swap", 'lrs = dict(embed=oc["lr_embed"], unembed=oc["lr_unembed"]', 'lrs = dict(embed=oc["lr_unembed"], unembed=oc["lr_embed"]'),
  ("fwd_lse_chunk", "row_loss[s0:s1] = lse_rows[s0:s1] - zc[np.arange(s1 - s0), tg[s0:s1]]", "row_loss[s0:s1] = lse_rows[0:s1 - s0] - zc[np.arange(s1 - s0), tg[s0:s1]]"),
  ("fwd_tgt", "row_loss[s0:s1] = lse_rows[s0:s1] - zc[np.arange(s1 - s0), tg[s0:s1]]", "row_loss[s0:s1] = lse_rows[s0:s1] - zc[np.arange(s1 - s0), tg[s0]]"),
  ("bwd_relu2", "du = da * 2.0 * np.maximum(L[\"u\"], 0.0)", "du = da * np.maximum(L[\"u\"], 0.0)"),
